@@ -1,0 +1,238 @@
+/*
+ * qdg.h -- C ABI of libqdg.so, a fused dequantize-and-multiply GEMM library for
+ * AMD Instinct MI355X (gfx950 / CDNA4).
+ *
+ * It computes Y = A * dequant(Wq, scales, zeros)^T for a linear layer whose
+ * weight W is stored [N, K] in a quantized "standard format", plus the
+ * expert-grouped MoE form of the same product.
+ *
+ * Design taken from the pages on the Humming kernel library:
+ *  - one standard representation of weights, scales and zero points, into
+ *    which every export format is brought; a preprocessing step then checks
+ *    the parameters, pads dimensions and repacks the tensors for the target
+ *    kernel (kinachrichten, "Wie die Architektur funktioniert");
+ *  - a kernel is described by a Layer config (shapes, types, quantization
+ *    parameters, target architecture), a Compute config (GEMM kind and options
+ *    such as batch invariance) and a Tuning config (tiles, pipeline, MMA
+ *    instruction); device heuristics fill the Tuning config when none is given
+ *    and different kernels may serve different input-size ranges (same
+ *    section);
+ *  - validation sits at the shared interface and unsupported combinations are
+ *    rejected clearly, never served silently ("vLLM Humming: why shared
+ *    quantization still needs specialized kernels", section "The architectural
+ *    gain is a smaller maintenance surface"); the record of which
+ *    implementation serves which combination is available
+ *    (retrivium analysis, section "A compatibility example").
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are device pointers owned by the caller (hipMalloc or
+ *    a framework allocator). The library keeps no tensor pointer after a call
+ *    returns and never allocates device memory in a compute call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Device work is enqueued asynchronously on it; host-side validation is
+ *    synchronous and happens before anything is enqueued.
+ *  - Every call returns a qdg_status. On anything but QDG_OK nothing has been
+ *    enqueued (except QDG_ERR_HIP, reported when a launch fails) and
+ *    qdg_last_error() returns a thread-local message.
+ *  - Row-major layouts; "bf16" = IEEE binary32 upper half; "f16" = binary16.
+ */
+#ifndef QDG_H
+#define QDG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QDG_LAYOUT_VERSION 1
+
+typedef enum qdg_status {
+  QDG_OK = 0,
+  QDG_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size, bad enum */
+  QDG_ERR_UNSUPPORTED = 2, /* a valid combination that no kernel instance serves */
+  QDG_ERR_MISALIGNED = 3,  /* a pointer or row stride breaks the 16-byte rule */
+  QDG_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  QDG_ERR_HIP = 5          /* the HIP runtime reported an error */
+} qdg_status;
+
+/* Weight element types of the standard format. */
+enum { QDG_W_INT4 = 0,  /* two's-complement 4-bit, symmetric (no zeros) */
+       QDG_W_UINT4 = 1, /* unsigned 4-bit with uint8 zero points (asymmetric) */
+       QDG_W_INT8 = 2,  /* int8, symmetric, one fp32 scale per output channel */
+       QDG_W_MXFP4 = 3  /* OCP MX FP4 E2M1 with E8M0 scale per 32 along K */ };
+/* Scale storage types. */
+enum { QDG_S_F16 = 0, QDG_S_F32 = 1, QDG_S_E8M0 = 2 };
+/* Activation types. */
+enum { QDG_A_BF16 = 0, QDG_A_INT8 = 1, QDG_A_FP8E4M3 = 2 };
+/* Output types. QDG_O_I32 returns the raw integer accumulator
+   sum_k qa*qw (integer-weight paths only; every scale ignored). */
+enum { QDG_O_BF16 = 0, QDG_O_F32 = 1, QDG_O_I32 = 2 };
+/* GEMM kinds (Compute config). */
+enum { QDG_KIND_DENSE = 0, QDG_KIND_MOE = 1 };
+
+/* Layer config: what the layer is. The weight of one layer (one expert) is
+   [n, k]. Supported combinations (anything else is QDG_ERR_UNSUPPORTED):
+     W4A16      wtype INT4 (has_zeros 0) or UINT4 (has_zeros 1), stype F16,
+                group_size 128, atype BF16, otype BF16 or F32
+     W8A8       wtype INT8, stype F32 (per channel, group_size 0), atype INT8,
+                act_group 0 (per token), otype BF16, F32 or I32
+     W4A8-INT8  wtype INT4, stype F16, group_size 128, atype INT8, act_group 0,
+                otype BF16, F32 or I32
+     W4A8-MXFP4 wtype MXFP4, stype E8M0, group_size 32, atype FP8E4M3,
+                act_group 128, otype BF16 or F32
+   Shapes: k a positive multiple of 128; n >= 1 (padded internally to a
+   multiple of 16); num_experts >= 1 (1 for a dense layer). arch = 950. */
+typedef struct qdg_layer_config {
+  int64_t n, k, num_experts;
+  int32_t wtype, stype, group_size, has_zeros;
+  int32_t atype, act_group, otype, arch;
+} qdg_layer_config;
+
+/* Compute config: which computation. kind DENSE or MOE (MoE: W4A16 INT4
+   only). batch_invariant = 1 makes row m of Y bitwise independent of M and
+   of the other rows (one fixed reduction order for every M). top_k: MoE
+   slots per token. */
+typedef struct qdg_compute_config {
+  int32_t kind, batch_invariant, top_k, reserved;
+} qdg_compute_config;
+
+/* Tuning config: how to run. Zero in any field means "heuristic". block_m
+   selects the kernel family (<= 64: streaming split-K family; >= 128: the
+   LDS-tiled MFMA family), block_n is the N tile (multiple of 16), split_k the
+   number of K partitions reduced in a fixed order, waves the wavefronts per
+   workgroup. Fields block_k, stages, mfma and load_path are recorded in the
+   description but only one value each is implemented (128, 2, 16, 0). */
+typedef struct qdg_tuning_config {
+  int32_t block_m, block_n, block_k, split_k;
+  int32_t stages, waves, mfma, load_path;
+} qdg_tuning_config;
+
+/* Standard-format weights (device pointers; all experts back to back):
+     INT4 / UINT4 / MXFP4 qweight  u8 [E][n][k/2], element k of a row in byte
+                                   k/2, even k in the low nibble
+     INT8 qweight                  i8 [E][n][k]
+     F16 scales                    f16 [E][n][k/group_size]
+     F32 scales (INT8)             f32 [E][n]
+     E8M0 scales (MXFP4)           u8 [E][n][k/32], value 2^(e-127); 255 invalid
+     zeros (UINT4 only)            u8 [E][n][k/group_size], values 0..15
+   Dequantized weight: w = (q - z) * s, z = 0 when symmetric; MXFP4:
+   w = e2m1(q) * 2^(e-127). */
+typedef struct qdg_std_weights {
+  const void* qweight;
+  const void* scales;
+  const void* zeros;
+} qdg_std_weights;
+
+typedef struct qdg_plan qdg_plan;
+
+/* Library identity: "qdg <version> gfx950 layout <QDG_LAYOUT_VERSION>". */
+const char* qdg_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* qdg_last_error(void);
+
+/* Checks a layer config against the supported combinations (host only). */
+qdg_status qdg_validate_layer(const qdg_layer_config* layer);
+
+/* Bytes of the packed (kernel-layout) buffer qdg_preprocess writes for this
+   layer, all experts included. */
+qdg_status qdg_preprocess_query(const qdg_layer_config* layer, size_t* packed_bytes);
+
+/* Preprocess (once per layer, not part of steady-state timing): validates
+   the layer, pads n to a multiple of 16 and rewrites the standard-format
+   weights into the gfx950 MFMA fragment layout of the target kernels.
+   `packed` (>= qdg_preprocess_query bytes, 256-byte aligned) is written
+   entirely; the standard-format buffers are only read. MXFP4 scale code 255
+   is not checked on the device: preprocess maps it to the largest finite
+   scale, so callers validate E8M0 input on the host when it is untrusted. */
+qdg_status qdg_preprocess(const qdg_layer_config* layer, const qdg_std_weights* weights,
+                          void* packed, size_t packed_bytes, void* stream);
+
+/* Quantize float32 weights [E][n][k] (device) into the standard format of
+   `layer` (a producer of the standard format). Decisions are taken in
+   binary32 with RNE:
+     INT4  s = f16(amax/7),  q = clamp(rne(w/s), -8, 7), per group of 128
+     UINT4 s = f16((max-min)/15), z = clamp(rne(-min/s), 0, 15),
+           q = clamp(rne(w/s) + z, 0, 15)
+     INT8  s = f32(amax/127), q = clamp(rne(w/s), -127, 127), per row
+     MXFP4 X = floor(log2(amax)) - 2 per 32, e = X + 127, q = e2m1_rne_sat(w/2^X)
+   A scale that is zero is stored as 1.0 (all-zero group). `zeros` is used
+   for UINT4 only. */
+qdg_status qdg_quantize_weights(const qdg_layer_config* layer, const float* w,
+                                void* qweight, void* scales, void* zeros, void* stream);
+
+/* Activation quantization for the W8A8 / W4A8 paths (layer->atype INT8 or
+   FP8E4M3). a_bf16 [M][k] row-major ->
+     INT8:    qa i8 [M][k], a_scales f32 [M];       per token
+     FP8E4M3: qa u8 E4M3 [M][k], a_scales f32 [M][k/128]; per 128-group
+   with amax the largest |x|, inv = f32(Q/amax) (Q = 127 or 448),
+   code = rne(clamp(f32(x*inv), -Q, Q)), scale = f32(amax/Q); amax = 0 gives
+   scale 1 and zero codes. Bit-exact by construction (binary32, RNE). */
+qdg_status qdg_quantize_act(const qdg_layer_config* layer, const void* a_bf16, int64_t M,
+                            void* qa, float* a_scales, void* stream);
+
+/* Build an execution plan (host only, no device work). tuning may be NULL
+   (device heuristics per M range). The plan is immutable and may be shared
+   across threads and streams; destroy it with qdg_plan_destroy. */
+qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_config* compute,
+                           const qdg_tuning_config* tuning, qdg_plan** out);
+void qdg_plan_destroy(qdg_plan* plan);
+
+/* Workspace bytes qdg_gemm / qdg_moe_gemm need for M rows (M = T for MoE).
+   The first 64 KiB are reduction counters: zero them once after allocating
+   (for example hipMemset); every call leaves them zero again. Calls that
+   share one workspace must be ordered on one stream. */
+qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes);
+
+/* Writes a one-line record of the kernel instance that serves M rows (family,
+   tiles, split, waves, MFMA shape, packed layout version, arch) into buf.
+   Returns the length of the full record (snprintf semantics), -1 on error. */
+int qdg_plan_describe(const qdg_plan* plan, int64_t M, char* buf, size_t len);
+
+/* Dense GEMM Y[M][n] = A[M][k] * dequant(W)^T.
+   A: bf16 [M][k] (W4A16), i8 [M][k] (W8A8, W4A8) or E4M3 [M][k] (MXFP4), row
+      stride k elements, 16-byte aligned.
+   a_scales: NULL for W4A16; f32 [M] (W8A8, W4A8); f32 [M][k/128] (MXFP4);
+      ignored (may be NULL) with otype I32.
+   packed: the qdg_preprocess output for this layer.
+   Y: [M][n] of otype (bf16, f32 or i32), row stride n.
+   M >= 0 (M = 0 enqueues nothing). workspace >= qdg_plan_workspace bytes. */
+qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, const void* packed,
+                    void* Y, int64_t M, void* workspace, size_t ws_bytes, void* stream);
+
+/* Capacity (entries of sorted_ids) that qdg_moe_align may need:
+   round_up(T*top_k + E*(block_m-1), block_m); block_expert needs
+   capacity/block_m entries. */
+qdg_status qdg_moe_align_capacity(int64_t T, int32_t top_k, int32_t num_experts, int32_t block_m,
+                                  int64_t* capacity);
+
+/* Expert sort for the grouped GEMM. topk_ids i32 [T][top_k] (values in
+   [0, E)) -> pairs (flat index t*top_k+j) sorted by expert, ascending flat
+   index within an expert, each expert padded to a multiple of block_m with
+   the sentinel T*top_k; experts with no pair get no block.
+   Outputs (capacity from qdg_moe_align_capacity): sorted_ids i32 [capacity]
+   (entries past num_padded hold the sentinel), block_expert i32
+   [capacity/block_m] (-1 past the last block), num_padded i32 [1].
+   block_m in {16, 32, 64, 128}; 1 <= top_k <= 32; T*top_k <= 2^20. */
+qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t num_experts,
+                         int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                         int32_t* num_padded, void* stream);
+
+/* Grouped MoE GEMM (W4A16): for every real entry i of sorted_ids in block b,
+   row i of Y = A[r] * dequant(W_e)^T with e = block_expert[b] and
+   r = i (a_per_pair = 1, e.g. the down projection) or r = i / top_k
+   (a_per_pair = 0, e.g. gate+up reading token rows). Y is [T*top_k][n];
+   rows are written only for real pairs. block_m must be the value passed to
+   qdg_moe_align and one the plan supports (see qdg_plan_describe). */
+qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scales,
+                        const void* packed, const int32_t* sorted_ids,
+                        const int32_t* block_expert, const int32_t* num_padded, int64_t T,
+                        int32_t block_m, int32_t a_per_pair, void* Y, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QDG_H */

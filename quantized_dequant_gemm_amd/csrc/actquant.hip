@@ -1,0 +1,133 @@
+// Activation quantization for the integer and fp8 paths (bf16 in).
+//
+// The pages name W8A8 and W4A8 as common configurations (kinachrichten,
+// "Warum quantisierte Kernel wichtig sind"; jetabc, section on what
+// quantization is) without the activation scheme. Implemented schemes:
+//   int8, one fp32 scale per token:   inv = f32(127/amax), q = rne(clamp(x*inv))
+//   fp8 E4M3 (OCP), one fp32 scale per token and 128-wide K group:
+//                                     inv = f32(448/amax), q = e4m3_rne(clamp(x*inv))
+// Scale = f32(amax/Q); amax = 0 gives scale 1 and zero codes. Every step is
+// binary32 with RNE and correctly rounded division, so the codes are
+// reproducible bit for bit by any implementation doing the same steps.
+#include "qdg_device.h"
+#include "qdg_internal.h"
+
+namespace qdg {
+namespace {
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
+
+// OCP E4M3 ("fn") encoding of a finite value with |v| <= 448, RNE; the sign
+// of zero is kept. Written from the format definition: bias 7, 3 mantissa
+// bits, exponent field 0 subnormal (units of 2^-9).
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t sign = __builtin_signbit(v) ? 0x80u : 0u;
+  const float a = fabsf(v);
+  const uint32_t u = __builtin_bit_cast(uint32_t, a);
+  const int e = (int)(u >> 23) - 127;
+  uint32_t code;
+  if (e < -6) {
+    code = (uint32_t)rintf(a * 512.0f);  // exact scaling; 8 becomes the min normal
+  } else {
+    const uint32_t mant = u & 0x7FFFFFu;
+    uint32_t m = mant >> 20;
+    const uint32_t rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
+    int ee = e;
+    if (m == 8) {
+      m = 0;
+      ++ee;
+    }
+    code = ((uint32_t)(ee + 7) << 3) | m;
+  }
+  return code | sign;
+}
+
+// int8 per token: one workgroup per row.
+__global__ __launch_bounds__(256) void act_int8_kernel(const uint16_t* __restrict__ a, int8_t* __restrict__ q,
+                                                       float* __restrict__ scales, int64_t K) {
+  const int64_t row = blockIdx.x;
+  const uint16_t* x = a + row * K;
+  float amax = 0.f;
+  for (int64_t k = threadIdx.x * 8; k < K; k += 256 * 8) {
+    const u32x4_t v = *(const u32x4_t*)(x + k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = fmaxf(amax, fabsf(bf16_to_f32(v[i] & 0xFFFFu)));
+      amax = fmaxf(amax, fabsf(bf16_to_f32(v[i] >> 16)));
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const bool nz = amax > 0.f;
+  const float inv = nz ? __fdiv_rn(127.0f, amax) : 0.f;
+  if (threadIdx.x == 0) scales[row] = nz ? __fdiv_rn(amax, 127.0f) : 1.0f;
+  int8_t* y = q + row * K;
+  for (int64_t k = threadIdx.x * 8; k < K; k += 256 * 8) {
+    const u32x4_t v = *(const u32x4_t*)(x + k);
+    u32x2_t out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f0 = fminf(fmaxf(rintf(bf16_to_f32(v[i] & 0xFFFFu) * inv), -127.f), 127.f);
+      const float f1 = fminf(fmaxf(rintf(bf16_to_f32(v[i] >> 16) * inv), -127.f), 127.f);
+      const uint32_t b = ((uint32_t)(int)f0 & 0xFFu) | (((uint32_t)(int)f1 & 0xFFu) << 8);
+      if (i & 1) out[i >> 1] |= b << 16;
+      else out[i >> 1] = b;
+    }
+    *(u32x2_t*)(y + k) = out;
+  }
+}
+
+// fp8 per (token, 128-group): 16 lanes per group, 8 values per lane.
+__global__ __launch_bounds__(256) void act_fp8_kernel(const uint16_t* __restrict__ a, uint8_t* __restrict__ q,
+                                                      float* __restrict__ scales, int64_t M, int64_t K) {
+  const int64_t gid = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // (row, group) index
+  const int sub = threadIdx.x & 15;
+  const int64_t groups = K / 128;
+  if (gid >= M * groups) return;  // whole 16-lane segments exit together
+  const int64_t row = gid / groups, g = gid % groups;
+  const uint16_t* x = a + row * K + g * 128 + sub * 8;
+  const u32x4_t v = *(const u32x4_t*)x;
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32(v[i] & 0xFFFFu);
+    f[2 * i + 1] = bf16_to_f32(v[i] >> 16);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  const bool nz = amax > 0.f;
+  const float inv = nz ? __fdiv_rn(448.0f, amax) : 0.f;
+  if (sub == 0) scales[row * groups + g] = nz ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  u32x2_t out = {0, 0};
+  if (nz) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float t = fminf(fmaxf(f[i] * inv, -448.f), 448.f);
+      out[i >> 2] |= e4m3_rne(t) << (8 * (i & 3));
+    }
+  }
+  *(u32x2_t*)(q + row * K + g * 128 + sub * 8) = out;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_act(int atype, const void* a, int64_t M, int64_t K, void* qa, float* scales,
+                               hipStream_t s) {
+  if (atype == QDG_A_INT8) {
+    hipLaunchKernelGGL(act_int8_kernel, dim3((unsigned)M), dim3(256), 0, s, (const uint16_t*)a, (int8_t*)qa,
+                       scales, K);
+  } else {
+    const int64_t threads = M * (K / 128) * 16;
+    hipLaunchKernelGGL(act_fp8_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       (const uint16_t*)a, (uint8_t*)qa, scales, M, K);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qdg

@@ -1,0 +1,452 @@
+// C ABI of libqdg.so: validation, plans (kernel-instance selection per M
+// range), workspace accounting and launches. See include/qdg.h.
+//
+// The split follows the pages: the standard format says what the stored
+// values mean, the Layer/Compute/Tuning configs and the per-device heuristics
+// decide how a given M is executed (kinachrichten, "Wie die Architektur
+// funktioniert"). Unsupported combinations are rejected with a message, and
+// qdg_plan_describe reports which instance serves which M ("vLLM Humming: why
+// shared quantization still needs specialized kernels", sections
+// "Specialization should leave a reproducible trail" and "The architectural
+// gain is a smaller maintenance surface").
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "qdg_internal.h"
+
+using namespace qdg;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qdg_status fail(qdg_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+qdg_status ok() { return QDG_OK; }
+
+qdg_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return QDG_OK;
+  return fail(QDG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(unsigned));
+constexpr int kTargetWorkgroups = 512;  // two 4-wave workgroups per CU (256 CUs)
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+namespace qdg {
+
+Format format_of(const qdg_layer_config& L) {
+  if (L.wtype == QDG_W_INT8) return FMT_W8A8;
+  if (L.wtype == QDG_W_MXFP4) return FMT_MXFP4;
+  if (L.atype == QDG_A_INT8) return FMT_W4A8;
+  return FMT_W4A16;
+}
+
+PackedGeom packed_geom(const qdg_layer_config& L, Format f) {
+  PackedGeom g;
+  g.n = L.n;
+  g.k = L.k;
+  g.n_pad = align_up(L.n, 16);
+  g.ntiles = g.n_pad / 16;
+  g.groups = L.k / 128;
+  g.experts = L.num_experts;
+  const int64_t units = g.ntiles * g.groups;
+  g.w_bytes = units * (f == FMT_W8A8 ? 2048 : 1024);  // bytes per 16x128 unit
+  switch (f) {
+    case FMT_W4A16: g.s_bytes = units * 16 * 8; break;  // {f32 s, bf16x2 -(128+z)}
+    case FMT_W4A8: g.s_bytes = units * 16 * 4; break;   // f32 s/16
+    case FMT_MXFP4: g.s_bytes = units * 64; break;      // E8M0 per lane
+    case FMT_W8A8: g.s_bytes = g.n_pad * 4; break;      // f32 per column
+  }
+  g.s_offset = align_up(g.w_bytes, 256);
+  g.expert_stride = align_up(g.s_offset + g.s_bytes, 256);
+  return g;
+}
+
+}  // namespace qdg
+
+struct qdg_plan {
+  qdg_layer_config layer;
+  qdg_compute_config compute;
+  qdg_tuning_config tuning;
+  bool has_tuning;
+  Format fmt;
+  PackedGeom geom;
+};
+
+namespace {
+
+const char* fmt_name(Format f, const qdg_layer_config& L) {
+  switch (f) {
+    case FMT_W4A16: return L.wtype == QDG_W_UINT4 ? "w4a16-uint4-asym" : "w4a16-int4-sym";
+    case FMT_W8A8: return "w8a8-int8";
+    case FMT_W4A8: return "w4a8-int8";
+    case FMT_MXFP4: return "w4a8-mxfp4-fp8";
+  }
+  return "?";
+}
+
+qdg_status validate_layer(const qdg_layer_config* L) {
+  if (!L) return fail(QDG_ERR_INVALID_ARG, "layer config is NULL");
+  if (L->n < 1 || L->k < 1 || L->num_experts < 1)
+    return fail(QDG_ERR_INVALID_ARG, "n, k and num_experts must be positive (n=%lld k=%lld E=%lld)",
+                (long long)L->n, (long long)L->k, (long long)L->num_experts);
+  if (L->arch != 950) return fail(QDG_ERR_UNSUPPORTED, "arch %d: only gfx950 (950) is built", L->arch);
+  if (L->k % 128 != 0)
+    return fail(QDG_ERR_UNSUPPORTED, "k=%lld is not a multiple of 128 (K is never padded)", (long long)L->k);
+  if (L->n > (int64_t)1 << 26 || L->k > (int64_t)1 << 24)
+    return fail(QDG_ERR_UNSUPPORTED, "n or k too large for the 32-bit tile indexing");
+  if (L->otype < QDG_O_BF16 || L->otype > QDG_O_I32) return fail(QDG_ERR_INVALID_ARG, "bad otype %d", L->otype);
+  switch (L->wtype) {
+    case QDG_W_INT4:
+    case QDG_W_UINT4: {
+      if (L->stype != QDG_S_F16) return fail(QDG_ERR_UNSUPPORTED, "4-bit integer weights need f16 group scales");
+      if (L->group_size != 128)
+        return fail(QDG_ERR_UNSUPPORTED, "group_size %d: only 128 is implemented", L->group_size);
+      const bool asym = L->wtype == QDG_W_UINT4;
+      if (L->has_zeros != (asym ? 1 : 0))
+        return fail(QDG_ERR_INVALID_ARG, "has_zeros must be %d for %s", asym ? 1 : 0, asym ? "UINT4" : "INT4");
+      if (L->atype == QDG_A_BF16) {
+        if (L->otype == QDG_O_I32) return fail(QDG_ERR_UNSUPPORTED, "W4A16 has no integer accumulator to return");
+        return ok();
+      }
+      if (L->atype == QDG_A_INT8) {
+        if (L->k > 65536) return fail(QDG_ERR_UNSUPPORTED, "int8 paths keep 16*|q*qa| sums in int32: k <= 65536");
+        if (asym) return fail(QDG_ERR_UNSUPPORTED, "W4A8 with asymmetric uint4 weights is not implemented");
+        if (L->act_group != 0) return fail(QDG_ERR_UNSUPPORTED, "W4A8 uses per-token activation scales (act_group 0)");
+        return ok();
+      }
+      return fail(QDG_ERR_UNSUPPORTED, "4-bit integer weights with activation type %d", L->atype);
+    }
+    case QDG_W_INT8:
+      if (L->stype != QDG_S_F32) return fail(QDG_ERR_UNSUPPORTED, "int8 weights need f32 per-channel scales");
+      if (L->group_size != 0) return fail(QDG_ERR_UNSUPPORTED, "int8 weights are per channel (group_size 0)");
+      if (L->has_zeros) return fail(QDG_ERR_UNSUPPORTED, "int8 weights are symmetric");
+      if (L->atype != QDG_A_INT8 || L->act_group != 0)
+        return fail(QDG_ERR_UNSUPPORTED, "int8 weights run with per-token int8 activations only");
+      if (L->k > 65536) return fail(QDG_ERR_UNSUPPORTED, "int8 paths keep |q*qa| sums in int32: k <= 65536");
+      return ok();
+    case QDG_W_MXFP4:
+      if (L->stype != QDG_S_E8M0 || L->group_size != 32)
+        return fail(QDG_ERR_UNSUPPORTED, "MXFP4 needs E8M0 scales over blocks of 32");
+      if (L->has_zeros) return fail(QDG_ERR_UNSUPPORTED, "MXFP4 has no zero points");
+      if (L->atype != QDG_A_FP8E4M3 || L->act_group != 128)
+        return fail(QDG_ERR_UNSUPPORTED, "MXFP4 weights run with fp8 E4M3 activations, 128-group scales");
+      if (L->otype == QDG_O_I32) return fail(QDG_ERR_UNSUPPORTED, "MXFP4 has no integer accumulator");
+      return ok();
+    default:
+      return fail(QDG_ERR_INVALID_ARG, "bad wtype %d", L->wtype);
+  }
+}
+
+struct Choice {
+  bool tile;
+  StreamCfg sc;
+  TileCfg tc;
+  int grid_m;
+  size_t partial_bytes;
+  size_t rowsum_bytes;
+};
+
+// Device heuristics per M range for gfx950 (256 CUs): small M streams the
+// weights with split-K to give every CU work; large M uses LDS-tiled MFMA.
+Choice choose(const qdg_plan& P, int64_t M) {
+  Choice ch{};
+  const PackedGeom& g = P.geom;
+  const qdg_tuning_config& T = P.tuning;
+  const bool moe = P.compute.kind == QDG_KIND_MOE;
+  int bm = P.has_tuning && T.block_m ? T.block_m : 0;
+  if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : 64;
+  if (P.compute.batch_invariant && bm > 64) bm = 64;
+  ch.tile = false;
+  ch.sc.mt = bm / 16;
+  ch.sc.kw = P.has_tuning && T.waves ? T.waves : 4;
+  int nt = P.has_tuning && T.block_n ? T.block_n / 16 : 0;
+  if (!nt) nt = (ch.sc.mt == 1 && g.ntiles < 128 && !P.compute.batch_invariant) ? 1 : 2;
+  ch.sc.nt = nt;
+  ch.grid_m = (int)((M + bm - 1) / bm);
+  const int64_t nblocks = (g.ntiles + nt - 1) / nt;
+  int split = P.has_tuning && T.split_k ? T.split_k : 0;
+  if (!split) {
+    const int64_t wgs = nblocks * (P.compute.batch_invariant ? 1 : ch.grid_m);
+    split = (int)(kTargetWorkgroups / (wgs > 0 ? wgs : 1));
+    if (split < 1) split = 1;
+    const int maxs = (int)(g.groups / ch.sc.kw);
+    if (split > maxs) split = maxs > 0 ? maxs : 1;
+  }
+  if (moe) split = 1;
+  if (nblocks * ch.grid_m > kMaxCounters) split = 1;
+  ch.sc.split = split;
+  ch.partial_bytes = split > 1 ? (size_t)nblocks * ch.grid_m * split * ch.sc.mt * nt * 4 * 64 * 4 : 0;
+  ch.rowsum_bytes = 0;
+  return ch;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qdg_version(void) { return "qdg 0.1.0 gfx950 layout 1"; }
+
+const char* qdg_last_error(void) { return g_last_error.c_str(); }
+
+qdg_status qdg_validate_layer(const qdg_layer_config* layer) { return validate_layer(layer); }
+
+qdg_status qdg_preprocess_query(const qdg_layer_config* layer, size_t* packed_bytes) {
+  qdg_status st = validate_layer(layer);
+  if (st != QDG_OK) return st;
+  if (!packed_bytes) return fail(QDG_ERR_INVALID_ARG, "packed_bytes is NULL");
+  const PackedGeom g = packed_geom(*layer, format_of(*layer));
+  *packed_bytes = (size_t)(g.expert_stride * g.experts);
+  return ok();
+}
+
+qdg_status qdg_preprocess(const qdg_layer_config* layer, const qdg_std_weights* w, void* packed,
+                          size_t packed_bytes, void* stream) {
+  qdg_status st = validate_layer(layer);
+  if (st != QDG_OK) return st;
+  if (!w || !w->qweight || !w->scales || !packed) return fail(QDG_ERR_INVALID_ARG, "NULL weight or packed pointer");
+  if (layer->wtype == QDG_W_UINT4 && !w->zeros) return fail(QDG_ERR_INVALID_ARG, "UINT4 weights need zero points");
+  const Format f = format_of(*layer);
+  const PackedGeom g = packed_geom(*layer, f);
+  if (packed_bytes < (size_t)(g.expert_stride * g.experts))
+    return fail(QDG_ERR_INVALID_ARG, "packed buffer has %zu bytes, needs %lld", packed_bytes,
+                (long long)(g.expert_stride * g.experts));
+  if (!aligned(packed, 256)) return fail(QDG_ERR_MISALIGNED, "packed buffer must be 256-byte aligned");
+  if (!aligned(w->qweight, 16)) return fail(QDG_ERR_MISALIGNED, "qweight must be 16-byte aligned");
+  if (!aligned(w->scales, 4)) return fail(QDG_ERR_MISALIGNED, "scales must be 4-byte aligned");
+  return hip_status(launch_preprocess(*layer, f, g, *w, packed, (hipStream_t)stream), "preprocess launch");
+}
+
+qdg_status qdg_quantize_weights(const qdg_layer_config* layer, const float* w, void* qweight, void* scales,
+                                void* zeros, void* stream) {
+  qdg_status st = validate_layer(layer);
+  if (st != QDG_OK) return st;
+  if (!w || !qweight || !scales) return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
+  if (layer->wtype == QDG_W_UINT4 && !zeros) return fail(QDG_ERR_INVALID_ARG, "UINT4 needs a zeros buffer");
+  return hip_status(launch_quantize_weights(*layer, w, qweight, scales, zeros, (hipStream_t)stream),
+                    "quantize_weights launch");
+}
+
+qdg_status qdg_quantize_act(const qdg_layer_config* layer, const void* a, int64_t M, void* qa, float* scales,
+                            void* stream) {
+  qdg_status st = validate_layer(layer);
+  if (st != QDG_OK) return st;
+  if (layer->atype != QDG_A_INT8 && layer->atype != QDG_A_FP8E4M3)
+    return fail(QDG_ERR_UNSUPPORTED, "this layer takes bf16 activations directly");
+  if (M < 0) return fail(QDG_ERR_INVALID_ARG, "M < 0");
+  if (M == 0) return ok();
+  if (M > 0x7FFFFFFF) return fail(QDG_ERR_UNSUPPORTED, "M too large");
+  if (!a || !qa || !scales) return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(a, 16) || !aligned(qa, 16) || !aligned(scales, 4))
+    return fail(QDG_ERR_MISALIGNED, "activations must be 16-byte aligned");
+  return hip_status(launch_quantize_act(layer->atype, a, M, layer->k, qa, scales, (hipStream_t)stream),
+                    "quantize_act launch");
+}
+
+qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_config* compute,
+                           const qdg_tuning_config* tuning, qdg_plan** out) {
+  qdg_status st = validate_layer(layer);
+  if (st != QDG_OK) return st;
+  if (!compute || !out) return fail(QDG_ERR_INVALID_ARG, "NULL compute config or output");
+  if (compute->kind != QDG_KIND_DENSE && compute->kind != QDG_KIND_MOE)
+    return fail(QDG_ERR_INVALID_ARG, "bad kind %d", compute->kind);
+  const Format f = format_of(*layer);
+  if (compute->kind == QDG_KIND_MOE) {
+    if (f != FMT_W4A16 || layer->wtype != QDG_W_INT4)
+      return fail(QDG_ERR_UNSUPPORTED, "grouped MoE is implemented for W4A16 int4 symmetric only");
+    if (compute->top_k < 1 || compute->top_k > 32) return fail(QDG_ERR_INVALID_ARG, "top_k must be in [1, 32]");
+  } else if (layer->num_experts != 1) {
+    return fail(QDG_ERR_INVALID_ARG, "a dense layer has num_experts = 1");
+  }
+  if (tuning) {
+    if (tuning->block_m && tuning->block_m != 16 && tuning->block_m != 32 && tuning->block_m != 64)
+      return fail(QDG_ERR_UNSUPPORTED, "block_m %d: implemented 16, 32, 64", tuning->block_m);
+    if (tuning->block_n && (tuning->block_n % 16 || tuning->block_n > 64))
+      return fail(QDG_ERR_UNSUPPORTED, "block_n %d: implemented 16, 32, 64", tuning->block_n);
+    if (tuning->block_k && tuning->block_k != 128) return fail(QDG_ERR_UNSUPPORTED, "block_k must be 128");
+    if (tuning->waves && tuning->waves != 4) return fail(QDG_ERR_UNSUPPORTED, "waves must be 4");
+    if (tuning->mfma && tuning->mfma != 16) return fail(QDG_ERR_UNSUPPORTED, "mfma must be 16 (16x16 tiles)");
+    if (tuning->split_k < 0) return fail(QDG_ERR_INVALID_ARG, "split_k < 0");
+    if (compute->kind == QDG_KIND_MOE && tuning->split_k > 1)
+      return fail(QDG_ERR_UNSUPPORTED, "grouped MoE does not split K");
+  }
+  qdg_plan* p = new (std::nothrow) qdg_plan;
+  if (!p) return fail(QDG_ERR_INVALID_ARG, "out of host memory");
+  p->layer = *layer;
+  p->compute = *compute;
+  p->has_tuning = tuning != nullptr;
+  if (tuning) p->tuning = *tuning;
+  else std::memset(&p->tuning, 0, sizeof p->tuning);
+  p->fmt = f;
+  p->geom = packed_geom(*layer, f);
+  if (tuning) {
+    const Choice c = choose(*p, 1);
+    if (!stream_cfg_supported(f, c.sc)) {
+      delete p;
+      return fail(QDG_ERR_UNSUPPORTED, "no kernel instance for block_m/block_n/waves of this tuning");
+    }
+  }
+  *out = p;
+  return ok();
+}
+
+void qdg_plan_destroy(qdg_plan* plan) { delete plan; }
+
+qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes) {
+  if (!plan || !bytes) return fail(QDG_ERR_INVALID_ARG, "NULL plan or output");
+  if (M < 0) return fail(QDG_ERR_INVALID_ARG, "M < 0");
+  const Choice c = choose(*plan, M > 0 ? M : 1);
+  *bytes = kCounterBytes + align_up((int64_t)c.partial_bytes, 256) + align_up((int64_t)c.rowsum_bytes, 256);
+  return ok();
+}
+
+int qdg_plan_describe(const qdg_plan* plan, int64_t M, char* buf, size_t len) {
+  if (!plan || M < 0) return -1;
+  const Choice c = choose(*plan, M > 0 ? M : 1);
+  const char* kind = plan->compute.kind == QDG_KIND_MOE ? "moe" : "dense";
+  return snprintf(buf, buf ? len : 0,
+                  "%s %s n=%lld k=%lld E=%lld M=%lld: family=stream block_m=%d block_n=%d split_k=%d "
+                  "waves=%d mfma=16x16 grid_m=%d batch_invariant=%d tuning=%s layout=%d arch=gfx950",
+                  fmt_name(plan->fmt, plan->layer), kind, (long long)plan->layer.n, (long long)plan->layer.k,
+                  (long long)plan->layer.num_experts, (long long)M, c.sc.mt * 16, c.sc.nt * 16, c.sc.split,
+                  c.sc.kw, c.grid_m, plan->compute.batch_invariant, plan->has_tuning ? "user" : "heuristic",
+                  QDG_LAYOUT_VERSION);
+}
+
+static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales, const void* packed, void* Y,
+                      int64_t M, void* workspace, size_t ws_bytes, hipStream_t stream, bool moe,
+                      const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,
+                      int64_t T, int32_t block_m, int32_t a_per_pair) {
+  const Choice c0 = choose(*plan, M);
+  Choice c = c0;
+  int64_t rows = M;
+  if (moe) {
+    rows = T * plan->compute.top_k;
+    c.sc.mt = block_m / 16;
+    c.sc.split = 1;
+    c.partial_bytes = 0;
+    int64_t cap = 0;
+    const int64_t E = plan->layer.num_experts;
+    cap = align_up(rows + E * (block_m - 1), block_m);
+    c.grid_m = (int)(cap / block_m);
+    if (!stream_cfg_supported(plan->fmt, c.sc)) return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
+  }
+  size_t need = 0;
+  qdg_plan_workspace(plan, M, &need);
+  if (!workspace || ws_bytes < need)
+    return fail(QDG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+  if (!aligned(workspace, 256)) return fail(QDG_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  GemmArgs a{};
+  a.A = A;
+  a.a_scales = a_scales;
+  a.packed = (const uint8_t*)packed;
+  a.Y = Y;
+  a.M = (int)M;
+  a.N = (int)plan->layer.n;
+  a.K = (int)plan->layer.k;
+  a.groups = (int)plan->geom.groups;
+  a.ntiles = (int)plan->geom.ntiles;
+  a.expert_stride = plan->geom.expert_stride;
+  a.s_offset = plan->geom.s_offset;
+  a.otype = plan->layer.otype;
+  a.split = c.sc.split;
+  a.counters = (unsigned*)workspace;
+  a.partial = (char*)workspace + kCounterBytes;
+  a.sorted_ids = sorted_ids;
+  a.block_expert = block_expert;
+  a.num_padded = num_padded;
+  a.top_k = plan->compute.top_k;
+  a.a_per_pair = a_per_pair;
+  a.num_pairs = (int)rows;
+  const bool asym = plan->layer.wtype == QDG_W_UINT4;
+  hipError_t e = launch_stream(plan->fmt, asym, moe, c.sc, a, c.grid_m, stream);
+  if (e == hipErrorInvalidValue) return fail(QDG_ERR_UNSUPPORTED, "no kernel instance for this tuning");
+  return hip_status(e, "gemm launch");
+}
+
+qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, const void* packed, void* Y,
+                    int64_t M, void* workspace, size_t ws_bytes, void* stream) {
+  if (!plan) return fail(QDG_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->compute.kind != QDG_KIND_DENSE) return fail(QDG_ERR_INVALID_ARG, "MoE plans run with qdg_moe_gemm");
+  if (M < 0) return fail(QDG_ERR_INVALID_ARG, "M < 0");
+  if (M == 0) return ok();
+  if (M > 0x7FFFFFFF / 2) return fail(QDG_ERR_UNSUPPORTED, "M too large");
+  if (!A || !packed || !Y) return fail(QDG_ERR_INVALID_ARG, "NULL A, packed or Y");
+  const bool need_scales = plan->fmt != FMT_W4A16 && plan->layer.otype != QDG_O_I32;
+  if (plan->fmt == FMT_MXFP4) {
+    if (!a_scales) return fail(QDG_ERR_INVALID_ARG, "MXFP4 needs activation scales");
+  } else if (need_scales && !a_scales) {
+    return fail(QDG_ERR_INVALID_ARG, "activation scales are NULL");
+  }
+  if (!aligned(A, 16)) return fail(QDG_ERR_MISALIGNED, "A must be 16-byte aligned");
+  if (!aligned(packed, 256)) return fail(QDG_ERR_MISALIGNED, "packed must be 256-byte aligned");
+  const size_t ybytes = plan->layer.otype == QDG_O_BF16 ? 2 : 4;
+  if (!aligned(Y, ybytes)) return fail(QDG_ERR_MISALIGNED, "Y must be aligned to its element size");
+  return run(plan, A, a_scales, packed, Y, M, workspace, ws_bytes, (hipStream_t)stream, false, nullptr, nullptr,
+             nullptr, 0, 0, 0);
+}
+
+qdg_status qdg_moe_align_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m, int64_t* capacity) {
+  if (!capacity) return fail(QDG_ERR_INVALID_ARG, "capacity is NULL");
+  if (T < 0 || top_k < 1 || top_k > 32 || E < 1) return fail(QDG_ERR_INVALID_ARG, "bad T, top_k or E");
+  if (E > 1024) return fail(QDG_ERR_UNSUPPORTED, "at most 1024 experts");
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128)
+    return fail(QDG_ERR_UNSUPPORTED, "block_m must be 16, 32, 64 or 128");
+  if (T * top_k > (1 << 20)) return fail(QDG_ERR_UNSUPPORTED, "T*top_k above 2^20");
+  *capacity = align_up(T * top_k + (int64_t)E * (block_m - 1), block_m);
+  return ok();
+}
+
+qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int32_t block_m,
+                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded, void* stream) {
+  int64_t cap = 0;
+  qdg_status st = qdg_moe_align_capacity(T, top_k, E, block_m, &cap);
+  if (st != QDG_OK) return st;
+  if (!sorted_ids || !block_expert || !num_padded) return fail(QDG_ERR_INVALID_ARG, "NULL output");
+  if (T > 0 && !topk_ids) return fail(QDG_ERR_INVALID_ARG, "topk_ids is NULL");
+  return hip_status(launch_moe_align(topk_ids, T, top_k, E, block_m, cap, sorted_ids, block_expert, num_padded,
+                                     (hipStream_t)stream),
+                    "moe_align launch");
+}
+
+qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scales, const void* packed,
+                        const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,
+                        int64_t T, int32_t block_m, int32_t a_per_pair, void* Y, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  if (!plan) return fail(QDG_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->compute.kind != QDG_KIND_MOE) return fail(QDG_ERR_INVALID_ARG, "not a MoE plan");
+  if (T < 0) return fail(QDG_ERR_INVALID_ARG, "T < 0");
+  if (T == 0) return ok();
+  if (block_m != 16 && block_m != 32 && block_m != 64)
+    return fail(QDG_ERR_UNSUPPORTED, "grouped GEMM block_m must be 16, 32 or 64");
+  if (T * plan->compute.top_k > (1 << 20)) return fail(QDG_ERR_UNSUPPORTED, "T*top_k above 2^20");
+  if (!A || !packed || !Y || !sorted_ids || !block_expert || !num_padded)
+    return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(A, 16)) return fail(QDG_ERR_MISALIGNED, "A must be 16-byte aligned");
+  if (!aligned(packed, 256)) return fail(QDG_ERR_MISALIGNED, "packed must be 256-byte aligned");
+  return run(plan, A, a_scales, packed, Y, T, workspace, ws_bytes, (hipStream_t)stream, true, sorted_ids,
+             block_expert, num_padded, T, block_m, a_per_pair ? 1 : 0);
+}
+
+}  // extern "C"

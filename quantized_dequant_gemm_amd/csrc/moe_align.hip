@@ -1,0 +1,111 @@
+// Expert sort for the grouped MoE GEMM: (token, slot) pairs ordered by
+// expert, ascending flat index within an expert, each expert padded to a
+// multiple of block_m. One workgroup of 16 wavefronts:
+//   1. each wave counts experts over its contiguous slice of the pair list
+//      (LDS atomics; order does not matter for counts);
+//   2. per expert: total, padded size, exclusive scan -> segment offsets, and
+//      the start of each wave's run inside the segment;
+//   3. each wave walks its slice 64 pairs at a time; lanes with the same
+//      expert are found with one ballot per expert-id bit, the rank among
+//      them is a popcount, so every pair lands at a unique, order-preserving
+//      position without any atomics (the result is deterministic).
+// The pages motivate MoE (each token activates a few experts while all are
+// stored; kinachrichten, "Warum quantisierte Kernel wichtig sind") and name
+// the grouped MoE path (jetabc, "跑得有多快"); the sort itself is a reading.
+#include "qdg_device.h"
+#include "qdg_internal.h"
+
+namespace qdg {
+namespace {
+
+constexpr int kWaves = 16;
+constexpr int kMaxE = 1024;
+
+__global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restrict__ ids, int total, int E,
+                                                         int bm, int capacity, int32_t* __restrict__ sorted_ids,
+                                                         int32_t* __restrict__ block_expert,
+                                                         int32_t* __restrict__ num_padded) {
+  __shared__ int cnt[kWaves][kMaxE];
+  __shared__ int off[kMaxE + 1];
+  __shared__ int scan_tmp[1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kWaves * kMaxE; i += 1024) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int slice = (total + kWaves - 1) / kWaves;
+  const int lo = min(total, wave * slice), hi = min(total, lo + slice);
+  for (int i = lo + lane; i < hi; i += 64) {
+    const int e = ids[i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[wave][e], 1);  // out-of-range ids are dropped
+  }
+  __syncthreads();
+
+  // per-expert totals and padded sizes; block-wide exclusive scan (E <= 1024)
+  int padded = 0, tot = 0;
+  if (tid < E) {
+    for (int w = 0; w < kWaves; ++w) tot += cnt[w][tid];
+    padded = (tot + bm - 1) / bm * bm;
+  }
+  scan_tmp[tid] = padded;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = tid >= d ? scan_tmp[tid - d] : 0;
+    __syncthreads();
+    scan_tmp[tid] += v;
+    __syncthreads();
+  }
+  const int excl = scan_tmp[tid] - padded;
+  if (tid < E) {
+    off[tid] = excl;
+    // start of each wave's run inside the expert's segment
+    int run = excl;
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = cnt[w][tid];
+      cnt[w][tid] = run;
+      run += c;
+    }
+    // padding slots of this expert hold the sentinel
+    for (int p = excl + tot; p < excl + padded; ++p) sorted_ids[p] = total;
+    for (int b = excl / bm; b < (excl + padded) / bm; ++b) block_expert[b] = tid;
+  }
+  if (tid == 1023) off[kMaxE] = scan_tmp[1023];
+  __syncthreads();
+  const int npad = off[kMaxE];
+  if (tid == 0) *num_padded = npad;
+  for (int p = npad + tid; p < capacity; p += 1024) sorted_ids[p] = total;
+  for (int b = npad / bm + tid; b < capacity / bm; b += 1024) block_expert[b] = -1;
+
+  // stable scatter, one wave per slice, 64 pairs per step
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + lane;
+    const int e = i < hi ? ids[i] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t ones = __ballot(bit);
+      same &= bit ? ones : ~ones;
+    }
+    if (valid) {
+      const int rank = __popcll(same & lt);
+      const int n = __popcll(same);
+      const int pos = cnt[wave][e] + rank;
+      sorted_ids[pos] = i;
+      if (rank == n - 1) cnt[wave][e] += n;  // one writer per expert
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int block_m,
+                            int64_t capacity, int32_t* sorted_ids, int32_t* block_expert,
+                            int32_t* num_padded, hipStream_t s) {
+  hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(1024), 0, s, topk_ids, (int)(T * top_k), E, block_m,
+                     (int)capacity, sorted_ids, block_expert, num_padded);
+  return hipGetLastError();
+}
+
+}  // namespace qdg

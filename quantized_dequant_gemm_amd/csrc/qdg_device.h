@@ -1,0 +1,104 @@
+// Device-side building blocks shared by the gfx950 kernels: vector types,
+// MFMA wrappers, unpackers and the packed-layout constants.
+//
+// The packed layout is organised in "units": 16 output columns x 128 K values
+// (one K-group of the group-128 formats). A unit is consumed by one wavefront
+// with one (or two) 16-byte loads per lane, so every unit read is a fully
+// coalesced 1 KiB (or 2 KiB) access. Lane l of a wave owns column l % 16 and
+// the K quarter c = l / 16 (32 consecutive K values) of the unit; the MFMA
+// operand of lane l is therefore built from A[row][32c .. 32c+31] and the
+// matching weights, which keeps the A loads contiguous as well.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qdg {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+constexpr int kUnitK = 128;      // K values per unit (= group size)
+constexpr int kUnitN = 16;       // columns per unit
+constexpr int kUnit4Bytes = 1024;  // 4-bit unit
+constexpr int kUnit8Bytes = 2048;  // int8 unit
+
+// ------------------------------------------------------------------ MFMA
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] B[32x16]. Lane l supplies
+// row (A) / column (B) l%16 and 8 K values; D lane l holds column l%16,
+// rows 4*(l/16) + i. The K order inside an operand is irrelevant to the
+// product as long as A and B use the same one, which the packers ensure.
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// v_mfma_i32_16x16x64_i8: 16 int8 per lane, exact int32 accumulation.
+__device__ __forceinline__ i32x4_t mfma_i8(u32x4_t a, u32x4_t b, i32x4_t c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
+                                               __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
+}
+
+// v_mfma_scale_f32_16x16x128_f8f6f4 with A = FP8 E4M3 (format 0) and
+// B = FP4 E2M1 (format 4); lane l supplies row (A) / column (B) l%16. Measured
+// operand layout: the FP4 operand of lane group c = l/16 holds K 32c..32c+31
+// in nibble order (4 dwords); the FP8 operand of lane group c holds K
+// 16c..16c+15 in bytes 0-15 and K 64+16c..64+16c+15 in bytes 16-31. The E8M0
+// scale of lane group c (byte 0 of sa / sb) applies to the K block
+// 32c..32c+31 of that lane's row / column.
+__device__ __forceinline__ f32x4_t mfma_fp8_fp4_scaled(i32x8_t a, i32x8_t b, f32x4_t c, int sa,
+                                                       int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
+}
+
+// ------------------------------------------------------------------ unpack
+// W4A16: one dword holds 8 biased nibbles u (u = q for uint4, q + 8 for
+// int4). Element 2i of the MFMA operand is nibble i, element 2i+1 is nibble
+// i+4. Each nibble becomes the bf16 number 128 + u (exponent of 128 with u
+// in the low mantissa bits: exact), so the MFMA sees weights offset by 128;
+// the offset and the zero point are removed through the row sums of A.
+__device__ __forceinline__ u32x4_t unpack_u4_bf16_offset128(uint32_t x) {
+  u32x4_t r;
+  r.x = (x & 0x000F000Fu) | 0x43004300u;
+  r.y = ((x >> 4) & 0x000F000Fu) | 0x43004300u;
+  r.z = ((x >> 8) & 0x000F000Fu) | 0x43004300u;
+  r.w = ((x >> 12) & 0x000F000Fu) | 0x43004300u;
+  return r;
+}
+
+// W4A8: two's-complement nibbles moved into the high half of a byte give the
+// int8 value 16*q exactly; the factor 16 is folded into the group scale.
+// Byte i of the low result is nibble 2i, byte i of the high result nibble 2i+1.
+__device__ __forceinline__ u32x2_t unpack_i4_i8x16(uint32_t x) {
+  u32x2_t r;
+  r.x = (x << 4) & 0xF0F0F0F0u;
+  r.y = x & 0xF0F0F0F0u;
+  return r;
+}
+
+// ------------------------------------------------------------------ misc
+// Bit reinterpretation through a by-value scalar. Applying __builtin_bit_cast
+// directly to an ext_vector element (v[i]) is miscompiled by this toolchain
+// (it reads element 0 for every i), so vector elements always go through
+// this function.
+template <class To, class From>
+__device__ __forceinline__ To bits_as(From v) {
+  static_assert(sizeof(To) == sizeof(From), "size mismatch");
+  return __builtin_bit_cast(To, v);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (u >> 16) | 0x40u;  // NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <typename T>
+__device__ __forceinline__ T ldg_nt(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+}  // namespace qdg

