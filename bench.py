@@ -1,0 +1,195 @@
+"""Benchmark of the fused dequantize-and-multiply GEMM on one MI355X.
+
+One step = the dense W4A16 layer (int4 symmetric weights, group 128, fp16
+scales, bf16 activations, bf16 output) at its two projection shapes
+(K=4096 -> N=14336 and K=14336 -> N=4096) for every M of the sweep
+{1, 16, 128, 1024, 8192}: ten GEMM launches on one stream, inputs resident in
+HBM. Small-M cases rotate over enough packed weight copies to defeat the
+256 MB last-level cache, so their weights really stream from HBM.
+
+Prints one JSON line. `value` is the step's algorithmic TFLOP/s; `roofline`
+describes the kernel that dominates the step's time, `roofline_m16` the
+HBM-bound M=16 case, `cases` every launch; `cpu_baseline` times the fp64 CPU
+oracle on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16/W4A8 GEMM TFLOP/s + %HBM roofline (M=16), %MFMA peak (M=4096)"
+SHAPES = [(4096, 14336), (14336, 4096)]  # (K, N): up and down projection
+M_SWEEP = [1, 16, 128, 1024, 8192]
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+CACHE_BYTES = 256 << 20
+
+
+def alg_bytes(m, n, k):
+    # packed int4 weights + fp16 group scales + bf16 A + bf16 Y, each once
+    return n * k // 2 + n * (k // 128) * 2 + m * k * 2 + m * n * 2
+
+
+def alg_flops(m, n, k):
+    return 2 * m * n * k
+
+
+def gpu_leg(args):
+    import torch
+    import quantized_dequant_gemm_amd as q
+    import synth
+
+    q.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    layers = {}
+    for (k, n) in SHAPES:
+        layer = q.layer_w4a16(n, k)
+        nbytes = q.qdg_preprocess_query(layer)
+        qw = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((n, k // 128), dtype=torch.int16, device=dev)
+        w = synth.device_normal_f32((n, k), 0.02, seed=synth.seed_for(1, synth.TID_W))
+        q.qdg_quantize_weights(layer, w.data_ptr(), qw.data_ptr(), sc.data_ptr(), None, sh)
+        del w
+        copies = max(2, -(-2 * CACHE_BYTES // nbytes))  # >= 2x the cache
+        bufs = []
+        for _ in range(copies):
+            b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            q.qdg_preprocess(layer, q.StdWeights(qw.data_ptr(), sc.data_ptr(), None), b.data_ptr(), nbytes, sh)
+            bufs.append(b)
+        layers[(k, n)] = (layer, q.qdg_plan_create(layer, q.dense()), bufs)
+
+    cases = []
+    for (k, n) in SHAPES:
+        layer, plan, bufs = layers[(k, n)]
+        for m in M_SWEEP:
+            a = synth.device_activations_bf16(m, k, seed=synth.seed_for(1, synth.TID_A, m))
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            wsb = q.qdg_plan_workspace(plan, m)
+            ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+            cases.append(dict(k=k, n=n, m=m, plan=plan, bufs=bufs, a=a, y=y, ws=ws, wsb=wsb,
+                              desc=q.qdg_plan_describe(plan, m), times=[]))
+    torch.cuda.synchronize()
+
+    it = [0]
+
+    def step(record):
+        for c in cases:
+            buf = c["bufs"][it[0] % len(c["bufs"])]
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            q.qdg_gemm(c["plan"], c["a"].data_ptr(), None, buf.data_ptr(), c["y"].data_ptr(), c["m"],
+                       c["ws"].data_ptr(), c["wsb"], sh)
+            if record:
+                e1.record(stream)
+                c["times"].append((e0, e1))
+        it[0] += 1
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    flops_step = 0
+    out_cases = []
+    for c in cases:
+        us = sum(e0.elapsed_time(e1) for e0, e1 in c["times"]) * 1e3 / len(c["times"])
+        fl = alg_flops(c["m"], c["n"], c["k"])
+        by = alg_bytes(c["m"], c["n"], c["k"])
+        flops_step += fl
+        out_cases.append(dict(M=c["m"], K=c["k"], N=c["n"], us=round(us, 3),
+                              tflops=round(fl / us / 1e6, 2), gbs=round(by / us / 1e3, 1),
+                              hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4),
+                              mfma_frac=round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4),
+                              instance=c["desc"].split(": ", 1)[1]))
+    dom = max(out_cases, key=lambda d: d["us"])
+    big = dom["M"] >= 128
+    if big:
+        roof = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(dom["tflops"] / PEAK_BF16_TFLOPS, 4), traffic=None,
+                    kernel=f"w4a16 M={dom['M']} K={dom['K']} N={dom['N']}",
+                    per_launch=alg_flops(dom["M"], dom["N"], dom["K"]))
+    else:
+        roof = dict(bound="hbm", achieved=dom["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(dom["gbs"] / PEAK_HBM_GBS, 4), traffic=None,
+                    kernel=f"w4a16 M={dom['M']} K={dom['K']} N={dom['N']}",
+                    per_launch=alg_bytes(dom["M"], dom["N"], dom["K"]))
+    m16 = [d for d in out_cases if d["M"] == 16]
+    roof16 = [dict(bound="hbm", achieved=d["gbs"], peak=PEAK_HBM_GBS, unit="GB/s", frac=d["hbm_frac"],
+                   kernel=f"w4a16 M=16 K={d['K']} N={d['N']}", us=d["us"]) for d in m16]
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    return dict(value=value, ms_per_step=ms_per_step, roofline=roof, roofline_m16=roof16, cases=out_cases)
+
+
+def cpu_leg():
+    """The fp64 oracle, untuned, on a bounded sample of the step: both
+    projection shapes over the whole M sweep (dequantize the layer, then the
+    GEMM), about 10-30 s of host work."""
+    import numpy as np
+    import synth
+    from oracle import quant, ref
+
+    cores = len(os.sched_getaffinity(0))
+    flops = 0
+    elapsed = 0.0
+    for (k, n) in SHAPES:
+        w = synth.weights_f32(n, k, workload_id=1)
+        qv, s = quant.quantize_int4_sym(w)
+        for m in M_SWEEP:
+            a = synth.activations_bf16_bits(m, k, workload_id=1, salt=m)
+            t0 = time.perf_counter()
+            w64 = ref.dequant_int4_sym(qv, s)
+            ref.gemm_w4a16(a, w64)
+            elapsed += time.perf_counter() - t0
+            flops += alg_flops(m, n, k)
+    return dict(value=round(flops / elapsed / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+                sample="fp64 dequantize + BLAS GEMM of the dense W4A16 layer, both shapes, M in {1,16,128,1024,8192} (the whole step, once)",
+                seconds=round(elapsed, 2), blas_threads=os.environ.get("OMP_NUM_THREADS", "default"))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(sharding is described, not built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    g = gpu_leg(args)
+    line = {
+        "metric": METRIC, "value": round(g["value"], 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(g["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; weights N(0,0.02) quantized on device, activations N(0,1))",
+        "config": {"workload": "dense W4A16 layer: int4 sym g128 fp16 scales, bf16 act/out; "
+                               "(K,N) in {(4096,14336),(14336,4096)}, M in {1,16,128,1024,8192}",
+                   "launches_per_step": len(g["cases"])},
+        "roofline": g["roofline"], "roofline_m16": g["roofline_m16"], "cases": g["cases"],
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_leg()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

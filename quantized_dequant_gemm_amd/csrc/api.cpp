@@ -176,8 +176,20 @@ Choice choose(const qdg_plan& P, int64_t M) {
   const qdg_tuning_config& T = P.tuning;
   const bool moe = P.compute.kind == QDG_KIND_MOE;
   int bm = P.has_tuning && T.block_m ? T.block_m : 0;
-  if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : 64;
+  if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : M <= 1024 ? 128 : 256;
   if (P.compute.batch_invariant && bm > 64) bm = 64;
+  if (bm >= 128 && P.fmt == FMT_W4A16 && !moe) {
+    // LDS-tiled family: BM x 128 tiles, row sums of A per group in the workspace
+    ch.tile = true;
+    ch.tc.bm = bm;
+    ch.tc.bn = 128;
+    ch.grid_m = (int)((M + bm - 1) / bm);
+    ch.sc = StreamCfg{bm / 16, 8, 4, 1};
+    ch.partial_bytes = 0;
+    ch.rowsum_bytes = (size_t)ch.grid_m * bm * g.groups * 4;
+    return ch;
+  }
+  if (bm > 64) bm = 64;  // other formats: the streaming family serves every M
   ch.tile = false;
   ch.sc.mt = bm / 16;
   ch.sc.kw = P.has_tuning && T.waves ? T.waves : 4;
@@ -280,10 +292,18 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
     return fail(QDG_ERR_INVALID_ARG, "a dense layer has num_experts = 1");
   }
   if (tuning) {
-    if (tuning->block_m && tuning->block_m != 16 && tuning->block_m != 32 && tuning->block_m != 64)
-      return fail(QDG_ERR_UNSUPPORTED, "block_m %d: implemented 16, 32, 64", tuning->block_m);
-    if (tuning->block_n && (tuning->block_n % 16 || tuning->block_n > 64))
+    const bool tile_ok = f == FMT_W4A16 && compute->kind == QDG_KIND_DENSE && !compute->batch_invariant;
+    if (tuning->block_m && tuning->block_m != 16 && tuning->block_m != 32 && tuning->block_m != 64 &&
+        !(tile_ok && (tuning->block_m == 128 || tuning->block_m == 256)))
+      return fail(QDG_ERR_UNSUPPORTED, "block_m %d: implemented 16, 32, 64 (128, 256: dense W4A16)",
+                  tuning->block_m);
+    if (tuning->block_m >= 128) {
+      if (tuning->block_n && tuning->block_n != 128)
+        return fail(QDG_ERR_UNSUPPORTED, "the tiled family uses block_n 128");
+      if (tuning->split_k > 1) return fail(QDG_ERR_UNSUPPORTED, "the tiled family does not split K");
+    } else if (tuning->block_n && (tuning->block_n % 16 || tuning->block_n > 64)) {
       return fail(QDG_ERR_UNSUPPORTED, "block_n %d: implemented 16, 32, 64", tuning->block_n);
+    }
     if (tuning->block_k && tuning->block_k != 128) return fail(QDG_ERR_UNSUPPORTED, "block_k must be 128");
     if (tuning->waves && tuning->waves != 4) return fail(QDG_ERR_UNSUPPORTED, "waves must be 4");
     if (tuning->mfma && tuning->mfma != 16) return fail(QDG_ERR_UNSUPPORTED, "mfma must be 16 (16x16 tiles)");
@@ -302,7 +322,7 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
   p->geom = packed_geom(*layer, f);
   if (tuning) {
     const Choice c = choose(*p, 1);
-    if (!stream_cfg_supported(f, c.sc)) {
+    if (c.tile ? !tile_cfg_supported(f, c.tc) : !stream_cfg_supported(f, c.sc)) {
       delete p;
       return fail(QDG_ERR_UNSUPPORTED, "no kernel instance for block_m/block_n/waves of this tuning");
     }
@@ -326,11 +346,12 @@ int qdg_plan_describe(const qdg_plan* plan, int64_t M, char* buf, size_t len) {
   const Choice c = choose(*plan, M > 0 ? M : 1);
   const char* kind = plan->compute.kind == QDG_KIND_MOE ? "moe" : "dense";
   return snprintf(buf, buf ? len : 0,
-                  "%s %s n=%lld k=%lld E=%lld M=%lld: family=stream block_m=%d block_n=%d split_k=%d "
-                  "waves=%d mfma=16x16 grid_m=%d batch_invariant=%d tuning=%s layout=%d arch=gfx950",
+                  "%s %s n=%lld k=%lld E=%lld M=%lld: family=%s block_m=%d block_n=%d split_k=%d "
+                  "waves=%d mfma=16x16x32 grid_m=%d batch_invariant=%d tuning=%s layout=%d arch=gfx950",
                   fmt_name(plan->fmt, plan->layer), kind, (long long)plan->layer.n, (long long)plan->layer.k,
-                  (long long)plan->layer.num_experts, (long long)M, c.sc.mt * 16, c.sc.nt * 16, c.sc.split,
-                  c.sc.kw, c.grid_m, plan->compute.batch_invariant, plan->has_tuning ? "user" : "heuristic",
+                  (long long)plan->layer.num_experts, (long long)M, c.tile ? "tile" : "stream",
+                  c.tile ? c.tc.bm : c.sc.mt * 16, c.tile ? c.tc.bn : c.sc.nt * 16, c.sc.split, c.sc.kw,
+                  c.grid_m, plan->compute.batch_invariant, plan->has_tuning ? "user" : "heuristic",
                   QDG_LAYOUT_VERSION);
 }
 
@@ -380,7 +401,17 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   a.a_per_pair = a_per_pair;
   a.num_pairs = (int)rows;
   const bool asym = plan->layer.wtype == QDG_W_UINT4;
-  hipError_t e = launch_stream(plan->fmt, asym, moe, c.sc, a, c.grid_m, stream);
+  hipError_t e;
+  if (c.tile) {
+    a.m_pad = c.grid_m * c.tc.bm;
+    float* rs = (float*)((char*)workspace + kCounterBytes + align_up((int64_t)c.partial_bytes, 256));
+    a.rowsum = rs;
+    e = launch_rowsum(A, nullptr, nullptr, 0, 0, (int)rows, (int)M, a.K, a.m_pad, rs, stream);
+    if (e != hipSuccess) return hip_status(e, "rowsum launch");
+    e = launch_tile(plan->fmt, asym, moe, c.tc, a, c.grid_m, stream);
+  } else {
+    e = launch_stream(plan->fmt, asym, moe, c.sc, a, c.grid_m, stream);
+  }
   if (e == hipErrorInvalidValue) return fail(QDG_ERR_UNSUPPORTED, "no kernel instance for this tuning");
   return hip_status(e, "gemm launch");
 }

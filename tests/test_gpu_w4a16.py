@@ -107,3 +107,31 @@ def test_m_zero_is_noop(qdg):
     layer = q.layer_w4a16(64, 128)
     plan = q.qdg_plan_create(layer, q.dense())
     q.qdg_gemm(plan, 0, None, 0, 0, 0, 0, 0, q.current_stream())  # enqueues nothing
+
+
+@pytest.mark.parametrize("k,n", [(4096, 14336), (14336, 4096)])
+@pytest.mark.parametrize("m", [128, 1024, 8192])
+def test_dense_large_m_sampled_rows(qdg, m, k, n):
+    # the dense layer at M in {128, 1024, 8192}, launched as the benchmark
+    # launches it; the oracle checks 48 sampled rows (every column)
+    qv, s, z, w64 = _layer_data(n, k, asym=False)
+    a = synth.activations_bf16_bits(m, k, workload_id=1, salt=m)
+    y = H.w4a16(a, qv, s, z)
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(m).integers(0, m, 46)]))
+    y64 = ref.gemm_w4a16(a[rows], w64)
+    err = metrics.rel_frob(H.to_f64(y[torch.from_numpy(rows).cuda()]), y64)
+    print(f"W4A16 M={m} K={k} N={n} sampled rows: rel_frob={err:.3e}")
+    assert err <= 2e-3
+    assert not torch.isnan(y.float()).any()  # every output written
+
+
+def test_tile_family_asym_and_ragged(qdg):
+    # uint4 with zero points through the tiled family, ragged M and N
+    for m, n, k in [(300, 200, 640), (129, 1040, 256)]:
+        qv, s, z, w64 = _layer_data(n, k, asym=True, salt=m)
+        a = synth.activations_bf16_bits(m, k, workload_id=0, salt=m)
+        y64 = ref.gemm_w4a16(a, w64)
+        y = H.w4a16(a, qv, s, z, otype=q.QDG_O_F32)
+        assert metrics.rel_frob(H.to_f64(y), y64) <= 5e-5
+        yb = H.w4a16(a, qv, s, z)
+        assert metrics.rel_frob(H.to_f64(yb), y64) <= 2e-3
