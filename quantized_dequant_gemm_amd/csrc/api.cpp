@@ -176,15 +176,15 @@ Choice choose(const qdg_plan& P, int64_t M) {
   const qdg_tuning_config& T = P.tuning;
   const bool moe = P.compute.kind == QDG_KIND_MOE;
   int bm = P.has_tuning && T.block_m ? T.block_m : 0;
-  if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : M <= 1024 ? 128 : 256;
+  if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : M <= 2048 ? 128 : 256;
   if (P.compute.batch_invariant && bm > 64) bm = 64;
   if (bm >= 128 && P.fmt == FMT_W4A16 && !moe) {
     // LDS-tiled family: BM x 128 tiles, row sums of A per group in the workspace
     ch.tile = true;
     ch.tc.bm = bm;
-    ch.tc.bn = 128;
+    ch.tc.bn = bm == 256 ? 128 : 256;
     ch.grid_m = (int)((M + bm - 1) / bm);
-    ch.sc = StreamCfg{bm / 16, 8, 4, 1};
+    ch.sc = StreamCfg{bm / 16, ch.tc.bn / 16, 8, 1};
     ch.partial_bytes = 0;
     ch.rowsum_bytes = (size_t)ch.grid_m * bm * g.groups * 4;
     return ch;
@@ -298,14 +298,15 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
       return fail(QDG_ERR_UNSUPPORTED, "block_m %d: implemented 16, 32, 64 (128, 256: dense W4A16)",
                   tuning->block_m);
     if (tuning->block_m >= 128) {
-      if (tuning->block_n && tuning->block_n != 128)
-        return fail(QDG_ERR_UNSUPPORTED, "the tiled family uses block_n 128");
+      if (tuning->block_n && tuning->block_n != (tuning->block_m == 256 ? 128 : 256))
+        return fail(QDG_ERR_UNSUPPORTED, "the tiled family pairs block_m 256 with block_n 128, 128 with 256");
       if (tuning->split_k > 1) return fail(QDG_ERR_UNSUPPORTED, "the tiled family does not split K");
     } else if (tuning->block_n && (tuning->block_n % 16 || tuning->block_n > 64)) {
       return fail(QDG_ERR_UNSUPPORTED, "block_n %d: implemented 16, 32, 64", tuning->block_n);
     }
     if (tuning->block_k && tuning->block_k != 128) return fail(QDG_ERR_UNSUPPORTED, "block_k must be 128");
-    if (tuning->waves && tuning->waves != 4) return fail(QDG_ERR_UNSUPPORTED, "waves must be 4");
+    if (tuning->waves && tuning->waves != 4 && tuning->waves != 8)
+      return fail(QDG_ERR_UNSUPPORTED, "waves must be 4 (streaming family) or 8 (tiled family)");
     if (tuning->mfma && tuning->mfma != 16) return fail(QDG_ERR_UNSUPPORTED, "mfma must be 16 (16x16 tiles)");
     if (tuning->split_k < 0) return fail(QDG_ERR_INVALID_ARG, "split_k < 0");
     if (compute->kind == QDG_KIND_MOE && tuning->split_k > 1)
@@ -400,13 +401,16 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   a.top_k = plan->compute.top_k;
   a.a_per_pair = a_per_pair;
   a.num_pairs = (int)rows;
+  a.unpack_mask = 0x000F000Fu;
+  a.unpack_exp = 0x43004300u;
   const bool asym = plan->layer.wtype == QDG_W_UINT4;
   hipError_t e;
   if (c.tile) {
     a.m_pad = c.grid_m * c.tc.bm;
     float* rs = (float*)((char*)workspace + kCounterBytes + align_up((int64_t)c.partial_bytes, 256));
     a.rowsum = rs;
-    e = launch_rowsum(A, nullptr, nullptr, 0, 0, (int)rows, (int)M, a.K, a.m_pad, rs, stream);
+    e = launch_rowsum(A, nullptr, nullptr, 0, 0, (int)rows, (int)M, a.K, a.m_pad, asym ? 1.0f : -136.0f, rs,
+                      stream);
     if (e != hipSuccess) return hip_status(e, "rowsum launch");
     e = launch_tile(plan->fmt, asym, moe, c.tc, a, c.grid_m, stream);
   } else {

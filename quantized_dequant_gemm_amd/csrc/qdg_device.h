@@ -69,6 +69,18 @@ __device__ __forceinline__ u32x4_t unpack_u4_bf16_offset128(uint32_t x) {
   return r;
 }
 
+// Same as above with the mask and exponent constants held in registers
+// (m = 0x000F000F, e = 0x43004300): each output dword is then one
+// v_and_or_b32 (plus a shift), since VOP3 forms cannot take literals.
+__device__ __forceinline__ u32x4_t unpack_u4_bf16_offset128(uint32_t x, uint32_t m, uint32_t e) {
+  u32x4_t r;
+  r.x = (x & m) | e;
+  r.y = ((x >> 4) & m) | e;
+  r.z = ((x >> 8) & m) | e;
+  r.w = ((x >> 12) & m) | e;
+  return r;
+}
+
 // W4A8: two's-complement nibbles moved into the high half of a byte give the
 // int8 value 16*q exactly; the factor 16 is folded into the group scale.
 // Byte i of the low result is nibble 2i, byte i of the high result nibble 2i+1.

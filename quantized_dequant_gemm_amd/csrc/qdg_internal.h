@@ -43,6 +43,9 @@ struct GemmArgs {
   // large-M W4A16: per (group, row) negated row sums of A
   const float* rowsum;
   int m_pad;
+  // unpack constants, passed at run time so the compiler keeps them in
+  // registers (0x000F000F and 0x43004300)
+  uint32_t unpack_mask, unpack_exp;
 };
 
 // A kernel instance of the streaming (small-M) family.
@@ -67,7 +70,7 @@ bool tile_cfg_supported(Format f, const TileCfg& c);
 
 hipError_t launch_rowsum(const void* a_bf16, const int* sorted_ids, const int* num_padded,
                          int top_k, int a_per_pair, int num_pairs, int M, int K, int m_pad,
-                         float* out, hipStream_t s);
+                         float factor, float* out, hipStream_t s);
 
 hipError_t launch_preprocess(const qdg_layer_config& L, Format f, const PackedGeom& g,
                              const qdg_std_weights& w, void* packed, hipStream_t s);

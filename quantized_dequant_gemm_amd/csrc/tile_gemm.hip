@@ -3,21 +3,24 @@
 // The pages' library switches to a different, throughput-oriented pipeline
 // for large batches (kinachrichten, "Wie die Architektur funktioniert"). Here
 // the large-M path is MFMA-bound, so it is organised around MFMA issue:
-//   * a 256-thread workgroup owns a BM x 128 output tile; its 4 wavefronts
-//     are arranged 2 x 2, each owning (BM/2) x 64;
-//   * the K loop advances one 128-wide group per iteration. The A tile of the
-//     next group is copied global -> LDS with direct 16-byte LDS loads (no
-//     register staging) into the other half of a double buffer; 16-byte
-//     chunks are XOR-swizzled by row so fragment reads are conflict-free;
-//   * weights need no LDS: the packed unit of a (16-column tile, group) is one
-//     coalesced 16-byte-per-lane load straight into the registers of the wave
-//     that uses it, prefetched a group ahead;
-//   * dequantization in registers as in the streaming family (bf16 128+u);
-//     the MFMA chain of each group starts from -(128+z) * rowsum(A) instead of
-//     zero, with the row sums computed once per call by rowsum_kernel, so the
-//     only per-group epilogue is acc += s * P;
+//   * a 512-thread workgroup owns a 256 x 128 or 128 x 256 output tile; its
+//     8 wavefronts (two per SIMD) each own a 64 x 64 tile, small enough that
+//     accumulators, A fragments and unpacked weights all stay in the 256
+//     VGPRs the vector ALU can address (no AGPR shuffling, no spills);
+//   * the K loop advances one 128-wide group per iteration. Everything the
+//     next group needs -- the A tile, the A row sums, the packed weight units
+//     and the scale records -- is copied global -> LDS with direct 16-byte
+//     LDS loads into the other half of a double buffer, so no registers are
+//     held for prefetch; A chunks are XOR-swizzled by row so fragment reads
+//     are bank-conflict-free;
+//   * dequantization in registers as in the streaming family (bf16 128+u,
+//     one v_and_or_b32 per dword); the four N-tile MFMA chains of a 16-row
+//     A tile are interleaved and each starts from -(128+z) * rowsum(A)
+//     instead of zero, with the row sums computed (and, when symmetric,
+//     pre-scaled by -136) once per call by rowsum_kernel, so the only
+//     per-group epilogue is acc += s * P;
 //   * the output tile is transposed through LDS so every global store writes
-//     whole 16-byte row segments.
+//     whole 16-byte row segments; the tile order is XCD-aware.
 #include <type_traits>
 
 #include "qdg_device.h"
@@ -28,11 +31,12 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Row sums of A per 128-wide K group: out[g * m_pad + r] = sum_k A[row(r)][128g + k]
-// where row(r) = r (dense; rows >= M give 0) or the gathered MoE row.
+// Row sums of A per 128-wide K group, times `factor`:
+// out[g * m_pad + r] = factor * sum_k A[row(r)][128g + k], row(r) = r (dense;
+// rows >= M give 0) or the gathered MoE row.
 __global__ void rowsum_kernel(const uint16_t* __restrict__ A, const int* __restrict__ sorted_ids,
                               const int* __restrict__ num_padded, int top_k, int a_per_pair, int num_pairs,
-                              int M, int K, int m_pad, float* __restrict__ out) {
+                              int M, int K, int m_pad, float factor, float* __restrict__ out) {
   const int groups = K / 128;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (tid >= (int64_t)m_pad * groups) return;
@@ -58,49 +62,132 @@ __global__ void rowsum_kernel(const uint16_t* __restrict__ A, const int* __restr
       }
     }
   }
-  out[tid] = s;
+  out[tid] = s * factor;
 }
 
-// Global -> LDS copy of one group's A tile (and its row sums). Kept out of
-// lambdas: a device-only builtin inside an (implicitly host+device) lambda
-// makes the host pass drop the kernel.
-template <int BM>
-__device__ __forceinline__ void load_a_tile(const char* const* a_src, const GemmArgs& p, char* a_lds,
-                                            char* rs_lds, int wave, int lane, int mb, int g, int stage) {
-  constexpr int A_STAGE = BM * 256;
-  constexpr int RS_STAGE = BM * 4;
+// Layout of one LDS stage (everything one K group needs):
+//   A      BM rows x 256 bytes, 16-byte chunks XOR-swizzled by row
+//   RS     BM floats (row sums, pre-scaled)
+//   W      BN/16 packed weight units of 1 KiB (tile-major)
+//   S      BN/16 x 16 scale records of 8 bytes
+template <int BM, int BN>
+struct Stage {
+  static constexpr int A = 0;
+  static constexpr int RS = BM * 256;
+  static constexpr int W = RS + BM * 4;
+  static constexpr int S = W + (BN / 16) * 1024;
+  static constexpr int BYTES = S + (BN / 16) * 128;
+};
+
+// Issue the global -> LDS copies of group g into `st` (direct 16-byte LDS
+// loads: lane l of a wave instruction writes bytes 16l..16l+15 of a 1 KiB
+// LDS span). Kept out of lambdas: a device-only builtin inside an
+// (implicitly host+device) lambda makes the host pass drop the kernel.
+template <int BM, int BN, int NW>
+__device__ __forceinline__ void load_stage(char* st, const char* a_base, const int* a_row, size_t a_row_bytes,
+                                           const GemmArgs& p, const uint8_t* wbase, const uint8_t* sbase,
+                                           int wg_tile0, int wave, int lane, int mb, int g) {
+  using L = Stage<BM, BN>;
+  // A: wave instruction i covers rows 4i..4i+3
 #pragma unroll
-  for (int r = 0; r < BM / 16; ++r) {
-    const int i = r * 4 + wave;
-    __builtin_amdgcn_global_load_lds(a_src[r] + (size_t)g * 256, (lds_void*)(a_lds + stage * A_STAGE + i * 1024),
-                                     16, 0, 0);
+  for (int r = 0; r < BM / 4 / NW; ++r) {
+    const int i = r * NW + wave;
+    __builtin_amdgcn_global_load_lds(a_base + (size_t)a_row[r] * a_row_bytes + (size_t)g * 256,
+                                     (lds_void*)(st + L::A + i * 1024), 16, 0, 0);
   }
-  // row sums of this group: BM floats, 16 bytes per lane of wave 0
+  // weights: one 1 KiB unit per instruction (tiles past the layer re-read
+  // the last tile; their results are never stored)
+#pragma unroll
+  for (int r = 0; r < (BN / 16 + NW - 1) / NW; ++r) {
+    const int t = r * NW + wave;
+    if (t < BN / 16) {
+      const int tile = min(wg_tile0 + t, p.ntiles - 1);
+      __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * kUnit4Bytes + lane * 16,
+                                       (lds_void*)(st + L::W + t * 1024), 16, 0, 0);
+    }
+  }
+  // scale records: 128 bytes per tile, 8 tiles per instruction
+  if (wave == NW - 1) {
+#pragma unroll
+    for (int r = 0; r < BN / 128; ++r) {
+      const int t = r * 8 + (lane >> 3);
+      const int tile = min(wg_tile0 + t, p.ntiles - 1);
+      __builtin_amdgcn_global_load_lds(sbase + ((size_t)tile * p.groups + g) * 128 + (lane & 7) * 16,
+                                       (lds_void*)(st + L::S + r * 1024), 16, 0, 0);
+    }
+  }
+  // row sums: BM floats
   if (wave == 0 && lane < BM / 4) {
     const float* rs = p.rowsum + (size_t)g * p.m_pad + mb * BM + lane * 4;
-    __builtin_amdgcn_global_load_lds(rs, (lds_void*)(rs_lds + stage * RS_STAGE), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(rs, (lds_void*)(st + L::RS), 16, 0, 0);
   }
 }
 
-template <bool ASYM, int BM, bool MOE>
-__global__ __launch_bounds__(256) void tile_gemm_kernel(const GemmArgs p, int m_blocks, int n_blocks) {
-  constexpr int BN = 128;
-  constexpr int WM = BM / 2;          // rows per wave
-  constexpr int MTW = WM / 16;        // 16-row tiles per wave
-  constexpr int A_STAGE = BM * 256;   // bytes of one A group tile (BM rows x 128 bf16)
-  constexpr int RS_STAGE = BM * 4;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* a_lds = smem;                         // [2][A_STAGE]
-  char* rs_lds = smem + 2 * A_STAGE;          // [2][RS_STAGE]
+// One K group for a 64 x 64 wave tile: unpack the wave's 4 weight tiles once,
+// then for each 16-row A tile run the four N-tile MFMA chains interleaved
+// (each chain seeded with -(128+z) * rowsum) and fold them into the
+// accumulators with the group scales. N tiles past the end of the layer hold
+// duplicate data: computed like the others and never stored.
+template <bool ASYM, int BM, int BN>
+__device__ __forceinline__ void tile_group(const char* st, int wm, int wn, int lane, uint32_t um, uint32_t ue,
+                                           f32x4_t (&acc)[4][4]) {
+  using L = Stage<BM, BN>;
+  const int c = lane >> 4, col = lane & 15;
+  u32x4_t bw[4][4];
+  float sc[4], negz[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int tt = wn * 4 + t;
+    const u32x4_t b = *(const u32x4_t*)(st + L::W + tt * 1024 + lane * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bw[t][j] = unpack_u4_bf16_offset128(b[j], um, ue);
+    const u32x2_t rec = *(const u32x2_t*)(st + L::S + tt * 128 + col * 8);
+    sc[t] = bits_as<float>(rec.x);
+    negz[t] = __builtin_bit_cast(float, (rec.y & 0xFFFFu) << 16);  // -(128+z)
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int row = wm * 64 + mt * 16 + col;
+    u32x4_t a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a[j] = *(const u32x4_t*)(st + L::A + row * 256 + (((4 * c + j) ^ (row & 15)) * 16));
+    const f32x4_t rs = *(const f32x4_t*)(st + L::RS + (wm * 64 + mt * 16 + 4 * c) * 4);
+    f32x4_t pacc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (ASYM)
+        pacc[t] = f32x4_t{negz[t] * rs[0], negz[t] * rs[1], negz[t] * rs[2], negz[t] * rs[3]};
+      else
+        pacc[t] = rs;  // row sums pre-scaled by -136
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) pacc[t] = mfma_bf16(a[j], bw[t][j], pacc[t]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][t][i] = __builtin_fmaf(sc[t], pacc[t][i], acc[mt][t][i]);
+  }
+}
+
+template <bool ASYM, int WAVES_M, int WAVES_N, bool MOE>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const GemmArgs p, int m_blocks,
+                                                                           int n_blocks) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int BM = 64 * WAVES_M, BN = 64 * WAVES_N;
+  using L = Stage<BM, BN>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // [2][L::BYTES]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int c = lane >> 4, col = lane & 15;
 
   // XCD-aware tile order: consecutive workgroup ids land on different XCDs,
-  // so give each XCD a contiguous range of tiles (row-major over N blocks),
-  // keeping the A rows of the tiles resident on one XCD together in its L2.
+  // so each XCD gets a contiguous range of tiles (row-major over N blocks)
+  // and the A rows its CUs share stay in that XCD's L2.
   const int total = m_blocks * n_blocks;
   int lin = blockIdx.x;
   if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
@@ -115,14 +202,13 @@ __global__ __launch_bounds__(256) void tile_gemm_kernel(const GemmArgs p, int m_
   const uint8_t* sbase = wbase + p.s_offset;
   const int groups = p.groups;
 
-  // ---- A tile loader: wave instruction i covers LDS rows 4i..4i+3
-  const size_t a_row_bytes = (size_t)p.K * 2;
-  const char* a_src[BM / 16];  // per instruction handled by this wave
+  // A rows this lane copies (one per wave instruction); the 16-byte chunk it
+  // fetches is the same for all of them (row % 16 does not depend on r)
+  int a_row[BM / 4 / NW];
+  const int a_chunk = (lane & 15) ^ ((4 * wave + (lane >> 4)) & 15);
 #pragma unroll
-  for (int r = 0; r < BM / 16; ++r) {
-    const int i = r * 4 + wave;
-    const int row = 4 * i + (lane >> 4);
-    const int chunk = (lane & 15) ^ (row & 15);
+  for (int r = 0; r < BM / 4 / NW; ++r) {
+    const int row = 4 * (r * NW + wave) + (lane >> 4);
     const int grow = mb * BM + row;
     int src;
     if constexpr (MOE) {
@@ -131,105 +217,45 @@ __global__ __launch_bounds__(256) void tile_gemm_kernel(const GemmArgs p, int m_
     } else {
       src = grow < p.M ? grow : p.M - 1;
     }
-    a_src[r] = (const char*)p.A + (size_t)src * a_row_bytes + chunk * 16;
+    a_row[r] = src;
   }
+  const char* a_base = (const char*)p.A + a_chunk * 16;
+  const size_t a_row_bytes = (size_t)p.K * 2;
+  const int wg_tile0 = nb * (BN / 16);
 
-  // ---- weights: the 4 N tiles of this wave
-  const int tile0 = nb * (BN / 16) + wn * 4;
-  int ntv = p.ntiles - tile0;  // valid tiles of this wave (wave-uniform)
-  ntv = ntv < 0 ? 0 : (ntv > 4 ? 4 : ntv);
-  u32x4_t bcur[4], bnxt[4];
-  float scur[4], snxt[4];
-  uint32_t ocur[4], onxt[4];
-  auto load_b = [&](int g, u32x4_t(&b)[4], float(&s)[4], uint32_t(&o)[4]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < ntv) {
-        const size_t u = (size_t)(tile0 + t) * groups + g;
-        b[t] = ldg_nt((const u32x4_t*)(wbase + u * kUnit4Bytes) + lane);
-        const u32x2_t rec = *((const u32x2_t*)sbase + u * 16 + col);
-        s[t] = bits_as<float>(rec.x);
-        o[t] = rec.y;
-      } else {
-        b[t] = u32x4_t{0, 0, 0, 0};
-        s[t] = 0.f;
-        o[t] = 0;
-      }
-    }
-  };
+  // one unpack constant in a VGPR, the other in an SGPR: lets each unpacked
+  // dword be a single v_and_or_b32 (VOP3 reads at most one scalar operand)
+  uint32_t um;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(um) : "s"(p.unpack_mask));
+  const uint32_t ue = p.unpack_exp;
 
-  f32x4_t acc[MTW][4];
+  f32x4_t acc[4][4];
 #pragma unroll
-  for (int mt = 0; mt < MTW; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load_a_tile<BM>(a_src, p, a_lds, rs_lds, wave, lane, mb, 0, 0);
-  load_b(0, bcur, scur, ocur);
+  load_stage<BM, BN, NW>(smem, a_base, a_row, a_row_bytes, p, wbase, sbase, wg_tile0, wave, lane, mb, 0);
   for (int g = 0; g < groups; ++g) {
-    const int stage = g & 1;
-    // all loads of group g are complete and visible to every wave
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (g + 1 < groups) {
-      load_a_tile<BM>(a_src, p, a_lds, rs_lds, wave, lane, mb, g + 1, stage ^ 1);
-      load_b(g + 1, bnxt, snxt, onxt);
-    }
-    // A fragments of this wave for the whole group, and the row sums
-    u32x4_t a[MTW][4];
-    f32x4_t rsv[MTW];
-    const char* abase = a_lds + stage * A_STAGE;
-#pragma unroll
-    for (int mt = 0; mt < MTW; ++mt) {
-      const int row = wm * WM + mt * 16 + col;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ch = (4 * c + j) ^ (row & 15);
-        a[mt][j] = *(const u32x4_t*)(abase + row * 256 + ch * 16);
-      }
-      rsv[mt] = *(const f32x4_t*)(rs_lds + stage * RS_STAGE + (wm * WM + mt * 16 + 4 * c) * 4);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t >= ntv) continue;  // wave-uniform
-      u32x4_t bw[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bw[j] = unpack_u4_bf16_offset128(bcur[t][j]);
-      // -(128 + z) for this column: bf16 bits in both halves of o
-      const float negz = __builtin_bit_cast(float, (ocur[t] & 0xFFFFu) << 16);
-#pragma unroll
-      for (int mt = 0; mt < MTW; ++mt) {
-        f32x4_t pacc;
-        if constexpr (ASYM) {
-          pacc = f32x4_t{negz * rsv[mt][0], negz * rsv[mt][1], negz * rsv[mt][2], negz * rsv[mt][3]};
-        } else {
-          pacc = f32x4_t{-136.f * rsv[mt][0], -136.f * rsv[mt][1], -136.f * rsv[mt][2], -136.f * rsv[mt][3]};
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pacc = mfma_bf16(a[mt][j], bw[j], pacc);
-        const float s = scur[t];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][t][i] = __builtin_fmaf(s, pacc[i], acc[mt][t][i]);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      bcur[t] = bnxt[t];
-      scur[t] = snxt[t];
-      ocur[t] = onxt[t];
-    }
+    char* cur = smem + (g & 1) * L::BYTES;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of group g landed
+    __syncthreads();                // ... and every other wave's; the other stage is free
+    if (g + 1 < groups)
+      load_stage<BM, BN, NW>(smem + ((g + 1) & 1) * L::BYTES, a_base, a_row, a_row_bytes, p, wbase, sbase,
+                             wg_tile0, wave, lane, mb, g + 1);
+    tile_group<ASYM, BM, BN>(cur, wm, wn, lane, um, ue, acc);
   }
 
   // ---- epilogue: per wave, transpose each 16 x 64 strip through LDS so that
   // every lane stores whole 16-byte row segments
-  __syncthreads();  // everyone is done with the A stages
+  __syncthreads();  // everyone is done with the stages
   const bool f32out = p.otype == QDG_O_F32;
   char* strip = smem + wave * (16 * 64 * 4);
-  const int nbase = tile0 * 16;
-  const int esz = f32out ? 4 : 2;            // bytes per output element
-  const int cpr = 64 * esz / 16;             // 16-byte chunks per strip row
+  const int nbase = (wg_tile0 + wn * 4) * 16;
+  const int esz = f32out ? 4 : 2;  // bytes per output element
+  const int cpr = 64 * esz / 16;   // 16-byte chunks per strip row
 #pragma unroll
-  for (int mt = 0; mt < MTW; ++mt) {
+  for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -244,7 +270,7 @@ __global__ __launch_bounds__(256) void tile_gemm_kernel(const GemmArgs p, int m_
     __builtin_amdgcn_wave_barrier();
     for (int chunk = lane; chunk < 16 * cpr; chunk += 64) {
       const int r = chunk / cpr, cc = chunk % cpr;
-      const int lrow = mb * BM + wm * WM + mt * 16 + r;
+      const int lrow = mb * BM + wm * 64 + mt * 16 + r;
       int yrow = lrow;
       bool v;
       if constexpr (MOE) {
@@ -273,49 +299,51 @@ __global__ __launch_bounds__(256) void tile_gemm_kernel(const GemmArgs p, int m_
   }
 }
 
-template <bool ASYM, int BM, bool MOE>
-hipError_t launch_tile_bm(const GemmArgs& a, int m_blocks, hipStream_t s) {
-  const int n_blocks = (a.ntiles + 7) / 8;
-  const size_t smem = 2 * (BM * 256) + 2 * (BM * 4);
+template <bool ASYM, int WAVES_M, int WAVES_N, bool MOE>
+hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, hipStream_t s) {
+  constexpr int BM = 64 * WAVES_M, BN = 64 * WAVES_N;
+  const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
+  const size_t smem = 2 * Stage<BM, BN>::BYTES;
   static bool attr_set = false;  // idempotent; a race only repeats the call
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm_kernel<ASYM, BM, MOE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, MOE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, BM, MOE>), dim3(m_blocks * n_blocks), dim3(256), smem, s, a,
-                     m_blocks, n_blocks);
+  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, MOE>), dim3(m_blocks * n_blocks),
+                     dim3(64 * WAVES_M * WAVES_N), smem, s, a, m_blocks, n_blocks);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool tile_cfg_supported(Format f, const TileCfg& c) {
-  return f == FMT_W4A16 && (c.bm == 128 || c.bm == 256) && c.bn == 128;
+  return f == FMT_W4A16 && ((c.bm == 256 && c.bn == 128) || (c.bm == 128 && c.bn == 256));
 }
 
 hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const GemmArgs& a, int m_blocks,
                        hipStream_t s) {
   if (!tile_cfg_supported(f, c)) return hipErrorInvalidValue;
-#define QDG_T(ASYM_, BM_, MOE_) \
-  if (asym == ASYM_ && c.bm == BM_ && moe == MOE_) return launch_tile_bm<ASYM_, BM_, MOE_>(a, m_blocks, s);
-  QDG_T(false, 256, false)
-  QDG_T(false, 128, false)
-  QDG_T(true, 256, false)
-  QDG_T(true, 128, false)
-  QDG_T(false, 256, true)
-  QDG_T(false, 128, true)
+#define QDG_T(ASYM_, WM_, WN_, MOE_) \
+  if (asym == ASYM_ && c.bm == 64 * WM_ && moe == MOE_) return launch_tile_cfg<ASYM_, WM_, WN_, MOE_>(a, m_blocks, s);
+  QDG_T(false, 4, 2, false)
+  QDG_T(false, 2, 4, false)
+  QDG_T(true, 4, 2, false)
+  QDG_T(true, 2, 4, false)
+  QDG_T(false, 4, 2, true)
+  QDG_T(false, 2, 4, true)
 #undef QDG_T
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_rowsum(const void* a_bf16, const int* sorted_ids, const int* num_padded, int top_k,
-                         int a_per_pair, int num_pairs, int M, int K, int m_pad, float* out, hipStream_t s) {
+                         int a_per_pair, int num_pairs, int M, int K, int m_pad, float factor, float* out,
+                         hipStream_t s) {
   const int64_t threads = (int64_t)m_pad * (K / 128);
   hipLaunchKernelGGL(rowsum_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                      (const uint16_t*)a_bf16, sorted_ids, num_padded, top_k, a_per_pair, num_pairs, M, K, m_pad,
-                     out);
+                     factor, out);
   return hipGetLastError();
 }
 
