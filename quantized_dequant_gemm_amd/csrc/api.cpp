@@ -176,16 +176,30 @@ Choice choose(const qdg_plan& P, int64_t M) {
   const qdg_tuning_config& T = P.tuning;
   const bool moe = P.compute.kind == QDG_KIND_MOE;
   int bm = P.has_tuning && T.block_m ? T.block_m : 0;
-  if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : M <= 2048 ? 128 : 256;
+  if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
   if (P.compute.batch_invariant && bm > 64) bm = 64;
-  if (bm >= 128 && P.fmt == FMT_W4A16 && !moe) {
+  // the tiled family addresses A with 32-bit byte offsets
+  const bool a_fits = (double)(M > 0 ? M : 1) * (double)g.k * 2.0 < 4294967296.0;
+  if (bm >= 128 && P.fmt == FMT_W4A16 && !moe && a_fits) {
     // LDS-tiled family: BM x 128 tiles, row sums of A per group in the workspace
     ch.tile = true;
     ch.tc.bm = bm;
     ch.tc.bn = bm == 256 ? 128 : 256;
+    ch.tc.waves = P.has_tuning && T.waves ? T.waves : 8;
     ch.grid_m = (int)((M + bm - 1) / bm);
-    ch.sc = StreamCfg{bm / 16, ch.tc.bn / 16, 8, 1};
-    ch.partial_bytes = 0;
+    const int64_t n_blocks = (g.ntiles + ch.tc.bn / 16 - 1) / (ch.tc.bn / 16);
+    const int64_t tiles = n_blocks * ch.grid_m;
+    // split K when the tiles alone leave CUs idle (fixed order: deterministic,
+    // and independent of M only through the tile count)
+    int split = P.has_tuning && T.split_k ? T.split_k : 0;
+    if (!split) {
+      split = tiles >= 256 ? 1 : (int)((300 + tiles - 1) / tiles);
+      const int maxs = (int)(g.groups / 2);
+      if (split > maxs) split = maxs > 0 ? maxs : 1;
+      if (split > 16) split = 16;
+    }
+    ch.sc = StreamCfg{bm / 16, ch.tc.bn / 16, ch.tc.waves, split};
+    ch.partial_bytes = split > 1 ? (size_t)tiles * split * ch.tc.bm * ch.tc.bn * 4 : 0;
     ch.rowsum_bytes = (size_t)ch.grid_m * bm * g.groups * 4;
     return ch;
   }
@@ -300,7 +314,7 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
     if (tuning->block_m >= 128) {
       if (tuning->block_n && tuning->block_n != (tuning->block_m == 256 ? 128 : 256))
         return fail(QDG_ERR_UNSUPPORTED, "the tiled family pairs block_m 256 with block_n 128, 128 with 256");
-      if (tuning->split_k > 1) return fail(QDG_ERR_UNSUPPORTED, "the tiled family does not split K");
+
     } else if (tuning->block_n && (tuning->block_n % 16 || tuning->block_n > 64)) {
       return fail(QDG_ERR_UNSUPPORTED, "block_n %d: implemented 16, 32, 64", tuning->block_n);
     }
@@ -413,6 +427,10 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
                       stream);
     if (e != hipSuccess) return hip_status(e, "rowsum launch");
     e = launch_tile(plan->fmt, asym, moe, c.tc, a, c.grid_m, stream);
+    if (e == hipSuccess && a.split > 1) {
+      const int n_pad = (int)((plan->geom.ntiles + c.tc.bn / 16 - 1) / (c.tc.bn / 16) * c.tc.bn);
+      e = launch_reduce_splits(a, a.m_pad, n_pad, stream);
+    }
   } else {
     e = launch_stream(plan->fmt, asym, moe, c.sc, a, c.grid_m, stream);
   }

@@ -58,13 +58,14 @@ struct StreamCfg {
 
 // A kernel instance of the LDS-tiled (large-M) family.
 struct TileCfg {
-  int bm, bn;
+  int bm, bn, waves;
 };
 
 hipError_t launch_stream(Format f, bool asym, bool moe, const StreamCfg& c, const GemmArgs& a,
                          int grid_m_blocks, hipStream_t s);
 hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const GemmArgs& a,
                        int grid_m_blocks, hipStream_t s);
+hipError_t launch_reduce_splits(const GemmArgs& a, int m_pad, int n_pad, hipStream_t s);
 bool stream_cfg_supported(Format f, const StreamCfg& c);
 bool tile_cfg_supported(Format f, const TileCfg& c);
 

@@ -65,15 +65,43 @@ __global__ void rowsum_kernel(const uint16_t* __restrict__ A, const int* __restr
   out[tid] = s * factor;
 }
 
+// Sum of the split-K partials in split order (deterministic), converted to
+// the output type. partial is [nsplit][m_pad][n_pad] fp32.
+__global__ void reduce_splits_kernel(const float* __restrict__ partial, void* __restrict__ Y, int M, int N,
+                                     int m_pad, int n_pad, int nsplit, int otype) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 4-column chunk
+  const int cpr = n_pad / 4;
+  if (q >= (int64_t)M * cpr) return;
+  const int row = (int)(q / cpr), c4 = (int)(q % cpr) * 4;
+  if (c4 >= N) return;
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const f32x4_t v = *(const f32x4_t*)(partial + ((size_t)sp * m_pad + row) * n_pad + c4);
+    s = f32x4_t{s[0] + v[0], s[1] + v[1], s[2] + v[2], s[3] + v[3]};
+  }
+  for (int e = 0; e < 4 && c4 + e < N; ++e) {
+    const size_t o = (size_t)row * N + c4 + e;
+    if (otype == QDG_O_F32)
+      ((float*)Y)[o] = s[e];
+    else
+      ((uint16_t*)Y)[o] = (uint16_t)f32_to_bf16_rne(s[e]);
+  }
+}
+
 // Layout of one LDS stage (everything one K group needs):
-//   A      BM rows x 256 bytes, 16-byte chunks XOR-swizzled by row
+//   A      BM rows of 272 bytes (128 bf16 + 16 bytes of padding: rows start
+//          16 bytes apart modulo 128, so the 8 lanes served together by a
+//          16-byte LDS read always hit distinct banks, and every fragment
+//          address is one per-lane base plus an immediate offset)
 //   RS     BM floats (row sums, pre-scaled)
 //   W      BN/16 packed weight units of 1 KiB (tile-major)
 //   S      BN/16 x 16 scale records of 8 bytes
 template <int BM, int BN>
 struct Stage {
+  static constexpr int ROW = 272;
   static constexpr int A = 0;
-  static constexpr int RS = BM * 256;
+  static constexpr int A_SLOTS = BM * ROW / 16;  // 16-byte slots, 17 per row
+  static constexpr int RS = BM * ROW;
   static constexpr int W = RS + BM * 4;
   static constexpr int S = W + (BN / 16) * 1024;
   static constexpr int BYTES = S + (BN / 16) * 128;
@@ -81,44 +109,41 @@ struct Stage {
 
 // Issue the global -> LDS copies of group g into `st` (direct 16-byte LDS
 // loads: lane l of a wave instruction writes bytes 16l..16l+15 of a 1 KiB
-// LDS span). Kept out of lambdas: a device-only builtin inside an
-// (implicitly host+device) lambda makes the host pass drop the kernel.
+// LDS span). Global addresses are a wave-uniform base plus a 32-bit lane
+// offset fixed for the whole K loop. Kept out of lambdas: a device-only
+// builtin inside an (implicitly host+device) lambda makes the host pass drop
+// the kernel.
 template <int BM, int BN, int NW>
-__device__ __forceinline__ void load_stage(char* st, const char* a_base, const int* a_row, size_t a_row_bytes,
-                                           const GemmArgs& p, const uint8_t* wbase, const uint8_t* sbase,
+__device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint32_t* a_off, const GemmArgs& p,
+                                           const uint8_t* wbase, const uint8_t* sbase, const uint32_t* s_off,
                                            int wg_tile0, int wave, int lane, int mb, int g) {
   using L = Stage<BM, BN>;
-  // A: wave instruction i covers rows 4i..4i+3
+  constexpr int A_INST = (L::A_SLOTS + 63) / 64;
+  const char* ag = a_g + (size_t)g * 256;
 #pragma unroll
-  for (int r = 0; r < BM / 4 / NW; ++r) {
+  for (int r = 0; r < (A_INST + NW - 1) / NW; ++r) {
     const int i = r * NW + wave;
-    __builtin_amdgcn_global_load_lds(a_base + (size_t)a_row[r] * a_row_bytes + (size_t)g * 256,
-                                     (lds_void*)(st + L::A + i * 1024), 16, 0, 0);
+    if (i < A_INST)
+      __builtin_amdgcn_global_load_lds(ag + a_off[r], (lds_void*)(st + L::A + i * 1024), 16, 0, 0);
   }
-  // weights: one 1 KiB unit per instruction (tiles past the layer re-read
-  // the last tile; their results are never stored)
 #pragma unroll
   for (int r = 0; r < (BN / 16 + NW - 1) / NW; ++r) {
     const int t = r * NW + wave;
     if (t < BN / 16) {
+      // tiles past the layer re-read the last tile; their results are never stored
       const int tile = min(wg_tile0 + t, p.ntiles - 1);
       __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * kUnit4Bytes + lane * 16,
                                        (lds_void*)(st + L::W + t * 1024), 16, 0, 0);
     }
   }
-  // scale records: 128 bytes per tile, 8 tiles per instruction
   if (wave == NW - 1) {
 #pragma unroll
-    for (int r = 0; r < BN / 128; ++r) {
-      const int t = r * 8 + (lane >> 3);
-      const int tile = min(wg_tile0 + t, p.ntiles - 1);
-      __builtin_amdgcn_global_load_lds(sbase + ((size_t)tile * p.groups + g) * 128 + (lane & 7) * 16,
-                                       (lds_void*)(st + L::S + r * 1024), 16, 0, 0);
-    }
+    for (int r = 0; r < BN / 128; ++r)
+      __builtin_amdgcn_global_load_lds(sbase + (size_t)g * 128 + s_off[r], (lds_void*)(st + L::S + r * 1024), 16,
+                                       0, 0);
   }
-  // row sums: BM floats
   if (wave == 0 && lane < BM / 4) {
-    const float* rs = p.rowsum + (size_t)g * p.m_pad + mb * BM + lane * 4;
+    const char* rs = (const char*)(p.rowsum + (size_t)g * p.m_pad + mb * BM) + lane * 16;
     __builtin_amdgcn_global_load_lds(rs, (lds_void*)(st + L::RS), 16, 0, 0);
   }
 }
@@ -128,31 +153,26 @@ __device__ __forceinline__ void load_stage(char* st, const char* a_base, const i
 // (each chain seeded with -(128+z) * rowsum) and fold them into the
 // accumulators with the group scales. N tiles past the end of the layer hold
 // duplicate data: computed like the others and never stored.
-template <bool ASYM, int BM, int BN>
-__device__ __forceinline__ void tile_group(const char* st, int wm, int wn, int lane, uint32_t um, uint32_t ue,
-                                           f32x4_t (&acc)[4][4]) {
+template <bool ASYM, int BM, int BN, int MTW>
+__device__ __forceinline__ void tile_group(const char* st, int a_lane, int w_lane, int s_lane, int rs_lane,
+                                           uint32_t um, uint32_t ue, f32x4_t (&acc)[MTW][4]) {
   using L = Stage<BM, BN>;
-  const int c = lane >> 4, col = lane & 15;
+  u32x4_t bp[4];
   u32x4_t bw[4][4];
   float sc[4], negz[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int tt = wn * 4 + t;
-    const u32x4_t b = *(const u32x4_t*)(st + L::W + tt * 1024 + lane * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bw[t][j] = unpack_u4_bf16_offset128(b[j], um, ue);
-    const u32x2_t rec = *(const u32x2_t*)(st + L::S + tt * 128 + col * 8);
+    bp[t] = *(const u32x4_t*)(st + w_lane + t * 1024);
+    const u32x2_t rec = *(const u32x2_t*)(st + s_lane + t * 128);
     sc[t] = bits_as<float>(rec.x);
     negz[t] = __builtin_bit_cast(float, (rec.y & 0xFFFFu) << 16);  // -(128+z)
   }
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int row = wm * 64 + mt * 16 + col;
+  for (int mt = 0; mt < MTW; ++mt) {
     u32x4_t a[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      a[j] = *(const u32x4_t*)(st + L::A + row * 256 + (((4 * c + j) ^ (row & 15)) * 16));
-    const f32x4_t rs = *(const f32x4_t*)(st + L::RS + (wm * 64 + mt * 16 + 4 * c) * 4);
+    for (int j = 0; j < 4; ++j) a[j] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + j * 16);
+    const f32x4_t rs = *(const f32x4_t*)(st + rs_lane + mt * 64);
     f32x4_t pacc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -162,9 +182,16 @@ __device__ __forceinline__ void tile_group(const char* st, int wm, int wn, int l
         pacc[t] = rs;  // row sums pre-scaled by -136
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      // unpack step j of every tile right before its first use, so the
+      // first MFMAs of the group start early
+      if (mt == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bw[t][j] = unpack_u4_bf16_offset128(bp[t][j], um, ue);
+      }
 #pragma unroll
       for (int t = 0; t < 4; ++t) pacc[t] = mfma_bf16(a[j], bw[t][j], pacc[t]);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -172,13 +199,20 @@ __device__ __forceinline__ void tile_group(const char* st, int wm, int wn, int l
   }
 }
 
-template <bool ASYM, int WAVES_M, int WAVES_N, bool MOE>
+template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, int NS, bool MOE>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const GemmArgs p, int m_blocks,
                                                                            int n_blocks) {
   constexpr int NW = WAVES_M * WAVES_N;
-  constexpr int BM = 64 * WAVES_M, BN = 64 * WAVES_N;
+  constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
+  constexpr int MTW = WTM / 16;  // 16-row tiles per wave
   using L = Stage<BM, BN>;
-  extern __shared__ __attribute__((aligned(16))) char smem[];  // [2][L::BYTES]
+  constexpr int A_INST = (L::A_SLOTS + 63) / 64;
+  constexpr int A_PER_WAVE = (A_INST + NW - 1) / NW;
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // [NS][L::BYTES]
+  // copies every wave has in flight per stage at least (A and weight units);
+  // waiting for the count to drop to this leaves the next stage in flight
+  constexpr int VM_NEXT = A_INST / NW + (BN / 16) / NW;
+  static_assert(NS == 2 || NS == 3, "two or three stages");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -192,6 +226,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   int lin = blockIdx.x;
   if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
   const int mb = lin / n_blocks, nb = lin % n_blocks;
+  // split-K: this workgroup reduces K groups [g0, g1) of the tile
+  const int split = blockIdx.y, nsplit = gridDim.y;
+  const int g0 = (int)(((int64_t)split * p.groups) / nsplit);
+  const int g1 = (int)(((int64_t)(split + 1) * p.groups) / nsplit);
 
   int expert = 0;
   if constexpr (MOE) {
@@ -201,14 +239,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   const uint8_t* wbase = p.packed + (size_t)expert * p.expert_stride;
   const uint8_t* sbase = wbase + p.s_offset;
   const int groups = p.groups;
+  const int wg_tile0 = nb * (BN / 16);
 
-  // A rows this lane copies (one per wave instruction); the 16-byte chunk it
-  // fetches is the same for all of them (row % 16 does not depend on r)
-  int a_row[BM / 4 / NW];
-  const int a_chunk = (lane & 15) ^ ((4 * wave + (lane >> 4)) & 15);
+  // A copy plan: slot q = 64 i + lane of the padded tile is row q / 17,
+  // 16-byte chunk q % 17 (chunk 16 is padding: it re-reads chunk 0)
+  uint32_t a_off[A_PER_WAVE];
 #pragma unroll
-  for (int r = 0; r < BM / 4 / NW; ++r) {
-    const int row = 4 * (r * NW + wave) + (lane >> 4);
+  for (int r = 0; r < A_PER_WAVE; ++r) {
+    const int q = (r * NW + wave) * 64 + lane;
+    const int row = min(q / 17, BM - 1), ch = q % 17;
     const int grow = mb * BM + row;
     int src;
     if constexpr (MOE) {
@@ -217,11 +256,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
     } else {
       src = grow < p.M ? grow : p.M - 1;
     }
-    a_row[r] = src;
+    a_off[r] = (uint32_t)src * (uint32_t)(p.K * 2) + (uint32_t)(ch < 16 ? ch : 0) * 16;
   }
-  const char* a_base = (const char*)p.A + a_chunk * 16;
-  const size_t a_row_bytes = (size_t)p.K * 2;
-  const int wg_tile0 = nb * (BN / 16);
+  // scale records: lane l fetches 16 bytes (l % 8) of tile 8r + l / 8
+  uint32_t s_off[BN / 128];
+#pragma unroll
+  for (int r = 0; r < BN / 128; ++r) {
+    const int s_tile = min(wg_tile0 + 8 * r + (lane >> 3), p.ntiles - 1);
+    s_off[r] = (uint32_t)s_tile * (uint32_t)groups * 128u + (lane & 7) * 16;
+  }
+
+  // per-lane LDS bases of the fragment reads (byte offsets inside a stage)
+  const int a_lane = L::A + (wm * WTM + col) * L::ROW + c * 64;
+  const int w_lane = L::W + (wn * 4) * 1024 + lane * 16;
+  const int s_lane = L::S + (wn * 4) * 128 + col * 8;
+  const int rs_lane = L::RS + (wm * WTM + 4 * c) * 4;
 
   // one unpack constant in a VGPR, the other in an SGPR: lets each unpacked
   // dword be a single v_and_or_b32 (VOP3 reads at most one scalar operand)
@@ -229,33 +278,50 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   asm volatile("v_mov_b32 %0, %1" : "=v"(um) : "s"(p.unpack_mask));
   const uint32_t ue = p.unpack_exp;
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[MTW][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load_stage<BM, BN, NW>(smem, a_base, a_row, a_row_bytes, p, wbase, sbase, wg_tile0, wave, lane, mb, 0);
-  for (int g = 0; g < groups; ++g) {
-    char* cur = smem + (g & 1) * L::BYTES;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of group g landed
-    __syncthreads();                // ... and every other wave's; the other stage is free
-    if (g + 1 < groups)
-      load_stage<BM, BN, NW>(smem + ((g + 1) & 1) * L::BYTES, a_base, a_row, a_row_bytes, p, wbase, sbase,
-                             wg_tile0, wave, lane, mb, g + 1);
-    tile_group<ASYM, BM, BN>(cur, wm, wn, lane, um, ue, acc);
+  const char* a_g = (const char*)p.A;
+  // NS-stage ring: groups g+1 .. g+NS-1 are in flight while g is computed
+#pragma unroll
+  for (int q = 0; q < NS - 1; ++q)
+    if (g0 + q < g1)
+      load_stage<BM, BN, NW>(smem + q * L::BYTES, a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane, mb,
+                             g0 + q);
+  int cur = 0;  // stage of group g
+  for (int g = g0; g < g1; ++g) {
+    if (NS == 3 && g + 1 < g1)
+      __builtin_amdgcn_s_waitcnt((VM_NEXT & 15) | (7 << 4) | (15 << 8) | ((VM_NEXT >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // group g is in LDS for every wave; stage of g-1 is free
+    if (g + NS - 1 < g1) {
+      int nxt = cur + NS - 1;
+      if (nxt >= NS) nxt -= NS;
+      load_stage<BM, BN, NW>(smem + nxt * L::BYTES, a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane, mb,
+                             g + NS - 1);
+    }
+    tile_group<ASYM, BM, BN, MTW>(smem + cur * L::BYTES, a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
+    cur = cur + 1 == NS ? 0 : cur + 1;
   }
 
   // ---- epilogue: per wave, transpose each 16 x 64 strip through LDS so that
   // every lane stores whole 16-byte row segments
   __syncthreads();  // everyone is done with the stages
-  const bool f32out = p.otype == QDG_O_F32;
+  // split-K: each split stores its fp32 partial tile row-major into the
+  // workspace ([split][m_pad][n_pad]); reduce_splits_kernel sums them
+  const bool to_partial = nsplit > 1;
+  const int n_pad = n_blocks * BN;
+  const bool f32out = to_partial || p.otype == QDG_O_F32;
   char* strip = smem + wave * (16 * 64 * 4);
   const int nbase = (wg_tile0 + wn * 4) * 16;
   const int esz = f32out ? 4 : 2;  // bytes per output element
   const int cpr = 64 * esz / 16;   // 16-byte chunks per strip row
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MTW; ++mt) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -270,7 +336,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
     __builtin_amdgcn_wave_barrier();
     for (int chunk = lane; chunk < 16 * cpr; chunk += 64) {
       const int r = chunk / cpr, cc = chunk % cpr;
-      const int lrow = mb * BM + wm * 64 + mt * 16 + r;
+      const int lrow = mb * BM + wm * WTM + mt * 16 + r;
       int yrow = lrow;
       bool v;
       if constexpr (MOE) {
@@ -283,6 +349,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
       const int per = 16 / esz;  // elements per chunk
       const int n0 = nbase + cc * per;
       const u32x4_t val = *(const u32x4_t*)(strip + r * 64 * esz + cc * 16);
+      if (to_partial) {
+        float* dst = (float*)p.partial + ((size_t)split * p.m_pad + lrow) * n_pad + n0;
+        *(u32x4_t*)dst = val;
+        continue;
+      }
       if (v && n0 < p.N) {
         char* dst = (char*)p.Y + ((size_t)yrow * p.N + n0) * esz;
         if (n0 + per <= p.N && ((uintptr_t)dst & 15) == 0) {
@@ -299,42 +370,60 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   }
 }
 
-template <bool ASYM, int WAVES_M, int WAVES_N, bool MOE>
-hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, hipStream_t s) {
-  constexpr int BM = 64 * WAVES_M, BN = 64 * WAVES_N;
+template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE>
+hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s) {
+  constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
+  // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256, 2 for 256 x 128)
+  constexpr int NS = 3 * Stage<BM, BN>::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-  const size_t smem = 2 * Stage<BM, BN>::BYTES;
+  const size_t smem = NS * Stage<BM, BN>::BYTES;
   static bool attr_set = false;  // idempotent; a race only repeats the call
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, MOE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, MOE>), dim3(m_blocks * n_blocks),
+  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE>), dim3(m_blocks * n_blocks, nsplit),
                      dim3(64 * WAVES_M * WAVES_N), smem, s, a, m_blocks, n_blocks);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Instances: (block_m, block_n, waves) = (256, 128, 8), (128, 256, 8) with
+// 64 x 64 wave tiles (two waves per SIMD) and (128, 256, 4) with 128 x 64
+// wave tiles (one wave per SIMD, half the unpack work per MFMA).
 bool tile_cfg_supported(Format f, const TileCfg& c) {
-  return f == FMT_W4A16 && ((c.bm == 256 && c.bn == 128) || (c.bm == 128 && c.bn == 256));
+  if (f != FMT_W4A16) return false;
+  if (c.bm == 256 && c.bn == 128) return c.waves == 8;
+  if (c.bm == 128 && c.bn == 256) return c.waves == 8 || c.waves == 4;
+  return false;
 }
 
 hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const GemmArgs& a, int m_blocks,
                        hipStream_t s) {
   if (!tile_cfg_supported(f, c)) return hipErrorInvalidValue;
-#define QDG_T(ASYM_, WM_, WN_, MOE_) \
-  if (asym == ASYM_ && c.bm == 64 * WM_ && moe == MOE_) return launch_tile_cfg<ASYM_, WM_, WN_, MOE_>(a, m_blocks, s);
-  QDG_T(false, 4, 2, false)
-  QDG_T(false, 2, 4, false)
-  QDG_T(true, 4, 2, false)
-  QDG_T(true, 2, 4, false)
-  QDG_T(false, 4, 2, true)
-  QDG_T(false, 2, 4, true)
+#define QDG_T(ASYM_, WM_, WN_, WTM_, MOE_)                                                 \
+  if (asym == ASYM_ && c.bm == WM_ * WTM_ && c.waves == WM_ * WN_ && moe == MOE_)         \
+    return launch_tile_cfg<ASYM_, WM_, WN_, WTM_, MOE_>(a, m_blocks, a.split, s);
+  QDG_T(false, 4, 2, 64, false)
+  QDG_T(false, 2, 4, 64, false)
+  QDG_T(false, 1, 4, 128, false)
+  QDG_T(true, 4, 2, 64, false)
+  QDG_T(true, 2, 4, 64, false)
+  QDG_T(true, 1, 4, 128, false)
+  QDG_T(false, 2, 4, 64, true)
+  QDG_T(false, 1, 4, 128, true)
 #undef QDG_T
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_reduce_splits(const GemmArgs& a, int m_pad, int n_pad, hipStream_t s) {
+  const int64_t threads = (int64_t)a.M * (n_pad / 4);
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     (const float*)a.partial, a.Y, a.M, a.N, m_pad, n_pad, a.split, a.otype);
+  return hipGetLastError();
 }
 
 hipError_t launch_rowsum(const void* a_bf16, const int* sorted_ids, const int* num_padded, int top_k,

@@ -135,3 +135,21 @@ def test_tile_family_asym_and_ragged(qdg):
         assert metrics.rel_frob(H.to_f64(y), y64) <= 5e-5
         yb = H.w4a16(a, qv, s, z)
         assert metrics.rel_frob(H.to_f64(yb), y64) <= 2e-3
+
+
+def test_tile_family_split_k_deterministic(qdg):
+    # the tiled family's fixed-order split-K: bitwise repeatable, and equal to
+    # the unsplit result within fp32 reordering
+    m, k, n = 200, 2048, 512
+    qv, s, z, w64 = _layer_data(n, k, asym=False, salt=17)
+    a = synth.activations_bf16_bits(m, k, workload_id=1, salt=17)
+    y64 = ref.gemm_w4a16(a, w64)
+    outs = {}
+    for split in (1, 3, 8):
+        t = q.TuningConfig(block_m=128, split_k=split)
+        y1 = H.w4a16(a, qv, s, z, otype=q.QDG_O_F32, tuning=t)
+        y2 = H.w4a16(a, qv, s, z, otype=q.QDG_O_F32, tuning=t)
+        assert torch.equal(y1, y2), f"split {split} not deterministic"
+        assert metrics.rel_frob(H.to_f64(y1), y64) <= 5e-5
+        outs[split] = H.to_f64(y1)
+    assert np.allclose(outs[1], outs[8], rtol=1e-5, atol=1e-5)
