@@ -48,6 +48,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr size_t kCounterBytes = 64 * 1024;
 constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(unsigned));
 constexpr int kTargetWorkgroups = 512;  // two 4-wave workgroups per CU (256 CUs)
+constexpr int kWsTargetWorkgroups = 256;  // weight streaming: one workgroup per CU
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -161,6 +162,7 @@ qdg_status validate_layer(const qdg_layer_config* L) {
 
 struct Choice {
   bool tile;
+  bool ws;  // weight-streaming family (dense M <= 16, MoE 16-row blocks)
   StreamCfg sc;
   TileCfg tc;
   int grid_m;
@@ -201,6 +203,23 @@ Choice choose(const qdg_plan& P, int64_t M) {
     ch.sc = StreamCfg{bm / 16, ch.tc.bn / 16, ch.tc.waves, split};
     ch.partial_bytes = split > 1 ? (size_t)tiles * split * ch.tc.bm * ch.tc.bn * 4 : 0;
     ch.rowsum_bytes = (size_t)ch.grid_m * bm * g.groups * 4;
+    return ch;
+  }
+  // weight-streaming family: W4A16 with M <= 16, unless the caller pins a
+  // streaming-family shape or asks for batch invariance (whose results must
+  // not depend on which family a given M selects)
+  const bool ws_tuning_ok =
+      !P.has_tuning || ((!T.block_m || T.block_m == 16) && (!T.block_n || T.block_n == 64) && (!T.waves || T.waves == 4));
+  if (bm == 16 && P.fmt == FMT_W4A16 && !P.compute.batch_invariant && ws_tuning_ok &&
+      (!moe || P.layer.wtype == QDG_W_INT4)) {
+    ch.ws = true;
+    ch.grid_m = 1;
+    const int64_t nblocks = (g.ntiles + 3) / 4;
+    int split = P.has_tuning && T.split_k ? T.split_k : (int)(kWsTargetWorkgroups / nblocks);
+    if (moe || split < 1) split = 1;
+    if (split > g.groups) split = (int)g.groups;
+    ch.sc = StreamCfg{1, 4, 4, split};
+    ch.partial_bytes = split > 1 ? (size_t)split * 16 * g.ntiles * 16 * 4 : 0;
     return ch;
   }
   if (bm > 64) bm = 64;  // other formats: the streaming family serves every M
@@ -337,7 +356,7 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
   p->geom = packed_geom(*layer, f);
   if (tuning) {
     const Choice c = choose(*p, 1);
-    if (c.tile ? !tile_cfg_supported(f, c.tc) : !stream_cfg_supported(f, c.sc)) {
+    if (c.tile ? !tile_cfg_supported(f, c.tc) : !c.ws && !stream_cfg_supported(f, c.sc)) {
       delete p;
       return fail(QDG_ERR_UNSUPPORTED, "no kernel instance for block_m/block_n/waves of this tuning");
     }
@@ -364,7 +383,7 @@ int qdg_plan_describe(const qdg_plan* plan, int64_t M, char* buf, size_t len) {
                   "%s %s n=%lld k=%lld E=%lld M=%lld: family=%s block_m=%d block_n=%d split_k=%d "
                   "waves=%d mfma=16x16x32 grid_m=%d batch_invariant=%d tuning=%s layout=%d arch=gfx950",
                   fmt_name(plan->fmt, plan->layer), kind, (long long)plan->layer.n, (long long)plan->layer.k,
-                  (long long)plan->layer.num_experts, (long long)M, c.tile ? "tile" : "stream",
+                  (long long)plan->layer.num_experts, (long long)M, c.tile ? "tile" : c.ws ? "wstream" : "stream",
                   c.tile ? c.tc.bm : c.sc.mt * 16, c.tile ? c.tc.bn : c.sc.nt * 16, c.sc.split, c.sc.kw,
                   c.grid_m, plan->compute.batch_invariant, plan->has_tuning ? "user" : "heuristic",
                   QDG_LAYOUT_VERSION);
@@ -386,7 +405,14 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
     const int64_t E = plan->layer.num_experts;
     cap = align_up(rows + E * (block_m - 1), block_m);
     c.grid_m = (int)(cap / block_m);
-    if (!stream_cfg_supported(plan->fmt, c.sc)) return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
+    // the caller's block size decides the family: 16-row blocks stream the
+    // weights unless a tuning pins the streaming family
+    const qdg_tuning_config& tu = plan->tuning;
+    c.ws = block_m == 16 && !plan->compute.batch_invariant &&
+           (!plan->has_tuning || ((!tu.block_n || tu.block_n == 64) && (!tu.waves || tu.waves == 4)));
+    if (!c.ws && !c0.tile && c0.ws) c.sc = StreamCfg{block_m / 16, 2, 4, 1};
+    if (!c.ws && !stream_cfg_supported(plan->fmt, c.sc))
+      return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
   }
   size_t need = 0;
   qdg_plan_workspace(plan, M, &need);
@@ -431,6 +457,8 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
       const int n_pad = (int)((plan->geom.ntiles + c.tc.bn / 16 - 1) / (c.tc.bn / 16) * c.tc.bn);
       e = launch_reduce_splits(a, a.m_pad, n_pad, stream);
     }
+  } else if (c.ws) {
+    e = launch_wstream(asym, moe, a, c.sc.split, c.grid_m, stream);
   } else {
     e = launch_stream(plan->fmt, asym, moe, c.sc, a, c.grid_m, stream);
   }

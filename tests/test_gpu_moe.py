@@ -92,16 +92,23 @@ def test_moe_gemm_small_experts(qdg, t, bm):
     assert metrics.rel_frob(H.to_f64(yd), yd64) <= 2e-3
 
 
-def test_moe_single_expert_equals_dense(qdg):
-    # everything routed to expert 0 of 2: same rows as the dense GEMM, bitwise
+@pytest.mark.parametrize("bm", [16, 32])
+def test_moe_single_expert_equals_dense(qdg, bm):
+    # everything routed to expert 0 of 2: the MoE blocks hold the same rows as
+    # the dense GEMM run block by block with the same kernel family, so every
+    # output matches bitwise (16-row blocks: weight streaming; 32: streaming)
     t, hid, n = 40, 512, 128
     qs, ss = _experts(2, n, hid, salt=3)
     layer, pk = _moe_packed(qs, ss, n, hid)
     x = synth.activations_bf16_bits(t, hid, workload_id=4, salt=5)
     ids = np.zeros((t, 1), np.int32)
-    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, 16, 0, 1)
-    t1 = q.TuningConfig(block_m=16, block_n=32, split_k=1)
-    yd = H.w4a16(x, qs[0], ss[0], None, tuning=t1)
+    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 0, 1)
+    if bm == 16:
+        t1 = q.TuningConfig(block_m=16, block_n=64, split_k=1)
+        yd = torch.cat([H.w4a16(x[r:r + 16], qs[0], ss[0], None, tuning=t1) for r in range(0, t, 16)])
+    else:
+        t1 = q.TuningConfig(block_m=32, block_n=32, split_k=1)
+        yd = H.w4a16(x, qs[0], ss[0], None, tuning=t1)
     assert torch.equal(y, yd)
 
 

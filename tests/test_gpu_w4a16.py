@@ -125,6 +125,51 @@ def test_dense_large_m_sampled_rows(qdg, m, k, n):
     assert not torch.isnan(y.float()).any()  # every output written
 
 
+def _family(n, k, m, tuning=None, asym=False):
+    layer = q.layer_w4a16(n, k, asym=asym)
+    plan = q.qdg_plan_create(layer, q.dense(), tuning)
+    return q.qdg_plan_describe(plan, m).split("family=")[1].split()[0]
+
+
+def test_weight_streaming_selected_for_small_m(qdg):
+    assert _family(14336, 4096, 1) == "wstream"
+    assert _family(4096, 14336, 16) == "wstream"
+    assert _family(4096, 14336, 17) == "stream"
+    assert _family(512, 1024, 16, q.TuningConfig(block_m=16, block_n=32)) == "stream"
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_weight_streaming_one_hot_exact(qdg, asym):
+    # 16 one-hot rows per call through the weight-streaming kernel: each output
+    # is a dequantized weight, exact in fp32 (offset trick, zero points, scales)
+    k, n = 4608, 80  # 36 groups: one full 32-group chunk and a 4-group tail
+    qv, s, z, w64 = _layer_data(n, k, asym, salt=12)
+    eye = codecs.f32_to_bf16_bits(np.eye(k, dtype=np.float32))
+    for r0 in (0, 16, 4080, 4592):
+        y = H.w4a16(eye[r0:r0 + 16], qv, s, z, otype=q.QDG_O_F32, tuning=q.TuningConfig(split_k=1))
+        assert np.array_equal(H.to_f64(y), w64.T[r0:r0 + 16]), f"rows {r0}.."
+
+
+def test_weight_streaming_split_k(qdg):
+    # K = 14336 (112 groups) with N = 272 (17 tiles, a ragged workgroup): every
+    # split count is deterministic and within the fp32 bound, chunks of 32
+    # groups and ragged chunk tails included
+    k, n, m = 14336, 272, 16
+    qv, s, z, w64 = _layer_data(n, k, asym=False, salt=13)
+    a = synth.activations_bf16_bits(m, k, workload_id=1, salt=13)
+    y64 = ref.gemm_w4a16(a, w64)
+    outs = {}
+    for split in (1, 3, 7, 112):
+        t = q.TuningConfig(split_k=split)
+        assert _family(n, k, m, t) == "wstream"
+        y1 = H.w4a16(a, qv, s, z, otype=q.QDG_O_F32, tuning=t)
+        y2 = H.w4a16(a, qv, s, z, otype=q.QDG_O_F32, tuning=t)
+        assert torch.equal(y1, y2), f"split {split} not deterministic"
+        assert metrics.rel_frob(H.to_f64(y1), y64) <= 5e-5, f"split {split}"
+        outs[split] = H.to_f64(y1)
+    assert np.allclose(outs[1], outs[112], rtol=1e-5, atol=1e-5)
+
+
 def test_tile_family_asym_and_ragged(qdg):
     # uint4 with zero points through the tiled family, ragged M and N
     for m, n, k in [(300, 200, 640), (129, 1040, 256)]:
