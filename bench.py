@@ -69,10 +69,14 @@ def gpu_leg(args):
             bufs.append(b)
         layers[(k, n)] = (layer, q.qdg_plan_create(layer, q.dense()), bufs)
 
+    # launch order within a step: largest M first, so that while its
+    # millisecond-scale GEMMs run the host has queued every small-M launch;
+    # the small cases then run back to back and their events time the
+    # kernels, not the host's launch latency
     cases = []
-    for (k, n) in SHAPES:
-        layer, plan, bufs = layers[(k, n)]
-        for m in M_SWEEP:
+    for m in sorted(M_SWEEP, reverse=True):
+        for (k, n) in SHAPES:
+            layer, plan, bufs = layers[(k, n)]
             a = synth.device_activations_bf16(m, k, seed=synth.seed_for(1, synth.TID_A, m))
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
             wsb = q.qdg_plan_workspace(plan, m)

@@ -74,10 +74,19 @@ __global__ void reduce_splits_kernel(const float* __restrict__ partial, void* __
   if (q >= (int64_t)M * cpr) return;
   const int row = (int)(q / cpr), c4 = (int)(q % cpr) * 4;
   if (c4 >= N) return;
+  // four splits per step with their loads in flight together; the sum is
+  // still taken in split order (deterministic)
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const f32x4_t v = *(const f32x4_t*)(partial + ((size_t)sp * m_pad + row) * n_pad + c4);
-    s = f32x4_t{s[0] + v[0], s[1] + v[1], s[2] + v[2], s[3] + v[3]};
+  for (int sp0 = 0; sp0 < nsplit; sp0 += 4) {
+    f32x4_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sp = sp0 + j < nsplit ? sp0 + j : nsplit - 1;
+      v[j] = *(const f32x4_t*)(partial + ((size_t)sp * m_pad + row) * n_pad + c4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (sp0 + j < nsplit) s = f32x4_t{s[0] + v[j][0], s[1] + v[j][1], s[2] + v[j][2], s[3] + v[j][3]};
   }
   for (int e = 0; e < 4 && c4 + e < N; ++e) {
     const size_t o = (size_t)row * N + c4 + e;

@@ -139,21 +139,24 @@ def test_weight_streaming_selected_for_small_m(qdg):
 
 
 @pytest.mark.parametrize("asym", [False, True])
-def test_weight_streaming_one_hot_exact(qdg, asym):
-    # 16 one-hot rows per call through the weight-streaming kernel: each output
-    # is a dequantized weight, exact in fp32 (offset trick, zero points, scales)
-    k, n = 4608, 80  # 36 groups: one full 32-group chunk and a 4-group tail
+@pytest.mark.parametrize("k", [4096, 4608])
+def test_weight_streaming_one_hot_exact(qdg, asym, k):
+    # 16 one-hot rows per call through the weight-streaming kernels: each
+    # output is a dequantized weight, exact in fp32 (offset trick, zero points,
+    # scales). K = 4096 (32 groups) keeps all of A in LDS; K = 4608 (36
+    # groups) streams A in 8-group chunks, the last one ragged (4 groups)
+    n = 80
     qv, s, z, w64 = _layer_data(n, k, asym, salt=12)
     eye = codecs.f32_to_bf16_bits(np.eye(k, dtype=np.float32))
-    for r0 in (0, 16, 4080, 4592):
+    for r0 in (0, 16, k - 528, k - 16):
         y = H.w4a16(eye[r0:r0 + 16], qv, s, z, otype=q.QDG_O_F32, tuning=q.TuningConfig(split_k=1))
         assert np.array_equal(H.to_f64(y), w64.T[r0:r0 + 16]), f"rows {r0}.."
 
 
 def test_weight_streaming_split_k(qdg):
     # K = 14336 (112 groups) with N = 272 (17 tiles, a ragged workgroup): every
-    # split count is deterministic and within the fp32 bound, chunks of 32
-    # groups and ragged chunk tails included
+    # split count is deterministic and within the fp32 bound; splits 1 and 3
+    # stream A in chunks (ragged tails included), 7 and 112 keep it in LDS
     k, n, m = 14336, 272, 16
     qv, s, z, w64 = _layer_data(n, k, asym=False, salt=13)
     a = synth.activations_bf16_bits(m, k, workload_id=1, salt=13)
