@@ -142,6 +142,159 @@ def gpu_leg(args):
     return dict(value=value, ms_per_step=ms_per_step, roofline=roof, roofline_m16=roof16, cases=out_cases)
 
 
+PEAK_INT8_TOPS = 5000.0
+PEAK_FP8_TFLOPS = 5000.0
+
+
+def _time_launches(launch, reps, stream):
+    """Per-launch GPU time (us): the host first queues `reps` launches behind
+    a short spin kernel, so the events bracket kernels, not launch latency."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda._sleep(int(3e6))
+    for i in range(reps):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    return t[len(t) // 2]
+
+
+def rows_leg(reps=30):
+    """The other rows of the hot path, each timed at its own shapes (not part
+    of `value`): W8A8 and W4A8-INT8 (K=4096, N in {4096, 14336}, M in
+    {16, 256, 4096}), W4A8-MXFP4 ((K,N) in {(7168,2048), (2048,7168)}, M in
+    {16, 512, 4096}), the activation quantizers, and the grouped MoE W4A16
+    GEMMs (E=256, top-8, hidden 7168, intermediate 2048, T in {64, 512,
+    4096}) with their expert sort."""
+    import torch
+    import quantized_dequant_gemm_amd as q
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    out = []
+
+    def dense_row(name, layer, k, n, ms, qa_dtype, act_group, peak, w_bytes):
+        nbytes = q.qdg_preprocess_query(layer)
+        w = synth.device_normal_f32((n, k), 0.02, seed=synth.seed_for(2, synth.TID_W, n + k))
+        if layer.wtype == q.QDG_W_INT8:
+            qw = torch.empty((n, k), dtype=torch.int8, device=dev)
+            sc = torch.empty(n, dtype=torch.float32, device=dev)
+        elif layer.wtype == q.QDG_W_MXFP4:
+            qw = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+            sc = torch.empty((n, k // 32), dtype=torch.uint8, device=dev)
+        else:
+            qw = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+            sc = torch.empty((n, k // 128), dtype=torch.int16, device=dev)
+        q.qdg_quantize_weights(layer, w.data_ptr(), qw.data_ptr(), sc.data_ptr(), None, sh)
+        del w
+        copies = max(2, -(-2 * CACHE_BYTES // nbytes))
+        bufs = []
+        for _ in range(copies):
+            b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            q.qdg_preprocess(layer, q.StdWeights(qw.data_ptr(), sc.data_ptr(), None), b.data_ptr(), nbytes, sh)
+            bufs.append(b)
+        plan = q.qdg_plan_create(layer, q.dense())
+        for m in ms:
+            a = synth.device_activations_bf16(m, k, seed=synth.seed_for(2, synth.TID_A, m))
+            qa = torch.empty((m, k), dtype=qa_dtype, device=dev)
+            sa = torch.empty((m, k // act_group) if act_group else m, dtype=torch.float32, device=dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            wsb = q.qdg_plan_workspace(plan, m)
+            ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+
+            def quant(i):
+                q.qdg_quantize_act(layer, a.data_ptr(), m, qa.data_ptr(), sa.data_ptr(), sh)
+
+            def gemm(i):
+                q.qdg_gemm(plan, qa.data_ptr(), sa.data_ptr(), bufs[i % len(bufs)].data_ptr(), y.data_ptr(), m,
+                           ws.data_ptr(), wsb, sh)
+            quant(0)
+            for i in range(3):
+                gemm(i)
+            us_q = _time_launches(quant, reps, stream)
+            us = _time_launches(gemm, reps, stream)
+            fl = 2 * m * n * k
+            by = w_bytes + m * k * 1 + (m * (k // act_group) * 4 if act_group else m * 4) + m * n * 2
+            print(f"row {name} M={m} K={k} N={n}: {us:.2f} us", file=sys.stderr, flush=True)
+            out.append(dict(row=name, M=m, K=k, N=n, us=round(us, 3), tflops=round(fl / us / 1e6, 2),
+                            gbs=round(by / us / 1e3, 1), hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4),
+                            mfma_frac=round(fl / us / 1e6 / peak, 4), act_quant_us=round(us_q, 3),
+                            instance=q.qdg_plan_describe(plan, m).split(": ", 1)[1]))
+        del bufs
+
+    for n in (4096, 14336):
+        k = 4096
+        dense_row("w8a8", q.layer_w8a8(n, k), k, n, (16, 256, 4096), torch.int8, 0, PEAK_INT8_TOPS,
+                  n * k + n * 4)
+        dense_row("w4a8-int8", q.layer_w4a8(n, k), k, n, (16, 256, 4096), torch.int8, 0, PEAK_INT8_TOPS,
+                  n * k // 2 + n * (k // 128) * 2)
+    for (k, n) in ((7168, 2048), (2048, 7168)):
+        dense_row("w4a8-mxfp4", q.layer_mxfp4(n, k), k, n, (16, 512, 4096), torch.uint8, 128, PEAK_FP8_TFLOPS,
+                  n * k // 2 + n * (k // 32))
+
+    # ---- grouped MoE W4A16
+    E, top_k, hid, inter = 256, 8, 7168, 2048
+    layers = {}
+    for name, (n, k) in (("moe-gate-up", (2 * inter, hid)), ("moe-down", (hid, inter))):
+        layer = q.layer_w4a16(n, k, num_experts=E)
+        qw = torch.empty((E, n, k // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((E, n, k // 128), dtype=torch.int16, device=dev)
+        one = q.layer_w4a16(n, k)
+        for e in range(E):
+            w = synth.device_normal_f32((n, k), 0.02, seed=synth.seed_for(4, synth.TID_W, e + (E if k == inter else 0)))
+            q.qdg_quantize_weights(one, w.data_ptr(), qw[e].data_ptr(), sc[e].data_ptr(), None, sh)
+        nbytes = q.qdg_preprocess_query(layer)
+        pk = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        q.qdg_preprocess(layer, q.StdWeights(qw.data_ptr(), sc.data_ptr(), None), pk.data_ptr(), nbytes, sh)
+        del qw, sc
+        layers[name] = (layer, pk, n, k, q.qdg_plan_create(layer, q.moe(top_k)))
+        print(f"row {name}: {E} experts packed", file=sys.stderr, flush=True)
+    for t in (64, 512, 4096):
+        g = torch.Generator(device=dev)
+        g.manual_seed(synth.seed_for(4, synth.TID_LOGITS, t))
+        logits = torch.randn((t, E), generator=g, device=dev, dtype=torch.float32)
+        ids = torch.topk(logits, top_k, dim=1).indices.to(torch.int32).contiguous()
+        touched = int(torch.unique(ids).numel())
+        bm = 16 if t * top_k <= 32 * E else 64
+        cap = q.qdg_moe_align_capacity(t, top_k, E, bm)
+        sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+        block_expert = torch.empty(cap // bm, dtype=torch.int32, device=dev)
+        npad = torch.empty(1, dtype=torch.int32, device=dev)
+
+        def align(i):
+            q.qdg_moe_align(ids.data_ptr(), t, top_k, E, bm, sorted_ids.data_ptr(), block_expert.data_ptr(),
+                            npad.data_ptr(), sh)
+        align(0)
+        us_align = _time_launches(align, reps, stream)
+        for name, (layer, pk, n, k, plan) in layers.items():
+            per_pair = name == "moe-down"
+            rows_in = t * top_k if per_pair else t
+            a = synth.device_activations_bf16(rows_in, k, seed=synth.seed_for(4, synth.TID_H, t + k))
+            y = torch.empty((t * top_k, n), dtype=torch.bfloat16, device=dev)
+            wsb = q.qdg_plan_workspace(plan, t)
+            ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+
+            def gemm(i):
+                q.qdg_moe_gemm(plan, a.data_ptr(), None, pk.data_ptr(), sorted_ids.data_ptr(),
+                               block_expert.data_ptr(), npad.data_ptr(), t, bm, 1 if per_pair else 0,
+                               y.data_ptr(), ws.data_ptr(), wsb, sh)
+            gemm(0)
+            us = _time_launches(gemm, max(5, reps // 3), stream)
+            fl = 2 * t * top_k * n * k
+            by = touched * (n * k // 2 + n * (k // 128) * 2) + rows_in * k * 2 + t * top_k * n * 2
+            print(f"row {name} T={t}: {us:.2f} us", file=sys.stderr, flush=True)
+            out.append(dict(row=name, T=t, K=k, N=n, block_m=bm, experts_touched=touched, us=round(us, 3),
+                            tflops=round(fl / us / 1e6, 2), gbs=round(by / us / 1e3, 1),
+                            hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4),
+                            mfma_frac=round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4), align_us=round(us_align, 3),
+                            instance=q.qdg_plan_describe(plan, t).split(": ", 1)[1]))
+    return out
+
+
 def cpu_leg():
     """The fp64 oracle, untuned, on a bounded sample of the step: both
     projection shapes over the whole M sweep (dequantize the layer, then the
@@ -174,6 +327,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-rows", action="store_true", help="skip the W8A8 / W4A8 / MXFP4 / MoE rows")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -190,6 +344,8 @@ def main():
                    "launches_per_step": len(g["cases"])},
         "roofline": g["roofline"], "roofline_m16": g["roofline_m16"], "cases": g["cases"],
     }
+    if not args.no_rows:
+        line["rows"] = rows_leg()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_leg()
     print(json.dumps(line), flush=True)

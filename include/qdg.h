@@ -98,12 +98,18 @@ typedef struct qdg_compute_config {
   int32_t kind, batch_invariant, top_k, reserved;
 } qdg_compute_config;
 
-/* Tuning config: how to run. Zero in any field means "heuristic". block_m
-   selects the kernel family (<= 64: streaming split-K family; >= 128: the
-   LDS-tiled MFMA family), block_n is the N tile (multiple of 16), split_k the
-   number of K partitions reduced in a fixed order, waves the wavefronts per
-   workgroup. Fields block_k, stages, mfma and load_path are recorded in the
-   description but only one value each is implemented (128, 2, 16, 0). */
+/* Tuning config: how to run. Zero in any field means "heuristic". Three
+   kernel families exist; block_m and waves select one:
+     weight streaming  block_m 16, block_n 64, waves 8 (W4A16 only; the
+                       default for M <= 16 and 16-row MoE blocks)
+     streaming         block_m 16, 32 or 64, block_n 16, 32 or 64, waves 4
+                       (every format; the default otherwise for M <= 64)
+     LDS-tiled         block_m 128 (block_n 256) or 256 (block_n 128), waves
+                       8 or 4 (dense W4A16; the default for M > 64)
+   split_k is the number of K partitions (dense only), reduced in a fixed
+   order. batch_invariant plans use the streaming family for every M. Fields
+   block_k, stages, mfma and load_path are recorded in the description but
+   only one value each is implemented (128, 2, 16, 0). */
 typedef struct qdg_tuning_config {
   int32_t block_m, block_n, block_k, split_k;
   int32_t stages, waves, mfma, load_path;

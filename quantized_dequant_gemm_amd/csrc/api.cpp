@@ -209,7 +209,7 @@ Choice choose(const qdg_plan& P, int64_t M) {
   // streaming-family shape or asks for batch invariance (whose results must
   // not depend on which family a given M selects)
   const bool ws_tuning_ok =
-      !P.has_tuning || ((!T.block_m || T.block_m == 16) && (!T.block_n || T.block_n == 64) && (!T.waves || T.waves == 4));
+      !P.has_tuning || ((!T.block_m || T.block_m == 16) && (!T.block_n || T.block_n == 64) && (!T.waves || T.waves == 8));
   if (bm == 16 && P.fmt == FMT_W4A16 && !P.compute.batch_invariant && ws_tuning_ok &&
       (!moe || P.layer.wtype == QDG_W_INT4)) {
     ch.ws = true;
@@ -218,7 +218,7 @@ Choice choose(const qdg_plan& P, int64_t M) {
     int split = P.has_tuning && T.split_k ? T.split_k : (int)(kWsTargetWorkgroups / nblocks);
     if (moe || split < 1) split = 1;
     if (split > g.groups) split = (int)g.groups;
-    ch.sc = StreamCfg{1, 4, 4, split};
+    ch.sc = StreamCfg{1, 4, 8, split};  // 16 x 64 per workgroup of 8 waves
     ch.partial_bytes = split > 1 ? (size_t)split * 16 * g.ntiles * 16 * 4 : 0;
     return ch;
   }
@@ -339,7 +339,7 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
     }
     if (tuning->block_k && tuning->block_k != 128) return fail(QDG_ERR_UNSUPPORTED, "block_k must be 128");
     if (tuning->waves && tuning->waves != 4 && tuning->waves != 8)
-      return fail(QDG_ERR_UNSUPPORTED, "waves must be 4 (streaming family) or 8 (tiled family)");
+      return fail(QDG_ERR_UNSUPPORTED, "waves must be 4 (streaming, tiled) or 8 (weight streaming, tiled)");
     if (tuning->mfma && tuning->mfma != 16) return fail(QDG_ERR_UNSUPPORTED, "mfma must be 16 (16x16 tiles)");
     if (tuning->split_k < 0) return fail(QDG_ERR_INVALID_ARG, "split_k < 0");
     if (compute->kind == QDG_KIND_MOE && tuning->split_k > 1)
@@ -409,7 +409,7 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
     // weights unless a tuning pins the streaming family
     const qdg_tuning_config& tu = plan->tuning;
     c.ws = block_m == 16 && !plan->compute.batch_invariant &&
-           (!plan->has_tuning || ((!tu.block_n || tu.block_n == 64) && (!tu.waves || tu.waves == 4)));
+           (!plan->has_tuning || ((!tu.block_n || tu.block_n == 64) && (!tu.waves || tu.waves == 8)));
     if (!c.ws && !c0.tile && c0.ws) c.sc = StreamCfg{block_m / 16, 2, 4, 1};
     if (!c.ws && !stream_cfg_supported(plan->fmt, c.sc))
       return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
