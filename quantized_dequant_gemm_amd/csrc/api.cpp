@@ -162,7 +162,8 @@ qdg_status validate_layer(const qdg_layer_config* L) {
 
 struct Choice {
   bool tile;
-  bool ws;  // weight-streaming family (dense M <= 16, MoE 16-row blocks)
+  bool ws;     // weight-streaming family (dense M <= 16, MoE 16-row blocks)
+  bool qtile;  // LDS-tiled family of the 8-bit-activation formats
   StreamCfg sc;
   TileCfg tc;
   int grid_m;
@@ -220,6 +221,31 @@ Choice choose(const qdg_plan& P, int64_t M) {
     if (split > g.groups) split = (int)g.groups;
     ch.sc = StreamCfg{1, 4, 8, split};  // 16 x 64 per workgroup of 8 waves
     ch.partial_bytes = split > 1 ? (size_t)split * 16 * g.ntiles * 16 * 4 : 0;
+    return ch;
+  }
+  // LDS-tiled family of the int8 / fp8 formats: 128 x 256 tiles, used once
+  // there are enough of them (or M >= 512) to beat the streaming family
+  const bool a8_fits = (double)(M > 0 ? M : 1) * (double)g.k < 4294967296.0;
+  const int64_t q_tiles = ((M + 127) / 128) * ((g.ntiles + 15) / 16);
+  const bool q_enough = (P.has_tuning && T.block_m >= 128) || M >= 512 || q_tiles >= 64;
+  if (bm >= 128 && P.fmt != FMT_W4A16 && !moe && a8_fits && q_enough) {
+    ch.tile = true;
+    ch.qtile = true;
+    ch.tc = TileCfg{128, 256, 8};
+    ch.grid_m = (int)((M + 127) / 128);
+    const int64_t n_blocks = (g.ntiles + 15) / 16;
+    const int64_t tiles = n_blocks * ch.grid_m;
+    int split = P.has_tuning && T.split_k ? T.split_k : 0;
+    if (!split) {
+      split = tiles >= 256 ? 1 : (int)((300 + tiles - 1) / tiles);
+      const int maxs = (int)(g.groups / 2);
+      if (split > maxs) split = maxs > 0 ? maxs : 1;
+      if (split > 16) split = 16;
+    }
+    if (P.layer.otype == QDG_O_I32) split = 1;  // integer results are never split
+    ch.sc = StreamCfg{8, 16, 8, split};
+    ch.partial_bytes = split > 1 ? (size_t)tiles * split * 128 * 256 * 4 : 0;
+    ch.rowsum_bytes = 0;
     return ch;
   }
   if (bm > 64) bm = 64;  // other formats: the streaming family serves every M
@@ -325,14 +351,18 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
     return fail(QDG_ERR_INVALID_ARG, "a dense layer has num_experts = 1");
   }
   if (tuning) {
-    const bool tile_ok = f == FMT_W4A16 && compute->kind == QDG_KIND_DENSE && !compute->batch_invariant;
-    if (tuning->block_m && tuning->block_m != 16 && tuning->block_m != 32 && tuning->block_m != 64 &&
-        !(tile_ok && (tuning->block_m == 128 || tuning->block_m == 256)))
-      return fail(QDG_ERR_UNSUPPORTED, "block_m %d: implemented 16, 32, 64 (128, 256: dense W4A16)",
-                  tuning->block_m);
+    const bool dense_tiled = compute->kind == QDG_KIND_DENSE && !compute->batch_invariant;
+    const bool tile_ok = dense_tiled && (tuning->block_m == 128 || (f == FMT_W4A16 && tuning->block_m == 256));
+    if (tuning->block_m && tuning->block_m != 16 && tuning->block_m != 32 && tuning->block_m != 64 && !tile_ok)
+      return fail(QDG_ERR_UNSUPPORTED,
+                  "block_m %d: implemented 16, 32, 64 (dense: 128; dense W4A16: 256)", tuning->block_m);
     if (tuning->block_m >= 128) {
       if (tuning->block_n && tuning->block_n != (tuning->block_m == 256 ? 128 : 256))
-        return fail(QDG_ERR_UNSUPPORTED, "the tiled family pairs block_m 256 with block_n 128, 128 with 256");
+        return fail(QDG_ERR_UNSUPPORTED, "the tiled families pair block_m 256 with block_n 128, 128 with 256");
+      if (f != FMT_W4A16 && tuning->waves && tuning->waves != 8)
+        return fail(QDG_ERR_UNSUPPORTED, "the 8-bit-activation tiled family runs 8 waves");
+      if (f != FMT_W4A16 && layer->otype == QDG_O_I32 && tuning->split_k > 1)
+        return fail(QDG_ERR_UNSUPPORTED, "raw int32 output is not split");
 
     } else if (tuning->block_n && (tuning->block_n % 16 || tuning->block_n > 64)) {
       return fail(QDG_ERR_UNSUPPORTED, "block_n %d: implemented 16, 32, 64", tuning->block_n);
@@ -356,7 +386,7 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
   p->geom = packed_geom(*layer, f);
   if (tuning) {
     const Choice c = choose(*p, 1);
-    if (c.tile ? !tile_cfg_supported(f, c.tc) : !c.ws && !stream_cfg_supported(f, c.sc)) {
+    if (c.qtile ? false : c.tile ? !tile_cfg_supported(f, c.tc) : !c.ws && !stream_cfg_supported(f, c.sc)) {
       delete p;
       return fail(QDG_ERR_UNSUPPORTED, "no kernel instance for block_m/block_n/waves of this tuning");
     }
@@ -383,7 +413,8 @@ int qdg_plan_describe(const qdg_plan* plan, int64_t M, char* buf, size_t len) {
                   "%s %s n=%lld k=%lld E=%lld M=%lld: family=%s block_m=%d block_n=%d split_k=%d "
                   "waves=%d mfma=16x16x32 grid_m=%d batch_invariant=%d tuning=%s layout=%d arch=gfx950",
                   fmt_name(plan->fmt, plan->layer), kind, (long long)plan->layer.n, (long long)plan->layer.k,
-                  (long long)plan->layer.num_experts, (long long)M, c.tile ? "tile" : c.ws ? "wstream" : "stream",
+                  (long long)plan->layer.num_experts, (long long)M,
+                  c.qtile ? "qtile" : c.tile ? "tile" : c.ws ? "wstream" : "stream",
                   c.tile ? c.tc.bm : c.sc.mt * 16, c.tile ? c.tc.bn : c.sc.nt * 16, c.sc.split, c.sc.kw,
                   c.grid_m, plan->compute.batch_invariant, plan->has_tuning ? "user" : "heuristic",
                   QDG_LAYOUT_VERSION);
@@ -445,7 +476,14 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   a.unpack_exp = 0x43004300u;
   const bool asym = plan->layer.wtype == QDG_W_UINT4;
   hipError_t e;
-  if (c.tile) {
+  if (c.qtile) {
+    a.m_pad = c.grid_m * c.tc.bm;
+    e = launch_qtile(plan->fmt, a, c.grid_m, stream);
+    if (e == hipSuccess && a.split > 1) {
+      const int n_pad = (int)((plan->geom.ntiles + 15) / 16 * 256);
+      e = launch_reduce_splits(a, a.m_pad, n_pad, stream);
+    }
+  } else if (c.tile) {
     a.m_pad = c.grid_m * c.tc.bm;
     float* rs = (float*)((char*)workspace + kCounterBytes + align_up((int64_t)c.partial_bytes, 256));
     a.rowsum = rs;

@@ -1,0 +1,358 @@
+// LDS-tiled (large-M) GEMM family for the 8-bit-activation formats:
+// W8A8 and W4A8-INT8 (int8 x int8 -> exact int32 on v_mfma_i32_16x16x64_i8)
+// and W4A8-MXFP4 (fp8 E4M3 x E2M1 on the scaled 16x16x128 MFMA, with the
+// E8M0 block scales applied by the hardware).
+//
+// The pages' library serves large batches with a different, throughput-
+// oriented pipeline than small ones (kinachrichten, "Wie die Architektur
+// funktioniert") and names W8A8, W4A8 and the MXFP4 W4A8 path as formats it
+// covers ("Warum quantisierte Kernel wichtig sind", "Kompilierzeiten und
+// gerätespezifisches Tuning"). The structure is that of the W4A16 LDS-tiled
+// family:
+//   * a 512-thread workgroup owns a 128 x 256 output tile, its 8 wavefronts
+//     (two per SIMD) a 64 x 64 tile each;
+//   * the K loop advances one 128-wide group per step; the A tile (128 rows
+//     of 128 bytes, padded to 144 so 16-byte fragment reads are conflict-
+//     free), the packed weight units, the per-group weight records and (fp8)
+//     the per-(row, group) activation scales of the next groups are copied
+//     global -> LDS by direct LDS loads into a 3-stage ring;
+//   * W8A8 accumulates exact int32 over the whole K range and applies the
+//     token and channel scales once in the epilogue; W4A8 moves each int4 to
+//     the high nibble of an int8 (16 q, exact; 1/16 is folded into the
+//     scale), takes an exact int32 partial per group and adds s * P in fp32
+//     (raw int32 mode keeps integers throughout); MXFP4 adds a_scale * P per
+//     group in fp32;
+//   * the output tile goes through LDS so stores are whole 16-byte row
+//     segments; split-K writes fp32 partials that reduce_splits_kernel adds
+//     in split order.
+#include "qdg_device.h"
+#include "qdg_internal.h"
+
+namespace qdg {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+enum QKind { Q_W8A8 = 0, Q_W4A8 = 1, Q_MXFP4 = 2 };
+
+template <int KIND, int BM, int BN>
+struct QStage {
+  static constexpr int ROW = 144;                           // 128 bytes of A + 16 of padding
+  static constexpr int UNIT = KIND == Q_W8A8 ? 2048 : 1024;  // bytes per 16 x 128 weight unit
+  static constexpr int A = 0;
+  static constexpr int A_SLOTS = BM * ROW / 16;              // 9 slots per row
+  static constexpr int AS = BM * ROW;                        // fp8: BM activation scales
+  static constexpr int W = AS + (KIND == Q_MXFP4 ? BM * 4 : 0);
+  static constexpr int REC = W + (BN / 16) * UNIT;           // W4A8 / MXFP4: 64 bytes per unit
+  static constexpr int BYTES = REC + (KIND == Q_W8A8 ? 0 : (BN / 16) * 64);
+};
+
+// Copies of group g into stage `st` (device-only builtins: kept out of any
+// lambda). A: slot q = 64 i + lane is row q / 9, 16-byte chunk q % 9 (chunk 8
+// is padding and re-reads chunk 0); a_off holds each slot's row offset.
+// RAW is not used here: it only gives every kernel instance its own
+// specialization (hipcc's host pass rejects a second kernel that calls the
+// same specialization of a device function using target builtins).
+template <int KIND, bool RAW, int BM, int BN, int NW>
+__device__ __forceinline__ void q_load_stage(char* st, const char* a_g, const uint32_t* a_off,
+                                             const uint32_t* as_off, const GemmArgs& p, const uint8_t* wbase,
+                                             const uint8_t* sbase, int wg_tile0, int wave, int lane, int g) {
+  using L = QStage<KIND, BM, BN>;
+  constexpr int A_INST = (L::A_SLOTS + 63) / 64;
+  const char* ag = a_g + (size_t)g * 128;
+#pragma unroll
+  for (int r = 0; r < (A_INST + NW - 1) / NW; ++r) {
+    const int i = r * NW + wave;
+    if (i < A_INST) __builtin_amdgcn_global_load_lds(ag + a_off[r], (lds_void*)(st + L::A + i * 1024), 16, 0, 0);
+  }
+  constexpr int W_INST = (BN / 16) * (L::UNIT / 1024);
+#pragma unroll
+  for (int r = 0; r < (W_INST + NW - 1) / NW; ++r) {
+    const int i = r * NW + wave;
+    if (i < W_INST) {
+      const int t = i / (L::UNIT / 1024), h = i % (L::UNIT / 1024);
+      // tiles past the layer re-read the last tile; their results are never stored
+      const int tile = min(wg_tile0 + t, p.ntiles - 1);
+      __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * L::UNIT + h * 1024 + lane * 16,
+                                       (lds_void*)(st + L::W + i * 1024), 16, 0, 0);
+    }
+  }
+  if constexpr (KIND != Q_W8A8) {
+    static_assert(BN / 16 * 64 == 1024, "one record copy per stage");
+    if (wave == NW - 1) {
+      const int tile = min(wg_tile0 + (lane >> 2), p.ntiles - 1);
+      __builtin_amdgcn_global_load_lds(sbase + ((size_t)tile * p.groups + g) * 64 + (lane & 3) * 16,
+                                       (lds_void*)(st + L::REC), 16, 0, 0);
+    }
+  }
+  if constexpr (KIND == Q_MXFP4) {
+    // activation scales a_scales[row][g], one dword per row
+#pragma unroll
+    for (int r = 0; r < BM / 64; ++r)
+      if (wave == r % NW)
+        __builtin_amdgcn_global_load_lds((const char*)p.a_scales + as_off[r] + (size_t)g * 4,
+                                         (lds_void*)(st + L::AS + r * 256), 4, 0, 0);
+  }
+}
+
+// One K group for a 64 x 64 wave tile (4 x 4 MFMA tiles of 16 x 16).
+template <int KIND, bool RAW, int BM, int BN, class Acc>
+__device__ __forceinline__ void q_group(const char* st, int a_lane, int w_lane, int rec_lane, int as_lane,
+                                        Acc (&acc)[4][4]) {
+  using L = QStage<KIND, BM, BN>;
+  u32x4_t b[4][2];
+  float ws[4];
+  int e8[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (KIND == Q_W8A8) {
+      b[t][0] = *(const u32x4_t*)(st + w_lane + t * 2048);
+      b[t][1] = *(const u32x4_t*)(st + w_lane + t * 2048 + 1024);
+    } else if constexpr (KIND == Q_W4A8) {
+      const u32x4_t x = *(const u32x4_t*)(st + w_lane + t * 1024);
+      const u32x2_t l0 = unpack_i4_i8x16(x.x), h0 = unpack_i4_i8x16(x.y);
+      const u32x2_t l1 = unpack_i4_i8x16(x.z), h1 = unpack_i4_i8x16(x.w);
+      b[t][0] = u32x4_t{l0.x, l0.y, h0.x, h0.y};
+      b[t][1] = u32x4_t{l1.x, l1.y, h1.x, h1.y};
+      ws[t] = *(const float*)(st + rec_lane + t * 64);
+    } else {
+      b[t][0] = *(const u32x4_t*)(st + w_lane + t * 1024);
+      e8[t] = *(const uint8_t*)(st + rec_lane + t * 64);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    u32x4_t a0, a1;
+    if constexpr (KIND == Q_MXFP4) {
+      // fp8 operand: lane group c holds K 16c..16c+15 and 64+16c..64+16c+15
+      a0 = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW);
+      a1 = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + 64);
+    } else {
+      // int8 operand: lane group c holds K 32c..32c+15 (step 0), +16 (step 1)
+      a0 = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW);
+      a1 = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + 16);
+    }
+    f32x4_t as;
+    if constexpr (KIND == Q_MXFP4) as = *(const f32x4_t*)(st + as_lane + mt * 64);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (KIND == Q_MXFP4) {
+        const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        const i32x8_t bv = {(int)b[t][0].x, (int)b[t][0].y, (int)b[t][0].z, (int)b[t][0].w, 0, 0, 0, 0};
+        const f32x4_t pr = mfma_fp8_fp4_scaled(av, bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 127, e8[t]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][t][i] = __builtin_fmaf(as[i], pr[i], acc[mt][t][i]);
+      } else if constexpr (KIND == Q_W8A8 || RAW) {
+        acc[mt][t] = mfma_i8(a1, b[t][1], mfma_i8(a0, b[t][0], acc[mt][t]));
+      } else {
+        const i32x4_t pr = mfma_i8(a1, b[t][1], mfma_i8(a0, b[t][0], i32x4_t{0, 0, 0, 0}));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][t][i] = __builtin_fmaf(ws[t], (float)pr[i], acc[mt][t][i]);
+      }
+    }
+  }
+}
+
+template <int KIND, bool RAW>
+struct QAcc {
+  using T = typename std::conditional<KIND == Q_W8A8 || RAW, i32x4_t, f32x4_t>::type;
+};
+
+template <int KIND, bool RAW, int NS>
+__global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m_blocks, int n_blocks) {
+  constexpr int WAVES_M = 2, WAVES_N = 4, NW = 8, WTM = 64;
+  constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
+  using L = QStage<KIND, BM, BN>;
+  using Acc = typename QAcc<KIND, RAW>::T;
+  constexpr int A_INST = (L::A_SLOTS + 63) / 64;
+  constexpr int A_PER_WAVE = (A_INST + NW - 1) / NW;
+  constexpr int W_INST = (BN / 16) * (L::UNIT / 1024);
+  // copies every wave has in flight per stage at least (A and weight units);
+  // waiting for the count to drop to this leaves the next stage in flight
+  constexpr int VM_NEXT = A_INST / NW + W_INST / NW;
+  static_assert(NS == 2 || NS == 3, "two or three stages");
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // [NS][L::BYTES]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int c = lane >> 4, col = lane & 15;
+
+  // XCD-aware tile order (consecutive workgroup ids go to different XCDs)
+  const int total = m_blocks * n_blocks;
+  int lin = blockIdx.x;
+  if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
+  const int mb = lin / n_blocks, nb = lin % n_blocks;
+  const int split = blockIdx.y, nsplit = gridDim.y;
+  const int g0 = (int)(((int64_t)split * p.groups) / nsplit);
+  const int g1 = (int)(((int64_t)(split + 1) * p.groups) / nsplit);
+
+  const uint8_t* wbase = p.packed;
+  const uint8_t* sbase = wbase + p.s_offset;
+  const int wg_tile0 = nb * (BN / 16);
+
+  uint32_t a_off[A_PER_WAVE];
+#pragma unroll
+  for (int r = 0; r < A_PER_WAVE; ++r) {
+    const int q = (r * NW + wave) * 64 + lane;
+    const int row = min(q / 9, BM - 1), ch = q % 9;
+    const int grow = mb * BM + row;
+    const int src = grow < p.M ? grow : p.M - 1;
+    a_off[r] = (uint32_t)src * (uint32_t)p.K + (uint32_t)(ch < 8 ? ch : 0) * 16;
+  }
+  uint32_t as_off[BM / 64];
+#pragma unroll
+  for (int r = 0; r < BM / 64; ++r) {
+    const int grow = mb * BM + r * 64 + lane;
+    const int src = grow < p.M ? grow : p.M - 1;
+    as_off[r] = (uint32_t)src * (uint32_t)p.groups * 4u;
+  }
+
+  // per-lane LDS offsets of the fragment reads inside a stage
+  const int a_lane = L::A + (wm * WTM + col) * L::ROW + (KIND == Q_MXFP4 ? 16 : 32) * c;
+  const int w_lane = L::W + (wn * 4) * L::UNIT + lane * 16;
+  const int rec_lane = L::REC + (wn * 4) * 64 + (KIND == Q_MXFP4 ? lane : col * 4);
+  const int as_lane = L::AS + (wm * WTM + 4 * c) * 4;
+
+  Acc acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[mt][t] = Acc{0, 0, 0, 0};
+
+  const char* a_g = (const char*)p.A;
+#pragma unroll
+  for (int q = 0; q < NS - 1; ++q)
+    if (g0 + q < g1)
+      q_load_stage<KIND, RAW, BM, BN, NW>(smem + q * L::BYTES, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane,
+                                     g0 + q);
+  int cur = 0;
+  for (int g = g0; g < g1; ++g) {
+    if (NS == 3 && g + 1 < g1)
+      __builtin_amdgcn_s_waitcnt((VM_NEXT & 15) | (7 << 4) | (15 << 8) | ((VM_NEXT >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // group g is in LDS for every wave; the stage of g-1 is free
+    if (g + NS - 1 < g1) {
+      int nxt = cur + NS - 1;
+      if (nxt >= NS) nxt -= NS;
+      q_load_stage<KIND, RAW, BM, BN, NW>(smem + nxt * L::BYTES, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave,
+                                     lane, g + NS - 1);
+    }
+    q_group<KIND, RAW, BM, BN>(smem + cur * L::BYTES, a_lane, w_lane, rec_lane, as_lane, acc);
+    cur = cur + 1 == NS ? 0 : cur + 1;
+  }
+
+  // ---- epilogue: scale, then per wave transpose each 16 x 64 strip through
+  // LDS so that every lane stores whole 16-byte row segments
+  __syncthreads();
+  const bool to_partial = nsplit > 1;
+  const int n_pad = n_blocks * BN;
+  const bool raw = p.otype == QDG_O_I32;
+  const bool f32out = to_partial || p.otype == QDG_O_F32 || raw;  // 4-byte elements
+  char* strip = smem + wave * (16 * 64 * 4);
+  const int nbase = (wg_tile0 + wn * 4) * 16;
+  const int esz = f32out ? 4 : 2;
+  const int cpr = 64 * esz / 16;  // 16-byte chunks per strip row
+  float wsc[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (KIND == Q_W8A8) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tile = min(wg_tile0 + wn * 4 + t, p.ntiles - 1);
+      wsc[t] = ((const float*)sbase)[tile * 16 + col];
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    float asc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int grow = mb * BM + wm * WTM + mt * 16 + 4 * c + i;
+      asc[i] = (KIND != Q_MXFP4 && !raw && grow < p.M) ? p.a_scales[grow] : 1.f;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = (4 * c + i) * 64 + t * 16 + col;
+        uint32_t bits;
+        if (raw) {
+          int v = bits_as<int>(acc[mt][t][i]);
+          if constexpr (KIND == Q_W4A8) v >>= 4;  // 16 q * qa: exact shift back
+          bits = (uint32_t)v;
+        } else {
+          float y;
+          if constexpr (KIND == Q_W8A8)
+            y = (float)acc[mt][t][i] * asc[i] * wsc[t];
+          else if constexpr (KIND == Q_W4A8)
+            y = acc[mt][t][i] * asc[i];
+          else
+            y = acc[mt][t][i];
+          bits = f32out ? __builtin_bit_cast(uint32_t, y) : f32_to_bf16_rne(y);
+        }
+        if (f32out)
+          ((uint32_t*)strip)[e] = bits;
+        else
+          ((uint16_t*)strip)[e] = (uint16_t)bits;
+      }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    for (int chunk = lane; chunk < 16 * cpr; chunk += 64) {
+      const int r = chunk / cpr, cc = chunk % cpr;
+      const int lrow = mb * BM + wm * WTM + mt * 16 + r;
+      const int per = 16 / esz;  // elements per chunk
+      const int n0 = nbase + cc * per;
+      const u32x4_t val = *(const u32x4_t*)(strip + r * 64 * esz + cc * 16);
+      if (to_partial) {
+        *(u32x4_t*)((float*)p.partial + ((size_t)split * p.m_pad + lrow) * n_pad + n0) = val;
+        continue;
+      }
+      if (lrow < p.M && n0 < p.N) {
+        char* dst = (char*)p.Y + ((size_t)lrow * p.N + n0) * esz;
+        if (n0 + per <= p.N && ((uintptr_t)dst & 15) == 0) {
+          *(u32x4_t*)dst = val;
+        } else if (f32out) {
+          for (int e = 0; e < per && n0 + e < p.N; ++e) ((uint32_t*)dst)[e] = val[e];
+        } else {
+          for (int e = 0; e < per && n0 + e < p.N; ++e)
+            ((uint16_t*)dst)[e] = (uint16_t)(val[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int KIND, bool RAW>
+hipError_t launch_q(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s) {
+  constexpr int BM = 128, BN = 256;
+  using L = QStage<KIND, BM, BN>;
+  constexpr int NS = 3 * L::BYTES <= 160 * 1024 ? 3 : 2;
+  const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
+  const size_t smem = NS * L::BYTES;
+  static bool attr_set = false;  // idempotent; a race only repeats the call
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qtile_gemm_kernel<KIND, RAW, NS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS>), dim3(m_blocks * n_blocks, nsplit), dim3(512), smem, s, a,
+                     m_blocks, n_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qtile(Format f, const GemmArgs& a, int m_blocks, hipStream_t s) {
+  const bool raw = a.otype == QDG_O_I32;
+  if (raw && a.split > 1) return hipErrorInvalidValue;  // integer partials are not split
+  switch (f) {
+    case FMT_W8A8: return raw ? launch_q<Q_W8A8, true>(a, m_blocks, 1, s) : launch_q<Q_W8A8, false>(a, m_blocks, a.split, s);
+    case FMT_W4A8: return raw ? launch_q<Q_W4A8, true>(a, m_blocks, 1, s) : launch_q<Q_W4A8, false>(a, m_blocks, a.split, s);
+    case FMT_MXFP4: return launch_q<Q_MXFP4, false>(a, m_blocks, a.split, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qdg

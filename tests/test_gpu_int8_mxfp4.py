@@ -24,8 +24,8 @@ def _act_int8(m, k, salt=0):
     return a, qa, sa
 
 
-def _run_int(layer, pk, qa, sa, m):
-    return H.gemm(layer, pk, H.dev(qa), m, a_scales=H.dev(sa))[0]
+def _run_int(layer, pk, qa, sa, m, tuning=None):
+    return H.gemm(layer, pk, H.dev(qa), m, a_scales=H.dev(sa), tuning=tuning)[0]
 
 
 # ------------------------------------------------------------ activations
@@ -179,3 +179,125 @@ def test_quantize_weights_bit_exact(qdg, kind):
         c, e = quant.quantize_mxfp4(w)
         assert np.array_equal(qw.cpu().numpy(), codecs.pack_nibbles(c))
         assert np.array_equal(sc.cpu().numpy(), e)
+
+
+# ------------------------------------------------------------ LDS-tiled family (M > 64)
+
+
+def _int_layer_data(kind, n, k, salt):
+    w = synth.weights_f32(n, k, workload_id=2, salt=salt)
+    if kind == "w8a8":
+        qw, sw = quant.quantize_int8_per_channel(w)
+        return dict(qw=qw, sw=sw, std=(H.dev(qw.astype(np.int8)), H.dev(sw)))
+    qv, s16 = quant.quantize_int4_sym(w)
+    qw_d, sc_d, _ = H.std_w4(qv, s16)
+    return dict(qv=qv, s16=s16, std=(qw_d, sc_d))
+
+
+def _int_ref(kind, d, qa, sa):
+    if kind == "w8a8":
+        return ref.gemm_w8a8(qa, sa, d["qw"], d["sw"])
+    return ref.gemm_w4a8(qa, sa, d["qv"], d["s16"])
+
+
+def _int_layer(kind, n, k, otype):
+    return q.layer_w8a8(n, k, otype=otype) if kind == "w8a8" else q.layer_w4a8(n, k, otype=otype)
+
+
+def _family(layer, m, tuning=None):
+    plan = q.qdg_plan_create(layer, q.dense(), tuning)
+    return q.qdg_plan_describe(plan, m).split("family=")[1].split()[0]
+
+
+@pytest.mark.parametrize("kind", ["w8a8", "w4a8"])
+@pytest.mark.parametrize("m,n,k", [(300, 200, 640), (129, 1040, 1024)])
+def test_int8_tiled_ragged(qdg, kind, m, n, k):
+    # ragged M (partial 128-row tiles), ragged N (a partial 256-column tile)
+    # and a split K range through the 8-bit tiled family (pinned by the
+    # tuning: at so few tiles the heuristic picks the streaming family)
+    d = _int_layer_data(kind, n, k, salt=m)
+    a, qa, sa = _act_int8(m, k, salt=m + 7)
+    y64, p = _int_ref(kind, d, qa, sa)
+    t = q.TuningConfig(block_m=128)
+    for otype in (q.QDG_O_I32, q.QDG_O_F32, q.QDG_O_BF16):
+        layer = _int_layer(kind, n, k, otype)
+        assert _family(layer, m, t) == "qtile"
+        pk = H.Packed(layer, *d["std"])
+        y = _run_int(layer, pk, qa, sa, m, tuning=t)
+        if otype == q.QDG_O_I32:
+            assert np.array_equal(y.cpu().numpy().astype(np.int64), p)
+        else:
+            err = metrics.rel_frob(H.to_f64(y), y64)
+            assert err <= (1e-3 if otype == q.QDG_O_F32 else 2e-3), err
+
+
+@pytest.mark.parametrize("kind", ["w8a8", "w4a8"])
+@pytest.mark.parametrize("n", [4096, 14336])
+def test_int8_full_size_sampled_rows(qdg, kind, n):
+    # M = 4096, K = 4096 as the benchmark runs it; the oracle checks 40
+    # sampled rows (every column); raw int32 must match exactly
+    m, k = 4096, 4096
+    d = _int_layer_data(kind, n, k, salt=n)
+    a, qa, sa = _act_int8(m, k, salt=5)
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(n).integers(0, m, 38)]))
+    y64, p = _int_ref(kind, d, qa[rows], sa[rows])
+    rows_d = torch.from_numpy(rows).cuda()
+    for otype in (q.QDG_O_I32, q.QDG_O_BF16):
+        layer = _int_layer(kind, n, k, otype)
+        pk = H.Packed(layer, *d["std"])
+        y = _run_int(layer, pk, qa, sa, m)
+        ys = y[rows_d]
+        if otype == q.QDG_O_I32:
+            assert np.array_equal(ys.cpu().numpy().astype(np.int64), p)
+        else:
+            err = metrics.rel_frob(H.to_f64(ys), y64)
+            print(f"{kind} M={m} K={k} N={n} sampled rows: rel_frob={err:.3e}")
+            assert err <= 2e-3, err
+            assert not torch.isnan(y.float()).any()
+
+
+@pytest.mark.parametrize("kind", ["w8a8", "w4a8", "mxfp4"])
+def test_tiled_8bit_split_k_deterministic(qdg, kind):
+    m, n, k = 256, 512, 2048
+    if kind == "mxfp4":
+        codes, e, ac, sa, y64 = _mxfp4_case(m, n, k, salt=31)
+        std = (H.dev(codecs.pack_nibbles(codes)), H.dev(e))
+        a_d, sa_d = H.dev(ac), H.dev(sa)
+        mk = lambda: q.layer_mxfp4(n, k, otype=q.QDG_O_F32)  # noqa: E731
+    else:
+        d = _int_layer_data(kind, n, k, salt=31)
+        a, qa, sa = _act_int8(m, k, salt=32)
+        y64, _ = _int_ref(kind, d, qa, sa)
+        std = d["std"]
+        a_d, sa_d = H.dev(qa), H.dev(sa)
+        mk = lambda: _int_layer(kind, n, k, q.QDG_O_F32)  # noqa: E731
+    outs = {}
+    for split in (1, 3, 8):
+        layer = mk()
+        t = q.TuningConfig(block_m=128, split_k=split)
+        assert _family(layer, m, t) == "qtile"
+        pk = H.Packed(layer, *std)
+        y1 = H.gemm(layer, pk, a_d, m, a_scales=sa_d, tuning=t)[0]
+        y2 = H.gemm(layer, pk, a_d, m, a_scales=sa_d, tuning=t)[0]
+        assert torch.equal(y1, y2), f"split {split} not deterministic"
+        assert metrics.rel_frob(H.to_f64(y1), y64) <= 1e-3
+        outs[split] = H.to_f64(y1)
+    assert np.allclose(outs[1], outs[8], rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("k,n", [(7168, 2048), (2048, 7168)])
+def test_mxfp4_full_size_sampled_rows(qdg, k, n):
+    m = 4096
+    codes, e, ac, sa, _ = _mxfp4_case(16, n, k, salt=41)  # weights only; A below
+    a = synth.activations_bf16_bits(m, k, workload_id=3, salt=42)
+    ac, sa = quant.quantize_act_fp8(a)
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(k).integers(0, m, 38)]))
+    y64 = ref.gemm_mxfp4(ac[rows], sa[rows], codes, e)
+    layer = q.layer_mxfp4(n, k)
+    assert _family(layer, m) == "qtile"
+    pk = H.Packed(layer, H.dev(codecs.pack_nibbles(codes)), H.dev(e))
+    y = H.gemm(layer, pk, H.dev(ac), m, a_scales=H.dev(sa))[0]
+    err = metrics.rel_frob(H.to_f64(y[torch.from_numpy(rows).cuda()]), y64)
+    print(f"MXFP4 M={m} K={k} N={n} sampled rows: rel_frob={err:.3e}")
+    assert err <= 2e-3, err
+    assert not torch.isnan(y.float()).any()
