@@ -30,6 +30,8 @@ M_SWEEP = [1, 16, 128, 1024, 8192]
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 CACHE_BYTES = 256 << 20
+COPY_CAL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_w4a16_dense.md")
 
 
 def alg_bytes(m, n, k):
@@ -39,6 +41,33 @@ def alg_bytes(m, n, k):
 
 def alg_flops(m, n, k):
     return 2 * m * n * k
+
+
+def kernel_source_sha(name):
+    import hashlib
+    with open(os.path.join(ROOT, "quantized_dequant_gemm_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(case, source):
+    """HBM bytes per launch of `case` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the copy calibration), or None
+    when there is none or the kernel source has changed since it was taken."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    sha = next((l.split(":", 1)[1].strip() for l in lines if l.startswith(f"source sha256 {source}:")), None)
+    if sha != kernel_source_sha(source):
+        return None
+    for l in lines:
+        cells = [c.strip() for c in l.strip().strip("|").split("|")]
+        if len(cells) >= 4 and cells[0] == case:
+            try:
+                return int(float(cells[3]))
+            except ValueError:
+                return None
+    return None
 
 
 def gpu_leg(args):
@@ -51,6 +80,12 @@ def gpu_leg(args):
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    if args.copy_calibration:
+        src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     layers = {}
     for (k, n) in SHAPES:
@@ -125,19 +160,22 @@ def gpu_leg(args):
                               instance=c["desc"].split(": ", 1)[1]))
     dom = max(out_cases, key=lambda d: d["us"])
     big = dom["M"] >= 128
+    case_name = f"M={dom['M']} K={dom['K']} N={dom['N']}"
+    traffic = measured_traffic(case_name, "tile_gemm.hip" if big else "wstream_gemm.hip")
     if big:
         roof = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(dom["tflops"] / PEAK_BF16_TFLOPS, 4), traffic=None,
+                    frac=round(dom["tflops"] / PEAK_BF16_TFLOPS, 4), traffic=traffic,
                     kernel=f"w4a16 M={dom['M']} K={dom['K']} N={dom['N']}",
                     per_launch=alg_flops(dom["M"], dom["N"], dom["K"]))
     else:
         roof = dict(bound="hbm", achieved=dom["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(dom["gbs"] / PEAK_HBM_GBS, 4), traffic=None,
+                    frac=round(dom["gbs"] / PEAK_HBM_GBS, 4), traffic=traffic,
                     kernel=f"w4a16 M={dom['M']} K={dom['K']} N={dom['N']}",
                     per_launch=alg_bytes(dom["M"], dom["N"], dom["K"]))
     m16 = [d for d in out_cases if d["M"] == 16]
     roof16 = [dict(bound="hbm", achieved=d["gbs"], peak=PEAK_HBM_GBS, unit="GB/s", frac=d["hbm_frac"],
-                   kernel=f"w4a16 M=16 K={d['K']} N={d['N']}", us=d["us"]) for d in m16]
+                   kernel=f"w4a16 M=16 K={d['K']} N={d['N']}", us=d["us"],
+                   traffic=measured_traffic(f"M=16 K={d['K']} N={d['N']}", "wstream_gemm.hip")) for d in m16]
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     return dict(value=value, ms_per_step=ms_per_step, roofline=roof, roofline_m16=roof16, cases=out_cases)
 
@@ -259,7 +297,7 @@ def rows_leg(reps=30):
         logits = torch.randn((t, E), generator=g, device=dev, dtype=torch.float32)
         ids = torch.topk(logits, top_k, dim=1).indices.to(torch.int32).contiguous()
         touched = int(torch.unique(ids).numel())
-        bm = 16 if t * top_k <= 32 * E else 64
+        bm = 16 if t * top_k <= 32 * E else 128
         cap = q.qdg_moe_align_capacity(t, top_k, E, bm)
         sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
         block_expert = torch.empty(cap // bm, dtype=torch.int32, device=dev)
@@ -328,6 +366,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-rows", action="store_true", help="skip the W8A8 / W4A8 / MXFP4 / MoE rows")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 256 MiB device to device once (the known-size reference that scales "
+                         "HBM byte counters in a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "

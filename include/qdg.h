@@ -231,7 +231,8 @@ qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int3
    r = i (a_per_pair = 1, e.g. the down projection) or r = i / top_k
    (a_per_pair = 0, e.g. gate+up reading token rows). Y is [T*top_k][n];
    rows are written only for real pairs. block_m must be the value passed to
-   qdg_moe_align and one the plan supports (see qdg_plan_describe). */
+   qdg_moe_align: 16 (weight-streaming family), 32 or 64 (streaming family)
+   or 128 (LDS-tiled family; batch-invariant plans take 16 to 64). */
 qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scales,
                         const void* packed, const int32_t* sorted_ids,
                         const int32_t* block_expert, const int32_t* num_padded, int64_t T,

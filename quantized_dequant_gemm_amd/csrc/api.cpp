@@ -269,7 +269,6 @@ Choice choose(const qdg_plan& P, int64_t M) {
   if (nblocks * ch.grid_m > kMaxCounters) split = 1;
   ch.sc.split = split;
   ch.partial_bytes = split > 1 ? (size_t)nblocks * ch.grid_m * split * ch.sc.mt * nt * 4 * 64 * 4 : 0;
-  ch.rowsum_bytes = 0;
   return ch;
 }
 
@@ -401,7 +400,14 @@ qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes) {
   if (!plan || !bytes) return fail(QDG_ERR_INVALID_ARG, "NULL plan or output");
   if (M < 0) return fail(QDG_ERR_INVALID_ARG, "M < 0");
   const Choice c = choose(*plan, M > 0 ? M : 1);
-  *bytes = kCounterBytes + align_up((int64_t)c.partial_bytes, 256) + align_up((int64_t)c.rowsum_bytes, 256);
+  int64_t rowsum = (int64_t)c.rowsum_bytes;
+  if (plan->compute.kind == QDG_KIND_MOE) {
+    // MoE: room for the row sums of 128-row blocks (the largest block size)
+    const int64_t cap =
+        align_up((M > 0 ? M : 1) * plan->compute.top_k + plan->layer.num_experts * 127, 128);
+    rowsum = cap * plan->geom.groups * 4;
+  }
+  *bytes = kCounterBytes + align_up((int64_t)c.partial_bytes, 256) + align_up(rowsum, 256);
   return ok();
 }
 
@@ -442,8 +448,22 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
     c.ws = block_m == 16 && !plan->compute.batch_invariant &&
            (!plan->has_tuning || ((!tu.block_n || tu.block_n == 64) && (!tu.waves || tu.waves == 8)));
     if (!c.ws && !c0.tile && c0.ws) c.sc = StreamCfg{block_m / 16, 2, 4, 1};
-    if (!c.ws && !stream_cfg_supported(plan->fmt, c.sc))
+    c.tile = false;
+    c.qtile = false;
+    if (block_m == 128) {
+      // 128-row blocks: the LDS-tiled family (128 x 256 tiles, one expert per
+      // row block); A rows are addressed with 32-bit byte offsets
+      const int64_t a_rows = a_per_pair ? rows : T;
+      if ((double)a_rows * (double)plan->layer.k * 2.0 >= 4294967296.0)
+        return fail(QDG_ERR_UNSUPPORTED, "A of %lld rows is too large for 128-row MoE blocks", (long long)a_rows);
+      if (plan->compute.batch_invariant)
+        return fail(QDG_ERR_UNSUPPORTED, "batch-invariant MoE plans use block_m <= 64");
+      c.tile = true;
+      c.ws = false;
+      c.tc = TileCfg{128, 256, 8};
+    } else if (!c.ws && !stream_cfg_supported(plan->fmt, c.sc)) {
       return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
+    }
   }
   size_t need = 0;
   qdg_plan_workspace(plan, M, &need);
@@ -487,8 +507,10 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
     a.m_pad = c.grid_m * c.tc.bm;
     float* rs = (float*)((char*)workspace + kCounterBytes + align_up((int64_t)c.partial_bytes, 256));
     a.rowsum = rs;
-    e = launch_rowsum(A, nullptr, nullptr, 0, 0, (int)rows, (int)M, a.K, a.m_pad, asym ? 1.0f : -136.0f, rs,
-                      stream);
+    e = moe ? launch_rowsum(A, sorted_ids, num_padded, a.top_k, a_per_pair, (int)rows, (int)M, a.K, a.m_pad,
+                            asym ? 1.0f : -136.0f, rs, stream)
+            : launch_rowsum(A, nullptr, nullptr, 0, 0, (int)rows, (int)M, a.K, a.m_pad, asym ? 1.0f : -136.0f, rs,
+                            stream);
     if (e != hipSuccess) return hip_status(e, "rowsum launch");
     e = launch_tile(plan->fmt, asym, moe, c.tc, a, c.grid_m, stream);
     if (e == hipSuccess && a.split > 1) {
@@ -557,8 +579,8 @@ qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scal
   if (plan->compute.kind != QDG_KIND_MOE) return fail(QDG_ERR_INVALID_ARG, "not a MoE plan");
   if (T < 0) return fail(QDG_ERR_INVALID_ARG, "T < 0");
   if (T == 0) return ok();
-  if (block_m != 16 && block_m != 32 && block_m != 64)
-    return fail(QDG_ERR_UNSUPPORTED, "grouped GEMM block_m must be 16, 32 or 64");
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128)
+    return fail(QDG_ERR_UNSUPPORTED, "grouped GEMM block_m must be 16, 32, 64 or 128");
   if (T * plan->compute.top_k > (1 << 20)) return fail(QDG_ERR_UNSUPPORTED, "T*top_k above 2^20");
   if (!A || !packed || !Y || !sorted_ids || !block_expert || !num_padded)
     return fail(QDG_ERR_INVALID_ARG, "NULL pointer");

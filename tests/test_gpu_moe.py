@@ -27,7 +27,7 @@ def _align_dev(ids, E, bm):
 
 
 @pytest.mark.parametrize("t", [1, 64, 512, 4096])
-@pytest.mark.parametrize("bm", [16, 32, 64])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
 def test_moe_align_bit_exact(qdg, t, bm):
     ids, _ = ref.route_topk(synth.router_logits(t, 256, salt=t), 8)
     sid, blk, npad, cap = _align_dev(ids, 256, bm)
@@ -72,7 +72,7 @@ def _moe_gemm(layer, pk, a_dev, ids, bm, a_per_pair, top_k):
     return y
 
 
-@pytest.mark.parametrize("t,bm", [(8, 16), (64, 16), (256, 32), (300, 64)])
+@pytest.mark.parametrize("t,bm", [(8, 16), (64, 16), (256, 32), (300, 64), (300, 128), (1024, 128)])
 def test_moe_gemm_small_experts(qdg, t, bm):
     # E=16 experts, top-4, hidden 1024 -> intermediate 2*256 (gate+up) and back
     E, top_k, hid, inter = 16, 4, 1024, 256
@@ -92,11 +92,12 @@ def test_moe_gemm_small_experts(qdg, t, bm):
     assert metrics.rel_frob(H.to_f64(yd), yd64) <= 2e-3
 
 
-@pytest.mark.parametrize("bm", [16, 32])
+@pytest.mark.parametrize("bm", [16, 32, 128])
 def test_moe_single_expert_equals_dense(qdg, bm):
     # everything routed to expert 0 of 2: the MoE blocks hold the same rows as
     # the dense GEMM run block by block with the same kernel family, so every
-    # output matches bitwise (16-row blocks: weight streaming; 32: streaming)
+    # output matches bitwise (16-row blocks: weight streaming; 32: streaming;
+    # 128: LDS-tiled)
     t, hid, n = 40, 512, 128
     qs, ss = _experts(2, n, hid, salt=3)
     layer, pk = _moe_packed(qs, ss, n, hid)
@@ -106,21 +107,25 @@ def test_moe_single_expert_equals_dense(qdg, bm):
     if bm == 16:
         t1 = q.TuningConfig(block_m=16, block_n=64, split_k=1)
         yd = torch.cat([H.w4a16(x[r:r + 16], qs[0], ss[0], None, tuning=t1) for r in range(0, t, 16)])
-    else:
+    elif bm == 32:
         t1 = q.TuningConfig(block_m=32, block_n=32, split_k=1)
+        yd = H.w4a16(x, qs[0], ss[0], None, tuning=t1)
+    else:
+        t1 = q.TuningConfig(block_m=128, split_k=1)
         yd = H.w4a16(x, qs[0], ss[0], None, tuning=t1)
     assert torch.equal(y, yd)
 
 
-def test_moe_full_size_sampled_rows(qdg):
-    # the real MoE shape (E=256, top-8, hidden 7168, gate+up N=4096), T=64;
-    # expert weights are quantized on the device, outputs checked on sampled pairs
-    E, top_k, hid, n, t = 256, 8, 7168, 4096, 64
+@pytest.mark.parametrize("t,bm", [(64, 16), (512, 128)])
+def test_moe_full_size_sampled_rows(qdg, t, bm):
+    # the real MoE shape (E=256, top-8, hidden 7168, gate+up N=4096); expert
+    # weights are quantized on the device, outputs checked on sampled pairs
+    E, top_k, hid, n = 256, 8, 7168, 4096
     layer = q.layer_w4a16(n, hid, num_experts=E)
     qw = torch.empty((E, n, hid // 2), dtype=torch.uint8, device="cuda")
     sc = torch.empty((E, n, hid // 128), dtype=torch.int16, device="cuda")
     ids, _ = ref.route_topk(synth.router_logits(t, E), top_k)
-    pairs = [0, 7, 100, 257, 511]
+    pairs = sorted({0, 7, 100, 257, t * top_k // 2 + 3, t * top_k - 1})
     sample_experts = sorted({int(ids.reshape(-1)[p]) for p in pairs})
     w_host = {}
     for e in range(E):
@@ -131,7 +136,7 @@ def test_moe_full_size_sampled_rows(qdg):
                                q.current_stream())
     pk = H.Packed(layer, qw, sc)
     x = synth.activations_bf16_bits(t, hid, workload_id=4)
-    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, 16, 0, top_k)
+    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 0, top_k)
     xf = codecs.bf16_bits_to_f64(x)
     for p in pairs:
         e = int(ids.reshape(-1)[p])
