@@ -44,7 +44,8 @@ struct QStage {
   static constexpr int AS = BM * ROW;                        // fp8: BM activation scales
   static constexpr int W = AS + (KIND == Q_MXFP4 ? BM * 4 : 0);
   static constexpr int REC = W + (BN / 16) * UNIT;           // W4A8 / MXFP4: 64 bytes per unit
-  static constexpr int BYTES = REC + (KIND == Q_W8A8 ? 0 : (BN / 16) * 64);
+  static constexpr int SCR = REC + (KIND == Q_W8A8 ? 0 : (BN / 16) * 64);  // 1 KiB sink for padding copies
+  static constexpr int BYTES = SCR + 1024;
 };
 
 // Copies of group g into stage `st` (device-only builtins: kept out of any
@@ -57,97 +58,115 @@ template <int KIND, bool RAW, int BM, int BN, int NW>
 __device__ __forceinline__ void q_load_stage(char* st, const char* a_g, const uint32_t* a_off,
                                              const uint32_t* as_off, const GemmArgs& p, const uint8_t* wbase,
                                              const uint8_t* sbase, int wg_tile0, int wave, int lane, int g) {
+  // Every wave issues the same sequence of copies (those past the stage's
+  // data re-read a valid address into the sink), without branches: the
+  // compiler can then count exactly which copies a later wait covers.
   using L = QStage<KIND, BM, BN>;
   constexpr int A_INST = (L::A_SLOTS + 63) / 64;
   const char* ag = a_g + (size_t)g * 128;
 #pragma unroll
   for (int r = 0; r < (A_INST + NW - 1) / NW; ++r) {
     const int i = r * NW + wave;
-    if (i < A_INST) __builtin_amdgcn_global_load_lds(ag + a_off[r], (lds_void*)(st + L::A + i * 1024), 16, 0, 0);
+    const int dst = i < A_INST ? L::A + i * 1024 : L::SCR;
+    __builtin_amdgcn_global_load_lds(ag + a_off[r], (lds_void*)(st + dst), 16, 0, 0);
   }
   constexpr int W_INST = (BN / 16) * (L::UNIT / 1024);
 #pragma unroll
   for (int r = 0; r < (W_INST + NW - 1) / NW; ++r) {
-    const int i = r * NW + wave;
-    if (i < W_INST) {
-      const int t = i / (L::UNIT / 1024), h = i % (L::UNIT / 1024);
-      // tiles past the layer re-read the last tile; their results are never stored
-      const int tile = min(wg_tile0 + t, p.ntiles - 1);
-      __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * L::UNIT + h * 1024 + lane * 16,
-                                       (lds_void*)(st + L::W + i * 1024), 16, 0, 0);
-    }
+    const int i = min(r * NW + wave, W_INST - 1);
+    const int dst = r * NW + wave < W_INST ? L::W + i * 1024 : L::SCR;
+    const int t = i / (L::UNIT / 1024), h = i % (L::UNIT / 1024);
+    // tiles past the layer re-read the last tile; their results are never stored
+    const int tile = min(wg_tile0 + t, p.ntiles - 1);
+    __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * L::UNIT + h * 1024 + lane * 16,
+                                     (lds_void*)(st + dst), 16, 0, 0);
   }
   if constexpr (KIND != Q_W8A8) {
     static_assert(BN / 16 * 64 == 1024, "one record copy per stage");
-    if (wave == NW - 1) {
-      const int tile = min(wg_tile0 + (lane >> 2), p.ntiles - 1);
-      __builtin_amdgcn_global_load_lds(sbase + ((size_t)tile * p.groups + g) * 64 + (lane & 3) * 16,
-                                       (lds_void*)(st + L::REC), 16, 0, 0);
-    }
+    const int tile = min(wg_tile0 + (lane >> 2), p.ntiles - 1);
+    __builtin_amdgcn_global_load_lds(sbase + ((size_t)tile * p.groups + g) * 64 + (lane & 3) * 16,
+                                     (lds_void*)(st + (wave == NW - 1 ? L::REC : L::SCR)), 16, 0, 0);
   }
   if constexpr (KIND == Q_MXFP4) {
     // activation scales a_scales[row][g], one dword per row
 #pragma unroll
     for (int r = 0; r < BM / 64; ++r)
-      if (wave == r % NW)
-        __builtin_amdgcn_global_load_lds((const char*)p.a_scales + as_off[r] + (size_t)g * 4,
-                                         (lds_void*)(st + L::AS + r * 256), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const char*)p.a_scales + as_off[r] + (size_t)g * 4,
+                                       (lds_void*)(st + (wave == r % NW ? L::AS + r * 256 : L::SCR)), 4, 0, 0);
   }
 }
 
-// One K group for a 64 x 64 wave tile (4 x 4 MFMA tiles of 16 x 16).
-template <int KIND, bool RAW, int BM, int BN, class Acc>
-__device__ __forceinline__ void q_group(const char* st, int a_lane, int w_lane, int rec_lane, int as_lane,
-                                        Acc (&acc)[4][4]) {
+// The LDS fragments one wave needs for one K group of its 64 x 64 tile
+// (4 x 4 MFMA tiles of 16 x 16).
+template <int KIND>
+struct QFrag {
+  u32x4_t a[4][2];  // A rows of the 4 row tiles (two 16-byte K slices)
+  u32x4_t b[4][2];  // weights of the 4 column tiles (W4A8: packed int4 in b[t][0])
+  float ws[4];      // W4A8: group scale s/16 of the lane's column
+  int e8[4];        // MXFP4: E8M0 block scale of the lane
+  f32x4_t as[4];    // MXFP4: activation scales of the lane's 4 rows
+};
+
+template <int KIND, int BM, int BN>
+__device__ __forceinline__ void q_frag_load(QFrag<KIND>& f, const char* st, int a_lane, int w_lane, int rec_lane,
+                                            int as_lane) {
   using L = QStage<KIND, BM, BN>;
-  u32x4_t b[4][2];
-  float ws[4];
-  int e8[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     if constexpr (KIND == Q_W8A8) {
-      b[t][0] = *(const u32x4_t*)(st + w_lane + t * 2048);
-      b[t][1] = *(const u32x4_t*)(st + w_lane + t * 2048 + 1024);
-    } else if constexpr (KIND == Q_W4A8) {
-      const u32x4_t x = *(const u32x4_t*)(st + w_lane + t * 1024);
-      const u32x2_t l0 = unpack_i4_i8x16(x.x), h0 = unpack_i4_i8x16(x.y);
-      const u32x2_t l1 = unpack_i4_i8x16(x.z), h1 = unpack_i4_i8x16(x.w);
-      b[t][0] = u32x4_t{l0.x, l0.y, h0.x, h0.y};
-      b[t][1] = u32x4_t{l1.x, l1.y, h1.x, h1.y};
-      ws[t] = *(const float*)(st + rec_lane + t * 64);
+      f.b[t][0] = *(const u32x4_t*)(st + w_lane + t * 2048);
+      f.b[t][1] = *(const u32x4_t*)(st + w_lane + t * 2048 + 1024);
     } else {
-      b[t][0] = *(const u32x4_t*)(st + w_lane + t * 1024);
-      e8[t] = *(const uint8_t*)(st + rec_lane + t * 64);
+      f.b[t][0] = *(const u32x4_t*)(st + w_lane + t * 1024);
+      if constexpr (KIND == Q_W4A8)
+        f.ws[t] = *(const float*)(st + rec_lane + t * 64);
+      else
+        f.e8[t] = *(const uint8_t*)(st + rec_lane + t * 64);
     }
   }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    u32x4_t a0, a1;
-    if constexpr (KIND == Q_MXFP4) {
-      // fp8 operand: lane group c holds K 16c..16c+15 and 64+16c..64+16c+15
-      a0 = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW);
-      a1 = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + 64);
+    // int8 operand: lane group c holds K 32c..32c+15 (step 0) and +16 (step 1);
+    // fp8 operand: K 16c..16c+15 and 64+16c..64+16c+15
+    f.a[mt][0] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW);
+    f.a[mt][1] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + (KIND == Q_MXFP4 ? 64 : 16));
+    if constexpr (KIND == Q_MXFP4) f.as[mt] = *(const f32x4_t*)(st + as_lane + mt * 64);
+  }
+}
+
+template <int KIND, bool RAW, class Acc>
+__device__ __forceinline__ void q_frag_compute(const QFrag<KIND>& f, Acc (&acc)[4][4]) {
+  u32x4_t b[4][2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (KIND == Q_W4A8) {
+      const u32x4_t x = f.b[t][0];
+      const u32x2_t l0 = unpack_i4_i8x16(x.x), h0 = unpack_i4_i8x16(x.y);
+      const u32x2_t l1 = unpack_i4_i8x16(x.z), h1 = unpack_i4_i8x16(x.w);
+      b[t][0] = u32x4_t{l0.x, l0.y, h0.x, h0.y};
+      b[t][1] = u32x4_t{l1.x, l1.y, h1.x, h1.y};
     } else {
-      // int8 operand: lane group c holds K 32c..32c+15 (step 0), +16 (step 1)
-      a0 = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW);
-      a1 = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + 16);
+      b[t][0] = f.b[t][0];
+      b[t][1] = f.b[t][1];
     }
-    f32x4_t as;
-    if constexpr (KIND == Q_MXFP4) as = *(const f32x4_t*)(st + as_lane + mt * 64);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if constexpr (KIND == Q_MXFP4) {
+        const u32x4_t a0 = f.a[mt][0], a1 = f.a[mt][1];
         const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
         const i32x8_t bv = {(int)b[t][0].x, (int)b[t][0].y, (int)b[t][0].z, (int)b[t][0].w, 0, 0, 0, 0};
-        const f32x4_t pr = mfma_fp8_fp4_scaled(av, bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 127, e8[t]);
+        const f32x4_t pr = mfma_fp8_fp4_scaled(av, bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 127, f.e8[t]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][t][i] = __builtin_fmaf(as[i], pr[i], acc[mt][t][i]);
+        for (int i = 0; i < 4; ++i) acc[mt][t][i] = __builtin_fmaf(f.as[mt][i], pr[i], acc[mt][t][i]);
       } else if constexpr (KIND == Q_W8A8 || RAW) {
-        acc[mt][t] = mfma_i8(a1, b[t][1], mfma_i8(a0, b[t][0], acc[mt][t]));
+        acc[mt][t] = mfma_i8(f.a[mt][1], b[t][1], mfma_i8(f.a[mt][0], b[t][0], acc[mt][t]));
       } else {
-        const i32x4_t pr = mfma_i8(a1, b[t][1], mfma_i8(a0, b[t][0], i32x4_t{0, 0, 0, 0}));
+        const i32x4_t pr = mfma_i8(f.a[mt][1], b[t][1], mfma_i8(f.a[mt][0], b[t][0], i32x4_t{0, 0, 0, 0}));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][t][i] = __builtin_fmaf(ws[t], (float)pr[i], acc[mt][t][i]);
+        for (int i = 0; i < 4; ++i) acc[mt][t][i] = __builtin_fmaf(f.ws[t], (float)pr[i], acc[mt][t][i]);
       }
     }
   }
@@ -167,22 +186,40 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
   constexpr int A_INST = (L::A_SLOTS + 63) / 64;
   constexpr int A_PER_WAVE = (A_INST + NW - 1) / NW;
   constexpr int W_INST = (BN / 16) * (L::UNIT / 1024);
-  // copies every wave has in flight per stage at least (A and weight units);
-  // waiting for the count to drop to this leaves the next stage in flight
-  constexpr int VM_NEXT = A_INST / NW + W_INST / NW;
+  // copies every wave issues per stage; waiting for the count to drop to
+  // this leaves the next stage in flight
+  constexpr int VM_NEXT = (A_INST + NW - 1) / NW + (W_INST + NW - 1) / NW + (KIND != Q_W8A8 ? 1 : 0) +
+                          (KIND == Q_MXFP4 ? BM / 64 : 0);
   static_assert(NS == 2 || NS == 3, "two or three stages");
-  extern __shared__ __attribute__((aligned(16))) char smem[];  // [NS][L::BYTES]
+  // The stages are separate LDS objects (not one dynamic array) so that the
+  // compiler can tell a copy into one stage from a read of another: reads of
+  // stage s then wait only for the copies of stage s.
+  __shared__ __attribute__((aligned(1024))) char st0[L::BYTES];
+  __shared__ __attribute__((aligned(1024))) char st1[L::BYTES];
+  __shared__ __attribute__((aligned(1024))) char st2[NS == 3 ? L::BYTES : 16];
+  char* const stage[3] = {st0, st1, st2};
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int c = lane >> 4, col = lane & 15;
 
-  // XCD-aware tile order (consecutive workgroup ids go to different XCDs)
+  // XCD-aware tile order: consecutive workgroup ids go to different XCDs,
+  // so XCD x takes the x-th eighth of the tile order; that order walks 4 x 8
+  // blocks of tiles, so the 32 tiles an XCD runs at once share 4 row blocks
+  // of A and 8 column blocks of W in its L2
   const int total = m_blocks * n_blocks;
   int lin = blockIdx.x;
+  int mb, nb;
   if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
-  const int mb = lin / n_blocks, nb = lin % n_blocks;
+  if (m_blocks % 4 == 0 && n_blocks % 8 == 0) {
+    const int sb = lin / 32, w = lin % 32;
+    mb = (sb / (n_blocks / 8)) * 4 + w / 8;
+    nb = (sb % (n_blocks / 8)) * 8 + w % 8;
+  } else {
+    mb = lin / n_blocks;
+    nb = lin % n_blocks;
+  }
   const int split = blockIdx.y, nsplit = gridDim.y;
   const int g0 = (int)(((int64_t)split * p.groups) / nsplit);
   const int g1 = (int)(((int64_t)(split + 1) * p.groups) / nsplit);
@@ -221,36 +258,53 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
     for (int t = 0; t < 4; ++t) acc[mt][t] = Acc{0, 0, 0, 0};
 
   const char* a_g = (const char*)p.A;
+  // NS-stage ring. Full rounds of NS groups run unrolled with constant stage
+  // indices and unconditional copies (past the range they re-read the last
+  // group into a stage nobody reads again), so that the compiler's waits
+  // before LDS reads stay exact; the last partial round waits for all copies.
 #pragma unroll
   for (int q = 0; q < NS - 1; ++q)
-    if (g0 + q < g1)
-      q_load_stage<KIND, RAW, BM, BN, NW>(smem + q * L::BYTES, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane,
-                                     g0 + q);
-  int cur = 0;
-  for (int g = g0; g < g1; ++g) {
-    if (NS == 3 && g + 1 < g1)
+    q_load_stage<KIND, RAW, BM, BN, NW>(stage[q], a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane,
+                                        min(g0 + q, g1 - 1));
+  QFrag<KIND> fr;
+  int gb = g0;
+  for (; gb + NS <= g1; gb += NS) {
+#pragma unroll
+    for (int cur = 0; cur < NS; ++cur) {
+      // this wave's copies of group gb+cur are done once at most the copies
+      // of one later group remain in flight (copies complete in order)
       __builtin_amdgcn_s_waitcnt((VM_NEXT & 15) | (7 << 4) | (15 << 8) | ((VM_NEXT >> 4) << 14));
-    else
-      __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // group g is in LDS for every wave; the stage of g-1 is free
-    if (g + NS - 1 < g1) {
-      int nxt = cur + NS - 1;
-      if (nxt >= NS) nxt -= NS;
-      q_load_stage<KIND, RAW, BM, BN, NW>(smem + nxt * L::BYTES, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave,
-                                     lane, g + NS - 1);
+      // every wave's copies of the group landed; the stage of the previous
+      // group is free. A bare s_barrier: __syncthreads would also wait for
+      // the copies in flight.
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+      q_load_stage<KIND, RAW, BM, BN, NW>(stage[(cur + NS - 1) % NS], a_g, a_off, as_off, p, wbase, sbase,
+                                          wg_tile0, wave, lane, min(gb + cur + NS - 1, g1 - 1));
+      q_frag_load<KIND, BM, BN>(fr, stage[cur], a_lane, w_lane, rec_lane, as_lane);
+      q_frag_compute<KIND, RAW>(fr, acc);
     }
-    q_group<KIND, RAW, BM, BN>(smem + cur * L::BYTES, a_lane, w_lane, rec_lane, as_lane, acc);
-    cur = cur + 1 == NS ? 0 : cur + 1;
+  }
+#pragma unroll
+  for (int cur = 0; cur < NS - 1; ++cur) {
+    if (gb + cur < g1) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      q_frag_load<KIND, BM, BN>(fr, stage[cur], a_lane, w_lane, rec_lane, as_lane);
+      q_frag_compute<KIND, RAW>(fr, acc);
+    }
   }
 
   // ---- epilogue: scale, then per wave transpose each 16 x 64 strip through
   // LDS so that every lane stores whole 16-byte row segments
+  __builtin_amdgcn_s_waitcnt(0);  // the trailing copies have landed
   __syncthreads();
   const bool to_partial = nsplit > 1;
   const int n_pad = n_blocks * BN;
   const bool raw = p.otype == QDG_O_I32;
   const bool f32out = to_partial || p.otype == QDG_O_F32 || raw;  // 4-byte elements
-  char* strip = smem + wave * (16 * 64 * 4);
+  char* strip = st0 + wave * (16 * 64 * 4);
+  static_assert(NW * 16 * 64 * 4 <= L::BYTES, "epilogue strips fit one stage");
   const int nbase = (wg_tile0 + wn * 4) * 16;
   const int esz = f32out ? 4 : 2;
   const int cpr = 64 * esz / 16;  // 16-byte chunks per strip row
@@ -329,15 +383,7 @@ hipError_t launch_q(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s) 
   using L = QStage<KIND, BM, BN>;
   constexpr int NS = 3 * L::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-  const size_t smem = NS * L::BYTES;
-  static bool attr_set = false;  // idempotent; a race only repeats the call
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qtile_gemm_kernel<KIND, RAW, NS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS>), dim3(m_blocks * n_blocks, nsplit), dim3(512), smem, s, a,
+  hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS>), dim3(m_blocks * n_blocks, nsplit), dim3(512), 0, s, a,
                      m_blocks, n_blocks);
   return hipGetLastError();
 }
