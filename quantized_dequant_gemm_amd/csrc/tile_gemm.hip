@@ -229,12 +229,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   const int c = lane >> 4, col = lane & 15;
 
   // XCD-aware tile order: consecutive workgroup ids land on different XCDs,
-  // so each XCD gets a contiguous range of tiles (row-major over N blocks)
-  // and the A rows its CUs share stay in that XCD's L2.
+  // so XCD x takes the x-th eighth of the tile order; that order walks 4 x 8
+  // blocks of tiles, so the tiles an XCD runs at once share row blocks of A
+  // and column blocks of W in its L2
   const int total = m_blocks * n_blocks;
   int lin = blockIdx.x;
   if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
-  const int mb = lin / n_blocks, nb = lin % n_blocks;
+  int mb, nb;
+  if (m_blocks % 4 == 0 && n_blocks % 8 == 0) {
+    const int sb = lin / 32, w = lin % 32;
+    mb = (sb / (n_blocks / 8)) * 4 + w / 8;
+    nb = (sb % (n_blocks / 8)) * 8 + w % 8;
+  } else {
+    mb = lin / n_blocks;
+    nb = lin % n_blocks;
+  }
   // split-K: this workgroup reduces K groups [g0, g1) of the tile
   const int split = blockIdx.y, nsplit = gridDim.y;
   const int g0 = (int)(((int64_t)split * p.groups) / nsplit);
