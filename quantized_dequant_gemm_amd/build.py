@@ -17,7 +17,8 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqdg.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "preprocess.hip", "actquant.hip", "moe_align.hip", "stream_gemm.hip", "tile_gemm.hip", "wstream_gemm.hip", "qtile_gemm.hip"]
+SOURCES = ["api.cpp", "preprocess.hip", "actquant.hip", "moe_align.hip", "stream_gemm.hip", "tile_gemm.hip", "wstream_gemm.hip", "qtile_gemm.hip",
+           "wstream8_gemm.hip"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -223,6 +223,24 @@ Choice choose(const qdg_plan& P, int64_t M) {
     ch.partial_bytes = split > 1 ? (size_t)split * 16 * g.ntiles * 16 * 4 : 0;
     return ch;
   }
+  // weight-streaming family of the int8 / fp8 formats (dense M <= 16): the
+  // K range of a workgroup must fit its LDS; raw int32 output is not split
+  if (bm == 16 && P.fmt != FMT_W4A16 && !moe && !P.compute.batch_invariant && ws_tuning_ok) {
+    const int64_t nblocks = (g.ntiles + 3) / 4;
+    const int min_split = (int)((g.groups + wstream8_max_groups() - 1) / wstream8_max_groups());
+    int split = P.has_tuning && T.split_k ? T.split_k : (int)(kWsTargetWorkgroups / nblocks);
+    if (split < min_split) split = min_split;
+    if (split < 1) split = 1;
+    if (split > g.groups) split = (int)g.groups;
+    if (P.layer.otype == QDG_O_I32) split = min_split;
+    if (P.layer.otype != QDG_O_I32 || split == 1) {
+      ch.ws = true;
+      ch.grid_m = 1;
+      ch.sc = StreamCfg{1, 4, 8, split};
+      ch.partial_bytes = split > 1 ? (size_t)split * 16 * g.ntiles * 16 * 4 : 0;
+      return ch;
+    }
+  }
   // LDS-tiled family of the int8 / fp8 formats: 128 x 256 tiles, used once
   // there are enough of them (or M >= 512) to beat the streaming family
   const bool a8_fits = (double)(M > 0 ? M : 1) * (double)g.k < 4294967296.0;
@@ -518,7 +536,8 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
       e = launch_reduce_splits(a, a.m_pad, n_pad, stream);
     }
   } else if (c.ws) {
-    e = launch_wstream(asym, moe, a, c.sc.split, c.grid_m, stream);
+    e = plan->fmt == FMT_W4A16 ? launch_wstream(asym, moe, a, c.sc.split, c.grid_m, stream)
+                               : launch_wstream8(plan->fmt, a, c.sc.split, stream);
   } else {
     e = launch_stream(plan->fmt, asym, moe, c.sc, a, c.grid_m, stream);
   }

@@ -301,3 +301,57 @@ def test_mxfp4_full_size_sampled_rows(qdg, k, n):
     print(f"MXFP4 M={m} K={k} N={n} sampled rows: rel_frob={err:.3e}")
     assert err <= 2e-3, err
     assert not torch.isnan(y.float()).any()
+
+
+# ------------------------------------------------------------ weight streaming (M <= 16)
+
+
+def _any_case(kind, m, n, k, salt):
+    """(layer maker, std tensors, A codes, A scales, Y64, raw P or None)."""
+    if kind == "mxfp4":
+        codes, e, ac, sa, y64 = _mxfp4_case(m, n, k, salt=salt)
+        return (lambda o: q.layer_mxfp4(n, k, otype=o)), (H.dev(codecs.pack_nibbles(codes)), H.dev(e)), ac, sa, y64, None
+    d = _int_layer_data(kind, n, k, salt=salt)
+    a, qa, sa = _act_int8(m, k, salt=salt + 1)
+    y64, p = _int_ref(kind, d, qa, sa)
+    return (lambda o: _int_layer(kind, n, k, o)), d["std"], qa, sa, y64, p
+
+
+@pytest.mark.parametrize("kind", ["w8a8", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (3, 272, 1152), (16, 1040, 8320)])
+def test_8bit_weight_streaming(qdg, kind, m, n, k):
+    # M <= 16 through the weight-streaming family: one row, a ragged tile
+    # count with a short K, and K = 8320 (65 groups: more than one workgroup
+    # holds, so K is split at least in two)
+    mk, std, ac, sa, y64, p = _any_case(kind, m, n, k, salt=50 + m)
+    otypes = (q.QDG_O_F32, q.QDG_O_BF16) if kind == "mxfp4" else (q.QDG_O_I32, q.QDG_O_F32, q.QDG_O_BF16)
+    for otype in otypes:
+        layer = mk(otype)
+        fam = _family(layer, m)
+        raw = otype == q.QDG_O_I32
+        assert fam == ("stream" if raw and k > 8192 else "wstream"), fam
+        pk = H.Packed(layer, *std)
+        y = H.gemm(layer, pk, H.dev(ac), m, a_scales=H.dev(sa))[0]
+        if raw:
+            assert np.array_equal(y.cpu().numpy().astype(np.int64), p)
+        else:
+            err = metrics.rel_frob(H.to_f64(y), y64)
+            assert err <= (1e-3 if otype == q.QDG_O_F32 else 2e-3), (otype, err)
+
+
+@pytest.mark.parametrize("kind", ["w8a8", "w4a8", "mxfp4"])
+def test_8bit_weight_streaming_split_k(qdg, kind):
+    m, n, k = 16, 512, 4096
+    mk, std, ac, sa, y64, _ = _any_case(kind, m, n, k, salt=61)
+    outs = {}
+    for split in (1, 3, 32):
+        layer = mk(q.QDG_O_F32)
+        t = q.TuningConfig(split_k=split)
+        assert _family(layer, m, t) == "wstream"
+        pk = H.Packed(layer, *std)
+        y1 = H.gemm(layer, pk, H.dev(ac), m, a_scales=H.dev(sa), tuning=t)[0]
+        y2 = H.gemm(layer, pk, H.dev(ac), m, a_scales=H.dev(sa), tuning=t)[0]
+        assert torch.equal(y1, y2), f"split {split} not deterministic"
+        assert metrics.rel_frob(H.to_f64(y1), y64) <= 1e-3
+        outs[split] = H.to_f64(y1)
+    assert np.allclose(outs[1], outs[32], rtol=1e-5, atol=1e-4)
