@@ -226,9 +226,12 @@ Choice choose(const qdg_plan& P, int64_t M) {
   // weight-streaming family of the int8 / fp8 formats (dense M <= 16): the
   // K range of a workgroup must fit its LDS; raw int32 output is not split
   if (bm == 16 && P.fmt != FMT_W4A16 && !moe && !P.compute.batch_invariant && ws_tuning_ok) {
-    const int64_t nblocks = (g.ntiles + 3) / 4;
+    // 4 N tiles per workgroup when that gives enough workgroups, else one
+    // tile with all 8 waves on its K range (no split across workgroups)
+    const int nt = (g.ntiles + 3) / 4 >= 128 ? 4 : 1;
+    const int64_t nblocks = (g.ntiles + nt - 1) / nt;
     const int min_split = (int)((g.groups + wstream8_max_groups() - 1) / wstream8_max_groups());
-    int split = P.has_tuning && T.split_k ? T.split_k : (int)(kWsTargetWorkgroups / nblocks);
+    int split = P.has_tuning && T.split_k ? T.split_k : (nblocks >= 128 ? 1 : (int)(kWsTargetWorkgroups / nblocks));
     if (split < min_split) split = min_split;
     if (split < 1) split = 1;
     if (split > g.groups) split = (int)g.groups;
@@ -236,7 +239,7 @@ Choice choose(const qdg_plan& P, int64_t M) {
     if (P.layer.otype != QDG_O_I32 || split == 1) {
       ch.ws = true;
       ch.grid_m = 1;
-      ch.sc = StreamCfg{1, 4, 8, split};
+      ch.sc = StreamCfg{1, nt, 8, split};
       ch.partial_bytes = split > 1 ? (size_t)split * 16 * g.ntiles * 16 * 4 : 0;
       return ch;
     }
@@ -537,7 +540,7 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
     }
   } else if (c.ws) {
     e = plan->fmt == FMT_W4A16 ? launch_wstream(asym, moe, a, c.sc.split, c.grid_m, stream)
-                               : launch_wstream8(plan->fmt, a, c.sc.split, stream);
+                               : launch_wstream8(plan->fmt, a, c.sc.split, c.sc.nt, stream);
   } else {
     e = launch_stream(plan->fmt, asym, moe, c.sc, a, c.grid_m, stream);
   }

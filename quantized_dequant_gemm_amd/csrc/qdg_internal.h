@@ -68,7 +68,7 @@ hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const Ge
 hipError_t launch_reduce_splits(const GemmArgs& a, int m_pad, int n_pad, hipStream_t s);
 hipError_t launch_wstream(bool asym, bool moe, const GemmArgs& a, int nsplit, int grid_m, hipStream_t s);
 hipError_t launch_qtile(Format f, const GemmArgs& a, int m_blocks, hipStream_t s);
-hipError_t launch_wstream8(Format f, const GemmArgs& a, int nsplit, hipStream_t s);
+hipError_t launch_wstream8(Format f, const GemmArgs& a, int nsplit, int nt, hipStream_t s);
 int wstream8_max_groups();
 bool stream_cfg_supported(Format f, const StreamCfg& c);
 bool tile_cfg_supported(Format f, const TileCfg& c);

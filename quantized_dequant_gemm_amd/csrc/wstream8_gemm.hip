@@ -25,19 +25,20 @@ namespace {
 
 enum W8Kind { K_W8A8 = 0, K_W4A8 = 1, K_MXFP4 = 2 };
 
-constexpr int NT = 4;                    // N tiles per workgroup
-constexpr int KW = 2;                    // K halves
-constexpr int WAVES = NT * KW;           // 8
+// A workgroup has 8 waves: NT N tiles x KW = 8 / NT parts of its K range
+// (NT = 4 for wide layers; NT = 1 when there are too few tiles to occupy the
+// CUs, which avoids splitting K across workgroups).
+constexpr int WAVES = 8;
 constexpr int RG = 64;                   // groups per workgroup at most
-constexpr int RGW = RG / KW;             // per wave (32)
 constexpr int PITCH = RG * 128 + 16;     // 8208-byte LDS rows of A
 constexpr int L_A = 16 * PITCH;
 constexpr int RAL = RG * 128 / 1024;     // 16-byte loads per lane per A row (8)
-constexpr int L_REC = L_A;               // per wave: RGW groups x 64 bytes of records
-constexpr int L_AS = L_REC + WAVES * RGW * 64;  // fp8: [group][16 rows] activation scales
+constexpr int REC_W = 2048;              // per wave: up to 32 groups x 64 bytes of records
+constexpr int L_REC = L_A;
+constexpr int L_AS = L_REC + WAVES * REC_W;  // fp8: [group][16 rows] activation scales
 constexpr int L_BYTES = L_AS + RG * 16 * 4;
 static_assert(L_BYTES <= 160 * 1024, "fits the LDS of one CU");
-static_assert(RGW * 64 == 2 * 1024, "two record loads per wave");
+static_assert(7 * 256 * 4 <= L_A, "the K-part exchange fits the A area");
 
 __shared__ __attribute__((aligned(1024))) char w8_lds[L_BYTES];
 
@@ -51,8 +52,12 @@ struct W8Acc {
   using T = typename std::conditional<KIND == K_W8A8 || RAW, i32x4_t, f32x4_t>::type;
 };
 
-template <int KIND, bool RAW>
+template <int KIND, bool RAW, int NT>
 __global__ __launch_bounds__(512) void wsr8_kernel(const GemmArgs p) {
+  constexpr int KW = WAVES / NT;              // K parts
+  constexpr int RGW = RG / KW;                // groups per wave at most
+  constexpr int SRL = (RGW * 64 + 1023) / 1024;  // record loads per lane
+  static_assert(RGW * 64 <= REC_W, "records of a wave fit its LDS slice");
   constexpr int UL = KIND == K_W8A8 ? 2 : 1;  // 16-byte loads per lane per weight unit
   constexpr int UB = UL * 1024;               // bytes per unit
   constexpr int RU = 8 / UL;                  // units in flight per wave (8 loads)
@@ -71,9 +76,11 @@ __global__ __launch_bounds__(512) void wsr8_kernel(const GemmArgs p) {
   const int g0 = (int)(((int64_t)split * groups) / gridDim.y);
   const int g1 = (int)(((int64_t)(split + 1) * groups) / gridDim.y);
   const int gsz = g1 - g0;  // <= RG (checked by the host)
-  const int half = (gsz + 1) / 2;
-  const int hg0 = g0 + kp * half;  // this wave's groups [hg0, hg0 + cnt)
-  const int cnt = min(half, g1 - hg0);
+  const int per = (gsz + KW - 1) / KW;
+  const int hg0 = g0 + kp * per;  // this wave's groups [hg0, hg0 + cnt); cnt may be <= 0
+  const int cnt = min(per, g1 - hg0);
+  // unit u of this wave reads group wg(u) (past cnt: a valid group, unused)
+  auto wg = [&](int u) { return max(min(hg0 + min(u, cnt - 1), g1 - 1), g0); };
   const int rows_used = p.M < 16 ? p.M : 16;
 
   // ---- prologue: A rows 2w, 2w+1 (rows that do not exist are not loaded:
@@ -93,13 +100,13 @@ __global__ __launch_bounds__(512) void wsr8_kernel(const GemmArgs p) {
       }
     }
   }
-  u32x4_t sr[2];
+  u32x4_t sr[SRL];
   if constexpr (KIND != K_W8A8) {
     // records of unit (tile, group): 64 bytes (W4A8: 16 x f32 s/16; MXFP4: E8M0 per lane)
     const uint8_t* srec = sbase + (size_t)ltile * groups * 64;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int g = min(hg0 + (k * 64 + lane) / 4, g1 - 1);
+    for (int k = 0; k < SRL; ++k) {
+      const int g = wg((k * 64 + lane) / 4);
       sr[k] = *(const u32x4_t*)(srec + (size_t)g * 64 + (lane & 3) * 16);
     }
   }
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(512) void wsr8_kernel(const GemmArgs p) {
   u32x4_t ring[RU][UL];
 #pragma unroll
   for (int u = 0; u < RU; ++u) {
-    const int g = hg0 + (u < cnt ? u : cnt - 1);
+    const int g = wg(u);
 #pragma unroll
     for (int h = 0; h < UL; ++h) ring[u][h] = ldg_nt((const u32x4_t*)(wt + (size_t)g * UB + h * 1024));
   }
@@ -128,7 +135,8 @@ __global__ __launch_bounds__(512) void wsr8_kernel(const GemmArgs p) {
   }
   if constexpr (KIND != K_W8A8) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) *(u32x4_t*)(w8_lds + L_REC + wave * 2048 + k * 1024 + lane * 16) = sr[k];
+    for (int k = 0; k < SRL; ++k)
+      if (k * 1024 + lane * 16 < REC_W) *(u32x4_t*)(w8_lds + L_REC + wave * REC_W + k * 1024 + lane * 16) = sr[k];
   }
   if constexpr (KIND == K_MXFP4) {
 #pragma unroll
@@ -139,7 +147,7 @@ __global__ __launch_bounds__(512) void wsr8_kernel(const GemmArgs p) {
   // ---- the ring: unit u is computed, then unit u + RU takes its registers;
   // every unit is computed (straight-line code keeps the load waits exact)
   // and units past cnt (in-bounds re-reads, finite) are dropped by a select
-  const char* recs = w8_lds + L_REC + wave * 2048;
+  const char* recs = w8_lds + L_REC + wave * REC_W;
   Acc acc = {0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < RGW; ++u) {
@@ -177,29 +185,33 @@ __global__ __launch_bounds__(512) void wsr8_kernel(const GemmArgs p) {
       for (int e = 0; e < 4; ++e) acc[e] = valid ? __builtin_fmaf(as[e], pr[e], acc[e]) : acc[e];
     }
     if (u + RU < RGW) {
-      const int g = hg0 + (u + RU < cnt ? u + RU : cnt - 1);
+      const int g = wg(u + RU);
 #pragma unroll
       for (int h = 0; h < UL; ++h) ring[u % RU][h] = ldg_nt((const u32x4_t*)(wt + (size_t)g * UB + h * 1024));
     }
   }
 
-  // ---- add the two K halves in a fixed order: half 1 parks its sums in LDS
+  // ---- add the K parts in a fixed order: parts 1..KW-1 park their sums in
+  // LDS, part 0 adds them in order
   __syncthreads();
-  uint32_t* park = (uint32_t*)w8_lds;  // [NT][16 rows][16 cols]
-  if (kp == 1) {
+  uint32_t* park = (uint32_t*)w8_lds;  // [KW-1][NT][16 rows][16 cols]
+  if (kp > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) park[(t * 16 + 4 * c + e) * 16 + col] = bits_as<uint32_t>(acc[e]);
+    for (int e = 0; e < 4; ++e)
+      park[(((kp - 1) * NT + t) * 16 + 4 * c + e) * 16 + col] = bits_as<uint32_t>(acc[e]);
   }
   __syncthreads();
-  if (kp == 1 || tile >= p.ntiles) return;
+  if (kp > 0 || tile >= p.ntiles) return;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t v = park[(t * 16 + 4 * c + e) * 16 + col];
-    if constexpr (KIND == K_W8A8 || RAW)
-      acc[e] += (int)v;
-    else
-      acc[e] += __builtin_bit_cast(float, v);
-  }
+  for (int j = 1; j < KW; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t v = park[(((j - 1) * NT + t) * 16 + 4 * c + e) * 16 + col];
+      if constexpr (KIND == K_W8A8 || RAW)
+        acc[e] += (int)v;
+      else
+        acc[e] += __builtin_bit_cast(float, v);
+    }
 
   // ---- epilogue: lane holds rows 4c+e of column `col` of its tile
   const int n = tile * 16 + col;
@@ -236,9 +248,12 @@ __global__ __launch_bounds__(512) void wsr8_kernel(const GemmArgs p) {
 }
 
 template <int KIND, bool RAW>
-hipError_t launch_w8(const GemmArgs& a, int nsplit, hipStream_t s) {
-  dim3 grid((a.ntiles + NT - 1) / NT, nsplit, 1);
-  hipLaunchKernelGGL((wsr8_kernel<KIND, RAW>), grid, dim3(64 * WAVES), 0, s, a);
+hipError_t launch_w8(const GemmArgs& a, int nsplit, int nt, hipStream_t s) {
+  if (nt == 1) {
+    hipLaunchKernelGGL((wsr8_kernel<KIND, RAW, 1>), dim3(a.ntiles, nsplit, 1), dim3(64 * WAVES), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((wsr8_kernel<KIND, RAW, 4>), dim3((a.ntiles + 3) / 4, nsplit, 1), dim3(64 * WAVES), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -247,14 +262,15 @@ hipError_t launch_w8(const GemmArgs& a, int nsplit, hipStream_t s) {
 // Largest K range (in 128-wide groups) one workgroup of this family holds.
 int wstream8_max_groups() { return RG; }
 
-hipError_t launch_wstream8(Format f, const GemmArgs& a, int nsplit, hipStream_t s) {
+hipError_t launch_wstream8(Format f, const GemmArgs& a, int nsplit, int nt, hipStream_t s) {
   const bool raw = a.otype == QDG_O_I32;
-  if ((a.groups + nsplit - 1) / nsplit > RG || (raw && nsplit > 1)) return hipErrorInvalidValue;
+  if ((a.groups + nsplit - 1) / nsplit > RG || (raw && nsplit > 1) || (nt != 1 && nt != 4))
+    return hipErrorInvalidValue;
   hipError_t e;
   switch (f) {
-    case FMT_W8A8: e = raw ? launch_w8<K_W8A8, true>(a, 1, s) : launch_w8<K_W8A8, false>(a, nsplit, s); break;
-    case FMT_W4A8: e = raw ? launch_w8<K_W4A8, true>(a, 1, s) : launch_w8<K_W4A8, false>(a, nsplit, s); break;
-    case FMT_MXFP4: e = launch_w8<K_MXFP4, false>(a, nsplit, s); break;
+    case FMT_W8A8: e = raw ? launch_w8<K_W8A8, true>(a, 1, nt, s) : launch_w8<K_W8A8, false>(a, nsplit, nt, s); break;
+    case FMT_W4A8: e = raw ? launch_w8<K_W4A8, true>(a, 1, nt, s) : launch_w8<K_W4A8, false>(a, nsplit, nt, s); break;
+    case FMT_MXFP4: e = launch_w8<K_MXFP4, false>(a, nsplit, nt, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e == hipSuccess && nsplit > 1) e = launch_reduce_splits(a, 16, a.ntiles * 16, s);
