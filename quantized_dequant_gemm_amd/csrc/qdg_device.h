@@ -16,6 +16,7 @@ namespace qdg {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
@@ -33,6 +34,15 @@ constexpr int kUnit8Bytes = 2048;  // int8 unit
 // product as long as A and B use the same one, which the packers ensure.
 __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x16_bf16: D[32x32] += A[32x16] B[16x32]. Lane l supplies
+// row (A) / column (B) l%32 and 8 K values (lane half l/32 the second 8 of
+// the step); D lane l holds column l%32, rows 8*(i/4) + 4*(l/32) + i%4
+// (measured). Twice the work of the 16 x 16 form per issued instruction.
+__device__ __forceinline__ f32x16_t mfma_bf16_32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 

@@ -4,21 +4,25 @@
 // for large batches (kinachrichten, "Wie die Architektur funktioniert"). Here
 // the large-M path is MFMA-bound, so it is organised around MFMA issue:
 //   * a 512-thread workgroup owns a 256 x 128 or 128 x 256 output tile; its
-//     8 wavefronts (two per SIMD) each own a 64 x 64 tile, small enough that
-//     accumulators, A fragments and unpacked weights all stay in the 256
-//     VGPRs the vector ALU can address (no AGPR shuffling, no spills);
+//     8 wavefronts (two per SIMD) each own a 64 x 64 tile computed as 2 x 2
+//     blocks of 32 x 32 (v_mfma_f32_32x32x16_bf16). Per issued instruction
+//     that form does twice the work of the 16 x 16 one, which leaves room for
+//     the dequantization and scale VALU work to run under the matrix core
+//     (measured: about six independent VALU ops hide under each 32 x 32 MFMA,
+//     two under each 16 x 16 one);
 //   * the K loop advances one 128-wide group per iteration. Everything the
-//     next group needs -- the A tile, the A row sums, the packed weight units
+//     next groups need -- the A tile, the A row sums, the packed weight units
 //     and the scale records -- is copied global -> LDS with direct 16-byte
-//     LDS loads into the other half of a double buffer, so no registers are
-//     held for prefetch; A chunks are XOR-swizzled by row so fragment reads
-//     are bank-conflict-free;
+//     LDS loads into a three-stage ring of separate LDS arrays, so no
+//     registers are held for prefetch. Every wave issues the same branch-free
+//     copy sequence, so the wait before a group leaves the next group's
+//     copies in flight; A rows are padded to 272 bytes so fragment reads are
+//     bank-conflict-free;
 //   * dequantization in registers as in the streaming family (bf16 128+u,
-//     one v_and_or_b32 per dword); the four N-tile MFMA chains of a 16-row
-//     A tile are interleaved and each starts from -(128+z) * rowsum(A)
-//     instead of zero, with the row sums computed (and, when symmetric,
-//     pre-scaled by -136) once per call by rowsum_kernel, so the only
-//     per-group epilogue is acc += s * P;
+//     one v_and_or_b32 per dword); each MFMA chain of a group starts from
+//     -(128+z) * rowsum(A) instead of zero, with the row sums computed (and,
+//     when symmetric, pre-scaled by -136) once per call by rowsum_kernel, so
+//     the only per-group epilogue is acc += s * P;
 //   * the output tile is transposed through LDS so every global store writes
 //     whole 16-byte row segments; the tile order is XCD-aware.
 #include <type_traits>
@@ -102,7 +106,8 @@ __global__ void reduce_splits_kernel(const float* __restrict__ partial, void* __
 //          16 bytes apart modulo 128, so the 8 lanes served together by a
 //          16-byte LDS read always hit distinct banks, and every fragment
 //          address is one per-lane base plus an immediate offset)
-//   RS     BM floats (row sums, pre-scaled)
+//   RS     BM floats (row sums, pre-scaled), in a slot of at least 1 KiB
+//          so that one whole-wave copy fills it
 //   W      BN/16 packed weight units of 1 KiB (tile-major)
 //   S      BN/16 x 16 scale records of 8 bytes
 template <int BM, int BN>
@@ -111,7 +116,7 @@ struct Stage {
   static constexpr int A = 0;
   static constexpr int A_SLOTS = BM * ROW / 16;  // 16-byte slots, 17 per row
   static constexpr int RS = BM * ROW;
-  static constexpr int W = RS + BM * 4;
+  static constexpr int W = RS + (BM * 4 > 1024 ? BM * 4 : 1024);
   static constexpr int S = W + (BN / 16) * 1024;
   static constexpr int BYTES = S + (BN / 16) * 128;
 };
@@ -124,37 +129,37 @@ struct Stage {
 // the kernel.
 template <int BM, int BN, int NW>
 __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint32_t* a_off, const GemmArgs& p,
-                                           const uint8_t* wbase, const uint8_t* sbase, const uint32_t* s_off,
+                                           const uint8_t* wbase, const uint8_t* sbase, uint32_t s_off,
                                            int wg_tile0, int wave, int lane, int mb, int g) {
+  // Every wave issues the same copies without branches, so that a wait on
+  // the copy count is exact for every wave and the compiler can tell which
+  // stage each copy writes. Surplus copies repeat another wave's copy (the
+  // same bytes to the same place).
   using L = Stage<BM, BN>;
   constexpr int A_INST = (L::A_SLOTS + 63) / 64;
+  static_assert((BN / 16) % NW == 0, "whole weight units per wave");
   const char* ag = a_g + (size_t)g * 256;
 #pragma unroll
   for (int r = 0; r < (A_INST + NW - 1) / NW; ++r) {
-    const int i = r * NW + wave;
-    if (i < A_INST)
-      __builtin_amdgcn_global_load_lds(ag + a_off[r], (lds_void*)(st + L::A + i * 1024), 16, 0, 0);
+    const int i = min(r * NW + wave, A_INST - 1);
+    __builtin_amdgcn_global_load_lds(ag + a_off[r], (lds_void*)(st + L::A + i * 1024), 16, 0, 0);
   }
 #pragma unroll
-  for (int r = 0; r < (BN / 16 + NW - 1) / NW; ++r) {
+  for (int r = 0; r < (BN / 16) / NW; ++r) {
     const int t = r * NW + wave;
-    if (t < BN / 16) {
-      // tiles past the layer re-read the last tile; their results are never stored
-      const int tile = min(wg_tile0 + t, p.ntiles - 1);
-      __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * kUnit4Bytes + lane * 16,
-                                       (lds_void*)(st + L::W + t * 1024), 16, 0, 0);
-    }
+    // tiles past the layer re-read the last tile; their results are never stored
+    const int tile = min(wg_tile0 + t, p.ntiles - 1);
+    __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * kUnit4Bytes + lane * 16,
+                                     (lds_void*)(st + L::W + t * 1024), 16, 0, 0);
   }
-  if (wave == NW - 1) {
-#pragma unroll
-    for (int r = 0; r < BN / 128; ++r)
-      __builtin_amdgcn_global_load_lds(sbase + (size_t)g * 128 + s_off[r], (lds_void*)(st + L::S + r * 1024), 16,
-                                       0, 0);
-  }
-  if (wave == 0 && lane < BM / 4) {
-    const char* rs = (const char*)(p.rowsum + (size_t)g * p.m_pad + mb * BM) + lane * 16;
-    __builtin_amdgcn_global_load_lds(rs, (lds_void*)(st + L::RS), 16, 0, 0);
-  }
+  // scale records: BN / 128 copies of 1 KiB, copy wave % (BN / 128) per wave
+  __builtin_amdgcn_global_load_lds(sbase + (size_t)g * 128 + s_off, (lds_void*)(st + L::S + (wave % (BN / 128)) * 1024),
+                                   16, 0, 0);
+  // row sums: one whole-wave copy per wave; lanes past BM / 4 repeat rows
+  // into the unused rest of the slot
+  static_assert(BM / 4 <= 64, "one copy of row sums");
+  const char* rs = (const char*)(p.rowsum + (size_t)g * p.m_pad + mb * BM) + (lane % (BM / 4)) * 16;
+  __builtin_amdgcn_global_load_lds(rs, (lds_void*)(st + L::RS), 16, 0, 0);
 }
 
 // One K group for a 64 x 64 wave tile: unpack the wave's 4 weight tiles once,
@@ -208,20 +213,83 @@ __device__ __forceinline__ void tile_group(const char* st, int a_lane, int w_lan
   }
 }
 
+// One K group for a 64 x 64 wave tile as 2 x 2 blocks of 32 x 32 outputs
+// (v_mfma_f32_32x32x16_bf16). Each MFMA does twice the work of the 16 x 16
+// form for the same issue cost, so the unpack and scale VALU work of the
+// group fits under the matrix core. Any assignment of the group's 128 K
+// values to the eight K steps works as long as A and W agree: lane half h
+// takes, at step s, dword s % 4 of unit quarter h + 2 * (s / 4), i.e. K
+// values 32 (h + 2 (s / 4)) + 8 (s % 4) .. +7, and reads the same eight
+// A values.
+template <bool ASYM, int BM, int BN>
+__device__ __forceinline__ void tile_group32(const char* st, int a_lane, int w_lane, int s_lane, int rs_lane,
+                                             uint32_t um, uint32_t ue, f32x16_t (&acc)[2][2]) {
+  using L = Stage<BM, BN>;
+  u32x4_t bp[2][2];  // [column block][quarter h, quarter h + 2]
+  float sc[2], negz[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) bp[cb][q] = *(const u32x4_t*)(st + w_lane + cb * 2048 + q * 512);
+    const u32x2_t rec = *(const u32x2_t*)(st + s_lane + cb * 256);
+    sc[cb] = bits_as<float>(rec.x);
+    negz[cb] = __builtin_bit_cast(float, (rec.y & 0xFFFFu) << 16);  // -(128+z)
+  }
+  // each chain starts from the row sums of its rows (times -(128+z))
+  f32x16_t pacc[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    f32x4_t r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = *(const f32x4_t*)(st + rs_lane + rb * 128 + q * 32);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pacc[rb][cb][i] = ASYM ? negz[cb] * r[i / 4][i % 4] : r[i / 4][i % 4];
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    u32x4_t a[2], b[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      a[rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + (s / 4) * 128 + (s % 4) * 16);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) b[cb] = unpack_u4_bf16_offset128(bp[cb][s / 4][s % 4], um, ue);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) pacc[rb][cb] = mfma_bf16_32(a[rb], b[cb], pacc[rb][cb]);
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][cb][i] = __builtin_fmaf(sc[cb], pacc[rb][cb][i], acc[rb][cb][i]);
+}
+
 template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, int NS, bool MOE>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const GemmArgs p, int m_blocks,
                                                                            int n_blocks) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
   constexpr int MTW = WTM / 16;  // 16-row tiles per wave
+  constexpr bool M32 = WTM == 64;  // 64 x 64 wave tiles run 32 x 32 MFMA blocks
   using L = Stage<BM, BN>;
   constexpr int A_INST = (L::A_SLOTS + 63) / 64;
   constexpr int A_PER_WAVE = (A_INST + NW - 1) / NW;
-  extern __shared__ __attribute__((aligned(16))) char smem[];  // [NS][L::BYTES]
-  // copies every wave has in flight per stage at least (A and weight units);
-  // waiting for the count to drop to this leaves the next stage in flight
-  constexpr int VM_NEXT = A_INST / NW + (BN / 16) / NW;
+  // copies every wave issues per stage (A, weight units, scale records, row
+  // sums); waiting for the count to drop to this leaves the next stage in
+  // flight
+  constexpr int VM_NEXT = A_PER_WAVE + (BN / 16) / NW + 2;
   static_assert(NS == 2 || NS == 3, "two or three stages");
+  // The stages are separate LDS objects (not one dynamic array) so that the
+  // compiler can tell a copy into one stage from a read of another: reads of
+  // a stage then wait only for that stage's copies.
+  __shared__ __attribute__((aligned(16))) char st0[L::BYTES];
+  __shared__ __attribute__((aligned(16))) char st1[L::BYTES];
+  __shared__ __attribute__((aligned(16))) char st2[NS == 3 ? L::BYTES : 16];
+  char* const stage[3] = {st0, st1, st2};
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -264,7 +332,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   uint32_t a_off[A_PER_WAVE];
 #pragma unroll
   for (int r = 0; r < A_PER_WAVE; ++r) {
-    const int q = (r * NW + wave) * 64 + lane;
+    const int q = min(r * NW + wave, A_INST - 1) * 64 + lane;
     const int row = min(q / 17, BM - 1), ch = q % 17;
     const int grow = mb * BM + row;
     int src;
@@ -277,18 +345,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
     a_off[r] = (uint32_t)src * (uint32_t)(p.K * 2) + (uint32_t)(ch < 16 ? ch : 0) * 16;
   }
   // scale records: lane l fetches 16 bytes (l % 8) of tile 8r + l / 8
-  uint32_t s_off[BN / 128];
-#pragma unroll
-  for (int r = 0; r < BN / 128; ++r) {
-    const int s_tile = min(wg_tile0 + 8 * r + (lane >> 3), p.ntiles - 1);
-    s_off[r] = (uint32_t)s_tile * (uint32_t)groups * 128u + (lane & 7) * 16;
+  // scale records: lane l fetches 16 bytes (l % 8) of tile 8 r + l / 8 of
+  // copy r = wave % (BN / 128)
+  uint32_t s_off;
+  {
+    const int s_tile = min(wg_tile0 + 8 * (wave % (BN / 128)) + (lane >> 3), p.ntiles - 1);
+    s_off = (uint32_t)s_tile * (uint32_t)groups * 128u + (lane & 7) * 16;
   }
 
-  // per-lane LDS bases of the fragment reads (byte offsets inside a stage)
-  const int a_lane = L::A + (wm * WTM + col) * L::ROW + c * 64;
-  const int w_lane = L::W + (wn * 4) * 1024 + lane * 16;
-  const int s_lane = L::S + (wn * 4) * 128 + col * 8;
-  const int rs_lane = L::RS + (wm * WTM + 4 * c) * 4;
+  // per-lane LDS bases of the fragment reads (byte offsets inside a stage);
+  // 64 x 64 wave tiles use 32 x 32 blocks: lane half h = lane / 32 reads
+  // row / column lane % 32 (column block b covers units 4 wn + 2 b + 0..1)
+  const int h = lane >> 5, l32 = lane & 31;
+  const int a_lane = M32 ? L::A + (wm * WTM + l32) * L::ROW + h * 64 : L::A + (wm * WTM + col) * L::ROW + c * 64;
+  const int w_lane = M32 ? L::W + (wn * 4 + (l32 >> 4)) * 1024 + (h * 16 + col) * 16 : L::W + (wn * 4) * 1024 + lane * 16;
+  const int s_lane = M32 ? L::S + (wn * 4 + (l32 >> 4)) * 128 + col * 8 : L::S + (wn * 4) * 128 + col * 8;
+  const int rs_lane = M32 ? L::RS + (wm * WTM + 4 * h) * 4 : L::RS + (wm * WTM + 4 * c) * 4;
 
   // one unpack constant in a VGPR, the other in an SGPR: lets each unpacked
   // dword be a single v_and_or_b32 (VOP3 reads at most one scalar operand)
@@ -297,59 +369,113 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   const uint32_t ue = p.unpack_exp;
 
   f32x4_t acc[MTW][4];
+  f32x16_t acc32[2][2];
+  if constexpr (M32) {
 #pragma unroll
-  for (int mt = 0; mt < MTW; ++mt)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc32[rb][cb][i] = 0.f;
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   const char* a_g = (const char*)p.A;
-  // NS-stage ring: groups g+1 .. g+NS-1 are in flight while g is computed
+  // NS-stage ring. Full rounds of NS groups run unrolled with constant stage
+  // indices; each group issues the copies of the group NS - 1 ahead (clamped
+  // to the last group: past the range they re-read it into a stage nobody
+  // reads again), so with three stages the wait before a group leaves the
+  // next group's copies in flight. The last partial round waits for all
+  // copies.
+  if (g0 < g1) {
 #pragma unroll
-  for (int q = 0; q < NS - 1; ++q)
-    if (g0 + q < g1)
-      load_stage<BM, BN, NW>(smem + q * L::BYTES, a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane, mb,
-                             g0 + q);
-  int cur = 0;  // stage of group g
-  for (int g = g0; g < g1; ++g) {
-    if (NS == 3 && g + 1 < g1)
-      __builtin_amdgcn_s_waitcnt((VM_NEXT & 15) | (7 << 4) | (15 << 8) | ((VM_NEXT >> 4) << 14));
-    else
-      __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // group g is in LDS for every wave; stage of g-1 is free
-    if (g + NS - 1 < g1) {
-      int nxt = cur + NS - 1;
-      if (nxt >= NS) nxt -= NS;
-      load_stage<BM, BN, NW>(smem + nxt * L::BYTES, a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane, mb,
-                             g + NS - 1);
+    for (int q = 0; q < NS - 1; ++q)
+      load_stage<BM, BN, NW>(stage[q], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane, mb,
+                             min(g0 + q, g1 - 1));
+  }
+  int gb = g0;
+  for (; gb + NS <= g1; gb += NS) {
+#pragma unroll
+    for (int cur = 0; cur < NS; ++cur) {
+      // this wave's copies of group gb+cur are done once at most the copies
+      // of one later group remain in flight (copies complete in order)
+      if constexpr (NS == 3)
+        __builtin_amdgcn_s_waitcnt((VM_NEXT & 15) | (7 << 4) | (15 << 8) | ((VM_NEXT >> 4) << 14));
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      // every wave's copies of the group landed and every wave is done with
+      // the previous group's stage. A bare s_barrier: __syncthreads would also
+      // wait for the copies in flight.
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+      load_stage<BM, BN, NW>(stage[(cur + NS - 1) % NS], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane,
+                             mb, min(gb + cur + NS - 1, g1 - 1));
+      if constexpr (M32)
+        tile_group32<ASYM, BM, BN>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
+      else
+        tile_group<ASYM, BM, BN, MTW>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
     }
-    tile_group<ASYM, BM, BN, MTW>(smem + cur * L::BYTES, a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
-    cur = cur + 1 == NS ? 0 : cur + 1;
+  }
+#pragma unroll
+  for (int cur = 0; cur < NS - 1; ++cur) {
+    if (gb + cur < g1) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if constexpr (M32)
+        tile_group32<ASYM, BM, BN>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
+      else
+        tile_group<ASYM, BM, BN, MTW>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
+    }
   }
 
   // ---- epilogue: per wave, transpose each 16 x 64 strip through LDS so that
   // every lane stores whole 16-byte row segments
-  __syncthreads();  // everyone is done with the stages
+  __builtin_amdgcn_s_waitcnt(0);  // the trailing copies have landed
+  __syncthreads();                 // everyone is done with the stages
   // split-K: each split stores its fp32 partial tile row-major into the
   // workspace ([split][m_pad][n_pad]); reduce_splits_kernel sums them
   const bool to_partial = nsplit > 1;
   const int n_pad = n_blocks * BN;
   const bool f32out = to_partial || p.otype == QDG_O_F32;
-  char* strip = smem + wave * (16 * 64 * 4);
+  char* strip = st0 + wave * (16 * 64 * 4);
+  static_assert(NW * 16 * 64 * 4 <= L::BYTES, "epilogue strips fit one stage");
   const int nbase = (wg_tile0 + wn * 4) * 16;
   const int esz = f32out ? 4 : 2;  // bytes per output element
   const int cpr = 64 * esz / 16;   // 16-byte chunks per strip row
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt) {
+    if constexpr (M32) {
+      // rows 16 mt .. 16 mt + 15 of the wave tile: block mt / 2, result
+      // elements i with i / 4 = 2 (mt % 2) + q
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = (4 * c + i) * 64 + t * 16 + col;
-        if (f32out)
-          ((float*)strip)[e] = acc[mt][t][i];
-        else
-          ((uint16_t*)strip)[e] = (uint16_t)f32_to_bf16_rne(acc[mt][t][i]);
-      }
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = acc32[mt / 2][cb][(2 * (mt % 2) + q) * 4 + i];
+            const int e = (8 * q + 4 * h + i) * 64 + cb * 32 + l32;
+            if (f32out)
+              ((float*)strip)[e] = v;
+            else
+              ((uint16_t*)strip)[e] = (uint16_t)f32_to_bf16_rne(v);
+          }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = (4 * c + i) * 64 + t * 16 + col;
+          if (f32out)
+            ((float*)strip)[e] = acc[mt][t][i];
+          else
+            ((uint16_t*)strip)[e] = (uint16_t)f32_to_bf16_rne(acc[mt][t][i]);
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
     for (int chunk = lane; chunk < 16 * cpr; chunk += 64) {
@@ -394,16 +520,8 @@ hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStrea
   // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256, 2 for 256 x 128)
   constexpr int NS = 3 * Stage<BM, BN>::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-  const size_t smem = NS * Stage<BM, BN>::BYTES;
-  static bool attr_set = false;  // idempotent; a race only repeats the call
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE>), dim3(m_blocks * n_blocks, nsplit),
-                     dim3(64 * WAVES_M * WAVES_N), smem, s, a, m_blocks, n_blocks);
+                     dim3(64 * WAVES_M * WAVES_N), 0, s, a, m_blocks, n_blocks);
   return hipGetLastError();
 }
 
