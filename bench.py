@@ -329,7 +329,7 @@ def rows_leg(reps=30):
                             tflops=round(fl / us / 1e6, 2), gbs=round(by / us / 1e3, 1),
                             hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4),
                             mfma_frac=round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4), align_us=round(us_align, 3),
-                            instance=q.qdg_plan_describe(plan, t).split(": ", 1)[1]))
+                            instance=q.qdg_moe_describe(plan, t, bm).split(": ", 1)[1]))
     return out
 
 

@@ -197,6 +197,11 @@ qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes);
    Returns the length of the full record (snprintf semantics), -1 on error. */
 int qdg_plan_describe(const qdg_plan* plan, int64_t M, char* buf, size_t len);
 
+/* The same record for a grouped MoE call of T tokens with block_m-row expert
+   blocks (16, 32, 64 or 128): the family and tiles qdg_moe_gemm runs.
+   Returns the record length, -1 on error (not a MoE plan, bad block_m). */
+int qdg_moe_describe(const qdg_plan* plan, int64_t T, int32_t block_m, char* buf, size_t len);
+
 /* Dense GEMM Y[M][n] = A[M][k] * dequant(W)^T.
    A: bf16 [M][k] (W4A16), i8 [M][k] (W8A8, W4A8) or E4M3 [M][k] (MXFP4), row
       stride k elements, 16-byte aligned.

@@ -32,7 +32,8 @@ STATUS_NAMES = {0: "QDG_OK", 1: "QDG_ERR_INVALID_ARG", 2: "QDG_ERR_UNSUPPORTED",
 EXPORTS = (
     "qdg_version", "qdg_last_error", "qdg_validate_layer", "qdg_preprocess_query", "qdg_preprocess",
     "qdg_quantize_weights", "qdg_quantize_act", "qdg_plan_create", "qdg_plan_destroy", "qdg_plan_workspace",
-    "qdg_plan_describe", "qdg_gemm", "qdg_moe_align_capacity", "qdg_moe_align", "qdg_moe_gemm",
+    "qdg_plan_describe", "qdg_moe_describe", "qdg_gemm", "qdg_moe_align_capacity", "qdg_moe_align",
+    "qdg_moe_gemm",
 )
 
 
@@ -88,6 +89,7 @@ def load():
         "qdg_plan_destroy": (None, [P]),
         "qdg_plan_workspace": (I32, [P, I64, P]),
         "qdg_plan_describe": (ctypes.c_int, [P, I64, ctypes.c_char_p, SZ]),
+        "qdg_moe_describe": (ctypes.c_int, [P, I64, I32, ctypes.c_char_p, SZ]),
         "qdg_gemm": (I32, [P, P, P, P, P, I64, P, SZ, P]),
         "qdg_moe_align_capacity": (I32, [I64, I32, I32, I32, P]),
         "qdg_moe_align": (I32, [P, I64, I32, I32, I32, P, P, P, P]),
@@ -183,6 +185,15 @@ def qdg_plan_describe(plan, M):
         raise QdgError(QDG_ERR_INVALID_ARG, "describe failed")
     buf = ctypes.create_string_buffer(n + 1)
     load().qdg_plan_describe(plan.handle, M, buf, n + 1)
+    return buf.value.decode()
+
+
+def qdg_moe_describe(plan, T, block_m):
+    n = load().qdg_moe_describe(plan.handle, T, block_m, None, 0)
+    if n < 0:
+        raise QdgError(QDG_ERR_INVALID_ARG, "describe failed (not a MoE plan or unsupported block_m)")
+    buf = ctypes.create_string_buffer(n + 1)
+    load().qdg_moe_describe(plan.handle, T, block_m, buf, n + 1)
     return buf.value.decode()
 
 

@@ -180,6 +180,11 @@ Choice choose(const qdg_plan& P, int64_t M) {
   const bool moe = P.compute.kind == QDG_KIND_MOE;
   int bm = P.has_tuning && T.block_m ? T.block_m : 0;
   if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
+  // measured on MI355X: one (partly filled) 128-row block of the tiled
+  // families, with K split into one pass of workgroups, beats the streaming
+  // family from M = 33 (W4A16) and from M = 64 (int8 / fp8 activations)
+  if (!P.has_tuning && !P.compute.batch_invariant && !moe && bm < 128 && M > (P.fmt == FMT_W4A16 ? 32 : 63))
+    bm = 128;
   if (P.compute.batch_invariant && bm > 64) bm = 64;
   // the tiled family addresses A with 32-bit byte offsets
   const bool a_fits = (double)(M > 0 ? M : 1) * (double)g.k * 2.0 < 4294967296.0;
@@ -196,7 +201,8 @@ Choice choose(const qdg_plan& P, int64_t M) {
     // and independent of M only through the tile count)
     int split = P.has_tuning && T.split_k ? T.split_k : 0;
     if (!split) {
-      split = tiles >= 256 ? 1 : (int)((300 + tiles - 1) / tiles);
+      // as many K splits as keep the workgroups within one pass over the CUs
+      split = tiles >= 256 ? 1 : (int)(256 / tiles);
       const int maxs = (int)(g.groups / 2);
       if (split > maxs) split = maxs > 0 ? maxs : 1;
       if (split > 16) split = 16;
@@ -248,7 +254,9 @@ Choice choose(const qdg_plan& P, int64_t M) {
   // there are enough of them (or M >= 512) to beat the streaming family
   const bool a8_fits = (double)(M > 0 ? M : 1) * (double)g.k < 4294967296.0;
   const int64_t q_tiles = ((M + 127) / 128) * ((g.ntiles + 15) / 16);
-  const bool q_enough = (P.has_tuning && T.block_m >= 128) || M >= 512 || q_tiles >= 64;
+  // (measured on MI355X: from M = 64 the tiled family with K split into one
+  // pass of 256 workgroups beats the streaming family at these layer sizes)
+  const bool q_enough = (P.has_tuning && T.block_m >= 128) || M >= 64;
   if (bm >= 128 && P.fmt != FMT_W4A16 && !moe && a8_fits && q_enough) {
     ch.tile = true;
     ch.qtile = true;
@@ -258,7 +266,8 @@ Choice choose(const qdg_plan& P, int64_t M) {
     const int64_t tiles = n_blocks * ch.grid_m;
     int split = P.has_tuning && T.split_k ? T.split_k : 0;
     if (!split) {
-      split = tiles >= 256 ? 1 : (int)((300 + tiles - 1) / tiles);
+      // as many K splits as keep the workgroups within one pass over the CUs
+      split = tiles >= 256 ? 1 : (int)(256 / tiles);
       const int maxs = (int)(g.groups / 2);
       if (split > maxs) split = maxs > 0 ? maxs : 1;
       if (split > 16) split = 16;
@@ -432,59 +441,86 @@ qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes) {
   return ok();
 }
 
+// Kernel choice of a grouped MoE call: the caller's block size decides the
+// family. 16-row blocks stream the weights (unless a tuning pins the
+// streaming family), 128-row blocks run the LDS-tiled family with one expert
+// per row block, 32 and 64 rows the streaming family.
+static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, int32_t a_per_pair, Choice* out) {
+  const Choice c0 = choose(plan, T);
+  Choice c = c0;
+  const int64_t rows = T * plan.compute.top_k;
+  c.sc.mt = block_m / 16;
+  c.sc.split = 1;
+  c.partial_bytes = 0;
+  const int64_t E = plan.layer.num_experts;
+  const int64_t cap = align_up(rows + E * (block_m - 1), block_m);
+  c.grid_m = (int)(cap / block_m);
+  const qdg_tuning_config& tu = plan.tuning;
+  c.ws = block_m == 16 && !plan.compute.batch_invariant &&
+         (!plan.has_tuning || ((!tu.block_n || tu.block_n == 64) && (!tu.waves || tu.waves == 8)));
+  if (!c.ws && !c0.tile && c0.ws) c.sc = StreamCfg{block_m / 16, 2, 4, 1};
+  c.tile = false;
+  c.qtile = false;
+  if (block_m == 128) {
+    // A rows are addressed with 32-bit byte offsets in the tiled family
+    const int64_t a_rows = a_per_pair ? rows : T;
+    if ((double)a_rows * (double)plan.layer.k * 2.0 >= 4294967296.0)
+      return fail(QDG_ERR_UNSUPPORTED, "A of %lld rows is too large for 128-row MoE blocks", (long long)a_rows);
+    if (plan.compute.batch_invariant)
+      return fail(QDG_ERR_UNSUPPORTED, "batch-invariant MoE plans use block_m <= 64");
+    c.tile = true;
+    c.ws = false;
+    c.tc = TileCfg{128, 256, 8};
+  } else if (!c.ws && !stream_cfg_supported(plan.fmt, c.sc)) {
+    return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
+  }
+  *out = c;
+  return QDG_OK;
+}
+
+// The MFMA instruction an instance issues.
+static const char* mfma_name(Format f, const Choice& c) {
+  if (f == FMT_W4A16) return c.tile && c.tc.bm * c.tc.bn / (64 * c.tc.waves) == 64 ? "32x32x16_bf16" : "16x16x32_bf16";
+  if (f == FMT_MXFP4) return "scale_16x16x128_f8f6f4";
+  return "16x16x64_i8";
+}
+
+static int describe(const qdg_plan& plan, const Choice& c, int64_t M, const char* kind, char* buf, size_t len) {
+  return snprintf(buf, buf ? len : 0,
+                  "%s %s n=%lld k=%lld E=%lld M=%lld: family=%s block_m=%d block_n=%d split_k=%d "
+                  "waves=%d mfma=%s grid_m=%d batch_invariant=%d tuning=%s layout=%d arch=gfx950",
+                  fmt_name(plan.fmt, plan.layer), kind, (long long)plan.layer.n, (long long)plan.layer.k,
+                  (long long)plan.layer.num_experts, (long long)M,
+                  c.qtile ? "qtile" : c.tile ? "tile" : c.ws ? "wstream" : "stream",
+                  c.tile || c.qtile ? c.tc.bm : c.sc.mt * 16, c.tile || c.qtile ? c.tc.bn : c.sc.nt * 16,
+                  c.sc.split, c.tile || c.qtile ? c.tc.waves : c.sc.kw, mfma_name(plan.fmt, c), c.grid_m,
+                  plan.compute.batch_invariant, plan.has_tuning ? "user" : "heuristic", QDG_LAYOUT_VERSION);
+}
+
 int qdg_plan_describe(const qdg_plan* plan, int64_t M, char* buf, size_t len) {
   if (!plan || M < 0) return -1;
   const Choice c = choose(*plan, M > 0 ? M : 1);
-  const char* kind = plan->compute.kind == QDG_KIND_MOE ? "moe" : "dense";
-  return snprintf(buf, buf ? len : 0,
-                  "%s %s n=%lld k=%lld E=%lld M=%lld: family=%s block_m=%d block_n=%d split_k=%d "
-                  "waves=%d mfma=16x16x32 grid_m=%d batch_invariant=%d tuning=%s layout=%d arch=gfx950",
-                  fmt_name(plan->fmt, plan->layer), kind, (long long)plan->layer.n, (long long)plan->layer.k,
-                  (long long)plan->layer.num_experts, (long long)M,
-                  c.qtile ? "qtile" : c.tile ? "tile" : c.ws ? "wstream" : "stream",
-                  c.tile ? c.tc.bm : c.sc.mt * 16, c.tile ? c.tc.bn : c.sc.nt * 16, c.sc.split, c.sc.kw,
-                  c.grid_m, plan->compute.batch_invariant, plan->has_tuning ? "user" : "heuristic",
-                  QDG_LAYOUT_VERSION);
+  return describe(*plan, c, M, plan->compute.kind == QDG_KIND_MOE ? "moe" : "dense", buf, len);
+}
+
+int qdg_moe_describe(const qdg_plan* plan, int64_t T, int32_t block_m, char* buf, size_t len) {
+  if (!plan || T < 0 || plan->compute.kind != QDG_KIND_MOE) return -1;
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return -1;
+  Choice c;
+  if (choose_moe(*plan, T > 0 ? T : 1, block_m, 0, &c) != QDG_OK) return -1;
+  return describe(*plan, c, T, "moe", buf, len);
 }
 
 static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales, const void* packed, void* Y,
                       int64_t M, void* workspace, size_t ws_bytes, hipStream_t stream, bool moe,
                       const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,
                       int64_t T, int32_t block_m, int32_t a_per_pair) {
-  const Choice c0 = choose(*plan, M);
-  Choice c = c0;
+  Choice c = choose(*plan, M);
   int64_t rows = M;
   if (moe) {
     rows = T * plan->compute.top_k;
-    c.sc.mt = block_m / 16;
-    c.sc.split = 1;
-    c.partial_bytes = 0;
-    int64_t cap = 0;
-    const int64_t E = plan->layer.num_experts;
-    cap = align_up(rows + E * (block_m - 1), block_m);
-    c.grid_m = (int)(cap / block_m);
-    // the caller's block size decides the family: 16-row blocks stream the
-    // weights unless a tuning pins the streaming family
-    const qdg_tuning_config& tu = plan->tuning;
-    c.ws = block_m == 16 && !plan->compute.batch_invariant &&
-           (!plan->has_tuning || ((!tu.block_n || tu.block_n == 64) && (!tu.waves || tu.waves == 8)));
-    if (!c.ws && !c0.tile && c0.ws) c.sc = StreamCfg{block_m / 16, 2, 4, 1};
-    c.tile = false;
-    c.qtile = false;
-    if (block_m == 128) {
-      // 128-row blocks: the LDS-tiled family (128 x 256 tiles, one expert per
-      // row block); A rows are addressed with 32-bit byte offsets
-      const int64_t a_rows = a_per_pair ? rows : T;
-      if ((double)a_rows * (double)plan->layer.k * 2.0 >= 4294967296.0)
-        return fail(QDG_ERR_UNSUPPORTED, "A of %lld rows is too large for 128-row MoE blocks", (long long)a_rows);
-      if (plan->compute.batch_invariant)
-        return fail(QDG_ERR_UNSUPPORTED, "batch-invariant MoE plans use block_m <= 64");
-      c.tile = true;
-      c.ws = false;
-      c.tc = TileCfg{128, 256, 8};
-    } else if (!c.ws && !stream_cfg_supported(plan->fmt, c.sc)) {
-      return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
-    }
+    const qdg_status st = choose_moe(*plan, T, block_m, a_per_pair, &c);
+    if (st != QDG_OK) return st;
   }
   size_t need = 0;
   qdg_plan_workspace(plan, M, &need);

@@ -77,6 +77,33 @@ def test_plan_and_workspace_validation():
     assert _status(q.qdg_plan_create, l8, q.moe(8)) == q.QDG_ERR_UNSUPPORTED
 
 
+def test_describe_reports_the_instance_that_runs():
+    # dense W4A16: weight streaming at M = 16, 32 x 32 MFMA blocks in the tiled family at large M
+    p = q.qdg_plan_create(q.layer_w4a16(14336, 4096), q.dense())
+    assert "family=wstream" in q.qdg_plan_describe(p, 16)
+    big = q.qdg_plan_describe(p, 8192)
+    assert "family=tile" in big and "mfma=32x32x16_bf16" in big and "waves=8" in big
+    p8 = q.qdg_plan_create(q.layer_w8a8(14336, 4096), q.dense())
+    assert "mfma=16x16x64_i8" in q.qdg_plan_describe(p8, 4096)
+    # mid M: one partly filled 128-row block of the tiled families
+    assert "family=stream" in q.qdg_plan_describe(p, 32)
+    assert "family=tile" in q.qdg_plan_describe(p, 33)
+    assert "family=stream" in q.qdg_plan_describe(p8, 63)
+    assert "family=qtile" in q.qdg_plan_describe(p8, 64)
+    # batch-invariant plans never switch family with M
+    pb = q.qdg_plan_create(q.layer_w4a16(14336, 4096), q.dense(batch_invariant=1))
+    assert "family=stream" in q.qdg_plan_describe(pb, 100)
+    # grouped MoE: the caller's block size picks the family
+    pm = q.qdg_plan_create(q.layer_w4a16(4096, 7168, num_experts=256), q.moe(8))
+    assert "family=wstream" in q.qdg_moe_describe(pm, 64, 16)
+    assert "family=stream" in q.qdg_moe_describe(pm, 512, 32)
+    assert "family=tile" in q.qdg_moe_describe(pm, 4096, 128)
+    with pytest.raises(q.QdgError):
+        q.qdg_moe_describe(pm, 64, 48)
+    with pytest.raises(q.QdgError):
+        q.qdg_moe_describe(p, 64, 16)  # not a MoE plan
+
+
 def test_gemm_argument_errors_before_device_work():
     l = q.layer_w4a16(64, 128)
     p = q.qdg_plan_create(l, q.dense())

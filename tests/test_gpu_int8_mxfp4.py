@@ -355,3 +355,22 @@ def test_8bit_weight_streaming_split_k(qdg, kind):
         assert metrics.rel_frob(H.to_f64(y1), y64) <= 1e-3
         outs[split] = H.to_f64(y1)
     assert np.allclose(outs[1], outs[32], rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("kind", ["w8a8", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("m,n,k", [(64, 4096, 4096), (100, 528, 2048)])
+def test_8bit_tiled_partial_row_block(qdg, kind, m, n, k):
+    # 64 <= M < 128: the tiled family with one partly filled 128-row block
+    # and K split into one pass of workgroups; integer results stay exact
+    mk, std, ac, sa, y64, p = _any_case(kind, m, n, k, salt=70 + m)
+    otypes = (q.QDG_O_F32, q.QDG_O_BF16) if kind == "mxfp4" else (q.QDG_O_I32, q.QDG_O_F32, q.QDG_O_BF16)
+    for otype in otypes:
+        layer = mk(otype)
+        assert _family(layer, m) == "qtile"
+        pk = H.Packed(layer, *std)
+        y = H.gemm(layer, pk, H.dev(ac), m, a_scales=H.dev(sa))[0]
+        if otype == q.QDG_O_I32:
+            assert np.array_equal(y.cpu().numpy().astype(np.int64), p)
+        else:
+            err = metrics.rel_frob(H.to_f64(y), y64)
+            assert err <= (1e-3 if otype == q.QDG_O_F32 else 2e-3), (otype, err)
