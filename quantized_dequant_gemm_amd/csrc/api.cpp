@@ -458,6 +458,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   const qdg_tuning_config& tu = plan.tuning;
   c.ws = block_m == 16 && !plan.compute.batch_invariant &&
          (!plan.has_tuning || ((!tu.block_n || tu.block_n == 64) && (!tu.waves || tu.waves == 8)));
+  if (c.ws) c.sc = StreamCfg{1, 4, 8, 1};  // 16 x 64 per workgroup of 8 waves
   if (!c.ws && !c0.tile && c0.ws) c.sc = StreamCfg{block_m / 16, 2, 4, 1};
   c.tile = false;
   c.qtile = false;
