@@ -37,14 +37,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Row sums of A per 128-wide K group, times `factor`:
 // out[g * m_pad + r] = factor * sum_k A[row(r)][128g + k], row(r) = r (dense;
-// rows >= M give 0) or the gathered MoE row.
+// rows >= M give 0) or the gathered MoE row. Sixteen lanes take one
+// (row, group) pair, 16 bytes each, so a wave reads 1 KiB of contiguous A
+// (four consecutive groups of one row); the 16 partial sums meet by lane
+// shuffles.
 __global__ void rowsum_kernel(const uint16_t* __restrict__ A, const int* __restrict__ sorted_ids,
                               const int* __restrict__ num_padded, int top_k, int a_per_pair, int num_pairs,
                               int M, int K, int m_pad, float factor, float* __restrict__ out) {
   const int groups = K / 128;
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (tid >= (int64_t)m_pad * groups) return;
-  const int r = (int)(tid % m_pad), g = (int)(tid / m_pad);
+  const int64_t pair = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  if (pair >= (int64_t)m_pad * groups) return;  // whole 16-lane groups
+  const int r = (int)(pair / groups), g = (int)(pair % groups);
   int src = r;
   bool v = r < M;
   if (sorted_ids) {
@@ -55,18 +59,16 @@ __global__ void rowsum_kernel(const uint16_t* __restrict__ A, const int* __restr
   }
   float s = 0.f;
   if (v) {
-    const u32x4_t* p = (const u32x4_t*)(A + (size_t)src * K + (size_t)g * 128);
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const u32x4_t x = p[i];
+    const u32x4_t x = *(const u32x4_t*)(A + (size_t)src * K + (size_t)g * 128 + sub * 8);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s += __builtin_bit_cast(float, (uint32_t)(x[j] << 16));
-        s += __builtin_bit_cast(float, (uint32_t)(x[j] & 0xFFFF0000u));
-      }
+    for (int j = 0; j < 4; ++j) {
+      s += __builtin_bit_cast(float, (uint32_t)(x[j] << 16));
+      s += __builtin_bit_cast(float, (uint32_t)(x[j] & 0xFFFF0000u));
     }
   }
-  out[tid] = s * factor;
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
+  if (sub == 0) out[(size_t)g * m_pad + r] = s * factor;
 }
 
 // Sum of the split-K partials in split order (deterministic), converted to
@@ -565,7 +567,7 @@ hipError_t launch_reduce_splits(const GemmArgs& a, int m_pad, int n_pad, hipStre
 hipError_t launch_rowsum(const void* a_bf16, const int* sorted_ids, const int* num_padded, int top_k,
                          int a_per_pair, int num_pairs, int M, int K, int m_pad, float factor, float* out,
                          hipStream_t s) {
-  const int64_t threads = (int64_t)m_pad * (K / 128);
+  const int64_t threads = (int64_t)m_pad * (K / 128) * 16;  // 16 lanes per (row, group)
   hipLaunchKernelGGL(rowsum_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                      (const uint16_t*)a_bf16, sorted_ids, num_padded, top_k, a_per_pair, num_pairs, M, K, m_pad,
                      factor, out);
