@@ -9,8 +9,9 @@ HBM. Small-M cases rotate over enough packed weight copies to defeat the
 
 Prints one JSON line. `value` is the step's algorithmic TFLOP/s; `roofline`
 describes the kernel that dominates the step's time, `roofline_m16` the
-HBM-bound M=16 case, `cases` every launch; `cpu_baseline` times the fp64 CPU
-oracle on a bounded sample of the same workload.
+HBM-bound M=16 case (also as a fraction of `hbm_copy_gbs`, the box's measured
+device-to-device copy rate), `cases` every launch; `cpu_baseline` times the
+fp64 CPU oracle over the same workload once.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
 """
@@ -80,12 +81,24 @@ def gpu_leg(args):
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    if args.copy_calibration:
-        src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
+    # the box's own device-to-device copy rate (read + write bytes), the
+    # practical HBM reference next to the published 8 TB/s; with
+    # --copy-calibration the first copy is the counters' known-size reference
+    src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
         dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * COPY_CAL_BYTES * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
 
     layers = {}
     for (k, n) in SHAPES:
@@ -174,10 +187,12 @@ def gpu_leg(args):
                     per_launch=alg_bytes(dom["M"], dom["N"], dom["K"]))
     m16 = [d for d in out_cases if d["M"] == 16]
     roof16 = [dict(bound="hbm", achieved=d["gbs"], peak=PEAK_HBM_GBS, unit="GB/s", frac=d["hbm_frac"],
-                   kernel=f"w4a16 M=16 K={d['K']} N={d['N']}", us=d["us"],
-                   traffic=measured_traffic(f"M=16 K={d['K']} N={d['N']}", "wstream_gemm.hip")) for d in m16]
+                   frac_of_copy=round(d["gbs"] / copy_gbs, 4), kernel=f"w4a16 M=16 K={d['K']} N={d['N']}",
+                   us=d["us"], traffic=measured_traffic(f"M=16 K={d['K']} N={d['N']}", "wstream_gemm.hip"))
+              for d in m16]
     value = flops_step / (ms_per_step * 1e-3) / 1e12
-    return dict(value=value, ms_per_step=ms_per_step, roofline=roof, roofline_m16=roof16, cases=out_cases)
+    return dict(value=value, ms_per_step=ms_per_step, roofline=roof, roofline_m16=roof16, cases=out_cases,
+                hbm_copy_gbs=round(copy_gbs, 1))
 
 
 PEAK_INT8_TOPS = 5000.0
@@ -297,19 +312,26 @@ def rows_leg(reps=30):
         logits = torch.randn((t, E), generator=g, device=dev, dtype=torch.float32)
         ids = torch.topk(logits, top_k, dim=1).indices.to(torch.int32).contiguous()
         touched = int(torch.unique(ids).numel())
-        bm = 16 if t * top_k <= 32 * E else 128
-        cap = q.qdg_moe_align_capacity(t, top_k, E, bm)
-        sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
-        block_expert = torch.empty(cap // bm, dtype=torch.int32, device=dev)
-        npad = torch.empty(1, dtype=torch.int32, device=dev)
+        # expert block size per projection (the caller's choice in the API;
+        # measured on MI355X): 16-row blocks for gate+up and 32-row blocks for
+        # down while most experts hold few rows, 128-row blocks beyond
+        small = t * top_k <= 32 * E
+        aligned = {}
+        for bm in sorted({16, 32} if small else {128}):
+            cap = q.qdg_moe_align_capacity(t, top_k, E, bm)
+            sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+            block_expert = torch.empty(cap // bm, dtype=torch.int32, device=dev)
+            npad = torch.empty(1, dtype=torch.int32, device=dev)
 
-        def align(i):
-            q.qdg_moe_align(ids.data_ptr(), t, top_k, E, bm, sorted_ids.data_ptr(), block_expert.data_ptr(),
-                            npad.data_ptr(), sh)
-        align(0)
-        us_align = _time_launches(align, reps, stream)
+            def align(i, bm=bm, sorted_ids=sorted_ids, block_expert=block_expert, npad=npad):
+                q.qdg_moe_align(ids.data_ptr(), t, top_k, E, bm, sorted_ids.data_ptr(), block_expert.data_ptr(),
+                                npad.data_ptr(), sh)
+            align(0)
+            aligned[bm] = (sorted_ids, block_expert, npad, _time_launches(align, reps, stream))
         for name, (layer, pk, n, k, plan) in layers.items():
             per_pair = name == "moe-down"
+            bm = (32 if per_pair else 16) if small else 128
+            sorted_ids, block_expert, npad, us_align = aligned[bm]
             rows_in = t * top_k if per_pair else t
             a = synth.device_activations_bf16(rows_in, k, seed=synth.seed_for(4, synth.TID_H, t + k))
             y = torch.empty((t * top_k, n), dtype=torch.bfloat16, device=dev)
@@ -383,7 +405,8 @@ def main():
         "config": {"workload": "dense W4A16 layer: int4 sym g128 fp16 scales, bf16 act/out; "
                                "(K,N) in {(4096,14336),(14336,4096)}, M in {1,16,128,1024,8192}",
                    "launches_per_step": len(g["cases"])},
-        "roofline": g["roofline"], "roofline_m16": g["roofline_m16"], "cases": g["cases"],
+        "roofline": g["roofline"], "roofline_m16": g["roofline_m16"], "hbm_copy_gbs": g["hbm_copy_gbs"],
+        "cases": g["cases"],
     }
     if not args.no_rows:
         line["rows"] = rows_leg()
