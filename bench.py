@@ -220,7 +220,8 @@ def rows_leg(reps=30):
     {16, 256, 4096}), W4A8-MXFP4 ((K,N) in {(7168,2048), (2048,7168)}, M in
     {16, 512, 4096}), the activation quantizers, and the grouped MoE W4A16
     GEMMs (E=256, top-8, hidden 7168, intermediate 2048, T in {64, 512,
-    4096}) with their expert sort."""
+    4096}) with their expert sort, and the grouped MoE W4A8-INT8 GEMMs of
+    the same experts at T in {64, 512}."""
     import torch
     import quantized_dequant_gemm_amd as q
     import synth
@@ -312,12 +313,12 @@ def rows_leg(reps=30):
         logits = torch.randn((t, E), generator=g, device=dev, dtype=torch.float32)
         ids = torch.topk(logits, top_k, dim=1).indices.to(torch.int32).contiguous()
         touched = int(torch.unique(ids).numel())
-        # expert block size per projection (the caller's choice in the API;
-        # measured on MI355X): 16-row blocks for gate+up and 32-row blocks for
-        # down while most experts hold few rows, 128-row blocks beyond
+        # expert block size (the caller's choice in the API; measured on
+        # MI355X): 16-row blocks while most experts hold few rows, 128-row
+        # blocks beyond
         small = t * top_k <= 32 * E
         aligned = {}
-        for bm in sorted({16, 32} if small else {128}):
+        for bm in (16,) if small else (128,):
             cap = q.qdg_moe_align_capacity(t, top_k, E, bm)
             sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
             block_expert = torch.empty(cap // bm, dtype=torch.int32, device=dev)
@@ -330,7 +331,7 @@ def rows_leg(reps=30):
             aligned[bm] = (sorted_ids, block_expert, npad, _time_launches(align, reps, stream))
         for name, (layer, pk, n, k, plan) in layers.items():
             per_pair = name == "moe-down"
-            bm = (32 if per_pair else 16) if small else 128
+            bm = 16 if small else 128
             sorted_ids, block_expert, npad, us_align = aligned[bm]
             rows_in = t * top_k if per_pair else t
             a = synth.device_activations_bf16(rows_in, k, seed=synth.seed_for(4, synth.TID_H, t + k))
@@ -351,6 +352,68 @@ def rows_leg(reps=30):
                             tflops=round(fl / us / 1e6, 2), gbs=round(by / us / 1e3, 1),
                             hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4),
                             mfma_frac=round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4), align_us=round(us_align, 3),
+                            instance=q.qdg_moe_describe(plan, t, bm).split(": ", 1)[1]))
+
+    # ---- grouped MoE W4A8-INT8 (the same experts; int8 activations per token
+    # for gate+up and per pair for down; streaming family)
+    del layers
+    torch.cuda.empty_cache()
+    layers8 = {}
+    for name, (n, k) in (("moe-w4a8-gate-up", (2 * inter, hid)), ("moe-w4a8-down", (hid, inter))):
+        layer = q.layer_w4a8(n, k, num_experts=E)
+        qw = torch.empty((E, n, k // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((E, n, k // 128), dtype=torch.int16, device=dev)
+        one = q.layer_w4a8(n, k)
+        for e in range(E):
+            w = synth.device_normal_f32((n, k), 0.02, seed=synth.seed_for(4, synth.TID_W, e + (E if k == inter else 0)))
+            q.qdg_quantize_weights(one, w.data_ptr(), qw[e].data_ptr(), sc[e].data_ptr(), None, sh)
+        nbytes = q.qdg_preprocess_query(layer)
+        pk = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        q.qdg_preprocess(layer, q.StdWeights(qw.data_ptr(), sc.data_ptr(), None), pk.data_ptr(), nbytes, sh)
+        del qw, sc
+        layers8[name] = (layer, pk, n, k, q.qdg_plan_create(layer, q.moe(top_k)))
+        print(f"row {name}: {E} experts packed", file=sys.stderr, flush=True)
+    for t in (64, 512):
+        g = torch.Generator(device=dev)
+        g.manual_seed(synth.seed_for(4, synth.TID_LOGITS, t))
+        logits = torch.randn((t, E), generator=g, device=dev, dtype=torch.float32)
+        ids = torch.topk(logits, top_k, dim=1).indices.to(torch.int32).contiguous()
+        touched = int(torch.unique(ids).numel())
+        bm = 16 if t == 64 else 32
+        cap = q.qdg_moe_align_capacity(t, top_k, E, bm)
+        sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+        block_expert = torch.empty(cap // bm, dtype=torch.int32, device=dev)
+        npad = torch.empty(1, dtype=torch.int32, device=dev)
+        q.qdg_moe_align(ids.data_ptr(), t, top_k, E, bm, sorted_ids.data_ptr(), block_expert.data_ptr(),
+                        npad.data_ptr(), sh)
+        for name, (layer, pk, n, k, plan) in layers8.items():
+            per_pair = name.endswith("down")
+            rows_in = t * top_k if per_pair else t
+            a = synth.device_activations_bf16(rows_in, k, seed=synth.seed_for(4, synth.TID_H, t + k))
+            qa = torch.empty((rows_in, k), dtype=torch.int8, device=dev)
+            sa = torch.empty(rows_in, dtype=torch.float32, device=dev)
+
+            def quant(i):
+                q.qdg_quantize_act(layer, a.data_ptr(), rows_in, qa.data_ptr(), sa.data_ptr(), sh)
+            quant(0)
+            us_q = _time_launches(quant, reps, stream)
+            y = torch.empty((t * top_k, n), dtype=torch.bfloat16, device=dev)
+            wsb = q.qdg_plan_workspace(plan, t)
+            ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+
+            def gemm(i):
+                q.qdg_moe_gemm(plan, qa.data_ptr(), sa.data_ptr(), pk.data_ptr(), sorted_ids.data_ptr(),
+                               block_expert.data_ptr(), npad.data_ptr(), t, bm, 1 if per_pair else 0,
+                               y.data_ptr(), ws.data_ptr(), wsb, sh)
+            gemm(0)
+            us = _time_launches(gemm, max(5, reps // 3), stream)
+            fl = 2 * t * top_k * n * k
+            by = touched * (n * k // 2 + n * (k // 128) * 2) + rows_in * (k + 4) + t * top_k * n * 2
+            print(f"row {name} T={t}: {us:.2f} us", file=sys.stderr, flush=True)
+            out.append(dict(row=name, T=t, K=k, N=n, block_m=bm, experts_touched=touched, us=round(us, 3),
+                            tflops=round(fl / us / 1e6, 2), gbs=round(by / us / 1e3, 1),
+                            hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4),
+                            mfma_frac=round(fl / us / 1e6 / PEAK_INT8_TOPS, 4), act_quant_us=round(us_q, 3),
                             instance=q.qdg_moe_describe(plan, t, bm).split(": ", 1)[1]))
     return out
 

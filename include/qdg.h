@@ -90,8 +90,8 @@ typedef struct qdg_layer_config {
   int32_t atype, act_group, otype, arch;
 } qdg_layer_config;
 
-/* Compute config: which computation. kind DENSE or MOE (MoE: W4A16 INT4
-   only). batch_invariant = 1 makes row m of Y bitwise independent of M and
+/* Compute config: which computation. kind DENSE or MOE (MoE: W4A16 with
+   INT4 symmetric weights, W8A8, W4A8-INT8, W4A8-MXFP4). batch_invariant = 1 makes row m of Y bitwise independent of M and
    of the other rows (one fixed reduction order for every M). top_k: MoE
    slots per token. */
 typedef struct qdg_compute_config {
@@ -231,13 +231,17 @@ qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int3
                          int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                          int32_t* num_padded, void* stream);
 
-/* Grouped MoE GEMM (W4A16): for every real entry i of sorted_ids in block b,
+/* Grouped MoE GEMM: for every real entry i of sorted_ids in block b,
    row i of Y = A[r] * dequant(W_e)^T with e = block_expert[b] and
    r = i (a_per_pair = 1, e.g. the down projection) or r = i / top_k
    (a_per_pair = 0, e.g. gate+up reading token rows). Y is [T*top_k][n];
-   rows are written only for real pairs. block_m must be the value passed to
-   qdg_moe_align: 16 (weight-streaming family), 32 or 64 (streaming family)
-   or 128 (LDS-tiled family; batch-invariant plans take 16 to 64). */
+   rows are written only for real pairs. A and a_scales are laid out as for
+   qdg_gemm with one row per r (the int8 / fp8 formats take the codes and
+   scales of qdg_quantize_act over those rows). block_m must be the value
+   passed to qdg_moe_align. W4A16: 16 (weight-streaming family), 32 or 64
+   (streaming family) or 128 (LDS-tiled family; batch-invariant plans take
+   16 to 64). W8A8, W4A8-INT8, W4A8-MXFP4: 16, 32 or 64 (streaming family;
+   128 returns QDG_ERR_UNSUPPORTED). */
 qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scales,
                         const void* packed, const int32_t* sorted_ids,
                         const int32_t* block_expert, const int32_t* num_padded, int64_t T,

@@ -186,3 +186,32 @@ def moe_gemm_rows(a_rows_bf16_bits, topk_ids, expert_w64, input_is_per_pair):
             y = np.zeros((flat.size, w.shape[0]))
         y[pairs] = ye
     return y
+
+
+def moe_rows(topk_ids, input_is_per_pair, expert_rows_ref):
+    """The grouped GEMM of any format: for every (token, slot) pair, the dense
+    reference of the expert it was routed to, on the pair's input row.
+
+    ``expert_rows_ref(e, rows)`` returns expert e's dense reference on the
+    activation rows ``rows`` (token rows for gate+up, pair rows for down):
+    either Y64 [len(rows), N] or (Y64, P) with P the exact integer
+    accumulator of the integer formats. Returns Y64 [T*top_k, N], and P int64
+    [T*top_k, N] when the reference gives one (else None).
+    """
+    ids = np.asarray(topk_ids)
+    top_k = ids.shape[1]
+    flat = ids.reshape(-1)
+    y = p = None
+    for e in np.unique(flat):
+        pairs = np.nonzero(flat == e)[0]
+        rows = pairs if input_is_per_pair else pairs // top_k
+        r = expert_rows_ref(int(e), rows)
+        ye, pe = r if isinstance(r, tuple) else (r, None)
+        if y is None:
+            y = np.zeros((flat.size, ye.shape[1]))
+            if pe is not None:
+                p = np.zeros((flat.size, ye.shape[1]), dtype=np.int64)
+        y[pairs] = ye
+        if pe is not None:
+            p[pairs] = pe
+    return y, p

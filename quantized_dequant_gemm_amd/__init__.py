@@ -226,18 +226,18 @@ def layer_w4a16(n, k, asym=False, num_experts=1, otype=QDG_O_BF16):
                        act_group=0, otype=otype, arch=950)
 
 
-def layer_w8a8(n, k, otype=QDG_O_BF16):
-    return LayerConfig(n=n, k=k, num_experts=1, wtype=QDG_W_INT8, stype=QDG_S_F32, group_size=0, has_zeros=0,
+def layer_w8a8(n, k, otype=QDG_O_BF16, num_experts=1):
+    return LayerConfig(n=n, k=k, num_experts=num_experts, wtype=QDG_W_INT8, stype=QDG_S_F32, group_size=0, has_zeros=0,
                        atype=QDG_A_INT8, act_group=0, otype=otype, arch=950)
 
 
-def layer_w4a8(n, k, otype=QDG_O_BF16):
-    return LayerConfig(n=n, k=k, num_experts=1, wtype=QDG_W_INT4, stype=QDG_S_F16, group_size=128, has_zeros=0,
+def layer_w4a8(n, k, otype=QDG_O_BF16, num_experts=1):
+    return LayerConfig(n=n, k=k, num_experts=num_experts, wtype=QDG_W_INT4, stype=QDG_S_F16, group_size=128, has_zeros=0,
                        atype=QDG_A_INT8, act_group=0, otype=otype, arch=950)
 
 
-def layer_mxfp4(n, k, otype=QDG_O_BF16):
-    return LayerConfig(n=n, k=k, num_experts=1, wtype=QDG_W_MXFP4, stype=QDG_S_E8M0, group_size=32,
+def layer_mxfp4(n, k, otype=QDG_O_BF16, num_experts=1):
+    return LayerConfig(n=n, k=k, num_experts=num_experts, wtype=QDG_W_MXFP4, stype=QDG_S_E8M0, group_size=32,
                        has_zeros=0, atype=QDG_A_FP8E4M3, act_group=128, otype=otype, arch=950)
 
 

@@ -373,8 +373,8 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
     return fail(QDG_ERR_INVALID_ARG, "bad kind %d", compute->kind);
   const Format f = format_of(*layer);
   if (compute->kind == QDG_KIND_MOE) {
-    if (f != FMT_W4A16 || layer->wtype != QDG_W_INT4)
-      return fail(QDG_ERR_UNSUPPORTED, "grouped MoE is implemented for W4A16 int4 symmetric only");
+    if (f == FMT_W4A16 && layer->wtype != QDG_W_INT4)
+      return fail(QDG_ERR_UNSUPPORTED, "grouped W4A16 MoE is implemented for int4 symmetric weights only");
     if (compute->top_k < 1 || compute->top_k > 32) return fail(QDG_ERR_INVALID_ARG, "top_k must be in [1, 32]");
   } else if (layer->num_experts != 1) {
     return fail(QDG_ERR_INVALID_ARG, "a dense layer has num_experts = 1");
@@ -431,7 +431,7 @@ qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes) {
   if (M < 0) return fail(QDG_ERR_INVALID_ARG, "M < 0");
   const Choice c = choose(*plan, M > 0 ? M : 1);
   int64_t rowsum = (int64_t)c.rowsum_bytes;
-  if (plan->compute.kind == QDG_KIND_MOE) {
+  if (plan->compute.kind == QDG_KIND_MOE && plan->fmt == FMT_W4A16) {
     // MoE: room for the row sums of 128-row blocks (the largest block size)
     const int64_t cap =
         align_up((M > 0 ? M : 1) * plan->compute.top_k + plan->layer.num_experts * 127, 128);
@@ -456,10 +456,27 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   const int64_t cap = align_up(rows + E * (block_m - 1), block_m);
   c.grid_m = (int)(cap / block_m);
   const qdg_tuning_config& tu = plan.tuning;
+  // 16-row blocks: weight streaming for long K ranges (its chunked kernel);
+  // when K fits the resident kernel (<= 32 groups) the streaming family is
+  // faster per block (measured on MI355X: no per-block staging of A), unless
+  // a tuning pins weight streaming
+  const bool ws_pinned = plan.has_tuning && tu.block_n == 64 && tu.waves == 8;
   c.ws = block_m == 16 && !plan.compute.batch_invariant &&
-         (!plan.has_tuning || ((!tu.block_n || tu.block_n == 64) && (!tu.waves || tu.waves == 8)));
+         (!plan.has_tuning || ((!tu.block_n || tu.block_n == 64) && (!tu.waves || tu.waves == 8))) &&
+         (plan.geom.groups > 32 || ws_pinned);
+  if (plan.fmt != FMT_W4A16) {
+    // int8 / fp8 activations: the streaming family, block_m / 16 row tiles
+    if (block_m > 64)
+      return fail(QDG_ERR_UNSUPPORTED, "grouped MoE with int8/fp8 activations uses block_m 16, 32 or 64");
+    c.ws = c.tile = c.qtile = false;
+    c.sc = StreamCfg{block_m / 16, 2, 4, 1};
+    c.rowsum_bytes = 0;
+    *out = c;
+    return QDG_OK;
+  }
   if (c.ws) c.sc = StreamCfg{1, 4, 8, 1};  // 16 x 64 per workgroup of 8 waves
-  if (!c.ws && !c0.tile && c0.ws) c.sc = StreamCfg{block_m / 16, 2, 4, 1};
+  else if (!plan.has_tuning || c0.tile || c0.ws || !stream_cfg_supported(plan.fmt, c.sc))
+    c.sc = StreamCfg{block_m / 16, 2, 4, 1};
   c.tile = false;
   c.qtile = false;
   if (block_m == 128) {
@@ -643,8 +660,12 @@ qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scal
   if (T * plan->compute.top_k > (1 << 20)) return fail(QDG_ERR_UNSUPPORTED, "T*top_k above 2^20");
   if (!A || !packed || !Y || !sorted_ids || !block_expert || !num_padded)
     return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
+  if (plan->fmt != FMT_W4A16 && (plan->fmt == FMT_MXFP4 || plan->layer.otype != QDG_O_I32) && !a_scales)
+    return fail(QDG_ERR_INVALID_ARG, "activation scales are NULL");
   if (!aligned(A, 16)) return fail(QDG_ERR_MISALIGNED, "A must be 16-byte aligned");
   if (!aligned(packed, 256)) return fail(QDG_ERR_MISALIGNED, "packed must be 256-byte aligned");
+  if (!aligned(Y, plan->layer.otype == QDG_O_BF16 ? 2 : 4))
+    return fail(QDG_ERR_MISALIGNED, "Y must be aligned to its element size");
   return run(plan, A, a_scales, packed, Y, T, workspace, ws_bytes, (hipStream_t)stream, true, sorted_ids,
              block_expert, num_padded, T, block_m, a_per_pair ? 1 : 0);
 }

@@ -73,8 +73,15 @@ def test_plan_and_workspace_validation():
     lm = q.layer_w4a16(4096, 7168, num_experts=256)
     assert _status(q.qdg_plan_create, lm, q.dense()) == q.QDG_ERR_INVALID_ARG
     assert _status(q.qdg_plan_create, lm, q.moe(0)) == q.QDG_ERR_INVALID_ARG
-    l8 = q.layer_w8a8(4096, 4096)
-    assert _status(q.qdg_plan_create, l8, q.moe(8)) == q.QDG_ERR_UNSUPPORTED
+    # grouped MoE: W4A16 with int4 symmetric weights and the int8 / fp8
+    # activation formats (streaming family, 16- to 64-row blocks)
+    la = q.layer_w4a16(4096, 7168, asym=True, num_experts=8)
+    assert _status(q.qdg_plan_create, la, q.moe(8)) == q.QDG_ERR_UNSUPPORTED
+    for mk in (q.layer_w8a8, q.layer_w4a8, q.layer_mxfp4):
+        p8 = q.qdg_plan_create(mk(4096, 2048, num_experts=8), q.moe(8))
+        assert "family=stream" in q.qdg_moe_describe(p8, 64, 32)
+        with pytest.raises(q.QdgError):
+            q.qdg_moe_describe(p8, 64, 128)
 
 
 def test_describe_reports_the_instance_that_runs():

@@ -60,10 +60,10 @@ def _moe_packed(qs, ss, n, k):
     return layer, H.Packed(layer, qw, sc)
 
 
-def _moe_gemm(layer, pk, a_dev, ids, bm, a_per_pair, top_k):
+def _moe_gemm(layer, pk, a_dev, ids, bm, a_per_pair, top_k, tuning=None):
     t = ids.shape[0]
     sid, blk, npad, cap = _align_dev(ids, layer.num_experts, bm)
-    plan = q.qdg_plan_create(layer, q.moe(top_k))
+    plan = q.qdg_plan_create(layer, q.moe(top_k), tuning)
     ws, nbytes = H.workspace(plan, t)
     y = H.out_tensor(t * top_k, layer.n, q.QDG_O_BF16)
     q.qdg_moe_gemm(plan, a_dev.data_ptr(), None, pk.buf.data_ptr(), sid.data_ptr(), blk.data_ptr(),
@@ -92,23 +92,27 @@ def test_moe_gemm_small_experts(qdg, t, bm):
     assert metrics.rel_frob(H.to_f64(yd), yd64) <= 2e-3
 
 
-@pytest.mark.parametrize("bm", [16, 32, 128])
-def test_moe_single_expert_equals_dense(qdg, bm):
+@pytest.mark.parametrize("bm,pin_ws", [(16, False), (16, True), (32, False), (128, False)])
+def test_moe_single_expert_equals_dense(qdg, bm, pin_ws):
     # everything routed to expert 0 of 2: the MoE blocks hold the same rows as
     # the dense GEMM run block by block with the same kernel family, so every
-    # output matches bitwise (16-row blocks: weight streaming; 32: streaming;
-    # 128: LDS-tiled)
+    # output matches bitwise (16-row blocks with this short K: streaming, or
+    # weight streaming when a tuning pins it; 32: streaming; 128: LDS-tiled)
     t, hid, n = 40, 512, 128
     qs, ss = _experts(2, n, hid, salt=3)
     layer, pk = _moe_packed(qs, ss, n, hid)
     x = synth.activations_bf16_bits(t, hid, workload_id=4, salt=5)
     ids = np.zeros((t, 1), np.int32)
-    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 0, 1)
-    if bm == 16:
+    tm = q.TuningConfig(block_n=64, waves=8) if pin_ws else None
+    plan = q.qdg_plan_create(layer, q.moe(1), tm)
+    fam = q.qdg_moe_describe(plan, t, bm).split("family=")[1].split()[0]
+    assert fam == {16: "wstream" if pin_ws else "stream", 32: "stream", 128: "tile"}[bm]
+    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 0, 1, tuning=tm)
+    if bm == 16 and pin_ws:
         t1 = q.TuningConfig(block_m=16, block_n=64, split_k=1)
         yd = torch.cat([H.w4a16(x[r:r + 16], qs[0], ss[0], None, tuning=t1) for r in range(0, t, 16)])
-    elif bm == 32:
-        t1 = q.TuningConfig(block_m=32, block_n=32, split_k=1)
+    elif bm <= 32:
+        t1 = q.TuningConfig(block_m=bm, block_n=32, split_k=1)
         yd = H.w4a16(x, qs[0], ss[0], None, tuning=t1)
     else:
         t1 = q.TuningConfig(block_m=128, split_k=1)

@@ -205,6 +205,33 @@ def test_moe_gemm_rows_reduces_to_dense():
     assert np.allclose(yd[5], hf[5] @ ws[ids[2, 1]].T, rtol=1e-14, atol=0)
 
 
+def test_moe_rows_brute_force_integer_experts():
+    # the format-generic grouped reference against exact per-pair brute force
+    # (Python integers): token rows for gate+up, one row per pair for down,
+    # with the integer accumulator carried through
+    t, top_k, n, k = 5, 3, 4, 32
+    r = np.random.default_rng(31)
+    qa = r.integers(-127, 128, (t * top_k, k))
+    sa = r.uniform(0.5, 2.0, t * top_k)
+    qw = {e: r.integers(-127, 128, (n, k)) for e in range(4)}
+    sw = {e: r.uniform(0.5, 2.0, n) for e in range(4)}
+    ids = np.array([[0, 3, 1], [2, 2, 0], [3, 1, 1], [0, 0, 2], [1, 3, 3]])
+    for per_pair in (0, 1):
+        y, p = ref.moe_rows(ids, per_pair, lambda e, rows: ref.gemm_w8a8(qa[rows], sa[rows], qw[e], sw[e]))
+        for tt in range(t):
+            for j in range(top_k):
+                i = tt * top_k + j
+                row = i if per_pair else tt
+                e = int(ids[tt, j])
+                for c in range(n):
+                    acc = sum(int(qa[row, kk]) * int(qw[e][c, kk]) for kk in range(k))
+                    assert p[i, c] == acc
+                    assert y[i, c] == acc * sa[row] * sw[e][c]
+    # a format without an integer accumulator returns P = None
+    y2, p2 = ref.moe_rows(ids, 0, lambda e, rows: np.ones((len(rows), 2)) * e)
+    assert p2 is None and np.array_equal(y2[:, 0], ids.reshape(-1).astype(float))
+
+
 def test_tiny_workload_oracle_shapes():
     # the tiny W4A16 workload end to end through the oracle
     a = synth.activations_bf16_bits(16, 1024, workload_id=0)
