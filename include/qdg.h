@@ -95,8 +95,18 @@ typedef struct qdg_layer_config {
    of the other rows (one fixed reduction order for every M). top_k: MoE
    slots per token. */
 typedef struct qdg_compute_config {
-  int32_t kind, batch_invariant, top_k, reserved;
+  int32_t kind, batch_invariant, top_k;
+  int32_t epilogue; /* QDG_EPI_*; QDG_EPI_NONE for plain Y */
 } qdg_compute_config;
+
+/* Output epilogues of a MoE plan (the MoE block around the grouped GEMM:
+   jetabc, "跑得有多快", names the grouped MoE path the library serves).
+   QDG_EPI_SILU_MUL: the layer is a fused gate+up projection with n = 2*I
+   output rows, rows [0, I) the gate and [I, 2I) the up projection (I a
+   multiple of 16); Y is [T*top_k][I] with Y[r][i] = silu(G[r][i]) * U[r][i],
+   silu(x) = x / (1 + exp(-x)), computed in fp32 from the fp32 GEMM results
+   before the output conversion. Not for int32 output. */
+enum { QDG_EPI_NONE = 0, QDG_EPI_SILU_MUL = 1 };
 
 /* Tuning config: how to run. Zero in any field means "heuristic". Three
    kernel families exist; block_m and waves select one:
@@ -247,6 +257,16 @@ qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scal
                         const int32_t* block_expert, const int32_t* num_padded, int64_t T,
                         int32_t block_m, int32_t a_per_pair, void* Y, void* workspace,
                         size_t ws_bytes, void* stream);
+
+/* Top-k weighted combine of the grouped GEMM's pair rows (the last step of
+   the MoE block): out[t][c] = sum_{j < top_k} w[t*top_k + j] *
+   y[t*top_k + j][c], summed in fp32 in ascending j (deterministic), then
+   converted to otype (QDG_O_BF16 or QDG_O_F32). y: f32 [T*top_k][n] (a
+   qdg_moe_gemm output with otype F32); w: f32 [T*top_k] routing weights;
+   out: [T][n]. All device pointers, 16-byte aligned; n a multiple of 4.
+   Enqueued on stream; T = 0 enqueues nothing. */
+qdg_status qdg_moe_combine(const float* y, const float* w, int64_t T, int32_t top_k, int64_t n, void* out,
+                           int32_t otype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -215,3 +215,28 @@ def moe_rows(topk_ids, input_is_per_pair, expert_rows_ref):
         if pe is not None:
             p[pairs] = pe
     return y, p
+
+
+# ---------------------------------------------------------------- MoE block
+
+def silu_mul(y_gate_up):
+    """The gate+up epilogue: Y [R, 2I] holds the gate projection in columns
+    [0, I) and the up projection in [I, 2I); returns H [R, I] with
+    ``H = silu(G) * U`` and ``silu(x) = x * sigmoid(x) = x / (1 + exp(-x))``
+    in float64 (the MoE block around the grouped GEMM; jetabc, "跑得有多快")."""
+    y = np.asarray(y_gate_up, dtype=np.float64)
+    i = y.shape[1] // 2
+    g, u = y[:, :i], y[:, i:]
+    # x * sigmoid(x) with the sigmoid in the form that cannot overflow
+    e = np.exp(-np.abs(g))
+    sig = np.where(g >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return g * sig * u
+
+
+def moe_combine(y_pairs, route_w, top_k):
+    """The top-k weighted combine: ``out[t] = sum_j w[t, j] * Y[t*top_k + j]``
+    over the grouped GEMM's pair rows, in float64."""
+    y = np.asarray(y_pairs, dtype=np.float64)
+    w = np.asarray(route_w, dtype=np.float64).reshape(-1, top_k)
+    t = w.shape[0]
+    return np.einsum("tj,tjc->tc", w, y.reshape(t, top_k, -1))

@@ -24,6 +24,7 @@ QDG_S_F16, QDG_S_F32, QDG_S_E8M0 = range(3)
 QDG_A_BF16, QDG_A_INT8, QDG_A_FP8E4M3 = range(3)
 QDG_O_BF16, QDG_O_F32, QDG_O_I32 = range(3)
 QDG_KIND_DENSE, QDG_KIND_MOE = range(2)
+QDG_EPI_NONE, QDG_EPI_SILU_MUL = range(2)
 
 STATUS_NAMES = {0: "QDG_OK", 1: "QDG_ERR_INVALID_ARG", 2: "QDG_ERR_UNSUPPORTED", 3: "QDG_ERR_MISALIGNED",
                 4: "QDG_ERR_WORKSPACE", 5: "QDG_ERR_HIP"}
@@ -33,7 +34,7 @@ EXPORTS = (
     "qdg_version", "qdg_last_error", "qdg_validate_layer", "qdg_preprocess_query", "qdg_preprocess",
     "qdg_quantize_weights", "qdg_quantize_act", "qdg_plan_create", "qdg_plan_destroy", "qdg_plan_workspace",
     "qdg_plan_describe", "qdg_moe_describe", "qdg_gemm", "qdg_moe_align_capacity", "qdg_moe_align",
-    "qdg_moe_gemm",
+    "qdg_moe_gemm", "qdg_moe_combine",
 )
 
 
@@ -46,7 +47,7 @@ class LayerConfig(ctypes.Structure):
 
 class ComputeConfig(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("batch_invariant", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("epilogue", ctypes.c_int32)]
 
 
 class TuningConfig(ctypes.Structure):
@@ -94,6 +95,7 @@ def load():
         "qdg_moe_align_capacity": (I32, [I64, I32, I32, I32, P]),
         "qdg_moe_align": (I32, [P, I64, I32, I32, I32, P, P, P, P]),
         "qdg_moe_gemm": (I32, [P, P, P, P, P, P, P, I64, I32, I32, P, P, SZ, P]),
+        "qdg_moe_combine": (I32, [P, P, I64, I32, I64, P, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -218,6 +220,10 @@ def qdg_moe_gemm(plan, A, a_scales, packed, sorted_ids, block_expert, num_padded
                                block_m, a_per_pair, Y, workspace, ws_bytes, stream))
 
 
+def qdg_moe_combine(y, w, T, top_k, n, out, otype, stream=0):
+    _check(load().qdg_moe_combine(y, w, T, top_k, n, out, otype, stream))
+
+
 # ------------------------------------------------------------- config helpers
 
 def layer_w4a16(n, k, asym=False, num_experts=1, otype=QDG_O_BF16):
@@ -242,8 +248,8 @@ def layer_mxfp4(n, k, otype=QDG_O_BF16, num_experts=1):
 
 
 def dense(batch_invariant=0):
-    return ComputeConfig(kind=QDG_KIND_DENSE, batch_invariant=batch_invariant, top_k=0, reserved=0)
+    return ComputeConfig(kind=QDG_KIND_DENSE, batch_invariant=batch_invariant, top_k=0, epilogue=QDG_EPI_NONE)
 
 
-def moe(top_k, batch_invariant=0):
-    return ComputeConfig(kind=QDG_KIND_MOE, batch_invariant=batch_invariant, top_k=top_k, reserved=0)
+def moe(top_k, batch_invariant=0, epilogue=0):
+    return ComputeConfig(kind=QDG_KIND_MOE, batch_invariant=batch_invariant, top_k=top_k, epilogue=epilogue)

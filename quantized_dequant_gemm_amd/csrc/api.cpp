@@ -379,6 +379,14 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
   } else if (layer->num_experts != 1) {
     return fail(QDG_ERR_INVALID_ARG, "a dense layer has num_experts = 1");
   }
+  if (compute->epilogue != QDG_EPI_NONE) {
+    if (compute->epilogue != QDG_EPI_SILU_MUL) return fail(QDG_ERR_INVALID_ARG, "bad epilogue %d", compute->epilogue);
+    if (compute->kind != QDG_KIND_MOE)
+      return fail(QDG_ERR_UNSUPPORTED, "the SiLU*mul epilogue is implemented for MoE plans");
+    if (layer->n % 32 != 0)
+      return fail(QDG_ERR_UNSUPPORTED, "SiLU*mul needs n = 2*I with I a multiple of 16 (n=%lld)", (long long)layer->n);
+    if (layer->otype == QDG_O_I32) return fail(QDG_ERR_UNSUPPORTED, "SiLU*mul has no int32 output");
+  }
   if (tuning) {
     const bool dense_tiled = compute->kind == QDG_KIND_DENSE && !compute->batch_invariant;
     const bool tile_ok = dense_tiled && (tuning->block_m == 128 || (f == FMT_W4A16 && tuning->block_m == 256));
@@ -461,7 +469,8 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   // faster per block (measured on MI355X: no per-block staging of A), unless
   // a tuning pins weight streaming
   const bool ws_pinned = plan.has_tuning && tu.block_n == 64 && tu.waves == 8;
-  c.ws = block_m == 16 && !plan.compute.batch_invariant &&
+  const bool silu = plan.compute.epilogue == QDG_EPI_SILU_MUL;  // weight streaming has no such epilogue
+  c.ws = block_m == 16 && !plan.compute.batch_invariant && !silu &&
          (!plan.has_tuning || ((!tu.block_n || tu.block_n == 64) && (!tu.waves || tu.waves == 8))) &&
          (plan.geom.groups > 32 || ws_pinned);
   if (plan.fmt != FMT_W4A16) {
@@ -492,6 +501,9 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   } else if (!c.ws && !stream_cfg_supported(plan.fmt, c.sc)) {
     return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
   }
+  if (silu && c.tile) return fail(QDG_ERR_UNSUPPORTED, "SiLU*mul with 128-row blocks: not yet");
+  if (silu && !c.tile && c.sc.nt != 2)
+    return fail(QDG_ERR_UNSUPPORTED, "the SiLU*mul epilogue pairs 2 tiles: block_n must be 32");
   *out = c;
   return QDG_OK;
 }
@@ -506,13 +518,14 @@ static const char* mfma_name(Format f, const Choice& c) {
 static int describe(const qdg_plan& plan, const Choice& c, int64_t M, const char* kind, char* buf, size_t len) {
   return snprintf(buf, buf ? len : 0,
                   "%s %s n=%lld k=%lld E=%lld M=%lld: family=%s block_m=%d block_n=%d split_k=%d "
-                  "waves=%d mfma=%s grid_m=%d batch_invariant=%d tuning=%s layout=%d arch=gfx950",
+                  "waves=%d mfma=%s grid_m=%d batch_invariant=%d epilogue=%s tuning=%s layout=%d arch=gfx950",
                   fmt_name(plan.fmt, plan.layer), kind, (long long)plan.layer.n, (long long)plan.layer.k,
                   (long long)plan.layer.num_experts, (long long)M,
                   c.qtile ? "qtile" : c.tile ? "tile" : c.ws ? "wstream" : "stream",
                   c.tile || c.qtile ? c.tc.bm : c.sc.mt * 16, c.tile || c.qtile ? c.tc.bn : c.sc.nt * 16,
                   c.sc.split, c.tile || c.qtile ? c.tc.waves : c.sc.kw, mfma_name(plan.fmt, c), c.grid_m,
-                  plan.compute.batch_invariant, plan.has_tuning ? "user" : "heuristic", QDG_LAYOUT_VERSION);
+                  plan.compute.batch_invariant, plan.compute.epilogue == QDG_EPI_SILU_MUL ? "silu_mul" : "none",
+                  plan.has_tuning ? "user" : "heuristic", QDG_LAYOUT_VERSION);
 }
 
 int qdg_plan_describe(const qdg_plan* plan, int64_t M, char* buf, size_t len) {
@@ -567,6 +580,7 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   a.top_k = plan->compute.top_k;
   a.a_per_pair = a_per_pair;
   a.num_pairs = (int)rows;
+  a.epi = plan->compute.epilogue;
   a.unpack_mask = 0x000F000Fu;
   a.unpack_exp = 0x43004300u;
   const bool asym = plan->layer.wtype == QDG_W_UINT4;
@@ -668,6 +682,18 @@ qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scal
     return fail(QDG_ERR_MISALIGNED, "Y must be aligned to its element size");
   return run(plan, A, a_scales, packed, Y, T, workspace, ws_bytes, (hipStream_t)stream, true, sorted_ids,
              block_expert, num_padded, T, block_m, a_per_pair ? 1 : 0);
+}
+
+qdg_status qdg_moe_combine(const float* y, const float* w, int64_t T, int32_t top_k, int64_t n, void* out,
+                           int32_t otype, void* stream) {
+  if (T < 0 || n < 1 || top_k < 1 || top_k > 32) return fail(QDG_ERR_INVALID_ARG, "bad T, n or top_k");
+  if (otype != QDG_O_BF16 && otype != QDG_O_F32) return fail(QDG_ERR_INVALID_ARG, "otype must be BF16 or F32");
+  if (n % 4 != 0) return fail(QDG_ERR_UNSUPPORTED, "n must be a multiple of 4");
+  if (T == 0) return ok();
+  if (!y || !w || !out) return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(y, 16) || !aligned(out, 16)) return fail(QDG_ERR_MISALIGNED, "y and out must be 16-byte aligned");
+  if (!aligned(w, 4)) return fail(QDG_ERR_MISALIGNED, "w must be 4-byte aligned");
+  return hip_status(launch_moe_combine(y, w, T, top_k, n, out, otype, (hipStream_t)stream), "moe_combine launch");
 }
 
 }  // extern "C"

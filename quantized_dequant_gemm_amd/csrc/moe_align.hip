@@ -98,7 +98,41 @@ __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restri
   }
 }
 
+// Top-k weighted combine: one thread per (token, 4 columns). The top_k pair
+// rows of a token are added in ascending slot order (deterministic).
+__global__ void moe_combine_kernel(const float* __restrict__ y, const float* __restrict__ w, int64_t T,
+                                   int top_k, int64_t n, void* __restrict__ out, int otype) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = n / 4;
+  if (q >= T * per_row) return;
+  const int64_t t = q / per_row, c = (q % per_row) * 4;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < top_k; ++j) {
+    const int64_t r = t * top_k + j;
+    const float wj = w[r];
+    const float4 v = *(const float4*)(y + r * n + c);
+    s[0] = __builtin_fmaf(wj, v.x, s[0]);
+    s[1] = __builtin_fmaf(wj, v.y, s[1]);
+    s[2] = __builtin_fmaf(wj, v.z, s[2]);
+    s[3] = __builtin_fmaf(wj, v.w, s[3]);
+  }
+  if (otype == QDG_O_F32) {
+    *(float4*)((float*)out + t * n + c) = make_float4(s[0], s[1], s[2], s[3]);
+  } else {
+    uint16_t* o = (uint16_t*)out + t * n + c;
+    for (int e = 0; e < 4; ++e) o[e] = (uint16_t)f32_to_bf16_rne(s[e]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_moe_combine(const float* y, const float* w, int64_t T, int top_k, int64_t n, void* out,
+                              int otype, hipStream_t s) {
+  const int64_t threads = T * (n / 4);
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, y, w, T,
+                     top_k, n, out, otype);
+  return hipGetLastError();
+}
 
 hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int block_m,
                             int64_t capacity, int32_t* sorted_ids, int32_t* block_expert,

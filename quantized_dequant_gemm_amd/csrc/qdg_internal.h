@@ -40,6 +40,7 @@ struct GemmArgs {
   const int* block_expert;
   const int* num_padded;
   int top_k, a_per_pair, num_pairs;
+  int epi;              // output epilogue (QDG_EPI_*)
   // large-M W4A16: per (group, row) negated row sums of A
   const float* rowsum;
   int m_pad;
@@ -83,6 +84,8 @@ hipError_t launch_quantize_weights(const qdg_layer_config& L, const float* w, vo
                                    void* scales, void* zeros, hipStream_t s);
 hipError_t launch_quantize_act(int atype, const void* a, int64_t M, int64_t K, void* qa,
                                float* scales, hipStream_t s);
+hipError_t launch_moe_combine(const float* y, const float* w, int64_t T, int top_k, int64_t n, void* out,
+                              int otype, hipStream_t s);
 hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int block_m,
                             int64_t capacity, int32_t* sorted_ids, int32_t* block_expert,
                             int32_t* num_padded, hipStream_t s);

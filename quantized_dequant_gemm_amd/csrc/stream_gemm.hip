@@ -41,6 +41,7 @@ struct Ctx {
   const uint8_t* wbase;  // weight units of this expert
   const uint8_t* sbase;  // scale records of this expert
   int tile0, groups, lane, col, c, kgroups_a;
+  int tstride;           // tile t of the workgroup is tile0 + t * tstride
 };
 
 // W4A16: bf16 activations, int4/uint4 weights, fp16 group scales (fp32 in the
@@ -69,7 +70,7 @@ struct FmtW4A16 {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t < ntv) {
-        const size_t u = (size_t)(x.tile0 + t) * x.groups + g;
+        const size_t u = (size_t)(x.tile0 + t * x.tstride) * x.groups + g;
         f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
         const u32x2_t r = *((const u32x2_t*)(x.sbase) + u * 16 + x.col);
         f.s[t] = bits_as<float>(r.x);
@@ -145,7 +146,7 @@ struct FmtInt8 {
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const size_t u = (size_t)(x.tile0 + t) * x.groups + g;
+      const size_t u = (size_t)(x.tile0 + t * x.tstride) * x.groups + g;
       if (t < ntv) {
         if constexpr (W4) {
           f.b[t][0] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
@@ -223,7 +224,7 @@ struct FmtMxfp4 {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t < ntv) {
-        const size_t u = (size_t)(x.tile0 + t) * x.groups + g;
+        const size_t u = (size_t)(x.tile0 + t * x.tstride) * x.groups + g;
         f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
         f.sc[t] = x.sbase[u * 64 + x.lane];
       } else {
@@ -267,8 +268,11 @@ __global__ __launch_bounds__(64 * KW) void stream_gemm_kernel(const GemmArgs p) 
   x.col = lane & 15;
   x.c = lane >> 4;
   x.groups = p.groups;
-  x.tile0 = nb * NT;
-  const int ntv = min(NT, p.ntiles - x.tile0);
+  // SiLU*mul epilogue (NT = 2): the gate tile nb and the up tile nb + I/16
+  const bool silu = p.epi == QDG_EPI_SILU_MUL;
+  x.tile0 = silu ? nb : nb * NT;
+  x.tstride = silu ? p.ntiles / 2 : 1;
+  const int ntv = silu ? NT : min(NT, p.ntiles - x.tile0);
   int expert = 0;
   if constexpr (MOE) {
     if (mb * BM >= *p.num_padded) return;
@@ -439,9 +443,11 @@ __global__ __launch_bounds__(64 * KW) void stream_gemm_kernel(const GemmArgs p) 
         v = r < p.M;
       }
       if (!v) continue;
+      float yv[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int n = (x.tile0 + t) * 16 + x.col;
+        const int n = (x.tile0 + t * x.tstride) * 16 + x.col;
+        yv[t] = 0.f;
         if (t >= ntv || n >= p.N) continue;
         const size_t o = (size_t)yrow * p.N + n;
         if (p.otype == QDG_O_I32) {
@@ -463,10 +469,22 @@ __global__ __launch_bounds__(64 * KW) void stream_gemm_kernel(const GemmArgs p) 
         } else {
           y = acc[mt][t][i];
         }
+        yv[t] = y;
+        if (silu) continue;
         if (p.otype == QDG_O_F32)
           ((float*)p.Y)[o] = y;
         else
           ((uint16_t*)p.Y)[o] = (uint16_t)f32_to_bf16_rne(y);
+      }
+      if (silu) {
+        // gate in tile 0, up in tile 1; Y rows hold I = N / 2 columns
+        const float g = yv[0], u = yv[NT - 1];
+        const float h = g / (1.f + expf(-g)) * u;
+        const size_t o = (size_t)yrow * (p.N / 2) + nb * 16 + x.col;
+        if (p.otype == QDG_O_F32)
+          ((float*)p.Y)[o] = h;
+        else
+          ((uint16_t*)p.Y)[o] = (uint16_t)f32_to_bf16_rne(h);
       }
     }
   }

@@ -111,6 +111,26 @@ def test_describe_reports_the_instance_that_runs():
         q.qdg_moe_describe(p, 64, 16)  # not a MoE plan
 
 
+def test_epilogue_and_combine_validation():
+    lm = q.layer_w4a16(4096, 7168, num_experts=8)
+    silu = q.QDG_EPI_SILU_MUL
+    p = q.qdg_plan_create(lm, q.moe(8, epilogue=silu))
+    assert "epilogue=silu_mul" in q.qdg_moe_describe(p, 64, 16)
+    assert "family=stream" in q.qdg_moe_describe(p, 64, 16)  # weight streaming has no such epilogue
+    assert _status(q.qdg_plan_create, q.layer_w4a16(4096, 7168), q.ComputeConfig(
+        kind=q.QDG_KIND_DENSE, batch_invariant=0, top_k=0, epilogue=silu)) == q.QDG_ERR_UNSUPPORTED
+    assert _status(q.qdg_plan_create, q.layer_w4a16(4112, 7168, num_experts=8),
+                   q.moe(8, epilogue=silu)) == q.QDG_ERR_UNSUPPORTED  # I = 2056 is no multiple of 16
+    assert _status(q.qdg_plan_create, q.layer_w4a8(4096, 7168, otype=q.QDG_O_I32, num_experts=8),
+                   q.moe(8, epilogue=silu)) == q.QDG_ERR_UNSUPPORTED
+    assert _status(q.qdg_plan_create, lm, q.moe(8, epilogue=7)) == q.QDG_ERR_INVALID_ARG
+    # combine: argument checks before any device work
+    assert _status(q.qdg_moe_combine, 1, 1, 4, 8, 64, 1, q.QDG_O_I32) == q.QDG_ERR_INVALID_ARG
+    assert _status(q.qdg_moe_combine, 16, 16, 4, 8, 66, 16, q.QDG_O_BF16) == q.QDG_ERR_UNSUPPORTED
+    assert _status(q.qdg_moe_combine, 16, 16, 4, 8, 64, 8, q.QDG_O_BF16) == q.QDG_ERR_MISALIGNED
+    q.qdg_moe_combine(0, 0, 0, 8, 64, 0, q.QDG_O_BF16)  # T = 0 enqueues nothing
+
+
 def test_gemm_argument_errors_before_device_work():
     l = q.layer_w4a16(64, 128)
     p = q.qdg_plan_create(l, q.dense())

@@ -147,3 +147,50 @@ def test_moe_full_size_sampled_rows(qdg, t, bm):
         qv, s = quant.quantize_int4_sym(w_host[e])
         yr = xf[p // top_k] @ ref.dequant_int4_sym(qv, s).T
         assert metrics.rel_frob(H.to_f64(y[p]), yr) <= 2e-3
+
+
+@pytest.mark.parametrize("t,bm", [(8, 16), (64, 32), (300, 64)])
+@pytest.mark.parametrize("otype", [q.QDG_O_F32, q.QDG_O_BF16])
+def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, otype):
+    # fused gate+up (n = 2I) with the SiLU*mul epilogue: Y = silu(G) * U, [T*top_k][I]
+    E, top_k, hid, inter = 16, 4, 1024, 256
+    ids, _ = ref.route_topk(synth.router_logits(t, E, salt=t + 11), top_k)
+    qs, ss = _experts(E, 2 * inter, hid, salt=9)
+    layer = q.layer_w4a16(2 * inter, hid, num_experts=E, otype=otype)
+    qw = H.dev(np.stack([codecs.pack_nibbles(codecs.encode_int4(x)) for x in qs]))
+    sc = H.dev(np.stack(ss).view(np.int16))
+    pk = H.Packed(layer, qw, sc)
+    x = synth.activations_bf16_bits(t, hid, workload_id=4, salt=t + 12)
+    a_dev = H.bf16_dev(x)
+    sid, blk, npad, cap = _align_dev(ids, E, bm)
+    plan = q.qdg_plan_create(layer, q.moe(top_k, epilogue=q.QDG_EPI_SILU_MUL))
+    assert "epilogue=silu_mul" in q.qdg_moe_describe(plan, t, bm)
+    ws, nbytes = H.workspace(plan, t)
+    y = H.out_tensor(t * top_k, inter, otype)
+    q.qdg_moe_gemm(plan, a_dev.data_ptr(), None, pk.buf.data_ptr(), sid.data_ptr(), blk.data_ptr(),
+                   npad.data_ptr(), t, bm, 0, y.data_ptr(), ws.data_ptr(), nbytes, q.current_stream())
+    torch.cuda.synchronize()
+    gu64 = ref.moe_gemm_rows(x, ids, lambda e: ref.dequant_int4_sym(qs[e], ss[e]), input_is_per_pair=False)
+    h64 = ref.silu_mul(gu64)
+    assert not torch.isnan(y.float()).any()
+    err = metrics.rel_frob(H.to_f64(y), h64)
+    print(f"silu*mul T={t} bm={bm} otype={otype}: rel_frob={err:.3e}")
+    assert err <= (1e-3 if otype == q.QDG_O_F32 else 2e-3), err
+
+
+@pytest.mark.parametrize("t,otype", [(64, q.QDG_O_F32), (64, q.QDG_O_BF16), (1000, q.QDG_O_BF16)])
+def test_moe_combine(qdg, t, otype):
+    top_k, n = 8, 7168
+    r = np.random.default_rng(40 + t)
+    y = r.normal(size=(t * top_k, n)).astype(np.float32)
+    w = r.uniform(0.0, 0.5, t * top_k).astype(np.float32)
+    y_dev, w_dev = H.dev(y), H.dev(w)
+    out = H.out_tensor(t, n, otype)
+    q.qdg_moe_combine(y_dev.data_ptr(), w_dev.data_ptr(), t, top_k, n, out.data_ptr(), otype, q.current_stream())
+    out2 = H.out_tensor(t, n, otype)
+    q.qdg_moe_combine(y_dev.data_ptr(), w_dev.data_ptr(), t, top_k, n, out2.data_ptr(), otype, q.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)  # fixed summation order
+    ref64 = ref.moe_combine(y, w, top_k)
+    err = metrics.rel_frob(H.to_f64(out), ref64)
+    assert err <= (1e-6 if otype == q.QDG_O_F32 else 2e-3), err

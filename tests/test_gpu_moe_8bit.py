@@ -103,3 +103,26 @@ def test_moe_8bit_rejects_128_row_blocks(qdg):
                        dummy.data_ptr(), dummy.data_ptr(), 8, 128, 0, dummy.data_ptr(), ws.data_ptr(), nbytes,
                        q.current_stream())
     assert ex.value.status == q.QDG_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kind", ["w4a8", "mxfp4"])
+def test_moe_8bit_silu_mul_epilogue(qdg, kind):
+    t, bm, n, k = 64, 16, 512, 1024
+    ids, _ = ref.route_topk(synth.router_logits(t, E, salt=41), TOP_K)
+    std, dense_ref = _experts(kind, n, k, salt=42)
+    ac, sa = _acts(kind, t, k, salt=43)
+    y64, _ = ref.moe_rows(ids, 0, lambda e, rows: dense_ref(e, ac[rows], sa[rows]))
+    h64 = ref.silu_mul(y64)
+    sid, blk, npad = _align_dev(ids, bm)
+    a_dev, sa_dev = H.dev(ac), H.dev(sa)
+    layer = _layer(kind, n, k, q.QDG_O_BF16)
+    pk = H.Packed(layer, *std)
+    plan = q.qdg_plan_create(layer, q.moe(TOP_K, epilogue=q.QDG_EPI_SILU_MUL))
+    ws, nbytes = H.workspace(plan, t)
+    y = H.out_tensor(t * TOP_K, n // 2, q.QDG_O_BF16)
+    q.qdg_moe_gemm(plan, a_dev.data_ptr(), sa_dev.data_ptr(), pk.buf.data_ptr(), sid.data_ptr(), blk.data_ptr(),
+                   npad.data_ptr(), t, bm, 0, y.data_ptr(), ws.data_ptr(), nbytes, q.current_stream())
+    torch.cuda.synchronize()
+    assert not torch.isnan(y.float()).any()
+    err = metrics.rel_frob(H.to_f64(y), h64)
+    assert err <= 2e-3, err

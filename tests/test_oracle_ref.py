@@ -232,6 +232,37 @@ def test_moe_rows_brute_force_integer_experts():
     assert p2 is None and np.array_equal(y2[:, 0], ids.reshape(-1).astype(float))
 
 
+def test_silu_mul_closed_forms():
+    # silu(0) = 0, silu(1) = 1 / (1 + e^-1), silu(-x) = silu(x) - x, saturation
+    # to x and to 0, and the gate / up column split
+    g = np.array([[0.0, 1.0, -1.0, 60.0, -60.0, 2.5]])
+    u = np.array([[3.0, 2.0, 2.0, 0.5, 7.0, -1.0]])
+    h = ref.silu_mul(np.concatenate([g, u], axis=1))
+    s1 = 1.0 / (1.0 + np.exp(-1.0))
+    assert h.shape == (1, 6)
+    assert h[0, 0] == 0.0
+    assert abs(h[0, 1] - 2.0 * s1) <= 1e-15
+    assert abs(h[0, 2] - 2.0 * (s1 - 1.0)) <= 1e-15  # silu(-1) = silu(1) - 1
+    assert abs(h[0, 3] - 30.0) <= 1e-12 and abs(h[0, 4]) <= 1e-20
+    assert abs(h[0, 5] - (-2.5 / (1.0 + np.exp(-2.5)))) <= 1e-15
+    # x * sigmoid(x) against the plain formula on random values
+    r = np.random.default_rng(33)
+    y = r.normal(size=(5, 8))
+    hh = ref.silu_mul(y)
+    assert np.allclose(hh, y[:, :4] / (1.0 + np.exp(-y[:, :4])) * y[:, 4:], rtol=1e-14, atol=0)
+
+
+def test_moe_combine_brute_force():
+    t, top_k, n = 3, 4, 5
+    r = np.random.default_rng(34)
+    y = r.integers(-9, 10, (t * top_k, n)).astype(np.float64)
+    w = r.integers(1, 5, t * top_k).astype(np.float64)
+    out = ref.moe_combine(y, w, top_k)
+    for tt in range(t):
+        for c in range(n):
+            assert out[tt, c] == sum(w[tt * top_k + j] * y[tt * top_k + j, c] for j in range(top_k))
+
+
 def test_tiny_workload_oracle_shapes():
     # the tiny W4A16 workload end to end through the oracle
     a = synth.activations_bf16_bits(16, 1024, workload_id=0)
