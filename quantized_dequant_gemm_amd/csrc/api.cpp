@@ -501,7 +501,6 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   } else if (!c.ws && !stream_cfg_supported(plan.fmt, c.sc)) {
     return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
   }
-  if (silu && c.tile) return fail(QDG_ERR_UNSUPPORTED, "SiLU*mul with 128-row blocks: not yet");
   if (silu && !c.tile && c.sc.nt != 2)
     return fail(QDG_ERR_UNSUPPORTED, "the SiLU*mul epilogue pairs 2 tiles: block_n must be 32");
   *out = c;

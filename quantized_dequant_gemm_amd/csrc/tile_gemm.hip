@@ -129,6 +129,19 @@ struct Stage {
 // offset fixed for the whole K loop. Kept out of lambdas: a device-only
 // builtin inside an (implicitly host+device) lambda makes the host pass drop
 // the kernel.
+// Packed N tile behind stage tile t of a workgroup whose tiles start at
+// `base`. With the SiLU*mul epilogue (16 stage tiles) the first 8 are gate
+// tiles base.. and the last 8 the matching up tiles G + base.. (G = I / 16);
+// tiles past the layer re-read the last one and are never stored.
+__device__ __forceinline__ int stage_tile(const GemmArgs& p, int base, int t) {
+  if (p.epi == QDG_EPI_SILU_MUL) {
+    const int G = p.ntiles / 2;
+    const int j = min(base + (t & 7), G - 1);
+    return t < 8 ? j : G + j;
+  }
+  return min(base + t, p.ntiles - 1);
+}
+
 template <int BM, int BN, int NW>
 __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint32_t* a_off, const GemmArgs& p,
                                            const uint8_t* wbase, const uint8_t* sbase, uint32_t s_off,
@@ -149,8 +162,7 @@ __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint
 #pragma unroll
   for (int r = 0; r < (BN / 16) / NW; ++r) {
     const int t = r * NW + wave;
-    // tiles past the layer re-read the last tile; their results are never stored
-    const int tile = min(wg_tile0 + t, p.ntiles - 1);
+    const int tile = stage_tile(p, wg_tile0, t);
     __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * kUnit4Bytes + lane * 16,
                                      (lds_void*)(st + L::W + t * 1024), 16, 0, 0);
   }
@@ -327,7 +339,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   const uint8_t* wbase = p.packed + (size_t)expert * p.expert_stride;
   const uint8_t* sbase = wbase + p.s_offset;
   const int groups = p.groups;
-  const int wg_tile0 = nb * (BN / 16);
+  // SiLU*mul (MoE gate+up): 16 stage tiles = 8 gate + 8 up tiles, i.e. 8
+  // output tiles per workgroup
+  const bool silu = MOE && p.epi == QDG_EPI_SILU_MUL;
+  static_assert(!MOE || BN == 256, "the SiLU*mul pairing assumes 16 stage tiles");
+  const int wg_tile0 = silu ? nb * (BN / 32) : nb * (BN / 16);
 
   // A copy plan: slot q = 64 i + lane of the padded tile is row q / 17,
   // 16-byte chunk q % 17 (chunk 16 is padding: it re-reads chunk 0)
@@ -351,7 +367,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   // copy r = wave % (BN / 128)
   uint32_t s_off;
   {
-    const int s_tile = min(wg_tile0 + 8 * (wave % (BN / 128)) + (lane >> 3), p.ntiles - 1);
+    const int s_tile = stage_tile(p, wg_tile0, 8 * (wave % (BN / 128)) + (lane >> 3));
     s_off = (uint32_t)s_tile * (uint32_t)groups * 128u + (lane & 7) * 16;
   }
 
@@ -438,6 +454,58 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   // every lane stores whole 16-byte row segments
   __builtin_amdgcn_s_waitcnt(0);  // the trailing copies have landed
   __syncthreads();                 // everyone is done with the stages
+  if (silu) {
+    // gate columns sit in waves wn = 0, 1 and the matching up columns in
+    // waves wn + 2: per 16-row strip every wave parks its fp32 values in LDS,
+    // then the gate waves form silu(G) * U and store I-wide rows
+    float* own = (float*)(st0 + wave * (16 * 64 * 4));
+    const float* up = (const float*)(st0 + (wave + 2) * (16 * 64 * 4));
+    const int I = p.N / 2;
+    const bool f32o = p.otype == QDG_O_F32;
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+      if constexpr (M32) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              own[(8 * q + 4 * h + i) * 64 + cb * 32 + l32] = acc32[mt / 2][cb][(2 * (mt % 2) + q) * 4 + i];
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) own[(4 * c + i) * 64 + t * 16 + col] = acc[mt][t][i];
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (wn < 2) {
+        for (int chunk = lane; chunk < 16 * 16; chunk += 64) {  // 16 rows x 16 chunks of 4 columns
+          const int r = chunk >> 4, cc = chunk & 15;
+          const int lrow = mb * BM + wm * WTM + mt * 16 + r;
+          const int id = p.sorted_ids[lrow];
+          const int n0 = wg_tile0 * 16 + wn * 64 + cc * 4;
+          if (id >= p.num_pairs || n0 >= I) continue;
+          const f32x4_t g4 = *(const f32x4_t*)(own + r * 64 + cc * 4);
+          const f32x4_t u4 = *(const f32x4_t*)(up + r * 64 + cc * 4);
+          float hv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] = g4[e] / (1.f + expf(-g4[e])) * u4[e];
+          if (f32o) {
+            *(f32x4_t*)((float*)p.Y + (size_t)id * I + n0) = f32x4_t{hv[0], hv[1], hv[2], hv[3]};
+          } else {
+            u32x2_t pk;
+            pk.x = f32_to_bf16_rne(hv[0]) | (f32_to_bf16_rne(hv[1]) << 16);
+            pk.y = f32_to_bf16_rne(hv[2]) | (f32_to_bf16_rne(hv[3]) << 16);
+            *(u32x2_t*)((uint16_t*)p.Y + (size_t)id * I + n0) = pk;
+          }
+        }
+      }
+      __syncthreads();  // the strips are rewritten for the next 16 rows
+    }
+    return;
+  }
   // split-K: each split stores its fp32 partial tile row-major into the
   // workspace ([split][m_pad][n_pad]); reduce_splits_kernel sums them
   const bool to_partial = nsplit > 1;

@@ -149,11 +149,14 @@ def test_moe_full_size_sampled_rows(qdg, t, bm):
         assert metrics.rel_frob(H.to_f64(y[p]), yr) <= 2e-3
 
 
-@pytest.mark.parametrize("t,bm", [(8, 16), (64, 32), (300, 64)])
+@pytest.mark.parametrize("t,bm,inter", [(8, 16, 256), (64, 32, 256), (300, 64, 256), (300, 128, 256),
+                                         (1024, 128, 144)])
 @pytest.mark.parametrize("otype", [q.QDG_O_F32, q.QDG_O_BF16])
-def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, otype):
-    # fused gate+up (n = 2I) with the SiLU*mul epilogue: Y = silu(G) * U, [T*top_k][I]
-    E, top_k, hid, inter = 16, 4, 1024, 256
+def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, inter, otype):
+    # fused gate+up (n = 2I) with the SiLU*mul epilogue: Y = silu(G) * U,
+    # [T*top_k][I]; 16-64-row blocks run the streaming family, 128-row blocks
+    # the LDS-tiled one (I = 144: a workgroup tile partly past the layer)
+    E, top_k, hid = 16, 4, 1024
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=t + 11), top_k)
     qs, ss = _experts(E, 2 * inter, hid, salt=9)
     layer = q.layer_w4a16(2 * inter, hid, num_experts=E, otype=otype)
@@ -164,7 +167,8 @@ def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, otype):
     a_dev = H.bf16_dev(x)
     sid, blk, npad, cap = _align_dev(ids, E, bm)
     plan = q.qdg_plan_create(layer, q.moe(top_k, epilogue=q.QDG_EPI_SILU_MUL))
-    assert "epilogue=silu_mul" in q.qdg_moe_describe(plan, t, bm)
+    desc = q.qdg_moe_describe(plan, t, bm)
+    assert "epilogue=silu_mul" in desc and ("family=tile" in desc) == (bm == 128)
     ws, nbytes = H.workspace(plan, t)
     y = H.out_tensor(t * top_k, inter, otype)
     q.qdg_moe_gemm(plan, a_dev.data_ptr(), None, pk.buf.data_ptr(), sid.data_ptr(), blk.data_ptr(),
