@@ -185,10 +185,26 @@ def gpu_leg(args):
                     frac=round(dom["gbs"] / PEAK_HBM_GBS, 4), traffic=traffic,
                     kernel=f"w4a16 M={dom['M']} K={dom['K']} N={dom['N']}",
                     per_launch=alg_bytes(dom["M"], dom["N"], dom["K"]))
+    # the small-M cases once more as a stream of back-to-back launches (one
+    # event pair over all of them): per-launch markers add about 2 us to a
+    # 10 us kernel, back-to-back launches agree with the profiler's kernel
+    # durations
+    for c, d in zip(cases, out_cases):
+        if c["m"] > 16:
+            continue
+
+        def launch(i, c=c):
+            q.qdg_gemm(c["plan"], c["a"].data_ptr(), None, c["bufs"][i % len(c["bufs"])].data_ptr(),
+                       c["y"].data_ptr(), c["m"], c["ws"].data_ptr(), c["wsb"], sh)
+        us = _time_launches(launch, 60, stream)
+        by = alg_bytes(c["m"], c["n"], c["k"])
+        d.update(us_stream=round(us, 3), gbs_stream=round(by / us / 1e3, 1),
+                 hbm_frac_stream=round(by / us / 1e3 / PEAK_HBM_GBS, 4))
     m16 = [d for d in out_cases if d["M"] == 16]
-    roof16 = [dict(bound="hbm", achieved=d["gbs"], peak=PEAK_HBM_GBS, unit="GB/s", frac=d["hbm_frac"],
-                   frac_of_copy=round(d["gbs"] / copy_gbs, 4), kernel=f"w4a16 M=16 K={d['K']} N={d['N']}",
-                   us=d["us"], traffic=measured_traffic(f"M=16 K={d['K']} N={d['N']}", "wstream_gemm.hip"))
+    roof16 = [dict(bound="hbm", achieved=d["gbs_stream"], peak=PEAK_HBM_GBS, unit="GB/s", frac=d["hbm_frac_stream"],
+                   frac_of_copy=round(d["gbs_stream"] / copy_gbs, 4), kernel=f"w4a16 M=16 K={d['K']} N={d['N']}",
+                   us=d["us_stream"], us_with_markers=d["us"],
+                   traffic=measured_traffic(f"M=16 K={d['K']} N={d['N']}", "wstream_gemm.hip"))
               for d in m16]
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     return dict(value=value, ms_per_step=ms_per_step, roofline=roof, roofline_m16=roof16, cases=out_cases,
@@ -200,18 +216,21 @@ PEAK_FP8_TFLOPS = 5000.0
 
 
 def _time_launches(launch, reps, stream):
-    """Per-launch GPU time (us): the host first queues `reps` launches behind
-    a short spin kernel, so the events bracket kernels, not launch latency."""
+    """Average GPU time per launch (us) over `reps` back-to-back launches:
+    the host queues them behind a short spin kernel and one event pair
+    brackets them all, so the figure is the kernels' duration plus the
+    launch gaps between them (the rate a stream of such calls sustains),
+    without the host's launch latency or per-launch event markers."""
     import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(int(3e6))
+    e0.record(stream)
     for i in range(reps):
-        ev[i][0].record(stream)
         launch(i)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
-    return t[len(t) // 2]
+    return e0.elapsed_time(e1) * 1e3 / reps
 
 
 def rows_leg(reps=30):
@@ -220,8 +239,10 @@ def rows_leg(reps=30):
     {16, 256, 4096}), W4A8-MXFP4 ((K,N) in {(7168,2048), (2048,7168)}, M in
     {16, 512, 4096}), the activation quantizers, and the grouped MoE W4A16
     GEMMs (E=256, top-8, hidden 7168, intermediate 2048, T in {64, 512,
-    4096}) with their expert sort, and the grouped MoE W4A8-INT8 GEMMs of
-    the same experts at T in {64, 512}."""
+    4096}) with their expert sort, the gate+up GEMM with the SiLU*mul
+    epilogue and the top-k combine, and the grouped MoE W4A8-INT8 GEMMs of
+    the same experts at T in {64, 512}. Every figure is the average over
+    back-to-back launches."""
     import torch
     import quantized_dequant_gemm_amd as q
     import synth
@@ -307,6 +328,7 @@ def rows_leg(reps=30):
         del qw, sc
         layers[name] = (layer, pk, n, k, q.qdg_plan_create(layer, q.moe(top_k)))
         print(f"row {name}: {E} experts packed", file=sys.stderr, flush=True)
+    silu_plan = q.qdg_plan_create(layers["moe-gate-up"][0], q.moe(top_k, epilogue=q.QDG_EPI_SILU_MUL))
     for t in (64, 512, 4096):
         g = torch.Generator(device=dev)
         g.manual_seed(synth.seed_for(4, synth.TID_LOGITS, t))
@@ -353,6 +375,41 @@ def rows_leg(reps=30):
                             hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4),
                             mfma_frac=round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4), align_us=round(us_align, 3),
                             instance=q.qdg_moe_describe(plan, t, bm).split(": ", 1)[1]))
+            if not per_pair:
+                # the same gate+up GEMM with the SiLU*mul epilogue: [T*top_k][n/2] out
+                yh = torch.empty((t * top_k, n // 2), dtype=torch.bfloat16, device=dev)
+                wsb_h = q.qdg_plan_workspace(silu_plan, t)
+                ws_h = torch.zeros(max(wsb_h, 1), dtype=torch.uint8, device=dev)
+
+                def gemm_h(i):
+                    q.qdg_moe_gemm(silu_plan, a.data_ptr(), None, pk.data_ptr(), sorted_ids.data_ptr(),
+                                   block_expert.data_ptr(), npad.data_ptr(), t, bm, 0, yh.data_ptr(),
+                                   ws_h.data_ptr(), wsb_h, sh)
+                gemm_h(0)
+                us = _time_launches(gemm_h, max(5, reps // 3), stream)
+                by = touched * (n * k // 2 + n * (k // 128) * 2) + rows_in * k * 2 + t * top_k * (n // 2) * 2
+                print(f"row moe-gate-up-silu T={t}: {us:.2f} us", file=sys.stderr, flush=True)
+                out.append(dict(row="moe-gate-up-silu", T=t, K=k, N=n, block_m=bm, experts_touched=touched,
+                                us=round(us, 3), tflops=round(fl / us / 1e6, 2), gbs=round(by / us / 1e3, 1),
+                                hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4),
+                                mfma_frac=round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4),
+                                instance=q.qdg_moe_describe(silu_plan, t, bm).split(": ", 1)[1]))
+                del yh, ws_h
+            else:
+                # top-k weighted combine of the down projection's pair rows
+                y32 = torch.empty((t * top_k, n), dtype=torch.float32, device=dev)
+                rw = torch.rand(t * top_k, dtype=torch.float32, device=dev)
+                yo = torch.empty((t, n), dtype=torch.bfloat16, device=dev)
+
+                def comb(i):
+                    q.qdg_moe_combine(y32.data_ptr(), rw.data_ptr(), t, top_k, n, yo.data_ptr(), q.QDG_O_BF16, sh)
+                comb(0)
+                us = _time_launches(comb, reps, stream)
+                by = t * top_k * (n * 4 + 4) + t * n * 2
+                print(f"row moe-combine T={t}: {us:.2f} us", file=sys.stderr, flush=True)
+                out.append(dict(row="moe-combine", T=t, N=n, top_k=top_k, us=round(us, 3),
+                                gbs=round(by / us / 1e3, 1), hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4)))
+                del y32, rw, yo
 
     # ---- grouped MoE W4A8-INT8 (the same experts; int8 activations per token
     # for gate+up and per pair for down; streaming family)
