@@ -248,9 +248,9 @@ qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int3
    rows are written only for real pairs. A and a_scales are laid out as for
    qdg_gemm with one row per r (the int8 / fp8 formats take the codes and
    scales of qdg_quantize_act over those rows). block_m must be the value
-   passed to qdg_moe_align. W4A16: 16 (weight-streaming family), 32 or 64
-   (streaming family) or 128 (LDS-tiled family; batch-invariant plans take
-   16 to 64). W8A8, W4A8-INT8, W4A8-MXFP4: 16, 32 or 64 (streaming family;
+   passed to qdg_moe_align. W4A16: 16, 32 or 64 (streaming family; a tuning
+   with block_n 64 and 8 waves pins the weight-streaming family for 16) or
+   128 (LDS-tiled family; batch-invariant plans take 16 to 64). W8A8, W4A8-INT8, W4A8-MXFP4: 16, 32 or 64 (streaming family;
    128 returns QDG_ERR_UNSUPPORTED). */
 qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scales,
                         const void* packed, const int32_t* sorted_ids,

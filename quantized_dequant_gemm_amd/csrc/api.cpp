@@ -464,15 +464,14 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   const int64_t cap = align_up(rows + E * (block_m - 1), block_m);
   c.grid_m = (int)(cap / block_m);
   const qdg_tuning_config& tu = plan.tuning;
-  // 16-row blocks: weight streaming for long K ranges (its chunked kernel);
-  // when K fits the resident kernel (<= 32 groups) the streaming family is
-  // faster per block (measured on MI355X: no per-block staging of A), unless
-  // a tuning pins weight streaming
+  // 16-row blocks: the streaming family with four 16-column tiles per wave
+  // (measured on MI355X at E = 256, hidden 7168: 29 % faster than weight
+  // streaming for gate+up at T = 64, a few % for down and at T = 512, since
+  // each expert block would otherwise restage its A rows per workgroup),
+  // unless a tuning pins weight streaming
   const bool ws_pinned = plan.has_tuning && tu.block_n == 64 && tu.waves == 8;
   const bool silu = plan.compute.epilogue == QDG_EPI_SILU_MUL;  // weight streaming has no such epilogue
-  c.ws = block_m == 16 && !plan.compute.batch_invariant && !silu &&
-         (!plan.has_tuning || ((!tu.block_n || tu.block_n == 64) && (!tu.waves || tu.waves == 8))) &&
-         (plan.geom.groups > 32 || ws_pinned);
+  c.ws = block_m == 16 && !plan.compute.batch_invariant && !silu && ws_pinned;
   if (plan.fmt != FMT_W4A16) {
     // int8 / fp8 activations: the streaming family, block_m / 16 row tiles
     if (block_m > 64)
@@ -485,7 +484,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   }
   if (c.ws) c.sc = StreamCfg{1, 4, 8, 1};  // 16 x 64 per workgroup of 8 waves
   else if (!plan.has_tuning || c0.tile || c0.ws || !stream_cfg_supported(plan.fmt, c.sc))
-    c.sc = StreamCfg{block_m / 16, 2, 4, 1};
+    c.sc = StreamCfg{block_m / 16, block_m == 16 && !silu ? 4 : 2, 4, 1};  // SiLU*mul pairs 2 tiles
   c.tile = false;
   c.qtile = false;
   if (block_m == 128) {

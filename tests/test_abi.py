@@ -102,7 +102,10 @@ def test_describe_reports_the_instance_that_runs():
     assert "family=stream" in q.qdg_plan_describe(pb, 100)
     # grouped MoE: the caller's block size picks the family
     pm = q.qdg_plan_create(q.layer_w4a16(4096, 7168, num_experts=256), q.moe(8))
-    assert "family=wstream" in q.qdg_moe_describe(pm, 64, 16)
+    d16 = q.qdg_moe_describe(pm, 64, 16)
+    assert "family=stream" in d16 and "block_n=64" in d16
+    pw = q.qdg_plan_create(q.layer_w4a16(4096, 7168, num_experts=256), q.moe(8), q.TuningConfig(block_n=64, waves=8))
+    assert "family=wstream" in q.qdg_moe_describe(pw, 64, 16)
     assert "family=stream" in q.qdg_moe_describe(pm, 512, 32)
     assert "family=tile" in q.qdg_moe_describe(pm, 4096, 128)
     with pytest.raises(q.QdgError):

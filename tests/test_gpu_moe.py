@@ -111,7 +111,10 @@ def test_moe_single_expert_equals_dense(qdg, bm, pin_ws):
     if bm == 16 and pin_ws:
         t1 = q.TuningConfig(block_m=16, block_n=64, split_k=1)
         yd = torch.cat([H.w4a16(x[r:r + 16], qs[0], ss[0], None, tuning=t1) for r in range(0, t, 16)])
-    elif bm <= 32:
+    elif bm == 16:
+        t1 = q.TuningConfig(block_m=16, block_n=64, waves=4, split_k=1)
+        yd = H.w4a16(x, qs[0], ss[0], None, tuning=t1)
+    elif bm == 32:
         t1 = q.TuningConfig(block_m=bm, block_n=32, split_k=1)
         yd = H.w4a16(x, qs[0], ss[0], None, tuning=t1)
     else:
