@@ -608,6 +608,12 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
     e = plan->fmt == FMT_W4A16 ? launch_wstream(asym, moe, a, c.sc.split, c.grid_m, stream)
                                : launch_wstream8(plan->fmt, a, c.sc.split, c.sc.nt, stream);
   } else {
+    // the streaming family addresses A with 31-bit byte offsets
+    const int64_t a_rows = moe ? (a_per_pair ? rows : T) : M;
+    a.a_bytes = a_rows * (int64_t)a.K * (plan->fmt == FMT_W4A16 ? 2 : 1);
+    if (a.a_bytes >= ((int64_t)1 << 31))
+      return fail(QDG_ERR_UNSUPPORTED, "A of %lld bytes is too large for the streaming family (< 2 GiB)",
+                  (long long)a.a_bytes);
     e = launch_stream(plan->fmt, asym, moe, c.sc, a, c.grid_m, stream);
   }
   if (e == hipErrorInvalidValue) return fail(QDG_ERR_UNSUPPORTED, "no kernel instance for this tuning");

@@ -47,6 +47,9 @@ struct GemmArgs {
   // unpack constants, passed at run time so the compiler keeps them in
   // registers (0x000F000F and 0x43004300)
   uint32_t unpack_mask, unpack_exp;
+  // bytes of A (the streaming family reads A through a buffer resource of
+  // this size: < 2^31, checked by the host)
+  int64_t a_bytes;
 };
 
 // A kernel instance of the streaming (small-M) family.

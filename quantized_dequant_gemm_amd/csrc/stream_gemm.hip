@@ -34,12 +34,23 @@ namespace {
 // accumulator type), load(), compute() and value() (final scaling of one
 // accumulator element into the output domain).
 
+constexpr uint32_t kAOob = 0x80000000u;  // past every A (the host keeps A < 2^31 bytes)
+
+__device__ __forceinline__ u32x4_t lda(const __amdgpu_buffer_rsrc_t& r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 struct Ctx {
-  const char* arow[4];   // A row of this lane for each M tile
-  bool avalid[4];
-  int arow_idx[4];       // logical row index (for activation scales)
+  // A through a buffer resource: the byte offset of this lane's row for each
+  // M tile, or kAOob for a padding row, whose loads then return zeros without
+  // a memory access (the load is still issued, so every path issues the same
+  // loads)
+  __amdgpu_buffer_rsrc_t arsrc;
+  uint32_t aoff[4];
+  int as_row[4][4];      // A row of the D rows 4c+i of each M tile (fp8 activation scales)
   const uint8_t* wbase;  // weight units of this expert
   const uint8_t* sbase;  // scale records of this expert
+  const float* a_scales; // activation scales (fp8 activations)
   int tile0, groups, lane, col, c, kgroups_a;
   int tstride;           // tile t of the workgroup is tile0 + t * tstride
 };
@@ -63,27 +74,21 @@ struct FmtW4A16 {
   __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g, int ntv) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const u32x4_t* pa = (const u32x4_t*)(x.arow[mt] + ((size_t)g * 128 + 32 * x.c) * 2);
+      const uint32_t o = x.aoff[mt] + (uint32_t)(g * 256 + 64 * x.c);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) f.a[mt][j] = x.avalid[mt] ? pa[j] : u32x4_t{0, 0, 0, 0};
+      for (int j = 0; j < 4; ++j) f.a[mt][j] = lda(x.arsrc, o + 16 * j);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (t < ntv) {
-        const size_t u = (size_t)(x.tile0 + t * x.tstride) * x.groups + g;
-        f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
-        const u32x2_t r = *((const u32x2_t*)(x.sbase) + u * 16 + x.col);
-        f.s[t] = bits_as<float>(r.x);
-        f.o[t] = r.y;
-      } else {
-        f.b[t] = u32x4_t{0, 0, 0, 0};
-        f.s[t] = 0.f;
-        f.o[t] = 0;
-      }
+      const size_t u = (size_t)(x.tile0 + (t < ntv ? t : ntv - 1) * x.tstride) * x.groups + g;
+      f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
+      const u32x2_t r = *((const u32x2_t*)(x.sbase) + u * 16 + x.col);
+      f.s[t] = bits_as<float>(r.x);
+      f.o[t] = r.y;
     }
   }
   template <int MT, int NT>
-  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT]) {
+  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT], uint32_t um, uint32_t ue) {
     f32x4_t corr[MT];
     if constexpr (!ASYM) {
       const u32x4_t k136 = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};  // bf16 -136
@@ -99,7 +104,7 @@ struct FmtW4A16 {
     for (int t = 0; t < NT; ++t) {
       u32x4_t bw[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bw[j] = unpack_u4_bf16_offset128(f.b[t][j]);
+      for (int j = 0; j < 4; ++j) bw[j] = unpack_u4_bf16_offset128(f.b[t][j], um, ue);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x4_t p;
@@ -140,32 +145,26 @@ struct FmtInt8 {
   __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g, int ntv) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const u32x4_t* pa = (const u32x4_t*)(x.arow[mt] + (size_t)g * 128 + 32 * x.c);
+      const uint32_t o = x.aoff[mt] + (uint32_t)(g * 128 + 32 * x.c);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) f.a[mt][j] = x.avalid[mt] ? pa[j] : u32x4_t{0, 0, 0, 0};
+      for (int j = 0; j < 2; ++j) f.a[mt][j] = lda(x.arsrc, o + 16 * j);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const size_t u = (size_t)(x.tile0 + t * x.tstride) * x.groups + g;
-      if (t < ntv) {
-        if constexpr (W4) {
-          f.b[t][0] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
-          f.s[t] = RAW ? 0.f : *((const float*)x.sbase + u * 16 + x.col);
-        } else {
-          const u32x4_t* pu = (const u32x4_t*)(x.wbase + u * kUnit8Bytes);
-          f.b[t][0] = ldg_nt(pu + x.lane);
-          f.b[t][1] = ldg_nt(pu + 64 + x.lane);
-          f.s[t] = 0.f;
-        }
+      const size_t u = (size_t)(x.tile0 + (t < ntv ? t : ntv - 1) * x.tstride) * x.groups + g;
+      if constexpr (W4) {
+        f.b[t][0] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
+        f.s[t] = RAW ? 0.f : *((const float*)x.sbase + u * 16 + x.col);
       } else {
-#pragma unroll
-        for (int j = 0; j < (W4 ? 1 : 2); ++j) f.b[t][j] = u32x4_t{0, 0, 0, 0};
+        const u32x4_t* pu = (const u32x4_t*)(x.wbase + u * kUnit8Bytes);
+        f.b[t][0] = ldg_nt(pu + x.lane);
+        f.b[t][1] = ldg_nt(pu + 64 + x.lane);
         f.s[t] = 0.f;
       }
     }
   }
   template <int MT, int NT>
-  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT]) {
+  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT], uint32_t um, uint32_t ue) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       u32x4_t b0, b1;
@@ -212,29 +211,24 @@ struct FmtMxfp4 {
     // (bytes 16-31); the fp4 operand holds K 32c..32c+31 contiguously
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const char* pa = x.arow[mt] + (size_t)g * 128 + 16 * x.c;
-      f.a[mt][0] = x.avalid[mt] ? *(const u32x4_t*)pa : u32x4_t{0, 0, 0, 0};
-      f.a[mt][1] = x.avalid[mt] ? *(const u32x4_t*)(pa + 64) : u32x4_t{0, 0, 0, 0};
+      const uint32_t o = x.aoff[mt] + (uint32_t)(g * 128 + 16 * x.c);
+      f.a[mt][0] = lda(x.arsrc, o);
+      f.a[mt][1] = lda(x.arsrc, o + 64);
     }
     // activation scales of the D rows this lane holds: rows 4c+i of each tile
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f.as[mt][i] = 0.f;
+      for (int i = 0; i < 4; ++i) f.as[mt][i] = x.a_scales[(size_t)x.as_row[mt][i] * x.groups + g];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (t < ntv) {
-        const size_t u = (size_t)(x.tile0 + t * x.tstride) * x.groups + g;
-        f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
-        f.sc[t] = x.sbase[u * 64 + x.lane];
-      } else {
-        f.b[t] = u32x4_t{0, 0, 0, 0};
-        f.sc[t] = 127;
-      }
+      const size_t u = (size_t)(x.tile0 + (t < ntv ? t : ntv - 1) * x.tstride) * x.groups + g;
+      f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
+      f.sc[t] = x.sbase[u * 64 + x.lane];
     }
   }
   template <int MT, int NT>
-  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT]) {
+  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT], uint32_t um, uint32_t ue) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const i32x8_t b = {(int)f.b[t].x, (int)f.b[t].y, (int)f.b[t].z, (int)f.b[t].w, 0, 0, 0, 0};
@@ -253,7 +247,7 @@ struct FmtMxfp4 {
 // ----------------------------------------------------------------- kernel
 
 template <class F, int MT, int NT, int KW, int U, bool MOE>
-__global__ __launch_bounds__(64 * KW) void stream_gemm_kernel(const GemmArgs p) {
+__global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT <= 4 ? 2 : 1))) void stream_gemm_kernel(const GemmArgs p) {
   using Acc = typename F::Acc;
   using Frag = typename F::template Frag<MT, NT>;
   // `wave` must be wave-uniform (an SGPR): every guard around an MFMA has to
@@ -285,20 +279,29 @@ __global__ __launch_bounds__(64 * KW) void stream_gemm_kernel(const GemmArgs p) 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mb * BM + mt * 16 + x.col;
-    int src = r;
-    bool v;
+    uint32_t off = kAOob;
     if constexpr (MOE) {
       const int id = p.sorted_ids[r];
-      v = id < p.num_pairs;
-      src = v ? (p.a_per_pair ? id : id / p.top_k) : 0;
+      if (id < p.num_pairs) off = (uint32_t)((size_t)(p.a_per_pair ? id : id / p.top_k) * a_row_bytes);
     } else {
-      v = r < p.M;
-      src = v ? r : 0;
+      if (r < p.M) off = (uint32_t)((size_t)r * a_row_bytes);
     }
-    x.avalid[mt] = v;
-    x.arow[mt] = (const char*)p.A + (size_t)src * a_row_bytes;
-    x.arow_idx[mt] = src;
+    x.aoff[mt] = off;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int rr = mb * BM + mt * 16 + 4 * x.c + ii;
+      int srr = 0;
+      if constexpr (MOE) {
+        const int id = p.sorted_ids[rr];
+        srr = id < p.num_pairs ? (p.a_per_pair ? id : id / p.top_k) : 0;
+      } else {
+        srr = rr < p.M ? rr : 0;
+      }
+      x.as_row[mt][ii] = srr;
+    }
   }
+  x.a_scales = p.a_scales;
+  x.arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), (short)0, (int)p.a_bytes, 0x00020000);
 
   const int g0 = (int)(((int64_t)split * p.groups) / p.split);
   const int g1 = (int)(((int64_t)(split + 1) * p.groups) / p.split);
@@ -311,45 +314,46 @@ __global__ __launch_bounds__(64 * KW) void stream_gemm_kernel(const GemmArgs p) 
     for (int t = 0; t < NT; ++t) acc[mt][t] = Acc{0, 0, 0, 0};
 
   Frag fa[U], fb[U];
+  // Every chunk issues the same loads on every path (groups past this wave's
+  // last one re-read that group), so the compiler's load waits stay exact and
+  // the next chunk's loads remain in flight while the current one computes;
+  // a conditional load would make every wait a wait for all loads.
   auto load_chunk = [&](Frag(&f)[U], int i) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (i + u < cnt) {
-        const int g = g0 + wave + KW * (i + u);
-        F::template load<MT, NT>(f[u], x, g, ntv);
-        if constexpr (std::is_same<F, FmtMxfp4>::value) {
+    for (int u = 0; u < U; ++u) {
+      const int gi = i + u < cnt ? i + u : cnt - 1;
+      F::template load<MT, NT>(f[u], x, g0 + wave + KW * gi, ntv);
+    }
+  };
+  // W4A16 unpack constants in registers (a VGPR mask and a scalar exponent):
+  // each unpacked dword is then one v_and_or_b32 (VOP3 takes no literals)
+  uint32_t um;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(um) : "s"(0x000F000Fu));
+  const uint32_t ue = 0x43004300u;
+  auto compute_full = [&](const Frag(&f)[U]) {
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-              const int r = mb * BM + mt * 16 + 4 * x.c + ii;
-              int src = r;
-              bool v;
-              if constexpr (MOE) {
-                const int id = p.sorted_ids[r];
-                v = id < p.num_pairs;
-                src = v ? (p.a_per_pair ? id : id / p.top_k) : 0;
-              } else {
-                v = r < p.M;
-              }
-              f[u].as[mt][ii] = v ? p.a_scales[(size_t)src * p.groups + g] : 0.f;
-            }
-        }
-      }
+    for (int u = 0; u < U; ++u) F::template compute<MT, NT>(f[u], acc, um, ue);
   };
   auto compute_chunk = [&](const Frag(&f)[U], int i) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (i + u < cnt) F::template compute<MT, NT>(f[u], acc);
+      if (i + u < cnt) F::template compute<MT, NT>(f[u], acc, um, ue);
   };
   if (cnt > 0) {
     load_chunk(fa, 0);
-    for (int i = 0; i < cnt; i += 2 * U) {
-      if (i + U < cnt) load_chunk(fb, i + U);
-      compute_chunk(fa, i);
-      if (i + U >= cnt) break;
-      if (i + 2 * U < cnt) load_chunk(fa, i + 2 * U);
+    int i = 0;
+    for (; i + 2 * U < cnt; i += 2 * U) {  // chunks i, i + U complete; chunk i + 2U started
+      load_chunk(fb, i + U);
+      compute_full(fa);
+      load_chunk(fa, i + 2 * U);
+      compute_full(fb);
+    }
+    if (i + U < cnt) {
+      load_chunk(fb, i + U);
+      compute_full(fa);
       compute_chunk(fb, i + U);
+    } else {
+      compute_chunk(fa, i);
     }
   }
 
