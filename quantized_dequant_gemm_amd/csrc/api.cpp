@@ -484,7 +484,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   }
   if (c.ws) c.sc = StreamCfg{1, 4, 8, 1};  // 16 x 64 per workgroup of 8 waves
   else if (!plan.has_tuning || c0.tile || c0.ws || !stream_cfg_supported(plan.fmt, c.sc))
-    c.sc = StreamCfg{block_m / 16, block_m == 16 && !silu ? 4 : 2, 4, 1};  // SiLU*mul pairs 2 tiles
+    c.sc = StreamCfg{block_m / 16, block_m == 16 ? 4 : 2, 4, 1};
   c.tile = false;
   c.qtile = false;
   if (block_m == 128) {
@@ -500,8 +500,8 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   } else if (!c.ws && !stream_cfg_supported(plan.fmt, c.sc)) {
     return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
   }
-  if (silu && !c.tile && c.sc.nt != 2)
-    return fail(QDG_ERR_UNSUPPORTED, "the SiLU*mul epilogue pairs 2 tiles: block_n must be 32");
+  if (silu && !c.tile && c.sc.nt != 2 && c.sc.nt != 4)
+    return fail(QDG_ERR_UNSUPPORTED, "the SiLU*mul epilogue pairs gate and up tiles: block_n must be 32 or 64");
   *out = c;
   return QDG_OK;
 }

@@ -51,8 +51,9 @@ struct Ctx {
   const uint8_t* wbase;  // weight units of this expert
   const uint8_t* sbase;  // scale records of this expert
   const float* a_scales; // activation scales (fp8 activations)
-  int tile0, groups, lane, col, c, kgroups_a;
-  int tstride;           // tile t of the workgroup is tile0 + t * tstride
+  int groups, lane, col, c, kgroups_a;
+  int tile[4];           // N tile of slot t (clamped into the layer; see tvalid)
+  bool tvalid[4];        // slot t holds a real tile
 };
 
 // W4A16: bf16 activations, int4/uint4 weights, fp16 group scales (fp32 in the
@@ -71,7 +72,7 @@ struct FmtW4A16 {
     uint32_t o[NT];
   };
   template <int MT, int NT>
-  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g, int ntv) {
+  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint32_t o = x.aoff[mt] + (uint32_t)(g * 256 + 64 * x.c);
@@ -80,7 +81,7 @@ struct FmtW4A16 {
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const size_t u = (size_t)(x.tile0 + (t < ntv ? t : ntv - 1) * x.tstride) * x.groups + g;
+      const size_t u = (size_t)x.tile[t] * x.groups + g;
       f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
       const u32x2_t r = *((const u32x2_t*)(x.sbase) + u * 16 + x.col);
       f.s[t] = bits_as<float>(r.x);
@@ -142,7 +143,7 @@ struct FmtInt8 {
     float s[NT];
   };
   template <int MT, int NT>
-  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g, int ntv) {
+  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint32_t o = x.aoff[mt] + (uint32_t)(g * 128 + 32 * x.c);
@@ -151,7 +152,7 @@ struct FmtInt8 {
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const size_t u = (size_t)(x.tile0 + (t < ntv ? t : ntv - 1) * x.tstride) * x.groups + g;
+      const size_t u = (size_t)x.tile[t] * x.groups + g;
       if constexpr (W4) {
         f.b[t][0] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
         f.s[t] = RAW ? 0.f : *((const float*)x.sbase + u * 16 + x.col);
@@ -205,7 +206,7 @@ struct FmtMxfp4 {
     uint32_t sc[NT];
   };
   template <int MT, int NT>
-  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g, int ntv) {
+  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g) {
     // the fp8 operand of the 16x16x128 scaled MFMA is split in two K halves:
     // lane group c holds K 16c..16c+15 (bytes 0-15) and 64+16c..64+16c+15
     // (bytes 16-31); the fp4 operand holds K 32c..32c+31 contiguously
@@ -222,7 +223,7 @@ struct FmtMxfp4 {
       for (int i = 0; i < 4; ++i) f.as[mt][i] = x.a_scales[(size_t)x.as_row[mt][i] * x.groups + g];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const size_t u = (size_t)(x.tile0 + (t < ntv ? t : ntv - 1) * x.tstride) * x.groups + g;
+      const size_t u = (size_t)x.tile[t] * x.groups + g;
       f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
       f.sc[t] = x.sbase[u * 64 + x.lane];
     }
@@ -264,9 +265,25 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
   x.groups = p.groups;
   // SiLU*mul epilogue (NT = 2): the gate tile nb and the up tile nb + I/16
   const bool silu = p.epi == QDG_EPI_SILU_MUL;
-  x.tile0 = silu ? nb : nb * NT;
-  x.tstride = silu ? p.ntiles / 2 : 1;
-  const int ntv = silu ? NT : min(NT, p.ntiles - x.tile0);
+  // Slot t of the workgroup holds N tile nb * NT + t; with the SiLU*mul
+  // epilogue slots t < NT/2 hold gate tiles nb * NT/2 + t and slots NT/2 + t
+  // the matching up tiles, G = ntiles / 2 further on. Slots past the layer
+  // re-read its last tile (every path issues the same loads) and are never
+  // stored.
+  constexpr int TP = NT > 1 ? NT / 2 : 1;
+  const int G = p.ntiles / 2;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (silu) {
+      const int j = nb * TP + t % TP;
+      x.tvalid[t] = j < G;
+      x.tile[t] = (j < G ? j : G - 1) + (t / TP) * G;
+    } else {
+      const int j = nb * NT + t;
+      x.tvalid[t] = j < p.ntiles;
+      x.tile[t] = j < p.ntiles ? j : p.ntiles - 1;
+    }
+  }
   int expert = 0;
   if constexpr (MOE) {
     if (mb * BM >= *p.num_padded) return;
@@ -322,7 +339,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int gi = i + u < cnt ? i + u : cnt - 1;
-      F::template load<MT, NT>(f[u], x, g0 + wave + KW * gi, ntv);
+      F::template load<MT, NT>(f[u], x, g0 + wave + KW * gi);
     }
   };
   // W4A16 unpack constants in registers (a VGPR mask and a scalar exponent):
@@ -450,9 +467,9 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
       float yv[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int n = (x.tile0 + t * x.tstride) * 16 + x.col;
+        const int n = x.tile[t] * 16 + x.col;
         yv[t] = 0.f;
-        if (t >= ntv || n >= p.N) continue;
+        if (!x.tvalid[t] || n >= p.N) continue;
         const size_t o = (size_t)yrow * p.N + n;
         if (p.otype == QDG_O_I32) {
           int v = bits_as<int>(acc[mt][t][i]);
@@ -481,14 +498,18 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
           ((uint16_t*)p.Y)[o] = (uint16_t)f32_to_bf16_rne(y);
       }
       if (silu) {
-        // gate in tile 0, up in tile 1; Y rows hold I = N / 2 columns
-        const float g = yv[0], u = yv[NT - 1];
-        const float h = g / (1.f + expf(-g)) * u;
-        const size_t o = (size_t)yrow * (p.N / 2) + nb * 16 + x.col;
-        if (p.otype == QDG_O_F32)
-          ((float*)p.Y)[o] = h;
-        else
-          ((uint16_t*)p.Y)[o] = (uint16_t)f32_to_bf16_rne(h);
+        // gate in slot t, up in slot t + NT/2; Y rows hold I = N / 2 columns
+#pragma unroll
+        for (int t = 0; t < TP; ++t) {
+          if (!x.tvalid[t]) continue;
+          const float g = yv[t], u = yv[t + TP];
+          const float h = g / (1.f + expf(-g)) * u;
+          const size_t o = (size_t)yrow * (p.N / 2) + (nb * TP + t) * 16 + x.col;
+          if (p.otype == QDG_O_F32)
+            ((float*)p.Y)[o] = h;
+          else
+            ((uint16_t*)p.Y)[o] = (uint16_t)f32_to_bf16_rne(h);
+        }
       }
     }
   }

@@ -152,13 +152,15 @@ def test_moe_full_size_sampled_rows(qdg, t, bm):
         assert metrics.rel_frob(H.to_f64(y[p]), yr) <= 2e-3
 
 
-@pytest.mark.parametrize("t,bm,inter", [(8, 16, 256), (64, 32, 256), (300, 64, 256), (300, 128, 256),
-                                         (1024, 128, 144)])
+@pytest.mark.parametrize("t,bm,inter", [(8, 16, 256), (64, 16, 144), (64, 32, 256), (300, 64, 256),
+                                         (300, 64, 144), (300, 128, 256), (1024, 128, 144)])
 @pytest.mark.parametrize("otype", [q.QDG_O_F32, q.QDG_O_BF16])
 def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, inter, otype):
     # fused gate+up (n = 2I) with the SiLU*mul epilogue: Y = silu(G) * U,
-    # [T*top_k][I]; 16-64-row blocks run the streaming family, 128-row blocks
-    # the LDS-tiled one (I = 144: a workgroup tile partly past the layer)
+    # [T*top_k][I]; 16-64-row blocks run the streaming family (four tiles,
+    # two gate + two up, per workgroup at 16 rows, else two), 128-row blocks
+    # the LDS-tiled one (I = 144: an odd number of gate tiles, so a
+    # workgroup's tile slots run partly past the layer)
     E, top_k, hid = 16, 4, 1024
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=t + 11), top_k)
     qs, ss = _experts(E, 2 * inter, hid, salt=9)
