@@ -223,6 +223,32 @@ int qdg_moe_describe(const qdg_plan* plan, int64_t T, int32_t block_m, char* buf
 qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, const void* packed,
                     void* Y, int64_t M, void* workspace, size_t ws_bytes, void* stream);
 
+/* Per-M-range autotuning of a dense plan (the pages' per-device tuning of
+   the kernel instances per M range, with heuristics as the fallback:
+   kinachrichten, "Kompilierzeiten und gerätespezifisches Tuning"; jetabc,
+   "Humming 的做法", item 2). Times every kernel instance that can serve M
+   rows (weight streaming with several K splits, streaming with every row
+   block and tile count, LDS-tiled shapes) on the caller's buffers, with one
+   untimed launch and then reps launches between two events on stream, and
+   records the fastest for M's range: M in (2^(b-1), 2^b], b = 0..31. Later
+   qdg_gemm, qdg_plan_workspace and qdg_plan_describe calls with an M in that
+   range use it ("tuning=autotuned"). Arguments as for qdg_gemm; instances
+   whose workspace exceeds ws_bytes are skipped (query qdg_plan_workspace
+   again afterwards). Blocks until the timing is done; Y holds the GEMM
+   result of the chosen instance on return. chosen (may be NULL) receives
+   the winning tuning, which a later plan may take as its user tuning;
+   best_us (may be NULL) its time per launch in microseconds. Only dense
+   plans without a user tuning and without batch invariance are tuned
+   (else QDG_ERR_UNSUPPORTED); reps in [1, 1000]. The call modifies the
+   plan: no other call may use the plan concurrently. */
+qdg_status qdg_plan_autotune(qdg_plan* plan, const void* A, const float* a_scales, const void* packed, void* Y,
+                             int64_t M, void* workspace, size_t ws_bytes, int32_t reps, void* stream,
+                             qdg_tuning_config* chosen, float* best_us);
+
+/* Forgets every autotuned range of the plan (the heuristics serve again).
+   Not concurrently with other calls on the plan. */
+qdg_status qdg_plan_autotune_reset(qdg_plan* plan);
+
 /* Capacity (entries of sorted_ids) that qdg_moe_align may need:
    round_up(T*top_k + E*(block_m-1), block_m); block_expert needs
    capacity/block_m entries. */

@@ -34,7 +34,7 @@ EXPORTS = (
     "qdg_version", "qdg_last_error", "qdg_validate_layer", "qdg_preprocess_query", "qdg_preprocess",
     "qdg_quantize_weights", "qdg_quantize_act", "qdg_plan_create", "qdg_plan_destroy", "qdg_plan_workspace",
     "qdg_plan_describe", "qdg_moe_describe", "qdg_gemm", "qdg_moe_align_capacity", "qdg_moe_align",
-    "qdg_moe_gemm", "qdg_moe_combine",
+    "qdg_moe_gemm", "qdg_moe_combine", "qdg_plan_autotune", "qdg_plan_autotune_reset",
 )
 
 
@@ -96,6 +96,8 @@ def load():
         "qdg_moe_align": (I32, [P, I64, I32, I32, I32, P, P, P, P]),
         "qdg_moe_gemm": (I32, [P, P, P, P, P, P, P, I64, I32, I32, P, P, SZ, P]),
         "qdg_moe_combine": (I32, [P, P, I64, I32, I64, P, I32, P]),
+        "qdg_plan_autotune": (I32, [P, P, P, P, P, I64, P, SZ, I32, P, P, P]),
+        "qdg_plan_autotune_reset": (I32, [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -222,6 +224,19 @@ def qdg_moe_gemm(plan, A, a_scales, packed, sorted_ids, block_expert, num_padded
 
 def qdg_moe_combine(y, w, T, top_k, n, out, otype, stream=0):
     _check(load().qdg_moe_combine(y, w, T, top_k, n, out, otype, stream))
+
+
+def qdg_plan_autotune(plan, A, a_scales, packed, Y, M, workspace, ws_bytes, reps=10, stream=0):
+    """Returns (chosen TuningConfig, best time per launch in us)."""
+    chosen = TuningConfig()
+    us = ctypes.c_float()
+    _check(load().qdg_plan_autotune(plan.handle, A, a_scales, packed, Y, M, workspace, ws_bytes, reps, stream,
+                                    ctypes.byref(chosen), ctypes.byref(us)))
+    return chosen, us.value
+
+
+def qdg_plan_autotune_reset(plan):
+    _check(load().qdg_plan_autotune_reset(plan.handle))
 
 
 # ------------------------------------------------------------- config helpers

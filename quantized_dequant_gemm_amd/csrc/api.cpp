@@ -86,6 +86,14 @@ PackedGeom packed_geom(const qdg_layer_config& L, Format f) {
 
 }  // namespace qdg
 
+// One autotuned M range: M in (2^(b-1), 2^b] for entry b (entry 0: M = 1).
+struct AutoEntry {
+  bool valid;
+  qdg_tuning_config tuning;
+  float us;
+};
+constexpr int kAutoRanges = 32;
+
 struct qdg_plan {
   qdg_layer_config layer;
   qdg_compute_config compute;
@@ -93,6 +101,7 @@ struct qdg_plan {
   bool has_tuning;
   Format fmt;
   PackedGeom geom;
+  AutoEntry autot[kAutoRanges];  // written by qdg_plan_autotune only
 };
 
 namespace {
@@ -161,6 +170,7 @@ qdg_status validate_layer(const qdg_layer_config* L) {
 }
 
 struct Choice {
+  bool autotuned;  // served by an autotuned entry of the plan
   bool tile;
   bool ws;     // weight-streaming family (dense M <= 16, MoE 16-row blocks)
   bool qtile;  // LDS-tiled family of the 8-bit-activation formats
@@ -173,17 +183,16 @@ struct Choice {
 
 // Device heuristics per M range for gfx950 (256 CUs): small M streams the
 // weights with split-K to give every CU work; large M uses LDS-tiled MFMA.
-Choice choose(const qdg_plan& P, int64_t M) {
+Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool has_tuning) {
   Choice ch{};
   const PackedGeom& g = P.geom;
-  const qdg_tuning_config& T = P.tuning;
   const bool moe = P.compute.kind == QDG_KIND_MOE;
-  int bm = P.has_tuning && T.block_m ? T.block_m : 0;
+  int bm = has_tuning && T.block_m ? T.block_m : 0;
   if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
   // measured on MI355X: one (partly filled) 128-row block of the tiled
   // families, with K split into one pass of workgroups, beats the streaming
   // family from M = 33 (W4A16) and from M = 64 (int8 / fp8 activations)
-  if (!P.has_tuning && !P.compute.batch_invariant && !moe && bm < 128 && M > (P.fmt == FMT_W4A16 ? 32 : 63))
+  if (!has_tuning && !P.compute.batch_invariant && !moe && bm < 128 && M > (P.fmt == FMT_W4A16 ? 32 : 63))
     bm = 128;
   if (P.compute.batch_invariant && bm > 64) bm = 64;
   // the tiled family addresses A with 32-bit byte offsets
@@ -193,13 +202,13 @@ Choice choose(const qdg_plan& P, int64_t M) {
     ch.tile = true;
     ch.tc.bm = bm;
     ch.tc.bn = bm == 256 ? 128 : 256;
-    ch.tc.waves = P.has_tuning && T.waves ? T.waves : 8;
+    ch.tc.waves = has_tuning && T.waves ? T.waves : 8;
     ch.grid_m = (int)((M + bm - 1) / bm);
     const int64_t n_blocks = (g.ntiles + ch.tc.bn / 16 - 1) / (ch.tc.bn / 16);
     const int64_t tiles = n_blocks * ch.grid_m;
     // split K when the tiles alone leave CUs idle (fixed order: deterministic,
     // and independent of M only through the tile count)
-    int split = P.has_tuning && T.split_k ? T.split_k : 0;
+    int split = has_tuning && T.split_k ? T.split_k : 0;
     if (!split) {
       // as many K splits as keep the workgroups within one pass over the CUs
       split = tiles >= 256 ? 1 : (int)(256 / tiles);
@@ -216,13 +225,13 @@ Choice choose(const qdg_plan& P, int64_t M) {
   // streaming-family shape or asks for batch invariance (whose results must
   // not depend on which family a given M selects)
   const bool ws_tuning_ok =
-      !P.has_tuning || ((!T.block_m || T.block_m == 16) && (!T.block_n || T.block_n == 64) && (!T.waves || T.waves == 8));
+      !has_tuning || ((!T.block_m || T.block_m == 16) && (!T.block_n || T.block_n == 64) && (!T.waves || T.waves == 8));
   if (bm == 16 && P.fmt == FMT_W4A16 && !P.compute.batch_invariant && ws_tuning_ok &&
       (!moe || P.layer.wtype == QDG_W_INT4)) {
     ch.ws = true;
     ch.grid_m = 1;
     const int64_t nblocks = (g.ntiles + 3) / 4;
-    int split = P.has_tuning && T.split_k ? T.split_k : (int)(kWsTargetWorkgroups / nblocks);
+    int split = has_tuning && T.split_k ? T.split_k : (int)(kWsTargetWorkgroups / nblocks);
     if (moe || split < 1) split = 1;
     if (split > g.groups) split = (int)g.groups;
     ch.sc = StreamCfg{1, 4, 8, split};  // 16 x 64 per workgroup of 8 waves
@@ -237,7 +246,7 @@ Choice choose(const qdg_plan& P, int64_t M) {
     const int nt = (g.ntiles + 3) / 4 >= 128 ? 4 : 1;
     const int64_t nblocks = (g.ntiles + nt - 1) / nt;
     const int min_split = (int)((g.groups + wstream8_max_groups() - 1) / wstream8_max_groups());
-    int split = P.has_tuning && T.split_k ? T.split_k : (nblocks >= 128 ? 1 : (int)(kWsTargetWorkgroups / nblocks));
+    int split = has_tuning && T.split_k ? T.split_k : (nblocks >= 128 ? 1 : (int)(kWsTargetWorkgroups / nblocks));
     if (split < min_split) split = min_split;
     if (split < 1) split = 1;
     if (split > g.groups) split = (int)g.groups;
@@ -256,7 +265,7 @@ Choice choose(const qdg_plan& P, int64_t M) {
   const int64_t q_tiles = ((M + 127) / 128) * ((g.ntiles + 15) / 16);
   // (measured on MI355X: from M = 64 the tiled family with K split into one
   // pass of 256 workgroups beats the streaming family at these layer sizes)
-  const bool q_enough = (P.has_tuning && T.block_m >= 128) || M >= 64;
+  const bool q_enough = (has_tuning && T.block_m >= 128) || M >= 64;
   if (bm >= 128 && P.fmt != FMT_W4A16 && !moe && a8_fits && q_enough) {
     ch.tile = true;
     ch.qtile = true;
@@ -264,7 +273,7 @@ Choice choose(const qdg_plan& P, int64_t M) {
     ch.grid_m = (int)((M + 127) / 128);
     const int64_t n_blocks = (g.ntiles + 15) / 16;
     const int64_t tiles = n_blocks * ch.grid_m;
-    int split = P.has_tuning && T.split_k ? T.split_k : 0;
+    int split = has_tuning && T.split_k ? T.split_k : 0;
     if (!split) {
       // as many K splits as keep the workgroups within one pass over the CUs
       split = tiles >= 256 ? 1 : (int)(256 / tiles);
@@ -281,13 +290,13 @@ Choice choose(const qdg_plan& P, int64_t M) {
   if (bm > 64) bm = 64;  // other formats: the streaming family serves every M
   ch.tile = false;
   ch.sc.mt = bm / 16;
-  ch.sc.kw = P.has_tuning && T.waves ? T.waves : 4;
-  int nt = P.has_tuning && T.block_n ? T.block_n / 16 : 0;
+  ch.sc.kw = has_tuning && T.waves ? T.waves : 4;
+  int nt = has_tuning && T.block_n ? T.block_n / 16 : 0;
   if (!nt) nt = (ch.sc.mt == 1 && g.ntiles < 128 && !P.compute.batch_invariant) ? 1 : 2;
   ch.sc.nt = nt;
   ch.grid_m = (int)((M + bm - 1) / bm);
   const int64_t nblocks = (g.ntiles + nt - 1) / nt;
-  int split = P.has_tuning && T.split_k ? T.split_k : 0;
+  int split = has_tuning && T.split_k ? T.split_k : 0;
   if (!split) {
     const int64_t wgs = nblocks * (P.compute.batch_invariant ? 1 : ch.grid_m);
     split = (int)(kTargetWorkgroups / (wgs > 0 ? wgs : 1));
@@ -300,6 +309,59 @@ Choice choose(const qdg_plan& P, int64_t M) {
   ch.sc.split = split;
   ch.partial_bytes = split > 1 ? (size_t)nblocks * ch.grid_m * split * ch.sc.mt * nt * 4 * 64 * 4 : 0;
   return ch;
+}
+
+int auto_range(int64_t M) {
+  int b = 0;
+  while (b < kAutoRanges - 1 && ((int64_t)1 << b) < M) ++b;
+  return b;
+}
+
+// The instance serving M rows: a user tuning, else an autotuned entry for
+// M's range, else the device heuristics.
+Choice choose(const qdg_plan& P, int64_t M) {
+  if (!P.has_tuning) {
+    const AutoEntry& e = P.autot[auto_range(M)];
+    if (e.valid) {
+      Choice c = choose_t(P, M, e.tuning, true);
+      c.autotuned = true;
+      return c;
+    }
+  }
+  return choose_t(P, M, P.tuning, P.has_tuning);
+}
+
+bool instance_exists(Format f, const Choice& c) {
+  return c.qtile ? true : c.tile ? tile_cfg_supported(f, c.tc) : c.ws || stream_cfg_supported(f, c.sc);
+}
+
+// Checks a tuning against the implemented kernel instances (shapes only;
+// whether an instance exists for the resulting choice is checked apart).
+qdg_status check_tuning(const qdg_layer_config& layer, const qdg_compute_config& compute, Format f,
+                        const qdg_tuning_config& tuning) {
+  const bool dense_tiled = compute.kind == QDG_KIND_DENSE && !compute.batch_invariant;
+  const bool tile_ok = dense_tiled && (tuning.block_m == 128 || (f == FMT_W4A16 && tuning.block_m == 256));
+  if (tuning.block_m && tuning.block_m != 16 && tuning.block_m != 32 && tuning.block_m != 64 && !tile_ok)
+    return fail(QDG_ERR_UNSUPPORTED,
+                "block_m %d: implemented 16, 32, 64 (dense: 128; dense W4A16: 256)", tuning.block_m);
+  if (tuning.block_m >= 128) {
+    if (tuning.block_n && tuning.block_n != (tuning.block_m == 256 ? 128 : 256))
+      return fail(QDG_ERR_UNSUPPORTED, "the tiled families pair block_m 256 with block_n 128, 128 with 256");
+    if (f != FMT_W4A16 && tuning.waves && tuning.waves != 8)
+      return fail(QDG_ERR_UNSUPPORTED, "the 8-bit-activation tiled family runs 8 waves");
+    if (f != FMT_W4A16 && layer.otype == QDG_O_I32 && tuning.split_k > 1)
+      return fail(QDG_ERR_UNSUPPORTED, "raw int32 output is not split");
+  } else if (tuning.block_n && (tuning.block_n % 16 || tuning.block_n > 64)) {
+    return fail(QDG_ERR_UNSUPPORTED, "block_n %d: implemented 16, 32, 64", tuning.block_n);
+  }
+  if (tuning.block_k && tuning.block_k != 128) return fail(QDG_ERR_UNSUPPORTED, "block_k must be 128");
+  if (tuning.waves && tuning.waves != 4 && tuning.waves != 8)
+    return fail(QDG_ERR_UNSUPPORTED, "waves must be 4 (streaming, tiled) or 8 (weight streaming, tiled)");
+  if (tuning.mfma && tuning.mfma != 16) return fail(QDG_ERR_UNSUPPORTED, "mfma must be 16 (16x16 tiles)");
+  if (tuning.split_k < 0) return fail(QDG_ERR_INVALID_ARG, "split_k < 0");
+  if (compute.kind == QDG_KIND_MOE && tuning.split_k > 1)
+    return fail(QDG_ERR_UNSUPPORTED, "grouped MoE does not split K");
+  return QDG_OK;
 }
 
 }  // namespace
@@ -388,32 +450,12 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
     if (layer->otype == QDG_O_I32) return fail(QDG_ERR_UNSUPPORTED, "SiLU*mul has no int32 output");
   }
   if (tuning) {
-    const bool dense_tiled = compute->kind == QDG_KIND_DENSE && !compute->batch_invariant;
-    const bool tile_ok = dense_tiled && (tuning->block_m == 128 || (f == FMT_W4A16 && tuning->block_m == 256));
-    if (tuning->block_m && tuning->block_m != 16 && tuning->block_m != 32 && tuning->block_m != 64 && !tile_ok)
-      return fail(QDG_ERR_UNSUPPORTED,
-                  "block_m %d: implemented 16, 32, 64 (dense: 128; dense W4A16: 256)", tuning->block_m);
-    if (tuning->block_m >= 128) {
-      if (tuning->block_n && tuning->block_n != (tuning->block_m == 256 ? 128 : 256))
-        return fail(QDG_ERR_UNSUPPORTED, "the tiled families pair block_m 256 with block_n 128, 128 with 256");
-      if (f != FMT_W4A16 && tuning->waves && tuning->waves != 8)
-        return fail(QDG_ERR_UNSUPPORTED, "the 8-bit-activation tiled family runs 8 waves");
-      if (f != FMT_W4A16 && layer->otype == QDG_O_I32 && tuning->split_k > 1)
-        return fail(QDG_ERR_UNSUPPORTED, "raw int32 output is not split");
-
-    } else if (tuning->block_n && (tuning->block_n % 16 || tuning->block_n > 64)) {
-      return fail(QDG_ERR_UNSUPPORTED, "block_n %d: implemented 16, 32, 64", tuning->block_n);
-    }
-    if (tuning->block_k && tuning->block_k != 128) return fail(QDG_ERR_UNSUPPORTED, "block_k must be 128");
-    if (tuning->waves && tuning->waves != 4 && tuning->waves != 8)
-      return fail(QDG_ERR_UNSUPPORTED, "waves must be 4 (streaming, tiled) or 8 (weight streaming, tiled)");
-    if (tuning->mfma && tuning->mfma != 16) return fail(QDG_ERR_UNSUPPORTED, "mfma must be 16 (16x16 tiles)");
-    if (tuning->split_k < 0) return fail(QDG_ERR_INVALID_ARG, "split_k < 0");
-    if (compute->kind == QDG_KIND_MOE && tuning->split_k > 1)
-      return fail(QDG_ERR_UNSUPPORTED, "grouped MoE does not split K");
+    st = check_tuning(*layer, *compute, f, *tuning);
+    if (st != QDG_OK) return st;
   }
   qdg_plan* p = new (std::nothrow) qdg_plan;
   if (!p) return fail(QDG_ERR_INVALID_ARG, "out of host memory");
+  std::memset(p->autot, 0, sizeof p->autot);
   p->layer = *layer;
   p->compute = *compute;
   p->has_tuning = tuning != nullptr;
@@ -423,7 +465,7 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
   p->geom = packed_geom(*layer, f);
   if (tuning) {
     const Choice c = choose(*p, 1);
-    if (c.qtile ? false : c.tile ? !tile_cfg_supported(f, c.tc) : !c.ws && !stream_cfg_supported(f, c.sc)) {
+    if (!instance_exists(f, c)) {
       delete p;
       return fail(QDG_ERR_UNSUPPORTED, "no kernel instance for block_m/block_n/waves of this tuning");
     }
@@ -523,7 +565,7 @@ static int describe(const qdg_plan& plan, const Choice& c, int64_t M, const char
                   c.tile || c.qtile ? c.tc.bm : c.sc.mt * 16, c.tile || c.qtile ? c.tc.bn : c.sc.nt * 16,
                   c.sc.split, c.tile || c.qtile ? c.tc.waves : c.sc.kw, mfma_name(plan.fmt, c), c.grid_m,
                   plan.compute.batch_invariant, plan.compute.epilogue == QDG_EPI_SILU_MUL ? "silu_mul" : "none",
-                  plan.has_tuning ? "user" : "heuristic", QDG_LAYOUT_VERSION);
+                  c.autotuned ? "autotuned" : plan.has_tuning ? "user" : "heuristic", QDG_LAYOUT_VERSION);
 }
 
 int qdg_plan_describe(const qdg_plan* plan, int64_t M, char* buf, size_t len) {
@@ -640,6 +682,123 @@ qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, 
   if (!aligned(Y, ybytes)) return fail(QDG_ERR_MISALIGNED, "Y must be aligned to its element size");
   return run(plan, A, a_scales, packed, Y, M, workspace, ws_bytes, (hipStream_t)stream, false, nullptr, nullptr,
              nullptr, 0, 0, 0);
+}
+
+// Candidate tunings for M rows: every kernel family that can serve M, with
+// its tile shapes and (weight streaming) K splits; split 0 keeps the family's
+// split heuristic. Candidates without an instance are dropped by the caller.
+static void autotune_candidates(const qdg_plan& P, int64_t M, qdg_tuning_config* out, int* n, int cap) {
+  *n = 0;
+  auto add = [&](int bm, int bn, int split, int waves) {
+    if (*n >= cap) return;
+    qdg_tuning_config t;
+    std::memset(&t, 0, sizeof t);
+    t.block_m = bm;
+    t.block_n = bn;
+    t.split_k = split;
+    t.waves = waves;
+    out[(*n)++] = t;
+  };
+  if (M <= 16) {  // weight streaming
+    if (P.fmt == FMT_W4A16) {
+      for (int s : {0, 1, 2, 4, 8}) add(16, 64, s, 8);
+    } else {
+      add(16, 64, 0, 8);
+    }
+  }
+  if (M <= 256) {  // streaming: the smallest row block that holds M, and larger ones
+    for (int bm = M <= 16 ? 16 : M <= 32 ? 32 : 64; bm <= 64; bm *= 2)
+      for (int bn : {16, 32, 64}) add(bm, bn, 0, 4);
+  }
+  if (M > 16) {  // LDS-tiled
+    add(128, 256, 0, 8);
+    if (P.fmt == FMT_W4A16) {
+      add(128, 256, 0, 4);
+      if (M > 128) add(256, 128, 0, 8);
+    }
+  }
+}
+
+qdg_status qdg_plan_autotune(qdg_plan* plan, const void* A, const float* a_scales, const void* packed, void* Y,
+                             int64_t M, void* workspace, size_t ws_bytes, int32_t reps, void* stream,
+                             qdg_tuning_config* chosen, float* best_us) {
+  if (!plan) return fail(QDG_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->compute.kind != QDG_KIND_DENSE) return fail(QDG_ERR_UNSUPPORTED, "autotuning is for dense plans");
+  if (plan->has_tuning) return fail(QDG_ERR_UNSUPPORTED, "the plan carries a user tuning");
+  if (plan->compute.batch_invariant)
+    return fail(QDG_ERR_UNSUPPORTED, "a batch-invariant plan keeps one instance for every M");
+  if (M < 1 || M > 0x7FFFFFFF / 2) return fail(QDG_ERR_INVALID_ARG, "M must be in [1, 2^30)");
+  if (reps < 1 || reps > 1000) return fail(QDG_ERR_INVALID_ARG, "reps must be in [1, 1000]");
+  if (!A || !packed || !Y || !workspace) return fail(QDG_ERR_INVALID_ARG, "NULL A, packed, Y or workspace");
+  constexpr int kCap = 32;
+  qdg_tuning_config cand[kCap];
+  int ncand = 0;
+  autotune_candidates(*plan, M, cand, &ncand, kCap);
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return fail(QDG_ERR_HIP, "hipEventCreate failed");
+  }
+  int best = -1;
+  float best_t = 0.f;
+  qdg_status err = QDG_OK;
+  for (int i = 0; i < ncand && err == QDG_OK; ++i) {
+    if (check_tuning(plan->layer, plan->compute, plan->fmt, cand[i]) != QDG_OK) continue;
+    plan->tuning = cand[i];
+    plan->has_tuning = true;
+    const Choice c = choose(*plan, M);
+    size_t need = 0;
+    bool usable = instance_exists(plan->fmt, c) && qdg_plan_workspace(plan, M, &need) == QDG_OK && need <= ws_bytes;
+    if (usable) {
+      // one untimed launch, then reps launches between two events
+      qdg_status r = qdg_gemm(plan, A, a_scales, packed, Y, M, workspace, ws_bytes, stream);
+      if (r == QDG_ERR_UNSUPPORTED || r == QDG_ERR_WORKSPACE) {
+        usable = false;
+      } else if (r != QDG_OK) {
+        err = r;
+      } else {
+        hipError_t h = hipEventRecord(e0, st);
+        for (int k = 0; k < reps && r == QDG_OK && h == hipSuccess; ++k)
+          r = qdg_gemm(plan, A, a_scales, packed, Y, M, workspace, ws_bytes, stream);
+        if (h == hipSuccess) h = hipEventRecord(e1, st);
+        if (h == hipSuccess) h = hipEventSynchronize(e1);
+        float ms = 0.f;
+        if (h == hipSuccess) h = hipEventElapsedTime(&ms, e0, e1);
+        if (r != QDG_OK) {
+          err = r;
+        } else if (h != hipSuccess) {
+          err = hip_status(h, "autotune timing");
+        } else {
+          const float us = ms * 1000.f / (float)reps;
+          if (best < 0 || us < best_t) {
+            best = i;
+            best_t = us;
+          }
+        }
+      }
+    }
+    plan->has_tuning = false;
+    std::memset(&plan->tuning, 0, sizeof plan->tuning);
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (err != QDG_OK) return err;
+  if (best < 0) return fail(QDG_ERR_WORKSPACE, "no kernel instance for M = %lld fits the workspace", (long long)M);
+  AutoEntry& e = plan->autot[auto_range(M)];
+  e.tuning = cand[best];
+  e.us = best_t;
+  e.valid = true;
+  if (chosen) *chosen = cand[best];
+  if (best_us) *best_us = best_t;
+  // leave Y holding the result of the chosen instance
+  return qdg_gemm(plan, A, a_scales, packed, Y, M, workspace, ws_bytes, stream);
+}
+
+qdg_status qdg_plan_autotune_reset(qdg_plan* plan) {
+  if (!plan) return fail(QDG_ERR_INVALID_ARG, "plan is NULL");
+  std::memset(plan->autot, 0, sizeof plan->autot);
+  return ok();
 }
 
 qdg_status qdg_moe_align_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m, int64_t* capacity) {

@@ -161,3 +161,25 @@ def test_preprocess_and_moe_validation():
     assert q.qdg_moe_align_capacity(64, 8, 256, 16) == 512 + 256 * 15
     assert _status(q.qdg_moe_align_capacity, 64, 8, 256, 24) == q.QDG_ERR_UNSUPPORTED
     assert _status(q.qdg_moe_align_capacity, 64, 8, 2048, 16) == q.QDG_ERR_UNSUPPORTED
+
+
+def test_autotune_validation_before_device_work():
+    l = q.layer_w4a16(64, 128)
+    p = q.qdg_plan_create(l, q.dense())
+    at = q.qdg_plan_autotune
+    # MoE, user-tuned and batch-invariant plans are not autotuned
+    pm = q.qdg_plan_create(q.layer_w4a16(64, 128, num_experts=2), q.moe(1))
+    assert _status(at, pm, 0x1000, None, 256, 256, 4, 256, 1 << 20, 5, 0) == q.QDG_ERR_UNSUPPORTED
+    pu = q.qdg_plan_create(l, q.dense(), q.TuningConfig(block_m=16))
+    assert _status(at, pu, 0x1000, None, 256, 256, 4, 256, 1 << 20, 5, 0) == q.QDG_ERR_UNSUPPORTED
+    pb = q.qdg_plan_create(l, q.dense(batch_invariant=1))
+    assert _status(at, pb, 0x1000, None, 256, 256, 4, 256, 1 << 20, 5, 0) == q.QDG_ERR_UNSUPPORTED
+    # bad M, reps and NULL operands
+    assert _status(at, p, 0x1000, None, 256, 256, 0, 256, 1 << 20, 5, 0) == q.QDG_ERR_INVALID_ARG
+    assert _status(at, p, 0x1000, None, 256, 256, 4, 256, 1 << 20, 0, 0) == q.QDG_ERR_INVALID_ARG
+    assert _status(at, p, 0x1000, None, 256, 256, 4, 256, 1 << 20, 1001, 0) == q.QDG_ERR_INVALID_ARG
+    assert _status(at, p, 0, None, 256, 256, 4, 256, 1 << 20, 5, 0) == q.QDG_ERR_INVALID_ARG
+    assert _status(at, p, 0x1000, None, 256, 256, 4, 0, 1 << 20, 5, 0) == q.QDG_ERR_INVALID_ARG
+    # nothing was recorded: the heuristics still serve every M
+    q.qdg_plan_autotune_reset(p)
+    assert all("tuning=heuristic" in q.qdg_plan_describe(p, m) for m in (1, 16, 100, 5000))
