@@ -10,10 +10,12 @@ HBM. Small-M cases rotate over enough packed weight copies to defeat the
 Prints one JSON line. `value` is the step's algorithmic TFLOP/s; `roofline`
 describes the kernel that dominates the step's time, `roofline_m16` the
 HBM-bound M=16 case (also as a fraction of `hbm_copy_gbs`, the box's measured
-device-to-device copy rate), `cases` every launch; `cpu_baseline` times the
-fp64 CPU oracle over the same workload once.
+device-to-device copy rate), `cases` every launch, `autotuned` each case
+again with a plan tuned per M range (qdg_plan_autotune) next to the
+heuristic plan; `cpu_baseline` times the fp64 CPU oracle over the same
+workload once.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-rows] [--no-autotune]
 """
 
 import argparse
@@ -200,6 +202,34 @@ def gpu_leg(args):
         by = alg_bytes(c["m"], c["n"], c["k"])
         d.update(us_stream=round(us, 3), gbs_stream=round(by / us / 1e3, 1),
                  hbm_frac_stream=round(by / us / 1e3 / PEAK_HBM_GBS, 4))
+    # per-M-range autotuning: a fresh plan per shape, tuned at each M of the
+    # sweep on one weight copy, then timed like the heuristic plan (rotating
+    # copies, back-to-back launches); not part of `value`
+    autotuned = []
+    if args.autotune:
+        for (k, n) in SHAPES:
+            layer, plan_h, bufs = layers[(k, n)]
+            plan_a = q.qdg_plan_create(layer, q.dense())
+            for c in cases:
+                if (c["k"], c["n"]) != (k, n):
+                    continue
+                m = c["m"]
+                ws_a = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+                _, best = q.qdg_plan_autotune(plan_a, c["a"].data_ptr(), None, bufs[0].data_ptr(), c["y"].data_ptr(),
+                                              m, ws_a.data_ptr(), ws_a.numel(), 3 if m >= 1024 else 10, sh)
+                reps = 5 if m >= 1024 else 60
+
+                def run(i, plan=plan_h, c=c, ws=c["ws"], wsb=c["wsb"]):
+                    q.qdg_gemm(plan, c["a"].data_ptr(), None, c["bufs"][i % len(c["bufs"])].data_ptr(),
+                               c["y"].data_ptr(), c["m"], ws.data_ptr(), wsb, sh)
+                us_h = _time_launches(run, reps, stream)
+                us_a = _time_launches(lambda i: run(i, plan=plan_a, ws=ws_a, wsb=ws_a.numel()), reps, stream)
+                autotuned.append(dict(M=m, K=k, N=n, heuristic_us=round(us_h, 3), autotuned_us=round(us_a, 3),
+                                      speedup=round(us_h / us_a, 3), autotune_best_us_one_copy=round(best, 3),
+                                      instance=q.qdg_plan_describe(plan_a, m).split(": ", 1)[1]))
+                print(f"autotune M={m} K={k} N={n}: heuristic {us_h:.2f} us, autotuned {us_a:.2f} us",
+                      file=sys.stderr, flush=True)
+                del ws_a
     m16 = [d for d in out_cases if d["M"] == 16]
     roof16 = [dict(bound="hbm", achieved=d["gbs_stream"], peak=PEAK_HBM_GBS, unit="GB/s", frac=d["hbm_frac_stream"],
                    frac_of_copy=round(d["gbs_stream"] / copy_gbs, 4), kernel=f"w4a16 M=16 K={d['K']} N={d['N']}",
@@ -208,7 +238,7 @@ def gpu_leg(args):
               for d in m16]
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     return dict(value=value, ms_per_step=ms_per_step, roofline=roof, roofline_m16=roof16, cases=out_cases,
-                hbm_copy_gbs=round(copy_gbs, 1))
+                hbm_copy_gbs=round(copy_gbs, 1), autotuned=autotuned)
 
 
 PEAK_INT8_TOPS = 5000.0
@@ -508,6 +538,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-rows", action="store_true", help="skip the W8A8 / W4A8 / MXFP4 / MoE rows")
+    ap.add_argument("--no-autotune", dest="autotune", action="store_false",
+                    help="skip the autotuned-plan comparison of the dense sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 256 MiB device to device once (the known-size reference that scales "
                          "HBM byte counters in a profiler run)")
@@ -528,6 +560,8 @@ def main():
         "roofline": g["roofline"], "roofline_m16": g["roofline_m16"], "hbm_copy_gbs": g["hbm_copy_gbs"],
         "cases": g["cases"],
     }
+    if g["autotuned"]:
+        line["autotuned"] = g["autotuned"]
     if not args.no_rows:
         line["rows"] = rows_leg()
     if not args.no_cpu:

@@ -228,9 +228,10 @@ qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, 
    kinachrichten, "Kompilierzeiten und gerätespezifisches Tuning"; jetabc,
    "Humming 的做法", item 2). Times every kernel instance that can serve M
    rows (weight streaming with several K splits, streaming with every row
-   block and tile count, LDS-tiled shapes) on the caller's buffers, with one
-   untimed launch and then reps launches between two events on stream, and
-   records the fastest for M's range: M in (2^(b-1), 2^b], b = 0..31. Later
+   block and tile count, LDS-tiled shapes) on the caller's buffers, in three
+   interleaved rounds of one untimed launch and reps launches between two
+   events on stream, and records the instance with the lowest round time for
+   M's range: M in (2^(b-1), 2^b], b = 0..31. Later
    qdg_gemm, qdg_plan_workspace and qdg_plan_describe calls with an M in that
    range use it ("tuning=autotuned"). Arguments as for qdg_gemm; instances
    whose workspace exceeds ws_bytes are skipped (query qdg_plan_workspace
