@@ -28,6 +28,8 @@ representation (jetabc, section on what quantization is; kinachrichten,
 * Activations, fp8 E4M3 per (token, 128-wide K group): ``inv = f32(448 / amax)``,
   ``qa = e4m3_rne(clamp(f32(x * inv), -448, 448))``, ``sa = f32(amax / 448)``.
 * A row or group whose ``amax`` is zero gets scale 1.0 and all-zero codes.
+* Activations, MXFP4 (W4A4): the MXFP4 rule above applied to each row's
+  blocks of 32 consecutive K (the bf16 values are exact in binary32).
 """
 
 import numpy as np
@@ -123,6 +125,16 @@ def quantize_mxfp4(w, block=32):
     codes = codecs.encode_e2m1_rne_sat(scaled)
     codes = np.where(pos[:, :, None], codes, 0).astype(np.uint8)
     return codes.reshape(w.shape), e
+
+
+def quantize_act_mxfp4(a_bf16_bits):
+    """bf16 bits [M, K] -> (E2M1 codes u8 [M,K], E8M0 scale codes u8 [M, K/32]).
+
+    MX FP4 activations for the W4A4 path: the same shared-exponent rule and
+    element rounding as the weights, one block per 32 consecutive K of a row.
+    """
+    x = codecs.bf16_bits_to_f64(a_bf16_bits).astype(F32)
+    return quantize_mxfp4(x)
 
 
 def quantize_act_int8(a_bf16_bits):

@@ -116,6 +116,14 @@ def gemm_mxfp4(a_codes, sa, w_codes, w_e8m0):
     return a @ w.T
 
 
+def gemm_w4a4(a_codes, a_e8m0, w_codes, w_e8m0):
+    """MXFP4 activations times MXFP4 weights (W4A4): both sides decoded with
+    their E8M0 block-32 scales, then a float64 product."""
+    a = dequant_mxfp4(a_codes, a_e8m0)
+    w = dequant_mxfp4(w_codes, w_e8m0)
+    return a @ w.T
+
+
 def dequant_act_int8(qa, sa):
     return np.asarray(qa, np.float64) * np.asarray(sa, np.float64)[:, None]
 

@@ -147,3 +147,27 @@ def test_act_fp8_codes_match_torch_cast():
     # largest element of each group maps to +-448 exactly
     dec = codecs.decode_e4m3(codes).reshape(16, 8, 128)
     assert np.all(np.abs(dec).max(axis=2)[nz] == 448.0)
+
+
+def test_act_mxfp4_is_the_block_rule_on_each_row():
+    # rows of exactly representable values: every block reaches +-6 * 2**X,
+    # so the shared exponent is X and the codes round-trip exactly
+    r = np.random.default_rng(41)
+    m, k = 3, 96
+    codes = r.integers(0, 16, size=(m, k)).astype(np.uint8)
+    codes[:, 5::32] = 0xF  # -6 in every block
+    e = r.integers(118, 134, size=(m, k // 32)).astype(np.uint8)
+    x = ref.dequant_mxfp4(codes, e)
+    bits = codecs.f32_to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(codecs.bf16_bits_to_f64(bits), x)  # exact in bf16
+    c2, e2 = quant.quantize_act_mxfp4(bits)
+    assert np.array_equal(e2, e)
+    assert np.array_equal(codecs.decode_e2m1(c2), codecs.decode_e2m1(codes))
+    # hand block: amax 1.0 -> X = -2 (scale 1/4); 0.3/0.25 = 1.2 -> 1.0 (code 2);
+    # 0.0625/0.25 = 0.25 -> tie between 0 and 0.5 -> even -> 0; -0.1875/0.25 =
+    # -0.75 -> tie between 0.5 and 1.0 -> even -> -1.0 (code 0xA); 1.0 -> 4 (code 6)
+    row = np.zeros((1, 32), np.float32)
+    row[0, :4] = [0.3, 0.0625, -0.1875, 1.0]
+    c3, e3 = quant.quantize_act_mxfp4(codecs.f32_to_bf16_bits(row))
+    assert e3[0, 0] == 125
+    assert list(c3[0, :4]) == [2, 0, 0xA, 6]

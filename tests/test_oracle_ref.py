@@ -145,6 +145,41 @@ def test_mxfp4_gemm_brute_force():
             assert abs(float(acc) - y[i, j]) <= 1e-12 * abs(float(acc)) + 1e-300
 
 
+def test_w4a4_gemm_brute_force():
+    # every product e2m1 * e2m1 * 2**(Ea + Eb - 254) is a short dyadic number;
+    # the exact rational sum must equal the float64 reference
+    r = np.random.default_rng(23)
+    m, n, k = 3, 4, 96
+    a_codes = r.integers(0, 16, (m, k)).astype(np.uint8)
+    w_codes = r.integers(0, 16, (n, k)).astype(np.uint8)
+    ea = r.integers(124, 131, (m, k // 32)).astype(np.uint8)
+    ew = r.integers(124, 131, (n, k // 32)).astype(np.uint8)
+    y = ref.gemm_w4a4(a_codes, ea, w_codes, ew)
+    av = codecs.decode_e2m1(a_codes)
+    wv = codecs.decode_e2m1(w_codes)
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                acc += (Fraction(float(av[i, kk])) * Fraction(float(wv[j, kk]))
+                        * Fraction(2) ** (int(ea[i, kk // 32]) + int(ew[j, kk // 32]) - 254))
+            assert float(acc) == y[i, j]
+
+
+def test_w4a4_special_cases():
+    # unit scales (code 127): the product of the decoded E2M1 matrices; a
+    # power-of-two activation scale scales the result exactly
+    r = np.random.default_rng(24)
+    a_codes = r.integers(0, 16, (2, 64)).astype(np.uint8)
+    w_codes = r.integers(0, 16, (5, 64)).astype(np.uint8)
+    one_a = np.full((2, 2), 127, np.uint8)
+    one_w = np.full((5, 2), 127, np.uint8)
+    y = ref.gemm_w4a4(a_codes, one_a, w_codes, one_w)
+    assert np.array_equal(y, codecs.decode_e2m1(a_codes) @ codecs.decode_e2m1(w_codes).T)
+    y3 = ref.gemm_w4a4(a_codes, one_a + 3, w_codes, one_w)
+    assert np.array_equal(y3, 8.0 * y)
+
+
 def test_route_topk_order_and_ties():
     logits = np.array([[0.0, 2.0, 2.0, 1.0], [5.0, -1.0, 5.0, 5.0]])
     ids, p = ref.route_topk(logits, 2)
