@@ -64,8 +64,11 @@ enum { QDG_W_INT4 = 0,  /* two's-complement 4-bit, symmetric (no zeros) */
        QDG_W_MXFP4 = 3  /* OCP MX FP4 E2M1 with E8M0 scale per 32 along K */ };
 /* Scale storage types. */
 enum { QDG_S_F16 = 0, QDG_S_F32 = 1, QDG_S_E8M0 = 2 };
-/* Activation types. */
-enum { QDG_A_BF16 = 0, QDG_A_INT8 = 1, QDG_A_FP8E4M3 = 2 };
+/* Activation types. MXFP4 activations (W4A4): E2M1 codes u8 [M][k/2], two
+   per byte with the even k in the low nibble, and E8M0 scale codes u8
+   [M][k/32]; the qdg_gemm / qdg_moe_gemm a_scales pointer then carries the
+   E8M0 bytes. */
+enum { QDG_A_BF16 = 0, QDG_A_INT8 = 1, QDG_A_FP8E4M3 = 2, QDG_A_MXFP4 = 3 };
 /* Output types. QDG_O_I32 returns the raw integer accumulator
    sum_k qa*qw (integer-weight paths only; every scale ignored). */
 enum { QDG_O_BF16 = 0, QDG_O_F32 = 1, QDG_O_I32 = 2 };
@@ -82,6 +85,12 @@ enum { QDG_KIND_DENSE = 0, QDG_KIND_MOE = 1 };
                 otype BF16, F32 or I32
      W4A8-MXFP4 wtype MXFP4, stype E8M0, group_size 32, atype FP8E4M3,
                 act_group 128, otype BF16 or F32
+     W4A4-MXFP4 wtype MXFP4, stype E8M0, group_size 32, atype MXFP4,
+                act_group 32, otype BF16 or F32 (the pages list W4A4 among
+                the common configurations: kinachrichten, "Warum
+                quantisierte Kernel wichtig sind"; served by the streaming
+                family with fp4 x fp4 scaled MFMAs, both E8M0 scales applied
+                by the hardware)
    Shapes: k a positive multiple of 128; n >= 1 (padded internally to a
    multiple of 16); num_experts >= 1 (1 for a dense layer). arch = 950. */
 typedef struct qdg_layer_config {
@@ -91,7 +100,7 @@ typedef struct qdg_layer_config {
 } qdg_layer_config;
 
 /* Compute config: which computation. kind DENSE or MOE (MoE: W4A16 with
-   INT4 symmetric weights, W8A8, W4A8-INT8, W4A8-MXFP4). batch_invariant = 1 makes row m of Y bitwise independent of M and
+   INT4 symmetric weights, W8A8, W4A8-INT8, W4A8-MXFP4, W4A4-MXFP4). batch_invariant = 1 makes row m of Y bitwise independent of M and
    of the other rows (one fixed reduction order for every M). top_k: MoE
    slots per token. */
 typedef struct qdg_compute_config {
@@ -179,13 +188,18 @@ qdg_status qdg_preprocess(const qdg_layer_config* layer, const qdg_std_weights* 
 qdg_status qdg_quantize_weights(const qdg_layer_config* layer, const float* w,
                                 void* qweight, void* scales, void* zeros, void* stream);
 
-/* Activation quantization for the W8A8 / W4A8 paths (layer->atype INT8 or
-   FP8E4M3). a_bf16 [M][k] row-major ->
+/* Activation quantization for the W8A8 / W4A8 / W4A4 paths (layer->atype
+   INT8, FP8E4M3 or MXFP4). a_bf16 [M][k] row-major ->
      INT8:    qa i8 [M][k], a_scales f32 [M];       per token
      FP8E4M3: qa u8 E4M3 [M][k], a_scales f32 [M][k/128]; per 128-group
    with amax the largest |x|, inv = f32(Q/amax) (Q = 127 or 448),
    code = rne(clamp(f32(x*inv), -Q, Q)), scale = f32(amax/Q); amax = 0 gives
-   scale 1 and zero codes. Bit-exact by construction (binary32, RNE). */
+   scale 1 and zero codes;
+     MXFP4:   qa u8 [M][k/2] E2M1 codes (even k in the low nibble), a_scales
+              (as bytes) u8 E8M0 [M][k/32]: per block of 32 the MXFP4 rule of
+              qdg_quantize_weights (an all-zero block stores E8M0 code 0 and
+              zero codes; a negative value that rounds to zero keeps its sign).
+   Bit-exact by construction (binary32, RNE). */
 qdg_status qdg_quantize_act(const qdg_layer_config* layer, const void* a_bf16, int64_t M,
                             void* qa, float* a_scales, void* stream);
 

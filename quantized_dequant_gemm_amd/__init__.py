@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libqdg.so")
 QDG_OK, QDG_ERR_INVALID_ARG, QDG_ERR_UNSUPPORTED, QDG_ERR_MISALIGNED, QDG_ERR_WORKSPACE, QDG_ERR_HIP = range(6)
 QDG_W_INT4, QDG_W_UINT4, QDG_W_INT8, QDG_W_MXFP4 = range(4)
 QDG_S_F16, QDG_S_F32, QDG_S_E8M0 = range(3)
-QDG_A_BF16, QDG_A_INT8, QDG_A_FP8E4M3 = range(3)
+QDG_A_BF16, QDG_A_INT8, QDG_A_FP8E4M3, QDG_A_MXFP4 = range(4)
 QDG_O_BF16, QDG_O_F32, QDG_O_I32 = range(3)
 QDG_KIND_DENSE, QDG_KIND_MOE = range(2)
 QDG_EPI_NONE, QDG_EPI_SILU_MUL = range(2)
@@ -260,6 +260,12 @@ def layer_w4a8(n, k, otype=QDG_O_BF16, num_experts=1):
 def layer_mxfp4(n, k, otype=QDG_O_BF16, num_experts=1):
     return LayerConfig(n=n, k=k, num_experts=num_experts, wtype=QDG_W_MXFP4, stype=QDG_S_E8M0, group_size=32,
                        has_zeros=0, atype=QDG_A_FP8E4M3, act_group=128, otype=otype, arch=950)
+
+
+def layer_w4a4(n, k, otype=QDG_O_BF16, num_experts=1):
+    """MXFP4 weights with MXFP4 activations (E8M0 per 32-block on both sides)."""
+    return LayerConfig(n=n, k=k, num_experts=num_experts, wtype=QDG_W_MXFP4, stype=QDG_S_E8M0, group_size=32,
+                       has_zeros=0, atype=QDG_A_MXFP4, act_group=32, otype=otype, arch=950)
 
 
 def dense(batch_invariant=0):

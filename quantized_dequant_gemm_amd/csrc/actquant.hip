@@ -6,6 +6,8 @@
 //   int8, one fp32 scale per token:   inv = f32(127/amax), q = rne(clamp(x*inv))
 //   fp8 E4M3 (OCP), one fp32 scale per token and 128-wide K group:
 //                                     inv = f32(448/amax), q = e4m3_rne(clamp(x*inv))
+//   MXFP4 (OCP MX), one E8M0 scale per token and 32-wide K block:
+//                                     X = floor(log2(amax)) - 2, q = e2m1_rne_sat(x / 2^X)
 // Scale = f32(amax/Q); amax = 0 gives scale 1 and zero codes. Every step is
 // binary32 with RNE and correctly rounded division, so the codes are
 // reproducible bit for bit by any implementation doing the same steps.
@@ -41,6 +43,59 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
     code = ((uint32_t)(ee + 7) << 3) | m;
   }
   return code | sign;
+}
+
+// OCP E2M1 code of a real, round to nearest with ties to the even code,
+// saturating at 6 (the largest finite value): magnitudes 0, 0.5, 1, 1.5, 2,
+// 3, 4, 6 are codes 0..7, the sign is bit 3 (also for values that round to 0).
+__device__ __forceinline__ uint32_t e2m1_rne_sat(float v) {
+  const uint32_t sign = __builtin_signbit(v) ? 8u : 0u;
+  const float a = fabsf(v);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;        // tie 0.25 -> 0
+  else if (a < 0.75f) c = 1;    // tie 0.75 -> 1.0
+  else if (a <= 1.25f) c = 2;   // tie 1.25 -> 1.0
+  else if (a < 1.75f) c = 3;    // tie 1.75 -> 2.0
+  else if (a <= 2.5f) c = 4;    // tie 2.5 -> 2.0
+  else if (a < 3.5f) c = 5;     // tie 3.5 -> 4.0
+  else if (a <= 5.0f) c = 6;    // tie 5 -> 4.0
+  else c = 7;
+  return c | sign;
+}
+
+// MXFP4 per (token, 32-block): one thread per block (64 bytes in, 16 bytes of
+// codes and one E8M0 byte out; a wave covers 4 KiB of a row contiguously).
+__global__ __launch_bounds__(256) void act_fp4_kernel(const uint16_t* __restrict__ a, uint8_t* __restrict__ q,
+                                                      uint8_t* __restrict__ scales, int64_t blocks) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;  // block index: row * (K/32) + j
+  if (b >= blocks) return;
+  const uint16_t* x = a + b * 32;
+  float f[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4_t v = *(const u32x4_t*)(x + 8 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[8 * i + 2 * j] = bf16_to_f32(v[j] & 0xFFFFu);
+      f[8 * i + 2 * j + 1] = bf16_to_f32(v[j] >> 16);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  u32x4_t out = {0, 0, 0, 0};
+  uint32_t e8 = 0;
+  if (amax > 0.f) {
+    int ex;
+    (void)frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1): floor(log2(amax)) = ex - 1
+    int X = ex - 1 - 2;
+    X = X < -127 ? -127 : X > 127 ? 127 : X;
+    e8 = (uint32_t)(X + 127);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) out[i >> 3] |= e2m1_rne_sat(ldexpf(f[i], -X)) << (4 * (i & 7));
+  }
+  *(u32x4_t*)(q + b * 16) = out;
+  scales[b] = (uint8_t)e8;
 }
 
 // int8 per token: one workgroup per row.
@@ -122,6 +177,10 @@ hipError_t launch_quantize_act(int atype, const void* a, int64_t M, int64_t K, v
   if (atype == QDG_A_INT8) {
     hipLaunchKernelGGL(act_int8_kernel, dim3((unsigned)M), dim3(256), 0, s, (const uint16_t*)a, (int8_t*)qa,
                        scales, K);
+  } else if (atype == QDG_A_MXFP4) {
+    const int64_t blocks = M * (K / 32);
+    hipLaunchKernelGGL(act_fp4_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, s,
+                       (const uint16_t*)a, (uint8_t*)qa, (uint8_t*)scales, blocks);
   } else {
     const int64_t threads = M * (K / 128) * 16;
     hipLaunchKernelGGL(act_fp8_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,

@@ -84,7 +84,7 @@ __global__ void repack_kernel(int fmt, int wtype, const uint8_t* __restrict__ qw
         ((float*)sdst)[unit * 16 + col] = s * 0.0625f;
       }
     }
-  } else if (fmt == FMT_MXFP4) {
+  } else if (fmt == FMT_MXFP4 || fmt == FMT_W4A4) {  // the same weights for fp8 and fp4 activations
     u32x4_t out = {0, 0, 0, 0};
     if (valid) out = *(const u32x4_t*)(qw + (e * N + n) * (K / 2) + (g * 128 + 32 * c) / 2);
     *((u32x4_t*)(wdst + unit * kUnit4Bytes) + lane) = out;

@@ -64,6 +64,13 @@ __device__ __forceinline__ f32x4_t mfma_fp8_fp4_scaled(i32x8_t a, i32x8_t b, f32
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
 }
 
+// The same scaled MFMA with both operands FP4 E2M1 (format 4, W4A4): each
+// lane supplies 32 E2M1 values of its row / column (16 bytes, the low four
+// dwords; lane group c holds K 32c..32c+31) and the E8M0 byte of that block.
+__device__ __forceinline__ f32x4_t mfma_fp4_fp4_scaled(i32x8_t a, i32x8_t b, f32x4_t c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+}
+
 // ------------------------------------------------------------------ unpack
 // W4A16: one dword holds 8 biased nibbles u (u = q for uint4, q + 8 for
 // int4). Element 2i of the MFMA operand is nibble i, element 2i+1 is nibble

@@ -48,6 +48,8 @@ struct Ctx {
   __amdgpu_buffer_rsrc_t arsrc;
   uint32_t aoff[4];
   int as_row[4][4];      // A row of the D rows 4c+i of each M tile (fp8 activation scales)
+  int arow_s[4];         // A row of this lane for each M tile, 0 for padding rows (fp4 activation scales)
+  const uint8_t* a_e8m0; // fp4 activation scales (E8M0 per row and 32-block)
   const uint8_t* wbase;  // weight units of this expert
   const uint8_t* sbase;  // scale records of this expert
   const float* a_scales; // activation scales (fp8 activations)
@@ -245,6 +247,50 @@ struct FmtMxfp4 {
   }
 };
 
+// MXFP4 activations x MXFP4 weights (W4A4): both operands E2M1 with E8M0
+// block-32 scales. The scaled MFMA applies both scales exactly, so a K group
+// is one MFMA per tile accumulating straight into the fp32 accumulator, with
+// no per-group epilogue.
+struct FmtW4A4 {
+  using Acc = f32x4_t;
+  static constexpr bool kIntAcc = false;
+  template <int MT, int NT>
+  struct Frag {
+    u32x4_t a[MT];
+    uint32_t as[MT];
+    u32x4_t b[NT];
+    uint32_t sc[NT];
+  };
+  template <int MT, int NT>
+  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g) {
+    // lane group c: K 32c..32c+31 of the lane's row (16 bytes of codes) and
+    // the E8M0 byte of that block
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f.a[mt] = lda(x.arsrc, x.aoff[mt] + (uint32_t)(g * 64 + 16 * x.c));
+      f.as[mt] = x.a_e8m0[(size_t)x.arow_s[mt] * (x.groups * 4) + g * 4 + x.c];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const size_t u = (size_t)x.tile[t] * x.groups + g;
+      f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
+      f.sc[t] = x.sbase[u * 64 + x.lane];
+    }
+  }
+  template <int MT, int NT>
+  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT], uint32_t, uint32_t) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const i32x8_t b = {(int)f.b[t].x, (int)f.b[t].y, (int)f.b[t].z, (int)f.b[t].w, 0, 0, 0, 0};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const i32x8_t a = {(int)f.a[mt].x, (int)f.a[mt].y, (int)f.a[mt].z, (int)f.a[mt].w, 0, 0, 0, 0};
+        acc[mt][t] = mfma_fp4_fp4_scaled(a, b, acc[mt][t], (int)f.as[mt], (int)f.sc[t]);
+      }
+    }
+  }
+};
+
 // ----------------------------------------------------------------- kernel
 
 template <class F, int MT, int NT, int KW, int U, bool MOE>
@@ -291,19 +337,28 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
   }
   x.wbase = p.packed + (size_t)expert * p.expert_stride;
   x.sbase = x.wbase + p.s_offset;
-  constexpr bool kInt8A = !std::is_same<F, FmtW4A16<false>>::value && !std::is_same<F, FmtW4A16<true>>::value;
-  const size_t a_row_bytes = (size_t)p.K * (kInt8A ? 1 : 2);
+  constexpr bool kBf16A = std::is_same<F, FmtW4A16<false>>::value || std::is_same<F, FmtW4A16<true>>::value;
+  constexpr bool kFp4A = std::is_same<F, FmtW4A4>::value;
+  const size_t a_row_bytes = kBf16A ? (size_t)p.K * 2 : kFp4A ? (size_t)p.K / 2 : (size_t)p.K;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mb * BM + mt * 16 + x.col;
     uint32_t off = kAOob;
+    int srow = 0;
     if constexpr (MOE) {
       const int id = p.sorted_ids[r];
-      if (id < p.num_pairs) off = (uint32_t)((size_t)(p.a_per_pair ? id : id / p.top_k) * a_row_bytes);
+      if (id < p.num_pairs) {
+        srow = p.a_per_pair ? id : id / p.top_k;
+        off = (uint32_t)((size_t)srow * a_row_bytes);
+      }
     } else {
-      if (r < p.M) off = (uint32_t)((size_t)r * a_row_bytes);
+      if (r < p.M) {
+        srow = r;
+        off = (uint32_t)((size_t)r * a_row_bytes);
+      }
     }
     x.aoff[mt] = off;
+    x.arow_s[mt] = srow;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int rr = mb * BM + mt * 16 + 4 * x.c + ii;
@@ -318,6 +373,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
     }
   }
   x.a_scales = p.a_scales;
+  x.a_e8m0 = (const uint8_t*)p.a_scales;
   x.arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), (short)0, (int)p.a_bytes, 0x00020000);
 
   const int g0 = (int)(((int64_t)split * p.groups) / p.split);
@@ -566,6 +622,8 @@ hipError_t launch_stream(Format f, bool asym, bool moe, const StreamCfg& c, cons
                  : dispatch_shape<FmtInt8<true, false>>(c, moe, a, grid_m, s);
     case FMT_MXFP4:
       return dispatch_shape<FmtMxfp4>(c, moe, a, grid_m, s);
+    case FMT_W4A4:
+      return dispatch_shape<FmtW4A4>(c, moe, a, grid_m, s);
   }
   return hipErrorInvalidValue;
 }

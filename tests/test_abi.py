@@ -183,3 +183,19 @@ def test_autotune_validation_before_device_work():
     # nothing was recorded: the heuristics still serve every M
     q.qdg_plan_autotune_reset(p)
     assert all("tuning=heuristic" in q.qdg_plan_describe(p, m) for m in (1, 16, 100, 5000))
+
+
+def test_w4a4_layer_validation():
+    # MXFP4 weights take fp8 activations with 128-groups or MXFP4 activations with 32-blocks
+    q.qdg_validate_layer(q.layer_w4a4(64, 256))  # raises on a bad layer
+    bad = q.layer_w4a4(64, 256)
+    bad.act_group = 128
+    assert _status(q.qdg_plan_create, bad, q.dense()) == q.QDG_ERR_UNSUPPORTED
+    p = q.qdg_plan_create(q.layer_w4a4(64, 256), q.dense())
+    for m in (1, 16, 200, 5000):
+        d = q.qdg_plan_describe(p, m)
+        assert "w4a4-mxfp4" in d and "family=stream" in d and "f4f4" in d
+    pm = q.qdg_plan_create(q.layer_w4a4(64, 256, num_experts=4), q.moe(2))
+    assert "family=stream" in q.qdg_moe_describe(pm, 8, 16)
+    # the scales are required
+    assert _status(q.qdg_gemm, p, 0x1000, None, 256, 256, 4, 256, 1 << 20, 0) == q.QDG_ERR_INVALID_ARG
