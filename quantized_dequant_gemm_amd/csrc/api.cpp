@@ -269,7 +269,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   // (measured on MI355X: from M = 64 the tiled family with K split into one
   // pass of 256 workgroups beats the streaming family at these layer sizes)
   const bool q_enough = (has_tuning && T.block_m >= 128) || M >= 64;
-  if (bm >= 128 && P.fmt != FMT_W4A16 && P.fmt != FMT_W4A4 && !moe && a8_fits && q_enough) {
+  if (bm >= 128 && P.fmt != FMT_W4A16 && !moe && a8_fits && q_enough) {
     ch.tile = true;
     ch.qtile = true;
     ch.tc = TileCfg{128, 256, 8};

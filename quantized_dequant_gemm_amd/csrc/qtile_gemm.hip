@@ -1,7 +1,8 @@
 // LDS-tiled (large-M) GEMM family for the 8-bit-activation formats:
 // W8A8 and W4A8-INT8 (int8 x int8 -> exact int32 on v_mfma_i32_16x16x64_i8)
 // and W4A8-MXFP4 (fp8 E4M3 x E2M1 on the scaled 16x16x128 MFMA, with the
-// E8M0 block scales applied by the hardware).
+// E8M0 block scales applied by the hardware), and for W4A4-MXFP4 (E2M1 x
+// E2M1 on the same MFMA, both operands' E8M0 scales applied by it).
 //
 // The pages' library serves large batches with a different, throughput-
 // oriented pipeline than small ones (kinachrichten, "Wie die Architektur
@@ -13,15 +14,16 @@
 //     (two per SIMD) a 64 x 64 tile each;
 //   * the K loop advances one 128-wide group per step; the A tile (128 rows
 //     of 128 bytes, padded to 144 so 16-byte fragment reads are conflict-
-//     free), the packed weight units, the per-group weight records and (fp8)
-//     the per-(row, group) activation scales of the next groups are copied
+//     free; fp4: 64 bytes padded to 80), the packed weight units, the
+//     per-group weight records and (fp8, fp4) the per-(row, group) activation
+//     scales of the next groups are copied
 //     global -> LDS by direct LDS loads into a 3-stage ring;
 //   * W8A8 accumulates exact int32 over the whole K range and applies the
 //     token and channel scales once in the epilogue; W4A8 moves each int4 to
 //     the high nibble of an int8 (16 q, exact; 1/16 is folded into the
 //     scale), takes an exact int32 partial per group and adds s * P in fp32
 //     (raw int32 mode keeps integers throughout); MXFP4 adds a_scale * P per
-//     group in fp32;
+//     group in fp32; W4A4 accumulates the scaled MFMA results directly;
 //   * the output tile goes through LDS so stores are whole 16-byte row
 //     segments; split-K writes fp32 partials that reduce_splits_kernel adds
 //     in split order.
@@ -33,24 +35,28 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-enum QKind { Q_W8A8 = 0, Q_W4A8 = 1, Q_MXFP4 = 2 };
+enum QKind { Q_W8A8 = 0, Q_W4A8 = 1, Q_MXFP4 = 2, Q_W4A4 = 3 };
 
 template <int KIND, int BM, int BN>
 struct QStage {
-  static constexpr int ROW = 144;                           // 128 bytes of A + 16 of padding
+  static constexpr int AROW = KIND == Q_W4A4 ? 64 : 128;    // bytes of A per row and group
+  static constexpr int ROW = AROW + 16;                     // + 16 of padding
+  static constexpr int CH = ROW / 16;                       // 16-byte slots per row (the last is padding)
   static constexpr int UNIT = KIND == Q_W8A8 ? 2048 : 1024;  // bytes per 16 x 128 weight unit
   static constexpr int A = 0;
-  static constexpr int A_SLOTS = BM * ROW / 16;              // 9 slots per row
-  static constexpr int AS = BM * ROW;                        // fp8: BM activation scales
-  static constexpr int W = AS + (KIND == Q_MXFP4 ? BM * 4 : 0);
+  static constexpr int A_SLOTS = BM * ROW / 16;
+  static constexpr int AS = BM * ROW;                        // fp8: BM fp32 scales; fp4: BM x 4 E8M0
+  static constexpr int W = AS + (KIND == Q_MXFP4 || KIND == Q_W4A4 ? BM * 4 : 0);
   static constexpr int REC = W + (BN / 16) * UNIT;           // W4A8 / MXFP4: 64 bytes per unit
   static constexpr int SCR = REC + (KIND == Q_W8A8 ? 0 : (BN / 16) * 64);  // 1 KiB sink for padding copies
-  static constexpr int BYTES = SCR + 1024;
+  // at least the 8 waves' 16 x 64 fp32 epilogue strips
+  static constexpr int BYTES = SCR + 1024 > 8 * 16 * 64 * 4 ? SCR + 1024 : 8 * 16 * 64 * 4;
 };
 
 // Copies of group g into stage `st` (device-only builtins: kept out of any
-// lambda). A: slot q = 64 i + lane is row q / 9, 16-byte chunk q % 9 (chunk 8
-// is padding and re-reads chunk 0); a_off holds each slot's row offset.
+// lambda). A: slot q = 64 i + lane is row q / CH, 16-byte chunk q % CH (the
+// last chunk is padding and re-reads chunk 0); a_off holds each slot's row
+// offset.
 // RAW is not used here: it only gives every kernel instance its own
 // specialization (hipcc's host pass rejects a second kernel that calls the
 // same specialization of a device function using target builtins).
@@ -63,7 +69,7 @@ __device__ __forceinline__ void q_load_stage(char* st, const char* a_g, const ui
   // compiler can then count exactly which copies a later wait covers.
   using L = QStage<KIND, BM, BN>;
   constexpr int A_INST = (L::A_SLOTS + 63) / 64;
-  const char* ag = a_g + (size_t)g * 128;
+  const char* ag = a_g + (size_t)g * L::AROW;
 #pragma unroll
   for (int r = 0; r < (A_INST + NW - 1) / NW; ++r) {
     const int i = r * NW + wave;
@@ -87,8 +93,9 @@ __device__ __forceinline__ void q_load_stage(char* st, const char* a_g, const ui
     __builtin_amdgcn_global_load_lds(sbase + ((size_t)tile * p.groups + g) * 64 + (lane & 3) * 16,
                                      (lds_void*)(st + (wave == NW - 1 ? L::REC : L::SCR)), 16, 0, 0);
   }
-  if constexpr (KIND == Q_MXFP4) {
-    // activation scales a_scales[row][g], one dword per row
+  if constexpr (KIND == Q_MXFP4 || KIND == Q_W4A4) {
+    // activation scales a_scales[row][g] (fp8: one fp32; fp4: the 4 E8M0
+    // bytes of the group's 32-blocks), one dword per row
 #pragma unroll
     for (int r = 0; r < BM / 64; ++r)
       __builtin_amdgcn_global_load_lds((const char*)p.a_scales + as_off[r] + (size_t)g * 4,
@@ -103,8 +110,9 @@ struct QFrag {
   u32x4_t a[4][2];  // A rows of the 4 row tiles (two 16-byte K slices)
   u32x4_t b[4][2];  // weights of the 4 column tiles (W4A8: packed int4 in b[t][0])
   float ws[4];      // W4A8: group scale s/16 of the lane's column
-  int e8[4];        // MXFP4: E8M0 block scale of the lane
+  int e8[4];        // MXFP4, W4A4: E8M0 block scale of the lane
   f32x4_t as[4];    // MXFP4: activation scales of the lane's 4 rows
+  int ae8[4];       // W4A4: E8M0 scale of the lane's A row and 32-block
 };
 
 template <int KIND, int BM, int BN>
@@ -128,9 +136,12 @@ __device__ __forceinline__ void q_frag_load(QFrag<KIND>& f, const char* st, int 
   for (int mt = 0; mt < 4; ++mt) {
     // int8 operand: lane group c holds K 32c..32c+15 (step 0) and +16 (step 1);
     // fp8 operand: K 16c..16c+15 and 64+16c..64+16c+15
+    // fp4 operand: K 32c..32c+31 (16 bytes)
     f.a[mt][0] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW);
-    f.a[mt][1] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + (KIND == Q_MXFP4 ? 64 : 16));
+    if constexpr (KIND != Q_W4A4)
+      f.a[mt][1] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + (KIND == Q_MXFP4 ? 64 : 16));
     if constexpr (KIND == Q_MXFP4) f.as[mt] = *(const f32x4_t*)(st + as_lane + mt * 64);
+    if constexpr (KIND == Q_W4A4) f.ae8[mt] = *(const uint8_t*)(st + as_lane + mt * 64);
   }
 }
 
@@ -154,7 +165,12 @@ __device__ __forceinline__ void q_frag_compute(const QFrag<KIND>& f, Acc (&acc)[
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      if constexpr (KIND == Q_MXFP4) {
+      if constexpr (KIND == Q_W4A4) {
+        const u32x4_t a0 = f.a[mt][0];
+        const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+        const i32x8_t bv = {(int)b[t][0].x, (int)b[t][0].y, (int)b[t][0].z, (int)b[t][0].w, 0, 0, 0, 0};
+        acc[mt][t] = mfma_fp4_fp4_scaled(av, bv, acc[mt][t], f.ae8[mt], f.e8[t]);
+      } else if constexpr (KIND == Q_MXFP4) {
         const u32x4_t a0 = f.a[mt][0], a1 = f.a[mt][1];
         const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
         const i32x8_t bv = {(int)b[t][0].x, (int)b[t][0].y, (int)b[t][0].z, (int)b[t][0].w, 0, 0, 0, 0};
@@ -189,7 +205,7 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
   // copies every wave issues per stage; waiting for the count to drop to
   // this leaves the next stage in flight
   constexpr int VM_NEXT = (A_INST + NW - 1) / NW + (W_INST + NW - 1) / NW + (KIND != Q_W8A8 ? 1 : 0) +
-                          (KIND == Q_MXFP4 ? BM / 64 : 0);
+                          (KIND == Q_MXFP4 || KIND == Q_W4A4 ? BM / 64 : 0);
   static_assert(NS == 2 || NS == 3, "two or three stages");
   // The stages are separate LDS objects (not one dynamic array) so that the
   // compiler can tell a copy into one stage from a read of another: reads of
@@ -232,10 +248,11 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
 #pragma unroll
   for (int r = 0; r < A_PER_WAVE; ++r) {
     const int q = (r * NW + wave) * 64 + lane;
-    const int row = min(q / 9, BM - 1), ch = q % 9;
+    const int row = min(q / L::CH, BM - 1), ch = q % L::CH;
     const int grow = mb * BM + row;
     const int src = grow < p.M ? grow : p.M - 1;
-    a_off[r] = (uint32_t)src * (uint32_t)p.K + (uint32_t)(ch < 8 ? ch : 0) * 16;
+    const uint32_t a_row = KIND == Q_W4A4 ? (uint32_t)p.K / 2 : (uint32_t)p.K;
+    a_off[r] = (uint32_t)src * a_row + (uint32_t)(ch < L::CH - 1 ? ch : 0) * 16;
   }
   uint32_t as_off[BM / 64];
 #pragma unroll
@@ -246,10 +263,12 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
   }
 
   // per-lane LDS offsets of the fragment reads inside a stage
-  const int a_lane = L::A + (wm * WTM + col) * L::ROW + (KIND == Q_MXFP4 ? 16 : 32) * c;
+  const int a_lane = L::A + (wm * WTM + col) * L::ROW + (KIND == Q_MXFP4 || KIND == Q_W4A4 ? 16 : 32) * c;
   const int w_lane = L::W + (wn * 4) * L::UNIT + lane * 16;
-  const int rec_lane = L::REC + (wn * 4) * 64 + (KIND == Q_MXFP4 ? lane : col * 4);
-  const int as_lane = L::AS + (wm * WTM + 4 * c) * 4;
+  const int rec_lane = L::REC + (wn * 4) * 64 + (KIND == Q_MXFP4 || KIND == Q_W4A4 ? lane : col * 4);
+  // fp8: the fp32 scales of the lane's 4 D rows; fp4: the E8M0 byte of the
+  // lane's A row and 32-block
+  const int as_lane = KIND == Q_W4A4 ? L::AS + (wm * WTM + col) * 4 + c : L::AS + (wm * WTM + 4 * c) * 4;
 
   Acc acc[4][4];
 #pragma unroll
@@ -322,7 +341,7 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int grow = mb * BM + wm * WTM + mt * 16 + 4 * c + i;
-      asc[i] = (KIND != Q_MXFP4 && !raw && grow < p.M) ? p.a_scales[grow] : 1.f;
+      asc[i] = (KIND != Q_MXFP4 && KIND != Q_W4A4 && !raw && grow < p.M) ? p.a_scales[grow] : 1.f;
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -397,6 +416,7 @@ hipError_t launch_qtile(Format f, const GemmArgs& a, int m_blocks, hipStream_t s
     case FMT_W8A8: return raw ? launch_q<Q_W8A8, true>(a, m_blocks, 1, s) : launch_q<Q_W8A8, false>(a, m_blocks, a.split, s);
     case FMT_W4A8: return raw ? launch_q<Q_W4A8, true>(a, m_blocks, 1, s) : launch_q<Q_W4A8, false>(a, m_blocks, a.split, s);
     case FMT_MXFP4: return launch_q<Q_MXFP4, false>(a, m_blocks, a.split, s);
+    case FMT_W4A4: return launch_q<Q_W4A4, false>(a, m_blocks, a.split, s);
     default: return hipErrorInvalidValue;
   }
 }

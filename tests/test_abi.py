@@ -194,7 +194,7 @@ def test_w4a4_layer_validation():
     p = q.qdg_plan_create(q.layer_w4a4(64, 256), q.dense())
     for m in (1, 16, 200, 5000):
         d = q.qdg_plan_describe(p, m)
-        assert "w4a4-mxfp4" in d and "family=stream" in d and "f4f4" in d
+        assert "w4a4-mxfp4" in d and ("family=stream" if m < 64 else "family=qtile") in d and "f4f4" in d
     pm = q.qdg_plan_create(q.layer_w4a4(64, 256, num_experts=4), q.moe(2))
     assert "family=stream" in q.qdg_moe_describe(pm, 8, 16)
     # the scales are required

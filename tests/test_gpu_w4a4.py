@@ -51,12 +51,14 @@ def _w4a4_case(m, n, k, otype, salt):
     return layer, pk, H.dev(codecs.pack_nibbles(ac)), H.dev(ae), y64
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 48, 256), (16, 512, 1024), (40, 130, 640), (100, 272, 512), (300, 96, 384)])
+@pytest.mark.parametrize("m,n,k", [(1, 48, 256), (16, 512, 1024), (40, 130, 640), (100, 272, 512), (300, 96, 384),
+                                   (640, 520, 1280)])
 @pytest.mark.parametrize("otype", [q.QDG_O_F32, q.QDG_O_BF16])
 def test_w4a4_gemm(qdg, m, n, k, otype):
     layer, pk, qa, sa, y64 = _w4a4_case(m, n, k, otype, salt=m + n)
     plan = q.qdg_plan_create(layer, q.dense())
-    assert "w4a4-mxfp4" in q.qdg_plan_describe(plan, m) and "family=stream" in q.qdg_plan_describe(plan, m)
+    fam = "family=qtile" if m >= 64 else "family=stream"  # fp4 x fp4 LDS-tiled family from M = 64
+    assert "w4a4-mxfp4" in q.qdg_plan_describe(plan, m) and fam in q.qdg_plan_describe(plan, m)
     y, _ = H.gemm(layer, pk, qa, m, a_scales=sa)
     assert not torch.isnan(y.float()).any()
     err = metrics.rel_frob(H.to_f64(y), y64)
@@ -107,4 +109,16 @@ def test_w4a4_moe(qdg, t, bm, per_pair):
                    npad.data_ptr(), t, bm, per_pair, y.data_ptr(), wsp.data_ptr(), wsb, q.current_stream())
     torch.cuda.synchronize()
     assert not torch.isnan(y).any(), "a pair row was not written"
+    assert metrics.rel_frob(H.to_f64(y), y64) <= 1e-3
+
+
+@pytest.mark.parametrize("split", [1, 3])
+def test_w4a4_tiled_split_k(qdg, split):
+    # the LDS-tiled family with K split into fixed-order fp32 partials
+    m, n, k = 200, 300, 1536
+    layer, pk, qa, sa, y64 = _w4a4_case(m, n, k, q.QDG_O_F32, salt=900 + split)
+    t = q.TuningConfig(block_m=128, split_k=split)
+    y, plan = H.gemm(layer, pk, qa, m, a_scales=sa, tuning=t)
+    d = q.qdg_plan_describe(plan, m)
+    assert "family=qtile" in d and f"split_k={split}" in d
     assert metrics.rel_frob(H.to_f64(y), y64) <= 1e-3
