@@ -243,6 +243,7 @@ def gpu_leg(args):
 
 PEAK_INT8_TOPS = 5000.0
 PEAK_FP8_TFLOPS = 5000.0
+PEAK_FP4_TFLOPS = 10100.0
 
 
 def _time_launches(launch, reps, stream):
@@ -267,7 +268,8 @@ def rows_leg(reps=30):
     """The other rows of the hot path, each timed at its own shapes (not part
     of `value`): W8A8 and W4A8-INT8 (K=4096, N in {4096, 14336}, M in
     {16, 256, 4096}), W4A8-MXFP4 ((K,N) in {(7168,2048), (2048,7168)}, M in
-    {16, 512, 4096}), the activation quantizers, and the grouped MoE W4A16
+    {16, 512, 4096}) and W4A4-MXFP4 at the same shapes, the activation
+    quantizers, and the grouped MoE W4A16
     GEMMs (E=256, top-8, hidden 7168, intermediate 2048, T in {64, 512,
     4096}) with their expert sort, the gate+up GEMM with the SiLU*mul
     epilogue and the top-k combine, and the grouped MoE W4A8-INT8 GEMMs of
@@ -282,7 +284,7 @@ def rows_leg(reps=30):
     sh = stream.cuda_stream
     out = []
 
-    def dense_row(name, layer, k, n, ms, qa_dtype, act_group, peak, w_bytes):
+    def dense_row(name, layer, k, n, ms, qa_dtype, act_group, peak, w_bytes, a_bits=8, as_bytes=4):
         nbytes = q.qdg_preprocess_query(layer)
         w = synth.device_normal_f32((n, k), 0.02, seed=synth.seed_for(2, synth.TID_W, n + k))
         if layer.wtype == q.QDG_W_INT8:
@@ -323,7 +325,7 @@ def rows_leg(reps=30):
             us_q = _time_launches(quant, reps, stream)
             us = _time_launches(gemm, reps, stream)
             fl = 2 * m * n * k
-            by = w_bytes + m * k * 1 + (m * (k // act_group) * 4 if act_group else m * 4) + m * n * 2
+            by = w_bytes + m * k * a_bits // 8 + (m * (k // act_group) * as_bytes if act_group else m * 4) + m * n * 2
             print(f"row {name} M={m} K={k} N={n}: {us:.2f} us", file=sys.stderr, flush=True)
             out.append(dict(row=name, M=m, K=k, N=n, us=round(us, 3), tflops=round(fl / us / 1e6, 2),
                             gbs=round(by / us / 1e3, 1), hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4),
@@ -340,6 +342,8 @@ def rows_leg(reps=30):
     for (k, n) in ((7168, 2048), (2048, 7168)):
         dense_row("w4a8-mxfp4", q.layer_mxfp4(n, k), k, n, (16, 512, 4096), torch.uint8, 128, PEAK_FP8_TFLOPS,
                   n * k // 2 + n * (k // 32))
+        dense_row("w4a4-mxfp4", q.layer_w4a4(n, k), k, n, (16, 512, 4096), torch.uint8, 32, PEAK_FP4_TFLOPS,
+                  n * k // 2 + n * (k // 32), a_bits=4, as_bytes=1)
 
     # ---- grouped MoE W4A16
     E, top_k, hid, inter = 256, 8, 7168, 2048

@@ -211,9 +211,10 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
 void qdg_plan_destroy(qdg_plan* plan);
 
 /* Workspace bytes qdg_gemm / qdg_moe_gemm need for M rows (M = T for MoE).
-   The first 64 KiB are reduction counters: zero them once after allocating
-   (for example hipMemset); every call leaves them zero again. Calls that
-   share one workspace must be ordered on one stream. */
+   It holds fp32 split-K partials (added by a second kernel in split order)
+   and, for the LDS-tiled W4A16 family, the row sums of A; its contents need
+   no initialisation (the first 64 KiB are reserved). Calls that share one
+   workspace must be ordered on one stream. */
 qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes);
 
 /* Writes a one-line record of the kernel instance that serves M rows (family,

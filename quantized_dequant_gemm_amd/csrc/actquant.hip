@@ -63,39 +63,41 @@ __device__ __forceinline__ uint32_t e2m1_rne_sat(float v) {
   return c | sign;
 }
 
-// MXFP4 per (token, 32-block): one thread per block (64 bytes in, 16 bytes of
-// codes and one E8M0 byte out; a wave covers 4 KiB of a row contiguously).
+// MXFP4 per (token, 32-block): four lanes per block, 8 values (16 bytes) each;
+// the block's amax comes from a 4-lane reduction. X is read from the
+// exponent field of amax (a subnormal amax, below 2^-126, gives the clamped
+// X = -127), and x / 2^X is a product with the power of two 2^-X, exact for
+// every value whose code is not 0.
 __global__ __launch_bounds__(256) void act_fp4_kernel(const uint16_t* __restrict__ a, uint8_t* __restrict__ q,
                                                       uint8_t* __restrict__ scales, int64_t blocks) {
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;  // block index: row * (K/32) + j
-  if (b >= blocks) return;
-  const uint16_t* x = a + b * 32;
-  float f[32];
+  const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = gl >> 2;  // block index: row * (K/32) + j
+  const int sub = threadIdx.x & 3;
+  if (b >= blocks) return;    // whole 4-lane segments exit together
+  const u32x4_t v = *(const u32x4_t*)(a + b * 32 + sub * 8);
+  float f[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4_t v = *(const u32x4_t*)(x + 8 * i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f[8 * i + 2 * j] = bf16_to_f32(v[j] & 0xFFFFu);
-      f[8 * i + 2 * j + 1] = bf16_to_f32(v[j] >> 16);
-    }
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = bf16_to_f32(v[j] & 0xFFFFu);
+    f[2 * j + 1] = bf16_to_f32(v[j] >> 16);
   }
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  u32x4_t out = {0, 0, 0, 0};
-  uint32_t e8 = 0;
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 4));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 4));
+  uint32_t out = 0, e8 = 0;
   if (amax > 0.f) {
-    int ex;
-    (void)frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1): floor(log2(amax)) = ex - 1
-    int X = ex - 1 - 2;
-    X = X < -127 ? -127 : X > 127 ? 127 : X;
+    const int ef = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFFu);
+    int X = ef == 0 ? -127 : ef - 127 - 2;  // floor(log2(amax)) - 2
+    X = X < -127 ? -127 : X;
     e8 = (uint32_t)(X + 127);
+    const float inv = __builtin_bit_cast(float, (uint32_t)(127 - X) << 23);  // 2^-X, X in [-127, 125]
 #pragma unroll
-    for (int i = 0; i < 32; ++i) out[i >> 3] |= e2m1_rne_sat(ldexpf(f[i], -X)) << (4 * (i & 7));
+    for (int i = 0; i < 8; ++i) out |= e2m1_rne_sat(f[i] * inv) << (4 * i);
   }
-  *(u32x4_t*)(q + b * 16) = out;
-  scales[b] = (uint8_t)e8;
+  *(uint32_t*)(q + b * 16 + sub * 4) = out;
+  if (sub == 0) scales[b] = (uint8_t)e8;
 }
 
 // int8 per token: one workgroup per row.
@@ -179,7 +181,7 @@ hipError_t launch_quantize_act(int atype, const void* a, int64_t M, int64_t K, v
                        scales, K);
   } else if (atype == QDG_A_MXFP4) {
     const int64_t blocks = M * (K / 32);
-    hipLaunchKernelGGL(act_fp4_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(act_fp4_kernel, dim3((unsigned)((blocks * 4 + 255) / 256)), dim3(256), 0, s,
                        (const uint16_t*)a, (uint8_t*)qa, (uint8_t*)scales, blocks);
   } else {
     const int64_t threads = M * (K / 128) * 16;

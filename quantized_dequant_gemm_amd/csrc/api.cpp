@@ -46,7 +46,6 @@ qdg_status hip_status(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr size_t kCounterBytes = 64 * 1024;
-constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(unsigned));
 constexpr int kTargetWorkgroups = 512;  // two 4-wave workgroups per CU (256 CUs)
 constexpr int kWsTargetWorkgroups = 256;  // weight streaming: one workgroup per CU
 
@@ -307,8 +306,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
     const int maxs = (int)(g.groups / ch.sc.kw);
     if (split > maxs) split = maxs > 0 ? maxs : 1;
   }
-  if (moe) split = 1;
-  if (nblocks * ch.grid_m > kMaxCounters) split = 1;
+  if (moe || P.layer.otype == QDG_O_I32) split = 1;  // raw integer results are not split
   ch.sc.split = split;
   ch.partial_bytes = split > 1 ? (size_t)nblocks * ch.grid_m * split * ch.sc.mt * nt * 4 * 64 * 4 : 0;
   return ch;
@@ -660,7 +658,12 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
     if (a.a_bytes >= ((int64_t)1 << 31))
       return fail(QDG_ERR_UNSUPPORTED, "A of %lld bytes is too large for the streaming family (< 2 GiB)",
                   (long long)a.a_bytes);
+    a.m_pad = c.grid_m * c.sc.mt * 16;
     e = launch_stream(plan->fmt, asym, moe, c.sc, a, c.grid_m, stream);
+    if (e == hipSuccess && a.split > 1) {
+      const int n_pad = (int)((plan->geom.ntiles + c.sc.nt - 1) / c.sc.nt * c.sc.nt * 16);
+      e = launch_reduce_splits(a, a.m_pad, n_pad, stream);
+    }
   }
   if (e == hipErrorInvalidValue) return fail(QDG_ERR_UNSUPPORTED, "no kernel instance for this tuning");
   return hip_status(e, "gemm launch");

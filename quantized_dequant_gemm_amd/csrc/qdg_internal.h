@@ -34,7 +34,7 @@ struct GemmArgs {
   int otype;
   int split;            // K partitions reduced through the workspace
   void* partial;        // fp32 / int32 split partials
-  unsigned* counters;   // arrival counters (zero between calls)
+  unsigned* counters;   // reserved (the first 64 KiB of the workspace)
   // grouped MoE
   const int* sorted_ids;
   const int* block_expert;

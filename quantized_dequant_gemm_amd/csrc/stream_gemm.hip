@@ -462,46 +462,12 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
           }
   }
 
-  // ---- split-K: publish the partial, the last workgroup of the tile reduces
-  if (p.split > 1) {
-    const size_t tile_id = (size_t)mb * gridDim.x + nb;
-    float* part = (float*)p.partial + (tile_id * p.split) * (kVals * 64);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          part[(size_t)split * kVals * 64 + ((mt * NT + t) * 4 + i) * 64 + lane] =
-              bits_as<float>(acc[mt][t][i]);
-    __threadfence();
-    unsigned prev = 0;
-    if (lane == 0) prev = atomicAdd(p.counters + tile_id, 1u);
-    prev = __shfl(prev, 0);
-    if (prev != (unsigned)(p.split - 1)) return;
-    __threadfence();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][t][i] = 0;
-    for (int s = 0; s < p.split; ++s) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = __builtin_nontemporal_load(&part[(size_t)s * kVals * 64 + ((mt * NT + t) * 4 + i) * 64 + lane]);
-            if constexpr (F::kIntAcc)
-              acc[mt][t][i] += __builtin_bit_cast(int, v);
-            else
-              acc[mt][t][i] += v;
-          }
-    }
-    if (lane == 0) p.counters[tile_id] = 0u;  // leave the workspace clean
-  }
+  // ---- split-K (dense, not raw int32): the scaled fp32 partial of this
+  // split goes to the workspace as [split][m_pad][n_pad], and
+  // reduce_splits_kernel adds the splits in split order (deterministic; no
+  // cross-workgroup fences, which on this part write back and invalidate L2)
+  const bool to_partial = p.split > 1;
+  const int n_pad = gridDim.x * NT * 16;
 
   // ---- epilogue: final scaling and store
 #pragma unroll
@@ -547,6 +513,10 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
           y = acc[mt][t][i];
         }
         yv[t] = y;
+        if (to_partial) {
+          ((float*)p.partial)[((size_t)split * p.m_pad + r) * n_pad + n] = y;
+          continue;
+        }
         if (silu) continue;
         if (p.otype == QDG_O_F32)
           ((float*)p.Y)[o] = y;
