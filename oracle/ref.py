@@ -79,6 +79,15 @@ def gemm_w8a8(qa, sa, qw, sw):
     return y, p.astype(np.int64)
 
 
+def gemm_w8a16(a_bf16_bits, qw, sw):
+    """bf16 activations times per-channel int8 weights (W8A16, a WNA16 width
+    the pages list): ``Y = A @ (q * s).T`` with the dequantized weights
+    ``w[n,k] = q[n,k] * s[n]`` in float64."""
+    a = codecs.bf16_bits_to_f64(a_bf16_bits)
+    w = np.asarray(qw, np.float64) * np.asarray(sw, np.float64)[:, None]
+    return a @ w.T
+
+
 def gemm_w4a8(qa, sa, q_int4_vals, sw_f16_bits, group=128):
     """Per-token int8 activations times int4 weights with fp16 group scales.
 

@@ -145,6 +145,24 @@ def test_mxfp4_gemm_brute_force():
             assert abs(float(acc) - y[i, j]) <= 1e-12 * abs(float(acc)) + 1e-300
 
 
+def test_w8a16_gemm_brute_force_and_one_hot():
+    # exact rationals: bf16 activations times q * s (s fp32), summed exactly
+    r = np.random.default_rng(25)
+    m, n, k = 2, 3, 64
+    a = codecs.f32_to_bf16_bits(r.standard_normal((m, k)).astype(np.float32))
+    qw = r.integers(-127, 128, (n, k))
+    sw = r.uniform(1e-3, 1e-2, n).astype(np.float32)
+    y = ref.gemm_w8a16(a, qw, sw)
+    av = codecs.bf16_bits_to_f64(a)
+    for i in range(m):
+        for j in range(n):
+            acc = sum(Fraction(float(av[i, kk])) * int(qw[j, kk]) for kk in range(k)) * Fraction(float(sw[j]))
+            assert abs(float(acc) - y[i, j]) <= 1e-12 * abs(float(acc)) + 1e-300
+    # one-hot activations return every dequantized weight exactly
+    eye = codecs.f32_to_bf16_bits(np.eye(k, dtype=np.float32))
+    assert np.array_equal(ref.gemm_w8a16(eye, qw, sw), (qw * sw.astype(np.float64)[:, None]).T)
+
+
 def test_w4a4_gemm_brute_force():
     # every product e2m1 * e2m1 * 2**(Ea + Eb - 254) is a short dyadic number;
     # the exact rational sum must equal the float64 reference
