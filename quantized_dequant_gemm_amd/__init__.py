@@ -262,6 +262,12 @@ def layer_mxfp4(n, k, otype=QDG_O_BF16, num_experts=1):
                        has_zeros=0, atype=QDG_A_FP8E4M3, act_group=128, otype=otype, arch=950)
 
 
+def layer_w8a16(n, k, otype=QDG_O_BF16, num_experts=1):
+    """int8 weights with fp32 per-channel scales, bf16 activations."""
+    return LayerConfig(n=n, k=k, num_experts=num_experts, wtype=QDG_W_INT8, stype=QDG_S_F32, group_size=0,
+                       has_zeros=0, atype=QDG_A_BF16, act_group=0, otype=otype, arch=950)
+
+
 def layer_w4a4(n, k, otype=QDG_O_BF16, num_experts=1):
     """MXFP4 weights with MXFP4 activations (E8M0 per 32-block on both sides)."""
     return LayerConfig(n=n, k=k, num_experts=num_experts, wtype=QDG_W_MXFP4, stype=QDG_S_E8M0, group_size=32,

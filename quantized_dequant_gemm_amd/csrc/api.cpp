@@ -56,7 +56,7 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 namespace qdg {
 
 Format format_of(const qdg_layer_config& L) {
-  if (L.wtype == QDG_W_INT8) return FMT_W8A8;
+  if (L.wtype == QDG_W_INT8) return L.atype == QDG_A_BF16 ? FMT_W8A16 : FMT_W8A8;
   if (L.wtype == QDG_W_MXFP4) return L.atype == QDG_A_MXFP4 ? FMT_W4A4 : FMT_MXFP4;
   if (L.atype == QDG_A_INT8) return FMT_W4A8;
   return FMT_W4A16;
@@ -71,13 +71,14 @@ PackedGeom packed_geom(const qdg_layer_config& L, Format f) {
   g.groups = L.k / 128;
   g.experts = L.num_experts;
   const int64_t units = g.ntiles * g.groups;
-  g.w_bytes = units * (f == FMT_W8A8 ? 2048 : 1024);  // bytes per 16x128 unit
+  g.w_bytes = units * (f == FMT_W8A8 || f == FMT_W8A16 ? 2048 : 1024);  // bytes per 16x128 unit
   switch (f) {
     case FMT_W4A16: g.s_bytes = units * 16 * 8; break;  // {f32 s, bf16x2 -(128+z)}
     case FMT_W4A8: g.s_bytes = units * 16 * 4; break;   // f32 s/16
     case FMT_MXFP4:
     case FMT_W4A4: g.s_bytes = units * 64; break;       // E8M0 per lane
-    case FMT_W8A8: g.s_bytes = g.n_pad * 4; break;      // f32 per column
+    case FMT_W8A8:
+    case FMT_W8A16: g.s_bytes = g.n_pad * 4; break;     // f32 per column
   }
   g.s_offset = align_up(g.w_bytes, 256);
   g.expert_stride = align_up(g.s_offset + g.s_bytes, 256);
@@ -110,6 +111,7 @@ const char* fmt_name(Format f, const qdg_layer_config& L) {
   switch (f) {
     case FMT_W4A16: return L.wtype == QDG_W_UINT4 ? "w4a16-uint4-asym" : "w4a16-int4-sym";
     case FMT_W8A8: return "w8a8-int8";
+    case FMT_W8A16: return "w8a16-int8";
     case FMT_W4A8: return "w4a8-int8";
     case FMT_MXFP4: return "w4a8-mxfp4-fp8";
     case FMT_W4A4: return "w4a4-mxfp4";
@@ -153,8 +155,13 @@ qdg_status validate_layer(const qdg_layer_config* L) {
       if (L->stype != QDG_S_F32) return fail(QDG_ERR_UNSUPPORTED, "int8 weights need f32 per-channel scales");
       if (L->group_size != 0) return fail(QDG_ERR_UNSUPPORTED, "int8 weights are per channel (group_size 0)");
       if (L->has_zeros) return fail(QDG_ERR_UNSUPPORTED, "int8 weights are symmetric");
+      if (L->atype == QDG_A_BF16) {  // W8A16
+        if (L->act_group != 0) return fail(QDG_ERR_INVALID_ARG, "bf16 activations have no groups");
+        if (L->otype == QDG_O_I32) return fail(QDG_ERR_UNSUPPORTED, "W8A16 has no integer accumulator");
+        return ok();
+      }
       if (L->atype != QDG_A_INT8 || L->act_group != 0)
-        return fail(QDG_ERR_UNSUPPORTED, "int8 weights run with per-token int8 activations only");
+        return fail(QDG_ERR_UNSUPPORTED, "int8 weights run with per-token int8 or bf16 activations");
       if (L->k > 65536) return fail(QDG_ERR_UNSUPPORTED, "int8 paths keep |q*qa| sums in int32: k <= 65536");
       return ok();
     case QDG_W_MXFP4:
@@ -242,7 +249,8 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   }
   // weight-streaming family of the int8 / fp8 formats (dense M <= 16): the
   // K range of a workgroup must fit its LDS; raw int32 output is not split
-  if (bm == 16 && P.fmt != FMT_W4A16 && P.fmt != FMT_W4A4 && !moe && !P.compute.batch_invariant && ws_tuning_ok) {
+  if (bm == 16 && P.fmt != FMT_W4A16 && P.fmt != FMT_W4A4 && P.fmt != FMT_W8A16 && !moe && !P.compute.batch_invariant &&
+      ws_tuning_ok) {
     // 4 N tiles per workgroup when that gives enough workgroups, else one
     // tile with all 8 waves on its K range (no split across workgroups)
     const int nt = (g.ntiles + 3) / 4 >= 128 ? 4 : 1;
@@ -268,7 +276,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   // (measured on MI355X: from M = 64 the tiled family with K split into one
   // pass of 256 workgroups beats the streaming family at these layer sizes)
   const bool q_enough = (has_tuning && T.block_m >= 128) || M >= 64;
-  if (bm >= 128 && P.fmt != FMT_W4A16 && !moe && a8_fits && q_enough) {
+  if (bm >= 128 && P.fmt != FMT_W4A16 && P.fmt != FMT_W8A16 && !moe && a8_fits && q_enough) {
     ch.tile = true;
     ch.qtile = true;
     ch.tc = TileCfg{128, 256, 8};
@@ -552,6 +560,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
 // The MFMA instruction an instance issues.
 static const char* mfma_name(Format f, const Choice& c) {
   if (f == FMT_W4A16) return c.tile && c.tc.bm * c.tc.bn / (64 * c.tc.waves) == 64 ? "32x32x16_bf16" : "16x16x32_bf16";
+  if (f == FMT_W8A16) return "16x16x32_bf16";
   if (f == FMT_MXFP4) return "scale_16x16x128_f8f6f4";
   if (f == FMT_W4A4) return "scale_16x16x128_f4f4";
   return "16x16x64_i8";
@@ -654,7 +663,8 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   } else {
     // the streaming family addresses A with 31-bit byte offsets
     const int64_t a_rows = moe ? (a_per_pair ? rows : T) : M;
-    a.a_bytes = a_rows * (plan->fmt == FMT_W4A16 ? 2 * (int64_t)a.K : plan->fmt == FMT_W4A4 ? a.K / 2 : a.K);
+    const bool bf16_a = plan->fmt == FMT_W4A16 || plan->fmt == FMT_W8A16;
+    a.a_bytes = a_rows * (bf16_a ? 2 * (int64_t)a.K : plan->fmt == FMT_W4A4 ? a.K / 2 : a.K);
     if (a.a_bytes >= ((int64_t)1 << 31))
       return fail(QDG_ERR_UNSUPPORTED, "A of %lld bytes is too large for the streaming family (< 2 GiB)",
                   (long long)a.a_bytes);
@@ -677,7 +687,7 @@ qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, 
   if (M == 0) return ok();
   if (M > 0x7FFFFFFF / 2) return fail(QDG_ERR_UNSUPPORTED, "M too large");
   if (!A || !packed || !Y) return fail(QDG_ERR_INVALID_ARG, "NULL A, packed or Y");
-  const bool need_scales = plan->fmt != FMT_W4A16 && plan->layer.otype != QDG_O_I32;
+  const bool need_scales = plan->fmt != FMT_W4A16 && plan->fmt != FMT_W8A16 && plan->layer.otype != QDG_O_I32;
   if (plan->fmt == FMT_MXFP4 || plan->fmt == FMT_W4A4) {
     if (!a_scales) return fail(QDG_ERR_INVALID_ARG, "MXFP4 needs activation scales");
   } else if (need_scales && !a_scales) {
@@ -857,8 +867,8 @@ qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scal
   if (T * plan->compute.top_k > (1 << 20)) return fail(QDG_ERR_UNSUPPORTED, "T*top_k above 2^20");
   if (!A || !packed || !Y || !sorted_ids || !block_expert || !num_padded)
     return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
-  if (plan->fmt != FMT_W4A16 && (plan->fmt == FMT_MXFP4 || plan->fmt == FMT_W4A4 || plan->layer.otype != QDG_O_I32) &&
-      !a_scales)
+  if (plan->fmt != FMT_W4A16 && plan->fmt != FMT_W8A16 &&
+      (plan->fmt == FMT_MXFP4 || plan->fmt == FMT_W4A4 || plan->layer.otype != QDG_O_I32) && !a_scales)
     return fail(QDG_ERR_INVALID_ARG, "activation scales are NULL");
   if (!aligned(A, 16)) return fail(QDG_ERR_MISALIGNED, "A must be 16-byte aligned");
   if (!aligned(packed, 256)) return fail(QDG_ERR_MISALIGNED, "packed must be 256-byte aligned");

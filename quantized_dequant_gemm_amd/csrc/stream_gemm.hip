@@ -291,6 +291,82 @@ struct FmtW4A4 {
   }
 };
 
+// W8A16: bf16 activations, int8 weights with one fp32 scale per output
+// channel. The weight unit is the W8A8 one (lane group c holds K 32c..32c+15
+// in its first 16-byte chunk and 32c+16..32c+31 in its second). Each int8 q
+// enters the bf16 MFMA as the integer q + 128 (0..255, exact in bf16: byte to
+// fp32 conversion, then the fp32 bits' upper half); a group's chain starts
+// from -128 * rowsum(A), so the MFMA sums are exactly sum A*q per group in
+// fp32; the channel scale is applied once in the epilogue.
+struct FmtW8A16 {
+  using Acc = f32x4_t;
+  static constexpr bool kIntAcc = false;
+  template <int MT, int NT>
+  struct Frag {
+    u32x4_t a[MT][4];
+    u32x4_t b[NT][2];
+  };
+  template <int MT, int NT>
+  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t o = x.aoff[mt] + (uint32_t)(g * 256 + 64 * x.c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.a[mt][j] = lda(x.arsrc, o + 16 * j);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4_t* pu = (const u32x4_t*)(x.wbase + ((size_t)x.tile[t] * x.groups + g) * kUnit8Bytes);
+      f.b[t][0] = ldg_nt(pu + x.lane);
+      f.b[t][1] = ldg_nt(pu + 64 + x.lane);
+    }
+  }
+  // four int8 codes (one dword) -> two bf16 pairs of q + 128
+  __device__ static void widen(uint32_t d, uint32_t& lo, uint32_t& hi) {
+    const uint32_t u = d ^ 0x80808080u;
+    const uint32_t f0 = __builtin_bit_cast(uint32_t, (float)(u & 0xFFu));
+    const uint32_t f1 = __builtin_bit_cast(uint32_t, (float)((u >> 8) & 0xFFu));
+    const uint32_t f2 = __builtin_bit_cast(uint32_t, (float)((u >> 16) & 0xFFu));
+    const uint32_t f3 = __builtin_bit_cast(uint32_t, (float)(u >> 24));
+    lo = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+    hi = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+  }
+  template <int MT, int NT>
+  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT], uint32_t, uint32_t) {
+    f32x4_t corr[MT];
+    const u32x4_t k128 = {0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u};  // bf16 -128
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z = mfma_bf16(f.a[mt][j], k128, z);
+      corr[mt] = z;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      u32x4_t bw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // step j: K 32c + 8j .. +7 = bytes 8 (j % 2) .. +7 of chunk j / 2
+        const u32x4_t ch = f.b[t][j / 2];
+        const uint32_t d0 = (j % 2) ? ch.z : ch.x, d1 = (j % 2) ? ch.w : ch.y;
+        uint32_t w0, w1, w2, w3;
+        widen(d0, w0, w1);
+        widen(d1, w2, w3);
+        bw[j] = u32x4_t{w0, w1, w2, w3};
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4_t p = corr[mt];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p = mfma_bf16(f.a[mt][j], bw[j], p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][t][i] += p[i];
+      }
+    }
+  }
+};
+
 // ----------------------------------------------------------------- kernel
 
 template <class F, int MT, int NT, int KW, int U, bool MOE>
@@ -337,7 +413,8 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
   }
   x.wbase = p.packed + (size_t)expert * p.expert_stride;
   x.sbase = x.wbase + p.s_offset;
-  constexpr bool kBf16A = std::is_same<F, FmtW4A16<false>>::value || std::is_same<F, FmtW4A16<true>>::value;
+  constexpr bool kBf16A = std::is_same<F, FmtW4A16<false>>::value || std::is_same<F, FmtW4A16<true>>::value ||
+                          std::is_same<F, FmtW8A16>::value;
   constexpr bool kFp4A = std::is_same<F, FmtW4A4>::value;
   const size_t a_row_bytes = kBf16A ? (size_t)p.K * 2 : kFp4A ? (size_t)p.K / 2 : (size_t)p.K;
 #pragma unroll
@@ -505,6 +582,8 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
           // W8A8: exact int32 sum, then per-token x per-channel scale
           const float sw = ((const float*)x.sbase)[n];
           y = (float)acc[mt][t][i] * p.a_scales[arow] * sw;
+        } else if constexpr (std::is_same<F, FmtW8A16>::value) {
+          y = acc[mt][t][i] * ((const float*)x.sbase)[n];  // per-channel scale
         } else if constexpr (std::is_same<F, FmtInt8<true, false>>::value) {
           y = acc[mt][t][i] * p.a_scales[arow];
         } else if constexpr (F::kIntAcc) {
@@ -594,6 +673,8 @@ hipError_t launch_stream(Format f, bool asym, bool moe, const StreamCfg& c, cons
       return dispatch_shape<FmtMxfp4>(c, moe, a, grid_m, s);
     case FMT_W4A4:
       return dispatch_shape<FmtW4A4>(c, moe, a, grid_m, s);
+    case FMT_W8A16:
+      return dispatch_shape<FmtW8A16>(c, moe, a, grid_m, s);
   }
   return hipErrorInvalidValue;
 }

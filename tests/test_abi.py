@@ -199,3 +199,13 @@ def test_w4a4_layer_validation():
     assert "family=stream" in q.qdg_moe_describe(pm, 8, 16)
     # the scales are required
     assert _status(q.qdg_gemm, p, 0x1000, None, 256, 256, 4, 256, 1 << 20, 0) == q.QDG_ERR_INVALID_ARG
+
+
+def test_w8a16_layer_validation():
+    q.qdg_validate_layer(q.layer_w8a16(64, 256))
+    p = q.qdg_plan_create(q.layer_w8a16(64, 256), q.dense())
+    for m in (1, 16, 200):
+        d = q.qdg_plan_describe(p, m)
+        assert "w8a16-int8" in d and "family=stream" in d
+    bad = q.layer_w8a16(64, 256, otype=q.QDG_O_I32)
+    assert _status(q.qdg_validate_layer, bad) == q.QDG_ERR_UNSUPPORTED
