@@ -266,7 +266,7 @@ def _time_launches(launch, reps, stream):
 
 def rows_leg(reps=30):
     """The other rows of the hot path, each timed at its own shapes (not part
-    of `value`): W8A8 and W4A8-INT8 (K=4096, N in {4096, 14336}, M in
+    of `value`): W8A8, W4A8-INT8 and W8A16 (K=4096, N in {4096, 14336}, M in
     {16, 256, 4096}), W4A8-MXFP4 ((K,N) in {(7168,2048), (2048,7168)}, M in
     {16, 512, 4096}) and W4A4-MXFP4 at the same shapes, the activation
     quantizers, and the grouped MoE W4A16
@@ -313,19 +313,26 @@ def rows_leg(reps=30):
             wsb = q.qdg_plan_workspace(plan, m)
             ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
 
+            bf16_a = layer.atype == q.QDG_A_BF16  # W8A16: A goes in as it is
+
             def quant(i):
                 q.qdg_quantize_act(layer, a.data_ptr(), m, qa.data_ptr(), sa.data_ptr(), sh)
 
             def gemm(i):
-                q.qdg_gemm(plan, qa.data_ptr(), sa.data_ptr(), bufs[i % len(bufs)].data_ptr(), y.data_ptr(), m,
-                           ws.data_ptr(), wsb, sh)
-            quant(0)
+                q.qdg_gemm(plan, (a if bf16_a else qa).data_ptr(), None if bf16_a else sa.data_ptr(),
+                           bufs[i % len(bufs)].data_ptr(), y.data_ptr(), m, ws.data_ptr(), wsb, sh)
+            if not bf16_a:
+                quant(0)
             for i in range(3):
                 gemm(i)
-            us_q = _time_launches(quant, reps, stream)
+            us_q = 0.0 if bf16_a else _time_launches(quant, reps, stream)
             us = _time_launches(gemm, reps, stream)
             fl = 2 * m * n * k
-            by = w_bytes + m * k * a_bits // 8 + (m * (k // act_group) * as_bytes if act_group else m * 4) + m * n * 2
+            if bf16_a:
+                by = w_bytes + m * k * 2 + m * n * 2
+            else:
+                by = (w_bytes + m * k * a_bits // 8 + (m * (k // act_group) * as_bytes if act_group else m * 4)
+                      + m * n * 2)
             print(f"row {name} M={m} K={k} N={n}: {us:.2f} us", file=sys.stderr, flush=True)
             out.append(dict(row=name, M=m, K=k, N=n, us=round(us, 3), tflops=round(fl / us / 1e6, 2),
                             gbs=round(by / us / 1e3, 1), hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4),
@@ -339,6 +346,8 @@ def rows_leg(reps=30):
                   n * k + n * 4)
         dense_row("w4a8-int8", q.layer_w4a8(n, k), k, n, (16, 256, 4096), torch.int8, 0, PEAK_INT8_TOPS,
                   n * k // 2 + n * (k // 128) * 2)
+        dense_row("w8a16", q.layer_w8a16(n, k), k, n, (16, 256, 4096), torch.int8, 0, PEAK_BF16_TFLOPS,
+                  n * k + n * 4)
     for (k, n) in ((7168, 2048), (2048, 7168)):
         dense_row("w4a8-mxfp4", q.layer_mxfp4(n, k), k, n, (16, 512, 4096), torch.uint8, 128, PEAK_FP8_TFLOPS,
                   n * k // 2 + n * (k // 32))
