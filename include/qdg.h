@@ -39,8 +39,10 @@
 #ifndef QDG_H
 #define QDG_H
 
+#ifndef __HIPCC_RTC__
 #include <stddef.h>
 #include <stdint.h>
+#endif
 
 #ifdef __cplusplus
 extern "C" {
@@ -237,6 +239,29 @@ int qdg_moe_describe(const qdg_plan* plan, int64_t T, int32_t block_m, char* buf
    M >= 0 (M = 0 enqueues nothing). workspace >= qdg_plan_workspace bytes. */
 qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, const void* packed,
                     void* Y, int64_t M, void* workspace, size_t ws_bytes, void* stream);
+
+/* Run-time compilation (the pages build each kernel instance at run time
+   from its configuration: kinachrichten, "Kompilierzeiten und
+   gerätespezifisches Tuning"; jetabc, "Humming 的做法", item 3). Compiles
+   with hipRTC the streaming-family instance that serves M rows of the plan
+   (for a MoE plan: T = M tokens in block_m-row blocks; block_m is ignored
+   for dense plans), from the kernel source embedded in the library, loads
+   it on the current device, and makes the plan launch it for every call
+   that selects that instance ("code=jit" in the descriptions). With a
+   cache_dir (may be NULL) the code object is stored there, under a key of
+   the instance, the target, the options and the source text, and later
+   processes load it instead of compiling. Instances of the other families
+   return QDG_ERR_UNSUPPORTED; a compile or load failure QDG_ERR_HIP (with
+   the compiler log in qdg_last_error). Blocks while compiling. The plan is
+   modified: no other call may use it concurrently. */
+typedef struct qdg_jit_info {
+  double compile_ms;  /* hipRTC compile time; 0 when no compile was needed */
+  double load_ms;     /* code object load time */
+  int32_t from_cache; /* 0 compiled now, 1 read from cache_dir, 2 already loaded */
+  int32_t code_bytes;
+  char key[32];       /* cache key (hex) */
+} qdg_jit_info;
+qdg_status qdg_plan_jit(qdg_plan* plan, int64_t M, int32_t block_m, const char* cache_dir, qdg_jit_info* info);
 
 /* Per-M-range autotuning of a dense plan (the pages' per-device tuning of
    the kernel instances per M range, with heuristics as the fallback:

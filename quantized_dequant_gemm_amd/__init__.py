@@ -35,6 +35,7 @@ EXPORTS = (
     "qdg_quantize_weights", "qdg_quantize_act", "qdg_plan_create", "qdg_plan_destroy", "qdg_plan_workspace",
     "qdg_plan_describe", "qdg_moe_describe", "qdg_gemm", "qdg_moe_align_capacity", "qdg_moe_align",
     "qdg_moe_gemm", "qdg_moe_combine", "qdg_plan_autotune", "qdg_plan_autotune_reset",
+    "qdg_plan_jit",
 )
 
 
@@ -98,6 +99,7 @@ def load():
         "qdg_moe_combine": (I32, [P, P, I64, I32, I64, P, I32, P]),
         "qdg_plan_autotune": (I32, [P, P, P, P, P, I64, P, SZ, I32, P, P, P]),
         "qdg_plan_autotune_reset": (I32, [P]),
+        "qdg_plan_jit": (I32, [P, I64, I32, ctypes.c_char_p, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -233,6 +235,19 @@ def qdg_plan_autotune(plan, A, a_scales, packed, Y, M, workspace, ws_bytes, reps
     _check(load().qdg_plan_autotune(plan.handle, A, a_scales, packed, Y, M, workspace, ws_bytes, reps, stream,
                                     ctypes.byref(chosen), ctypes.byref(us)))
     return chosen, us.value
+
+
+class JitInfo(ctypes.Structure):
+    _fields_ = [("compile_ms", ctypes.c_double), ("load_ms", ctypes.c_double), ("from_cache", ctypes.c_int32),
+                ("code_bytes", ctypes.c_int32), ("key", ctypes.c_char * 32)]
+
+
+def qdg_plan_jit(plan, M, block_m=0, cache_dir=None):
+    """Returns the JitInfo of the run-time compiled instance serving M."""
+    info = JitInfo()
+    _check(load().qdg_plan_jit(plan.handle, M, block_m, cache_dir.encode() if cache_dir else None,
+                               ctypes.byref(info)))
+    return info
 
 
 def qdg_plan_autotune_reset(plan):

@@ -17,6 +17,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "qdg_internal.h"
 
@@ -95,6 +96,14 @@ struct AutoEntry {
 };
 constexpr int kAutoRanges = 32;
 
+// A run-time compiled streaming-family instance the plan launches instead of
+// the ahead-of-time one (qdg_plan_jit).
+struct JitInstance {
+  int mt, nt, kw, device;
+  bool moe;
+  hipFunction_t fn;
+};
+
 struct qdg_plan {
   qdg_layer_config layer;
   qdg_compute_config compute;
@@ -103,6 +112,7 @@ struct qdg_plan {
   Format fmt;
   PackedGeom geom;
   AutoEntry autot[kAutoRanges];  // written by qdg_plan_autotune only
+  std::vector<JitInstance> jit;  // written by qdg_plan_jit only
 };
 
 namespace {
@@ -566,17 +576,27 @@ static const char* mfma_name(Format f, const Choice& c) {
   return "16x16x64_i8";
 }
 
+static const JitInstance* find_jit(const qdg_plan& plan, const Choice& c, bool moe) {
+  if (c.ws || c.tile || c.qtile || plan.jit.empty()) return nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  for (const JitInstance& j : plan.jit)
+    if (j.mt == c.sc.mt && j.nt == c.sc.nt && j.kw == c.sc.kw && j.moe == moe && j.device == dev) return &j;
+  return nullptr;
+}
+
 static int describe(const qdg_plan& plan, const Choice& c, int64_t M, const char* kind, char* buf, size_t len) {
   return snprintf(buf, buf ? len : 0,
                   "%s %s n=%lld k=%lld E=%lld M=%lld: family=%s block_m=%d block_n=%d split_k=%d "
-                  "waves=%d mfma=%s grid_m=%d batch_invariant=%d epilogue=%s tuning=%s layout=%d arch=gfx950",
+                  "waves=%d mfma=%s grid_m=%d batch_invariant=%d epilogue=%s tuning=%s code=%s layout=%d arch=gfx950",
                   fmt_name(plan.fmt, plan.layer), kind, (long long)plan.layer.n, (long long)plan.layer.k,
                   (long long)plan.layer.num_experts, (long long)M,
                   c.qtile ? "qtile" : c.tile ? "tile" : c.ws ? "wstream" : "stream",
                   c.tile || c.qtile ? c.tc.bm : c.sc.mt * 16, c.tile || c.qtile ? c.tc.bn : c.sc.nt * 16,
                   c.sc.split, c.tile || c.qtile ? c.tc.waves : c.sc.kw, mfma_name(plan.fmt, c), c.grid_m,
                   plan.compute.batch_invariant, plan.compute.epilogue == QDG_EPI_SILU_MUL ? "silu_mul" : "none",
-                  c.autotuned ? "autotuned" : plan.has_tuning ? "user" : "heuristic", QDG_LAYOUT_VERSION);
+                  c.autotuned ? "autotuned" : plan.has_tuning ? "user" : "heuristic",
+                  find_jit(plan, c, plan.compute.kind == QDG_KIND_MOE) ? "jit" : "aot", QDG_LAYOUT_VERSION);
 }
 
 int qdg_plan_describe(const qdg_plan* plan, int64_t M, char* buf, size_t len) {
@@ -669,7 +689,9 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
       return fail(QDG_ERR_UNSUPPORTED, "A of %lld bytes is too large for the streaming family (< 2 GiB)",
                   (long long)a.a_bytes);
     a.m_pad = c.grid_m * c.sc.mt * 16;
-    e = launch_stream(plan->fmt, asym, moe, c.sc, a, c.grid_m, stream);
+    const JitInstance* jit = find_jit(*plan, c, moe);
+    e = jit ? launch_stream_jit(jit->fn, c.sc, a, c.grid_m, stream)
+            : launch_stream(plan->fmt, asym, moe, c.sc, a, c.grid_m, stream);
     if (e == hipSuccess && a.split > 1) {
       const int n_pad = (int)((plan->geom.ntiles + c.sc.nt - 1) / c.sc.nt * c.sc.nt * 16);
       e = launch_reduce_splits(a, a.m_pad, n_pad, stream);
@@ -828,6 +850,42 @@ qdg_status qdg_plan_autotune(qdg_plan* plan, const void* A, const float* a_scale
 qdg_status qdg_plan_autotune_reset(qdg_plan* plan) {
   if (!plan) return fail(QDG_ERR_INVALID_ARG, "plan is NULL");
   std::memset(plan->autot, 0, sizeof plan->autot);
+  return ok();
+}
+
+qdg_status qdg_plan_jit(qdg_plan* plan, int64_t M, int32_t block_m, const char* cache_dir, qdg_jit_info* info) {
+  if (!plan) return fail(QDG_ERR_INVALID_ARG, "plan is NULL");
+  if (M < 1) return fail(QDG_ERR_INVALID_ARG, "M must be >= 1");
+  const bool moe = plan->compute.kind == QDG_KIND_MOE;
+  Choice c;
+  if (moe) {
+    if (choose_moe(*plan, M, block_m, 0, &c) != QDG_OK) return QDG_ERR_UNSUPPORTED;
+  } else {
+    c = choose(*plan, M);
+  }
+  if (c.ws || c.tile || c.qtile || !stream_cfg_supported(plan->fmt, c.sc))
+    return fail(QDG_ERR_UNSUPPORTED, "run-time compilation covers the streaming family; this M runs %s",
+                c.qtile ? "the 8-bit LDS-tiled family" : c.tile ? "the LDS-tiled family" : "weight streaming");
+  const bool asym = plan->layer.wtype == QDG_W_UINT4;
+  const bool raw = plan->layer.otype == QDG_O_I32;
+  JitResult r = jit_stream_kernel(plan->fmt, asym, raw, c.sc, moe, cache_dir);
+  if (!r.fn) return fail(QDG_ERR_HIP, "%s", r.error.c_str());
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  bool found = false;
+  for (JitInstance& j : plan->jit)
+    if (j.mt == c.sc.mt && j.nt == c.sc.nt && j.kw == c.sc.kw && j.moe == moe && j.device == dev) {
+      j.fn = r.fn;
+      found = true;
+    }
+  if (!found) plan->jit.push_back(JitInstance{c.sc.mt, c.sc.nt, c.sc.kw, dev, moe, r.fn});
+  if (info) {
+    info->compile_ms = r.compile_ms;
+    info->load_ms = r.load_ms;
+    info->from_cache = r.from_cache;
+    info->code_bytes = r.code_bytes;
+    std::snprintf(info->key, sizeof info->key, "%s", r.key);
+  }
   return ok();
 }
 

@@ -9,8 +9,30 @@
 // operand of lane l is therefore built from A[row][32c .. 32c+31] and the
 // matching weights, which keeps the A loads contiguous as well.
 #pragma once
+#ifdef __HIPCC_RTC__
+// Run-time compilation (hipRTC, qdg_plan_jit) has no C library headers: the
+// fixed-width types and the two type traits the kernels use, from the
+// compiler's own definitions.
+typedef __INT8_TYPE__ int8_t;
+typedef __UINT8_TYPE__ uint8_t;
+typedef __INT16_TYPE__ int16_t;
+typedef __UINT16_TYPE__ uint16_t;
+typedef __INT32_TYPE__ int32_t;
+typedef __UINT32_TYPE__ uint32_t;
+typedef __INT64_TYPE__ int64_t;
+typedef __UINT64_TYPE__ uint64_t;
+typedef __SIZE_TYPE__ size_t;
+typedef __UINTPTR_TYPE__ uintptr_t;
+namespace std {
+template <class A, class B> struct is_same { static constexpr bool value = false; };
+template <class A> struct is_same<A, A> { static constexpr bool value = true; };
+template <bool C, class T, class F> struct conditional { using type = T; };
+template <class T, class F> struct conditional<false, T, F> { using type = F; };
+}  // namespace std
+#else
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#endif
 
 namespace qdg {
 

@@ -1,10 +1,14 @@
 // Internal (not exported) interface between the C-ABI layer and the kernels.
 #pragma once
+#ifndef __HIPCC_RTC__
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/qdg.h"
+#include <string>
+#endif
+
+#include "qdg.h"
 
 namespace qdg {
 
@@ -65,6 +69,7 @@ struct TileCfg {
   int bm, bn, waves;
 };
 
+#ifndef __HIPCC_RTC__  // host launchers (not part of a run-time compiled kernel)
 hipError_t launch_stream(Format f, bool asym, bool moe, const StreamCfg& c, const GemmArgs& a,
                          int grid_m_blocks, hipStream_t s);
 hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const GemmArgs& a,
@@ -89,8 +94,23 @@ hipError_t launch_quantize_act(int atype, const void* a, int64_t M, int64_t K, v
                                float* scales, hipStream_t s);
 hipError_t launch_moe_combine(const float* y, const float* w, int64_t T, int top_k, int64_t n, void* out,
                               int otype, hipStream_t s);
+// Run-time compiled streaming-family instance (hipRTC): the loaded kernel,
+// or an error. from_cache: 0 compiled now, 1 code object read from the cache
+// directory, 2 already loaded in this process.
+struct JitResult {
+  hipFunction_t fn;
+  double compile_ms, load_ms;
+  int from_cache, code_bytes;
+  char key[32];
+  std::string lowered, error;
+};
+JitResult jit_stream_kernel(Format f, bool asym, bool raw, const StreamCfg& c, bool moe, const char* cache_dir);
+hipError_t launch_stream_jit(hipFunction_t fn, const StreamCfg& c, const GemmArgs& a, int grid_m, hipStream_t s);
+
 hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int block_m,
                             int64_t capacity, int32_t* sorted_ids, int32_t* block_expert,
                             int32_t* num_padded, hipStream_t s);
+
+#endif
 
 }  // namespace qdg

@@ -21,7 +21,9 @@
 // processing; kinachrichten, "Kompilierzeiten und gerätespezifisches Tuning")
 // map to: the grid/wave-to-unit mapping, Fmt::load, Fmt::compute, the MFMA
 // wrappers, and epilogue().
+#ifndef __HIPCC_RTC__
 #include <type_traits>
+#endif
 
 #include "qdg_device.h"
 #include "qdg_internal.h"
@@ -620,6 +622,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
   }
 }
 
+#ifndef __HIPCC_RTC__  // host launchers
 template <class F, int MT, int NT, int KW, int U>
 hipError_t launch_one(bool moe, const GemmArgs& a, int grid_m, hipStream_t s) {
   dim3 grid((a.ntiles + NT - 1) / NT, a.split, grid_m);
@@ -647,8 +650,10 @@ hipError_t dispatch_shape(const StreamCfg& c, bool moe, const GemmArgs& a, int g
   return hipErrorInvalidValue;
 }
 
+#endif
 }  // namespace
 
+#ifndef __HIPCC_RTC__  // host launchers
 bool stream_cfg_supported(Format, const StreamCfg& c) {
   if (c.kw != 4) return false;
   if (c.mt == 1) return c.nt == 1 || c.nt == 2 || c.nt == 4;
@@ -678,5 +683,7 @@ hipError_t launch_stream(Format f, bool asym, bool moe, const StreamCfg& c, cons
   }
   return hipErrorInvalidValue;
 }
+
+#endif
 
 }  // namespace qdg

@@ -209,3 +209,12 @@ def test_w8a16_layer_validation():
         assert "w8a16-int8" in d and "family=stream" in d
     bad = q.layer_w8a16(64, 256, otype=q.QDG_O_I32)
     assert _status(q.qdg_validate_layer, bad) == q.QDG_ERR_UNSUPPORTED
+
+
+def test_jit_validation_before_device_work():
+    p = q.qdg_plan_create(q.layer_w4a16(14336, 4096), q.dense())
+    # M = 16 runs weight streaming, M = 5000 the LDS-tiled family: not compiled at run time
+    assert _status(q.qdg_plan_jit, p, 16) == q.QDG_ERR_UNSUPPORTED
+    assert _status(q.qdg_plan_jit, p, 5000) == q.QDG_ERR_UNSUPPORTED
+    assert _status(q.qdg_plan_jit, p, 0) == q.QDG_ERR_INVALID_ARG
+    assert "code=aot" in q.qdg_plan_describe(p, 24)
