@@ -12,10 +12,11 @@ describes the kernel that dominates the step's time, `roofline_m16` the
 HBM-bound M=16 case (also as a fraction of `hbm_copy_gbs`, the box's measured
 device-to-device copy rate), `cases` every launch, `autotuned` each case
 again with a plan tuned per M range (qdg_plan_autotune) next to the
-heuristic plan; `cpu_baseline` times the fp64 CPU oracle over the same
-workload once.
+heuristic plan, `jit` the hipRTC compile time of one streaming-family
+instance and its kernel time next to the ahead-of-time instance;
+`cpu_baseline` times the fp64 CPU oracle over the same workload once.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-rows] [--no-autotune]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-rows] [--no-autotune] [--no-jit]
 """
 
 import argparse
@@ -230,6 +231,36 @@ def gpu_leg(args):
                 print(f"autotune M={m} K={k} N={n}: heuristic {us_h:.2f} us, autotuned {us_a:.2f} us",
                       file=sys.stderr, flush=True)
                 del ws_a
+    # run-time compilation: one streaming-family instance (M = 32 of the up
+    # projection) compiled with hipRTC into a fresh cache directory, then
+    # timed against the ahead-of-time instance (rotating weight copies)
+    jit = None
+    if args.jit:
+        import tempfile
+        k, n = SHAPES[0]
+        m = 32
+        layer, plan_h, bufs = layers[(k, n)]
+        plan_j = q.qdg_plan_create(layer, q.dense())
+        with tempfile.TemporaryDirectory() as cache:
+            info = q.qdg_plan_jit(plan_j, m, 0, cache)
+        a = synth.device_activations_bf16(m, k, seed=synth.seed_for(1, synth.TID_A, m))
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        wsb = q.qdg_plan_workspace(plan_h, m)
+        wsj = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+        def run_j(i, plan):
+            q.qdg_gemm(plan, a.data_ptr(), None, bufs[i % len(bufs)].data_ptr(), y.data_ptr(), m, wsj.data_ptr(),
+                       wsb, sh)
+        run_j(0, plan_h)
+        run_j(0, plan_j)
+        us_aot = _time_launches(lambda i: run_j(i, plan_h), 60, stream)
+        us_jit = _time_launches(lambda i: run_j(i, plan_j), 60, stream)
+        jit = dict(M=m, K=k, N=n, compile_ms=round(info.compile_ms, 1), load_ms=round(info.load_ms, 2),
+                   code_bytes=info.code_bytes, us_aot=round(us_aot, 3), us_jit=round(us_jit, 3),
+                   instance=q.qdg_plan_describe(plan_j, m).split(": ", 1)[1],
+                   note="the pages' figure for compiling one W4A16 kernel: 1.82 s with NVCC (H200 host); context only")
+        print(f"jit M={m} K={k} N={n}: compile {info.compile_ms:.0f} ms, aot {us_aot:.2f} us, jit {us_jit:.2f} us",
+              file=sys.stderr, flush=True)
     m16 = [d for d in out_cases if d["M"] == 16]
     roof16 = [dict(bound="hbm", achieved=d["gbs_stream"], peak=PEAK_HBM_GBS, unit="GB/s", frac=d["hbm_frac_stream"],
                    frac_of_copy=round(d["gbs_stream"] / copy_gbs, 4), kernel=f"w4a16 M=16 K={d['K']} N={d['N']}",
@@ -238,7 +269,7 @@ def gpu_leg(args):
               for d in m16]
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     return dict(value=value, ms_per_step=ms_per_step, roofline=roof, roofline_m16=roof16, cases=out_cases,
-                hbm_copy_gbs=round(copy_gbs, 1), autotuned=autotuned)
+                hbm_copy_gbs=round(copy_gbs, 1), autotuned=autotuned, jit=jit)
 
 
 PEAK_INT8_TOPS = 5000.0
@@ -551,6 +582,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-rows", action="store_true", help="skip the W8A8 / W4A8 / MXFP4 / MoE rows")
+    ap.add_argument("--no-jit", dest="jit", action="store_false",
+                    help="skip the run-time compilation measurement")
     ap.add_argument("--no-autotune", dest="autotune", action="store_false",
                     help="skip the autotuned-plan comparison of the dense sweep")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -575,6 +608,8 @@ def main():
     }
     if g["autotuned"]:
         line["autotuned"] = g["autotuned"]
+    if g["jit"]:
+        line["jit"] = g["jit"]
     if not args.no_rows:
         line["rows"] = rows_leg()
     if not args.no_cpu:
