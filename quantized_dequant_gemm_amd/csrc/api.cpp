@@ -748,9 +748,11 @@ static void autotune_candidates(const qdg_plan& P, int64_t M, qdg_tuning_config*
   if (M <= 256) {  // streaming: the smallest row block that holds M, and larger ones
     for (int bm = M <= 16 ? 16 : M <= 32 ? 32 : 64; bm <= 64; bm *= 2)
       for (int bn : {16, 32, 64}) add(bm, bn, 0, 4);
+    if (M <= 64)
+      for (int bn : {16, 32, 64}) add(M <= 16 ? 16 : M <= 32 ? 32 : 64, bn, 1, 4);  // unsplit
   }
-  if (M > 16) {  // LDS-tiled
-    add(128, 256, 0, 8);
+  if (M > 16) {  // LDS-tiled, with the K-split heuristic and fixed splits
+    for (int s : {0, 1, 2, 4, 8}) add(128, 256, s, 8);
     if (P.fmt == FMT_W4A16) {
       add(128, 256, 0, 4);
       if (M > 128) add(256, 128, 0, 8);
@@ -769,7 +771,7 @@ qdg_status qdg_plan_autotune(qdg_plan* plan, const void* A, const float* a_scale
   if (M < 1 || M > 0x7FFFFFFF / 2) return fail(QDG_ERR_INVALID_ARG, "M must be in [1, 2^30)");
   if (reps < 1 || reps > 1000) return fail(QDG_ERR_INVALID_ARG, "reps must be in [1, 1000]");
   if (!A || !packed || !Y || !workspace) return fail(QDG_ERR_INVALID_ARG, "NULL A, packed, Y or workspace");
-  constexpr int kCap = 32;
+  constexpr int kCap = 48;
   qdg_tuning_config cand[kCap];
   int ncand = 0;
   autotune_candidates(*plan, M, cand, &ncand, kCap);
