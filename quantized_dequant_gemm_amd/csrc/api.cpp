@@ -284,8 +284,16 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   const bool a8_fits = (double)(M > 0 ? M : 1) * (double)g.k < 4294967296.0;
   const int64_t q_tiles = ((M + 127) / 128) * ((g.ntiles + 15) / 16);
   // (measured on MI355X: from M = 64 the tiled family with K split into one
-  // pass of 256 workgroups beats the streaming family at these layer sizes)
-  const bool q_enough = (has_tuning && T.block_m >= 128) || M >= 64;
+  // pass of 256 workgroups beats the streaming family at these layer sizes,
+  // except where the streaming family's cheaper unit still wins up to 128
+  // rows: fp4 x fp4 always, and int8 x int8 while the streaming grid of
+  // 64 x 32 blocks is small enough to need a K split of its own)
+  bool stream_mid = false;
+  if (!has_tuning && M <= 128) {
+    const int64_t stream_wgs = ((g.ntiles + 1) / 2) * ((M + 63) / 64);
+    stream_mid = P.fmt == FMT_W4A4 || (P.fmt == FMT_W8A8 && 2 * stream_wgs <= kTargetWorkgroups);
+  }
+  const bool q_enough = (has_tuning && T.block_m >= 128) || (M >= 64 && !stream_mid);
   if (bm >= 128 && P.fmt != FMT_W4A16 && P.fmt != FMT_W8A16 && !moe && a8_fits && q_enough) {
     ch.tile = true;
     ch.qtile = true;

@@ -97,6 +97,16 @@ def test_describe_reports_the_instance_that_runs():
     assert "family=tile" in q.qdg_plan_describe(p, 33)
     assert "family=stream" in q.qdg_plan_describe(p8, 63)
     assert "family=qtile" in q.qdg_plan_describe(p8, 64)
+    # ... but up to 128 rows the streaming family keeps fp4 x fp4 layers and
+    # int8 x int8 layers whose streaming grid is small enough to be split
+    narrow8 = q.qdg_plan_create(q.layer_w8a8(4096, 4096), q.dense())
+    assert "family=stream" in q.qdg_plan_describe(narrow8, 128)
+    assert "family=qtile" in q.qdg_plan_describe(narrow8, 129)
+    w4a8 = q.qdg_plan_create(q.layer_w4a8(4096, 4096), q.dense())
+    assert "family=qtile" in q.qdg_plan_describe(w4a8, 64)
+    w4a4 = q.qdg_plan_create(q.layer_w4a4(2048, 7168), q.dense())
+    assert "family=stream" in q.qdg_plan_describe(w4a4, 128)
+    assert "family=qtile" in q.qdg_plan_describe(w4a4, 129)
     # batch-invariant plans never switch family with M
     pb = q.qdg_plan_create(q.layer_w4a16(14336, 4096), q.dense(batch_invariant=1))
     assert "family=stream" in q.qdg_plan_describe(pb, 100)
@@ -194,7 +204,7 @@ def test_w4a4_layer_validation():
     p = q.qdg_plan_create(q.layer_w4a4(64, 256), q.dense())
     for m in (1, 16, 200, 5000):
         d = q.qdg_plan_describe(p, m)
-        assert "w4a4-mxfp4" in d and ("family=stream" if m < 64 else "family=qtile") in d and "f4f4" in d
+        assert "w4a4-mxfp4" in d and ("family=stream" if m <= 128 else "family=qtile") in d and "f4f4" in d
     pm = q.qdg_plan_create(q.layer_w4a4(64, 256, num_experts=4), q.moe(2))
     assert "family=stream" in q.qdg_moe_describe(pm, 8, 16)
     # the scales are required

@@ -57,7 +57,7 @@ def _w4a4_case(m, n, k, otype, salt):
 def test_w4a4_gemm(qdg, m, n, k, otype):
     layer, pk, qa, sa, y64 = _w4a4_case(m, n, k, otype, salt=m + n)
     plan = q.qdg_plan_create(layer, q.dense())
-    fam = "family=qtile" if m >= 64 else "family=stream"  # fp4 x fp4 LDS-tiled family from M = 64
+    fam = "family=qtile" if m > 128 else "family=stream"  # fp4 x fp4 LDS-tiled family above 128 rows
     assert "w4a4-mxfp4" in q.qdg_plan_describe(plan, m) and fam in q.qdg_plan_describe(plan, m)
     y, _ = H.gemm(layer, pk, qa, m, a_scales=sa)
     assert not torch.isnan(y.float()).any()
