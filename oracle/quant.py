@@ -30,6 +30,15 @@ representation (jetabc, section on what quantization is; kinachrichten,
 * A row or group whose ``amax`` is zero gets scale 1.0 and all-zero codes.
 * Activations, MXFP4 (W4A4): the MXFP4 rule above applied to each row's
   blocks of 32 consecutive K (the bf16 values are exact in binary32).
+* NVFP4 (named beside INT4 as a 4-bit format with its own number format and
+  scaling: kinachrichten, "Warum quantisierte Kernel wichtig sind"; the
+  pages give no recipe, so the public NVFP4 definition is taken): E2M1
+  elements, one E4M3 scale per 16 consecutive K, one binary32 scale per
+  tensor. ``ts = f32(amax_tensor / 2688)`` (2688 = 6 * 448, the largest E2M1
+  times the largest E4M3), 1.0 for an all-zero tensor;
+  ``sb = e4m3_rne(min(f32(f32(amax_block / 6) / ts), 448))``;
+  ``q = e2m1_rne_sat(f32(w / f32(e4m3(sb) * ts)))``, all-zero codes where the
+  block scale is zero.
 """
 
 import numpy as np
@@ -166,3 +175,23 @@ def quantize_act_fp8(a_bf16_bits, group=128):
     codes = np.where(nz[:, :, None], codes, 0).astype(np.uint8)
     sa = np.where(nz, (amax / F32(448.0)).astype(F32), F32(1.0)).astype(F32)
     return codes.reshape(m, k), sa
+
+
+def quantize_nvfp4(w, block=16):
+    """w f32 [N, K] -> (E2M1 codes u8 [N,K], E4M3 scale codes u8 [N, K/16],
+    tensor scale f32)."""
+    w = np.asarray(w, dtype=F32)
+    amax_t = F32(np.max(np.abs(w))) if w.size else F32(0.0)
+    ts = (amax_t / F32(2688.0)).astype(F32) if amax_t > 0 else F32(1.0)
+    if ts == 0:  # a tensor amax below 2688 * (smallest subnormal)
+        ts = F32(1.0)
+    wb = _grouped(w, block)
+    amax = np.max(np.abs(wb), axis=2).astype(F32)
+    r = ((amax / F32(6.0)).astype(F32) / ts).astype(F32)
+    sb = codecs.encode_e4m3_rne(np.minimum(r.astype(np.float64), 448.0))
+    den = (codecs.decode_e4m3(sb).astype(F32) * ts).astype(F32)
+    nz = den > 0
+    scaled = (wb / np.where(nz, den, F32(1.0))[:, :, None]).astype(F32)
+    codes = codecs.encode_e2m1_rne_sat(scaled)
+    codes = np.where(nz[:, :, None], codes, 0).astype(np.uint8)
+    return codes.reshape(w.shape), sb, F32(ts)

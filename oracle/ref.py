@@ -54,6 +54,19 @@ def dequant_mxfp4(codes, e8m0, block=32):
     return (v.reshape(n, k // block, block) * s[:, :, None]).reshape(n, k)
 
 
+def dequant_nvfp4(codes, e4m3, tensor_scale, block=16):
+    """E2M1 codes [N,K], E4M3 scale codes [N,K/16] and the binary32 tensor
+    scale -> W64 = e2m1(q) * e4m3(s) * ts (NVFP4: a 4-bit floating format
+    the pages name beside INT4, kinachrichten, "Warum quantisierte Kernel
+    wichtig sind")."""
+    sc = codecs.decode_e4m3(e4m3)
+    assert not np.any(np.isnan(sc)), "E4M3 NaN codes are not valid scales"
+    v = codecs.decode_e2m1(codes)
+    n, k = v.shape
+    w = v.reshape(n, k // block, block) * sc[:, :, None] * float(np.float32(tensor_scale))
+    return w.reshape(n, k)
+
+
 # ---------------------------------------------------------------- GEMMs
 
 
@@ -131,6 +144,12 @@ def gemm_w4a4(a_codes, a_e8m0, w_codes, w_e8m0):
     a = dequant_mxfp4(a_codes, a_e8m0)
     w = dequant_mxfp4(w_codes, w_e8m0)
     return a @ w.T
+
+
+def gemm_nvfp4a16(a_bf16_bits, codes, e4m3, tensor_scale):
+    """bf16 activations times NVFP4 weights: ``Y = A @ W64.T`` with the
+    weights dequantized in float64."""
+    return codecs.bf16_bits_to_f64(a_bf16_bits) @ dequant_nvfp4(codes, e4m3, tensor_scale).T
 
 
 def dequant_act_int8(qa, sa):
