@@ -63,9 +63,11 @@ typedef enum qdg_status {
 enum { QDG_W_INT4 = 0,  /* two's-complement 4-bit, symmetric (no zeros) */
        QDG_W_UINT4 = 1, /* unsigned 4-bit with uint8 zero points (asymmetric) */
        QDG_W_INT8 = 2,  /* int8, symmetric, one fp32 scale per output channel */
-       QDG_W_MXFP4 = 3  /* OCP MX FP4 E2M1 with E8M0 scale per 32 along K */ };
+       QDG_W_MXFP4 = 3, /* OCP MX FP4 E2M1 with E8M0 scale per 32 along K */
+       QDG_W_NVFP4 = 4  /* E2M1 with an E4M3 scale per 16 along K and one
+                           binary32 scale per tensor (expert) */ };
 /* Scale storage types. */
-enum { QDG_S_F16 = 0, QDG_S_F32 = 1, QDG_S_E8M0 = 2 };
+enum { QDG_S_F16 = 0, QDG_S_F32 = 1, QDG_S_E8M0 = 2, QDG_S_E4M3 = 3 };
 /* Activation types. MXFP4 activations (W4A4): E2M1 codes u8 [M][k/2], two
    per byte with the even k in the low nibble, and E8M0 scale codes u8
    [M][k/32]; the qdg_gemm / qdg_moe_gemm a_scales pointer then carries the
@@ -93,6 +95,14 @@ enum { QDG_KIND_DENSE = 0, QDG_KIND_MOE = 1 };
                 quantisierte Kernel wichtig sind"; served by the streaming
                 family with fp4 x fp4 scaled MFMAs, both E8M0 scales applied
                 by the hardware)
+     W4A16-NVFP4 wtype NVFP4, stype E4M3, group_size 16, atype BF16,
+                act_group 0, otype BF16 or F32 (the pages name NVFP4 beside
+                INT4 as a 4-bit format with its own number format and
+                scaling: kinachrichten, "Warum quantisierte Kernel wichtig
+                sind"; served by the streaming family: each E2M1 value times
+                its E4M3 block scale is exact in bf16, so the weights enter
+                the bf16 MFMA already scaled and the tensor scale is applied
+                to the fp32 result)
    Shapes: k a positive multiple of 128; n >= 1 (padded internally to a
    multiple of 16); num_experts >= 1 (1 for a dense layer). arch = 950. */
 typedef struct qdg_layer_config {
@@ -143,13 +153,18 @@ typedef struct qdg_tuning_config {
      F16 scales                    f16 [E][n][k/group_size]
      F32 scales (INT8)             f32 [E][n]
      E8M0 scales (MXFP4)           u8 [E][n][k/32], value 2^(e-127); 255 invalid
+     E4M3 scales (NVFP4)           u8 [E][n][k/16], OCP E4M3 codes; the NaN
+                                   codes 0x7F / 0xFF are invalid
      zeros (UINT4 only)            u8 [E][n][k/group_size], values 0..15
+     tensor_scale (NVFP4 only)     f32 [E], one scale per expert
    Dequantized weight: w = (q - z) * s, z = 0 when symmetric; MXFP4:
-   w = e2m1(q) * 2^(e-127). */
+   w = e2m1(q) * 2^(e-127); NVFP4: w = e2m1(q) * e4m3(s) * tensor_scale.
+   Pointers a format does not use may be NULL. */
 typedef struct qdg_std_weights {
   const void* qweight;
   const void* scales;
   const void* zeros;
+  const void* tensor_scale;
 } qdg_std_weights;
 
 typedef struct qdg_plan qdg_plan;
@@ -172,8 +187,9 @@ qdg_status qdg_preprocess_query(const qdg_layer_config* layer, size_t* packed_by
    weights into the gfx950 MFMA fragment layout of the target kernels.
    `packed` (>= qdg_preprocess_query bytes, 256-byte aligned) is written
    entirely; the standard-format buffers are only read. MXFP4 scale code 255
-   is not checked on the device: preprocess maps it to the largest finite
-   scale, so callers validate E8M0 input on the host when it is untrusted. */
+   and the NVFP4 E4M3 NaN codes are not checked on the device: preprocess
+   maps them to the largest finite scale of their sign, so callers validate
+   scale input on the host when it is untrusted. */
 qdg_status qdg_preprocess(const qdg_layer_config* layer, const qdg_std_weights* weights,
                           void* packed, size_t packed_bytes, void* stream);
 
@@ -186,7 +202,8 @@ qdg_status qdg_preprocess(const qdg_layer_config* layer, const qdg_std_weights* 
      INT8  s = f32(amax/127), q = clamp(rne(w/s), -127, 127), per row
      MXFP4 X = floor(log2(amax)) - 2 per 32, e = X + 127, q = e2m1_rne_sat(w/2^X)
    A scale that is zero is stored as 1.0 (all-zero group). `zeros` is used
-   for UINT4 only. */
+   for UINT4 only. NVFP4 is not produced here (QDG_ERR_UNSUPPORTED): its
+   tensor scale depends on the whole tensor. */
 qdg_status qdg_quantize_weights(const qdg_layer_config* layer, const float* w,
                                 void* qweight, void* scales, void* zeros, void* stream);
 

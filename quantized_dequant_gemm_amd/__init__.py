@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(HERE, "libqdg.so")
 
 # enums (mirror include/qdg.h)
 QDG_OK, QDG_ERR_INVALID_ARG, QDG_ERR_UNSUPPORTED, QDG_ERR_MISALIGNED, QDG_ERR_WORKSPACE, QDG_ERR_HIP = range(6)
-QDG_W_INT4, QDG_W_UINT4, QDG_W_INT8, QDG_W_MXFP4 = range(4)
-QDG_S_F16, QDG_S_F32, QDG_S_E8M0 = range(3)
+QDG_W_INT4, QDG_W_UINT4, QDG_W_INT8, QDG_W_MXFP4, QDG_W_NVFP4 = range(5)
+QDG_S_F16, QDG_S_F32, QDG_S_E8M0, QDG_S_E4M3 = range(4)
 QDG_A_BF16, QDG_A_INT8, QDG_A_FP8E4M3, QDG_A_MXFP4 = range(4)
 QDG_O_BF16, QDG_O_F32, QDG_O_I32 = range(3)
 QDG_KIND_DENSE, QDG_KIND_MOE = range(2)
@@ -58,7 +58,8 @@ class TuningConfig(ctypes.Structure):
 
 
 class StdWeights(ctypes.Structure):
-    _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p)]
+    _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p)]
 
 
 class QdgError(RuntimeError):
@@ -280,6 +281,13 @@ def layer_mxfp4(n, k, otype=QDG_O_BF16, num_experts=1):
 def layer_w8a16(n, k, otype=QDG_O_BF16, num_experts=1):
     """int8 weights with fp32 per-channel scales, bf16 activations."""
     return LayerConfig(n=n, k=k, num_experts=num_experts, wtype=QDG_W_INT8, stype=QDG_S_F32, group_size=0,
+                       has_zeros=0, atype=QDG_A_BF16, act_group=0, otype=otype, arch=950)
+
+
+def layer_nvfp4(n, k, otype=QDG_O_BF16, num_experts=1):
+    """NVFP4 weights (E2M1, E4M3 scale per 16 K, fp32 scale per tensor) with
+    bf16 activations."""
+    return LayerConfig(n=n, k=k, num_experts=num_experts, wtype=QDG_W_NVFP4, stype=QDG_S_E4M3, group_size=16,
                        has_zeros=0, atype=QDG_A_BF16, act_group=0, otype=otype, arch=950)
 
 

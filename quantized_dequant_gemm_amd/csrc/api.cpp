@@ -59,6 +59,7 @@ namespace qdg {
 Format format_of(const qdg_layer_config& L) {
   if (L.wtype == QDG_W_INT8) return L.atype == QDG_A_BF16 ? FMT_W8A16 : FMT_W8A8;
   if (L.wtype == QDG_W_MXFP4) return L.atype == QDG_A_MXFP4 ? FMT_W4A4 : FMT_MXFP4;
+  if (L.wtype == QDG_W_NVFP4) return FMT_NVFP4;
   if (L.atype == QDG_A_INT8) return FMT_W4A8;
   return FMT_W4A16;
 }
@@ -80,6 +81,7 @@ PackedGeom packed_geom(const qdg_layer_config& L, Format f) {
     case FMT_W4A4: g.s_bytes = units * 64; break;       // E8M0 per lane
     case FMT_W8A8:
     case FMT_W8A16: g.s_bytes = g.n_pad * 4; break;     // f32 per column
+    case FMT_NVFP4: g.s_bytes = 256 + units * 128; break;  // f32 tensor scale, then 2 E4M3 per lane
   }
   g.s_offset = align_up(g.w_bytes, 256);
   g.expert_stride = align_up(g.s_offset + g.s_bytes, 256);
@@ -125,6 +127,7 @@ const char* fmt_name(Format f, const qdg_layer_config& L) {
     case FMT_W4A8: return "w4a8-int8";
     case FMT_MXFP4: return "w4a8-mxfp4-fp8";
     case FMT_W4A4: return "w4a4-mxfp4";
+    case FMT_NVFP4: return "w4a16-nvfp4";
   }
   return "?";
 }
@@ -182,6 +185,14 @@ qdg_status validate_layer(const qdg_layer_config* L) {
         return fail(QDG_ERR_UNSUPPORTED,
                     "MXFP4 weights run with fp8 E4M3 activations (128-group scales) or MXFP4 activations (32-blocks)");
       if (L->otype == QDG_O_I32) return fail(QDG_ERR_UNSUPPORTED, "MXFP4 has no integer accumulator");
+      return ok();
+    case QDG_W_NVFP4:
+      if (L->stype != QDG_S_E4M3 || L->group_size != 16)
+        return fail(QDG_ERR_UNSUPPORTED, "NVFP4 needs E4M3 scales over blocks of 16");
+      if (L->has_zeros) return fail(QDG_ERR_UNSUPPORTED, "NVFP4 has no zero points");
+      if (L->atype != QDG_A_BF16 || L->act_group != 0)
+        return fail(QDG_ERR_UNSUPPORTED, "NVFP4 weights run with bf16 activations");
+      if (L->otype == QDG_O_I32) return fail(QDG_ERR_UNSUPPORTED, "NVFP4 has no integer accumulator");
       return ok();
     default:
       return fail(QDG_ERR_INVALID_ARG, "bad wtype %d", L->wtype);
@@ -259,7 +270,8 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   }
   // weight-streaming family of the int8 / fp8 formats (dense M <= 16): the
   // K range of a workgroup must fit its LDS; raw int32 output is not split
-  if (bm == 16 && P.fmt != FMT_W4A16 && P.fmt != FMT_W4A4 && P.fmt != FMT_W8A16 && !moe && !P.compute.batch_invariant &&
+  if (bm == 16 && P.fmt != FMT_W4A16 && P.fmt != FMT_W4A4 && P.fmt != FMT_W8A16 && P.fmt != FMT_NVFP4 && !moe &&
+      !P.compute.batch_invariant &&
       ws_tuning_ok) {
     // 4 N tiles per workgroup when that gives enough workgroups, else one
     // tile with all 8 waves on its K range (no split across workgroups)
@@ -294,7 +306,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
     stream_mid = P.fmt == FMT_W4A4 || (P.fmt == FMT_W8A8 && 2 * stream_wgs <= kTargetWorkgroups);
   }
   const bool q_enough = (has_tuning && T.block_m >= 128) || (M >= 64 && !stream_mid);
-  if (bm >= 128 && P.fmt != FMT_W4A16 && P.fmt != FMT_W8A16 && !moe && a8_fits && q_enough) {
+  if (bm >= 128 && P.fmt != FMT_W4A16 && P.fmt != FMT_W8A16 && P.fmt != FMT_NVFP4 && !moe && a8_fits && q_enough) {
     ch.tile = true;
     ch.qtile = true;
     ch.tc = TileCfg{128, 256, 8};
@@ -416,6 +428,8 @@ qdg_status qdg_preprocess(const qdg_layer_config* layer, const qdg_std_weights* 
   if (st != QDG_OK) return st;
   if (!w || !w->qweight || !w->scales || !packed) return fail(QDG_ERR_INVALID_ARG, "NULL weight or packed pointer");
   if (layer->wtype == QDG_W_UINT4 && !w->zeros) return fail(QDG_ERR_INVALID_ARG, "UINT4 weights need zero points");
+  if (layer->wtype == QDG_W_NVFP4 && (!w->tensor_scale || !aligned(w->tensor_scale, 4)))
+    return fail(QDG_ERR_INVALID_ARG, "NVFP4 weights need 4-byte aligned per-tensor scales");
   const Format f = format_of(*layer);
   const PackedGeom g = packed_geom(*layer, f);
   if (packed_bytes < (size_t)(g.expert_stride * g.experts))
@@ -433,6 +447,8 @@ qdg_status qdg_quantize_weights(const qdg_layer_config* layer, const float* w, v
   if (st != QDG_OK) return st;
   if (!w || !qweight || !scales) return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
   if (layer->wtype == QDG_W_UINT4 && !zeros) return fail(QDG_ERR_INVALID_ARG, "UINT4 needs a zeros buffer");
+  if (layer->wtype == QDG_W_NVFP4)
+    return fail(QDG_ERR_UNSUPPORTED, "NVFP4 weights are not produced here (the tensor scale needs the whole tensor)");
   return hip_status(launch_quantize_weights(*layer, w, qweight, scales, zeros, (hipStream_t)stream),
                     "quantize_weights launch");
 }
@@ -578,7 +594,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
 // The MFMA instruction an instance issues.
 static const char* mfma_name(Format f, const Choice& c) {
   if (f == FMT_W4A16) return c.tile && c.tc.bm * c.tc.bn / (64 * c.tc.waves) == 64 ? "32x32x16_bf16" : "16x16x32_bf16";
-  if (f == FMT_W8A16) return "16x16x32_bf16";
+  if (f == FMT_W8A16 || f == FMT_NVFP4) return "16x16x32_bf16";
   if (f == FMT_MXFP4) return "scale_16x16x128_f8f6f4";
   if (f == FMT_W4A4) return "scale_16x16x128_f4f4";
   return "16x16x64_i8";
@@ -691,7 +707,7 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   } else {
     // the streaming family addresses A with 31-bit byte offsets
     const int64_t a_rows = moe ? (a_per_pair ? rows : T) : M;
-    const bool bf16_a = plan->fmt == FMT_W4A16 || plan->fmt == FMT_W8A16;
+    const bool bf16_a = plan->fmt == FMT_W4A16 || plan->fmt == FMT_W8A16 || plan->fmt == FMT_NVFP4;
     a.a_bytes = a_rows * (bf16_a ? 2 * (int64_t)a.K : plan->fmt == FMT_W4A4 ? a.K / 2 : a.K);
     if (a.a_bytes >= ((int64_t)1 << 31))
       return fail(QDG_ERR_UNSUPPORTED, "A of %lld bytes is too large for the streaming family (< 2 GiB)",
@@ -717,7 +733,8 @@ qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, 
   if (M == 0) return ok();
   if (M > 0x7FFFFFFF / 2) return fail(QDG_ERR_UNSUPPORTED, "M too large");
   if (!A || !packed || !Y) return fail(QDG_ERR_INVALID_ARG, "NULL A, packed or Y");
-  const bool need_scales = plan->fmt != FMT_W4A16 && plan->fmt != FMT_W8A16 && plan->layer.otype != QDG_O_I32;
+  const bool need_scales = plan->fmt != FMT_W4A16 && plan->fmt != FMT_W8A16 && plan->fmt != FMT_NVFP4 &&
+                           plan->layer.otype != QDG_O_I32;
   if (plan->fmt == FMT_MXFP4 || plan->fmt == FMT_W4A4) {
     if (!a_scales) return fail(QDG_ERR_INVALID_ARG, "MXFP4 needs activation scales");
   } else if (need_scales && !a_scales) {
@@ -935,7 +952,7 @@ qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scal
   if (T * plan->compute.top_k > (1 << 20)) return fail(QDG_ERR_UNSUPPORTED, "T*top_k above 2^20");
   if (!A || !packed || !Y || !sorted_ids || !block_expert || !num_padded)
     return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
-  if (plan->fmt != FMT_W4A16 && plan->fmt != FMT_W8A16 &&
+  if (plan->fmt != FMT_W4A16 && plan->fmt != FMT_W8A16 && plan->fmt != FMT_NVFP4 &&
       (plan->fmt == FMT_MXFP4 || plan->fmt == FMT_W4A4 || plan->layer.otype != QDG_O_I32) && !a_scales)
     return fail(QDG_ERR_INVALID_ARG, "activation scales are NULL");
   if (!aligned(A, 16)) return fail(QDG_ERR_MISALIGNED, "A must be 16-byte aligned");

@@ -31,7 +31,7 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 // column `lane`.
 __global__ void repack_kernel(int fmt, int wtype, const uint8_t* __restrict__ qw,
                               const void* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                              uint8_t* __restrict__ packed, int64_t N, int64_t K, int64_t ntiles,
+                              const float* __restrict__ tscale, uint8_t* __restrict__ packed, int64_t N, int64_t K, int64_t ntiles,
                               int64_t groups, int64_t expert_stride, int64_t s_offset, int64_t experts) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_expert = ntiles * groups * 64;
@@ -94,6 +94,23 @@ __global__ void repack_kernel(int fmt, int wtype, const uint8_t* __restrict__ qw
       if (sc == 255) sc = 254;
     }
     sdst[unit * 64 + lane] = sc;
+  } else if (fmt == FMT_NVFP4) {
+    // codes as for MXFP4; the record of a lane holds the E4M3 codes of its
+    // two 16-blocks (8g + 2c, 8g + 2c + 1); the NaN codes become +-448. The
+    // expert's tensor scale leads its scale region.
+    u32x4_t out = {0, 0, 0, 0};
+    if (valid) out = *(const u32x4_t*)(qw + (e * N + n) * (K / 2) + (g * 128 + 32 * c) / 2);
+    *((u32x4_t*)(wdst + unit * kUnit4Bytes) + lane) = out;
+    uint32_t rec = 0;
+    if (valid) {
+      const uint8_t* sc = (const uint8_t*)scales + (e * N + n) * (K / 16) + 8 * g + 2 * c;
+      uint32_t s0 = sc[0], s1 = sc[1];
+      if ((s0 & 0x7Fu) == 0x7Fu) s0 -= 1;
+      if ((s1 & 0x7Fu) == 0x7Fu) s1 -= 1;
+      rec = s0 | (s1 << 8);
+    }
+    ((uint16_t*)(sdst + 256))[unit * 64 + lane] = (uint16_t)rec;
+    if (unit == 0 && lane == 0) *(float*)sdst = tscale[e];
   } else {  // FMT_W8A8: unit = [step j][lane][16 bytes]
     for (int j = 0; j < 2; ++j) {
       u32x4_t out = {0, 0, 0, 0};
@@ -206,7 +223,8 @@ hipError_t launch_preprocess(const qdg_layer_config& L, Format f, const PackedGe
   const int bs = 256;
   const int64_t blocks = (threads + bs - 1) / bs;
   hipLaunchKernelGGL(repack_kernel, dim3((unsigned)blocks), dim3(bs), 0, s, (int)f, (int)L.wtype,
-                     (const uint8_t*)w.qweight, w.scales, (const uint8_t*)w.zeros, (uint8_t*)packed, g.n,
+                     (const uint8_t*)w.qweight, w.scales, (const uint8_t*)w.zeros, (const float*)w.tensor_scale,
+                     (uint8_t*)packed, g.n,
                      g.k, g.ntiles, g.groups, g.expert_stride, g.s_offset, g.experts);
   return hipGetLastError();
 }

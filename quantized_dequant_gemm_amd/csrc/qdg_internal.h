@@ -12,7 +12,7 @@
 
 namespace qdg {
 
-enum Format { FMT_W4A16 = 0, FMT_W8A8 = 1, FMT_W4A8 = 2, FMT_MXFP4 = 3, FMT_W4A4 = 4, FMT_W8A16 = 5 };
+enum Format { FMT_W4A16 = 0, FMT_W8A8 = 1, FMT_W4A8 = 2, FMT_MXFP4 = 3, FMT_W4A4 = 4, FMT_W8A16 = 5, FMT_NVFP4 = 6 };
 
 // Geometry of the packed buffer of one layer.
 struct PackedGeom {

@@ -369,6 +369,75 @@ struct FmtW8A16 {
   }
 };
 
+// W4A16-NVFP4: bf16 activations, E2M1 weights with an E4M3 scale per 16 K
+// and one binary32 scale per tensor. An E2M1 value (at most 2 significant
+// bits) times an E4M3 scale (at most 4 significant bits, exponents -9..8) is
+// exact in bf16, so each weight is converted to fp32 by the hardware,
+// multiplied by its block scale in fp32 (exact) and packed to bf16 (exact:
+// the dropped half is zero). The MFMA then accumulates already-scaled
+// products over the whole K range; the tensor scale multiplies the fp32
+// result once. The weight unit is the MXFP4 one (lane group c holds K
+// 32c..32c+31 of its column, dword j = K 32c+8j..+7, so steps 0-1 use the
+// 16-block 2c and steps 2-3 the block 2c+1) and the A fragments are the
+// W4A16 ones (the same K values per lane and step).
+struct FmtNvfp4 {
+  using Acc = f32x4_t;
+  static constexpr bool kIntAcc = false;
+  template <int MT, int NT>
+  struct Frag {
+    u32x4_t a[MT][4];
+    u32x4_t b[NT];
+    uint32_t sc[NT];
+  };
+  static constexpr int kRecOffset = 256;  // the tensor scale comes first
+  template <int MT, int NT>
+  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t o = x.aoff[mt] + (uint32_t)(g * 256 + 64 * x.c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.a[mt][j] = lda(x.arsrc, o + 16 * j);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const size_t u = (size_t)x.tile[t] * x.groups + g;
+      f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
+      f.sc[t] = ((const uint16_t*)(x.sbase + kRecOffset))[u * 64 + x.lane];
+    }
+  }
+  // OCP E4M3 code -> its exact fp32 value (the NaN codes never reach here)
+  __device__ static float e4m3(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float mag = e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (b & 0x80u) ? -mag : mag;
+  }
+  // two E2M1 codes (byte SEL of d) times s -> a bf16 pair (even k low)
+  template <int SEL>
+  __device__ static uint32_t pair(uint32_t d, float s) {
+    const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, SEL);
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, v.y * s), __builtin_bit_cast(uint32_t, v.x * s),
+                                 0x07060302u);
+  }
+  template <int MT, int NT>
+  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT], uint32_t, uint32_t) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float s0 = e4m3(f.sc[t] & 0xFFu), s1 = e4m3((f.sc[t] >> 8) & 0xFFu);
+      u32x4_t bw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t d = f.b[t][j];
+        const float s = j < 2 ? s0 : s1;
+        bw[j] = u32x4_t{pair<0>(d, s), pair<1>(d, s), pair<2>(d, s), pair<3>(d, s)};
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mt][t] = mfma_bf16(f.a[mt][j], bw[j], acc[mt][t]);
+    }
+  }
+};
+
 // ----------------------------------------------------------------- kernel
 
 template <class F, int MT, int NT, int KW, int U, bool MOE>
@@ -416,7 +485,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
   x.wbase = p.packed + (size_t)expert * p.expert_stride;
   x.sbase = x.wbase + p.s_offset;
   constexpr bool kBf16A = std::is_same<F, FmtW4A16<false>>::value || std::is_same<F, FmtW4A16<true>>::value ||
-                          std::is_same<F, FmtW8A16>::value;
+                          std::is_same<F, FmtW8A16>::value || std::is_same<F, FmtNvfp4>::value;
   constexpr bool kFp4A = std::is_same<F, FmtW4A4>::value;
   const size_t a_row_bytes = kBf16A ? (size_t)p.K * 2 : kFp4A ? (size_t)p.K / 2 : (size_t)p.K;
 #pragma unroll
@@ -586,6 +655,8 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
           y = (float)acc[mt][t][i] * p.a_scales[arow] * sw;
         } else if constexpr (std::is_same<F, FmtW8A16>::value) {
           y = acc[mt][t][i] * ((const float*)x.sbase)[n];  // per-channel scale
+        } else if constexpr (std::is_same<F, FmtNvfp4>::value) {
+          y = acc[mt][t][i] * ((const float*)x.sbase)[0];  // tensor scale
         } else if constexpr (std::is_same<F, FmtInt8<true, false>>::value) {
           y = acc[mt][t][i] * p.a_scales[arow];
         } else if constexpr (F::kIntAcc) {
@@ -680,6 +751,8 @@ hipError_t launch_stream(Format f, bool asym, bool moe, const StreamCfg& c, cons
       return dispatch_shape<FmtW4A4>(c, moe, a, grid_m, s);
     case FMT_W8A16:
       return dispatch_shape<FmtW8A16>(c, moe, a, grid_m, s);
+    case FMT_NVFP4:
+      return dispatch_shape<FmtNvfp4>(c, moe, a, grid_m, s);
   }
   return hipErrorInvalidValue;
 }

@@ -42,13 +42,14 @@ def out_tensor(m, n, otype):
 class Packed:
     """A layer in the kernel layout (keeps its device buffers alive)."""
 
-    def __init__(self, layer, qweight, scales, zeros=None):
+    def __init__(self, layer, qweight, scales, zeros=None, tensor_scale=None):
         self.layer = layer
-        self.std = (qweight, scales, zeros)
+        self.std = (qweight, scales, zeros, tensor_scale)
         self.nbytes = q.qdg_preprocess_query(layer)
         self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device="cuda")
         w = q.StdWeights(qweight=qweight.data_ptr(), scales=scales.data_ptr(),
-                         zeros=zeros.data_ptr() if zeros is not None else None)
+                         zeros=zeros.data_ptr() if zeros is not None else None,
+                         tensor_scale=tensor_scale.data_ptr() if tensor_scale is not None else None)
         q.qdg_preprocess(layer, w, self.buf.data_ptr(), self.nbytes, q.current_stream())
 
 

@@ -228,3 +228,30 @@ def test_jit_validation_before_device_work():
     assert _status(q.qdg_plan_jit, p, 5000) == q.QDG_ERR_UNSUPPORTED
     assert _status(q.qdg_plan_jit, p, 0) == q.QDG_ERR_INVALID_ARG
     assert "code=aot" in q.qdg_plan_describe(p, 24)
+
+
+def test_nvfp4_layer_validation():
+    # NVFP4 weights: E4M3 scales per 16, bf16 activations, no zeros, float output
+    q.qdg_validate_layer(q.layer_nvfp4(64, 256))
+    for field, value in (("group_size", 32), ("stype", q.QDG_S_E8M0), ("atype", q.QDG_A_INT8), ("has_zeros", 1),
+                         ("otype", q.QDG_O_I32)):
+        bad = q.layer_nvfp4(64, 256)
+        setattr(bad, field, value)
+        assert _status(q.qdg_validate_layer, bad) == q.QDG_ERR_UNSUPPORTED, field
+    p = q.qdg_plan_create(q.layer_nvfp4(64, 256), q.dense())
+    for m in (1, 16, 200, 5000):
+        d = q.qdg_plan_describe(p, m)
+        assert "w4a16-nvfp4" in d and "family=stream" in d and "16x16x32_bf16" in d
+    pm = q.qdg_plan_create(q.layer_nvfp4(64, 256, num_experts=4), q.moe(2))
+    assert "w4a16-nvfp4" in q.qdg_moe_describe(pm, 8, 16)
+    # bf16 activations: no activation scales needed, none quantized here
+    assert _status(q.qdg_quantize_act, q.layer_nvfp4(64, 256), 0x1000, 4, 0x2000, 0x3000, 0) == q.QDG_ERR_UNSUPPORTED
+    # the per-tensor scale is required by preprocess; weights are not produced here
+    layer = q.layer_nvfp4(100, 256)
+    n = q.qdg_preprocess_query(layer)
+    w = q.StdWeights(qweight=0x1000, scales=0x2000, zeros=None, tensor_scale=None)
+    assert _status(q.qdg_preprocess, layer, w, 0x10000, n, 0) == q.QDG_ERR_INVALID_ARG
+    assert _status(q.qdg_quantize_weights, layer, 0x1000, 0x2000, 0x3000, None, 0) == q.QDG_ERR_UNSUPPORTED
+    # packed size: 1 KiB of codes and 128 bytes of scale records per 16 x 128 unit, plus the tensor scale
+    units = 7 * 2
+    assert n == ((units * 1024 + 255) // 256 * 256 + 256 + units * 128 + 255) // 256 * 256
