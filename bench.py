@@ -297,8 +297,9 @@ def _time_launches(launch, reps, stream):
 
 def rows_leg(reps=30):
     """The other rows of the hot path, each timed at its own shapes (not part
-    of `value`): W8A8, W4A8-INT8 and W8A16 (K=4096, N in {4096, 14336}, M in
-    {16, 256, 4096}), W4A8-MXFP4 ((K,N) in {(7168,2048), (2048,7168)}, M in
+    of `value`): W8A8, W4A8-INT8, W8A16 and W4A16-NVFP4 (K=4096, N in
+    {4096, 14336}, M in {16, 256, 4096}; NVFP4 from seeded random codes and
+    scales, since only the oracle quantizes to it), W4A8-MXFP4 ((K,N) in {(7168,2048), (2048,7168)}, M in
     {16, 512, 4096}) and W4A4-MXFP4 at the same shapes, the activation
     quantizers, and the grouped MoE W4A16
     GEMMs (E=256, top-8, hidden 7168, intermediate 2048, T in {64, 512,
@@ -324,16 +325,24 @@ def rows_leg(reps=30):
         elif layer.wtype == q.QDG_W_MXFP4:
             qw = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
             sc = torch.empty((n, k // 32), dtype=torch.uint8, device=dev)
+        elif layer.wtype == q.QDG_W_NVFP4:
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(synth.seed_for(2, synth.TID_W, n + k + 1))
+            qw = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device=dev, generator=gen)
+            sc = torch.randint(0x20, 0x60, (n, k // 16), dtype=torch.uint8, device=dev, generator=gen)
         else:
             qw = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
             sc = torch.empty((n, k // 128), dtype=torch.int16, device=dev)
-        q.qdg_quantize_weights(layer, w.data_ptr(), qw.data_ptr(), sc.data_ptr(), None, sh)
+        ts = torch.full((1,), 1e-4, dtype=torch.float32, device=dev)  # NVFP4 tensor scale
+        if layer.wtype != q.QDG_W_NVFP4:
+            q.qdg_quantize_weights(layer, w.data_ptr(), qw.data_ptr(), sc.data_ptr(), None, sh)
         del w
         copies = max(2, -(-2 * CACHE_BYTES // nbytes))
         bufs = []
         for _ in range(copies):
             b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-            q.qdg_preprocess(layer, q.StdWeights(qw.data_ptr(), sc.data_ptr(), None), b.data_ptr(), nbytes, sh)
+            q.qdg_preprocess(layer, q.StdWeights(qw.data_ptr(), sc.data_ptr(), None, ts.data_ptr()), b.data_ptr(),
+                             nbytes, sh)
             bufs.append(b)
         plan = q.qdg_plan_create(layer, q.dense())
         for m in ms:
@@ -379,6 +388,8 @@ def rows_leg(reps=30):
                   n * k // 2 + n * (k // 128) * 2)
         dense_row("w8a16", q.layer_w8a16(n, k), k, n, (16, 256, 4096), torch.int8, 0, PEAK_BF16_TFLOPS,
                   n * k + n * 4)
+        dense_row("w4a16-nvfp4", q.layer_nvfp4(n, k), k, n, (16, 256, 4096), torch.int8, 0, PEAK_BF16_TFLOPS,
+                  n * k // 2 + n * (k // 16) + 4)
     for (k, n) in ((7168, 2048), (2048, 7168)):
         dense_row("w4a8-mxfp4", q.layer_mxfp4(n, k), k, n, (16, 512, 4096), torch.uint8, 128, PEAK_FP8_TFLOPS,
                   n * k // 2 + n * (k // 32))
