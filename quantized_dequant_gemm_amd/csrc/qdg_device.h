@@ -153,4 +153,26 @@ __device__ __forceinline__ T ldg_nt(const T* p) {
   return __builtin_nontemporal_load(p);
 }
 
+// NVFP4 weights: OCP E4M3 block-scale code -> its exact fp32 value (the NaN
+// codes are mapped away by preprocess), and two E2M1 codes (byte SEL of d,
+// even k in the low nibble) times that scale -> a bf16 pair. The products are
+// exact in bf16 (at most 2 x 4 significant bits, exponents far inside the
+// range), so the fp32 multiply is exact and the pack drops only zero bits.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float mag = e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (b & 0x80u) ? -mag : mag;
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_scaled_bf16(uint32_t d, float s) {
+  const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, SEL);
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, v.y * s), __builtin_bit_cast(uint32_t, v.x * s),
+                               0x07060302u);
+}
+// eight E2M1 codes (one dword, K order) times s -> a bf16 MFMA operand
+__device__ __forceinline__ u32x4_t e2m1x8_scaled_bf16(uint32_t d, float s) {
+  return u32x4_t{e2m1x2_scaled_bf16<0>(d, s), e2m1x2_scaled_bf16<1>(d, s), e2m1x2_scaled_bf16<2>(d, s),
+                 e2m1x2_scaled_bf16<3>(d, s)};
+}
+
 }  // namespace qdg

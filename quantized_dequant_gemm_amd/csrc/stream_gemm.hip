@@ -405,31 +405,14 @@ struct FmtNvfp4 {
       f.sc[t] = ((const uint16_t*)(x.sbase + kRecOffset))[u * 64 + x.lane];
     }
   }
-  // OCP E4M3 code -> its exact fp32 value (the NaN codes never reach here)
-  __device__ static float e4m3(uint32_t b) {
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    const float mag = e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-    return (b & 0x80u) ? -mag : mag;
-  }
-  // two E2M1 codes (byte SEL of d) times s -> a bf16 pair (even k low)
-  template <int SEL>
-  __device__ static uint32_t pair(uint32_t d, float s) {
-    const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, SEL);
-    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, v.y * s), __builtin_bit_cast(uint32_t, v.x * s),
-                                 0x07060302u);
-  }
   template <int MT, int NT>
   __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT], uint32_t, uint32_t) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const float s0 = e4m3(f.sc[t] & 0xFFu), s1 = e4m3((f.sc[t] >> 8) & 0xFFu);
+      const float s0 = e4m3_to_f32(f.sc[t] & 0xFFu), s1 = e4m3_to_f32((f.sc[t] >> 8) & 0xFFu);
       u32x4_t bw[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t d = f.b[t][j];
-        const float s = j < 2 ? s0 : s1;
-        bw[j] = u32x4_t{pair<0>(d, s), pair<1>(d, s), pair<2>(d, s), pair<3>(d, s)};
-      }
+      for (int j = 0; j < 4; ++j) bw[j] = e2m1x8_scaled_bf16(f.b[t][j], j < 2 ? s0 : s1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll

@@ -142,7 +142,7 @@ __device__ __forceinline__ int stage_tile(const GemmArgs& p, int base, int t) {
   return min(base + t, p.ntiles - 1);
 }
 
-template <int BM, int BN, int NW>
+template <int BM, int BN, int NW, bool RS = true>
 __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint32_t* a_off, const GemmArgs& p,
                                            const uint8_t* wbase, const uint8_t* sbase, uint32_t s_off,
                                            int wg_tile0, int wave, int lane, int mb, int g) {
@@ -171,9 +171,11 @@ __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint
                                    16, 0, 0);
   // row sums: one whole-wave copy per wave; lanes past BM / 4 repeat rows
   // into the unused rest of the slot
-  static_assert(BM / 4 <= 64, "one copy of row sums");
-  const char* rs = (const char*)(p.rowsum + (size_t)g * p.m_pad + mb * BM) + (lane % (BM / 4)) * 16;
-  __builtin_amdgcn_global_load_lds(rs, (lds_void*)(st + L::RS), 16, 0, 0);
+  if constexpr (RS) {
+    static_assert(BM / 4 <= 64, "one copy of row sums");
+    const char* rs = (const char*)(p.rowsum + (size_t)g * p.m_pad + mb * BM) + (lane % (BM / 4)) * 16;
+    __builtin_amdgcn_global_load_lds(rs, (lds_void*)(st + L::RS), 16, 0, 0);
+  }
 }
 
 // One K group for a 64 x 64 wave tile: unpack the wave's 4 weight tiles once,
@@ -282,7 +284,43 @@ __device__ __forceinline__ void tile_group32(const char* st, int a_lane, int w_l
       for (int i = 0; i < 16; ++i) acc[rb][cb][i] = __builtin_fmaf(sc[cb], pacc[rb][cb][i], acc[rb][cb][i]);
 }
 
-template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, int NS, bool MOE>
+// NVFP4 weights (E2M1 with E4M3 scales per 16 K) in the same 2 x 2 blocks
+// of 32 x 32: each weight is converted, multiplied by its block scale (both
+// exact) and packed to bf16, so the MFMAs accumulate straight into the
+// result with no per-group epilogue and no row sums. The scale records hold,
+// per unit lane (c, col) of the streaming layout, the E4M3 codes of that
+// lane's two 16-blocks; a lane of quarter q = s / 4 at step s reads unit
+// lane h + 2q, whose dword s % 4 lies in its block (s % 4) / 2.
+template <int BM, int BN>
+__device__ __forceinline__ void tile_group32_nv(const char* st, int a_lane, int w_lane, int sv_lane,
+                                                f32x16_t (&acc)[2][2]) {
+  using L = Stage<BM, BN>;
+  u32x4_t bp[2][2];
+  uint32_t rec[2][2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      bp[cb][q] = *(const u32x4_t*)(st + w_lane + cb * 2048 + q * 512);
+      rec[cb][q] = *(const uint16_t*)(st + sv_lane + cb * 256 + q * 64);
+    }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    u32x4_t a[2], b[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      a[rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + (s / 4) * 128 + (s % 4) * 16);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      b[cb] = e2m1x8_scaled_bf16(bp[cb][s / 4][s % 4], e4m3_to_f32((rec[cb][s / 4] >> (8 * ((s % 4) / 2))) & 0xFFu));
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma_bf16_32(a[rb], b[cb], acc[rb][cb]);
+  }
+}
+
+template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, int NS, bool MOE, bool NV = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const GemmArgs p, int m_blocks,
                                                                            int n_blocks) {
   constexpr int NW = WAVES_M * WAVES_N;
@@ -295,7 +333,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   // copies every wave issues per stage (A, weight units, scale records, row
   // sums); waiting for the count to drop to this leaves the next stage in
   // flight
-  constexpr int VM_NEXT = A_PER_WAVE + (BN / 16) / NW + 2;
+  constexpr int VM_NEXT = A_PER_WAVE + (BN / 16) / NW + (NV ? 1 : 2);
+  static_assert(!NV || (M32 && !MOE), "NVFP4 runs the 64 x 64 wave tiles of dense layers");
   static_assert(NS == 2 || NS == 3, "two or three stages");
   // The stages are separate LDS objects (not one dynamic array) so that the
   // compiler can tell a copy into one stage from a read of another: reads of
@@ -337,7 +376,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
     expert = p.block_expert[mb];
   }
   const uint8_t* wbase = p.packed + (size_t)expert * p.expert_stride;
-  const uint8_t* sbase = wbase + p.s_offset;
+  // NVFP4: the expert's tensor scale leads its scale region, the records follow
+  const uint8_t* sbase = wbase + p.s_offset + (NV ? 256 : 0);
   const int groups = p.groups;
   // SiLU*mul (MoE gate+up): 16 stage tiles = 8 gate + 8 up tiles, i.e. 8
   // output tiles per workgroup
@@ -379,6 +419,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   const int w_lane = M32 ? L::W + (wn * 4 + (l32 >> 4)) * 1024 + (h * 16 + col) * 16 : L::W + (wn * 4) * 1024 + lane * 16;
   const int s_lane = M32 ? L::S + (wn * 4 + (l32 >> 4)) * 128 + col * 8 : L::S + (wn * 4) * 128 + col * 8;
   const int rs_lane = M32 ? L::RS + (wm * WTM + 4 * h) * 4 : L::RS + (wm * WTM + 4 * c) * 4;
+  const int sv_lane = L::S + (wn * 4 + (l32 >> 4)) * 128 + (h * 16 + col) * 2;  // NVFP4 scale records
 
   // one unpack constant in a VGPR, the other in an SGPR: lets each unpacked
   // dword be a single v_and_or_b32 (VOP3 reads at most one scalar operand)
@@ -412,7 +453,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   if (g0 < g1) {
 #pragma unroll
     for (int q = 0; q < NS - 1; ++q)
-      load_stage<BM, BN, NW>(stage[q], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane, mb,
+      load_stage<BM, BN, NW, !NV>(stage[q], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane, mb,
                              min(g0 + q, g1 - 1));
   }
   int gb = g0;
@@ -430,9 +471,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
       // wait for the copies in flight.
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       asm volatile("s_barrier" ::: "memory");
-      load_stage<BM, BN, NW>(stage[(cur + NS - 1) % NS], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane,
+      load_stage<BM, BN, NW, !NV>(stage[(cur + NS - 1) % NS], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane,
                              mb, min(gb + cur + NS - 1, g1 - 1));
-      if constexpr (M32)
+      if constexpr (NV)
+        tile_group32_nv<BM, BN>(stage[cur], a_lane, w_lane, sv_lane, acc32);
+      else if constexpr (M32)
         tile_group32<ASYM, BM, BN>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
       else
         tile_group<ASYM, BM, BN, MTW>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
@@ -443,7 +486,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
     if (gb + cur < g1) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if constexpr (M32)
+      if constexpr (NV)
+        tile_group32_nv<BM, BN>(stage[cur], a_lane, w_lane, sv_lane, acc32);
+      else if constexpr (M32)
         tile_group32<ASYM, BM, BN>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
       else
         tile_group<ASYM, BM, BN, MTW>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
@@ -515,6 +560,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   static_assert(NW * 16 * 64 * 4 <= L::BYTES, "epilogue strips fit one stage");
   const int nbase = (wg_tile0 + wn * 4) * 16;
   const int esz = f32out ? 4 : 2;  // bytes per output element
+  const float tscale = NV ? *(const float*)(wbase + p.s_offset) : 1.0f;  // NVFP4 tensor scale
   const int cpr = 64 * esz / 16;   // 16-byte chunks per strip row
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt) {
@@ -527,7 +573,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
         for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float v = acc32[mt / 2][cb][(2 * (mt % 2) + q) * 4 + i];
+            float v = acc32[mt / 2][cb][(2 * (mt % 2) + q) * 4 + i];
+            if constexpr (NV) v *= tscale;
             const int e = (8 * q + 4 * h + i) * 64 + cb * 32 + l32;
             if (f32out)
               ((float*)strip)[e] = v;
@@ -584,13 +631,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   }
 }
 
-template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE>
+template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE, bool NV = false>
 hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s) {
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
   // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256, 2 for 256 x 128)
   constexpr int NS = 3 * Stage<BM, BN>::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE>), dim3(m_blocks * n_blocks, nsplit),
+  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE, NV>), dim3(m_blocks * n_blocks, nsplit),
                      dim3(64 * WAVES_M * WAVES_N), 0, s, a, m_blocks, n_blocks);
   return hipGetLastError();
 }
@@ -601,6 +648,7 @@ hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStrea
 // 64 x 64 wave tiles (two waves per SIMD) and (128, 256, 4) with 128 x 64
 // wave tiles (one wave per SIMD, half the unpack work per MFMA).
 bool tile_cfg_supported(Format f, const TileCfg& c) {
+  if (f == FMT_NVFP4) return c.bm == 128 && c.bn == 256 && c.waves == 8;
   if (f != FMT_W4A16) return false;
   if (c.bm == 256 && c.bn == 128) return c.waves == 8;
   if (c.bm == 128 && c.bn == 256) return c.waves == 8 || c.waves == 4;
@@ -610,6 +658,7 @@ bool tile_cfg_supported(Format f, const TileCfg& c) {
 hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const GemmArgs& a, int m_blocks,
                        hipStream_t s) {
   if (!tile_cfg_supported(f, c)) return hipErrorInvalidValue;
+  if (f == FMT_NVFP4) return moe ? hipErrorInvalidValue : launch_tile_cfg<false, 2, 4, 64, false, true>(a, m_blocks, a.split, s);
 #define QDG_T(ASYM_, WM_, WN_, WTM_, MOE_)                                                 \
   if (asym == ASYM_ && c.bm == WM_ * WTM_ && c.waves == WM_ * WN_ && moe == MOE_)         \
     return launch_tile_cfg<ASYM_, WM_, WN_, WTM_, MOE_>(a, m_blocks, a.split, s);

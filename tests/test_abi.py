@@ -239,9 +239,13 @@ def test_nvfp4_layer_validation():
         setattr(bad, field, value)
         assert _status(q.qdg_validate_layer, bad) == q.QDG_ERR_UNSUPPORTED, field
     p = q.qdg_plan_create(q.layer_nvfp4(64, 256), q.dense())
-    for m in (1, 16, 200, 5000):
+    for m in (1, 16, 63, 64, 200, 5000):
         d = q.qdg_plan_describe(p, m)
-        assert "w4a16-nvfp4" in d and "family=stream" in d and "16x16x32_bf16" in d
+        fam, mfma = ("family=stream", "16x16x32_bf16") if m < 64 else ("family=tile", "32x32x16_bf16")
+        assert "w4a16-nvfp4" in d and fam in d and mfma in d, d
+    # the tiled NVFP4 instance is 128 x 256 with 8 waves only
+    t4 = q.TuningConfig(block_m=128, waves=4)
+    assert _status(q.qdg_plan_create, q.layer_nvfp4(64, 256), q.dense(), t4) == q.QDG_ERR_UNSUPPORTED
     pm = q.qdg_plan_create(q.layer_nvfp4(64, 256, num_experts=4), q.moe(2))
     assert "w4a16-nvfp4" in q.qdg_moe_describe(pm, 8, 16)
     # bf16 activations: no activation scales needed, none quantized here

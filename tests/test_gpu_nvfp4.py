@@ -37,7 +37,8 @@ def test_nvfp4_gemm(qdg, m, n, k, otype):
     y64 = ref.gemm_nvfp4a16(a, codes, sc, ts)
     plan = q.qdg_plan_create(layer, q.dense())
     d = q.qdg_plan_describe(plan, m)
-    assert "w4a16-nvfp4" in d and "family=stream" in d and "16x16x32_bf16" in d
+    fam = "family=stream" if m < 64 else "family=tile"  # LDS-tiled family from M = 64
+    assert "w4a16-nvfp4" in d and fam in d
     y, _ = H.gemm(layer, pk, H.bf16_dev(a), m)
     assert not torch.isnan(y.float()).any()
     err = metrics.rel_frob(H.to_f64(y), y64)
@@ -79,6 +80,24 @@ def test_nvfp4_every_code_and_scale_pattern(qdg):
     y_448, _ = H.gemm(layer, H.Packed(layer, qw, H.dev(sc448), tensor_scale=t), H.bf16_dev(a), m)
     assert torch.equal(y_nan, y_448)
     assert metrics.rel_frob(H.to_f64(y_448), ref.gemm_nvfp4a16(a, codes, sc448, ts)) <= 5e-5
+
+
+@pytest.mark.parametrize("m,n,k,split", [(129, 200, 640, 0), (300, 520, 1280, 3), (1024, 2048, 4096, 0),
+                                         (64, 4096, 2048, 0)])
+@pytest.mark.parametrize("otype", [q.QDG_O_F32, q.QDG_O_BF16])
+def test_nvfp4_tiled(qdg, m, n, k, split, otype):
+    # the LDS-tiled family: ragged M (partial 128-row blocks), ragged N (a
+    # partial 256-column block), K split heuristically or pinned
+    layer, pk, codes, sc, ts = _case(n, k, otype, salt=m + 2 * n)
+    a = synth.activations_bf16_bits(m, k, workload_id=10, salt=m + 1)
+    t = q.TuningConfig(block_m=128, split_k=split)
+    y, plan = H.gemm(layer, pk, H.bf16_dev(a), m, tuning=t)
+    d = q.qdg_plan_describe(plan, m)
+    assert "family=tile" in d and "32x32x16_bf16" in d and (not split or f"split_k={split}" in d), d
+    assert not torch.isnan(y.float()).any()
+    err = metrics.rel_frob(H.to_f64(y), ref.gemm_nvfp4a16(a, codes, sc, ts))
+    print(f"NVFP4 tiled M={m} N={n} K={k} split={split} otype={otype}: rel_frob={err:.3e}")
+    assert err <= (5e-5 if otype == q.QDG_O_F32 else 2e-3), err
 
 
 @pytest.mark.parametrize("split", [2, 3])
