@@ -14,7 +14,7 @@ import torch
 
 import quantized_dequant_gemm_amd as q
 import synth
-from oracle import metrics, quant, ref
+from oracle import codecs, metrics, quant, ref
 from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
@@ -90,7 +90,6 @@ def test_jit_moe_matches_aot(qdg):
     n, k = 128, 512
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=9), top_k)
     qs = [quant.quantize_int4_sym(synth.weights_f32(n, k, workload_id=10, salt=50 + e)) for e in range(E)]
-    from oracle import codecs
     layer = q.layer_w4a16(n, k, num_experts=E)
     qw = H.dev(np.stack([codecs.pack_nibbles(codecs.encode_int4(v)) for v, _ in qs]))
     sc = H.dev(np.stack([np.asarray(s_, np.uint16).view(np.int16) for _, s_ in qs]))
@@ -118,3 +117,22 @@ def test_jit_moe_matches_aot(qdg):
         torch.cuda.synchronize()
         outs.append(y)
     assert torch.equal(outs[0], outs[1])
+
+
+def test_jit_nvfp4_matches_aot(qdg):
+    # the NVFP4 policy (hardware E2M1 convert, E4M3 block scales) built by hipRTC
+    m, n, k = 40, 300, 1024
+    codes, sc, ts = quant.quantize_nvfp4(synth.weights_f32(n, k, workload_id=10, salt=5))
+    a = synth.activations_bf16_bits(m, k, workload_id=10, salt=6)
+    layer = q.layer_nvfp4(n, k, otype=q.QDG_O_F32)
+    pk = H.Packed(layer, H.dev(codecs.pack_nibbles(codes)), H.dev(sc),
+                  tensor_scale=H.dev(np.array([ts], np.float32)))
+    a_dev = H.bf16_dev(a)
+    aot = q.qdg_plan_create(layer, q.dense())
+    jit = q.qdg_plan_create(layer, q.dense())
+    q.qdg_plan_jit(jit, m)
+    assert "family=stream" in q.qdg_plan_describe(jit, m) and "code=jit" in q.qdg_plan_describe(jit, m)
+    y_aot = _run(aot, a_dev.data_ptr(), None, pk, m, n, layer.otype)
+    y_jit = _run(jit, a_dev.data_ptr(), None, pk, m, n, layer.otype)
+    assert torch.equal(y_aot, y_jit)
+    assert metrics.rel_frob(H.to_f64(y_jit), ref.gemm_nvfp4a16(a, codes, sc, ts)) <= 5e-5
