@@ -221,13 +221,13 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
   // measured on MI355X: one (partly filled) 128-row block of the tiled
   // families, with K split into one pass of workgroups, beats the streaming
-  // family from M = 33 (W4A16) and from M = 64 (NVFP4, int8 / fp8 activations)
+  // family from M = 33 (W4A16) and from M = 64 (NVFP4, W8A16, int8 / fp8 activations)
   if (!has_tuning && !P.compute.batch_invariant && !moe && bm < 128 && M > (P.fmt == FMT_W4A16 ? 32 : 63))
     bm = 128;
   if (P.compute.batch_invariant && bm > 64) bm = 64;
   // the tiled family addresses A with 32-bit byte offsets
   const bool a_fits = (double)(M > 0 ? M : 1) * (double)g.k * 2.0 < 4294967296.0;
-  if (bm >= 128 && (P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4) && !moe && a_fits) {
+  if (bm >= 128 && (P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4 || P.fmt == FMT_W8A16) && !moe && a_fits) {
     // LDS-tiled family: BM x 128 tiles, row sums of A per group in the workspace
     ch.tile = true;
     ch.tc.bm = bm;
@@ -594,8 +594,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
 // The MFMA instruction an instance issues.
 static const char* mfma_name(Format f, const Choice& c) {
   if (f == FMT_W4A16) return c.tile && c.tc.bm * c.tc.bn / (64 * c.tc.waves) == 64 ? "32x32x16_bf16" : "16x16x32_bf16";
-  if (f == FMT_W8A16) return "16x16x32_bf16";
-  if (f == FMT_NVFP4) return c.tile ? "32x32x16_bf16" : "16x16x32_bf16";
+  if (f == FMT_W8A16 || f == FMT_NVFP4) return c.tile ? "32x32x16_bf16" : "16x16x32_bf16";
   if (f == FMT_MXFP4) return "scale_16x16x128_f8f6f4";
   if (f == FMT_W4A4) return "scale_16x16x128_f4f4";
   return "16x16x64_i8";
@@ -692,12 +691,15 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
     a.m_pad = c.grid_m * c.tc.bm;
     float* rs = (float*)((char*)workspace + kCounterBytes + align_up((int64_t)c.partial_bytes, 256));
     a.rowsum = rs;
+    // offsets: -(128 + z) per group for UINT4 (applied in the kernel), 136 for
+    // INT4 and 128 for INT8 (pre-scaled here)
+    const float rs_factor = plan->fmt == FMT_W8A16 ? -128.0f : asym ? 1.0f : -136.0f;
     if (plan->fmt == FMT_NVFP4)  // scaled weights: no row-sum offsets
       e = hipSuccess;
     else
       e = moe ? launch_rowsum(A, sorted_ids, num_padded, a.top_k, a_per_pair, (int)rows, (int)M, a.K, a.m_pad,
-                              asym ? 1.0f : -136.0f, rs, stream)
-              : launch_rowsum(A, nullptr, nullptr, 0, 0, (int)rows, (int)M, a.K, a.m_pad, asym ? 1.0f : -136.0f, rs,
+                              rs_factor, rs, stream)
+              : launch_rowsum(A, nullptr, nullptr, 0, 0, (int)rows, (int)M, a.K, a.m_pad, rs_factor, rs,
                               stream);
     if (e != hipSuccess) return hip_status(e, "rowsum launch");
     e = launch_tile(plan->fmt, asym, moe, c.tc, a, c.grid_m, stream);

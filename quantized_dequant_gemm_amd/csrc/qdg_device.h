@@ -169,6 +169,25 @@ __device__ __forceinline__ uint32_t e2m1x2_scaled_bf16(uint32_t d, float s) {
   return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, v.y * s), __builtin_bit_cast(uint32_t, v.x * s),
                                0x07060302u);
 }
+// W8A16: four int8 codes (one dword, K order) -> two bf16 pairs of the
+// integers q + 128 (0..255, exact: byte -> fp32 conversion, then the fp32
+// word's upper half)
+__device__ __forceinline__ void widen_i8_bf16_offset128(uint32_t d, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = d ^ 0x80808080u;
+  const uint32_t f0 = __builtin_bit_cast(uint32_t, (float)(u & 0xFFu));
+  const uint32_t f1 = __builtin_bit_cast(uint32_t, (float)((u >> 8) & 0xFFu));
+  const uint32_t f2 = __builtin_bit_cast(uint32_t, (float)((u >> 16) & 0xFFu));
+  const uint32_t f3 = __builtin_bit_cast(uint32_t, (float)(u >> 24));
+  lo = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+  hi = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+}
+// eight int8 codes (two dwords, K order) -> a bf16 MFMA operand of q + 128
+__device__ __forceinline__ u32x4_t i8x8_bf16_offset128(uint32_t d0, uint32_t d1) {
+  uint32_t w0, w1, w2, w3;
+  widen_i8_bf16_offset128(d0, w0, w1);
+  widen_i8_bf16_offset128(d1, w2, w3);
+  return u32x4_t{w0, w1, w2, w3};
+}
 // eight E2M1 codes (one dword, K order) times s -> a bf16 MFMA operand
 __device__ __forceinline__ u32x4_t e2m1x8_scaled_bf16(uint32_t d, float s) {
   return u32x4_t{e2m1x2_scaled_bf16<0>(d, s), e2m1x2_scaled_bf16<1>(d, s), e2m1x2_scaled_bf16<2>(d, s),

@@ -323,16 +323,6 @@ struct FmtW8A16 {
       f.b[t][1] = ldg_nt(pu + 64 + x.lane);
     }
   }
-  // four int8 codes (one dword) -> two bf16 pairs of q + 128
-  __device__ static void widen(uint32_t d, uint32_t& lo, uint32_t& hi) {
-    const uint32_t u = d ^ 0x80808080u;
-    const uint32_t f0 = __builtin_bit_cast(uint32_t, (float)(u & 0xFFu));
-    const uint32_t f1 = __builtin_bit_cast(uint32_t, (float)((u >> 8) & 0xFFu));
-    const uint32_t f2 = __builtin_bit_cast(uint32_t, (float)((u >> 16) & 0xFFu));
-    const uint32_t f3 = __builtin_bit_cast(uint32_t, (float)(u >> 24));
-    lo = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
-    hi = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
-  }
   template <int MT, int NT>
   __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT], uint32_t, uint32_t) {
     f32x4_t corr[MT];
@@ -351,11 +341,7 @@ struct FmtW8A16 {
       for (int j = 0; j < 4; ++j) {
         // step j: K 32c + 8j .. +7 = bytes 8 (j % 2) .. +7 of chunk j / 2
         const u32x4_t ch = f.b[t][j / 2];
-        const uint32_t d0 = (j % 2) ? ch.z : ch.x, d1 = (j % 2) ? ch.w : ch.y;
-        uint32_t w0, w1, w2, w3;
-        widen(d0, w0, w1);
-        widen(d1, w2, w3);
-        bw[j] = u32x4_t{w0, w1, w2, w3};
+        bw[j] = i8x8_bf16_offset128((j % 2) ? ch.z : ch.x, (j % 2) ? ch.w : ch.y);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {

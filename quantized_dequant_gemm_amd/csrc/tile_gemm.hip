@@ -110,16 +110,17 @@ __global__ void reduce_splits_kernel(const float* __restrict__ partial, void* __
 //          address is one per-lane base plus an immediate offset)
 //   RS     BM floats (row sums, pre-scaled), in a slot of at least 1 KiB
 //          so that one whole-wave copy fills it
-//   W      BN/16 packed weight units of 1 KiB (tile-major)
+//   W      BN/16 packed weight units of UB bytes (1 KiB for 4-bit codes, 2 KiB
+//          for int8; tile-major)
 //   S      BN/16 x 16 scale records of 8 bytes
-template <int BM, int BN>
+template <int BM, int BN, int UB = 1024>
 struct Stage {
   static constexpr int ROW = 272;
   static constexpr int A = 0;
   static constexpr int A_SLOTS = BM * ROW / 16;  // 16-byte slots, 17 per row
   static constexpr int RS = BM * ROW;
   static constexpr int W = RS + (BM * 4 > 1024 ? BM * 4 : 1024);
-  static constexpr int S = W + (BN / 16) * 1024;
+  static constexpr int S = W + (BN / 16) * UB;
   static constexpr int BYTES = S + (BN / 16) * 128;
 };
 
@@ -142,7 +143,7 @@ __device__ __forceinline__ int stage_tile(const GemmArgs& p, int base, int t) {
   return min(base + t, p.ntiles - 1);
 }
 
-template <int BM, int BN, int NW, bool RS = true>
+template <int BM, int BN, int NW, bool RS = true, int UB = 1024>
 __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint32_t* a_off, const GemmArgs& p,
                                            const uint8_t* wbase, const uint8_t* sbase, uint32_t s_off,
                                            int wg_tile0, int wave, int lane, int mb, int g) {
@@ -150,9 +151,10 @@ __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint
   // the copy count is exact for every wave and the compiler can tell which
   // stage each copy writes. Surplus copies repeat another wave's copy (the
   // same bytes to the same place).
-  using L = Stage<BM, BN>;
+  using L = Stage<BM, BN, UB>;
   constexpr int A_INST = (L::A_SLOTS + 63) / 64;
-  static_assert((BN / 16) % NW == 0, "whole weight units per wave");
+  constexpr int WC = UB / 1024;  // 1 KiB copies per unit
+  static_assert((BN / 16) * WC % NW == 0, "whole weight copies per wave");
   const char* ag = a_g + (size_t)g * 256;
 #pragma unroll
   for (int r = 0; r < (A_INST + NW - 1) / NW; ++r) {
@@ -160,15 +162,18 @@ __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint
     __builtin_amdgcn_global_load_lds(ag + a_off[r], (lds_void*)(st + L::A + i * 1024), 16, 0, 0);
   }
 #pragma unroll
-  for (int r = 0; r < (BN / 16) / NW; ++r) {
-    const int t = r * NW + wave;
+  for (int r = 0; r < (BN / 16) * WC / NW; ++r) {
+    const int ci = r * NW + wave;
+    const int t = ci / WC, part = ci % WC;
     const int tile = stage_tile(p, wg_tile0, t);
-    __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * kUnit4Bytes + lane * 16,
-                                     (lds_void*)(st + L::W + t * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * UB + part * 1024 + lane * 16,
+                                     (lds_void*)(st + L::W + t * UB + part * 1024), 16, 0, 0);
   }
   // scale records: BN / 128 copies of 1 KiB, copy wave % (BN / 128) per wave
-  __builtin_amdgcn_global_load_lds(sbase + (size_t)g * 128 + s_off, (lds_void*)(st + L::S + (wave % (BN / 128)) * 1024),
-                                   16, 0, 0);
+  // (int8 weights have one scale per channel, applied in the epilogue)
+  if constexpr (UB == 1024)
+    __builtin_amdgcn_global_load_lds(sbase + (size_t)g * 128 + s_off,
+                                     (lds_void*)(st + L::S + (wave % (BN / 128)) * 1024), 16, 0, 0);
   // row sums: one whole-wave copy per wave; lanes past BM / 4 repeat rows
   // into the unused rest of the slot
   if constexpr (RS) {
@@ -320,21 +325,69 @@ __device__ __forceinline__ void tile_group32_nv(const char* st, int a_lane, int 
   }
 }
 
-template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, int NS, bool MOE, bool NV = false>
+// W8A16 (int8 weights, one fp32 scale per channel) in the same blocks: each
+// int8 q enters the MFMA as the bf16 integer q + 128 and each group's chains
+// start from the row sums of A pre-scaled by -128, so a group adds exactly
+// sum A * q; the channel scale is applied in the epilogue. Unit lane (c, col)
+// holds K 32c..32c+15 in its first 16-byte chunk and 32c+16..32c+31 in its
+// second (1 KiB further on); step s reads unit lane h + 2 (s / 4), chunk
+// (s % 4) / 2, dwords 2 (s % 2) and 2 (s % 2) + 1.
+template <int BM, int BN>
+__device__ __forceinline__ void tile_group32_w8(const char* st, int a_lane, int w8_lane, int rs_lane,
+                                                f32x16_t (&acc)[2][2]) {
+  using L = Stage<BM, BN, 2048>;
+  f32x16_t pacc[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    f32x4_t r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = *(const f32x4_t*)(st + rs_lane + rb * 128 + q * 32);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pacc[rb][cb][i] = r[i / 4][i % 4];
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    u32x4_t a[2], b[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      a[rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + (s / 4) * 128 + (s % 4) * 16);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const u32x4_t ch = *(const u32x4_t*)(st + w8_lane + cb * 2 * 2048 + (s / 4) * 512 + ((s % 4) / 2) * 1024);
+      b[cb] = i8x8_bf16_offset128(s % 2 ? ch.z : ch.x, s % 2 ? ch.w : ch.y);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) pacc[rb][cb] = mfma_bf16_32(a[rb], b[cb], pacc[rb][cb]);
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][cb][i] += pacc[rb][cb][i];
+}
+
+template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, int NS, bool MOE, bool NV = false, bool W8 = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const GemmArgs p, int m_blocks,
                                                                            int n_blocks) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
   constexpr int MTW = WTM / 16;  // 16-row tiles per wave
   constexpr bool M32 = WTM == 64;  // 64 x 64 wave tiles run 32 x 32 MFMA blocks
-  using L = Stage<BM, BN>;
+  constexpr int UB = W8 ? 2048 : 1024;  // bytes per weight unit
+  using L = Stage<BM, BN, UB>;
   constexpr int A_INST = (L::A_SLOTS + 63) / 64;
   constexpr int A_PER_WAVE = (A_INST + NW - 1) / NW;
   // copies every wave issues per stage (A, weight units, scale records, row
   // sums); waiting for the count to drop to this leaves the next stage in
   // flight
-  constexpr int VM_NEXT = A_PER_WAVE + (BN / 16) / NW + (NV ? 1 : 2);
+  constexpr int VM_NEXT = A_PER_WAVE + (BN / 16) * (UB / 1024) / NW + (W8 ? 0 : 1) + (NV ? 0 : 1);
   static_assert(!NV || (M32 && !MOE), "NVFP4 runs the 64 x 64 wave tiles of dense layers");
+  static_assert(!W8 || (M32 && !MOE && !NV), "W8A16 runs the 64 x 64 wave tiles of dense layers");
   static_assert(NS == 2 || NS == 3, "two or three stages");
   // The stages are separate LDS objects (not one dynamic array) so that the
   // compiler can tell a copy into one stage from a read of another: reads of
@@ -420,6 +473,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   const int s_lane = M32 ? L::S + (wn * 4 + (l32 >> 4)) * 128 + col * 8 : L::S + (wn * 4) * 128 + col * 8;
   const int rs_lane = M32 ? L::RS + (wm * WTM + 4 * h) * 4 : L::RS + (wm * WTM + 4 * c) * 4;
   const int sv_lane = L::S + (wn * 4 + (l32 >> 4)) * 128 + (h * 16 + col) * 2;  // NVFP4 scale records
+  const int w8_lane = L::W + (wn * 4 + (l32 >> 4)) * 2048 + (h * 16 + col) * 16;  // W8A16 units
 
   // one unpack constant in a VGPR, the other in an SGPR: lets each unpacked
   // dword be a single v_and_or_b32 (VOP3 reads at most one scalar operand)
@@ -453,7 +507,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   if (g0 < g1) {
 #pragma unroll
     for (int q = 0; q < NS - 1; ++q)
-      load_stage<BM, BN, NW, !NV>(stage[q], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane, mb,
+      load_stage<BM, BN, NW, !NV, UB>(stage[q], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane, mb,
                              min(g0 + q, g1 - 1));
   }
   int gb = g0;
@@ -471,10 +525,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
       // wait for the copies in flight.
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       asm volatile("s_barrier" ::: "memory");
-      load_stage<BM, BN, NW, !NV>(stage[(cur + NS - 1) % NS], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane,
+      load_stage<BM, BN, NW, !NV, UB>(stage[(cur + NS - 1) % NS], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane,
                              mb, min(gb + cur + NS - 1, g1 - 1));
       if constexpr (NV)
         tile_group32_nv<BM, BN>(stage[cur], a_lane, w_lane, sv_lane, acc32);
+      else if constexpr (W8)
+        tile_group32_w8<BM, BN>(stage[cur], a_lane, w8_lane, rs_lane, acc32);
       else if constexpr (M32)
         tile_group32<ASYM, BM, BN>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
       else
@@ -488,6 +544,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
       __syncthreads();
       if constexpr (NV)
         tile_group32_nv<BM, BN>(stage[cur], a_lane, w_lane, sv_lane, acc32);
+      else if constexpr (W8)
+        tile_group32_w8<BM, BN>(stage[cur], a_lane, w8_lane, rs_lane, acc32);
       else if constexpr (M32)
         tile_group32<ASYM, BM, BN>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
       else
@@ -561,6 +619,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   const int nbase = (wg_tile0 + wn * 4) * 16;
   const int esz = f32out ? 4 : 2;  // bytes per output element
   const float tscale = NV ? *(const float*)(wbase + p.s_offset) : 1.0f;  // NVFP4 tensor scale
+  float csc[2] = {1.0f, 1.0f};  // W8A16: the channel scales of this lane's two columns
+  if constexpr (W8) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int n = nbase + cb * 32 + l32;
+      csc[cb] = n < p.N ? ((const float*)(wbase + p.s_offset))[n] : 0.f;
+    }
+  }
   const int cpr = 64 * esz / 16;   // 16-byte chunks per strip row
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt) {
@@ -575,6 +641,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
           for (int i = 0; i < 4; ++i) {
             float v = acc32[mt / 2][cb][(2 * (mt % 2) + q) * 4 + i];
             if constexpr (NV) v *= tscale;
+            if constexpr (W8) v *= csc[cb];
             const int e = (8 * q + 4 * h + i) * 64 + cb * 32 + l32;
             if (f32out)
               ((float*)strip)[e] = v;
@@ -631,13 +698,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   }
 }
 
-template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE, bool NV = false>
+template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE, bool NV = false, bool W8 = false>
 hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s) {
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
-  // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256, 2 for 256 x 128)
-  constexpr int NS = 3 * Stage<BM, BN>::BYTES <= 160 * 1024 ? 3 : 2;
+  // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256, 2 for 256 x 128
+  // and for int8 units)
+  constexpr int NS = 3 * Stage<BM, BN, W8 ? 2048 : 1024>::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE, NV>), dim3(m_blocks * n_blocks, nsplit),
+  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE, NV, W8>), dim3(m_blocks * n_blocks, nsplit),
                      dim3(64 * WAVES_M * WAVES_N), 0, s, a, m_blocks, n_blocks);
   return hipGetLastError();
 }
@@ -648,7 +716,7 @@ hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStrea
 // 64 x 64 wave tiles (two waves per SIMD) and (128, 256, 4) with 128 x 64
 // wave tiles (one wave per SIMD, half the unpack work per MFMA).
 bool tile_cfg_supported(Format f, const TileCfg& c) {
-  if (f == FMT_NVFP4) return c.bm == 128 && c.bn == 256 && c.waves == 8;
+  if (f == FMT_NVFP4 || f == FMT_W8A16) return c.bm == 128 && c.bn == 256 && c.waves == 8;
   if (f != FMT_W4A16) return false;
   if (c.bm == 256 && c.bn == 128) return c.waves == 8;
   if (c.bm == 128 && c.bn == 256) return c.waves == 8 || c.waves == 4;
@@ -659,6 +727,8 @@ hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const Ge
                        hipStream_t s) {
   if (!tile_cfg_supported(f, c)) return hipErrorInvalidValue;
   if (f == FMT_NVFP4) return moe ? hipErrorInvalidValue : launch_tile_cfg<false, 2, 4, 64, false, true>(a, m_blocks, a.split, s);
+  if (f == FMT_W8A16)
+    return moe ? hipErrorInvalidValue : launch_tile_cfg<false, 2, 4, 64, false, false, true>(a, m_blocks, a.split, s);
 #define QDG_T(ASYM_, WM_, WN_, WTM_, MOE_)                                                 \
   if (asym == ASYM_ && c.bm == WM_ * WTM_ && c.waves == WM_ * WN_ && moe == MOE_)         \
     return launch_tile_cfg<ASYM_, WM_, WN_, WTM_, MOE_>(a, m_blocks, a.split, s);

@@ -214,9 +214,10 @@ def test_w4a4_layer_validation():
 def test_w8a16_layer_validation():
     q.qdg_validate_layer(q.layer_w8a16(64, 256))
     p = q.qdg_plan_create(q.layer_w8a16(64, 256), q.dense())
-    for m in (1, 16, 200):
+    for m in (1, 16, 63, 64, 200):
         d = q.qdg_plan_describe(p, m)
-        assert "w8a16-int8" in d and "family=stream" in d
+        fam, mfma = ("family=stream", "16x16x32_bf16") if m < 64 else ("family=tile", "32x32x16_bf16")
+        assert "w8a16-int8" in d and fam in d and mfma in d, d
     bad = q.layer_w8a16(64, 256, otype=q.QDG_O_I32)
     assert _status(q.qdg_validate_layer, bad) == q.QDG_ERR_UNSUPPORTED
 

@@ -33,7 +33,8 @@ def test_w8a16_gemm(qdg, m, n, k, otype):
     y64 = ref.gemm_w8a16(a, qw, sw)
     plan = q.qdg_plan_create(layer, q.dense())
     d = q.qdg_plan_describe(plan, m)
-    assert "w8a16-int8" in d and "family=stream" in d
+    fam = "family=stream" if m < 64 else "family=tile"  # LDS-tiled family from M = 64
+    assert "w8a16-int8" in d and fam in d
     y, _ = H.gemm(layer, pk, H.bf16_dev(a), m)
     assert not torch.isnan(y.float()).any()
     err = metrics.rel_frob(H.to_f64(y), y64)
@@ -47,6 +48,24 @@ def test_w8a16_one_hot_recovers_dequantized_weights(qdg):
     y, _ = H.gemm(layer, pk, H.bf16_dev(eye), k)
     want = (qw.astype(np.float64) * sw.astype(np.float64)[:, None]).T
     assert np.array_equal(H.to_f64(y), want.astype(np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("m,n,k,split", [(129, 200, 640, 0), (300, 520, 1280, 3), (1024, 2048, 4096, 0),
+                                         (64, 4096, 2048, 0)])
+@pytest.mark.parametrize("otype", [q.QDG_O_F32, q.QDG_O_BF16])
+def test_w8a16_tiled(qdg, m, n, k, split, otype):
+    # the LDS-tiled family: ragged M (partial 128-row blocks), ragged N (a
+    # partial 256-column block), K split heuristically or pinned
+    layer, pk, qw, sw = _case(n, k, otype, salt=m + 2 * n)
+    a = synth.activations_bf16_bits(m, k, workload_id=9, salt=m + 1)
+    t = q.TuningConfig(block_m=128, split_k=split)
+    y, plan = H.gemm(layer, pk, H.bf16_dev(a), m, tuning=t)
+    d = q.qdg_plan_describe(plan, m)
+    assert "family=tile" in d and "32x32x16_bf16" in d and (not split or f"split_k={split}" in d), d
+    assert not torch.isnan(y.float()).any()
+    err = metrics.rel_frob(H.to_f64(y), ref.gemm_w8a16(a, qw, sw))
+    print(f"W8A16 tiled M={m} N={n} K={k} split={split} otype={otype}: rel_frob={err:.3e}")
+    assert err <= (5e-5 if otype == q.QDG_O_F32 else 2e-3), err
 
 
 @pytest.mark.parametrize("split", [2, 3])
