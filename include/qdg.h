@@ -138,7 +138,7 @@ enum { QDG_EPI_NONE = 0, QDG_EPI_SILU_MUL = 1 };
      LDS-tiled         block_m 128 (block_n 256) or 256 (block_n 128), waves
                        8 or 4 (dense W4A16; the default from M = 33);
                        block_m 128, block_n 256, waves 8 for dense W8A16 and
-                       W4A16-NVFP4 (the default from M = 64); the 8-bit
+                       W4A16-NVFP4 (the default from M = 33); the 8-bit
                        activation formats have their own 128 x 256 tiles
                        (the default from M = 64, or above 128 for W4A4 and
                        narrow W8A8 layers)

@@ -221,8 +221,10 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
   // measured on MI355X: one (partly filled) 128-row block of the tiled
   // families, with K split into one pass of workgroups, beats the streaming
-  // family from M = 33 (W4A16) and from M = 64 (NVFP4, W8A16, int8 / fp8 activations)
-  if (!has_tuning && !P.compute.batch_invariant && !moe && bm < 128 && M > (P.fmt == FMT_W4A16 ? 32 : 63))
+  // family from M = 33 (bf16 activations: W4A16, NVFP4, W8A16) and from
+  // M = 64 (int8 / fp8 / fp4 activations)
+  const bool bf16_act = P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4 || P.fmt == FMT_W8A16;
+  if (!has_tuning && !P.compute.batch_invariant && !moe && bm < 128 && M > (bf16_act ? 32 : 63))
     bm = 128;
   if (P.compute.batch_invariant && bm > 64) bm = 64;
   // the tiled family addresses A with 32-bit byte offsets
@@ -332,7 +334,13 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   ch.sc.mt = bm / 16;
   ch.sc.kw = has_tuning && T.waves ? T.waves : 4;
   int nt = has_tuning && T.block_n ? T.block_n / 16 : 0;
-  if (!nt) nt = (ch.sc.mt == 1 && g.ntiles < 128 && !P.compute.batch_invariant) ? 1 : 2;
+  // measured on MI355X: NVFP4 and W8A16 in 16-row blocks, where two tiles per
+  // workgroup leave too few workgroups and need a K split (256 to 511 tiles),
+  // run fastest with one N tile per workgroup and no split instead (their
+  // unpack is VALU-heavy); wider layers keep two tiles and no split
+  const bool one_tile = ch.sc.mt == 1 && !P.compute.batch_invariant && !moe && g.ntiles >= 256 &&
+                        g.ntiles < 512 && (P.fmt == FMT_NVFP4 || (P.fmt == FMT_W8A16 && g.groups <= 64));
+  if (!nt) nt = one_tile || (ch.sc.mt == 1 && g.ntiles < 128 && !P.compute.batch_invariant) ? 1 : 2;
   ch.sc.nt = nt;
   ch.grid_m = (int)((M + bm - 1) / bm);
   const int64_t nblocks = (g.ntiles + nt - 1) / nt;
@@ -343,6 +351,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
     if (split < 1) split = 1;
     const int maxs = (int)(g.groups / ch.sc.kw);
     if (split > maxs) split = maxs > 0 ? maxs : 1;
+    if (one_tile) split = 1;
   }
   if (moe || P.layer.otype == QDG_O_I32) split = 1;  // raw integer results are not split
   ch.sc.split = split;

@@ -214,9 +214,9 @@ def test_w4a4_layer_validation():
 def test_w8a16_layer_validation():
     q.qdg_validate_layer(q.layer_w8a16(64, 256))
     p = q.qdg_plan_create(q.layer_w8a16(64, 256), q.dense())
-    for m in (1, 16, 63, 64, 200):
+    for m in (1, 16, 32, 33, 200):
         d = q.qdg_plan_describe(p, m)
-        fam, mfma = ("family=stream", "16x16x32_bf16") if m < 64 else ("family=tile", "32x32x16_bf16")
+        fam, mfma = ("family=stream", "16x16x32_bf16") if m <= 32 else ("family=tile", "32x32x16_bf16")
         assert "w8a16-int8" in d and fam in d and mfma in d, d
     bad = q.layer_w8a16(64, 256, otype=q.QDG_O_I32)
     assert _status(q.qdg_validate_layer, bad) == q.QDG_ERR_UNSUPPORTED
@@ -240,10 +240,13 @@ def test_nvfp4_layer_validation():
         setattr(bad, field, value)
         assert _status(q.qdg_validate_layer, bad) == q.QDG_ERR_UNSUPPORTED, field
     p = q.qdg_plan_create(q.layer_nvfp4(64, 256), q.dense())
-    for m in (1, 16, 63, 64, 200, 5000):
+    for m in (1, 16, 32, 33, 64, 200, 5000):
         d = q.qdg_plan_describe(p, m)
-        fam, mfma = ("family=stream", "16x16x32_bf16") if m < 64 else ("family=tile", "32x32x16_bf16")
+        fam, mfma = ("family=stream", "16x16x32_bf16") if m <= 32 else ("family=tile", "32x32x16_bf16")
         assert "w4a16-nvfp4" in d and fam in d and mfma in d, d
+    # 16-row blocks of a layer with >= 256 tiles: one tile per workgroup, no K split
+    d = q.qdg_plan_describe(q.qdg_plan_create(q.layer_nvfp4(4096, 4096), q.dense()), 16)
+    assert "block_n=16" in d and "split_k=1" in d, d
     # the tiled NVFP4 instance is 128 x 256 with 8 waves only
     t4 = q.TuningConfig(block_m=128, waves=4)
     assert _status(q.qdg_plan_create, q.layer_nvfp4(64, 256), q.dense(), t4) == q.QDG_ERR_UNSUPPORTED

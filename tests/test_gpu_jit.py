@@ -121,7 +121,7 @@ def test_jit_moe_matches_aot(qdg):
 
 def test_jit_nvfp4_matches_aot(qdg):
     # the NVFP4 policy (hardware E2M1 convert, E4M3 block scales) built by hipRTC
-    m, n, k = 40, 300, 1024
+    m, n, k = 24, 300, 1024
     codes, sc, ts = quant.quantize_nvfp4(synth.weights_f32(n, k, workload_id=10, salt=5))
     a = synth.activations_bf16_bits(m, k, workload_id=10, salt=6)
     layer = q.layer_nvfp4(n, k, otype=q.QDG_O_F32)

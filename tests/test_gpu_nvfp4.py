@@ -37,7 +37,7 @@ def test_nvfp4_gemm(qdg, m, n, k, otype):
     y64 = ref.gemm_nvfp4a16(a, codes, sc, ts)
     plan = q.qdg_plan_create(layer, q.dense())
     d = q.qdg_plan_describe(plan, m)
-    fam = "family=stream" if m < 64 else "family=tile"  # LDS-tiled family from M = 64
+    fam = "family=stream" if m <= 32 else "family=tile"  # LDS-tiled family from M = 33
     assert "w4a16-nvfp4" in d and fam in d
     y, _ = H.gemm(layer, pk, H.bf16_dev(a), m)
     assert not torch.isnan(y.float()).any()

@@ -33,7 +33,7 @@ def test_w8a16_gemm(qdg, m, n, k, otype):
     y64 = ref.gemm_w8a16(a, qw, sw)
     plan = q.qdg_plan_create(layer, q.dense())
     d = q.qdg_plan_describe(plan, m)
-    fam = "family=stream" if m < 64 else "family=tile"  # LDS-tiled family from M = 64
+    fam = "family=stream" if m <= 32 else "family=tile"  # LDS-tiled family from M = 33
     assert "w8a16-int8" in d and fam in d
     y, _ = H.gemm(layer, pk, H.bf16_dev(a), m)
     assert not torch.isnan(y.float()).any()
