@@ -567,9 +567,9 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   const bool silu = plan.compute.epilogue == QDG_EPI_SILU_MUL;  // weight streaming has no such epilogue
   c.ws = block_m == 16 && !plan.compute.batch_invariant && !silu && ws_pinned;
   if (plan.fmt != FMT_W4A16) {
-    // int8 / fp8 activations: the streaming family, block_m / 16 row tiles
+    // every other format: the streaming family, block_m / 16 row tiles
     if (block_m > 64)
-      return fail(QDG_ERR_UNSUPPORTED, "grouped MoE with int8/fp8 activations uses block_m 16, 32 or 64");
+      return fail(QDG_ERR_UNSUPPORTED, "grouped MoE of %s uses block_m 16, 32 or 64", fmt_name(plan.fmt, plan.layer));
     c.ws = c.tile = c.qtile = false;
     c.sc = StreamCfg{block_m / 16, 2, 4, 1};
     c.rowsum_bytes = 0;

@@ -263,3 +263,13 @@ def test_nvfp4_layer_validation():
     # packed size: 1 KiB of codes and 128 bytes of scale records per 16 x 128 unit, plus the tensor scale
     units = 7 * 2
     assert n == ((units * 1024 + 255) // 256 * 256 + 256 + units * 128 + 255) // 256 * 256
+
+
+def test_moe_128_row_blocks_are_w4a16_only():
+    # the other formats' grouped GEMMs run 16-, 32- or 64-row blocks
+    for layer in (q.layer_nvfp4(256, 256, num_experts=4), q.layer_w8a16(256, 256, num_experts=4),
+                  q.layer_w4a8(256, 256, num_experts=4)):
+        p = q.qdg_plan_create(layer, q.moe(2))
+        with pytest.raises(q.QdgError):
+            q.qdg_moe_describe(p, 8, 128)
+        assert "family=stream" in q.qdg_moe_describe(p, 8, 64)
