@@ -298,8 +298,7 @@ def _time_launches(launch, reps, stream):
 def rows_leg(reps=30):
     """The other rows of the hot path, each timed at its own shapes (not part
     of `value`): W8A8, W4A8-INT8, W8A16 and W4A16-NVFP4 (K=4096, N in
-    {4096, 14336}, M in {16, 256, 4096}; NVFP4 from seeded random codes and
-    scales, since only the oracle quantizes to it), W4A8-MXFP4 ((K,N) in {(7168,2048), (2048,7168)}, M in
+    {4096, 14336}, M in {16, 256, 4096}), W4A8-MXFP4 ((K,N) in {(7168,2048), (2048,7168)}, M in
     {16, 512, 4096}) and W4A4-MXFP4 at the same shapes, the activation
     quantizers, and the grouped MoE W4A16
     GEMMs (E=256, top-8, hidden 7168, intermediate 2048, T in {64, 512,
@@ -326,16 +325,14 @@ def rows_leg(reps=30):
             qw = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
             sc = torch.empty((n, k // 32), dtype=torch.uint8, device=dev)
         elif layer.wtype == q.QDG_W_NVFP4:
-            gen = torch.Generator(device=dev)
-            gen.manual_seed(synth.seed_for(2, synth.TID_W, n + k + 1))
-            qw = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device=dev, generator=gen)
-            sc = torch.randint(0x20, 0x60, (n, k // 16), dtype=torch.uint8, device=dev, generator=gen)
+            qw = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+            sc = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
         else:
             qw = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
             sc = torch.empty((n, k // 128), dtype=torch.int16, device=dev)
-        ts = torch.full((1,), 1e-4, dtype=torch.float32, device=dev)  # NVFP4 tensor scale
-        if layer.wtype != q.QDG_W_NVFP4:
-            q.qdg_quantize_weights(layer, w.data_ptr(), qw.data_ptr(), sc.data_ptr(), None, sh)
+        ts = torch.empty(1, dtype=torch.float32, device=dev)  # NVFP4 tensor scale
+        q.qdg_quantize_weights(layer, w.data_ptr(), qw.data_ptr(), sc.data_ptr(),
+                               ts.data_ptr() if layer.wtype == q.QDG_W_NVFP4 else None, sh)
         del w
         copies = max(2, -(-2 * CACHE_BYTES // nbytes))
         bufs = []

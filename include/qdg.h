@@ -207,8 +207,11 @@ qdg_status qdg_preprocess(const qdg_layer_config* layer, const qdg_std_weights* 
      INT8  s = f32(amax/127), q = clamp(rne(w/s), -127, 127), per row
      MXFP4 X = floor(log2(amax)) - 2 per 32, e = X + 127, q = e2m1_rne_sat(w/2^X)
    A scale that is zero is stored as 1.0 (all-zero group). `zeros` is used
-   for UINT4 only. NVFP4 is not produced here (QDG_ERR_UNSUPPORTED): its
-   tensor scale depends on the whole tensor. */
+   for UINT4 only, except for NVFP4, where it receives the f32 [E] tensor
+   scales:
+     NVFP4 ts = f32(amax_tensor/2688) (1 if all zero) per expert,
+           s = e4m3_rne(min(f32(f32(amax/6)/ts), 448)) per 16,
+           q = e2m1_rne_sat(f32(w/f32(e4m3(s)*ts))) (0 where that is 0). */
 qdg_status qdg_quantize_weights(const qdg_layer_config* layer, const float* w,
                                 void* qweight, void* scales, void* zeros, void* stream);
 

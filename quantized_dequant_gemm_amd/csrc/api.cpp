@@ -456,8 +456,8 @@ qdg_status qdg_quantize_weights(const qdg_layer_config* layer, const float* w, v
   if (st != QDG_OK) return st;
   if (!w || !qweight || !scales) return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
   if (layer->wtype == QDG_W_UINT4 && !zeros) return fail(QDG_ERR_INVALID_ARG, "UINT4 needs a zeros buffer");
-  if (layer->wtype == QDG_W_NVFP4)
-    return fail(QDG_ERR_UNSUPPORTED, "NVFP4 weights are not produced here (the tensor scale needs the whole tensor)");
+  if (layer->wtype == QDG_W_NVFP4 && (!zeros || !aligned(zeros, 4)))
+    return fail(QDG_ERR_INVALID_ARG, "NVFP4 needs a 4-byte aligned f32 [E] buffer for the tensor scales (zeros)");
   return hip_status(launch_quantize_weights(*layer, w, qweight, scales, zeros, (hipStream_t)stream),
                     "quantize_weights launch");
 }

@@ -215,6 +215,62 @@ __global__ void quantize_weights_kernel(int wtype, const float* __restrict__ w, 
   }
 }
 
+// ------------------------------------------------------------ NVFP4 producer
+// The per-expert tensor scale needs the whole tensor: zero the per-expert
+// amax slots, take the amax with one atomic max per wave (non-negative
+// binary32 values order like their bit patterns), turn it into the tensor
+// scale, then quantize one 16-block per thread with the binary32 steps
+// ts = f32(amax / 2688) (1 for an all-zero tensor),
+// sb = e4m3_rne(min(f32(f32(amax_b / 6) / ts), 448)),
+// q = e2m1_rne_sat(f32(w / f32(e4m3(sb) * ts))) (all zero when that is 0).
+__global__ void nvfp4_zero_kernel(uint32_t* __restrict__ slots, int64_t experts) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < experts) slots[i] = 0u;
+}
+__global__ void nvfp4_amax_kernel(const float* __restrict__ w, int64_t per_expert, uint32_t* __restrict__ slots) {
+  const int64_t e = blockIdx.y;
+  const float* src = w + e * per_expert;
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < per_expert; i += (int64_t)gridDim.x * blockDim.x)
+    m = fmaxf(m, fabsf(src[i]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(slots + e, __builtin_bit_cast(uint32_t, m));
+}
+__global__ void nvfp4_scale_kernel(uint32_t* __restrict__ slots, int64_t experts) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= experts) return;
+  const float amax = __builtin_bit_cast(float, slots[e]);
+  float ts = amax > 0.f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
+  if (ts == 0.f) ts = 1.0f;
+  slots[e] = __builtin_bit_cast(uint32_t, ts);  // now the tensor scale
+}
+__global__ void nvfp4_quantize_kernel(const float* __restrict__ w, uint8_t* __restrict__ qw, uint8_t* __restrict__ sc,
+                                      const float* __restrict__ ts_e, int64_t rows_per_expert, int64_t K,
+                                      int64_t blocks) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= blocks) return;
+  const int64_t bpr = K / 16;
+  const int64_t row = tid / bpr, b = tid % bpr;
+  const float ts = ts_e[row / rows_per_expert];
+  const float* src = w + row * K + b * 16;
+  float amax = 0.f;
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(src[i]));
+  const float r = __fdiv_rn(__fdiv_rn(amax, 6.0f), ts);
+  const uint32_t code = e4m3_rne(fminf(r, 448.0f));
+  sc[tid] = (uint8_t)code;
+  const float den = __fmul_rn(e4m3_to_f32(code), ts);
+  uint8_t* dst = qw + row * (K / 2) + b * 8;
+  for (int i = 0; i < 16; i += 2) {
+    uint32_t c0 = 0, c1 = 0;
+    if (den > 0.f) {
+      c0 = e2m1_rne_sat(__fdiv_rn(src[i], den));
+      c1 = e2m1_rne_sat(__fdiv_rn(src[i + 1], den));
+    }
+    dst[i / 2] = (uint8_t)(c0 | (c1 << 4));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_preprocess(const qdg_layer_config& L, Format f, const PackedGeom& g,
@@ -232,6 +288,19 @@ hipError_t launch_preprocess(const qdg_layer_config& L, Format f, const PackedGe
 hipError_t launch_quantize_weights(const qdg_layer_config& L, const float* w, void* qweight,
                                    void* scales, void* zeros, hipStream_t s) {
   const int64_t rows = L.n * L.num_experts;
+  if (L.wtype == QDG_W_NVFP4) {  // `zeros` receives the f32 tensor scale of each expert
+    uint32_t* slots = (uint32_t*)zeros;
+    const int64_t E = L.num_experts, per_expert = L.n * L.k;
+    hipLaunchKernelGGL(nvfp4_zero_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, s, slots, E);
+    const int64_t bx = (per_expert + 256 * 16 - 1) / (256 * 16);
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)(bx < 1024 ? bx : 1024), (unsigned)E), dim3(256), 0, s, w,
+                       per_expert, slots);
+    hipLaunchKernelGGL(nvfp4_scale_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, s, slots, E);
+    const int64_t blocks = rows * (L.k / 16);
+    hipLaunchKernelGGL(nvfp4_quantize_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, s, w,
+                       (uint8_t*)qweight, (uint8_t*)scales, (const float*)zeros, (int64_t)L.n, (int64_t)L.k, blocks);
+    return hipGetLastError();
+  }
   int group = L.wtype == QDG_W_INT8 ? (int)L.k : L.wtype == QDG_W_MXFP4 ? 32 : L.group_size;
   const int64_t threads = rows * (L.k / group);
   const int bs = 256;

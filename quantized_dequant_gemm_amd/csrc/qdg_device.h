@@ -153,6 +153,32 @@ __device__ __forceinline__ T ldg_nt(const T* p) {
   return __builtin_nontemporal_load(p);
 }
 
+// OCP E4M3 ("fn") encoding of a finite value with |v| <= 448, RNE; the sign
+// of zero is kept. Written from the format definition: bias 7, 3 mantissa
+// bits, exponent field 0 subnormal (units of 2^-9).
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t sign = __builtin_signbit(v) ? 0x80u : 0u;
+  const float a = fabsf(v);
+  const uint32_t u = __builtin_bit_cast(uint32_t, a);
+  const int e = (int)(u >> 23) - 127;
+  uint32_t code;
+  if (e < -6) {
+    code = (uint32_t)rintf(a * 512.0f);  // exact scaling; 8 becomes the min normal
+  } else {
+    const uint32_t mant = u & 0x7FFFFFu;
+    uint32_t m = mant >> 20;
+    const uint32_t rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
+    int ee = e;
+    if (m == 8) {
+      m = 0;
+      ++ee;
+    }
+    code = ((uint32_t)(ee + 7) << 3) | m;
+  }
+  return code | sign;
+}
+
 // NVFP4 weights: OCP E4M3 block-scale code -> its exact fp32 value (the NaN
 // codes are mapped away by preprocess), and two E2M1 codes (byte SEL of d,
 // even k in the low nibble) times that scale -> a bf16 pair. The products are

@@ -259,7 +259,8 @@ def test_nvfp4_layer_validation():
     n = q.qdg_preprocess_query(layer)
     w = q.StdWeights(qweight=0x1000, scales=0x2000, zeros=None, tensor_scale=None)
     assert _status(q.qdg_preprocess, layer, w, 0x10000, n, 0) == q.QDG_ERR_INVALID_ARG
-    assert _status(q.qdg_quantize_weights, layer, 0x1000, 0x2000, 0x3000, None, 0) == q.QDG_ERR_UNSUPPORTED
+    # the producer needs a buffer for the tensor scales (passed as `zeros`)
+    assert _status(q.qdg_quantize_weights, layer, 0x1000, 0x2000, 0x3000, None, 0) == q.QDG_ERR_INVALID_ARG
     # packed size: 1 KiB of codes and 128 bytes of scale records per 16 x 128 unit, plus the tensor scale
     units = 7 * 2
     assert n == ((units * 1024 + 255) // 256 * 256 + 256 + units * 128 + 255) // 256 * 256

@@ -152,3 +152,24 @@ def test_nvfp4_moe(qdg, per_pair, bm):
     torch.cuda.synchronize()
     assert not torch.isnan(y).any()
     assert metrics.rel_frob(H.to_f64(y), y64) <= 5e-5
+
+
+@pytest.mark.parametrize("n,k,e", [(200, 512, 1), (64, 256, 3)])
+def test_nvfp4_device_quantizer_matches_oracle(qdg, n, k, e):
+    # the library's NVFP4 producer takes the same binary32 decisions as the
+    # oracle's quantizer: codes, block scales and tensor scales bit for bit
+    w = np.stack([synth.weights_f32(n, k, workload_id=10, salt=900 + i) for i in range(e)])
+    if e > 1:
+        w[1] = 0.0  # an all-zero expert: tensor scale 1, zero codes and scales
+    layer = q.layer_nvfp4(n, k, num_experts=e)
+    qw = torch.empty((e, n, k // 2), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((e, n, k // 16), dtype=torch.uint8, device="cuda")
+    ts = torch.empty(e, dtype=torch.float32, device="cuda")
+    w_dev = H.dev(w)
+    q.qdg_quantize_weights(layer, w_dev.data_ptr(), qw.data_ptr(), sc.data_ptr(), ts.data_ptr(), q.current_stream())
+    torch.cuda.synchronize()
+    for i in range(e):
+        codes, s, t = quant.quantize_nvfp4(w[i])
+        assert ts[i].item() == float(t)
+        assert np.array_equal(sc[i].cpu().numpy(), s)
+        assert np.array_equal(qw[i].cpu().numpy(), codecs.pack_nibbles(codes))
