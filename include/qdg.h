@@ -112,7 +112,9 @@ typedef struct qdg_layer_config {
 } qdg_layer_config;
 
 /* Compute config: which computation. kind DENSE or MOE (MoE: W4A16 with
-   INT4 symmetric weights, W8A8, W4A8-INT8, W4A8-MXFP4, W4A4-MXFP4). batch_invariant = 1 makes row m of Y bitwise independent of M and
+   INT4 symmetric weights, W8A8, W4A8-INT8, W4A8-MXFP4, W4A4-MXFP4, W8A16,
+   W4A16-NVFP4; 128-row MoE blocks: W4A16, and W8A16 / W4A16-NVFP4 without
+   an epilogue). batch_invariant = 1 makes row m of Y bitwise independent of M and
    of the other rows (one fixed reduction order for every M). top_k: MoE
    slots per token. */
 typedef struct qdg_compute_config {

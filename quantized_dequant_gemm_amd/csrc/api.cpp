@@ -533,7 +533,7 @@ qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes) {
   if (M < 0) return fail(QDG_ERR_INVALID_ARG, "M < 0");
   const Choice c = choose(*plan, M > 0 ? M : 1);
   int64_t rowsum = (int64_t)c.rowsum_bytes;
-  if (plan->compute.kind == QDG_KIND_MOE && plan->fmt == FMT_W4A16) {
+  if (plan->compute.kind == QDG_KIND_MOE && (plan->fmt == FMT_W4A16 || plan->fmt == FMT_W8A16)) {
     // MoE: room for the row sums of 128-row blocks (the largest block size)
     const int64_t cap =
         align_up((M > 0 ? M : 1) * plan->compute.top_k + plan->layer.num_experts * 127, 128);
@@ -567,12 +567,25 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   const bool silu = plan.compute.epilogue == QDG_EPI_SILU_MUL;  // weight streaming has no such epilogue
   c.ws = block_m == 16 && !plan.compute.batch_invariant && !silu && ws_pinned;
   if (plan.fmt != FMT_W4A16) {
-    // every other format: the streaming family, block_m / 16 row tiles
-    if (block_m > 64)
-      return fail(QDG_ERR_UNSUPPORTED, "grouped MoE of %s uses block_m 16, 32 or 64", fmt_name(plan.fmt, plan.layer));
+    // every other format: the streaming family, block_m / 16 row tiles; the
+    // other bf16-activation formats (NVFP4, W8A16) also run 128-row blocks in
+    // the LDS-tiled family (plain output only)
+    const bool tiled = block_m == 128 && (plan.fmt == FMT_NVFP4 || plan.fmt == FMT_W8A16) && !silu &&
+                       !plan.compute.batch_invariant;
+    if (block_m > 64 && !tiled)
+      return fail(QDG_ERR_UNSUPPORTED, "grouped MoE of %s uses block_m 16, 32 or 64%s", fmt_name(plan.fmt, plan.layer),
+                  plan.fmt == FMT_NVFP4 || plan.fmt == FMT_W8A16 ? " (128 without an epilogue)" : "");
     c.ws = c.tile = c.qtile = false;
     c.sc = StreamCfg{block_m / 16, 2, 4, 1};
     c.rowsum_bytes = 0;
+    if (tiled) {
+      const int64_t a_rows = a_per_pair ? rows : T;
+      if ((double)a_rows * (double)plan.layer.k * 2.0 >= 4294967296.0)
+        return fail(QDG_ERR_UNSUPPORTED, "A of %lld rows is too large for 128-row MoE blocks", (long long)a_rows);
+      c.tile = true;
+      c.tc = TileCfg{128, 256, 8};
+      if (plan.fmt == FMT_W8A16) c.rowsum_bytes = (size_t)c.grid_m * 128 * plan.geom.groups * 4;
+    }
     *out = c;
     return QDG_OK;
   }

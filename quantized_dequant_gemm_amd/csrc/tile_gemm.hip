@@ -386,8 +386,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   // sums); waiting for the count to drop to this leaves the next stage in
   // flight
   constexpr int VM_NEXT = A_PER_WAVE + (BN / 16) * (UB / 1024) / NW + (W8 ? 0 : 1) + (NV ? 0 : 1);
-  static_assert(!NV || (M32 && !MOE), "NVFP4 runs the 64 x 64 wave tiles of dense layers");
-  static_assert(!W8 || (M32 && !MOE && !NV), "W8A16 runs the 64 x 64 wave tiles of dense layers");
+  static_assert(!NV || M32, "NVFP4 runs the 64 x 64 wave tiles");
+  static_assert(!W8 || (M32 && !NV), "W8A16 runs the 64 x 64 wave tiles");
   static_assert(NS == 2 || NS == 3, "two or three stages");
   // The stages are separate LDS objects (not one dynamic array) so that the
   // compiler can tell a copy into one stage from a read of another: reads of
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   const int groups = p.groups;
   // SiLU*mul (MoE gate+up): 16 stage tiles = 8 gate + 8 up tiles, i.e. 8
   // output tiles per workgroup
-  const bool silu = MOE && p.epi == QDG_EPI_SILU_MUL;
+  const bool silu = MOE && !NV && !W8 && p.epi == QDG_EPI_SILU_MUL;  // W4A16 only
   static_assert(!MOE || BN == 256, "the SiLU*mul pairing assumes 16 stage tiles");
   const int wg_tile0 = silu ? nb * (BN / 32) : nb * (BN / 16);
 
@@ -726,9 +726,12 @@ bool tile_cfg_supported(Format f, const TileCfg& c) {
 hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const GemmArgs& a, int m_blocks,
                        hipStream_t s) {
   if (!tile_cfg_supported(f, c)) return hipErrorInvalidValue;
-  if (f == FMT_NVFP4) return moe ? hipErrorInvalidValue : launch_tile_cfg<false, 2, 4, 64, false, true>(a, m_blocks, a.split, s);
+  if (f == FMT_NVFP4)
+    return moe ? launch_tile_cfg<false, 2, 4, 64, true, true>(a, m_blocks, a.split, s)
+               : launch_tile_cfg<false, 2, 4, 64, false, true>(a, m_blocks, a.split, s);
   if (f == FMT_W8A16)
-    return moe ? hipErrorInvalidValue : launch_tile_cfg<false, 2, 4, 64, false, false, true>(a, m_blocks, a.split, s);
+    return moe ? launch_tile_cfg<false, 2, 4, 64, true, false, true>(a, m_blocks, a.split, s)
+               : launch_tile_cfg<false, 2, 4, 64, false, false, true>(a, m_blocks, a.split, s);
 #define QDG_T(ASYM_, WM_, WN_, WTM_, MOE_)                                                 \
   if (asym == ASYM_ && c.bm == WM_ * WTM_ && c.waves == WM_ * WN_ && moe == MOE_)         \
     return launch_tile_cfg<ASYM_, WM_, WN_, WTM_, MOE_>(a, m_blocks, a.split, s);

@@ -266,11 +266,17 @@ def test_nvfp4_layer_validation():
     assert n == ((units * 1024 + 255) // 256 * 256 + 256 + units * 128 + 255) // 256 * 256
 
 
-def test_moe_128_row_blocks_are_w4a16_only():
-    # the other formats' grouped GEMMs run 16-, 32- or 64-row blocks
-    for layer in (q.layer_nvfp4(256, 256, num_experts=4), q.layer_w8a16(256, 256, num_experts=4),
-                  q.layer_w4a8(256, 256, num_experts=4)):
+def test_moe_128_row_blocks():
+    # 128-row blocks run the LDS-tiled family for the bf16-activation formats
+    # (NVFP4 and W8A16 with plain output only); the 8-bit-activation formats
+    # run 16-, 32- or 64-row blocks
+    for layer in (q.layer_nvfp4(256, 256, num_experts=4), q.layer_w8a16(256, 256, num_experts=4)):
         p = q.qdg_plan_create(layer, q.moe(2))
-        with pytest.raises(q.QdgError):
-            q.qdg_moe_describe(p, 8, 128)
+        assert "family=tile" in q.qdg_moe_describe(p, 8, 128)
         assert "family=stream" in q.qdg_moe_describe(p, 8, 64)
+        ps = q.qdg_plan_create(layer, q.moe(2, epilogue=q.QDG_EPI_SILU_MUL))
+        with pytest.raises(q.QdgError):
+            q.qdg_moe_describe(ps, 8, 128)
+    p = q.qdg_plan_create(q.layer_w4a8(256, 256, num_experts=4), q.moe(2))
+    with pytest.raises(q.QdgError):
+        q.qdg_moe_describe(p, 8, 128)

@@ -122,7 +122,7 @@ def test_nvfp4_decode_layer_shape(qdg):
     assert err <= 2e-3, err
 
 
-@pytest.mark.parametrize("per_pair,bm", [(0, 16), (1, 32)])
+@pytest.mark.parametrize("per_pair,bm", [(0, 16), (1, 32), (0, 128), (1, 128)])
 def test_nvfp4_moe(qdg, per_pair, bm):
     E, top_k, t = 4, 2, 40
     n, k = 96, 256

@@ -79,8 +79,9 @@ def test_w8a16_split_k(qdg, split):
     assert metrics.rel_frob(H.to_f64(y), ref.gemm_w8a16(a, qw, sw)) <= 5e-5
 
 
-def test_w8a16_moe(qdg):
-    E, top_k, t, bm = 4, 2, 40, 16
+@pytest.mark.parametrize("bm", [16, 128])
+def test_w8a16_moe(qdg, bm):
+    E, top_k, t = 4, 2, 40
     n, k = 96, 256
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=5), top_k)
     qs = [quant.quantize_int8_per_channel(synth.weights_f32(n, k, workload_id=9, salt=700 + e)) for e in range(E)]
