@@ -7,16 +7,20 @@ scales, bf16 activations, bf16 output) at its two projection shapes
 HBM. Small-M cases rotate over enough packed weight copies to defeat the
 256 MB last-level cache, so their weights really stream from HBM.
 
-Prints one JSON line. `value` is the step's algorithmic TFLOP/s; `roofline`
-describes the kernel that dominates the step's time, `roofline_m16` the
-HBM-bound M=16 case (also as a fraction of `hbm_copy_gbs`, the box's measured
-device-to-device copy rate), `cases` every launch, `autotuned` each case
-again with a plan tuned per M range (qdg_plan_autotune) next to the
-heuristic plan, `jit` the hipRTC compile time of one streaming-family
-instance and its kernel time next to the ahead-of-time instance;
-`cpu_baseline` times the fp64 CPU oracle over the same workload once.
+Prints one compact JSON line last on stdout: `value` is the step's
+algorithmic TFLOP/s; `roofline` describes the kernel that dominates the
+step's time, `roofline_m16` the HBM-bound M=16 cases (also as a fraction of
+`hbm_copy_gbs`, the box's measured device-to-device copy rate), and
+`cpu_baseline` the fp64 CPU oracle timed on a bounded sample of the same
+workload. The full record (`cases`: every launch of the step; `autotuned`:
+each case again with a plan tuned per M range next to the heuristic plan;
+`jit`: the hipRTC compile time of one streaming-family instance; `rows`: the
+other hot-path rows at their own shapes) goes to the JSON file named by
+--detail (default gpurun_out/bench_detail.json), and one progress line per
+measurement goes to stderr.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-rows] [--no-autotune] [--no-jit]
+                    [--detail PATH]
 """
 
 import argparse
@@ -557,30 +561,99 @@ def rows_leg(reps=30):
     return out
 
 
+def _blas_info():
+    """The BLAS numpy calls, as the BLAS itself reports it (vendor, version,
+    thread count)."""
+    try:
+        import threadpoolctl
+        for d in threadpoolctl.threadpool_info():
+            if d.get("user_api") == "blas":
+                return dict(vendor=d.get("internal_api"), version=d.get("version"), threads=d.get("num_threads"),
+                            threading_layer=d.get("threading_layer"))
+    except Exception as e:  # the BLAS still runs; only its report is missing
+        return dict(vendor="unknown", error=str(e))
+    return dict(vendor="unknown")
+
+
+def _oracle_pass(cases):
+    """One untuned pass of the fp64 oracle over `cases` (each: dequantize the
+    layer, then the GEMM). Returns (seconds, flops, dequant seconds)."""
+    from oracle import ref
+    t_all = t_deq = 0.0
+    fl = 0
+    for (qv, s, a, m, n, k) in cases:
+        t0 = time.perf_counter()
+        w64 = ref.dequant_int4_sym(qv, s)
+        t1 = time.perf_counter()
+        ref.gemm_w4a16(a, w64)
+        t2 = time.perf_counter()
+        t_all += t2 - t0
+        t_deq += t1 - t0
+        fl += alg_flops(m, n, k)
+    return t_all, fl, t_deq
+
+
 def cpu_leg():
-    """The fp64 oracle, untuned, on a bounded sample of the step: both
-    projection shapes over the whole M sweep (dequantize the layer, then the
-    GEMM), about 10-30 s of host work."""
+    """The fp64 oracle, untuned, on the host cores: the whole step (both
+    projection shapes, M in the sweep; dequantize the layer, then the GEMM)
+    three times, the median reported, about 10-20 s of host work; then the
+    tiny W4A16 workload and the M=16 cases on one BLAS thread."""
+    import statistics
     import numpy as np
     import synth
     from oracle import quant, ref
 
     cores = len(os.sched_getaffinity(0))
-    flops = 0
-    elapsed = 0.0
+    blas = _blas_info()
+    cases = []
     for (k, n) in SHAPES:
         w = synth.weights_f32(n, k, workload_id=1)
         qv, s = quant.quantize_int4_sym(w)
+        del w
         for m in M_SWEEP:
-            a = synth.activations_bf16_bits(m, k, workload_id=1, salt=m)
+            cases.append((qv, s, synth.activations_bf16_bits(m, k, workload_id=1, salt=m), m, n, k))
+    runs = [_oracle_pass(cases) for _ in range(3)]
+    secs = [r[0] for r in runs]
+    med = statistics.median(secs)
+    flops = runs[0][1]
+    out = dict(value=round(flops / med / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+               sample="fp64 dequantize + BLAS GEMM of the dense W4A16 layer, both shapes, "
+                      "M in {1,16,128,1024,8192}: the whole step, median of 3 runs",
+               seconds_median=round(med, 3), seconds_runs=[round(x, 3) for x in secs],
+               dequant_seconds_median=round(statistics.median(r[2] for r in runs), 3),
+               blas=blas)
+    # one BLAS thread: the tiny asymmetric uint4 workload and the M=16 cases
+    one = {}
+    try:
+        import threadpoolctl
+        limiter = threadpoolctl.threadpool_limits(limits=1, user_api="blas")
+    except Exception:
+        limiter = None
+    try:
+        m, k, n = 16, 1024, 512
+        a = synth.activations_bf16_bits(m, k, workload_id=0)
+        qv, s, z = quant.quantize_uint4_asym(synth.weights_f32(n, k, workload_id=0))
+        ts = []
+        for _ in range(3):
             t0 = time.perf_counter()
-            w64 = ref.dequant_int4_sym(qv, s)
-            ref.gemm_w4a16(a, w64)
-            elapsed += time.perf_counter() - t0
-            flops += alg_flops(m, n, k)
-    return dict(value=round(flops / elapsed / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
-                sample="fp64 dequantize + BLAS GEMM of the dense W4A16 layer, both shapes, M in {1,16,128,1024,8192} (the whole step, once)",
-                seconds=round(elapsed, 2), blas_threads=os.environ.get("OMP_NUM_THREADS", "default"))
+            ref.gemm_w4a16(a, ref.dequant_uint4_asym(qv, s, z))
+            ts.append(time.perf_counter() - t0)
+        t = statistics.median(ts)
+        one["tiny_M16_K1024_N512"] = dict(seconds=round(t, 5), gflops=round(alg_flops(m, n, k) / t / 1e9, 3))
+        for (qv, s, a, m, n, k) in cases:
+            if m != 16:
+                continue
+            rs = [_oracle_pass([(qv, s, a, m, n, k)]) for _ in range(3)]
+            t = statistics.median(r[0] for r in rs)
+            one[f"M16_K{k}_N{n}"] = dict(seconds=round(t, 4),
+                                         dequant_seconds=round(statistics.median(r[2] for r in rs), 4),
+                                         gflops=round(alg_flops(m, n, k) / t / 1e9, 3))
+        one["blas_threads"] = _blas_info().get("threads")
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+    out["one_thread"] = one
+    return out
 
 
 def main():
@@ -594,6 +667,8 @@ def main():
                     help="skip the run-time compilation measurement")
     ap.add_argument("--no-autotune", dest="autotune", action="store_false",
                     help="skip the autotuned-plan comparison of the dense sweep")
+    ap.add_argument("--detail", default=os.path.join(ROOT, "gpurun_out", "bench_detail.json"),
+                    help="file for the full record (every case, autotuned, jit, rows); '' for none")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 256 MiB device to device once (the known-size reference that scales "
                          "HBM byte counters in a profiler run)")
@@ -603,6 +678,13 @@ def main():
               "(sharding is described, not built). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     g = gpu_leg(args)
+    detail = dict(cases=g["cases"], hbm_copy_gbs=g["hbm_copy_gbs"])
+    if g["autotuned"]:
+        detail["autotuned"] = g["autotuned"]
+    if g["jit"]:
+        detail["jit"] = g["jit"]
+    if not args.no_rows:
+        detail["rows"] = rows_leg()
     line = {
         "metric": METRIC, "value": round(g["value"], 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(g["ms_per_step"], 4),
@@ -612,17 +694,15 @@ def main():
                                "(K,N) in {(4096,14336),(14336,4096)}, M in {1,16,128,1024,8192}",
                    "launches_per_step": len(g["cases"])},
         "roofline": g["roofline"], "roofline_m16": g["roofline_m16"], "hbm_copy_gbs": g["hbm_copy_gbs"],
-        "cases": g["cases"],
     }
-    if g["autotuned"]:
-        line["autotuned"] = g["autotuned"]
-    if g["jit"]:
-        line["jit"] = g["jit"]
-    if not args.no_rows:
-        line["rows"] = rows_leg()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_leg()
-    print(json.dumps(line), flush=True)
+    line["detail"] = os.path.relpath(args.detail, ROOT) if args.detail else None
+    if args.detail:
+        os.makedirs(os.path.dirname(os.path.abspath(args.detail)), exist_ok=True)
+        with open(args.detail, "w") as f:
+            json.dump(dict(line, **detail), f, indent=1)
+    print(json.dumps(line, separators=(",", ":")), flush=True)
 
 
 if __name__ == "__main__":

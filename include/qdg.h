@@ -176,6 +176,30 @@ typedef struct qdg_std_weights {
 
 typedef struct qdg_plan qdg_plan;
 
+/* Input flags: bits that qdg_preprocess and qdg_moe_align OR into an
+   optional caller-owned device status word (uint32_t, 4-byte aligned) when
+   they meet input the standard format does not allow. The call still
+   completes and its outputs are defined (noted per flag); a caller that
+   passes the word zeroes it beforehand and reads it after the stream has
+   run. The library never clears it, so one word can collect the flags of
+   several calls. Concentrating validation at the shared interface and
+   rejecting visibly is the pages' contract ("vLLM Humming: why shared
+   quantization still needs specialized kernels", section "The architectural
+   gain is a smaller maintenance surface"). */
+enum {
+  QDG_FLAG_BAD_SCALE = 1u,       /* a reserved or non-finite scale: E8M0 code
+                                    255, an E4M3 NaN code (0x7F, 0xFF), a
+                                    non-finite f16 / f32 scale or NVFP4 tensor
+                                    scale. Packed as the largest finite scale
+                                    of its sign (E8M0 254, E4M3 +-448); a
+                                    non-finite f16 / f32 scale is packed as it is */
+  QDG_FLAG_BAD_ZERO_POINT = 2u,  /* a UINT4 zero point above 15; packed
+                                    modulo 128 */
+  QDG_FLAG_BAD_EXPERT_ID = 4u    /* a top-k id outside [0, E); the pair is
+                                    left out of every expert block, so its
+                                    output row is never written */
+};
+
 /* Library identity: "qdg <version> gfx950 layout <QDG_LAYOUT_VERSION>". */
 const char* qdg_version(void);
 
@@ -189,16 +213,19 @@ qdg_status qdg_validate_layer(const qdg_layer_config* layer);
    layer, all experts included. */
 qdg_status qdg_preprocess_query(const qdg_layer_config* layer, size_t* packed_bytes);
 
-/* Preprocess (once per layer, not part of steady-state timing): validates
-   the layer, pads n to a multiple of 16 and rewrites the standard-format
-   weights into the gfx950 MFMA fragment layout of the target kernels.
-   `packed` (>= qdg_preprocess_query bytes, 256-byte aligned) is written
-   entirely; the standard-format buffers are only read. MXFP4 scale code 255
-   and the NVFP4 E4M3 NaN codes are not checked on the device: preprocess
-   maps them to the largest finite scale of their sign, so callers validate
-   scale input on the host when it is untrusted. */
+/* Preprocess (once per layer, not part of steady-state timing; the pages'
+   step that checks parameters, pads dimensions and repacks the standard
+   format for the target kernel: kinachrichten, "Wie die Architektur
+   funktioniert"): validates the layer, pads n to a multiple of 16 and
+   rewrites the standard-format weights into the gfx950 MFMA fragment layout
+   of the target kernels. `packed` (>= qdg_preprocess_query bytes, 256-byte
+   aligned) is written entirely; the standard-format buffers are only read.
+   Scale and zero-point values are checked on the device while they are
+   packed: `status` (may be NULL; device, 4-byte aligned, caller-owned and
+   caller-zeroed) receives QDG_FLAG_BAD_SCALE / QDG_FLAG_BAD_ZERO_POINT for
+   the values the standard format forbids (see the flags). */
 qdg_status qdg_preprocess(const qdg_layer_config* layer, const qdg_std_weights* weights,
-                          void* packed, size_t packed_bytes, void* stream);
+                          void* packed, size_t packed_bytes, uint32_t* status, void* stream);
 
 /* Quantize float32 weights [E][n][k] (device) into the standard format of
    `layer` (a producer of the standard format). Decisions are taken in
@@ -323,17 +350,23 @@ qdg_status qdg_plan_autotune_reset(qdg_plan* plan);
 qdg_status qdg_moe_align_capacity(int64_t T, int32_t top_k, int32_t num_experts, int32_t block_m,
                                   int64_t* capacity);
 
-/* Expert sort for the grouped GEMM. topk_ids i32 [T][top_k] (values in
-   [0, E)) -> pairs (flat index t*top_k+j) sorted by expert, ascending flat
-   index within an expert, each expert padded to a multiple of block_m with
-   the sentinel T*top_k; experts with no pair get no block.
+/* Expert sort for the grouped GEMM (the pages' grouped MoE path, jetabc,
+   "跑得有多快", over tokens that each activate a few of the stored experts,
+   kinachrichten, "Warum quantisierte Kernel wichtig sind"; the sort order
+   is this library's reading). topk_ids i32 [T][top_k] (values in [0, E))
+   -> pairs (flat index t*top_k+j) sorted by expert, ascending flat index
+   within an expert, each expert padded to a multiple of block_m with the
+   sentinel T*top_k; experts with no pair get no block.
    Outputs (capacity from qdg_moe_align_capacity): sorted_ids i32 [capacity]
    (entries past num_padded hold the sentinel), block_expert i32
    [capacity/block_m] (-1 past the last block), num_padded i32 [1].
-   block_m in {16, 32, 64, 128}; 1 <= top_k <= 32; T*top_k <= 2^20. */
+   block_m in {16, 32, 64, 128}; 1 <= E <= 1024; 1 <= top_k <= 32;
+   T*top_k <= 2^20. An id outside [0, E) is left out (its pair row of a
+   later qdg_moe_gemm is not written) and sets QDG_FLAG_BAD_EXPERT_ID in
+   `status` (may be NULL; device, caller-owned and caller-zeroed). */
 qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t num_experts,
                          int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
-                         int32_t* num_padded, void* stream);
+                         int32_t* num_padded, uint32_t* status, void* stream);
 
 /* Grouped MoE GEMM: for every real entry i of sorted_ids in block b,
    row i of Y = A[r] * dequant(W_e)^T with e = block_expert[b] and

@@ -25,6 +25,7 @@ QDG_A_BF16, QDG_A_INT8, QDG_A_FP8E4M3, QDG_A_MXFP4 = range(4)
 QDG_O_BF16, QDG_O_F32, QDG_O_I32 = range(3)
 QDG_KIND_DENSE, QDG_KIND_MOE = range(2)
 QDG_EPI_NONE, QDG_EPI_SILU_MUL = range(2)
+QDG_FLAG_BAD_SCALE, QDG_FLAG_BAD_ZERO_POINT, QDG_FLAG_BAD_EXPERT_ID = 1, 2, 4
 
 STATUS_NAMES = {0: "QDG_OK", 1: "QDG_ERR_INVALID_ARG", 2: "QDG_ERR_UNSUPPORTED", 3: "QDG_ERR_MISALIGNED",
                 4: "QDG_ERR_WORKSPACE", 5: "QDG_ERR_HIP"}
@@ -85,7 +86,7 @@ def load():
         "qdg_last_error": (ctypes.c_char_p, []),
         "qdg_validate_layer": (I32, [P]),
         "qdg_preprocess_query": (I32, [P, P]),
-        "qdg_preprocess": (I32, [P, P, P, SZ, P]),
+        "qdg_preprocess": (I32, [P, P, P, SZ, P, P]),
         "qdg_quantize_weights": (I32, [P, P, P, P, P, P]),
         "qdg_quantize_act": (I32, [P, P, I64, P, P, P]),
         "qdg_plan_create": (I32, [P, P, P, P]),
@@ -95,7 +96,7 @@ def load():
         "qdg_moe_describe": (ctypes.c_int, [P, I64, I32, ctypes.c_char_p, SZ]),
         "qdg_gemm": (I32, [P, P, P, P, P, I64, P, SZ, P]),
         "qdg_moe_align_capacity": (I32, [I64, I32, I32, I32, P]),
-        "qdg_moe_align": (I32, [P, I64, I32, I32, I32, P, P, P, P]),
+        "qdg_moe_align": (I32, [P, I64, I32, I32, I32, P, P, P, P, P]),
         "qdg_moe_gemm": (I32, [P, P, P, P, P, P, P, I64, I32, I32, P, P, SZ, P]),
         "qdg_moe_combine": (I32, [P, P, I64, I32, I64, P, I32, P]),
         "qdg_plan_autotune": (I32, [P, P, P, P, P, I64, P, SZ, I32, P, P, P]),
@@ -144,8 +145,10 @@ def qdg_preprocess_query(layer):
     return out.value
 
 
-def qdg_preprocess(layer, weights, packed, packed_bytes, stream=0):
-    _check(load().qdg_preprocess(ctypes.byref(layer), ctypes.byref(weights), packed, packed_bytes, stream))
+def qdg_preprocess(layer, weights, packed, packed_bytes, stream=0, status=None):
+    """status: optional device pointer to a caller-zeroed uint32 that receives QDG_FLAG_* bits."""
+    _check(load().qdg_preprocess(ctypes.byref(layer), ctypes.byref(weights), packed, packed_bytes, status,
+                                 stream))
 
 
 def qdg_quantize_weights(layer, w, qweight, scales, zeros=None, stream=0):
@@ -214,9 +217,11 @@ def qdg_moe_align_capacity(T, top_k, num_experts, block_m):
     return out.value
 
 
-def qdg_moe_align(topk_ids, T, top_k, num_experts, block_m, sorted_ids, block_expert, num_padded, stream=0):
+def qdg_moe_align(topk_ids, T, top_k, num_experts, block_m, sorted_ids, block_expert, num_padded, stream=0,
+                  status=None):
+    """status: optional device pointer to a caller-zeroed uint32 that receives QDG_FLAG_BAD_EXPERT_ID."""
     _check(load().qdg_moe_align(topk_ids, T, top_k, num_experts, block_m, sorted_ids, block_expert,
-                                num_padded, stream))
+                                num_padded, status, stream))
 
 
 def qdg_moe_gemm(plan, A, a_scales, packed, sorted_ids, block_expert, num_padded, T, block_m, a_per_pair, Y,

@@ -432,7 +432,7 @@ qdg_status qdg_preprocess_query(const qdg_layer_config* layer, size_t* packed_by
 }
 
 qdg_status qdg_preprocess(const qdg_layer_config* layer, const qdg_std_weights* w, void* packed,
-                          size_t packed_bytes, void* stream) {
+                          size_t packed_bytes, uint32_t* status, void* stream) {
   qdg_status st = validate_layer(layer);
   if (st != QDG_OK) return st;
   if (!w || !w->qweight || !w->scales || !packed) return fail(QDG_ERR_INVALID_ARG, "NULL weight or packed pointer");
@@ -447,7 +447,8 @@ qdg_status qdg_preprocess(const qdg_layer_config* layer, const qdg_std_weights* 
   if (!aligned(packed, 256)) return fail(QDG_ERR_MISALIGNED, "packed buffer must be 256-byte aligned");
   if (!aligned(w->qweight, 16)) return fail(QDG_ERR_MISALIGNED, "qweight must be 16-byte aligned");
   if (!aligned(w->scales, 4)) return fail(QDG_ERR_MISALIGNED, "scales must be 4-byte aligned");
-  return hip_status(launch_preprocess(*layer, f, g, *w, packed, (hipStream_t)stream), "preprocess launch");
+  if (!aligned(status, 4)) return fail(QDG_ERR_MISALIGNED, "status must be 4-byte aligned");
+  return hip_status(launch_preprocess(*layer, f, g, *w, packed, status, (hipStream_t)stream), "preprocess launch");
 }
 
 qdg_status qdg_quantize_weights(const qdg_layer_config* layer, const float* w, void* qweight, void* scales,
@@ -956,14 +957,16 @@ qdg_status qdg_moe_align_capacity(int64_t T, int32_t top_k, int32_t E, int32_t b
 }
 
 qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int32_t block_m,
-                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded, void* stream) {
+                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded, uint32_t* status,
+                         void* stream) {
   int64_t cap = 0;
   qdg_status st = qdg_moe_align_capacity(T, top_k, E, block_m, &cap);
   if (st != QDG_OK) return st;
   if (!sorted_ids || !block_expert || !num_padded) return fail(QDG_ERR_INVALID_ARG, "NULL output");
   if (T > 0 && !topk_ids) return fail(QDG_ERR_INVALID_ARG, "topk_ids is NULL");
+  if (!aligned(status, 4)) return fail(QDG_ERR_MISALIGNED, "status must be 4-byte aligned");
   return hip_status(launch_moe_align(topk_ids, T, top_k, E, block_m, cap, sorted_ids, block_expert, num_padded,
-                                     (hipStream_t)stream),
+                                     status, (hipStream_t)stream),
                     "moe_align launch");
 }
 

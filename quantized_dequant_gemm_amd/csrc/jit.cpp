@@ -8,9 +8,13 @@
 // the same source text (embedded in the library when it is built), loads it,
 // and the plan then launches that code object. Compiled code objects can be
 // kept in a cache directory under a key derived from the instance, the
-// target and the source text, so a later process loads instead of compiling.
+// target, the compiler version and the source text, so a later process loads
+// instead of compiling. One cache entry is one file (a header line with the
+// kernel's mangled name, then the code object), written under a per-process
+// temporary name and renamed into place, so readers never see half an entry.
 #include <hip/hip_runtime.h>
 #include <hip/hiprtc.h>
+#include <unistd.h>
 
 #include <chrono>
 #include <cstdio>
@@ -71,12 +75,38 @@ bool read_file(const std::string& path, std::vector<char>* out) {
 }
 
 bool write_file(const std::string& path, const std::vector<char>& data) {
-  const std::string tmp = path + ".tmp";
+  static unsigned counter = 0;
+  const std::string tmp = path + ".tmp." + std::to_string((long)getpid()) + "." + std::to_string(++counter);
   FILE* f = std::fopen(tmp.c_str(), "wb");
   if (!f) return false;
   const bool ok = std::fwrite(data.data(), 1, data.size(), f) == data.size();
-  std::fclose(f);
-  return ok && std::rename(tmp.c_str(), path.c_str()) == 0;
+  const bool closed = std::fclose(f) == 0;
+  if (ok && closed && std::rename(tmp.c_str(), path.c_str()) == 0) return true;
+  std::remove(tmp.c_str());
+  return false;
+}
+
+// Cache entry: "QDGJIT1 <name>\n" followed by the code object.
+constexpr char kEntryMagic[] = "QDGJIT1 ";
+
+std::vector<char> make_entry(const std::string& name, const std::vector<char>& code) {
+  std::vector<char> out(kEntryMagic, kEntryMagic + sizeof kEntryMagic - 1);
+  out.insert(out.end(), name.begin(), name.end());
+  out.push_back('\n');
+  out.insert(out.end(), code.begin(), code.end());
+  return out;
+}
+
+// Splits an entry into name and code; false for anything malformed.
+bool parse_entry(const std::vector<char>& in, std::string* name, std::vector<char>* code) {
+  const size_t m = sizeof kEntryMagic - 1;
+  if (in.size() <= m || std::memcmp(in.data(), kEntryMagic, m) != 0) return false;
+  size_t e = m;
+  while (e < in.size() && in[e] != '\n') ++e;
+  if (e == m || e >= in.size() - 1) return false;
+  name->assign(in.begin() + m, in.begin() + e);
+  code->assign(in.begin() + e + 1, in.end());
+  return true;
 }
 
 }  // namespace
@@ -97,6 +127,11 @@ JitResult jit_stream_kernel(Format f, bool asym, bool raw, const StreamCfg& c, b
   uint64_t h = 1469598103934665603ull;
   h = fnv1a(expr, std::strlen(expr), h);
   for (const char* o : opts) h = fnv1a(o, std::strlen(o), h);
+  int rtc_major = 0, rtc_minor = 0;
+  hiprtcVersion(&rtc_major, &rtc_minor);
+  char ver[32];
+  std::snprintf(ver, sizeof ver, "hiprtc %d.%d", rtc_major, rtc_minor);
+  h = fnv1a(ver, std::strlen(ver), h);
   const char* texts[] = {kJitStreamSrc, kJitDeviceHdr, kJitInternalHdr, kJitQdgHdr};
   for (const char* t : texts) h = fnv1a(t, std::strlen(t), h);
   std::snprintf(r.key, sizeof r.key, "%016llx", (unsigned long long)h);
@@ -113,9 +148,10 @@ JitResult jit_stream_kernel(Format f, bool asym, bool raw, const StreamCfg& c, b
     r.from_cache = 2;
     return r;
   }
-  std::vector<char> code;
-  const std::string path = cache_dir ? std::string(cache_dir) + "/qdg-" + r.key + ".hsaco" : std::string();
-  if (cache_dir && read_file(path, &code)) {
+  std::vector<char> code, entry;
+  std::string name;
+  const std::string path = cache_dir ? std::string(cache_dir) + "/qdg-" + r.key + ".jit" : std::string();
+  if (cache_dir && read_file(path, &entry) && parse_entry(entry, &name, &code)) {
     r.from_cache = 1;
   } else {
     auto t0 = std::chrono::steady_clock::now();
@@ -140,13 +176,19 @@ JitResult jit_stream_kernel(Format f, bool asym, bool raw, const StreamCfg& c, b
     const char* lowered = nullptr;
     hiprtcGetLoweredName(prog, expr, &lowered);
     r.lowered = lowered ? lowered : "";
+    name = r.lowered;
     size_t n = 0;
     hiprtcGetCodeSize(prog, &n);
     code.resize(n);
     hiprtcGetCode(prog, code.data());
     hiprtcDestroyProgram(&prog);
     r.compile_ms = ms_since(t0);
-    if (cache_dir) (void)write_file(path, code);  // a cache that cannot be written is skipped
+    if (name.empty()) {
+      r.error = "hipRTC returned no name for " + std::string(expr);
+      return r;
+    }
+    // a cache that cannot be written is skipped
+    if (cache_dir) (void)write_file(path, make_entry(name, code));
   }
   r.code_bytes = (int)code.size();
   auto t1 = std::chrono::steady_clock::now();
@@ -154,19 +196,6 @@ JitResult jit_stream_kernel(Format f, bool asym, bool raw, const StreamCfg& c, b
   if (hipModuleLoadData(&mod, code.data()) != hipSuccess) {
     r.error = "hipModuleLoadData failed";
     return r;
-  }
-  // the mangled name of the instance (the same in every build of this source)
-  std::string name = r.lowered;
-  if (name.empty()) {
-    // loaded from the cache: the name is stored beside the code object
-    std::vector<char> nm;
-    if (!read_file(path + ".name", &nm)) {
-      r.error = "cached code object without its kernel name";
-      return r;
-    }
-    name.assign(nm.begin(), nm.end());
-  } else if (cache_dir) {
-    (void)write_file(path + ".name", std::vector<char>(name.begin(), name.end()));
   }
   hipFunction_t fn;
   if (hipModuleGetFunction(&fn, mod, name.c_str()) != hipSuccess) {

@@ -24,7 +24,8 @@ constexpr int kMaxE = 1024;
 __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restrict__ ids, int total, int E,
                                                          int bm, int capacity, int32_t* __restrict__ sorted_ids,
                                                          int32_t* __restrict__ block_expert,
-                                                         int32_t* __restrict__ num_padded) {
+                                                         int32_t* __restrict__ num_padded,
+                                                         uint32_t* __restrict__ status) {
   __shared__ int cnt[kWaves][kMaxE];
   __shared__ int off[kMaxE + 1];
   __shared__ int scan_tmp[1024];
@@ -35,7 +36,8 @@ __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restri
   const int lo = min(total, wave * slice), hi = min(total, lo + slice);
   for (int i = lo + lane; i < hi; i += 64) {
     const int e = ids[i];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[wave][e], 1);  // out-of-range ids are dropped
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[wave][e], 1);
+    else if (status) atomicOr(status, QDG_FLAG_BAD_EXPERT_ID);  // the pair is left out
   }
   __syncthreads();
 
@@ -136,9 +138,9 @@ hipError_t launch_moe_combine(const float* y, const float* w, int64_t T, int top
 
 hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int block_m,
                             int64_t capacity, int32_t* sorted_ids, int32_t* block_expert,
-                            int32_t* num_padded, hipStream_t s) {
+                            int32_t* num_padded, uint32_t* status, hipStream_t s) {
   hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(1024), 0, s, topk_ids, (int)(T * top_k), E, block_m,
-                     (int)capacity, sorted_ids, block_expert, num_padded);
+                     (int)capacity, sorted_ids, block_expert, num_padded, status);
   return hipGetLastError();
 }
 

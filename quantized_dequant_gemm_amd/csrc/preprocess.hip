@@ -26,13 +26,24 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// Sets an input flag in the caller's status word (a vector atomic; taken
+// only on bad input, so it costs nothing on the common path).
+__device__ __forceinline__ void raise_flag(uint32_t* status, uint32_t flag) {
+  if (status) atomicOr(status, flag);
+}
+
+__device__ __forceinline__ bool finite_f32(float x) {
+  return (__builtin_bit_cast(uint32_t, x) & 0x7F800000u) != 0x7F800000u;
+}
+
 // One thread per (expert, tile, group, lane): writes the lane's 16 bytes of
 // the unit (32 bytes for int8) and, for lanes 0..15, the scale record of
 // column `lane`.
 __global__ void repack_kernel(int fmt, int wtype, const uint8_t* __restrict__ qw,
                               const void* __restrict__ scales, const uint8_t* __restrict__ zeros,
                               const float* __restrict__ tscale, uint8_t* __restrict__ packed, int64_t N, int64_t K, int64_t ntiles,
-                              int64_t groups, int64_t expert_stride, int64_t s_offset, int64_t experts) {
+                              int64_t groups, int64_t expert_stride, int64_t s_offset, int64_t experts,
+                              uint32_t* __restrict__ status) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_expert = ntiles * groups * 64;
   if (tid >= per_expert * experts) return;
@@ -73,9 +84,11 @@ __global__ void repack_kernel(int fmt, int wtype, const uint8_t* __restrict__ qw
     if (c == 0) {
       const uint16_t* sc = (const uint16_t*)scales;
       const float s = valid ? half_bits_to_float(sc[(e * N + n) * groups + g]) : 0.f;
+      if (!finite_f32(s)) raise_flag(status, QDG_FLAG_BAD_SCALE);
       if (fmt == FMT_W4A16) {
         uint32_t zq = 8;  // symmetric: q + 8 is stored, offset 128 + 8
         if (wtype == QDG_W_UINT4) zq = valid ? zeros[(e * N + n) * groups + g] : 0;
+        if (zq > 15) raise_flag(status, QDG_FLAG_BAD_ZERO_POINT);
         const uint32_t nego = 0xC300u | (zq & 0x7Fu);  // bf16 of -(128 + zq)
         u32x2_t rec = {__builtin_bit_cast(uint32_t, s), nego | (nego << 16)};
         *((u32x2_t*)sdst + unit * 16 + col) = rec;
@@ -91,7 +104,10 @@ __global__ void repack_kernel(int fmt, int wtype, const uint8_t* __restrict__ qw
     uint8_t sc = 127;
     if (valid) {
       sc = ((const uint8_t*)scales)[(e * N + n) * (K / 32) + 4 * g + c];
-      if (sc == 255) sc = 254;
+      if (sc == 255) {
+        sc = 254;
+        raise_flag(status, QDG_FLAG_BAD_SCALE);
+      }
     }
     sdst[unit * 64 + lane] = sc;
   } else if (fmt == FMT_NVFP4) {
@@ -105,19 +121,28 @@ __global__ void repack_kernel(int fmt, int wtype, const uint8_t* __restrict__ qw
     if (valid) {
       const uint8_t* sc = (const uint8_t*)scales + (e * N + n) * (K / 16) + 8 * g + 2 * c;
       uint32_t s0 = sc[0], s1 = sc[1];
+      if ((s0 & 0x7Fu) == 0x7Fu || (s1 & 0x7Fu) == 0x7Fu) raise_flag(status, QDG_FLAG_BAD_SCALE);
       if ((s0 & 0x7Fu) == 0x7Fu) s0 -= 1;
       if ((s1 & 0x7Fu) == 0x7Fu) s1 -= 1;
       rec = s0 | (s1 << 8);
     }
     ((uint16_t*)(sdst + 256))[unit * 64 + lane] = (uint16_t)rec;
-    if (unit == 0 && lane == 0) *(float*)sdst = tscale[e];
+    if (unit == 0 && lane == 0) {
+      const float ts = tscale[e];
+      if (!finite_f32(ts)) raise_flag(status, QDG_FLAG_BAD_SCALE);
+      *(float*)sdst = ts;
+    }
   } else {  // FMT_W8A8: unit = [step j][lane][16 bytes]
     for (int j = 0; j < 2; ++j) {
       u32x4_t out = {0, 0, 0, 0};
       if (valid) out = *(const u32x4_t*)(qw + (e * N + n) * K + g * 128 + 32 * c + 16 * j);
       *((u32x4_t*)(wdst + unit * kUnit8Bytes) + j * 64 + lane) = out;
     }
-    if (c == 0 && g == 0) ((float*)sdst)[tile * 16 + col] = valid ? ((const float*)scales)[e * N + n] : 0.f;
+    if (c == 0 && g == 0) {
+      const float s = valid ? ((const float*)scales)[e * N + n] : 0.f;
+      if (!finite_f32(s)) raise_flag(status, QDG_FLAG_BAD_SCALE);
+      ((float*)sdst)[tile * 16 + col] = s;
+    }
   }
 }
 
@@ -274,14 +299,14 @@ __global__ void nvfp4_quantize_kernel(const float* __restrict__ w, uint8_t* __re
 }  // namespace
 
 hipError_t launch_preprocess(const qdg_layer_config& L, Format f, const PackedGeom& g,
-                             const qdg_std_weights& w, void* packed, hipStream_t s) {
+                             const qdg_std_weights& w, void* packed, uint32_t* status, hipStream_t s) {
   const int64_t threads = g.experts * g.ntiles * g.groups * 64;
   const int bs = 256;
   const int64_t blocks = (threads + bs - 1) / bs;
   hipLaunchKernelGGL(repack_kernel, dim3((unsigned)blocks), dim3(bs), 0, s, (int)f, (int)L.wtype,
                      (const uint8_t*)w.qweight, w.scales, (const uint8_t*)w.zeros, (const float*)w.tensor_scale,
                      (uint8_t*)packed, g.n,
-                     g.k, g.ntiles, g.groups, g.expert_stride, g.s_offset, g.experts);
+                     g.k, g.ntiles, g.groups, g.expert_stride, g.s_offset, g.experts, status);
   return hipGetLastError();
 }
 

@@ -87,7 +87,7 @@ hipError_t launch_rowsum(const void* a_bf16, const int* sorted_ids, const int* n
                          float factor, float* out, hipStream_t s);
 
 hipError_t launch_preprocess(const qdg_layer_config& L, Format f, const PackedGeom& g,
-                             const qdg_std_weights& w, void* packed, hipStream_t s);
+                             const qdg_std_weights& w, void* packed, uint32_t* status, hipStream_t s);
 hipError_t launch_quantize_weights(const qdg_layer_config& L, const float* w, void* qweight,
                                    void* scales, void* zeros, hipStream_t s);
 hipError_t launch_quantize_act(int atype, const void* a, int64_t M, int64_t K, void* qa,
@@ -109,7 +109,7 @@ hipError_t launch_stream_jit(hipFunction_t fn, const StreamCfg& c, const GemmArg
 
 hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int block_m,
                             int64_t capacity, int32_t* sorted_ids, int32_t* block_expert,
-                            int32_t* num_padded, hipStream_t s);
+                            int32_t* num_padded, uint32_t* status, hipStream_t s);
 
 #endif
 

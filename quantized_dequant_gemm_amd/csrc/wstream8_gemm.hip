@@ -223,8 +223,9 @@ __global__ __launch_bounds__(512) void wsr8_kernel(const GemmArgs p) {
     const int r = 4 * c + e;
     if (r >= p.M) continue;
     float y;
+    // raw int32 output takes no scale: a_scales may be NULL then
     if constexpr (KIND == K_W8A8)
-      y = (float)acc[e] * p.a_scales[r] * sw;
+      y = RAW ? 0.f : (float)acc[e] * p.a_scales[r] * sw;
     else if constexpr (KIND == K_W4A8)
       y = RAW ? 0.f : (float)acc[e] * p.a_scales[r];
     else

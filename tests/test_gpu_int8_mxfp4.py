@@ -111,7 +111,8 @@ def _mxfp4_case(m, n, k, salt=0):
     return codes, e, ac, sa, ref.gemm_mxfp4(ac, sa, codes, e)
 
 
-@pytest.mark.parametrize("m,n,k", [(16, 2048, 7168), (16, 7168, 2048), (512, 2048, 7168), (9, 80, 256)])
+@pytest.mark.parametrize("m,n,k", [(16, 2048, 7168), (16, 7168, 2048), (512, 2048, 7168), (512, 7168, 2048),
+                                   (9, 80, 256)])
 def test_w4a8_mxfp4(qdg, m, n, k):
     codes, e, ac, sa, y64 = _mxfp4_case(m, n, k, salt=m)
     for otype in (q.QDG_O_F32, q.QDG_O_BF16):

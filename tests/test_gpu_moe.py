@@ -123,33 +123,49 @@ def test_moe_single_expert_equals_dense(qdg, bm, pin_ws):
     assert torch.equal(y, yd)
 
 
-@pytest.mark.parametrize("t,bm", [(64, 16), (512, 128)])
-def test_moe_full_size_sampled_rows(qdg, t, bm):
-    # the real MoE shape (E=256, top-8, hidden 7168, gate+up N=4096); expert
-    # weights are quantized on the device, outputs checked on sampled pairs
-    E, top_k, hid, n = 256, 8, 7168, 4096
-    layer = q.layer_w4a16(n, hid, num_experts=E)
-    qw = torch.empty((E, n, hid // 2), dtype=torch.uint8, device="cuda")
-    sc = torch.empty((E, n, hid // 128), dtype=torch.int16, device="cuda")
+@pytest.mark.parametrize("proj,t,bm", [("gate_up", 64, 16), ("gate_up", 512, 128), ("gate_up", 4096, 128),
+                                       ("down", 64, 16), ("down", 512, 32), ("down", 4096, 128)])
+def test_moe_full_size_sampled_rows(qdg, proj, t, bm):
+    # the real MoE shapes (E=256, top-8, hidden 7168, intermediate 2048):
+    # gate+up K=7168 -> N=4096 over token rows, down K=2048 -> N=7168 over
+    # pair rows; expert weights are quantized on the device, outputs checked
+    # on sampled pairs
+    E, top_k, hid, inter = 256, 8, 7168, 2048
+    n, k = (2 * inter, hid) if proj == "gate_up" else (hid, inter)
+    per_pair = proj == "down"
+    layer = q.layer_w4a16(n, k, num_experts=E)
+    qw = torch.empty((E, n, k // 2), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((E, n, k // 128), dtype=torch.int16, device="cuda")
     ids, _ = ref.route_topk(synth.router_logits(t, E), top_k)
     pairs = sorted({0, 7, 100, 257, t * top_k // 2 + 3, t * top_k - 1})
     sample_experts = sorted({int(ids.reshape(-1)[p]) for p in pairs})
     w_host = {}
     for e in range(E):
-        w = synth.device_normal_f32((n, hid), 0.02, seed=synth.seed_for(4, synth.TID_W, e))
+        w = synth.device_normal_f32((n, k), 0.02, seed=synth.seed_for(4, synth.TID_W, e + (E if per_pair else 0)))
         if e in sample_experts:
             w_host[e] = w.cpu().numpy()
-        q.qdg_quantize_weights(q.layer_w4a16(n, hid), w.data_ptr(), qw[e].data_ptr(), sc[e].data_ptr(), None,
+        q.qdg_quantize_weights(q.layer_w4a16(n, k), w.data_ptr(), qw[e].data_ptr(), sc[e].data_ptr(), None,
                                q.current_stream())
+        del w
     pk = H.Packed(layer, qw, sc)
-    x = synth.activations_bf16_bits(t, hid, workload_id=4)
-    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 0, top_k)
+    del qw, sc
+    if per_pair:
+        x = synth.moe_hidden_bf16_bits(t * top_k, k, salt=t)
+    else:
+        x = synth.activations_bf16_bits(t, k, workload_id=4)
+    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 1 if per_pair else 0, top_k)
+    fam = q.qdg_moe_describe(q.qdg_plan_create(layer, q.moe(top_k)), t, bm).split("family=")[1].split()[0]
+    assert fam == ("tile" if bm == 128 else "stream")
     xf = codecs.bf16_bits_to_f64(x)
     for p in pairs:
         e = int(ids.reshape(-1)[p])
         qv, s = quant.quantize_int4_sym(w_host[e])
-        yr = xf[p // top_k] @ ref.dequant_int4_sym(qv, s).T
-        assert metrics.rel_frob(H.to_f64(y[p]), yr) <= 2e-3
+        yr = xf[p if per_pair else p // top_k] @ ref.dequant_int4_sym(qv, s).T
+        err = metrics.rel_frob(H.to_f64(y[p]), yr)
+        print(f"MoE {proj} T={t} bm={bm} pair {p} expert {e}: rel_frob={err:.3e}")
+        assert err <= 2e-3, (p, err)
+    # every real pair row was written (the output was prefilled with NaN)
+    assert not torch.isnan(y.float()).any()
 
 
 @pytest.mark.parametrize("t,bm,inter", [(8, 16, 256), (64, 16, 144), (64, 32, 256), (300, 64, 256),
