@@ -294,6 +294,21 @@ int qdg_moe_describe(const qdg_plan* plan, int64_t T, int32_t block_m, char* buf
 qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, const void* packed,
                     void* Y, int64_t M, void* workspace, size_t ws_bytes, void* stream);
 
+/* qdg_gemm without a workspace argument, for callers that cannot allocate
+   device memory: code under HIP graph capture, tight serving loops,
+   harnesses that forbid allocation. The workspace is a fixed device array
+   of QDG_NOALLOC_SCRATCH_BYTES per GPU inside the library, held until the
+   process ends; a call whose qdg_plan_workspace(plan, M) exceeds it returns
+   QDG_ERR_WORKSPACE (use qdg_gemm with a caller workspace then). Every call
+   on one GPU shares that GPU's array, so calls that overlap on one GPU
+   (other streams or threads at the same time) race: order them on one
+   stream. No call allocates or frees device memory. The first call on a
+   device looks up that device's array address (host only, no allocation).
+   Other arguments, results and errors as for qdg_gemm. */
+#define QDG_NOALLOC_SCRATCH_BYTES (64ull << 20)
+qdg_status qdg_gemm_noalloc(const qdg_plan* plan, const void* A, const float* a_scales, const void* packed,
+                            void* Y, int64_t M, void* stream);
+
 /* Run-time compilation (the pages build each kernel instance at run time
    from its configuration: kinachrichten, "Kompilierzeiten und
    gerätespezifisches Tuning"; jetabc, "Humming 的做法", item 3). Compiles

@@ -36,7 +36,7 @@ EXPORTS = (
     "qdg_quantize_weights", "qdg_quantize_act", "qdg_plan_create", "qdg_plan_destroy", "qdg_plan_workspace",
     "qdg_plan_describe", "qdg_moe_describe", "qdg_gemm", "qdg_moe_align_capacity", "qdg_moe_align",
     "qdg_moe_gemm", "qdg_moe_combine", "qdg_plan_autotune", "qdg_plan_autotune_reset",
-    "qdg_plan_jit",
+    "qdg_plan_jit", "qdg_gemm_noalloc",
 )
 
 
@@ -95,6 +95,7 @@ def load():
         "qdg_plan_describe": (ctypes.c_int, [P, I64, ctypes.c_char_p, SZ]),
         "qdg_moe_describe": (ctypes.c_int, [P, I64, I32, ctypes.c_char_p, SZ]),
         "qdg_gemm": (I32, [P, P, P, P, P, I64, P, SZ, P]),
+        "qdg_gemm_noalloc": (I32, [P, P, P, P, P, I64, P]),
         "qdg_moe_align_capacity": (I32, [I64, I32, I32, I32, P]),
         "qdg_moe_align": (I32, [P, I64, I32, I32, I32, P, P, P, P, P]),
         "qdg_moe_gemm": (I32, [P, P, P, P, P, P, P, I64, I32, I32, P, P, SZ, P]),
@@ -209,6 +210,14 @@ def qdg_moe_describe(plan, T, block_m):
 
 def qdg_gemm(plan, A, a_scales, packed, Y, M, workspace, ws_bytes, stream=0):
     _check(load().qdg_gemm(plan.handle, A, a_scales, packed, Y, M, workspace, ws_bytes, stream))
+
+
+QDG_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def qdg_gemm_noalloc(plan, A, a_scales, packed, Y, M, stream=0):
+    """qdg_gemm on the library's own per-GPU scratch array (no workspace)."""
+    _check(load().qdg_gemm_noalloc(plan.handle, A, a_scales, packed, Y, M, stream))
 
 
 def qdg_moe_align_capacity(T, top_k, num_experts, block_m):

@@ -56,6 +56,8 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 namespace qdg {
 
+qdg_status report_error(qdg_status st, const char* msg) { return fail(st, "%s", msg); }
+
 Format format_of(const qdg_layer_config& L) {
   if (L.wtype == QDG_W_INT8) return L.atype == QDG_A_BF16 ? FMT_W8A16 : FMT_W8A8;
   if (L.wtype == QDG_W_MXFP4) return L.atype == QDG_A_MXFP4 ? FMT_W4A4 : FMT_MXFP4;

@@ -25,6 +25,10 @@ struct PackedGeom {
 };
 
 PackedGeom packed_geom(const qdg_layer_config& L, Format f);
+
+// Sets the thread's last-error message and returns st (for C-ABI entry
+// points defined outside api.cpp).
+qdg_status report_error(qdg_status st, const char* msg);
 Format format_of(const qdg_layer_config& L);
 
 // Kernel arguments shared by all GEMM kernels (passed by value).

@@ -281,3 +281,14 @@ def test_moe_128_row_blocks():
     p = q.qdg_plan_create(q.layer_w4a8(256, 256, num_experts=4), q.moe(2))
     with pytest.raises(q.QdgError):
         q.qdg_moe_describe(p, 8, 128)
+
+
+def test_noalloc_refuses_oversized_workspace_before_device_work():
+    # M = 8192 at K = 14336 with a 16-way K split needs GBs of partials: the
+    # allocation-free entry point refuses it on the host (no pointer is used)
+    layer = q.layer_w4a16(4096, 14336)
+    plan = q.qdg_plan_create(layer, q.dense(), q.TuningConfig(block_m=128, split_k=16))
+    assert q.qdg_plan_workspace(plan, 8192) > q.QDG_NOALLOC_SCRATCH_BYTES
+    assert _status(q.qdg_gemm_noalloc, plan, None, None, None, None, 8192) == q.QDG_ERR_WORKSPACE
+    assert "workspace" in q.qdg_last_error()
+    assert q.load().qdg_gemm_noalloc(None, None, None, None, None, 16, None) == q.QDG_ERR_INVALID_ARG
