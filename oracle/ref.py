@@ -138,6 +138,20 @@ def gemm_mxfp4(a_codes, sa, w_codes, w_e8m0):
     return a @ w.T
 
 
+def gemm_mxfp4_int8(qa, sa, w_codes, w_e8m0):
+    """Per-token int8 activations times MXFP4 weights (the pages' MXFP4 ->
+    INT8 path, kinachrichten, "Das Wichtigste in Kürze" and "Kompilierzeiten
+    und gerätespezifisches Tuning"): ``Y[m,n] = sa[m] * sum_k qa[m,k] *
+    w[n,k]`` with ``w = e2m1(q) * 2**(E - 127)`` per 32-block, in float64.
+    Every product qa * e2m1 * 2**(E-127) is a short dyadic number, so the
+    float64 sum of a row is exact whenever its terms' exponents stay within
+    53 bits of each other (always, for the block scales of quantized
+    weights)."""
+    a = np.asarray(qa, np.float64)
+    w = dequant_mxfp4(w_codes, w_e8m0)
+    return (a @ w.T) * np.asarray(sa, np.float64)[:, None]
+
+
 def gemm_w4a4(a_codes, a_e8m0, w_codes, w_e8m0):
     """MXFP4 activations times MXFP4 weights (W4A4): both sides decoded with
     their E8M0 block-32 scales, then a float64 product."""

@@ -326,3 +326,37 @@ def test_tiny_workload_oracle_shapes():
     # 4-bit quantization noise: step ~ range/15 ~ 0.35 sigma, noise ~ step/sqrt(12) ~ 0.1 sigma
     y_fp = codecs.bf16_bits_to_f64(a) @ w.astype(np.float64).T
     assert np.linalg.norm(y - y_fp) / np.linalg.norm(y_fp) < 0.15
+
+
+def test_mxfp4_int8_gemm_brute_force_and_special_cases():
+    # exact rationals: int8 codes times e2m1 * 2**(E-127), times the token scale
+    r = np.random.default_rng(26)
+    m, n, k = 3, 4, 96
+    qa = r.integers(-128, 128, (m, k))
+    qa[0, :3] = [-128, 127, 0]
+    sa = r.uniform(1e-3, 1e-1, m).astype(np.float32)
+    w_codes = r.integers(0, 16, (n, k)).astype(np.uint8)
+    e = r.integers(118, 136, (n, k // 32)).astype(np.uint8)
+    y = ref.gemm_mxfp4_int8(qa, sa, w_codes, e)
+    wv = codecs.decode_e2m1(w_codes)
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                acc += int(qa[i, kk]) * Fraction(float(wv[j, kk])) * Fraction(2) ** (int(e[j, kk // 32]) - 127)
+            acc *= Fraction(float(sa[i]))
+            assert abs(float(acc) - y[i, j]) <= 1e-15 * abs(float(acc)) + 1e-300
+    # unit block scales and token scales: half the exact integer product with
+    # the doubled E2M1 values (2 * e2m1 is an integer)
+    one = np.full((n, k // 32), 127, np.uint8)
+    twice = (2 * wv).astype(np.int64)
+    assert np.array_equal(ref.gemm_mxfp4_int8(qa, np.ones(m, np.float32), w_codes, one),
+                          ref.int_matmul(qa, twice) / 2.0)
+    # a block scale one step up doubles the result exactly; one-hot rows with
+    # unit token scale return the dequantized weights
+    assert np.array_equal(ref.gemm_mxfp4_int8(qa, sa, w_codes, e + 1), 2.0 * y)
+    eye = np.eye(k, dtype=np.int64)
+    assert np.array_equal(ref.gemm_mxfp4_int8(eye, np.ones(k, np.float32), w_codes, e),
+                          ref.dequant_mxfp4(w_codes, e).T)
+    # linear in the activations: negating them negates the result exactly
+    assert np.array_equal(ref.gemm_mxfp4_int8(-qa[1:], sa[1:], w_codes, e), -y[1:])
