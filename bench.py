@@ -396,6 +396,8 @@ def rows_leg(reps=30):
                   n * k // 2 + n * (k // 32))
         dense_row("w4a4-mxfp4", q.layer_w4a4(n, k), k, n, (16, 512, 4096), torch.uint8, 32, PEAK_FP4_TFLOPS,
                   n * k // 2 + n * (k // 32), a_bits=4, as_bytes=1)
+        dense_row("w4a8-mxfp4-int8", q.layer_mxfp4_int8(n, k), k, n, (16, 512), torch.int8, 0, PEAK_FP8_TFLOPS,
+                  n * k // 2 + n * (k // 32))
 
     # ---- grouped MoE W4A16
     E, top_k, hid, inter = 256, 8, 7168, 2048

@@ -89,6 +89,13 @@ enum { QDG_KIND_DENSE = 0, QDG_KIND_MOE = 1 };
                 otype BF16, F32 or I32
      W4A8-MXFP4 wtype MXFP4, stype E8M0, group_size 32, atype FP8E4M3,
                 act_group 128, otype BF16 or F32
+     W4A8-MXFP4-INT8 wtype MXFP4, stype E8M0, group_size 32, atype INT8,
+                act_group 0 (per token), otype BF16 or F32 (the pages' MXFP4 ->
+                INT8 path: kinachrichten, "Das Wichtigste in Kürze"; each int8
+                activation q is split exactly into 16 hi + lo, both E4M3, and
+                the fp4 weights meet both planes in the scaled fp8 x fp4 MFMA,
+                E8M0 applied by the hardware; streaming family at every M;
+                the planes take 2 * rows * k bytes of the workspace)
      W4A4-MXFP4 wtype MXFP4, stype E8M0, group_size 32, atype MXFP4,
                 act_group 32, otype BF16 or F32 (the pages list W4A4 among
                 the common configurations: kinachrichten, "Warum

@@ -60,7 +60,8 @@ qdg_status report_error(qdg_status st, const char* msg) { return fail(st, "%s", 
 
 Format format_of(const qdg_layer_config& L) {
   if (L.wtype == QDG_W_INT8) return L.atype == QDG_A_BF16 ? FMT_W8A16 : FMT_W8A8;
-  if (L.wtype == QDG_W_MXFP4) return L.atype == QDG_A_MXFP4 ? FMT_W4A4 : FMT_MXFP4;
+  if (L.wtype == QDG_W_MXFP4)
+    return L.atype == QDG_A_MXFP4 ? FMT_W4A4 : L.atype == QDG_A_INT8 ? FMT_MXFP4_I8 : FMT_MXFP4;
   if (L.wtype == QDG_W_NVFP4) return FMT_NVFP4;
   if (L.atype == QDG_A_INT8) return FMT_W4A8;
   return FMT_W4A16;
@@ -80,6 +81,7 @@ PackedGeom packed_geom(const qdg_layer_config& L, Format f) {
     case FMT_W4A16: g.s_bytes = units * 16 * 8; break;  // {f32 s, bf16x2 -(128+z)}
     case FMT_W4A8: g.s_bytes = units * 16 * 4; break;   // f32 s/16
     case FMT_MXFP4:
+    case FMT_MXFP4_I8:
     case FMT_W4A4: g.s_bytes = units * 64; break;       // E8M0 per lane
     case FMT_W8A8:
     case FMT_W8A16: g.s_bytes = g.n_pad * 4; break;     // f32 per column
@@ -129,6 +131,7 @@ const char* fmt_name(Format f, const qdg_layer_config& L) {
     case FMT_W4A8: return "w4a8-int8";
     case FMT_MXFP4: return "w4a8-mxfp4-fp8";
     case FMT_W4A4: return "w4a4-mxfp4";
+    case FMT_MXFP4_I8: return "w4a8-mxfp4-int8";
     case FMT_NVFP4: return "w4a16-nvfp4";
   }
   return "?";
@@ -183,9 +186,11 @@ qdg_status validate_layer(const qdg_layer_config* L) {
       if (L->stype != QDG_S_E8M0 || L->group_size != 32)
         return fail(QDG_ERR_UNSUPPORTED, "MXFP4 needs E8M0 scales over blocks of 32");
       if (L->has_zeros) return fail(QDG_ERR_UNSUPPORTED, "MXFP4 has no zero points");
-      if (!(L->atype == QDG_A_FP8E4M3 && L->act_group == 128) && !(L->atype == QDG_A_MXFP4 && L->act_group == 32))
+      if (!(L->atype == QDG_A_FP8E4M3 && L->act_group == 128) && !(L->atype == QDG_A_MXFP4 && L->act_group == 32) &&
+          !(L->atype == QDG_A_INT8 && L->act_group == 0))
         return fail(QDG_ERR_UNSUPPORTED,
-                    "MXFP4 weights run with fp8 E4M3 activations (128-group scales) or MXFP4 activations (32-blocks)");
+                    "MXFP4 weights run with fp8 E4M3 activations (128-group scales), MXFP4 activations (32-blocks) "
+                    "or per-token int8 activations");
       if (L->otype == QDG_O_I32) return fail(QDG_ERR_UNSUPPORTED, "MXFP4 has no integer accumulator");
       return ok();
     case QDG_W_NVFP4:
@@ -226,7 +231,9 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   // family from M = 33 (bf16 activations: W4A16, NVFP4, W8A16) and from
   // M = 64 (int8 / fp8 / fp4 activations)
   const bool bf16_act = P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4 || P.fmt == FMT_W8A16;
-  if (!has_tuning && !P.compute.batch_invariant && !moe && bm < 128 && M > (bf16_act ? 32 : 63))
+  // MXFP4 weights with int8 activations run the streaming family at every M
+  const bool stream_only = P.fmt == FMT_MXFP4_I8;
+  if (!has_tuning && !P.compute.batch_invariant && !moe && !stream_only && bm < 128 && M > (bf16_act ? 32 : 63))
     bm = 128;
   if (P.compute.batch_invariant && bm > 64) bm = 64;
   // the tiled family addresses A with 32-bit byte offsets
@@ -275,6 +282,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   // weight-streaming family of the int8 / fp8 formats (dense M <= 16): the
   // K range of a workgroup must fit its LDS; raw int32 output is not split
   if (bm == 16 && P.fmt != FMT_W4A16 && P.fmt != FMT_W4A4 && P.fmt != FMT_W8A16 && P.fmt != FMT_NVFP4 && !moe &&
+      !stream_only &&
       !P.compute.batch_invariant &&
       ws_tuning_ok) {
     // 4 N tiles per workgroup when that gives enough workgroups, else one
@@ -310,7 +318,8 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
     stream_mid = P.fmt == FMT_W4A4 || (P.fmt == FMT_W8A8 && 2 * stream_wgs <= kTargetWorkgroups);
   }
   const bool q_enough = (has_tuning && T.block_m >= 128) || (M >= 64 && !stream_mid);
-  if (bm >= 128 && P.fmt != FMT_W4A16 && P.fmt != FMT_W8A16 && P.fmt != FMT_NVFP4 && !moe && a8_fits && q_enough) {
+  if (bm >= 128 && P.fmt != FMT_W4A16 && P.fmt != FMT_W8A16 && P.fmt != FMT_NVFP4 && !stream_only && !moe &&
+      a8_fits && q_enough) {
     ch.tile = true;
     ch.qtile = true;
     ch.tc = TileCfg{128, 256, 8};
@@ -390,7 +399,7 @@ bool instance_exists(Format f, const Choice& c) {
 qdg_status check_tuning(const qdg_layer_config& layer, const qdg_compute_config& compute, Format f,
                         const qdg_tuning_config& tuning) {
   const bool dense_tiled = compute.kind == QDG_KIND_DENSE && !compute.batch_invariant;
-  const bool tile_ok = dense_tiled && (tuning.block_m == 128 || (f == FMT_W4A16 && tuning.block_m == 256));
+  const bool tile_ok = dense_tiled && f != FMT_MXFP4_I8 && (tuning.block_m == 128 || (f == FMT_W4A16 && tuning.block_m == 256));
   if (tuning.block_m && tuning.block_m != 16 && tuning.block_m != 32 && tuning.block_m != 64 && !tile_ok)
     return fail(QDG_ERR_UNSUPPORTED,
                 "block_m %d: implemented 16, 32, 64 (dense: 128; dense W4A16: 256)", tuning.block_m);
@@ -542,6 +551,12 @@ qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes) {
         align_up((M > 0 ? M : 1) * plan->compute.top_k + plan->layer.num_experts * 127, 128);
     rowsum = cap * plan->geom.groups * 4;
   }
+  if (plan->fmt == FMT_MXFP4_I8) {
+    // the two E4M3 planes of the int8 activations (MoE: room for one row per
+    // (token, slot), the per-pair input of a down projection)
+    const int64_t rows = (M > 0 ? M : 1) * (plan->compute.kind == QDG_KIND_MOE ? plan->compute.top_k : 1);
+    rowsum = 2 * rows * plan->layer.k;
+  }
   *bytes = kCounterBytes + align_up((int64_t)c.partial_bytes, 256) + align_up(rowsum, 256);
   return ok();
 }
@@ -622,6 +637,7 @@ static const char* mfma_name(Format f, const Choice& c) {
   if (f == FMT_W8A16 || f == FMT_NVFP4) return c.tile ? "32x32x16_bf16" : "16x16x32_bf16";
   if (f == FMT_MXFP4) return "scale_16x16x128_f8f6f4";
   if (f == FMT_W4A4) return "scale_16x16x128_f4f4";
+  if (f == FMT_MXFP4_I8) return "2x_scale_16x16x128_f8f6f4";
   return "16x16x64_i8";
 }
 
@@ -739,10 +755,17 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
     // the streaming family addresses A with 31-bit byte offsets
     const int64_t a_rows = moe ? (a_per_pair ? rows : T) : M;
     const bool bf16_a = plan->fmt == FMT_W4A16 || plan->fmt == FMT_W8A16 || plan->fmt == FMT_NVFP4;
-    a.a_bytes = a_rows * (bf16_a ? 2 * (int64_t)a.K : plan->fmt == FMT_W4A4 ? a.K / 2 : a.K);
+    const bool planes = plan->fmt == FMT_MXFP4_I8;  // int8 codes become two E4M3 planes
+    a.a_bytes = a_rows * (bf16_a || planes ? 2 * (int64_t)a.K : plan->fmt == FMT_W4A4 ? a.K / 2 : a.K);
     if (a.a_bytes >= ((int64_t)1 << 31))
       return fail(QDG_ERR_UNSUPPORTED, "A of %lld bytes is too large for the streaming family (< 2 GiB)",
                   (long long)a.a_bytes);
+    if (planes) {
+      uint8_t* pl = (uint8_t*)workspace + kCounterBytes + align_up((int64_t)c.partial_bytes, 256);
+      e = launch_act_i8_planes((const int8_t*)A, a_rows, a.K, pl, stream);
+      if (e != hipSuccess) return hip_status(e, "activation planes launch");
+      a.A = pl;
+    }
     a.m_pad = c.grid_m * c.sc.mt * 16;
     const JitInstance* jit = find_jit(*plan, c, moe);
     e = jit ? launch_stream_jit(jit->fn, c.sc, a, c.grid_m, stream)
@@ -766,7 +789,7 @@ qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, 
   if (!A || !packed || !Y) return fail(QDG_ERR_INVALID_ARG, "NULL A, packed or Y");
   const bool need_scales = plan->fmt != FMT_W4A16 && plan->fmt != FMT_W8A16 && plan->fmt != FMT_NVFP4 &&
                            plan->layer.otype != QDG_O_I32;
-  if (plan->fmt == FMT_MXFP4 || plan->fmt == FMT_W4A4) {
+  if (plan->fmt == FMT_MXFP4 || plan->fmt == FMT_W4A4 || plan->fmt == FMT_MXFP4_I8) {
     if (!a_scales) return fail(QDG_ERR_INVALID_ARG, "MXFP4 needs activation scales");
   } else if (need_scales && !a_scales) {
     return fail(QDG_ERR_INVALID_ARG, "activation scales are NULL");
@@ -986,7 +1009,8 @@ qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scal
   if (!A || !packed || !Y || !sorted_ids || !block_expert || !num_padded)
     return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
   if (plan->fmt != FMT_W4A16 && plan->fmt != FMT_W8A16 && plan->fmt != FMT_NVFP4 &&
-      (plan->fmt == FMT_MXFP4 || plan->fmt == FMT_W4A4 || plan->layer.otype != QDG_O_I32) && !a_scales)
+      (plan->fmt == FMT_MXFP4 || plan->fmt == FMT_W4A4 || plan->fmt == FMT_MXFP4_I8 ||
+       plan->layer.otype != QDG_O_I32) && !a_scales)
     return fail(QDG_ERR_INVALID_ARG, "activation scales are NULL");
   if (!aligned(A, 16)) return fail(QDG_ERR_MISALIGNED, "A must be 16-byte aligned");
   if (!aligned(packed, 256)) return fail(QDG_ERR_MISALIGNED, "packed must be 256-byte aligned");

@@ -12,7 +12,16 @@
 
 namespace qdg {
 
-enum Format { FMT_W4A16 = 0, FMT_W8A8 = 1, FMT_W4A8 = 2, FMT_MXFP4 = 3, FMT_W4A4 = 4, FMT_W8A16 = 5, FMT_NVFP4 = 6 };
+enum Format {
+  FMT_W4A16 = 0,
+  FMT_W8A8 = 1,
+  FMT_W4A8 = 2,
+  FMT_MXFP4 = 3,
+  FMT_W4A4 = 4,
+  FMT_W8A16 = 5,
+  FMT_NVFP4 = 6,
+  FMT_MXFP4_I8 = 7  // MXFP4 weights, per-token int8 activations
+};
 
 // Geometry of the packed buffer of one layer.
 struct PackedGeom {
@@ -96,6 +105,10 @@ hipError_t launch_quantize_weights(const qdg_layer_config& L, const float* w, vo
                                    void* scales, void* zeros, hipStream_t s);
 hipError_t launch_quantize_act(int atype, const void* a, int64_t M, int64_t K, void* qa,
                                float* scales, hipStream_t s);
+// int8 activation codes [rows][K] -> E4M3 planes [rows][2K]: per 128-wide
+// group g, bytes 256g .. 256g+127 hold hi = q >> 4 and 256g+128 .. 256g+255
+// hold lo = q & 15 of the group's K values (q = 16 hi + lo, both exact).
+hipError_t launch_act_i8_planes(const int8_t* qa, int64_t rows, int64_t K, uint8_t* planes, hipStream_t s);
 hipError_t launch_moe_combine(const float* y, const float* w, int64_t T, int top_k, int64_t n, void* out,
                               int otype, hipStream_t s);
 // Run-time compiled streaming-family instance (hipRTC): the loaded kernel,

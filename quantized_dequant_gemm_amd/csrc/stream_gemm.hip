@@ -249,6 +249,59 @@ struct FmtMxfp4 {
   }
 };
 
+// Per-token int8 activations x MXFP4 weights (the MXFP4 -> INT8 path). The
+// fp4 weights stay as they are and go through the same scaled MFMA as the fp8
+// path; each int8 activation q is split exactly into q = 16 hi + lo with
+// hi in [-8, 7] and lo in [0, 15], both small integers and so exact E4M3
+// codes, which a pre-pass writes as two planes (per 128-wide group: 128 hi
+// bytes, then 128 lo bytes). A K group is two scaled MFMAs per tile on the
+// same weights, the hi plane with the A-scale exponent 2^4: every product is
+// exact, the sums are fp32, and the token scale is applied once at the end.
+struct FmtMxfp4I8 {
+  using Acc = f32x4_t;
+  static constexpr bool kIntAcc = false;
+  template <int MT, int NT>
+  struct Frag {
+    u32x4_t a[MT][4];  // hi plane (two K halves), then lo plane
+    u32x4_t b[NT];
+    uint32_t sc[NT];
+  };
+  template <int MT, int NT>
+  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g) {
+    // each plane as the fp8 operand of the fp8 path: lane group c holds K
+    // 16c..16c+15 and 64+16c..64+16c+15 of the group
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t o = x.aoff[mt] + (uint32_t)(g * 256 + 16 * x.c);
+      f.a[mt][0] = lda(x.arsrc, o);
+      f.a[mt][1] = lda(x.arsrc, o + 64);
+      f.a[mt][2] = lda(x.arsrc, o + 128);
+      f.a[mt][3] = lda(x.arsrc, o + 192);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const size_t u = (size_t)x.tile[t] * x.groups + g;
+      f.b[t] = ldg_nt((const u32x4_t*)(x.wbase + u * kUnit4Bytes) + x.lane);
+      f.sc[t] = x.sbase[u * 64 + x.lane];
+    }
+  }
+  template <int MT, int NT>
+  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT], uint32_t, uint32_t) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const i32x8_t b = {(int)f.b[t].x, (int)f.b[t].y, (int)f.b[t].z, (int)f.b[t].w, 0, 0, 0, 0};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4_t h0 = f.a[mt][0], h1 = f.a[mt][1], l0 = f.a[mt][2], l1 = f.a[mt][3];
+        const i32x8_t ah = {(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+        const i32x8_t al = {(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+        acc[mt][t] = mfma_fp8_fp4_scaled(ah, b, acc[mt][t], 127 + 4, (int)f.sc[t]);
+        acc[mt][t] = mfma_fp8_fp4_scaled(al, b, acc[mt][t], 127, (int)f.sc[t]);
+      }
+    }
+  }
+};
+
 // MXFP4 activations x MXFP4 weights (W4A4): both operands E2M1 with E8M0
 // block-32 scales. The scaled MFMA applies both scales exactly, so a K group
 // is one MFMA per tile accumulating straight into the fp32 accumulator, with
@@ -456,7 +509,8 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
   constexpr bool kBf16A = std::is_same<F, FmtW4A16<false>>::value || std::is_same<F, FmtW4A16<true>>::value ||
                           std::is_same<F, FmtW8A16>::value || std::is_same<F, FmtNvfp4>::value;
   constexpr bool kFp4A = std::is_same<F, FmtW4A4>::value;
-  const size_t a_row_bytes = kBf16A ? (size_t)p.K * 2 : kFp4A ? (size_t)p.K / 2 : (size_t)p.K;
+  constexpr bool kPlanesA = std::is_same<F, FmtMxfp4I8>::value;  // two E4M3 planes per row
+  const size_t a_row_bytes = kBf16A || kPlanesA ? (size_t)p.K * 2 : kFp4A ? (size_t)p.K / 2 : (size_t)p.K;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mb * BM + mt * 16 + x.col;
@@ -626,8 +680,8 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
           y = acc[mt][t][i] * ((const float*)x.sbase)[n];  // per-channel scale
         } else if constexpr (std::is_same<F, FmtNvfp4>::value) {
           y = acc[mt][t][i] * ((const float*)x.sbase)[0];  // tensor scale
-        } else if constexpr (std::is_same<F, FmtInt8<true, false>>::value) {
-          y = acc[mt][t][i] * p.a_scales[arow];
+        } else if constexpr (std::is_same<F, FmtInt8<true, false>>::value || std::is_same<F, FmtMxfp4I8>::value) {
+          y = acc[mt][t][i] * p.a_scales[arow];  // per-token activation scale
         } else if constexpr (F::kIntAcc) {
           y = (float)acc[mt][t][i];
         } else {
@@ -718,6 +772,8 @@ hipError_t launch_stream(Format f, bool asym, bool moe, const StreamCfg& c, cons
       return dispatch_shape<FmtMxfp4>(c, moe, a, grid_m, s);
     case FMT_W4A4:
       return dispatch_shape<FmtW4A4>(c, moe, a, grid_m, s);
+    case FMT_MXFP4_I8:
+      return dispatch_shape<FmtMxfp4I8>(c, moe, a, grid_m, s);
     case FMT_W8A16:
       return dispatch_shape<FmtW8A16>(c, moe, a, grid_m, s);
     case FMT_NVFP4:
