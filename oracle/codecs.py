@@ -44,6 +44,25 @@ def pack_nibbles(codes):
     return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
 
 
+def unpack_crumbs(packed):
+    """u8 [..., K/4] -> u8 2-bit codes [..., K]: element k in byte k/4, bits
+    2 (k % 4) .. 2 (k % 4) + 1 (the lowest pair holds the first element)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 4,), dtype=np.uint8)
+    for j in range(4):
+        out[..., j::4] = (packed >> (2 * j)) & 0x3
+    return out
+
+
+def pack_crumbs(codes):
+    """u8 2-bit codes [..., K] (0..3, K a multiple of 4) -> u8 [..., K/4];
+    inverse of unpack_crumbs."""
+    codes = np.asarray(codes)
+    assert codes.shape[-1] % 4 == 0
+    c = codes.astype(np.uint8) & 0x3
+    return (c[..., 0::4] | (c[..., 1::4] << 2) | (c[..., 2::4] << 4) | (c[..., 3::4] << 6)).astype(np.uint8)
+
+
 def decode_int4(codes):
     """Two's-complement 4-bit code (0..15) -> integer in [-8, 7]."""
     c = np.asarray(codes).astype(np.int64) & 0xF

@@ -94,6 +94,31 @@ def quantize_uint4_asym(w, group=128):
     return q.reshape(w.shape), s16, z.astype(np.uint8)
 
 
+def quantize_uint2_asym(w, group=128):
+    """w f32 [N, K] -> (codes [N,K] in [0,3], scales f16 bits [N,K/G], zeros u8 [N,K/G]).
+
+    The asymmetric rule of ``quantize_uint4_asym`` with 2-bit codes (the
+    pages list WNA16 without fixing N: kinachrichten, "Warum quantisierte
+    Kernel wichtig sind"): ``s = f16(f32(max - min) / 3)``,
+    ``z = clamp(rne(f32(-min / s)), 0, 3)``, ``q = clamp(rne(f32(w / s)) + z, 0, 3)``,
+    with the stored scale; a zero range stores s = 1.
+    """
+    w = np.asarray(w, dtype=F32)
+    wg = _grouped(w, group)
+    mn = np.min(wg, axis=2)
+    mx = np.max(wg, axis=2)
+    s32 = ((mx - mn).astype(F32) / F32(3.0)).astype(F32)
+    s16 = codecs.f32_to_f16_bits(s32)
+    s = codecs.f16_bits_to_f64(s16).astype(F32)
+    zero = s == 0
+    s = np.where(zero, F32(1.0), s).astype(F32)
+    s16 = np.where(zero, codecs.f32_to_f16_bits(np.ones_like(s32)), s16).astype(np.uint16)
+    z = np.clip(_f32_rne((-mn / s).astype(F32)), 0, 3).astype(np.int64)
+    q = _f32_rne((wg / s[:, :, None]).astype(F32)) + z[:, :, None]
+    q = np.clip(q, 0, 3).astype(np.int64)
+    return q.reshape(w.shape), s16, z.astype(np.uint8)
+
+
 def quantize_int8_per_channel(w):
     """w f32 [N, K] -> (codes int [N,K] in [-127,127], scales f32 [N])."""
     w = np.asarray(w, dtype=F32)

@@ -44,6 +44,21 @@ def dequant_uint4_asym(q, scales_f16_bits, zeros, group=128):
     return w.reshape(n, k)
 
 
+def dequant_uint2_asym(q, scales_f16_bits, zeros, group=128):
+    """2-bit codes q [N,K] in [0,3], fp16 scales and uint8 zero points
+    [N,K/G] -> W64 = (q - z) * s per group (the affine rule of the 4-bit
+    codes; the pages list WNA16 widths without fixing them: kinachrichten,
+    "Warum quantisierte Kernel wichtig sind")."""
+    q = np.asarray(q).astype(np.int64)
+    assert np.all((q >= 0) & (q <= 3)), "2-bit codes are 0..3"
+    z = np.asarray(zeros).astype(np.int64)
+    assert np.all(z <= 3), "2-bit zero points are 0..3"
+    s = codecs.f16_bits_to_f64(scales_f16_bits)
+    n, k = q.shape
+    w = (q.reshape(n, k // group, group) - z[:, :, None]).astype(np.float64) * s[:, :, None]
+    return w.reshape(n, k)
+
+
 def dequant_mxfp4(codes, e8m0, block=32):
     """E2M1 codes [N,K] and E8M0 scale codes [N,K/32] -> W64."""
     e = np.asarray(e8m0)

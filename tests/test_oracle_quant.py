@@ -171,3 +171,35 @@ def test_act_mxfp4_is_the_block_rule_on_each_row():
     c3, e3 = quant.quantize_act_mxfp4(codecs.f32_to_bf16_bits(row))
     assert e3[0, 0] == 125
     assert list(c3[0, :4]) == [2, 0, 0xA, 6]
+
+
+def test_uint2_asym_roundtrip_bounds_and_packing():
+    # grid values (q - z) * s with every group reaching codes 0 and 3 come
+    # back exactly: scale, zero point and codes
+    r = np.random.default_rng(13)
+    n, k, g = 6, 256, 128
+    q = r.integers(0, 4, size=(n, k))
+    q[:, 0::g] = 0
+    q[:, 1::g] = 3
+    z = r.integers(0, 4, size=(n, k // g)).astype(np.uint8)
+    s = _f16_scales(r, (n, k // g))
+    w = ref.dequant_uint2_asym(q, s, z).astype(np.float32)
+    q2, s2, z2 = quant.quantize_uint2_asym(w, g)
+    assert np.array_equal(s2, s) and np.array_equal(z2, z) and np.array_equal(q2, q)
+    # error bound on N(0, 0.02) weights: inside the code range within s/2,
+    # and the zero point's code dequantizes to 0
+    w = synth.weights_f32(16, 512, workload_id=1, salt=9)
+    q, s, z = quant.quantize_uint2_asym(w)
+    assert q.min() >= 0 and q.max() <= 3 and z.max() <= 3
+    deq = ref.dequant_uint2_asym(q, s, z)
+    sc = np.repeat(codecs.f16_bits_to_f64(s), 128, axis=1)
+    inner = (q > 0) & (q < 3)
+    assert np.all(np.abs(deq - w)[inner] <= sc[inner] * 0.5 * (1 + 1e-3))
+    assert np.all(ref.dequant_uint2_asym(np.repeat(z.astype(np.int64), 128, axis=1), s, z) == 0)
+    # the scale is the group's range over 3 rounded to fp16
+    wg = w.reshape(16, 4, 128)
+    assert np.allclose(codecs.f16_bits_to_f64(s), (wg.max(axis=2) - wg.min(axis=2)) / 3, rtol=2 ** -10)
+    # 2-bit packing: element k in byte k/4 at bits 2 (k % 4); hand byte and round trip
+    assert list(codecs.pack_crumbs(np.array([[1, 2, 3, 0]]))[0]) == [1 | (2 << 2) | (3 << 4)]
+    codes = r.integers(0, 4, size=(3, 64)).astype(np.uint8)
+    assert np.array_equal(codecs.unpack_crumbs(codecs.pack_crumbs(codes)), codes)

@@ -360,3 +360,29 @@ def test_mxfp4_int8_gemm_brute_force_and_special_cases():
                           ref.dequant_mxfp4(w_codes, e).T)
     # linear in the activations: negating them negates the result exactly
     assert np.array_equal(ref.gemm_mxfp4_int8(-qa[1:], sa[1:], w_codes, e), -y[1:])
+
+
+def test_w2a16_dequant_hand_values_and_brute_force():
+    # hand values: q = 3, z = 1, s = 0.5 -> 1.0; q = 0, z = 2, s = 0.25 -> -0.5
+    s = codecs.f32_to_f16_bits(np.array([[0.5], [0.25]], np.float32))
+    q = np.zeros((2, 128), np.int64)
+    q[0, 0], q[1, 0] = 3, 0
+    z = np.array([[1], [2]], np.uint8)
+    w = ref.dequant_uint2_asym(q, s, z)
+    assert w[0, 0] == 1.0 and w[1, 0] == -0.5 and w[0, 1] == -0.5 and w[1, 1] == -0.5
+    # exact rational brute force of the bf16-activation GEMM on every code and zero point
+    r = np.random.default_rng(27)
+    m, n, k = 2, 4, 256
+    a = codecs.f32_to_bf16_bits(r.standard_normal((m, k)).astype(np.float32))
+    qv = r.integers(0, 4, (n, k))
+    zz = r.integers(0, 4, (n, k // 128)).astype(np.uint8)
+    ss = codecs.f32_to_f16_bits(r.uniform(1e-3, 1e-2, (n, k // 128)).astype(np.float32))
+    y = ref.gemm_w4a16(a, ref.dequant_uint2_asym(qv, ss, zz))
+    av = codecs.bf16_bits_to_f64(a)
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                acc += (Fraction(float(av[i, kk])) * (int(qv[j, kk]) - int(zz[j, kk // 128]))
+                        * _frac_f16(ss[j, kk // 128]))
+            assert abs(float(acc) - y[i, j]) <= 1e-12 * abs(float(acc)) + 1e-300
