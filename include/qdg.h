@@ -64,8 +64,9 @@ enum { QDG_W_INT4 = 0,  /* two's-complement 4-bit, symmetric (no zeros) */
        QDG_W_UINT4 = 1, /* unsigned 4-bit with uint8 zero points (asymmetric) */
        QDG_W_INT8 = 2,  /* int8, symmetric, one fp32 scale per output channel */
        QDG_W_MXFP4 = 3, /* OCP MX FP4 E2M1 with E8M0 scale per 32 along K */
-       QDG_W_NVFP4 = 4  /* E2M1 with an E4M3 scale per 16 along K and one
-                           binary32 scale per tensor (expert) */ };
+       QDG_W_NVFP4 = 4, /* E2M1 with an E4M3 scale per 16 along K and one
+                           binary32 scale per tensor (expert) */
+       QDG_W_UINT2 = 5  /* unsigned 2-bit with uint8 zero points (asymmetric) */ };
 /* Scale storage types. */
 enum { QDG_S_F16 = 0, QDG_S_F32 = 1, QDG_S_E8M0 = 2, QDG_S_E4M3 = 3 };
 /* Activation types. MXFP4 activations (W4A4): E2M1 codes u8 [M][k/2], two
@@ -110,6 +111,11 @@ enum { QDG_KIND_DENSE = 0, QDG_KIND_MOE = 1 };
                 its E4M3 block scale is exact in bf16, so the weights enter
                 the bf16 MFMA already scaled and the tensor scale is applied
                 to the fp32 result)
+     W2A16      wtype UINT2 (has_zeros 1), stype F16, group_size 128, atype
+                BF16, act_group 0, otype BF16 or F32 (a WNA16 width: the pages
+                list WNA16 without fixing N, kinachrichten, "Warum
+                quantisierte Kernel wichtig sind"; the 4-bit asymmetric rule
+                with 2-bit codes, streaming family at every M)
    Shapes: k a positive multiple of 128; n >= 1 (padded internally to a
    multiple of 16); num_experts >= 1 (1 for a dense layer). arch = 950. */
 typedef struct qdg_layer_config {
@@ -163,13 +169,16 @@ typedef struct qdg_tuning_config {
 /* Standard-format weights (device pointers; all experts back to back):
      INT4 / UINT4 / MXFP4 qweight  u8 [E][n][k/2], element k of a row in byte
                                    k/2, even k in the low nibble
+     UINT2 qweight                 u8 [E][n][k/4], element k in byte k/4 at
+                                   bits 2 (k % 4) .. 2 (k % 4) + 1
      INT8 qweight                  i8 [E][n][k]
      F16 scales                    f16 [E][n][k/group_size]
      F32 scales (INT8)             f32 [E][n]
      E8M0 scales (MXFP4)           u8 [E][n][k/32], value 2^(e-127); 255 invalid
      E4M3 scales (NVFP4)           u8 [E][n][k/16], OCP E4M3 codes; the NaN
                                    codes 0x7F / 0xFF are invalid
-     zeros (UINT4 only)            u8 [E][n][k/group_size], values 0..15
+     zeros (UINT4, UINT2)          u8 [E][n][k/group_size], values 0..15
+                                   (UINT2: 0..3)
      tensor_scale (NVFP4 only)     f32 [E], one scale per expert
    Dequantized weight: w = (q - z) * s, z = 0 when symmetric; MXFP4:
    w = e2m1(q) * 2^(e-127); NVFP4: w = e2m1(q) * e4m3(s) * tensor_scale.
@@ -200,8 +209,8 @@ enum {
                                     scale. Packed as the largest finite scale
                                     of its sign (E8M0 254, E4M3 +-448); a
                                     non-finite f16 / f32 scale is packed as it is */
-  QDG_FLAG_BAD_ZERO_POINT = 2u,  /* a UINT4 zero point above 15; packed
-                                    modulo 128 */
+  QDG_FLAG_BAD_ZERO_POINT = 2u,  /* a UINT4 zero point above 15 (UINT2:
+                                    above 3); packed modulo 128 */
   QDG_FLAG_BAD_EXPERT_ID = 4u    /* a top-k id outside [0, E); the pair is
                                     left out of every expert block, so its
                                     output row is never written */

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libqdg.so")
 
 # enums (mirror include/qdg.h)
 QDG_OK, QDG_ERR_INVALID_ARG, QDG_ERR_UNSUPPORTED, QDG_ERR_MISALIGNED, QDG_ERR_WORKSPACE, QDG_ERR_HIP = range(6)
-QDG_W_INT4, QDG_W_UINT4, QDG_W_INT8, QDG_W_MXFP4, QDG_W_NVFP4 = range(5)
+QDG_W_INT4, QDG_W_UINT4, QDG_W_INT8, QDG_W_MXFP4, QDG_W_NVFP4, QDG_W_UINT2 = range(6)
 QDG_S_F16, QDG_S_F32, QDG_S_E8M0, QDG_S_E4M3 = range(4)
 QDG_A_BF16, QDG_A_INT8, QDG_A_FP8E4M3, QDG_A_MXFP4 = range(4)
 QDG_O_BF16, QDG_O_F32, QDG_O_I32 = range(3)
@@ -290,6 +290,12 @@ def layer_w4a8(n, k, otype=QDG_O_BF16, num_experts=1):
 def layer_mxfp4(n, k, otype=QDG_O_BF16, num_experts=1):
     return LayerConfig(n=n, k=k, num_experts=num_experts, wtype=QDG_W_MXFP4, stype=QDG_S_E8M0, group_size=32,
                        has_zeros=0, atype=QDG_A_FP8E4M3, act_group=128, otype=otype, arch=950)
+
+
+def layer_w2a16(n, k, otype=QDG_O_BF16, num_experts=1):
+    """2-bit asymmetric weights (uint2 codes, uint8 zero points, fp16 group-128 scales), bf16 activations."""
+    return LayerConfig(n=n, k=k, num_experts=num_experts, wtype=QDG_W_UINT2, stype=QDG_S_F16, group_size=128,
+                       has_zeros=1, atype=QDG_A_BF16, act_group=0, otype=otype, arch=950)
 
 
 def layer_mxfp4_int8(n, k, otype=QDG_O_BF16, num_experts=1):

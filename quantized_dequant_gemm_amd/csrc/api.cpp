@@ -63,6 +63,7 @@ Format format_of(const qdg_layer_config& L) {
   if (L.wtype == QDG_W_MXFP4)
     return L.atype == QDG_A_MXFP4 ? FMT_W4A4 : L.atype == QDG_A_INT8 ? FMT_MXFP4_I8 : FMT_MXFP4;
   if (L.wtype == QDG_W_NVFP4) return FMT_NVFP4;
+  if (L.wtype == QDG_W_UINT2) return FMT_W2A16;
   if (L.atype == QDG_A_INT8) return FMT_W4A8;
   return FMT_W4A16;
 }
@@ -76,9 +77,10 @@ PackedGeom packed_geom(const qdg_layer_config& L, Format f) {
   g.groups = L.k / 128;
   g.experts = L.num_experts;
   const int64_t units = g.ntiles * g.groups;
-  g.w_bytes = units * (f == FMT_W8A8 || f == FMT_W8A16 ? 2048 : 1024);  // bytes per 16x128 unit
+  g.w_bytes = units * (f == FMT_W8A8 || f == FMT_W8A16 ? 2048 : f == FMT_W2A16 ? 512 : 1024);  // per 16x128 unit
   switch (f) {
-    case FMT_W4A16: g.s_bytes = units * 16 * 8; break;  // {f32 s, bf16x2 -(128+z)}
+    case FMT_W4A16:
+    case FMT_W2A16: g.s_bytes = units * 16 * 8; break;  // {f32 s, bf16x2 -(128+z)}
     case FMT_W4A8: g.s_bytes = units * 16 * 4; break;   // f32 s/16
     case FMT_MXFP4:
     case FMT_MXFP4_I8:
@@ -132,6 +134,7 @@ const char* fmt_name(Format f, const qdg_layer_config& L) {
     case FMT_MXFP4: return "w4a8-mxfp4-fp8";
     case FMT_W4A4: return "w4a4-mxfp4";
     case FMT_MXFP4_I8: return "w4a8-mxfp4-int8";
+    case FMT_W2A16: return "w2a16-uint2-asym";
     case FMT_NVFP4: return "w4a16-nvfp4";
   }
   return "?";
@@ -193,6 +196,14 @@ qdg_status validate_layer(const qdg_layer_config* L) {
                     "or per-token int8 activations");
       if (L->otype == QDG_O_I32) return fail(QDG_ERR_UNSUPPORTED, "MXFP4 has no integer accumulator");
       return ok();
+    case QDG_W_UINT2:
+      if (L->stype != QDG_S_F16 || L->group_size != 128)
+        return fail(QDG_ERR_UNSUPPORTED, "UINT2 weights need f16 scales over groups of 128");
+      if (!L->has_zeros) return fail(QDG_ERR_INVALID_ARG, "UINT2 weights are asymmetric (has_zeros 1)");
+      if (L->atype != QDG_A_BF16 || L->act_group != 0)
+        return fail(QDG_ERR_UNSUPPORTED, "UINT2 weights run with bf16 activations");
+      if (L->otype == QDG_O_I32) return fail(QDG_ERR_UNSUPPORTED, "W2A16 has no integer accumulator");
+      return ok();
     case QDG_W_NVFP4:
       if (L->stype != QDG_S_E4M3 || L->group_size != 16)
         return fail(QDG_ERR_UNSUPPORTED, "NVFP4 needs E4M3 scales over blocks of 16");
@@ -232,7 +243,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   // M = 64 (int8 / fp8 / fp4 activations)
   const bool bf16_act = P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4 || P.fmt == FMT_W8A16;
   // MXFP4 weights with int8 activations run the streaming family at every M
-  const bool stream_only = P.fmt == FMT_MXFP4_I8;
+  const bool stream_only = P.fmt == FMT_MXFP4_I8 || P.fmt == FMT_W2A16;
   if (!has_tuning && !P.compute.batch_invariant && !moe && !stream_only && bm < 128 && M > (bf16_act ? 32 : 63))
     bm = 128;
   if (P.compute.batch_invariant && bm > 64) bm = 64;
@@ -399,7 +410,8 @@ bool instance_exists(Format f, const Choice& c) {
 qdg_status check_tuning(const qdg_layer_config& layer, const qdg_compute_config& compute, Format f,
                         const qdg_tuning_config& tuning) {
   const bool dense_tiled = compute.kind == QDG_KIND_DENSE && !compute.batch_invariant;
-  const bool tile_ok = dense_tiled && f != FMT_MXFP4_I8 && (tuning.block_m == 128 || (f == FMT_W4A16 && tuning.block_m == 256));
+  const bool tile_ok = dense_tiled && f != FMT_MXFP4_I8 && f != FMT_W2A16 &&
+                       (tuning.block_m == 128 || (f == FMT_W4A16 && tuning.block_m == 256));
   if (tuning.block_m && tuning.block_m != 16 && tuning.block_m != 32 && tuning.block_m != 64 && !tile_ok)
     return fail(QDG_ERR_UNSUPPORTED,
                 "block_m %d: implemented 16, 32, 64 (dense: 128; dense W4A16: 256)", tuning.block_m);
@@ -447,7 +459,8 @@ qdg_status qdg_preprocess(const qdg_layer_config* layer, const qdg_std_weights* 
   qdg_status st = validate_layer(layer);
   if (st != QDG_OK) return st;
   if (!w || !w->qweight || !w->scales || !packed) return fail(QDG_ERR_INVALID_ARG, "NULL weight or packed pointer");
-  if (layer->wtype == QDG_W_UINT4 && !w->zeros) return fail(QDG_ERR_INVALID_ARG, "UINT4 weights need zero points");
+  if ((layer->wtype == QDG_W_UINT4 || layer->wtype == QDG_W_UINT2) && !w->zeros)
+    return fail(QDG_ERR_INVALID_ARG, "UINT4 / UINT2 weights need zero points");
   if (layer->wtype == QDG_W_NVFP4 && (!w->tensor_scale || !aligned(w->tensor_scale, 4)))
     return fail(QDG_ERR_INVALID_ARG, "NVFP4 weights need 4-byte aligned per-tensor scales");
   const Format f = format_of(*layer);
@@ -467,7 +480,8 @@ qdg_status qdg_quantize_weights(const qdg_layer_config* layer, const float* w, v
   qdg_status st = validate_layer(layer);
   if (st != QDG_OK) return st;
   if (!w || !qweight || !scales) return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
-  if (layer->wtype == QDG_W_UINT4 && !zeros) return fail(QDG_ERR_INVALID_ARG, "UINT4 needs a zeros buffer");
+  if ((layer->wtype == QDG_W_UINT4 || layer->wtype == QDG_W_UINT2) && !zeros)
+    return fail(QDG_ERR_INVALID_ARG, "UINT4 / UINT2 need a zeros buffer");
   if (layer->wtype == QDG_W_NVFP4 && (!zeros || !aligned(zeros, 4)))
     return fail(QDG_ERR_INVALID_ARG, "NVFP4 needs a 4-byte aligned f32 [E] buffer for the tensor scales (zeros)");
   return hip_status(launch_quantize_weights(*layer, w, qweight, scales, zeros, (hipStream_t)stream),
@@ -635,6 +649,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
 static const char* mfma_name(Format f, const Choice& c) {
   if (f == FMT_W4A16) return c.tile && c.tc.bm * c.tc.bn / (64 * c.tc.waves) == 64 ? "32x32x16_bf16" : "16x16x32_bf16";
   if (f == FMT_W8A16 || f == FMT_NVFP4) return c.tile ? "32x32x16_bf16" : "16x16x32_bf16";
+  if (f == FMT_W2A16) return "16x16x32_bf16";
   if (f == FMT_MXFP4) return "scale_16x16x128_f8f6f4";
   if (f == FMT_W4A4) return "scale_16x16x128_f4f4";
   if (f == FMT_MXFP4_I8) return "2x_scale_16x16x128_f8f6f4";
@@ -754,7 +769,8 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   } else {
     // the streaming family addresses A with 31-bit byte offsets
     const int64_t a_rows = moe ? (a_per_pair ? rows : T) : M;
-    const bool bf16_a = plan->fmt == FMT_W4A16 || plan->fmt == FMT_W8A16 || plan->fmt == FMT_NVFP4;
+    const bool bf16_a = plan->fmt == FMT_W4A16 || plan->fmt == FMT_W8A16 || plan->fmt == FMT_NVFP4 ||
+                        plan->fmt == FMT_W2A16;
     const bool planes = plan->fmt == FMT_MXFP4_I8;  // int8 codes become two E4M3 planes
     a.a_bytes = a_rows * (bf16_a || planes ? 2 * (int64_t)a.K : plan->fmt == FMT_W4A4 ? a.K / 2 : a.K);
     if (a.a_bytes >= ((int64_t)1 << 31))
@@ -788,6 +804,7 @@ qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, 
   if (M > 0x7FFFFFFF / 2) return fail(QDG_ERR_UNSUPPORTED, "M too large");
   if (!A || !packed || !Y) return fail(QDG_ERR_INVALID_ARG, "NULL A, packed or Y");
   const bool need_scales = plan->fmt != FMT_W4A16 && plan->fmt != FMT_W8A16 && plan->fmt != FMT_NVFP4 &&
+                           plan->fmt != FMT_W2A16 &&
                            plan->layer.otype != QDG_O_I32;
   if (plan->fmt == FMT_MXFP4 || plan->fmt == FMT_W4A4 || plan->fmt == FMT_MXFP4_I8) {
     if (!a_scales) return fail(QDG_ERR_INVALID_ARG, "MXFP4 needs activation scales");
@@ -1008,7 +1025,7 @@ qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scal
   if (T * plan->compute.top_k > (1 << 20)) return fail(QDG_ERR_UNSUPPORTED, "T*top_k above 2^20");
   if (!A || !packed || !Y || !sorted_ids || !block_expert || !num_padded)
     return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
-  if (plan->fmt != FMT_W4A16 && plan->fmt != FMT_W8A16 && plan->fmt != FMT_NVFP4 &&
+  if (plan->fmt != FMT_W4A16 && plan->fmt != FMT_W8A16 && plan->fmt != FMT_NVFP4 && plan->fmt != FMT_W2A16 &&
       (plan->fmt == FMT_MXFP4 || plan->fmt == FMT_W4A4 || plan->fmt == FMT_MXFP4_I8 ||
        plan->layer.otype != QDG_O_I32) && !a_scales)
     return fail(QDG_ERR_INVALID_ARG, "activation scales are NULL");

@@ -46,6 +46,7 @@ const char* policy_name(Format f, bool asym, bool raw) {
     case FMT_MXFP4: return "qdg::FmtMxfp4";
     case FMT_W4A4: return "qdg::FmtW4A4";
     case FMT_MXFP4_I8: return "qdg::FmtMxfp4I8";
+    case FMT_W2A16: return "qdg::FmtW2A16";
     case FMT_W8A16: return "qdg::FmtW8A16";
     case FMT_NVFP4: return "qdg::FmtNvfp4";
   }

@@ -60,7 +60,38 @@ __global__ void repack_kernel(int fmt, int wtype, const uint8_t* __restrict__ qw
   uint8_t* wdst = packed + e * expert_stride;
   uint8_t* sdst = wdst + s_offset;
 
-  if (fmt == FMT_W4A16 || fmt == FMT_W4A8) {
+  if (fmt == FMT_W2A16) {
+    // 512-byte unit: lane (c, col) holds K 32c .. 32c+31 of its column in two
+    // dwords; dword d serves the MFMA K steps 2d and 2d+1 (K 32c + 8j .. +7).
+    // Field i = 4h + m (h = step within the dword, m = bf16 pair of the
+    // operand) sits at bits 2i (element 2m of step 2d+h) and 16 + 2i
+    // (element 2m+1), so (x >> 2i) & 0x00030003 | 0x43004300 is that pair as
+    // bf16 128 + u.
+    const uint8_t* src = qw + (e * N + (valid ? n : 0)) * (K / 4);
+    u32x2_t out = {0, 0};
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t k0 = g * 128 + 32 * c + 16 * d + 8 * (i >> 2) + 2 * (i & 3);
+        const uint32_t c0 = (src[k0 / 4] >> (2 * (k0 % 4))) & 3u;
+        const uint32_t c1 = (src[(k0 + 1) / 4] >> (2 * ((k0 + 1) % 4))) & 3u;
+        v |= (c0 << (2 * i)) | (c1 << (16 + 2 * i));
+      }
+      out[d] = valid ? v : 0u;
+    }
+    *((u32x2_t*)(wdst + unit * kUnit2Bytes) + lane) = out;
+    if (c == 0) {
+      const float s = valid ? half_bits_to_float(((const uint16_t*)scales)[(e * N + n) * groups + g]) : 0.f;
+      if (!finite_f32(s)) raise_flag(status, QDG_FLAG_BAD_SCALE);
+      const uint32_t zq = valid ? zeros[(e * N + n) * groups + g] : 0;
+      if (zq > 3) raise_flag(status, QDG_FLAG_BAD_ZERO_POINT);
+      const uint32_t nego = 0xC300u | (zq & 0x7Fu);  // bf16 of -(128 + zq)
+      u32x2_t rec = {__builtin_bit_cast(uint32_t, s), nego | (nego << 16)};
+      *((u32x2_t*)sdst + unit * 16 + col) = rec;
+    }
+  } else if (fmt == FMT_W4A16 || fmt == FMT_W4A8) {
     const uint32_t* src = (const uint32_t*)(qw + (e * N + (valid ? n : 0)) * (K / 2));
     u32x4_t out;
     for (int d = 0; d < 4; ++d) {
@@ -175,7 +206,7 @@ __global__ void quantize_weights_kernel(int wtype, const float* __restrict__ w, 
   if (tid >= rows * gpr) return;
   const int64_t row = tid / gpr, g = tid % gpr;
   const float* src = w + row * K + g * group;
-  if (wtype == QDG_W_INT4 || wtype == QDG_W_UINT4) {
+  if (wtype == QDG_W_INT4 || wtype == QDG_W_UINT4 || wtype == QDG_W_UINT2) {
     float mn = src[0], mx = src[0], amax = 0.f;
     for (int i = 0; i < group; ++i) {
       const float v = src[i];
@@ -185,7 +216,20 @@ __global__ void quantize_weights_kernel(int wtype, const float* __restrict__ w, 
     }
     uint8_t* dst = qw + row * (K / 2) + g * group / 2;
     _Float16* sc = (_Float16*)scales + row * gpr + g;
-    if (wtype == QDG_W_INT4) {
+    if (wtype == QDG_W_UINT2) {  // the asymmetric rule with 2-bit codes, four per byte
+      float s = f16_round(__fdiv_rn(mx - mn, 3.0f));
+      if (s == 0.f) s = 1.0f;
+      *sc = (_Float16)s;
+      const float z = fminf(fmaxf(rintf(__fdiv_rn(-mn, s)), 0.f), 3.f);
+      zeros[row * gpr + g] = (uint8_t)z;
+      uint8_t* dst2 = qw + row * (K / 4) + g * group / 4;
+      for (int i = 0; i < group; i += 4) {
+        uint32_t b = 0;
+        for (int j = 0; j < 4; ++j)
+          b |= (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(src[i + j], s)) + z, 0.f), 3.f) << (2 * j);
+        dst2[i / 4] = (uint8_t)b;
+      }
+    } else if (wtype == QDG_W_INT4) {
       float s = f16_round(__fdiv_rn(amax, 7.0f));
       if (s == 0.f) s = 1.0f;
       *sc = (_Float16)s;

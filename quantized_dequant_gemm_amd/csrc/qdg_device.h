@@ -49,6 +49,7 @@ constexpr int kUnitK = 128;      // K values per unit (= group size)
 constexpr int kUnitN = 16;       // columns per unit
 constexpr int kUnit4Bytes = 1024;  // 4-bit unit
 constexpr int kUnit8Bytes = 2048;  // int8 unit
+constexpr int kUnit2Bytes = 512;   // 2-bit unit
 
 // ------------------------------------------------------------------ MFMA
 // v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] B[32x16]. Lane l supplies

@@ -20,7 +20,8 @@ enum Format {
   FMT_W4A4 = 4,
   FMT_W8A16 = 5,
   FMT_NVFP4 = 6,
-  FMT_MXFP4_I8 = 7  // MXFP4 weights, per-token int8 activations
+  FMT_MXFP4_I8 = 7,  // MXFP4 weights, per-token int8 activations
+  FMT_W2A16 = 8      // uint2 weights (zero points), bf16 activations
 };
 
 // Geometry of the packed buffer of one layer.

@@ -133,6 +133,70 @@ struct FmtW4A16 {
   static constexpr bool kIntAcc = false;
 };
 
+// W2A16: bf16 activations, 2-bit weights with fp16 group scales and zero
+// points (0..3). The offset trick of W4A16 on 512-byte units: lane (c, col)
+// holds its 32 K values in two dwords; each field pair is unpacked to the
+// bf16 pair 128 + u with one v_and_or_b32 after a shift, and each group's
+// chains start from -(128 + z) * sum(A).
+struct FmtW2A16 {
+  using Acc = f32x4_t;
+  static constexpr bool kIntAcc = false;
+  template <int MT, int NT>
+  struct Frag {
+    u32x4_t a[MT][4];
+    u32x2_t b[NT];
+    float s[NT];
+    uint32_t o[NT];
+  };
+  template <int MT, int NT>
+  __device__ static void load(Frag<MT, NT>& f, const Ctx& x, int g) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t o = x.aoff[mt] + (uint32_t)(g * 256 + 64 * x.c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.a[mt][j] = lda(x.arsrc, o + 16 * j);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const size_t u = (size_t)x.tile[t] * x.groups + g;
+      f.b[t] = ldg_nt((const u32x2_t*)(x.wbase + u * kUnit2Bytes) + x.lane);
+      const u32x2_t r = *((const u32x2_t*)(x.sbase) + u * 16 + x.col);
+      f.s[t] = bits_as<float>(r.x);
+      f.o[t] = r.y;
+    }
+  }
+  template <int MT, int NT>
+  __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT], uint32_t, uint32_t ue) {
+    uint32_t m2;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(m2) : "s"(0x00030003u));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      u32x4_t bw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t xw = f.b[t][j / 2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t v = (xw >> (2 * (4 * (j % 2) + m))) & m2;
+          bw[j][m] = v | ue;
+        }
+      }
+      const u32x4_t ko = {f.o[t], f.o[t], f.o[t], f.o[t]};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4_t p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p = mfma_bf16(f.a[mt][j], ko, p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p = mfma_bf16(f.a[mt][j], bw[j], p);
+        const float s = f.s[t];
+        acc[mt][t] = f32x4_t{__builtin_fmaf(s, p[0], acc[mt][t][0]), __builtin_fmaf(s, p[1], acc[mt][t][1]),
+                             __builtin_fmaf(s, p[2], acc[mt][t][2]), __builtin_fmaf(s, p[3], acc[mt][t][3])};
+      }
+    }
+  }
+};
+
 // Int8 activations (per token) with int8 (W8A8) or int4 (W4A8) weights.
 template <bool W4, bool RAW>
 struct FmtInt8 {
@@ -507,7 +571,8 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(MT * NT
   x.wbase = p.packed + (size_t)expert * p.expert_stride;
   x.sbase = x.wbase + p.s_offset;
   constexpr bool kBf16A = std::is_same<F, FmtW4A16<false>>::value || std::is_same<F, FmtW4A16<true>>::value ||
-                          std::is_same<F, FmtW8A16>::value || std::is_same<F, FmtNvfp4>::value;
+                          std::is_same<F, FmtW8A16>::value || std::is_same<F, FmtNvfp4>::value ||
+                          std::is_same<F, FmtW2A16>::value;
   constexpr bool kFp4A = std::is_same<F, FmtW4A4>::value;
   constexpr bool kPlanesA = std::is_same<F, FmtMxfp4I8>::value;  // two E4M3 planes per row
   const size_t a_row_bytes = kBf16A || kPlanesA ? (size_t)p.K * 2 : kFp4A ? (size_t)p.K / 2 : (size_t)p.K;
@@ -774,6 +839,8 @@ hipError_t launch_stream(Format f, bool asym, bool moe, const StreamCfg& c, cons
       return dispatch_shape<FmtW4A4>(c, moe, a, grid_m, s);
     case FMT_MXFP4_I8:
       return dispatch_shape<FmtMxfp4I8>(c, moe, a, grid_m, s);
+    case FMT_W2A16:
+      return dispatch_shape<FmtW2A16>(c, moe, a, grid_m, s);
     case FMT_W8A16:
       return dispatch_shape<FmtW8A16>(c, moe, a, grid_m, s);
     case FMT_NVFP4:
