@@ -301,14 +301,14 @@ def _time_launches(launch, reps, stream):
 
 def rows_leg(reps=30):
     """The other rows of the hot path, each timed at its own shapes (not part
-    of `value`): W8A8, W4A8-INT8, W8A16 and W4A16-NVFP4 (K=4096, N in
+    of `value`): W8A8, W4A8-INT8, W8A16, W4A16-NVFP4 and W2A16 (K=4096, N in
     {4096, 14336}, M in {16, 256, 4096}), W4A8-MXFP4 ((K,N) in {(7168,2048), (2048,7168)}, M in
-    {16, 512, 4096}) and W4A4-MXFP4 at the same shapes, the activation
+    {16, 512, 4096}), W4A4-MXFP4 at the same shapes and MXFP4 x INT8 at M in {16, 512}, the activation
     quantizers, and the grouped MoE W4A16
     GEMMs (E=256, top-8, hidden 7168, intermediate 2048, T in {64, 512,
     4096}) with their expert sort, the gate+up GEMM with the SiLU*mul
     epilogue and the top-k combine, and the grouped MoE W4A8-INT8 GEMMs of
-    the same experts at T in {64, 512}. Every figure is the average over
+    the same experts at T in {64, 512, 4096}. Every figure is the average over
     back-to-back launches."""
     import torch
     import quantized_dequant_gemm_amd as q
@@ -331,19 +331,24 @@ def rows_leg(reps=30):
         elif layer.wtype == q.QDG_W_NVFP4:
             qw = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
             sc = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+        elif layer.wtype == q.QDG_W_UINT2:
+            qw = torch.empty((n, k // 4), dtype=torch.uint8, device=dev)
+            sc = torch.empty((n, k // 128), dtype=torch.int16, device=dev)
         else:
             qw = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
             sc = torch.empty((n, k // 128), dtype=torch.int16, device=dev)
         ts = torch.empty(1, dtype=torch.float32, device=dev)  # NVFP4 tensor scale
+        zp = torch.empty((n, k // 128), dtype=torch.uint8, device=dev) if layer.has_zeros else None
         q.qdg_quantize_weights(layer, w.data_ptr(), qw.data_ptr(), sc.data_ptr(),
-                               ts.data_ptr() if layer.wtype == q.QDG_W_NVFP4 else None, sh)
+                               ts.data_ptr() if layer.wtype == q.QDG_W_NVFP4 else
+                               zp.data_ptr() if zp is not None else None, sh)
         del w
         copies = max(2, -(-2 * CACHE_BYTES // nbytes))
         bufs = []
         for _ in range(copies):
             b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-            q.qdg_preprocess(layer, q.StdWeights(qw.data_ptr(), sc.data_ptr(), None, ts.data_ptr()), b.data_ptr(),
-                             nbytes, sh)
+            q.qdg_preprocess(layer, q.StdWeights(qw.data_ptr(), sc.data_ptr(), zp.data_ptr() if zp is not None else None,
+                                                 ts.data_ptr()), b.data_ptr(), nbytes, sh)
             bufs.append(b)
         plan = q.qdg_plan_create(layer, q.dense())
         for m in ms:
@@ -391,6 +396,8 @@ def rows_leg(reps=30):
                   n * k + n * 4)
         dense_row("w4a16-nvfp4", q.layer_nvfp4(n, k), k, n, (16, 256, 4096), torch.int8, 0, PEAK_BF16_TFLOPS,
                   n * k // 2 + n * (k // 16) + 4)
+        dense_row("w2a16-uint2", q.layer_w2a16(n, k), k, n, (16, 256, 4096), torch.int8, 0, PEAK_BF16_TFLOPS,
+                  n * k // 4 + n * (k // 128) * 3)
     for (k, n) in ((7168, 2048), (2048, 7168)):
         dense_row("w4a8-mxfp4", q.layer_mxfp4(n, k), k, n, (16, 512, 4096), torch.uint8, 128, PEAK_FP8_TFLOPS,
                   n * k // 2 + n * (k // 32))
@@ -500,7 +507,7 @@ def rows_leg(reps=30):
                 del y32, rw, yo
 
     # ---- grouped MoE W4A8-INT8 (the same experts; int8 activations per token
-    # for gate+up and per pair for down; streaming family)
+    # for gate+up and per pair for down)
     del layers
     torch.cuda.empty_cache()
     layers8 = {}
@@ -518,13 +525,16 @@ def rows_leg(reps=30):
         del qw, sc
         layers8[name] = (layer, pk, n, k, q.qdg_plan_create(layer, q.moe(top_k)))
         print(f"row {name}: {E} experts packed", file=sys.stderr, flush=True)
-    for t in (64, 512):
+    for t in (64, 512, 4096):
         g = torch.Generator(device=dev)
         g.manual_seed(synth.seed_for(4, synth.TID_LOGITS, t))
         logits = torch.randn((t, E), generator=g, device=dev, dtype=torch.float32)
         ids = torch.topk(logits, top_k, dim=1).indices.to(torch.int32).contiguous()
         touched = int(torch.unique(ids).numel())
-        bm = 16 if t == 64 else 32
+        # 16 / 32-row blocks in the streaming family while experts hold few
+        # rows, 128-row blocks in the 8-bit LDS-tiled family beyond (measured
+        # on MI355X at T = 4096: 4584 -> 2636 us gate+up, 2859 -> 1833 us down)
+        bm = 16 if t == 64 else 32 if t == 512 else 128
         cap = q.qdg_moe_align_capacity(t, top_k, E, bm)
         sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
         block_expert = torch.empty(cap // bm, dtype=torch.int32, device=dev)

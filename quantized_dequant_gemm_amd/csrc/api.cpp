@@ -599,24 +599,33 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   const bool silu = plan.compute.epilogue == QDG_EPI_SILU_MUL;  // weight streaming has no such epilogue
   c.ws = block_m == 16 && !plan.compute.batch_invariant && !silu && ws_pinned;
   if (plan.fmt != FMT_W4A16) {
-    // every other format: the streaming family, block_m / 16 row tiles; the
-    // other bf16-activation formats (NVFP4, W8A16) also run 128-row blocks in
-    // the LDS-tiled family (plain output only)
-    const bool tiled = block_m == 128 && (plan.fmt == FMT_NVFP4 || plan.fmt == FMT_W8A16) && !silu &&
-                       !plan.compute.batch_invariant;
+    // every other format: the streaming family, block_m / 16 row tiles; 128-row
+    // blocks (plain output only) run in the LDS-tiled families: NVFP4 and
+    // W8A16 in the bf16 one, W8A8, W4A8 and the MXFP4 formats in the 8-bit one
+    const bool tiled_fmt = plan.fmt == FMT_NVFP4 || plan.fmt == FMT_W8A16;
+    const bool qtiled_fmt = plan.fmt == FMT_W8A8 || plan.fmt == FMT_W4A8 || plan.fmt == FMT_MXFP4 ||
+                            plan.fmt == FMT_W4A4;
+    const bool tiled = block_m == 128 && (tiled_fmt || qtiled_fmt) && !silu && !plan.compute.batch_invariant;
     if (block_m > 64 && !tiled)
       return fail(QDG_ERR_UNSUPPORTED, "grouped MoE of %s uses block_m 16, 32 or 64%s", fmt_name(plan.fmt, plan.layer),
-                  plan.fmt == FMT_NVFP4 || plan.fmt == FMT_W8A16 ? " (128 without an epilogue)" : "");
+                  tiled_fmt || qtiled_fmt ? " (128 without an epilogue)" : "");
     c.ws = c.tile = c.qtile = false;
     c.sc = StreamCfg{block_m / 16, 2, 4, 1};
     c.rowsum_bytes = 0;
     if (tiled) {
+      // A rows are addressed with 32-bit byte offsets in the tiled families
       const int64_t a_rows = a_per_pair ? rows : T;
-      if ((double)a_rows * (double)plan.layer.k * 2.0 >= 4294967296.0)
+      const double a_row_bytes = tiled_fmt ? 2.0 * plan.layer.k : plan.fmt == FMT_W4A4 ? plan.layer.k / 2.0
+                                                                                      : (double)plan.layer.k;
+      if ((double)a_rows * a_row_bytes >= 4294967296.0)
         return fail(QDG_ERR_UNSUPPORTED, "A of %lld rows is too large for 128-row MoE blocks", (long long)a_rows);
-      c.tile = true;
       c.tc = TileCfg{128, 256, 8};
-      if (plan.fmt == FMT_W8A16) c.rowsum_bytes = (size_t)c.grid_m * 128 * plan.geom.groups * 4;
+      if (tiled_fmt) {
+        c.tile = true;
+        if (plan.fmt == FMT_W8A16) c.rowsum_bytes = (size_t)c.grid_m * 128 * plan.geom.groups * 4;
+      } else {
+        c.qtile = true;
+      }
     }
     *out = c;
     return QDG_OK;
@@ -738,7 +747,7 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   hipError_t e;
   if (c.qtile) {
     a.m_pad = c.grid_m * c.tc.bm;
-    e = launch_qtile(plan->fmt, a, c.grid_m, stream);
+    e = launch_qtile(plan->fmt, moe, a, c.grid_m, stream);
     if (e == hipSuccess && a.split > 1) {
       const int n_pad = (int)((plan->geom.ntiles + 15) / 16 * 256);
       e = launch_reduce_splits(a, a.m_pad, n_pad, stream);

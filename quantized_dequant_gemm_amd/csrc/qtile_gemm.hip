@@ -26,7 +26,12 @@
 //     group in fp32; W4A4 accumulates the scaled MFMA results directly;
 //   * the output tile goes through LDS so stores are whole 16-byte row
 //     segments; split-K writes fp32 partials that reduce_splits_kernel adds
-//     in split order.
+//     in split order;
+//   * grouped MoE: each 128-row block of the expert-sorted rows belongs to
+//     one expert (moe_align pads every expert's rows to whole blocks), so the
+//     workgroup reads that expert's weights once for 128 rows and gathers its
+//     A rows (and activation scales) through the sorted row ids; padding rows
+//     read row 0 and are never stored.
 #include "qdg_device.h"
 #include "qdg_internal.h"
 
@@ -57,10 +62,10 @@ struct QStage {
 // lambda). A: slot q = 64 i + lane is row q / CH, 16-byte chunk q % CH (the
 // last chunk is padding and re-reads chunk 0); a_off holds each slot's row
 // offset.
-// RAW is not used here: it only gives every kernel instance its own
-// specialization (hipcc's host pass rejects a second kernel that calls the
-// same specialization of a device function using target builtins).
-template <int KIND, bool RAW, int BM, int BN, int NW>
+// RAW and MOE are not used here: they only give every kernel instance its
+// own specialization (hipcc's host pass rejects a second kernel that calls
+// the same specialization of a device function using target builtins).
+template <int KIND, bool RAW, bool MOE, int BM, int BN, int NW>
 __device__ __forceinline__ void q_load_stage(char* st, const char* a_g, const uint32_t* a_off,
                                              const uint32_t* as_off, const GemmArgs& p, const uint8_t* wbase,
                                              const uint8_t* sbase, int wg_tile0, int wave, int lane, int g) {
@@ -145,7 +150,7 @@ __device__ __forceinline__ void q_frag_load(QFrag<KIND>& f, const char* st, int 
   }
 }
 
-template <int KIND, bool RAW, class Acc>
+template <int KIND, bool RAW, bool MOE, class Acc>  // MOE: a specialization per kernel, as above
 __device__ __forceinline__ void q_frag_compute(const QFrag<KIND>& f, Acc (&acc)[4][4]) {
   u32x4_t b[4][2];
 #pragma unroll
@@ -193,7 +198,7 @@ struct QAcc {
   using T = typename std::conditional<KIND == Q_W8A8 || RAW, i32x4_t, f32x4_t>::type;
 };
 
-template <int KIND, bool RAW, int NS>
+template <int KIND, bool RAW, int NS, bool MOE>
 __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m_blocks, int n_blocks) {
   constexpr int WAVES_M = 2, WAVES_N = 4, NW = 8, WTM = 64;
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
@@ -240,25 +245,38 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
   const int g0 = (int)(((int64_t)split * p.groups) / nsplit);
   const int g1 = (int)(((int64_t)(split + 1) * p.groups) / nsplit);
 
-  const uint8_t* wbase = p.packed;
+  int expert = 0;
+  if constexpr (MOE) {
+    if (mb * BM >= *p.num_padded) return;  // the whole workgroup leaves together
+    expert = p.block_expert[mb];
+  }
+  const uint8_t* wbase = p.packed + (size_t)expert * p.expert_stride;
   const uint8_t* sbase = wbase + p.s_offset;
   const int wg_tile0 = nb * (BN / 16);
+  // the A row (and activation-scale row) behind output row `grow` of the
+  // tile, and whether that row is stored
+  auto a_row = [&](int grow) -> int {
+    if constexpr (MOE) {
+      const int id = p.sorted_ids[grow];
+      return id < p.num_pairs ? (p.a_per_pair ? id : id / p.top_k) : 0;
+    } else {
+      return grow < p.M ? grow : p.M - 1;
+    }
+  };
 
   uint32_t a_off[A_PER_WAVE];
 #pragma unroll
   for (int r = 0; r < A_PER_WAVE; ++r) {
     const int q = (r * NW + wave) * 64 + lane;
     const int row = min(q / L::CH, BM - 1), ch = q % L::CH;
-    const int grow = mb * BM + row;
-    const int src = grow < p.M ? grow : p.M - 1;
-    const uint32_t a_row = KIND == Q_W4A4 ? (uint32_t)p.K / 2 : (uint32_t)p.K;
-    a_off[r] = (uint32_t)src * a_row + (uint32_t)(ch < L::CH - 1 ? ch : 0) * 16;
+    const int src = a_row(mb * BM + row);
+    const uint32_t a_bytes = KIND == Q_W4A4 ? (uint32_t)p.K / 2 : (uint32_t)p.K;
+    a_off[r] = (uint32_t)src * a_bytes + (uint32_t)(ch < L::CH - 1 ? ch : 0) * 16;
   }
   uint32_t as_off[BM / 64];
 #pragma unroll
   for (int r = 0; r < BM / 64; ++r) {
-    const int grow = mb * BM + r * 64 + lane;
-    const int src = grow < p.M ? grow : p.M - 1;
+    const int src = a_row(mb * BM + r * 64 + lane);
     as_off[r] = (uint32_t)src * (uint32_t)p.groups * 4u;
   }
 
@@ -283,7 +301,7 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
   // before LDS reads stay exact; the last partial round waits for all copies.
 #pragma unroll
   for (int q = 0; q < NS - 1; ++q)
-    q_load_stage<KIND, RAW, BM, BN, NW>(stage[q], a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane,
+    q_load_stage<KIND, RAW, MOE, BM, BN, NW>(stage[q], a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane,
                                         min(g0 + q, g1 - 1));
   QFrag<KIND> fr;
   int gb = g0;
@@ -298,7 +316,7 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
       // the copies in flight.
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       asm volatile("s_barrier" ::: "memory");
-      q_load_stage<KIND, RAW, BM, BN, NW>(stage[(cur + NS - 1) % NS], a_g, a_off, as_off, p, wbase, sbase,
+      q_load_stage<KIND, RAW, MOE, BM, BN, NW>(stage[(cur + NS - 1) % NS], a_g, a_off, as_off, p, wbase, sbase,
                                           wg_tile0, wave, lane, min(gb + cur + NS - 1, g1 - 1));
       q_frag_load<KIND, BM, BN>(fr, stage[cur], a_lane, w_lane, rec_lane, as_lane);
       // MXFP4: all of the group's fragment reads go out before its first
@@ -307,7 +325,7 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
       // measured on MI355X at M = 4096: 84 -> 78 us at K = 7168, 113 -> 110 us
       // at K = 2048; the int8 formats run as fast or faster without it)
       if constexpr (KIND == Q_MXFP4) __builtin_amdgcn_sched_barrier(0);
-      q_frag_compute<KIND, RAW>(fr, acc);
+      q_frag_compute<KIND, RAW, MOE>(fr, acc);
     }
   }
 #pragma unroll
@@ -316,7 +334,7 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       q_frag_load<KIND, BM, BN>(fr, stage[cur], a_lane, w_lane, rec_lane, as_lane);
-      q_frag_compute<KIND, RAW>(fr, acc);
+      q_frag_compute<KIND, RAW, MOE>(fr, acc);
     }
   }
 
@@ -347,7 +365,7 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int grow = mb * BM + wm * WTM + mt * 16 + 4 * c + i;
-      asc[i] = (KIND != Q_MXFP4 && KIND != Q_W4A4 && !raw && grow < p.M) ? p.a_scales[grow] : 1.f;
+      asc[i] = (KIND != Q_MXFP4 && KIND != Q_W4A4 && !raw && (MOE || grow < p.M)) ? p.a_scales[a_row(grow)] : 1.f;
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -379,6 +397,14 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
     for (int chunk = lane; chunk < 16 * cpr; chunk += 64) {
       const int r = chunk / cpr, cc = chunk % cpr;
       const int lrow = mb * BM + wm * WTM + mt * 16 + r;
+      int yrow = lrow;
+      bool v;
+      if constexpr (MOE) {
+        yrow = p.sorted_ids[lrow];
+        v = yrow < p.num_pairs;
+      } else {
+        v = lrow < p.M;
+      }
       const int per = 16 / esz;  // elements per chunk
       const int n0 = nbase + cc * per;
       const u32x4_t val = *(const u32x4_t*)(strip + r * 64 * esz + cc * 16);
@@ -386,8 +412,8 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
         *(u32x4_t*)((float*)p.partial + ((size_t)split * p.m_pad + lrow) * n_pad + n0) = val;
         continue;
       }
-      if (lrow < p.M && n0 < p.N) {
-        char* dst = (char*)p.Y + ((size_t)lrow * p.N + n0) * esz;
+      if (v && n0 < p.N) {
+        char* dst = (char*)p.Y + ((size_t)yrow * p.N + n0) * esz;
         if (n0 + per <= p.N && ((uintptr_t)dst & 15) == 0) {
           *(u32x4_t*)dst = val;
         } else if (f32out) {
@@ -403,26 +429,34 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
 }
 
 template <int KIND, bool RAW>
-hipError_t launch_q(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s) {
+hipError_t launch_q(const GemmArgs& a, bool moe, int m_blocks, int nsplit, hipStream_t s) {
   constexpr int BM = 128, BN = 256;
   using L = QStage<KIND, BM, BN>;
   constexpr int NS = 3 * L::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-  hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS>), dim3(m_blocks * n_blocks, nsplit), dim3(512), 0, s, a,
-                     m_blocks, n_blocks);
+  if (moe) {
+    if (nsplit != 1) return hipErrorInvalidValue;  // grouped MoE is not split
+    hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, true>), dim3(m_blocks * n_blocks, 1), dim3(512), 0, s, a,
+                       m_blocks, n_blocks);
+  } else {
+    hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, false>), dim3(m_blocks * n_blocks, nsplit), dim3(512), 0,
+                       s, a, m_blocks, n_blocks);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_qtile(Format f, const GemmArgs& a, int m_blocks, hipStream_t s) {
+hipError_t launch_qtile(Format f, bool moe, const GemmArgs& a, int m_blocks, hipStream_t s) {
   const bool raw = a.otype == QDG_O_I32;
   if (raw && a.split > 1) return hipErrorInvalidValue;  // integer partials are not split
   switch (f) {
-    case FMT_W8A8: return raw ? launch_q<Q_W8A8, true>(a, m_blocks, 1, s) : launch_q<Q_W8A8, false>(a, m_blocks, a.split, s);
-    case FMT_W4A8: return raw ? launch_q<Q_W4A8, true>(a, m_blocks, 1, s) : launch_q<Q_W4A8, false>(a, m_blocks, a.split, s);
-    case FMT_MXFP4: return launch_q<Q_MXFP4, false>(a, m_blocks, a.split, s);
-    case FMT_W4A4: return launch_q<Q_W4A4, false>(a, m_blocks, a.split, s);
+    case FMT_W8A8:
+      return raw ? launch_q<Q_W8A8, true>(a, moe, m_blocks, 1, s) : launch_q<Q_W8A8, false>(a, moe, m_blocks, a.split, s);
+    case FMT_W4A8:
+      return raw ? launch_q<Q_W4A8, true>(a, moe, m_blocks, 1, s) : launch_q<Q_W4A8, false>(a, moe, m_blocks, a.split, s);
+    case FMT_MXFP4: return launch_q<Q_MXFP4, false>(a, moe, m_blocks, a.split, s);
+    case FMT_W4A4: return launch_q<Q_W4A4, false>(a, moe, m_blocks, a.split, s);
     default: return hipErrorInvalidValue;
   }
 }

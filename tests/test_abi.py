@@ -55,7 +55,7 @@ def test_layer_validation_codes():
     l = q.layer_w4a16(64, 128, otype=q.QDG_O_I32)
     assert _status(q.qdg_validate_layer, l) == q.QDG_ERR_UNSUPPORTED
     l = q.layer_mxfp4(64, 128)
-    l.atype = q.QDG_A_INT8  # MXFP4 x int8 is not a served combination
+    l.atype = q.QDG_A_INT8  # MXFP4 x int8 takes per-token scales (act_group 0), not groups of 128
     assert _status(q.qdg_validate_layer, l) == q.QDG_ERR_UNSUPPORTED
     l = q.layer_w4a16(64, 128)
     l.arch = 942
@@ -81,8 +81,11 @@ def test_plan_and_workspace_validation():
     for mk in (q.layer_w8a8, q.layer_w4a8, q.layer_mxfp4):
         p8 = q.qdg_plan_create(mk(4096, 2048, num_experts=8), q.moe(8))
         assert "family=stream" in q.qdg_moe_describe(p8, 64, 32)
+        # 128-row blocks: the 8-bit LDS-tiled family, without an epilogue
+        assert "family=qtile" in q.qdg_moe_describe(p8, 4096, 128)
+        p8s = q.qdg_plan_create(mk(4096, 2048, num_experts=8), q.moe(8, epilogue=q.QDG_EPI_SILU_MUL))
         with pytest.raises(q.QdgError):
-            q.qdg_moe_describe(p8, 64, 128)
+            q.qdg_moe_describe(p8s, 64, 128)
 
 
 def test_describe_reports_the_instance_that_runs():
@@ -268,19 +271,22 @@ def test_nvfp4_layer_validation():
 
 
 def test_moe_128_row_blocks():
-    # 128-row blocks run the LDS-tiled family for the bf16-activation formats
-    # (NVFP4 and W8A16 with plain output only); the 8-bit-activation formats
-    # run 16-, 32- or 64-row blocks
-    for layer in (q.layer_nvfp4(256, 256, num_experts=4), q.layer_w8a16(256, 256, num_experts=4)):
+    # 128-row blocks (plain output only) run the LDS-tiled families: the bf16
+    # one for NVFP4 and W8A16, the 8-bit one for W8A8, W4A8, W4A8-MXFP4 and
+    # W4A4; the MXFP4 x INT8 and W2A16 paths stay at 16- to 64-row blocks
+    for layer, fam in ((q.layer_nvfp4(256, 256, num_experts=4), "tile"), (q.layer_w8a16(256, 256, num_experts=4), "tile"),
+                       (q.layer_w8a8(256, 256, num_experts=4), "qtile"), (q.layer_w4a8(256, 256, num_experts=4), "qtile"),
+                       (q.layer_mxfp4(256, 256, num_experts=4), "qtile"), (q.layer_w4a4(256, 256, num_experts=4), "qtile")):
         p = q.qdg_plan_create(layer, q.moe(2))
-        assert "family=tile" in q.qdg_moe_describe(p, 8, 128)
+        assert f"family={fam} " in q.qdg_moe_describe(p, 8, 128)
         assert "family=stream" in q.qdg_moe_describe(p, 8, 64)
         ps = q.qdg_plan_create(layer, q.moe(2, epilogue=q.QDG_EPI_SILU_MUL))
         with pytest.raises(q.QdgError):
             q.qdg_moe_describe(ps, 8, 128)
-    p = q.qdg_plan_create(q.layer_w4a8(256, 256, num_experts=4), q.moe(2))
-    with pytest.raises(q.QdgError):
-        q.qdg_moe_describe(p, 8, 128)
+    for layer in (q.layer_mxfp4_int8(256, 256, num_experts=4), q.layer_w2a16(256, 256, num_experts=4)):
+        p = q.qdg_plan_create(layer, q.moe(2))
+        with pytest.raises(q.QdgError):
+            q.qdg_moe_describe(p, 8, 128)
 
 
 def test_noalloc_refuses_oversized_workspace_before_device_work():

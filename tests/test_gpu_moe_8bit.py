@@ -2,7 +2,8 @@
 against the oracle: every (token, slot) pair row equals its expert's dense
 reference on that pair's input row (exact int32 accumulators with raw output,
 relative Frobenius <= 1e-3 with fp32 and <= 2e-3 with bf16 output), every real
-pair row is written and padding rows are never touched."""
+pair row is written and padding rows are never touched. 16- to 64-row expert
+blocks run the streaming family, 128-row blocks the 8-bit LDS-tiled one."""
 
 import numpy as np
 import pytest
@@ -59,7 +60,7 @@ def _acts(kind, rows, k, salt):
 
 
 @pytest.mark.parametrize("kind", ["w8a8", "w4a8", "mxfp4"])
-@pytest.mark.parametrize("t,bm", [(8, 16), (64, 32), (300, 64)])
+@pytest.mark.parametrize("t,bm", [(8, 16), (64, 32), (300, 64), (300, 128), (1024, 128)])
 @pytest.mark.parametrize("per_pair", [0, 1])
 def test_moe_8bit(qdg, kind, t, bm, per_pair):
     # gate+up reads token rows (per_pair 0), down one row per pair (1)
@@ -76,7 +77,7 @@ def test_moe_8bit(qdg, kind, t, bm, per_pair):
         layer = _layer(kind, n, k, otype)
         pk = H.Packed(layer, *std)
         plan = q.qdg_plan_create(layer, q.moe(TOP_K))
-        assert "family=stream" in q.qdg_moe_describe(plan, t, bm)
+        assert ("family=qtile " if bm == 128 else "family=stream ") in q.qdg_moe_describe(plan, t, bm)
         ws, nbytes = H.workspace(plan, t)
         y = H.out_tensor(t * TOP_K, n, otype)  # NaN / INT_MIN canary
         q.qdg_moe_gemm(plan, a_dev.data_ptr(), sa_dev.data_ptr(), pk.buf.data_ptr(), sid.data_ptr(),
@@ -93,9 +94,9 @@ def test_moe_8bit(qdg, kind, t, bm, per_pair):
             assert err <= (1e-3 if otype == q.QDG_O_F32 else 2e-3), err
 
 
-def test_moe_8bit_rejects_128_row_blocks(qdg):
+def test_moe_8bit_rejects_128_row_blocks_with_epilogue(qdg):
     layer = _layer("w4a8", 256, 256, q.QDG_O_BF16)
-    plan = q.qdg_plan_create(layer, q.moe(TOP_K))
+    plan = q.qdg_plan_create(layer, q.moe(TOP_K, epilogue=q.QDG_EPI_SILU_MUL))
     ws, nbytes = H.workspace(plan, 8)
     dummy = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
     with pytest.raises(q.QdgError) as ex:

@@ -80,7 +80,7 @@ def test_w4a4_quantizer_then_gemm_end_to_end(qdg):
     assert metrics.rel_frob(H.to_f64(y), y64) <= 1e-3
 
 
-@pytest.mark.parametrize("t,bm,per_pair", [(8, 16, 0), (64, 32, 1), (300, 64, 0)])
+@pytest.mark.parametrize("t,bm,per_pair", [(8, 16, 0), (64, 32, 1), (300, 64, 0), (300, 128, 0), (600, 128, 1)])
 def test_w4a4_moe(qdg, t, bm, per_pair):
     E, top_k = 8, 2
     n, k = (256, 512) if not per_pair else (512, 256)
@@ -101,6 +101,7 @@ def test_w4a4_moe(qdg, t, bm, per_pair):
     q.qdg_moe_align(ids_dev.data_ptr(), t, top_k, E, bm, sid.data_ptr(), blk.data_ptr(), npad.data_ptr(),
                     q.current_stream())
     plan = q.qdg_plan_create(layer, q.moe(top_k))
+    assert ("family=qtile " if bm == 128 else "family=stream ") in q.qdg_moe_describe(plan, t, bm)
     wsb = q.qdg_plan_workspace(plan, t)
     wsp = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
     a_dev, s_dev = H.dev(codecs.pack_nibbles(ac)), H.dev(ae)
