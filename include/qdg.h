@@ -352,11 +352,17 @@ qdg_status qdg_plan_jit(qdg_plan* plan, int64_t M, int32_t block_m, const char* 
    the kernel instances per M range, with heuristics as the fallback:
    kinachrichten, "Kompilierzeiten und gerätespezifisches Tuning"; jetabc,
    "Humming 的做法", item 2). Times every kernel instance that can serve M
-   rows (weight streaming with several K splits, streaming with every row
-   block and tile count, LDS-tiled shapes) on the caller's buffers, in three
-   interleaved rounds of one untimed launch and reps launches between two
-   events on stream, and records the instance with the lowest round time for
-   M's range: M in (2^(b-1), 2^b], b = 0..31. Later
+   rows (the heuristics' own instance, weight streaming with several K
+   splits, streaming with every row block and tile count, LDS-tiled shapes)
+   in three interleaved rounds of one untimed launch and reps launches
+   between two events on stream. The timed launches rotate over copies of
+   packed that together hold at least 512 MiB (twice the MI355X last-level
+   cache), so no launch finds its weights cache-resident from the one
+   before; the call allocates them with hipMalloc, frees them before it
+   returns, and times on packed alone when the allocation fails. The
+   instance with the lowest round time is recorded for M's range (M in
+   (2^(b-1), 2^b], b = 0..31), except that the heuristics' instance is kept
+   unless the winner is more than 3 % faster. Later
    qdg_gemm, qdg_plan_workspace and qdg_plan_describe calls with an M in that
    range use it ("tuning=autotuned"). Arguments as for qdg_gemm; instances
    whose workspace exceeds ws_bytes are skipped (query qdg_plan_workspace

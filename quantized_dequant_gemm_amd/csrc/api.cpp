@@ -11,6 +11,7 @@
 // gain is a smaller maintenance surface").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -865,6 +866,38 @@ static void autotune_candidates(const qdg_plan& P, int64_t M, qdg_tuning_config*
   }
 }
 
+// Two choices launch the same kernel instance on the same grid.
+static bool same_instance(const Choice& a, const Choice& b) {
+  if (a.tile != b.tile || a.ws != b.ws || a.qtile != b.qtile || a.grid_m != b.grid_m) return false;
+  if (a.sc.mt != b.sc.mt || a.sc.nt != b.sc.nt || a.sc.kw != b.sc.kw || a.sc.split != b.sc.split) return false;
+  return !a.tile || (a.tc.bm == b.tc.bm && a.tc.bn == b.tc.bn && a.tc.waves == b.tc.waves);
+}
+
+// A tuning under which choose_t picks the heuristic's instance for M rows
+// (false if none does).
+static bool tuning_of_heuristic(const qdg_plan& P, int64_t M, qdg_tuning_config* out) {
+  const Choice h = choose_t(P, M, P.tuning, false);
+  qdg_tuning_config t;
+  std::memset(&t, 0, sizeof t);
+  t.block_m = h.tile ? h.tc.bm : h.ws ? 16 : h.sc.mt * 16;
+  t.block_n = h.tile ? h.tc.bn : h.ws ? 0 : h.sc.nt * 16;
+  t.split_k = h.sc.split;
+  t.waves = h.tile ? h.tc.waves : h.ws ? 0 : h.sc.kw;
+  if (check_tuning(P.layer, P.compute, P.fmt, t) != QDG_OK) return false;
+  if (!same_instance(choose_t(P, M, t, true), h)) return false;
+  *out = t;
+  return true;
+}
+
+// Weight copies the autotuner rotates over: together at least twice the
+// 256 MB last-level cache (MALL) of MI355X, so that no timed launch finds
+// its weights cache-resident from the launch before.
+constexpr size_t kRotateBytes = (size_t)512 << 20;
+constexpr int kMaxCopies = 64;
+// A candidate replaces the heuristic's instance only when it is faster by
+// more than the timing noise.
+constexpr float kHeuristicMargin = 0.03f;
+
 qdg_status qdg_plan_autotune(qdg_plan* plan, const void* A, const float* a_scales, const void* packed, void* Y,
                              int64_t M, void* workspace, size_t ws_bytes, int32_t reps, void* stream,
                              qdg_tuning_config* chosen, float* best_us) {
@@ -876,14 +909,41 @@ qdg_status qdg_plan_autotune(qdg_plan* plan, const void* A, const float* a_scale
   if (M < 1 || M > 0x7FFFFFFF / 2) return fail(QDG_ERR_INVALID_ARG, "M must be in [1, 2^30)");
   if (reps < 1 || reps > 1000) return fail(QDG_ERR_INVALID_ARG, "reps must be in [1, 1000]");
   if (!A || !packed || !Y || !workspace) return fail(QDG_ERR_INVALID_ARG, "NULL A, packed, Y or workspace");
-  constexpr int kCap = 48;
+  constexpr int kCap = 49;
   qdg_tuning_config cand[kCap];
+  // candidate 0: the heuristic's own instance, when a tuning reproduces it
   int ncand = 0;
-  autotune_candidates(*plan, M, cand, &ncand, kCap);
+  const bool heur = tuning_of_heuristic(*plan, M, &cand[0]);
+  if (heur) ncand = 1;
+  {
+    int more = 0;
+    autotune_candidates(*plan, M, cand + ncand, &more, kCap - ncand);
+    ncand += more;
+  }
   hipStream_t st = (hipStream_t)stream;
+  // weight copies to rotate over (copy 0 is the caller's buffer); without
+  // device memory for them the timing uses the caller's buffer alone
+  const size_t pb = align_up((int64_t)(plan->geom.expert_stride * plan->geom.experts), 256);
+  int ncopies = (int)std::min<size_t>(kMaxCopies, std::max<size_t>(1, (kRotateBytes + pb - 1) / pb));
+  uint8_t* rot = nullptr;
+  if (ncopies > 1 && hipMalloc((void**)&rot, (ncopies - 1) * pb) != hipSuccess) {
+    (void)hipGetLastError();
+    rot = nullptr;
+    ncopies = 1;
+  }
+  for (int i = 1; i < ncopies; ++i) {
+    if (hipMemcpyAsync(rot + (i - 1) * pb, packed, plan->geom.expert_stride * plan->geom.experts,
+                       hipMemcpyDeviceToDevice, st) != hipSuccess) {
+      (void)hipFree(rot);
+      return fail(QDG_ERR_HIP, "copying the weights for autotuning failed");
+    }
+  }
+  auto copy = [&](int k) -> const void* { return k % ncopies == 0 ? packed : rot + (k % ncopies - 1) * pb; };
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
     if (e0) (void)hipEventDestroy(e0);
+    (void)hipStreamSynchronize(st);
+    if (rot) (void)hipFree(rot);
     return fail(QDG_ERR_HIP, "hipEventCreate failed");
   }
   // Candidates are timed in three interleaved rounds and keep their best
@@ -891,9 +951,15 @@ qdg_status qdg_plan_autotune(qdg_plan* plan, const void* A, const float* a_scale
   // ones timed last.
   bool usable[kCap];
   float t_best[kCap];
+  Choice inst[kCap];
   for (int i = 0; i < ncand; ++i) {
     t_best[i] = -1.f;
     usable[i] = check_tuning(plan->layer, plan->compute, plan->fmt, cand[i]) == QDG_OK;
+    if (!usable[i]) continue;
+    inst[i] = choose_t(*plan, M, cand[i], true);
+    // candidates that launch an instance timed already are not timed again
+    for (int j = 0; j < i && usable[i]; ++j)
+      if (usable[j] && same_instance(inst[i], inst[j])) usable[i] = false;
   }
   qdg_status err = QDG_OK;
   for (int round = 0; round < 3 && err == QDG_OK; ++round) {
@@ -905,8 +971,9 @@ qdg_status qdg_plan_autotune(qdg_plan* plan, const void* A, const float* a_scale
       size_t need = 0;
       usable[i] = instance_exists(plan->fmt, c) && qdg_plan_workspace(plan, M, &need) == QDG_OK && need <= ws_bytes;
       if (usable[i]) {
-        // one untimed launch, then reps launches between two events
-        qdg_status r = qdg_gemm(plan, A, a_scales, packed, Y, M, workspace, ws_bytes, stream);
+        // one untimed launch, then reps launches over the rotated weight
+        // copies between two events
+        qdg_status r = qdg_gemm(plan, A, a_scales, copy(ncopies - 1), Y, M, workspace, ws_bytes, stream);
         if (r == QDG_ERR_UNSUPPORTED || r == QDG_ERR_WORKSPACE) {
           usable[i] = false;
         } else if (r != QDG_OK) {
@@ -914,7 +981,7 @@ qdg_status qdg_plan_autotune(qdg_plan* plan, const void* A, const float* a_scale
         } else {
           hipError_t h = hipEventRecord(e0, st);
           for (int k = 0; k < reps && r == QDG_OK && h == hipSuccess; ++k)
-            r = qdg_gemm(plan, A, a_scales, packed, Y, M, workspace, ws_bytes, stream);
+            r = qdg_gemm(plan, A, a_scales, copy(k), Y, M, workspace, ws_bytes, stream);
           if (h == hipSuccess) h = hipEventRecord(e1, st);
           if (h == hipSuccess) h = hipEventSynchronize(e1);
           float ms = 0.f;
@@ -940,8 +1007,15 @@ qdg_status qdg_plan_autotune(qdg_plan* plan, const void* A, const float* a_scale
       best = i;
       best_t = t_best[i];
     }
+  // keep the heuristic's instance unless the winner beats it by more than noise
+  if (heur && best > 0 && usable[0] && t_best[0] >= 0.f && best_t > t_best[0] * (1.f - kHeuristicMargin)) {
+    best = 0;
+    best_t = t_best[0];
+  }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
+  (void)hipStreamSynchronize(st);  // the launches that read the copies are done
+  if (rot) (void)hipFree(rot);
   if (err != QDG_OK) return err;
   if (best < 0) return fail(QDG_ERR_WORKSPACE, "no kernel instance for M = %lld fits the workspace", (long long)M);
   AutoEntry& e = plan->autot[auto_range(M)];
