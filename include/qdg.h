@@ -261,7 +261,11 @@ qdg_status qdg_quantize_weights(const qdg_layer_config* layer, const float* w,
                                 void* qweight, void* scales, void* zeros, void* stream);
 
 /* Activation quantization for the W8A8 / W4A8 / W4A4 paths (layer->atype
-   INT8, FP8E4M3 or MXFP4). a_bf16 [M][k] row-major ->
+   INT8, FP8E4M3 or MXFP4): the pages' formats lower the precision of the
+   activations as well as of the weights (kinachrichten, "Warum
+   quantisierte Kernel wichtig sind"; the A in W8A8, W4A8, W4A4 counts the
+   activation bits: jetabc, "量化是怎么回事"); the rules below are this
+   library's reading (the pages fix none). a_bf16 [M][k] row-major ->
      INT8:    qa i8 [M][k], a_scales f32 [M];       per token
      FP8E4M3: qa u8 E4M3 [M][k], a_scales f32 [M][k/128]; per 128-group
    with amax the largest |x|, inv = f32(Q/amax) (Q = 127 or 448),
@@ -271,7 +275,11 @@ qdg_status qdg_quantize_weights(const qdg_layer_config* layer, const float* w,
               (as bytes) u8 E8M0 [M][k/32]: per block of 32 the MXFP4 rule of
               qdg_quantize_weights (an all-zero block stores E8M0 code 0 and
               zero codes; a negative value that rounds to zero keeps its sign).
-   Bit-exact by construction (binary32, RNE). */
+   Bit-exact by construction (binary32, RNE). All pointers are device
+   pointers owned by the caller; a_bf16 and qa 16-byte aligned, a_scales
+   4-byte aligned (else QDG_ERR_MISALIGNED); M >= 0 (0 enqueues nothing).
+   QDG_ERR_INVALID_ARG for NULL pointers or M < 0, QDG_ERR_UNSUPPORTED for
+   a layer with bf16 activations or M >= 2^31. */
 qdg_status qdg_quantize_act(const qdg_layer_config* layer, const void* a_bf16, int64_t M,
                             void* qa, float* a_scales, void* stream);
 
@@ -283,10 +291,14 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
 void qdg_plan_destroy(qdg_plan* plan);
 
 /* Workspace bytes qdg_gemm / qdg_moe_gemm need for M rows (M = T for MoE).
-   It holds fp32 split-K partials (added by a second kernel in split order)
-   and, for the LDS-tiled W4A16 family, the row sums of A; its contents need
-   no initialisation (the first 64 KiB are reserved). Calls that share one
-   workspace must be ordered on one stream. */
+   The scratch the kernel instance that serves M uses (the instance differs
+   by M range: kinachrichten, "Wie die Architektur funktioniert"): fp32
+   split-K partials (added by a second kernel in split order), the row sums
+   of A for the LDS-tiled bf16 family, and the two E4M3 planes of the int8
+   activations of the MXFP4 x INT8 path. Its contents need no
+   initialisation (the first 64 KiB are reserved). Calls that share one
+   workspace must be ordered on one stream. QDG_ERR_INVALID_ARG for a NULL
+   plan or bytes, or M < 0. */
 qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes);
 
 /* Writes a one-line record of the kernel instance that serves M rows (family,
@@ -299,14 +311,30 @@ int qdg_plan_describe(const qdg_plan* plan, int64_t M, char* buf, size_t len);
    Returns the record length, -1 on error (not a MoE plan, bad block_m). */
 int qdg_moe_describe(const qdg_plan* plan, int64_t T, int32_t block_m, char* buf, size_t len);
 
-/* Dense GEMM Y[M][n] = A[M][k] * dequant(W)^T.
-   A: bf16 [M][k] (W4A16), i8 [M][k] (W8A8, W4A8) or E4M3 [M][k] (MXFP4), row
-      stride k elements, 16-byte aligned.
-   a_scales: NULL for W4A16; f32 [M] (W8A8, W4A8); f32 [M][k/128] (MXFP4);
-      ignored (may be NULL) with otype I32.
-   packed: the qdg_preprocess output for this layer.
-   Y: [M][n] of otype (bf16, f32 or i32), row stride n.
-   M >= 0 (M = 0 enqueues nothing). workspace >= qdg_plan_workspace bytes. */
+/* Dense GEMM Y[M][n] = dequant(A)[M][k] * dequant(W)^T: the quantized
+   linear layer, weights (and for the 8- and 4-bit activation formats the
+   activations) at reduced precision (kinachrichten, "Warum quantisierte
+   Kernel wichtig sind"), dequantization and scaling applied inside the one
+   kernel that feeds the matrix cores (kinachrichten, "Kompilierzeiten und
+   gerätespezifisches Tuning"), the kernel instance picked per M range
+   (kinachrichten, "Wie die Architektur funktioniert").
+   A (row stride k elements, 16-byte aligned):
+      bf16 [M][k]   W4A16 (INT4, UINT4), W8A16, W4A16-NVFP4, W2A16;
+      i8 [M][k]     W8A8, W4A8-INT8, W4A8-MXFP4-INT8;
+      E4M3 [M][k]   W4A8-MXFP4;
+      u8 [M][k/2]   W4A4 (E2M1 codes, even k in the low nibble).
+   a_scales: NULL for the bf16 formats; f32 [M] for the int8 formats
+      (ignored, may be NULL, with otype I32); f32 [M][k/128] for W4A8-MXFP4;
+      u8 E8M0 [M][k/32] for W4A4 (passed through this pointer).
+   packed: the qdg_preprocess output for this layer (256-byte aligned).
+   Y: [M][n] of otype (bf16, f32, or i32 for W8A8 / W4A8-INT8 only: the
+      exact integer accumulators), row stride n, aligned to its element.
+   M >= 0 (M = 0 enqueues nothing). workspace >= qdg_plan_workspace bytes,
+   256-byte aligned. All pointers are device pointers owned by the caller.
+   Errors: QDG_ERR_INVALID_ARG (NULL plan or operand, a MoE plan, M < 0),
+   QDG_ERR_MISALIGNED, QDG_ERR_WORKSPACE, QDG_ERR_UNSUPPORTED (A beyond the
+   serving family's addressing: 2 GiB streaming, 4 GiB tiled), QDG_ERR_HIP
+   (a launch failed). */
 qdg_status qdg_gemm(const qdg_plan* plan, const void* A, const float* a_scales, const void* packed,
                     void* Y, int64_t M, void* workspace, size_t ws_bytes, void* stream);
 
@@ -405,17 +433,30 @@ qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int3
                          int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                          int32_t* num_padded, uint32_t* status, void* stream);
 
-/* Grouped MoE GEMM: for every real entry i of sorted_ids in block b,
-   row i of Y = A[r] * dequant(W_e)^T with e = block_expert[b] and
-   r = i (a_per_pair = 1, e.g. the down projection) or r = i / top_k
-   (a_per_pair = 0, e.g. gate+up reading token rows). Y is [T*top_k][n];
-   rows are written only for real pairs. A and a_scales are laid out as for
-   qdg_gemm with one row per r (the int8 / fp8 formats take the codes and
-   scales of qdg_quantize_act over those rows). block_m must be the value
-   passed to qdg_moe_align. W4A16: 16, 32 or 64 (streaming family; a tuning
-   with block_n 64 and 8 waves pins the weight-streaming family for 16) or
-   128 (LDS-tiled family; batch-invariant plans take 16 to 64). W8A8, W4A8-INT8, W4A8-MXFP4: 16, 32 or 64 (streaming family;
-   128 returns QDG_ERR_UNSUPPORTED). */
+/* Grouped MoE GEMM (the pages' grouped MoE path, jetabc, "跑得有多快": each
+   token activates a few of the stored experts, kinachrichten, "Warum
+   quantisierte Kernel wichtig sind"; every format serves dense and MoE
+   layers alike, kinachrichten, "Was Humming bietet"): for every real entry
+   i of sorted_ids in block b, row i of Y = A[r] * dequant(W_e)^T with
+   e = block_expert[b] and r = i (a_per_pair = 1, e.g. the down projection)
+   or r = i / top_k (a_per_pair = 0, e.g. gate+up reading token rows).
+   Y is [T*top_k][n] (the SiLU*mul epilogue: [T*top_k][n/2]); rows are
+   written only for real pairs. A and a_scales are laid out as for qdg_gemm
+   with one row per r (the 8- and 4-bit activation formats take the codes
+   and scales of qdg_quantize_act over those rows). block_m must be the
+   value passed to qdg_moe_align:
+     16, 32, 64   every format (streaming family; for W4A16 a tuning with
+                  block_n 64 and 8 waves pins the weight-streaming family
+                  for 16);
+     128          W4A16 (LDS-tiled family, the SiLU*mul epilogue included),
+                  NVFP4 and W8A16 (LDS-tiled bf16 family), W8A8, W4A8-INT8,
+                  W4A8-MXFP4 and W4A4 (8-bit LDS-tiled family), the last five
+                  without an epilogue; batch-invariant plans, the SiLU*mul
+                  epilogue of the other formats, W4A8-MXFP4-INT8 and W2A16
+                  return QDG_ERR_UNSUPPORTED.
+   workspace >= qdg_plan_workspace(plan, T) bytes. Errors as for qdg_gemm,
+   plus QDG_ERR_INVALID_ARG for a dense plan or NULL routing arrays and
+   QDG_ERR_UNSUPPORTED for another block_m or T*top_k > 2^20. */
 qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scales,
                         const void* packed, const int32_t* sorted_ids,
                         const int32_t* block_expert, const int32_t* num_padded, int64_t T,
