@@ -13,9 +13,10 @@
 //     next U groups are issued before the current ones are consumed (register
 //     double buffering) to keep enough bytes in flight per CU;
 //   * dequantization happens in registers right before the MFMA;
-//   * the KW wave partials are reduced through LDS in a fixed order, and the
-//     `split` partitions through the caller's workspace by the last-arriving
-//     workgroup, again in a fixed order, so results are deterministic.
+//   * the KW wave partials are reduced through LDS in a fixed order; with
+//     `split` > 1 every workgroup writes its fp32 partial into the caller's
+//     workspace and reduce_splits_kernel adds the partitions in split order,
+//     so results are deterministic.
 // The five component roles the pages name for their CUDA layer (scheduling,
 // data movement, dequantization and scaling, matrix-core compute, output
 // processing; kinachrichten, "Kompilierzeiten und gerätespezifisches Tuning")
