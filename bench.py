@@ -441,11 +441,12 @@ def rows_leg(reps=30):
         ids = torch.topk(logits, top_k, dim=1).indices.to(torch.int32).contiguous()
         touched = int(torch.unique(ids).numel())
         # expert block size (the caller's choice in the API; measured on
-        # MI355X): 16-row blocks while most experts hold few rows, 128-row
-        # blocks beyond
-        small = t * top_k <= 32 * E
+        # MI355X): 16-row streaming blocks while experts hold a few rows
+        # (T = 64), 32-row tiled blocks around 16 rows per expert (T = 512),
+        # 128-row tiled blocks beyond
+        blk_m = 16 if t * top_k <= 4 * E else 32 if t * top_k <= 32 * E else 128
         aligned = {}
-        for bm in (16,) if small else (128,):
+        for bm in (blk_m,):
             cap = q.qdg_moe_align_capacity(t, top_k, E, bm)
             sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
             block_expert = torch.empty(cap // bm, dtype=torch.int32, device=dev)
@@ -458,7 +459,7 @@ def rows_leg(reps=30):
             aligned[bm] = (sorted_ids, block_expert, npad, _time_launches(align, reps, stream))
         for name, (layer, pk, n, k, plan) in layers.items():
             per_pair = name == "moe-down"
-            bm = 16 if small else 128
+            bm = blk_m
             sorted_ids, block_expert, npad, us_align = aligned[bm]
             rows_in = t * top_k if per_pair else t
             a = synth.device_activations_bf16(rows_in, k, seed=synth.seed_for(4, synth.TID_H, t + k))

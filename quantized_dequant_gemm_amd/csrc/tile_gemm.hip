@@ -109,7 +109,8 @@ __global__ void reduce_splits_kernel(const float* __restrict__ partial, void* __
 //          16-byte LDS read always hit distinct banks, and every fragment
 //          address is one per-lane base plus an immediate offset)
 //   RS     BM floats (row sums, pre-scaled), in a slot of at least 1 KiB
-//          so that one whole-wave copy fills it
+//          so that one whole-wave copy fills it, starting at the next 1 KiB
+//          boundary after A (the A copies move whole 1 KiB spans)
 //   W      BN/16 packed weight units of UB bytes (1 KiB for 4-bit codes, 2 KiB
 //          for int8; tile-major)
 //   S      BN/16 x 16 scale records of 8 bytes
@@ -118,7 +119,8 @@ struct Stage {
   static constexpr int ROW = 272;
   static constexpr int A = 0;
   static constexpr int A_SLOTS = BM * ROW / 16;  // 16-byte slots, 17 per row
-  static constexpr int RS = BM * ROW;
+  // whole 1 KiB copies fill A (the last one may run past BM rows)
+  static constexpr int RS = (BM * ROW + 1023) / 1024 * 1024;
   static constexpr int W = RS + (BM * 4 > 1024 ? BM * 4 : 1024);
   static constexpr int S = W + (BN / 16) * UB;
   static constexpr int BYTES = S + (BN / 16) * 128;
@@ -702,8 +704,8 @@ template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE, bool NV = fals
 hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s) {
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
   // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256, 2 for 256 x 128
-  // and for int8 units)
-  constexpr int NS = 3 * Stage<BM, BN, W8 ? 2048 : 1024>::BYTES <= 160 * 1024 ? 3 : 2;
+  // and for int8 units); 32-row blocks take 2 so that two workgroups share a CU
+  constexpr int NS = BM > 32 && 3 * Stage<BM, BN, W8 ? 2048 : 1024>::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
   hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE, NV, W8>), dim3(m_blocks * n_blocks, nsplit),
                      dim3(64 * WAVES_M * WAVES_N), 0, s, a, m_blocks, n_blocks);
@@ -713,13 +715,15 @@ hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStrea
 }  // namespace
 
 // Instances: (block_m, block_n, waves) = (256, 128, 8), (128, 256, 8) with
-// 64 x 64 wave tiles (two waves per SIMD) and (128, 256, 4) with 128 x 64
-// wave tiles (one wave per SIMD, half the unpack work per MFMA).
+// 64 x 64 wave tiles (two waves per SIMD), (128, 256, 4) with 128 x 64
+// wave tiles (one wave per SIMD, half the unpack work per MFMA) and, for
+// grouped MoE blocks of 32 rows, (32, 256, 4) with 32 x 64 wave tiles.
 bool tile_cfg_supported(Format f, const TileCfg& c) {
   if (f == FMT_NVFP4 || f == FMT_W8A16) return c.bm == 128 && c.bn == 256 && c.waves == 8;
   if (f != FMT_W4A16) return false;
   if (c.bm == 256 && c.bn == 128) return c.waves == 8;
   if (c.bm == 128 && c.bn == 256) return c.waves == 8 || c.waves == 4;
+  if (c.bm == 32 && c.bn == 256) return c.waves == 4;
   return false;
 }
 
@@ -743,6 +747,7 @@ hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const Ge
   QDG_T(true, 1, 4, 128, false)
   QDG_T(false, 2, 4, 64, true)
   QDG_T(false, 1, 4, 128, true)
+  QDG_T(false, 1, 4, 32, true)
 #undef QDG_T
   return hipErrorInvalidValue;
 }

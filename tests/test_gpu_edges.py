@@ -172,13 +172,13 @@ def test_moe_w4a16_int4_minus8_one_hot(qdg, bm):
     a = np.zeros((t, k), np.float32)
     a[np.arange(t), kt] = 1.0
     y, desc = _moe_run(layer, pk, H.bf16_dev(codecs.f32_to_bf16_bits(a)), None, ids, bm, 0)
-    assert ("family=tile" in desc) == (bm == 128)
+    assert ("family=tile" in desc) == (bm in (32, 128))
     want = np.stack([ref.dequant_int4_sym(vs[ids[p // top_k, p % top_k]], ss[ids[p // top_k, p % top_k]])[:, kt[p // top_k]]
                      for p in range(t * top_k)])
     assert np.array_equal(H.to_f64(y), want)
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
 @pytest.mark.parametrize("kind", ["w4a8", "w8a8"])
 def test_moe_int8_extreme_codes_raw_exact(qdg, kind, bm):
     E, top_k, k, n, t = 3, 2, 256, 96, 90
@@ -196,7 +196,7 @@ def test_moe_int8_extreme_codes_raw_exact(qdg, kind, bm):
         layer = q.layer_w8a8(n, k, num_experts=E, otype=q.QDG_O_I32)
         pk = H.Packed(layer, H.dev(np.stack(vs).astype(np.int8)), H.dev(np.full((E, n), 0.25, np.float32)))
     y, desc = _moe_run(layer, pk, H.dev(h.astype(np.int8)), None, ids, bm, 1)
-    assert "family=stream" in desc
+    assert ("family=qtile " if bm == 128 else "family=stream ") in desc
     flat = ids.reshape(-1)
     want = np.stack([ref.int_matmul(h[p:p + 1], vs[flat[p]])[0] for p in range(t * top_k)])
     assert np.array_equal(y.cpu().numpy().astype(np.int64), want)

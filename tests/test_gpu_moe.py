@@ -60,10 +60,10 @@ def _moe_packed(qs, ss, n, k):
     return layer, H.Packed(layer, qw, sc)
 
 
-def _moe_gemm(layer, pk, a_dev, ids, bm, a_per_pair, top_k, tuning=None):
+def _moe_gemm(layer, pk, a_dev, ids, bm, a_per_pair, top_k, tuning=None, batch_invariant=0):
     t = ids.shape[0]
     sid, blk, npad, cap = _align_dev(ids, layer.num_experts, bm)
-    plan = q.qdg_plan_create(layer, q.moe(top_k), tuning)
+    plan = q.qdg_plan_create(layer, q.moe(top_k, batch_invariant=batch_invariant), tuning)
     ws, nbytes = H.workspace(plan, t)
     y = H.out_tensor(t * top_k, layer.n, q.QDG_O_BF16)
     q.qdg_moe_gemm(plan, a_dev.data_ptr(), None, pk.buf.data_ptr(), sid.data_ptr(), blk.data_ptr(),
@@ -97,17 +97,18 @@ def test_moe_single_expert_equals_dense(qdg, bm, pin_ws):
     # everything routed to expert 0 of 2: the MoE blocks hold the same rows as
     # the dense GEMM run block by block with the same kernel family, so every
     # output matches bitwise (16-row blocks with this short K: streaming, or
-    # weight streaming when a tuning pins it; 32: streaming; 128: LDS-tiled)
+    # weight streaming when a tuning pins it; 32: the batch-invariant plan's
+    # streaming blocks; 128: LDS-tiled)
     t, hid, n = 40, 512, 128
     qs, ss = _experts(2, n, hid, salt=3)
     layer, pk = _moe_packed(qs, ss, n, hid)
     x = synth.activations_bf16_bits(t, hid, workload_id=4, salt=5)
     ids = np.zeros((t, 1), np.int32)
     tm = q.TuningConfig(block_n=64, waves=8) if pin_ws else None
-    plan = q.qdg_plan_create(layer, q.moe(1), tm)
+    plan = q.qdg_plan_create(layer, q.moe(1, batch_invariant=int(bm == 32)), tm)
     fam = q.qdg_moe_describe(plan, t, bm).split("family=")[1].split()[0]
     assert fam == {16: "wstream" if pin_ws else "stream", 32: "stream", 128: "tile"}[bm]
-    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 0, 1, tuning=tm)
+    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 0, 1, tuning=tm, batch_invariant=int(bm == 32))
     if bm == 16 and pin_ws:
         t1 = q.TuningConfig(block_m=16, block_n=64, split_k=1)
         yd = torch.cat([H.w4a16(x[r:r + 16], qs[0], ss[0], None, tuning=t1) for r in range(0, t, 16)])
@@ -155,7 +156,7 @@ def test_moe_full_size_sampled_rows(qdg, proj, t, bm):
         x = synth.activations_bf16_bits(t, k, workload_id=4)
     y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 1 if per_pair else 0, top_k)
     fam = q.qdg_moe_describe(q.qdg_plan_create(layer, q.moe(top_k)), t, bm).split("family=")[1].split()[0]
-    assert fam == ("tile" if bm == 128 else "stream")
+    assert fam == ("tile" if bm in (32, 128) else "stream")
     xf = codecs.bf16_bits_to_f64(x)
     for p in pairs:
         e = int(ids.reshape(-1)[p])
@@ -168,15 +169,15 @@ def test_moe_full_size_sampled_rows(qdg, proj, t, bm):
     assert not torch.isnan(y.float()).any()
 
 
-@pytest.mark.parametrize("t,bm,inter", [(8, 16, 256), (64, 16, 144), (64, 32, 256), (300, 64, 256),
+@pytest.mark.parametrize("t,bm,inter", [(8, 16, 256), (64, 16, 144), (64, 32, 256), (64, 32, 144), (300, 64, 256),
                                          (300, 64, 144), (300, 128, 256), (1024, 128, 144)])
 @pytest.mark.parametrize("otype", [q.QDG_O_F32, q.QDG_O_BF16])
 def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, inter, otype):
     # fused gate+up (n = 2I) with the SiLU*mul epilogue: Y = silu(G) * U,
-    # [T*top_k][I]; 16-64-row blocks run the streaming family (four tiles,
-    # two gate + two up, per workgroup at 16 rows, else two), 128-row blocks
-    # the LDS-tiled one (I = 144: an odd number of gate tiles, so a
-    # workgroup's tile slots run partly past the layer)
+    # [T*top_k][I]; 16- and 64-row blocks run the streaming family (four
+    # tiles, two gate + two up, per workgroup at 16 rows, else two), 32- and
+    # 128-row blocks the LDS-tiled one (I = 144: an odd number of gate tiles,
+    # so a workgroup's tile slots run partly past the layer)
     E, top_k, hid = 16, 4, 1024
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=t + 11), top_k)
     qs, ss = _experts(E, 2 * inter, hid, salt=9)
@@ -189,7 +190,7 @@ def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, inter, otype):
     sid, blk, npad, cap = _align_dev(ids, E, bm)
     plan = q.qdg_plan_create(layer, q.moe(top_k, epilogue=q.QDG_EPI_SILU_MUL))
     desc = q.qdg_moe_describe(plan, t, bm)
-    assert "epilogue=silu_mul" in desc and ("family=tile" in desc) == (bm == 128)
+    assert "epilogue=silu_mul" in desc and ("family=tile" in desc) == (bm in (32, 128))
     ws, nbytes = H.workspace(plan, t)
     y = H.out_tensor(t * top_k, inter, otype)
     q.qdg_moe_gemm(plan, a_dev.data_ptr(), None, pk.buf.data_ptr(), sid.data_ptr(), blk.data_ptr(),
