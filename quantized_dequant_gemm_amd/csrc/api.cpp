@@ -636,10 +636,11 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
     c.sc = StreamCfg{block_m / 16, block_m == 16 ? 4 : 2, 4, 1};
   c.tile = false;
   c.qtile = false;
-  // 32- and 128-row blocks: the LDS-tiled family (32 x 256 and 128 x 256
+  // 32- and 128-row blocks: the LDS-tiled family (32 x 512 and 128 x 256
   // tiles); measured on MI355X at E = 256, hidden 7168, T = 512, 32-row
-  // blocks in it run gate+up in 1138 us and down in 609 us, against 1467 and
-  // 1107 us in the streaming family (1284 and 761 us with 16-row blocks)
+  // blocks in it run gate+up in 1112 us and down in 577-588 us (32 x 256
+  // tiles: 1185-1208 and 618-622 us), against 1467 and 1107 us in the
+  // streaming family (1284 and 761 us with 16-row blocks)
   if (block_m == 128 || (block_m == 32 && !plan.compute.batch_invariant)) {
     // A rows are addressed with 32-bit byte offsets in the tiled family
     const int64_t a_rows = a_per_pair ? rows : T;
@@ -650,7 +651,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
       return fail(QDG_ERR_UNSUPPORTED, "batch-invariant MoE plans use block_m <= 64");
     c.tile = true;
     c.ws = false;
-    c.tc = block_m == 128 ? TileCfg{128, 256, 8} : TileCfg{32, 256, 4};
+    c.tc = block_m == 128 ? TileCfg{128, 256, 8} : TileCfg{32, 512, 8};
   } else if (!c.ws && !stream_cfg_supported(plan.fmt, c.sc)) {
     return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
   }

@@ -133,14 +133,17 @@ struct Stage {
 // builtin inside an (implicitly host+device) lambda makes the host pass drop
 // the kernel.
 // Packed N tile behind stage tile t of a workgroup whose tiles start at
-// `base`. With the SiLU*mul epilogue (16 stage tiles) the first 8 are gate
-// tiles base.. and the last 8 the matching up tiles G + base.. (G = I / 16);
-// tiles past the layer re-read the last one and are never stored.
+// `base`. With the SiLU*mul epilogue (BN / 16 stage tiles) the first half are
+// gate tiles base.. and the second half the matching up tiles G + base..
+// (G = I / 16); tiles past the layer re-read the last one and are never
+// stored.
+template <int BN>
 __device__ __forceinline__ int stage_tile(const GemmArgs& p, int base, int t) {
+  constexpr int HALF = BN / 32;
   if (p.epi == QDG_EPI_SILU_MUL) {
     const int G = p.ntiles / 2;
-    const int j = min(base + (t & 7), G - 1);
-    return t < 8 ? j : G + j;
+    const int j = min(base + t % HALF, G - 1);
+    return t < HALF ? j : G + j;
   }
   return min(base + t, p.ntiles - 1);
 }
@@ -167,7 +170,7 @@ __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint
   for (int r = 0; r < (BN / 16) * WC / NW; ++r) {
     const int ci = r * NW + wave;
     const int t = ci / WC, part = ci % WC;
-    const int tile = stage_tile(p, wg_tile0, t);
+    const int tile = stage_tile<BN>(p, wg_tile0, t);
     __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * UB + part * 1024 + lane * 16,
                                      (lds_void*)(st + L::W + t * UB + part * 1024), 16, 0, 0);
   }
@@ -437,7 +440,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   // SiLU*mul (MoE gate+up): 16 stage tiles = 8 gate + 8 up tiles, i.e. 8
   // output tiles per workgroup
   const bool silu = MOE && !NV && !W8 && p.epi == QDG_EPI_SILU_MUL;  // W4A16 only
-  static_assert(!MOE || BN == 256, "the SiLU*mul pairing assumes 16 stage tiles");
+  static_assert(!MOE || WAVES_N % 2 == 0, "the SiLU*mul pairing splits the waves' columns in halves");
   const int wg_tile0 = silu ? nb * (BN / 32) : nb * (BN / 16);
 
   // A copy plan: slot q = 64 i + lane of the padded tile is row q / 17,
@@ -462,7 +465,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   // copy r = wave % (BN / 128)
   uint32_t s_off;
   {
-    const int s_tile = stage_tile(p, wg_tile0, 8 * (wave % (BN / 128)) + (lane >> 3));
+    const int s_tile = stage_tile<BN>(p, wg_tile0, 8 * (wave % (BN / 128)) + (lane >> 3));
     s_off = (uint32_t)s_tile * (uint32_t)groups * 128u + (lane & 7) * 16;
   }
 
@@ -560,11 +563,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   __builtin_amdgcn_s_waitcnt(0);  // the trailing copies have landed
   __syncthreads();                 // everyone is done with the stages
   if (silu) {
-    // gate columns sit in waves wn = 0, 1 and the matching up columns in
-    // waves wn + 2: per 16-row strip every wave parks its fp32 values in LDS,
-    // then the gate waves form silu(G) * U and store I-wide rows
+    // gate columns sit in waves wn < WAVES_N / 2 and the matching up columns
+    // in waves wn + WAVES_N / 2: per 16-row strip every wave parks its fp32
+    // values in LDS, then the gate waves form silu(G) * U and store I-wide rows
     float* own = (float*)(st0 + wave * (16 * 64 * 4));
-    const float* up = (const float*)(st0 + (wave + 2) * (16 * 64 * 4));
+    const float* up = (const float*)(st0 + (wave + WAVES_N / 2) * (16 * 64 * 4));
     const int I = p.N / 2;
     const bool f32o = p.otype == QDG_O_F32;
 #pragma unroll
@@ -585,7 +588,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (wn < 2) {
+      if (wn < WAVES_N / 2) {
         for (int chunk = lane; chunk < 16 * 16; chunk += 64) {  // 16 rows x 16 chunks of 4 columns
           const int r = chunk >> 4, cc = chunk & 15;
           const int lrow = mb * BM + wm * WTM + mt * 16 + r;
@@ -703,9 +706,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
 template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE, bool NV = false, bool W8 = false>
 hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s) {
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
-  // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256, 2 for 256 x 128
-  // and for int8 units); 32-row blocks take 2 so that two workgroups share a CU
-  constexpr int NS = BM > 32 && 3 * Stage<BM, BN, W8 ? 2048 : 1024>::BYTES <= 160 * 1024 ? 3 : 2;
+  // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256 and 32 x 512,
+  // 2 for 256 x 128 and for int8 units)
+  constexpr int NS = 3 * Stage<BM, BN, W8 ? 2048 : 1024>::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
   hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE, NV, W8>), dim3(m_blocks * n_blocks, nsplit),
                      dim3(64 * WAVES_M * WAVES_N), 0, s, a, m_blocks, n_blocks);
@@ -717,13 +720,16 @@ hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStrea
 // Instances: (block_m, block_n, waves) = (256, 128, 8), (128, 256, 8) with
 // 64 x 64 wave tiles (two waves per SIMD), (128, 256, 4) with 128 x 64
 // wave tiles (one wave per SIMD, half the unpack work per MFMA) and, for
-// grouped MoE blocks of 32 rows, (32, 256, 4) with 32 x 64 wave tiles.
+// grouped MoE blocks of 32 rows, (32, 512, 8) with 32 x 64 wave tiles (one
+// workgroup per CU with three stages; measured on MI355X at E = 256, hidden
+// 7168, T = 512: 7 % faster than (32, 256, 4) with two stages and two
+// workgroups per CU).
 bool tile_cfg_supported(Format f, const TileCfg& c) {
   if (f == FMT_NVFP4 || f == FMT_W8A16) return c.bm == 128 && c.bn == 256 && c.waves == 8;
   if (f != FMT_W4A16) return false;
   if (c.bm == 256 && c.bn == 128) return c.waves == 8;
   if (c.bm == 128 && c.bn == 256) return c.waves == 8 || c.waves == 4;
-  if (c.bm == 32 && c.bn == 256) return c.waves == 4;
+  if (c.bm == 32 && c.bn == 512) return c.waves == 8;
   return false;
 }
 
@@ -747,7 +753,7 @@ hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const Ge
   QDG_T(true, 1, 4, 128, false)
   QDG_T(false, 2, 4, 64, true)
   QDG_T(false, 1, 4, 128, true)
-  QDG_T(false, 1, 4, 32, true)
+  QDG_T(false, 1, 8, 32, true)
 #undef QDG_T
   return hipErrorInvalidValue;
 }
