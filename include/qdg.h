@@ -450,11 +450,11 @@ qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int3
                   for 16, and 32 runs the LDS-tiled family with 32 x 512
                   tiles unless the plan is batch-invariant);
      128          W4A16 (LDS-tiled family, the SiLU*mul epilogue included),
-                  NVFP4 and W8A16 (LDS-tiled bf16 family), W8A8, W4A8-INT8,
-                  W4A8-MXFP4 and W4A4 (8-bit LDS-tiled family), the last five
-                  without an epilogue; batch-invariant plans, the SiLU*mul
-                  epilogue of the other formats, W4A8-MXFP4-INT8 and W2A16
-                  return QDG_ERR_UNSUPPORTED.
+                  NVFP4, W8A16 and W2A16 (LDS-tiled bf16 family), W8A8,
+                  W4A8-INT8, W4A8-MXFP4 and W4A4 (8-bit LDS-tiled family),
+                  all but W4A16 without an epilogue; batch-invariant plans, the SiLU*mul
+                  epilogue of the other formats and W4A8-MXFP4-INT8 return
+                  QDG_ERR_UNSUPPORTED.
    workspace >= qdg_plan_workspace(plan, T) bytes. Errors as for qdg_gemm,
    plus QDG_ERR_INVALID_ARG for a dense plan or NULL routing arrays and
    QDG_ERR_UNSUPPORTED for another block_m or T*top_k > 2^20. */

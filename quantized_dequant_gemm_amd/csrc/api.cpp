@@ -240,17 +240,21 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   if (!bm) bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
   // measured on MI355X: one (partly filled) 128-row block of the tiled
   // families, with K split into one pass of workgroups, beats the streaming
-  // family from M = 33 (bf16 activations: W4A16, NVFP4, W8A16) and from
-  // M = 64 (int8 / fp8 / fp4 activations)
-  const bool bf16_act = P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4 || P.fmt == FMT_W8A16;
-  // MXFP4 weights with int8 activations run the streaming family at every M
-  const bool stream_only = P.fmt == FMT_MXFP4_I8 || P.fmt == FMT_W2A16;
+  // family from M = 33 (bf16 activations: W4A16, NVFP4, W8A16, W2A16) and
+  // from M = 64 (int8 / fp8 / fp4 activations)
+  const bool bf16_act = P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4 || P.fmt == FMT_W8A16 || P.fmt == FMT_W2A16;
+  // MXFP4 weights with int8 activations run the streaming family at every M;
+  // W2A16 has no weight-streaming variant (the streaming family serves its
+  // small M)
+  const bool stream_only = P.fmt == FMT_MXFP4_I8;
+  const bool no_wstream = stream_only || P.fmt == FMT_W2A16;
   if (!has_tuning && !P.compute.batch_invariant && !moe && !stream_only && bm < 128 && M > (bf16_act ? 32 : 63))
     bm = 128;
   if (P.compute.batch_invariant && bm > 64) bm = 64;
   // the tiled family addresses A with 32-bit byte offsets
   const bool a_fits = (double)(M > 0 ? M : 1) * (double)g.k * 2.0 < 4294967296.0;
-  if (bm >= 128 && (P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4 || P.fmt == FMT_W8A16) && !moe && a_fits) {
+  if (bm >= 128 && (P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4 || P.fmt == FMT_W8A16 || P.fmt == FMT_W2A16) && !moe &&
+      a_fits) {
     // LDS-tiled family: BM x 128 tiles, row sums of A per group in the workspace
     ch.tile = true;
     ch.tc.bm = bm;
@@ -294,7 +298,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   // weight-streaming family of the int8 / fp8 formats (dense M <= 16): the
   // K range of a workgroup must fit its LDS; raw int32 output is not split
   if (bm == 16 && P.fmt != FMT_W4A16 && P.fmt != FMT_W4A4 && P.fmt != FMT_W8A16 && P.fmt != FMT_NVFP4 && !moe &&
-      !stream_only &&
+      !no_wstream &&
       !P.compute.batch_invariant &&
       ws_tuning_ok) {
     // 4 N tiles per workgroup when that gives enough workgroups, else one
@@ -330,7 +334,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
     stream_mid = P.fmt == FMT_W4A4 || (P.fmt == FMT_W8A8 && 2 * stream_wgs <= kTargetWorkgroups);
   }
   const bool q_enough = (has_tuning && T.block_m >= 128) || (M >= 64 && !stream_mid);
-  if (bm >= 128 && P.fmt != FMT_W4A16 && P.fmt != FMT_W8A16 && P.fmt != FMT_NVFP4 && !stream_only && !moe &&
+  if (bm >= 128 && P.fmt != FMT_W4A16 && P.fmt != FMT_W8A16 && P.fmt != FMT_NVFP4 && !no_wstream && !moe &&
       a8_fits && q_enough) {
     ch.tile = true;
     ch.qtile = true;
@@ -411,7 +415,7 @@ bool instance_exists(Format f, const Choice& c) {
 qdg_status check_tuning(const qdg_layer_config& layer, const qdg_compute_config& compute, Format f,
                         const qdg_tuning_config& tuning) {
   const bool dense_tiled = compute.kind == QDG_KIND_DENSE && !compute.batch_invariant;
-  const bool tile_ok = dense_tiled && f != FMT_MXFP4_I8 && f != FMT_W2A16 &&
+  const bool tile_ok = dense_tiled && f != FMT_MXFP4_I8 &&
                        (tuning.block_m == 128 || (f == FMT_W4A16 && tuning.block_m == 256));
   if (tuning.block_m && tuning.block_m != 16 && tuning.block_m != 32 && tuning.block_m != 64 && !tile_ok)
     return fail(QDG_ERR_UNSUPPORTED,
@@ -560,7 +564,8 @@ qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes) {
   if (M < 0) return fail(QDG_ERR_INVALID_ARG, "M < 0");
   const Choice c = choose(*plan, M > 0 ? M : 1);
   int64_t rowsum = (int64_t)c.rowsum_bytes;
-  if (plan->compute.kind == QDG_KIND_MOE && (plan->fmt == FMT_W4A16 || plan->fmt == FMT_W8A16)) {
+  if (plan->compute.kind == QDG_KIND_MOE &&
+      (plan->fmt == FMT_W4A16 || plan->fmt == FMT_W8A16 || plan->fmt == FMT_W2A16)) {
     // MoE: room for the row sums of 128-row blocks (the largest block size)
     const int64_t cap =
         align_up((M > 0 ? M : 1) * plan->compute.top_k + plan->layer.num_experts * 127, 128);
@@ -601,9 +606,10 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   c.ws = block_m == 16 && !plan.compute.batch_invariant && !silu && ws_pinned;
   if (plan.fmt != FMT_W4A16) {
     // every other format: the streaming family, block_m / 16 row tiles; 128-row
-    // blocks (plain output only) run in the LDS-tiled families: NVFP4 and
-    // W8A16 in the bf16 one, W8A8, W4A8 and the MXFP4 formats in the 8-bit one
-    const bool tiled_fmt = plan.fmt == FMT_NVFP4 || plan.fmt == FMT_W8A16;
+    // blocks (plain output only) run in the LDS-tiled families: NVFP4, W8A16
+    // and W2A16 in the bf16 one, W8A8, W4A8 and the MXFP4 formats in the
+    // 8-bit one
+    const bool tiled_fmt = plan.fmt == FMT_NVFP4 || plan.fmt == FMT_W8A16 || plan.fmt == FMT_W2A16;
     const bool qtiled_fmt = plan.fmt == FMT_W8A8 || plan.fmt == FMT_W4A8 || plan.fmt == FMT_MXFP4 ||
                             plan.fmt == FMT_W4A4;
     const bool tiled = block_m == 128 && (tiled_fmt || qtiled_fmt) && !silu && !plan.compute.batch_invariant;
@@ -623,7 +629,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
       c.tc = TileCfg{128, 256, 8};
       if (tiled_fmt) {
         c.tile = true;
-        if (plan.fmt == FMT_W8A16) c.rowsum_bytes = (size_t)c.grid_m * 128 * plan.geom.groups * 4;
+        if (plan.fmt != FMT_NVFP4) c.rowsum_bytes = (size_t)c.grid_m * 128 * plan.geom.groups * 4;
       } else {
         c.qtile = true;
       }
@@ -665,7 +671,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
 static const char* mfma_name(Format f, const Choice& c) {
   if (f == FMT_W4A16) return c.tile && c.tc.bm * c.tc.bn / (64 * c.tc.waves) == 64 ? "32x32x16_bf16" : "16x16x32_bf16";
   if (f == FMT_W8A16 || f == FMT_NVFP4) return c.tile ? "32x32x16_bf16" : "16x16x32_bf16";
-  if (f == FMT_W2A16) return "16x16x32_bf16";
+  if (f == FMT_W2A16) return c.tile ? "32x32x16_bf16" : "16x16x32_bf16";
   if (f == FMT_MXFP4) return "scale_16x16x128_f8f6f4";
   if (f == FMT_W4A4) return "scale_16x16x128_f4f4";
   if (f == FMT_MXFP4_I8) return "2x_scale_16x16x128_f8f6f4";
@@ -748,7 +754,7 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   a.a_per_pair = a_per_pair;
   a.num_pairs = (int)rows;
   a.epi = plan->compute.epilogue;
-  a.unpack_mask = 0x000F000Fu;
+  a.unpack_mask = plan->fmt == FMT_W2A16 ? 0x00030003u : 0x000F000Fu;
   a.unpack_exp = 0x43004300u;
   const bool asym = plan->layer.wtype == QDG_W_UINT4;
   hipError_t e;
@@ -765,7 +771,7 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
     a.rowsum = rs;
     // offsets: -(128 + z) per group for UINT4 (applied in the kernel), 136 for
     // INT4 and 128 for INT8 (pre-scaled here)
-    const float rs_factor = plan->fmt == FMT_W8A16 ? -128.0f : asym ? 1.0f : -136.0f;
+    const float rs_factor = plan->fmt == FMT_W8A16 ? -128.0f : asym || plan->fmt == FMT_W2A16 ? 1.0f : -136.0f;
     if (plan->fmt == FMT_NVFP4)  // scaled weights: no row-sum offsets
       e = hipSuccess;
     else

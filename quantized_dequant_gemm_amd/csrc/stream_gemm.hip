@@ -138,7 +138,8 @@ struct FmtW4A16 {
 // points (0..3). The offset trick of W4A16 on 512-byte units: lane (c, col)
 // holds its 32 K values in two dwords; each field pair is unpacked to the
 // bf16 pair 128 + u with one v_and_or_b32 after a shift, and each group's
-// chains start from -(128 + z) * sum(A).
+// chains start from -(128 + z) * sum(A), the row sums taken once per row
+// tile and group.
 struct FmtW2A16 {
   using Acc = f32x4_t;
   static constexpr bool kIntAcc = false;
@@ -170,6 +171,18 @@ struct FmtW2A16 {
   __device__ static void compute(const Frag<MT, NT>& f, Acc (&acc)[MT][NT], uint32_t, uint32_t ue) {
     uint32_t m2;
     asm volatile("v_mov_b32 %0, %1" : "=v"(m2) : "s"(0x00030003u));
+    // the group's row sums of A, once per row tile (MFMAs against bf16 1.0):
+    // each tile's chains then start from -(128 + z) * rowsum, a multiply
+    // instead of four more MFMAs per tile
+    f32x4_t rs[MT];
+    const u32x4_t one = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z = mfma_bf16(f.a[mt][j], one, z);
+      rs[mt] = z;
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       u32x4_t bw[4];
@@ -182,12 +195,10 @@ struct FmtW2A16 {
           bw[j][m] = v | ue;
         }
       }
-      const u32x4_t ko = {f.o[t], f.o[t], f.o[t], f.o[t]};
+      const float negz = __builtin_bit_cast(float, (f.o[t] & 0xFFFFu) << 16);  // -(128+z)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        f32x4_t p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p = mfma_bf16(f.a[mt][j], ko, p);
+        f32x4_t p = {negz * rs[mt][0], negz * rs[mt][1], negz * rs[mt][2], negz * rs[mt][3]};
 #pragma unroll
         for (int j = 0; j < 4; ++j) p = mfma_bf16(f.a[mt][j], bw[j], p);
         const float s = f.s[t];

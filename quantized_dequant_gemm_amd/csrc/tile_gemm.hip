@@ -158,7 +158,7 @@ __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint
   // same bytes to the same place).
   using L = Stage<BM, BN, UB>;
   constexpr int A_INST = (L::A_SLOTS + 63) / 64;
-  constexpr int WC = UB / 1024;  // 1 KiB copies per unit
+  constexpr int WC = UB >= 1024 ? UB / 1024 : 1;  // 1 KiB copies per unit
   static_assert((BN / 16) * WC % NW == 0, "whole weight copies per wave");
   const char* ag = a_g + (size_t)g * 256;
 #pragma unroll
@@ -166,17 +166,30 @@ __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint
     const int i = min(r * NW + wave, A_INST - 1);
     __builtin_amdgcn_global_load_lds(ag + a_off[r], (lds_void*)(st + L::A + i * 1024), 16, 0, 0);
   }
+  if constexpr (UB == 512) {
+    // 2-bit units: two copies of 256 bytes (4 per lane) per unit
+    static_assert((BN / 16) * 2 % NW == 0, "whole weight copies per wave");
 #pragma unroll
-  for (int r = 0; r < (BN / 16) * WC / NW; ++r) {
-    const int ci = r * NW + wave;
-    const int t = ci / WC, part = ci % WC;
-    const int tile = stage_tile<BN>(p, wg_tile0, t);
-    __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * UB + part * 1024 + lane * 16,
-                                     (lds_void*)(st + L::W + t * UB + part * 1024), 16, 0, 0);
+    for (int r = 0; r < (BN / 16) * 2 / NW; ++r) {
+      const int ci = r * NW + wave;
+      const int t = ci / 2, part = ci % 2;
+      const int tile = stage_tile<BN>(p, wg_tile0, t);
+      __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * UB + part * 256 + lane * 4,
+                                       (lds_void*)(st + L::W + t * UB + part * 256), 4, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < (BN / 16) * WC / NW; ++r) {
+      const int ci = r * NW + wave;
+      const int t = ci / WC, part = ci % WC;
+      const int tile = stage_tile<BN>(p, wg_tile0, t);
+      __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * UB + part * 1024 + lane * 16,
+                                       (lds_void*)(st + L::W + t * UB + part * 1024), 16, 0, 0);
+    }
   }
   // scale records: BN / 128 copies of 1 KiB, copy wave % (BN / 128) per wave
   // (int8 weights have one scale per channel, applied in the epilogue)
-  if constexpr (UB == 1024)
+  if constexpr (UB != 2048)
     __builtin_amdgcn_global_load_lds(sbase + (size_t)g * 128 + s_off,
                                      (lds_void*)(st + L::S + (wave % (BN / 128)) * 1024), 16, 0, 0);
   // row sums: one whole-wave copy per wave; lanes past BM / 4 repeat rows
@@ -294,6 +307,62 @@ __device__ __forceinline__ void tile_group32(const char* st, int a_lane, int w_l
       for (int i = 0; i < 16; ++i) acc[rb][cb][i] = __builtin_fmaf(sc[cb], pacc[rb][cb][i], acc[rb][cb][i]);
 }
 
+// W2A16 (2-bit codes, fp16 group scales, zero points 0..3) in the same 2 x 2
+// blocks: the 4-bit path with 512-byte units. A lane of quarter q = s / 4 at
+// step s reads unit lane h + 2q, whose dword (s % 4) / 2 holds that step's
+// eight codes in the fields 4 (s % 2) .. 4 (s % 2) + 3 (low and high half);
+// each bf16 pair 128 + u is one shift and one v_and_or_b32 (um = 0x00030003),
+// and each chain starts from -(128 + z) * rowsum(A).
+template <int BM, int BN>
+__device__ __forceinline__ void tile_group32_w2(const char* st, int a_lane, int w2_lane, int s_lane, int rs_lane,
+                                                uint32_t um, uint32_t ue, f32x16_t (&acc)[2][2]) {
+  using L = Stage<BM, BN, 512>;
+  u32x2_t bp[2][2];  // [column block][quarter h, quarter h + 2]
+  float sc[2], negz[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) bp[cb][q] = *(const u32x2_t*)(st + w2_lane + cb * 1024 + q * 256);
+    const u32x2_t rec = *(const u32x2_t*)(st + s_lane + cb * 256);
+    sc[cb] = bits_as<float>(rec.x);
+    negz[cb] = __builtin_bit_cast(float, (rec.y & 0xFFFFu) << 16);  // -(128+z)
+  }
+  f32x16_t pacc[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    f32x4_t r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = *(const f32x4_t*)(st + rs_lane + rb * 128 + q * 32);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pacc[rb][cb][i] = negz[cb] * r[i / 4][i % 4];
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    u32x4_t a[2], b[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      a[rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + (s / 4) * 128 + (s % 4) * 16);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const uint32_t x = bp[cb][s / 4][(s % 4) / 2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) b[cb][m] = ((x >> (8 * (s % 2) + 2 * m)) & um) | ue;
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) pacc[rb][cb] = mfma_bf16_32(a[rb], b[cb], pacc[rb][cb]);
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][cb][i] = __builtin_fmaf(sc[cb], pacc[rb][cb][i], acc[rb][cb][i]);
+}
+
 // NVFP4 weights (E2M1 with E4M3 scales per 16 K) in the same 2 x 2 blocks
 // of 32 x 32: each weight is converted, multiplied by its block scale (both
 // exact) and packed to bf16, so the MFMAs accumulate straight into the
@@ -376,23 +445,26 @@ __device__ __forceinline__ void tile_group32_w8(const char* st, int a_lane, int 
       for (int i = 0; i < 16; ++i) acc[rb][cb][i] += pacc[rb][cb][i];
 }
 
-template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, int NS, bool MOE, bool NV = false, bool W8 = false>
+template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, int NS, bool MOE, bool NV = false, bool W8 = false,
+          bool W2 = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const GemmArgs p, int m_blocks,
                                                                            int n_blocks) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
   constexpr int MTW = WTM / 16;  // 16-row tiles per wave
   constexpr bool M32 = WTM == 64;  // 64 x 64 wave tiles run 32 x 32 MFMA blocks
-  constexpr int UB = W8 ? 2048 : 1024;  // bytes per weight unit
+  constexpr int UB = W8 ? 2048 : W2 ? 512 : 1024;  // bytes per weight unit
   using L = Stage<BM, BN, UB>;
   constexpr int A_INST = (L::A_SLOTS + 63) / 64;
   constexpr int A_PER_WAVE = (A_INST + NW - 1) / NW;
   // copies every wave issues per stage (A, weight units, scale records, row
   // sums); waiting for the count to drop to this leaves the next stage in
   // flight
-  constexpr int VM_NEXT = A_PER_WAVE + (BN / 16) * (UB / 1024) / NW + (W8 ? 0 : 1) + (NV ? 0 : 1);
+  constexpr int VM_NEXT =
+      A_PER_WAVE + (BN / 16) * (W2 ? 2 : UB / 1024) / NW + (W8 ? 0 : 1) + (NV ? 0 : 1);
   static_assert(!NV || M32, "NVFP4 runs the 64 x 64 wave tiles");
   static_assert(!W8 || (M32 && !NV), "W8A16 runs the 64 x 64 wave tiles");
+  static_assert(!W2 || (M32 && ASYM && !NV && !W8), "W2A16 runs the 64 x 64 wave tiles with zero points");
   static_assert(NS == 2 || NS == 3, "two or three stages");
   // The stages are separate LDS objects (not one dynamic array) so that the
   // compiler can tell a copy into one stage from a read of another: reads of
@@ -479,6 +551,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   const int rs_lane = M32 ? L::RS + (wm * WTM + 4 * h) * 4 : L::RS + (wm * WTM + 4 * c) * 4;
   const int sv_lane = L::S + (wn * 4 + (l32 >> 4)) * 128 + (h * 16 + col) * 2;  // NVFP4 scale records
   const int w8_lane = L::W + (wn * 4 + (l32 >> 4)) * 2048 + (h * 16 + col) * 16;  // W8A16 units
+  const int w2_lane = L::W + (wn * 4 + (l32 >> 4)) * 512 + (h * 16 + col) * 8;    // W2A16 units
 
   // one unpack constant in a VGPR, the other in an SGPR: lets each unpacked
   // dword be a single v_and_or_b32 (VOP3 reads at most one scalar operand)
@@ -536,6 +609,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
         tile_group32_nv<BM, BN>(stage[cur], a_lane, w_lane, sv_lane, acc32);
       else if constexpr (W8)
         tile_group32_w8<BM, BN>(stage[cur], a_lane, w8_lane, rs_lane, acc32);
+      else if constexpr (W2)
+        tile_group32_w2<BM, BN>(stage[cur], a_lane, w2_lane, s_lane, rs_lane, um, ue, acc32);
       else if constexpr (M32)
         tile_group32<ASYM, BM, BN>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
       else
@@ -551,6 +626,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
         tile_group32_nv<BM, BN>(stage[cur], a_lane, w_lane, sv_lane, acc32);
       else if constexpr (W8)
         tile_group32_w8<BM, BN>(stage[cur], a_lane, w8_lane, rs_lane, acc32);
+      else if constexpr (W2)
+        tile_group32_w2<BM, BN>(stage[cur], a_lane, w2_lane, s_lane, rs_lane, um, ue, acc32);
       else if constexpr (M32)
         tile_group32<ASYM, BM, BN>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
       else
@@ -703,14 +780,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   }
 }
 
-template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE, bool NV = false, bool W8 = false>
+template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE, bool NV = false, bool W8 = false,
+          bool W2 = false>
 hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s) {
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
   // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256 and 32 x 512,
   // 2 for 256 x 128 and for int8 units)
-  constexpr int NS = 3 * Stage<BM, BN, W8 ? 2048 : 1024>::BYTES <= 160 * 1024 ? 3 : 2;
+  constexpr int NS = 3 * Stage<BM, BN, W8 ? 2048 : W2 ? 512 : 1024>::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE, NV, W8>), dim3(m_blocks * n_blocks, nsplit),
+  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE, NV, W8, W2>), dim3(m_blocks * n_blocks, nsplit),
                      dim3(64 * WAVES_M * WAVES_N), 0, s, a, m_blocks, n_blocks);
   return hipGetLastError();
 }
@@ -725,7 +803,7 @@ hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStrea
 // 7168, T = 512: 7 % faster than (32, 256, 4) with two stages and two
 // workgroups per CU).
 bool tile_cfg_supported(Format f, const TileCfg& c) {
-  if (f == FMT_NVFP4 || f == FMT_W8A16) return c.bm == 128 && c.bn == 256 && c.waves == 8;
+  if (f == FMT_NVFP4 || f == FMT_W8A16 || f == FMT_W2A16) return c.bm == 128 && c.bn == 256 && c.waves == 8;
   if (f != FMT_W4A16) return false;
   if (c.bm == 256 && c.bn == 128) return c.waves == 8;
   if (c.bm == 128 && c.bn == 256) return c.waves == 8 || c.waves == 4;
@@ -742,6 +820,9 @@ hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const Ge
   if (f == FMT_W8A16)
     return moe ? launch_tile_cfg<false, 2, 4, 64, true, false, true>(a, m_blocks, a.split, s)
                : launch_tile_cfg<false, 2, 4, 64, false, false, true>(a, m_blocks, a.split, s);
+  if (f == FMT_W2A16)
+    return moe ? launch_tile_cfg<true, 2, 4, 64, true, false, false, true>(a, m_blocks, a.split, s)
+               : launch_tile_cfg<true, 2, 4, 64, false, false, false, true>(a, m_blocks, a.split, s);
 #define QDG_T(ASYM_, WM_, WN_, WTM_, MOE_)                                                 \
   if (asym == ASYM_ && c.bm == WM_ * WTM_ && c.waves == WM_ * WN_ && moe == MOE_)         \
     return launch_tile_cfg<ASYM_, WM_, WN_, WTM_, MOE_>(a, m_blocks, a.split, s);

@@ -1,9 +1,11 @@
 """W2A16 (2-bit asymmetric weights, bf16 activations) on the GPU against the
-fp64 oracle: every integer q - z is exact in the bf16 MFMA and the group
-scale is applied in fp32, so fp32 output stays within 5e-5 relative
-Frobenius of the fp64 reference and bf16 output within 2e-3; one-hot rows
-reproduce every dequantized weight exactly; the device producer of the
-standard format matches the oracle's quantizer bit for bit."""
+fp64 oracle, through the streaming family (M <= 32, MoE blocks of 16 to 64
+rows) and the LDS-tiled bf16 family (M >= 33, 128-row MoE blocks): every
+integer q - z is exact in the bf16 MFMA and the group scale is applied in
+fp32, so fp32 output stays within 5e-5 relative Frobenius of the fp64
+reference and bf16 output within 2e-3; one-hot rows reproduce every
+dequantized weight exactly; the device producer of the standard format
+matches the oracle's quantizer bit for bit."""
 
 import numpy as np
 import pytest
@@ -30,7 +32,7 @@ def _packed(n, k, qv, s, z, otype, num_experts=1):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 96, 256), (16, 4096, 4096), (16, 1024, 14336), (37, 200, 640),
-                                   (64, 512, 1024), (150, 272, 512)])
+                                   (64, 512, 1024), (150, 272, 512), (300, 1040, 2048)])
 def test_w2a16_parity(qdg, m, n, k):
     qv, s, z, w64 = _data(n, k, salt=m)
     a = synth.activations_bf16_bits(m, k, workload_id=1, salt=m + 1)
@@ -38,13 +40,14 @@ def test_w2a16_parity(qdg, m, n, k):
     for otype, tol in ((q.QDG_O_F32, 5e-5), (q.QDG_O_BF16, 2e-3)):
         layer, pk = _packed(n, k, qv, s, z, otype)
         y, plan = H.gemm(layer, pk, H.bf16_dev(a), m)
-        assert "family=stream" in q.qdg_plan_describe(plan, m)
+        # the streaming family up to 32 rows, the LDS-tiled bf16 family above
+        assert ("family=stream " if m <= 32 else "family=tile ") in q.qdg_plan_describe(plan, m)
         err = metrics.rel_frob(H.to_f64(y), y64)
         print(f"W2A16 M={m} N={n} K={k} otype={otype}: rel_frob={err:.3e}")
         assert err <= tol, err
 
 
-@pytest.mark.parametrize("m", [16, 64])
+@pytest.mark.parametrize("m", [16, 64, 128])
 def test_w2a16_one_hot_every_code_and_zero(qdg, m):
     # codes and zero points over their whole range, power-of-two scales: one
     # identity row per k returns (q - z) * s exactly (fp32 output)
@@ -102,7 +105,7 @@ def test_w2a16_zero_point_flag(qdg):
     assert int(st.item()) == q.QDG_FLAG_BAD_ZERO_POINT
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
 def test_w2a16_moe(qdg, bm):
     E, top_k, t, hid, n = 4, 2, 70, 512, 192
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=bm + 40), top_k)
@@ -121,6 +124,7 @@ def test_w2a16_moe(qdg, bm):
         q.qdg_moe_align(H.dev(ids.astype(np.int32)).data_ptr(), t, top_k, E, bm, sid.data_ptr(), blk.data_ptr(),
                         npad.data_ptr(), q.current_stream())
         plan = q.qdg_plan_create(layer, q.moe(top_k))
+        assert ("family=tile " if bm == 128 else "family=stream ") in q.qdg_moe_describe(plan, t, bm)
         wsp, nbytes = H.workspace(plan, t)
         y = H.out_tensor(t * top_k, n, q.QDG_O_F32)
         a_d = H.bf16_dev(a)
