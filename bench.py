@@ -443,8 +443,9 @@ def rows_leg(reps=30):
         # expert block size (the caller's choice in the API; measured on
         # MI355X): 16-row streaming blocks while experts hold a few rows
         # (T = 64), 32-row tiled blocks around 16 rows per expert (T = 512),
-        # 128-row tiled blocks beyond
-        blk_m = 16 if t * top_k <= 4 * E else 32 if t * top_k <= 32 * E else 128
+        # 64-row tiled blocks around 128 (T = 4096: less padding than 128-row
+        # blocks)
+        blk_m = 16 if t * top_k <= 4 * E else 32 if t * top_k <= 32 * E else 64
         aligned = {}
         for bm in (blk_m,):
             cap = q.qdg_moe_align_capacity(t, top_k, E, bm)

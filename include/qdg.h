@@ -447,8 +447,9 @@ qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int3
    value passed to qdg_moe_align:
      16, 32, 64   every format (streaming family; for W4A16 a tuning with
                   block_n 64 and 8 waves pins the weight-streaming family
-                  for 16, and 32 runs the LDS-tiled family with 32 x 512
-                  tiles unless the plan is batch-invariant);
+                  for 16, and 32 and 64 run the LDS-tiled family with
+                  32 x 512 and 64 x 512 tiles unless the plan is
+                  batch-invariant);
      128          W4A16 (LDS-tiled family, the SiLU*mul epilogue included),
                   NVFP4, W8A16 and W2A16 (LDS-tiled bf16 family), W8A8,
                   W4A8-INT8, W4A8-MXFP4 and W4A4 (8-bit LDS-tiled family),

@@ -642,12 +642,15 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
     c.sc = StreamCfg{block_m / 16, block_m == 16 ? 4 : 2, 4, 1};
   c.tile = false;
   c.qtile = false;
-  // 32- and 128-row blocks: the LDS-tiled family (32 x 512 and 128 x 256
-  // tiles); measured on MI355X at E = 256, hidden 7168, T = 512, 32-row
-  // blocks in it run gate+up in 1112 us and down in 577-588 us (32 x 256
-  // tiles: 1185-1208 and 618-622 us), against 1467 and 1107 us in the
-  // streaming family (1284 and 761 us with 16-row blocks)
-  if (block_m == 128 || (block_m == 32 && !plan.compute.batch_invariant)) {
+  // 32-, 64- and 128-row blocks: the LDS-tiled family (32 x 512, 64 x 512
+  // and 128 x 256 tiles). Measured on MI355X at E = 256, hidden 7168: at
+  // T = 512 32-row blocks in it run gate+up in 1112 us and down in 577-588 us
+  // (32 x 256 tiles: 1185-1208 and 618-622 us), against 1467 and 1107 us in
+  // the streaming family (1284 and 761 us with 16-row blocks); at T = 4096
+  // 64-row blocks run gate+up in 3260 us and down in 1737 us against 3792 and
+  // 2136 us with 128-row blocks (less padding per expert), where 64-row
+  // streaming blocks took 7.1 and 7.4 ms
+  if (block_m == 128 || ((block_m == 32 || block_m == 64) && !plan.compute.batch_invariant)) {
     // A rows are addressed with 32-bit byte offsets in the tiled family
     const int64_t a_rows = a_per_pair ? rows : T;
     if ((double)a_rows * (double)plan.layer.k * 2.0 >= 4294967296.0)
@@ -657,7 +660,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
       return fail(QDG_ERR_UNSUPPORTED, "batch-invariant MoE plans use block_m <= 64");
     c.tile = true;
     c.ws = false;
-    c.tc = block_m == 128 ? TileCfg{128, 256, 8} : TileCfg{32, 512, 8};
+    c.tc = block_m == 128 ? TileCfg{128, 256, 8} : TileCfg{block_m, 512, 8};
   } else if (!c.ws && !stream_cfg_supported(plan.fmt, c.sc)) {
     return fail(QDG_ERR_UNSUPPORTED, "block_m %d unsupported", block_m);
   }

@@ -785,7 +785,7 @@ template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE, bool NV = fals
 hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s) {
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
   // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256 and 32 x 512,
-  // 2 for 256 x 128 and for int8 units)
+  // 2 for 256 x 128, 64 x 512 and int8 units)
   constexpr int NS = 3 * Stage<BM, BN, W8 ? 2048 : W2 ? 512 : 1024>::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
   hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE, NV, W8, W2>), dim3(m_blocks * n_blocks, nsplit),
@@ -801,13 +801,16 @@ hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStrea
 // grouped MoE blocks of 32 rows, (32, 512, 8) with 32 x 64 wave tiles (one
 // workgroup per CU with three stages; measured on MI355X at E = 256, hidden
 // 7168, T = 512: 7 % faster than (32, 256, 4) with two stages and two
-// workgroups per CU).
+// workgroups per CU), and of 64 rows, (64, 512, 8) with 64 x 64 wave tiles
+// and two stages (at T = 4096: 14-19 % faster than 128-row blocks, whose
+// padding wastes more rows; (64, 256, 4) was slower).
 bool tile_cfg_supported(Format f, const TileCfg& c) {
   if (f == FMT_NVFP4 || f == FMT_W8A16 || f == FMT_W2A16) return c.bm == 128 && c.bn == 256 && c.waves == 8;
   if (f != FMT_W4A16) return false;
   if (c.bm == 256 && c.bn == 128) return c.waves == 8;
   if (c.bm == 128 && c.bn == 256) return c.waves == 8 || c.waves == 4;
   if (c.bm == 32 && c.bn == 512) return c.waves == 8;
+  if (c.bm == 64 && c.bn == 512) return c.waves == 8;
   return false;
 }
 
@@ -835,6 +838,7 @@ hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const Ge
   QDG_T(false, 2, 4, 64, true)
   QDG_T(false, 1, 4, 128, true)
   QDG_T(false, 1, 8, 32, true)
+  QDG_T(false, 1, 8, 64, true)
 #undef QDG_T
   return hipErrorInvalidValue;
 }

@@ -172,7 +172,7 @@ def test_moe_w4a16_int4_minus8_one_hot(qdg, bm):
     a = np.zeros((t, k), np.float32)
     a[np.arange(t), kt] = 1.0
     y, desc = _moe_run(layer, pk, H.bf16_dev(codecs.f32_to_bf16_bits(a)), None, ids, bm, 0)
-    assert ("family=tile" in desc) == (bm in (32, 128))
+    assert ("family=tile" in desc) == (bm in (32, 64, 128))
     want = np.stack([ref.dequant_int4_sym(vs[ids[p // top_k, p % top_k]], ss[ids[p // top_k, p % top_k]])[:, kt[p // top_k]]
                      for p in range(t * top_k)])
     assert np.array_equal(H.to_f64(y), want)

@@ -124,7 +124,7 @@ def test_moe_single_expert_equals_dense(qdg, bm, pin_ws):
     assert torch.equal(y, yd)
 
 
-@pytest.mark.parametrize("proj,t,bm", [("gate_up", 64, 16), ("gate_up", 512, 128), ("gate_up", 4096, 128),
+@pytest.mark.parametrize("proj,t,bm", [("gate_up", 64, 16), ("gate_up", 512, 128), ("gate_up", 4096, 128), ("gate_up", 4096, 64),
                                        ("down", 64, 16), ("down", 512, 32), ("down", 4096, 128)])
 def test_moe_full_size_sampled_rows(qdg, proj, t, bm):
     # the real MoE shapes (E=256, top-8, hidden 7168, intermediate 2048):
@@ -156,7 +156,7 @@ def test_moe_full_size_sampled_rows(qdg, proj, t, bm):
         x = synth.activations_bf16_bits(t, k, workload_id=4)
     y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 1 if per_pair else 0, top_k)
     fam = q.qdg_moe_describe(q.qdg_plan_create(layer, q.moe(top_k)), t, bm).split("family=")[1].split()[0]
-    assert fam == ("tile" if bm in (32, 128) else "stream")
+    assert fam == ("tile" if bm in (32, 64, 128) else "stream")
     xf = codecs.bf16_bits_to_f64(x)
     for p in pairs:
         e = int(ids.reshape(-1)[p])
@@ -174,10 +174,10 @@ def test_moe_full_size_sampled_rows(qdg, proj, t, bm):
 @pytest.mark.parametrize("otype", [q.QDG_O_F32, q.QDG_O_BF16])
 def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, inter, otype):
     # fused gate+up (n = 2I) with the SiLU*mul epilogue: Y = silu(G) * U,
-    # [T*top_k][I]; 16- and 64-row blocks run the streaming family (four
-    # tiles, two gate + two up, per workgroup at 16 rows, else two), 32- and
-    # 128-row blocks the LDS-tiled one (I = 144: an odd number of gate tiles,
-    # so a workgroup's tile slots run partly past the layer)
+    # [T*top_k][I]; 16-row blocks run the streaming family (four tiles, two
+    # gate + two up, per workgroup), 32-, 64- and 128-row blocks the LDS-tiled
+    # one (I = 144: an odd number of gate tiles, so a workgroup's tile slots
+    # run partly past the layer)
     E, top_k, hid = 16, 4, 1024
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=t + 11), top_k)
     qs, ss = _experts(E, 2 * inter, hid, salt=9)
@@ -190,7 +190,7 @@ def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, inter, otype):
     sid, blk, npad, cap = _align_dev(ids, E, bm)
     plan = q.qdg_plan_create(layer, q.moe(top_k, epilogue=q.QDG_EPI_SILU_MUL))
     desc = q.qdg_moe_describe(plan, t, bm)
-    assert "epilogue=silu_mul" in desc and ("family=tile" in desc) == (bm in (32, 128))
+    assert "epilogue=silu_mul" in desc and ("family=tile" in desc) == (bm in (32, 64, 128))
     ws, nbytes = H.workspace(plan, t)
     y = H.out_tensor(t * top_k, inter, otype)
     q.qdg_moe_gemm(plan, a_dev.data_ptr(), None, pk.buf.data_ptr(), sid.data_ptr(), blk.data_ptr(),
