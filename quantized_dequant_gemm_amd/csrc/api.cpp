@@ -253,13 +253,18 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   if (P.compute.batch_invariant && bm > 64) bm = 64;
   // the tiled family addresses A with 32-bit byte offsets
   const bool a_fits = (double)(M > 0 ? M : 1) * (double)g.k * 2.0 < 4294967296.0;
-  if (bm >= 128 && (P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4 || P.fmt == FMT_W8A16 || P.fmt == FMT_W2A16) && !moe &&
-      a_fits) {
-    // LDS-tiled family: BM x 128 tiles, row sums of A per group in the workspace
+  // W4A16 with 33 to 64 rows: 64 x 512 tiles instead of one partly filled
+  // 128-row block (a tuning asks for them with block_m 64 and block_n 512)
+  const bool tile64 = P.fmt == FMT_W4A16 && !moe && !P.compute.batch_invariant &&
+                      (has_tuning ? T.block_m == 64 && T.block_n == 512 : M > 32 && M <= 64);
+  if ((bm >= 128 || tile64) &&
+      (P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4 || P.fmt == FMT_W8A16 || P.fmt == FMT_W2A16) && !moe && a_fits) {
+    // LDS-tiled family: BM x BN tiles, row sums of A per group in the workspace
+    if (tile64) bm = 64;
     ch.tile = true;
     ch.tc.bm = bm;
-    ch.tc.bn = bm == 256 ? 128 : 256;
-    ch.tc.waves = has_tuning && T.waves ? T.waves : 8;
+    ch.tc.bn = bm == 256 ? 128 : bm == 64 ? 512 : 256;
+    ch.tc.waves = tile64 ? 8 : has_tuning && T.waves ? T.waves : 8;
     ch.grid_m = (int)((M + bm - 1) / bm);
     const int64_t n_blocks = (g.ntiles + ch.tc.bn / 16 - 1) / (ch.tc.bn / 16);
     const int64_t tiles = n_blocks * ch.grid_m;
@@ -417,6 +422,15 @@ qdg_status check_tuning(const qdg_layer_config& layer, const qdg_compute_config&
   const bool dense_tiled = compute.kind == QDG_KIND_DENSE && !compute.batch_invariant;
   const bool tile_ok = dense_tiled && f != FMT_MXFP4_I8 &&
                        (tuning.block_m == 128 || (f == FMT_W4A16 && tuning.block_m == 256));
+  // dense W4A16: block_m 64 with block_n 512 names the 64 x 512 tiles
+  const bool tile64 = dense_tiled && f == FMT_W4A16 && tuning.block_m == 64 && tuning.block_n == 512;
+  if (tile64) {
+    if (tuning.waves && tuning.waves != 8) return fail(QDG_ERR_UNSUPPORTED, "64 x 512 tiles run 8 waves");
+    if (tuning.block_k && tuning.block_k != 128) return fail(QDG_ERR_UNSUPPORTED, "block_k must be 128");
+    if (tuning.mfma && tuning.mfma != 16) return fail(QDG_ERR_UNSUPPORTED, "mfma must be 16 (16x16 tiles)");
+    if (tuning.split_k < 0) return fail(QDG_ERR_INVALID_ARG, "split_k < 0");
+    return QDG_OK;
+  }
   if (tuning.block_m && tuning.block_m != 16 && tuning.block_m != 32 && tuning.block_m != 64 && !tile_ok)
     return fail(QDG_ERR_UNSUPPORTED,
                 "block_m %d: implemented 16, 32, 64 (dense: 128; dense W4A16: 256)", tuning.block_m);
@@ -877,6 +891,8 @@ static void autotune_candidates(const qdg_plan& P, int64_t M, qdg_tuning_config*
     if (P.fmt == FMT_W4A16) {
       add(128, 256, 0, 4);
       if (M > 128) add(256, 128, 0, 8);
+      if (M <= 128)
+        for (int s : {0, 2, 4, 8}) add(64, 512, s, 8);
     }
   }
 }

@@ -797,7 +797,9 @@ hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStrea
 
 // Instances: (block_m, block_n, waves) = (256, 128, 8), (128, 256, 8) with
 // 64 x 64 wave tiles (two waves per SIMD), (128, 256, 4) with 128 x 64
-// wave tiles (one wave per SIMD, half the unpack work per MFMA) and, for
+// wave tiles (one wave per SIMD, half the unpack work per MFMA), (64, 512, 8)
+// for dense M of 33 to 64 (measured on MI355X at M = 40 to 64: 27-29 us
+// against 31-32 us for one partly filled 128-row block, both shapes) and, for
 // grouped MoE blocks of 32 rows, (32, 512, 8) with 32 x 64 wave tiles (one
 // workgroup per CU with three stages; measured on MI355X at E = 256, hidden
 // 7168, T = 512: 7 % faster than (32, 256, 4) with two stages and two
@@ -839,6 +841,8 @@ hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const Ge
   QDG_T(false, 1, 4, 128, true)
   QDG_T(false, 1, 8, 32, true)
   QDG_T(false, 1, 8, 64, true)
+  QDG_T(false, 1, 8, 64, false)
+  QDG_T(true, 1, 8, 64, false)
 #undef QDG_T
   return hipErrorInvalidValue;
 }

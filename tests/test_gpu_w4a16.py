@@ -201,3 +201,40 @@ def test_tile_family_split_k_deterministic(qdg):
         assert metrics.rel_frob(H.to_f64(y1), y64) <= 5e-5
         outs[split] = H.to_f64(y1)
     assert np.allclose(outs[1], outs[8], rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("m,n,k", [(33, 520, 640), (48, 1040, 2048), (64, 4096, 1024)])
+def test_tile64_family(qdg, asym, m, n, k):
+    # 33 to 64 rows: 64 x 512 tiles (ragged N: a workgroup's tile slots run
+    # past the layer; K split by the heuristic), against the oracle
+    qv, s, z, w64 = _layer_data(n, k, asym, salt=m + n)
+    a = synth.activations_bf16_bits(m, k, workload_id=1, salt=m)
+    y64 = ref.gemm_w4a16(a, w64)
+    layer = q.layer_w4a16(n, k, asym=asym)
+    d = q.qdg_plan_describe(q.qdg_plan_create(layer, q.dense()), m)
+    assert "family=tile block_m=64 block_n=512" in d, d
+    y = H.w4a16(a, qv, s, z, otype=q.QDG_O_F32)
+    assert metrics.rel_frob(H.to_f64(y), y64) <= 5e-5
+    yb = H.w4a16(a, qv, s, z)
+    assert metrics.rel_frob(H.to_f64(yb), y64) <= 2e-3
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_tile64_one_hot_and_split_deterministic(qdg, asym):
+    # 64 one-hot rows per call: every output a dequantized weight, exact in
+    # fp32; fixed K splits of the 64 x 512 tiles are bitwise repeatable
+    k, n = 1024, 600
+    qv, s, z, w64 = _layer_data(n, k, asym, salt=21)
+    eye = codecs.f32_to_bf16_bits(np.eye(k, dtype=np.float32))
+    for r0 in (0, 448, k - 64):
+        y = H.w4a16(eye[r0:r0 + 64], qv, s, z, otype=q.QDG_O_F32)
+        assert np.array_equal(H.to_f64(y), w64.T[r0:r0 + 64]), f"rows {r0}.."
+    a = synth.activations_bf16_bits(40, k, workload_id=1, salt=22)
+    for split in (1, 3, 8):
+        t = q.TuningConfig(block_m=64, block_n=512, split_k=split)
+        assert _family(n, k, 40, t, asym) == "tile"
+        y1 = H.w4a16(a, qv, s, z, otype=q.QDG_O_F32, tuning=t)
+        y2 = H.w4a16(a, qv, s, z, otype=q.QDG_O_F32, tuning=t)
+        assert torch.equal(y1, y2), f"split {split} not deterministic"
+        assert metrics.rel_frob(H.to_f64(y1), ref.gemm_w4a16(a, w64)) <= 5e-5
