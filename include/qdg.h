@@ -151,12 +151,13 @@ enum { QDG_EPI_NONE = 0, QDG_EPI_SILU_MUL = 1 };
      streaming         block_m 16, 32 or 64, block_n 16, 32 or 64, waves 4
                        (every format; the default otherwise for M <= 64)
      LDS-tiled         block_m 128 (block_n 256) or 256 (block_n 128), waves
-                       8 or 4 (dense W4A16; the default from M = 33);
-                       block_m 128, block_n 256, waves 8 for dense W8A16 and
-                       W4A16-NVFP4 (the default from M = 33); the 8-bit
-                       activation formats have their own 128 x 256 tiles
-                       (the default from M = 64, or above 128 for W4A4 and
-                       narrow W8A8 layers)
+                       8 or 4 (dense W4A16; the default from M = 65), and
+                       block_m 64 with block_n 512, waves 8 (dense W4A16; the
+                       default for M = 33 to 64); block_m 128, block_n 256,
+                       waves 8 for dense W8A16, W4A16-NVFP4 and W2A16 (the
+                       default from M = 33); the 8-bit activation formats
+                       have their own 128 x 256 tiles (the default from
+                       M = 64, or above 128 for W4A4 and narrow W8A8 layers)
    split_k is the number of K partitions (dense only), reduced in a fixed
    order. batch_invariant plans use the streaming family for every M. Fields
    block_k, stages, mfma and load_path are recorded in the description but
