@@ -626,7 +626,8 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
     const bool tiled_fmt = plan.fmt == FMT_NVFP4 || plan.fmt == FMT_W8A16 || plan.fmt == FMT_W2A16;
     const bool qtiled_fmt = plan.fmt == FMT_W8A8 || plan.fmt == FMT_W4A8 || plan.fmt == FMT_MXFP4 ||
                             plan.fmt == FMT_W4A4;
-    const bool tiled = block_m == 128 && (tiled_fmt || qtiled_fmt) && !silu && !plan.compute.batch_invariant;
+    const bool tiled = (block_m == 128 || (block_m == 64 && qtiled_fmt)) && (tiled_fmt || qtiled_fmt) && !silu &&
+                       !plan.compute.batch_invariant;
     if (block_m > 64 && !tiled)
       return fail(QDG_ERR_UNSUPPORTED, "grouped MoE of %s uses block_m 16, 32 or 64%s", fmt_name(plan.fmt, plan.layer),
                   tiled_fmt || qtiled_fmt ? " (128 without an epilogue)" : "");
@@ -640,7 +641,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
                                                                                       : (double)plan.layer.k;
       if ((double)a_rows * a_row_bytes >= 4294967296.0)
         return fail(QDG_ERR_UNSUPPORTED, "A of %lld rows is too large for 128-row MoE blocks", (long long)a_rows);
-      c.tc = TileCfg{128, 256, 8};
+      c.tc = block_m == 64 ? TileCfg{64, 512, 8} : TileCfg{128, 256, 8};
       if (tiled_fmt) {
         c.tile = true;
         if (plan.fmt != FMT_NVFP4) c.rowsum_bytes = (size_t)c.grid_m * 128 * plan.geom.groups * 4;
@@ -777,7 +778,7 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   hipError_t e;
   if (c.qtile) {
     a.m_pad = c.grid_m * c.tc.bm;
-    e = launch_qtile(plan->fmt, moe, a, c.grid_m, stream);
+    e = launch_qtile(plan->fmt, moe, c.tc.bm, a, c.grid_m, stream);
     if (e == hipSuccess && a.split > 1) {
       const int n_pad = (int)((plan->geom.ntiles + 15) / 16 * 256);
       e = launch_reduce_splits(a, a.m_pad, n_pad, stream);

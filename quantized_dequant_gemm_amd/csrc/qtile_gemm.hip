@@ -54,8 +54,10 @@ struct QStage {
   static constexpr int W = AS + (KIND == Q_MXFP4 || KIND == Q_W4A4 ? BM * 4 : 0);
   static constexpr int REC = W + (BN / 16) * UNIT;           // W4A8 / MXFP4: 64 bytes per unit
   static constexpr int SCR = REC + (KIND == Q_W8A8 ? 0 : (BN / 16) * 64);  // 1 KiB sink for padding copies
+  static constexpr int REC_COPIES = KIND == Q_W8A8 ? 0 : BN / 256;     // 1 KiB record copies per stage
   // at least the 8 waves' 16 x 64 fp32 epilogue strips
-  static constexpr int BYTES = SCR + 1024 > 8 * 16 * 64 * 4 ? SCR + 1024 : 8 * 16 * 64 * 4;
+  static constexpr int NWAVES = (BM / 64) * (BN / 64);  // 64 x 64 wave tiles
+  static constexpr int BYTES = SCR + 1024 > NWAVES * 16 * 64 * 4 ? SCR + 1024 : NWAVES * 16 * 64 * 4;
 };
 
 // Copies of group g into stage `st` (device-only builtins: kept out of any
@@ -92,11 +94,13 @@ __device__ __forceinline__ void q_load_stage(char* st, const char* a_g, const ui
     __builtin_amdgcn_global_load_lds(wbase + ((size_t)tile * p.groups + g) * L::UNIT + h * 1024 + lane * 16,
                                      (lds_void*)(st + dst), 16, 0, 0);
   }
-  if constexpr (KIND != Q_W8A8) {
-    static_assert(BN / 16 * 64 == 1024, "one record copy per stage");
-    const int tile = min(wg_tile0 + (lane >> 2), p.ntiles - 1);
+  // records: copy r (16 tiles of 64 bytes) by wave NW - 1 - r; every wave
+  // issues REC_COPIES copies, the others into the sink
+#pragma unroll
+  for (int r = 0; r < L::REC_COPIES; ++r) {
+    const int tile = min(wg_tile0 + 16 * r + (lane >> 2), p.ntiles - 1);
     __builtin_amdgcn_global_load_lds(sbase + ((size_t)tile * p.groups + g) * 64 + (lane & 3) * 16,
-                                     (lds_void*)(st + (wave == NW - 1 ? L::REC : L::SCR)), 16, 0, 0);
+                                     (lds_void*)(st + (wave == NW - 1 - r ? L::REC + r * 1024 : L::SCR)), 16, 0, 0);
   }
   if constexpr (KIND == Q_MXFP4 || KIND == Q_W4A4) {
     // activation scales a_scales[row][g] (fp8: one fp32; fp4: the 4 E8M0
@@ -150,7 +154,7 @@ __device__ __forceinline__ void q_frag_load(QFrag<KIND>& f, const char* st, int 
   }
 }
 
-template <int KIND, bool RAW, bool MOE, class Acc>  // MOE: a specialization per kernel, as above
+template <int KIND, bool RAW, bool MOE, int BM, class Acc>  // MOE, BM: a specialization per kernel, as above
 __device__ __forceinline__ void q_frag_compute(const QFrag<KIND>& f, Acc (&acc)[4][4]) {
   u32x4_t b[4][2];
 #pragma unroll
@@ -198,9 +202,10 @@ struct QAcc {
   using T = typename std::conditional<KIND == Q_W8A8 || RAW, i32x4_t, f32x4_t>::type;
 };
 
-template <int KIND, bool RAW, int NS, bool MOE>
-__global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m_blocks, int n_blocks) {
-  constexpr int WAVES_M = 2, WAVES_N = 4, NW = 8, WTM = 64;
+template <int KIND, bool RAW, int NS, bool MOE, int WAVES_M = 2, int WAVES_N = 4>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qtile_gemm_kernel(const GemmArgs p, int m_blocks,
+                                                                            int n_blocks) {
+  constexpr int NW = WAVES_M * WAVES_N, WTM = 64;
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
   using L = QStage<KIND, BM, BN>;
   using Acc = typename QAcc<KIND, RAW>::T;
@@ -209,9 +214,10 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
   constexpr int W_INST = (BN / 16) * (L::UNIT / 1024);
   // copies every wave issues per stage; waiting for the count to drop to
   // this leaves the next stage in flight
-  constexpr int VM_NEXT = (A_INST + NW - 1) / NW + (W_INST + NW - 1) / NW + (KIND != Q_W8A8 ? 1 : 0) +
+  constexpr int VM_NEXT = (A_INST + NW - 1) / NW + (W_INST + NW - 1) / NW + L::REC_COPIES +
                           (KIND == Q_MXFP4 || KIND == Q_W4A4 ? BM / 64 : 0);
   static_assert(NS == 2 || NS == 3, "two or three stages");
+  static_assert(VM_NEXT * (NS - 2) < 64, "vmcnt holds the copies in flight");
   // The stages are separate LDS objects (not one dynamic array) so that the
   // compiler can tell a copy into one stage from a read of another: reads of
   // stage s then wait only for the copies of stage s.
@@ -309,8 +315,10 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
 #pragma unroll
     for (int cur = 0; cur < NS; ++cur) {
       // this wave's copies of group gb+cur are done once at most the copies
-      // of one later group remain in flight (copies complete in order)
-      __builtin_amdgcn_s_waitcnt((VM_NEXT & 15) | (7 << 4) | (15 << 8) | ((VM_NEXT >> 4) << 14));
+      // of the NS - 2 later groups in flight remain (copies complete in
+      // order; with two stages nothing later is in flight yet)
+      constexpr int VM_LEFT = VM_NEXT * (NS - 2);
+      __builtin_amdgcn_s_waitcnt((VM_LEFT & 15) | (7 << 4) | (15 << 8) | ((VM_LEFT >> 4) << 14));
       // every wave's copies of the group landed; the stage of the previous
       // group is free. A bare s_barrier: __syncthreads would also wait for
       // the copies in flight.
@@ -325,7 +333,7 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
       // measured on MI355X at M = 4096: 84 -> 78 us at K = 7168, 113 -> 110 us
       // at K = 2048; the int8 formats run as fast or faster without it)
       if constexpr (KIND == Q_MXFP4) __builtin_amdgcn_sched_barrier(0);
-      q_frag_compute<KIND, RAW, MOE>(fr, acc);
+      q_frag_compute<KIND, RAW, MOE, BM>(fr, acc);
     }
   }
 #pragma unroll
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       q_frag_load<KIND, BM, BN>(fr, stage[cur], a_lane, w_lane, rec_lane, as_lane);
-      q_frag_compute<KIND, RAW, MOE>(fr, acc);
+      q_frag_compute<KIND, RAW, MOE, BM>(fr, acc);
     }
   }
 
@@ -429,13 +437,23 @@ __global__ __launch_bounds__(512) void qtile_gemm_kernel(const GemmArgs p, int m
 }
 
 template <int KIND, bool RAW>
-hipError_t launch_q(const GemmArgs& a, bool moe, int m_blocks, int nsplit, hipStream_t s) {
+hipError_t launch_q(const GemmArgs& a, bool moe, int bm, int m_blocks, int nsplit, hipStream_t s) {
+  if (moe && nsplit != 1) return hipErrorInvalidValue;  // grouped MoE is not split
+  if (moe && bm == 64) {
+    // 64-row expert blocks: 64 x 512 tiles, 8 waves in one row
+    constexpr int BM = 64, BN = 512;
+    constexpr int NS = 3 * QStage<KIND, BM, BN>::BYTES <= 160 * 1024 ? 3 : 2;
+    const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
+    hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, true, 1, 8>), dim3(m_blocks * n_blocks, 1), dim3(512), 0, s,
+                       a, m_blocks, n_blocks);
+    return hipGetLastError();
+  }
+  if (bm != 128) return hipErrorInvalidValue;
   constexpr int BM = 128, BN = 256;
   using L = QStage<KIND, BM, BN>;
   constexpr int NS = 3 * L::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
   if (moe) {
-    if (nsplit != 1) return hipErrorInvalidValue;  // grouped MoE is not split
     hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, true>), dim3(m_blocks * n_blocks, 1), dim3(512), 0, s, a,
                        m_blocks, n_blocks);
   } else {
@@ -447,16 +465,18 @@ hipError_t launch_q(const GemmArgs& a, bool moe, int m_blocks, int nsplit, hipSt
 
 }  // namespace
 
-hipError_t launch_qtile(Format f, bool moe, const GemmArgs& a, int m_blocks, hipStream_t s) {
+hipError_t launch_qtile(Format f, bool moe, int bm, const GemmArgs& a, int m_blocks, hipStream_t s) {
   const bool raw = a.otype == QDG_O_I32;
   if (raw && a.split > 1) return hipErrorInvalidValue;  // integer partials are not split
   switch (f) {
     case FMT_W8A8:
-      return raw ? launch_q<Q_W8A8, true>(a, moe, m_blocks, 1, s) : launch_q<Q_W8A8, false>(a, moe, m_blocks, a.split, s);
+      return raw ? launch_q<Q_W8A8, true>(a, moe, bm, m_blocks, 1, s)
+                 : launch_q<Q_W8A8, false>(a, moe, bm, m_blocks, a.split, s);
     case FMT_W4A8:
-      return raw ? launch_q<Q_W4A8, true>(a, moe, m_blocks, 1, s) : launch_q<Q_W4A8, false>(a, moe, m_blocks, a.split, s);
-    case FMT_MXFP4: return launch_q<Q_MXFP4, false>(a, moe, m_blocks, a.split, s);
-    case FMT_W4A4: return launch_q<Q_W4A4, false>(a, moe, m_blocks, a.split, s);
+      return raw ? launch_q<Q_W4A8, true>(a, moe, bm, m_blocks, 1, s)
+                 : launch_q<Q_W4A8, false>(a, moe, bm, m_blocks, a.split, s);
+    case FMT_MXFP4: return launch_q<Q_MXFP4, false>(a, moe, bm, m_blocks, a.split, s);
+    case FMT_W4A4: return launch_q<Q_W4A4, false>(a, moe, bm, m_blocks, a.split, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -282,7 +282,8 @@ def test_moe_128_row_blocks():
                        (q.layer_mxfp4(256, 256, num_experts=4), "qtile"), (q.layer_w4a4(256, 256, num_experts=4), "qtile")):
         p = q.qdg_plan_create(layer, q.moe(2))
         assert f"family={fam} " in q.qdg_moe_describe(p, 8, 128)
-        assert "family=stream" in q.qdg_moe_describe(p, 8, 64)
+        # 64-row blocks: the 8-bit LDS-tiled family's 64 x 512 tiles
+        assert ("family=qtile " if fam == "qtile" else "family=stream ") in q.qdg_moe_describe(p, 8, 64)
         ps = q.qdg_plan_create(layer, q.moe(2, epilogue=q.QDG_EPI_SILU_MUL))
         with pytest.raises(q.QdgError):
             q.qdg_moe_describe(ps, 8, 128)
