@@ -313,7 +313,7 @@ def rows_leg(reps=30):
     """The other rows of the hot path, each timed at its own shapes (not part
     of `value`): W8A8, W4A8-INT8, W8A16, W4A16-NVFP4 and W2A16 (K=4096, N in
     {4096, 14336}, M in {16, 256, 4096}), W4A8-MXFP4 ((K,N) in {(7168,2048), (2048,7168)}, M in
-    {16, 512, 4096}), W4A4-MXFP4 at the same shapes and MXFP4 x INT8 at M in {16, 512}, the activation
+    {16, 512, 4096}), W4A4-MXFP4 and MXFP4 x INT8 at the same shapes, the activation
     quantizers, and the grouped MoE W4A16
     GEMMs (E=256, top-8, hidden 7168, intermediate 2048, T in {64, 512,
     4096}) with their expert sort, the gate+up GEMM with the SiLU*mul
@@ -413,7 +413,7 @@ def rows_leg(reps=30):
                   n * k // 2 + n * (k // 32))
         dense_row("w4a4-mxfp4", q.layer_w4a4(n, k), k, n, (16, 512, 4096), torch.uint8, 32, PEAK_FP4_TFLOPS,
                   n * k // 2 + n * (k // 32), a_bits=4, as_bytes=1)
-        dense_row("w4a8-mxfp4-int8", q.layer_mxfp4_int8(n, k), k, n, (16, 512), torch.int8, 0, PEAK_FP8_TFLOPS,
+        dense_row("w4a8-mxfp4-int8", q.layer_mxfp4_int8(n, k), k, n, (16, 512, 4096), torch.int8, 0, PEAK_FP8_TFLOPS,
                   n * k // 2 + n * (k // 32))
 
     # ---- grouped MoE W4A16

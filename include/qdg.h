@@ -450,15 +450,16 @@ qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int3
                   noted: for W4A16 a tuning with block_n 64 and 8 waves
                   pins the weight-streaming family for 16; W4A16 runs 32
                   and 64 in the LDS-tiled family (32 x 512 and 64 x 512
-                  tiles); W8A8, W4A8-INT8, W4A8-MXFP4 and W4A4 run 64 in
-                  the 8-bit LDS-tiled family (64 x 512 tiles) when the plan
-                  has no epilogue; batch-invariant plans always stream;
+                  tiles); W8A8, W4A8-INT8, W4A8-MXFP4, W4A4 and
+                  W4A8-MXFP4-INT8 run 64 in the 8-bit LDS-tiled family
+                  (64 x 512 tiles) when the plan has no epilogue;
+                  batch-invariant plans always stream;
      128          W4A16 (LDS-tiled family, the SiLU*mul epilogue included),
                   NVFP4, W8A16 and W2A16 (LDS-tiled bf16 family), W8A8,
-                  W4A8-INT8, W4A8-MXFP4 and W4A4 (8-bit LDS-tiled family),
-                  all but W4A16 without an epilogue; batch-invariant plans,
-                  the SiLU*mul epilogue of the other formats and
-                  W4A8-MXFP4-INT8 return QDG_ERR_UNSUPPORTED.
+                  W4A8-INT8, W4A8-MXFP4, W4A4 and W4A8-MXFP4-INT8 (8-bit
+                  LDS-tiled family), all but W4A16 without an epilogue;
+                  batch-invariant plans and the SiLU*mul epilogue of the
+                  other formats return QDG_ERR_UNSUPPORTED.
    workspace >= qdg_plan_workspace(plan, T) bytes. Errors as for qdg_gemm,
    plus QDG_ERR_INVALID_ARG for a dense plan or NULL routing arrays and
    QDG_ERR_UNSUPPORTED for another block_m or T*top_k > 2^20. */

@@ -243,12 +243,10 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   // family from M = 33 (bf16 activations: W4A16, NVFP4, W8A16, W2A16) and
   // from M = 64 (int8 / fp8 / fp4 activations)
   const bool bf16_act = P.fmt == FMT_W4A16 || P.fmt == FMT_NVFP4 || P.fmt == FMT_W8A16 || P.fmt == FMT_W2A16;
-  // MXFP4 weights with int8 activations run the streaming family at every M;
-  // W2A16 has no weight-streaming variant (the streaming family serves its
-  // small M)
-  const bool stream_only = P.fmt == FMT_MXFP4_I8;
-  const bool no_wstream = stream_only || P.fmt == FMT_W2A16;
-  if (!has_tuning && !P.compute.batch_invariant && !moe && !stream_only && bm < 128 && M > (bf16_act ? 32 : 63))
+  // W2A16 and MXFP4 weights with int8 activations have no weight-streaming
+  // variant (the streaming family serves their small M)
+  const bool no_wstream = P.fmt == FMT_MXFP4_I8 || P.fmt == FMT_W2A16;
+  if (!has_tuning && !P.compute.batch_invariant && !moe && bm < 128 && M > (bf16_act ? 32 : 63))
     bm = 128;
   if (P.compute.batch_invariant && bm > 64) bm = 64;
   // the tiled family addresses A with 32-bit byte offsets
@@ -326,7 +324,8 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   }
   // LDS-tiled family of the int8 / fp8 formats: 128 x 256 tiles, used once
   // there are enough of them (or M >= 512) to beat the streaming family
-  const bool a8_fits = (double)(M > 0 ? M : 1) * (double)g.k < 4294967296.0;
+  const bool a8_fits =
+      (double)(M > 0 ? M : 1) * (double)g.k * (P.fmt == FMT_MXFP4_I8 ? 2.0 : 1.0) < 4294967296.0;  // I8: two planes
   const int64_t q_tiles = ((M + 127) / 128) * ((g.ntiles + 15) / 16);
   // (measured on MI355X: from M = 64 the tiled family with K split into one
   // pass of 256 workgroups beats the streaming family at these layer sizes,
@@ -339,7 +338,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
     stream_mid = P.fmt == FMT_W4A4 || (P.fmt == FMT_W8A8 && 2 * stream_wgs <= kTargetWorkgroups);
   }
   const bool q_enough = (has_tuning && T.block_m >= 128) || (M >= 64 && !stream_mid);
-  if (bm >= 128 && P.fmt != FMT_W4A16 && P.fmt != FMT_W8A16 && P.fmt != FMT_NVFP4 && !no_wstream && !moe &&
+  if (bm >= 128 && P.fmt != FMT_W4A16 && P.fmt != FMT_W8A16 && P.fmt != FMT_NVFP4 && P.fmt != FMT_W2A16 && !moe &&
       a8_fits && q_enough) {
     ch.tile = true;
     ch.qtile = true;
@@ -420,8 +419,7 @@ bool instance_exists(Format f, const Choice& c) {
 qdg_status check_tuning(const qdg_layer_config& layer, const qdg_compute_config& compute, Format f,
                         const qdg_tuning_config& tuning) {
   const bool dense_tiled = compute.kind == QDG_KIND_DENSE && !compute.batch_invariant;
-  const bool tile_ok = dense_tiled && f != FMT_MXFP4_I8 &&
-                       (tuning.block_m == 128 || (f == FMT_W4A16 && tuning.block_m == 256));
+  const bool tile_ok = dense_tiled && (tuning.block_m == 128 || (f == FMT_W4A16 && tuning.block_m == 256));
   // dense W4A16: block_m 64 with block_n 512 names the 64 x 512 tiles
   const bool tile64 = dense_tiled && f == FMT_W4A16 && tuning.block_m == 64 && tuning.block_n == 512;
   if (tile64) {
@@ -625,7 +623,7 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
     // 8-bit one
     const bool tiled_fmt = plan.fmt == FMT_NVFP4 || plan.fmt == FMT_W8A16 || plan.fmt == FMT_W2A16;
     const bool qtiled_fmt = plan.fmt == FMT_W8A8 || plan.fmt == FMT_W4A8 || plan.fmt == FMT_MXFP4 ||
-                            plan.fmt == FMT_W4A4;
+                            plan.fmt == FMT_W4A4 || plan.fmt == FMT_MXFP4_I8;
     const bool tiled = (block_m == 128 || (block_m == 64 && qtiled_fmt)) && (tiled_fmt || qtiled_fmt) && !silu &&
                        !plan.compute.batch_invariant;
     if (block_m > 64 && !tiled)
@@ -637,8 +635,9 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
     if (tiled) {
       // A rows are addressed with 32-bit byte offsets in the tiled families
       const int64_t a_rows = a_per_pair ? rows : T;
-      const double a_row_bytes = tiled_fmt ? 2.0 * plan.layer.k : plan.fmt == FMT_W4A4 ? plan.layer.k / 2.0
-                                                                                      : (double)plan.layer.k;
+      const double a_row_bytes = tiled_fmt || plan.fmt == FMT_MXFP4_I8 ? 2.0 * plan.layer.k
+                                 : plan.fmt == FMT_W4A4             ? plan.layer.k / 2.0
+                                                                    : (double)plan.layer.k;
       if ((double)a_rows * a_row_bytes >= 4294967296.0)
         return fail(QDG_ERR_UNSUPPORTED, "A of %lld rows is too large for 128-row MoE blocks", (long long)a_rows);
       c.tc = block_m == 64 ? TileCfg{64, 512, 8} : TileCfg{128, 256, 8};
@@ -776,6 +775,14 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   a.unpack_exp = 0x43004300u;
   const bool asym = plan->layer.wtype == QDG_W_UINT4;
   hipError_t e;
+  if (plan->fmt == FMT_MXFP4_I8) {
+    // the int8 codes become two E4M3 planes in the workspace (either family)
+    const int64_t a_rows = moe ? (a_per_pair ? rows : T) : M;
+    uint8_t* pl = (uint8_t*)workspace + kCounterBytes + align_up((int64_t)c.partial_bytes, 256);
+    e = launch_act_i8_planes((const int8_t*)A, a_rows, a.K, pl, stream);
+    if (e != hipSuccess) return hip_status(e, "activation planes launch");
+    a.A = pl;
+  }
   if (c.qtile) {
     a.m_pad = c.grid_m * c.tc.bm;
     e = launch_qtile(plan->fmt, moe, c.tc.bm, a, c.grid_m, stream);
@@ -816,12 +823,6 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
     if (a.a_bytes >= ((int64_t)1 << 31))
       return fail(QDG_ERR_UNSUPPORTED, "A of %lld bytes is too large for the streaming family (< 2 GiB)",
                   (long long)a.a_bytes);
-    if (planes) {
-      uint8_t* pl = (uint8_t*)workspace + kCounterBytes + align_up((int64_t)c.partial_bytes, 256);
-      e = launch_act_i8_planes((const int8_t*)A, a_rows, a.K, pl, stream);
-      if (e != hipSuccess) return hip_status(e, "activation planes launch");
-      a.A = pl;
-    }
     a.m_pad = c.grid_m * c.sc.mt * 16;
     const JitInstance* jit = find_jit(*plan, c, moe);
     e = jit ? launch_stream_jit(jit->fn, c.sc, a, c.grid_m, stream)

@@ -1,8 +1,10 @@
 // LDS-tiled (large-M) GEMM family for the 8-bit-activation formats:
 // W8A8 and W4A8-INT8 (int8 x int8 -> exact int32 on v_mfma_i32_16x16x64_i8)
 // and W4A8-MXFP4 (fp8 E4M3 x E2M1 on the scaled 16x16x128 MFMA, with the
-// E8M0 block scales applied by the hardware), and for W4A4-MXFP4 (E2M1 x
-// E2M1 on the same MFMA, both operands' E8M0 scales applied by it).
+// E8M0 block scales applied by the hardware), for W4A4-MXFP4 (E2M1 x E2M1 on
+// the same MFMA, both operands' E8M0 scales applied by it) and for MXFP4
+// weights x int8 activations (the int8 codes as two exact E4M3 planes, each
+// through the fp8 x fp4 MFMA).
 //
 // The pages' library serves large batches with a different, throughput-
 // oriented pipeline than small ones (kinachrichten, "Wie die Architektur
@@ -40,11 +42,12 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-enum QKind { Q_W8A8 = 0, Q_W4A8 = 1, Q_MXFP4 = 2, Q_W4A4 = 3 };
+enum QKind { Q_W8A8 = 0, Q_W4A8 = 1, Q_MXFP4 = 2, Q_W4A4 = 3, Q_MXFP4_I8 = 4 };
 
 template <int KIND, int BM, int BN>
 struct QStage {
-  static constexpr int AROW = KIND == Q_W4A4 ? 64 : 128;    // bytes of A per row and group
+  // bytes of A per row and group (MXFP4 x INT8: the hi and lo E4M3 planes)
+  static constexpr int AROW = KIND == Q_W4A4 ? 64 : KIND == Q_MXFP4_I8 ? 256 : 128;
   static constexpr int ROW = AROW + 16;                     // + 16 of padding
   static constexpr int CH = ROW / 16;                       // 16-byte slots per row (the last is padding)
   static constexpr int UNIT = KIND == Q_W8A8 ? 2048 : 1024;  // bytes per 16 x 128 weight unit
@@ -116,7 +119,7 @@ __device__ __forceinline__ void q_load_stage(char* st, const char* a_g, const ui
 // (4 x 4 MFMA tiles of 16 x 16).
 template <int KIND>
 struct QFrag {
-  u32x4_t a[4][2];  // A rows of the 4 row tiles (two 16-byte K slices)
+  u32x4_t a[4][KIND == Q_MXFP4_I8 ? 4 : 2];  // A rows of the 4 row tiles (16-byte K slices; I8: hi, then lo)
   u32x4_t b[4][2];  // weights of the 4 column tiles (W4A8: packed int4 in b[t][0])
   float ws[4];      // W4A8: group scale s/16 of the lane's column
   int e8[4];        // MXFP4, W4A4: E8M0 block scale of the lane
@@ -148,7 +151,11 @@ __device__ __forceinline__ void q_frag_load(QFrag<KIND>& f, const char* st, int 
     // fp4 operand: K 32c..32c+31 (16 bytes)
     f.a[mt][0] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW);
     if constexpr (KIND != Q_W4A4)
-      f.a[mt][1] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + (KIND == Q_MXFP4 ? 64 : 16));
+      f.a[mt][1] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + (KIND == Q_MXFP4 || KIND == Q_MXFP4_I8 ? 64 : 16));
+    if constexpr (KIND == Q_MXFP4_I8) {  // the lo plane, 128 bytes on
+      f.a[mt][2] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + 128);
+      f.a[mt][3] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + 192);
+    }
     if constexpr (KIND == Q_MXFP4) f.as[mt] = *(const f32x4_t*)(st + as_lane + mt * 64);
     if constexpr (KIND == Q_W4A4) f.ae8[mt] = *(const uint8_t*)(st + as_lane + mt * 64);
   }
@@ -179,6 +186,16 @@ __device__ __forceinline__ void q_frag_compute(const QFrag<KIND>& f, Acc (&acc)[
         const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
         const i32x8_t bv = {(int)b[t][0].x, (int)b[t][0].y, (int)b[t][0].z, (int)b[t][0].w, 0, 0, 0, 0};
         acc[mt][t] = mfma_fp4_fp4_scaled(av, bv, acc[mt][t], f.ae8[mt], f.e8[t]);
+      } else if constexpr (KIND == Q_MXFP4_I8) {
+        // int8 = 16 hi + lo, both exact in E4M3: the hi plane with A scale
+        // 2^4 (E8M0 131), the lo plane with 2^0, the weights' E8M0 on both;
+        // the products are exact and accumulate over the whole K range (the
+        // token scale is applied once in the epilogue)
+        const u32x4_t h0 = f.a[mt][0], h1 = f.a[mt][1], l0 = f.a[mt][2], l1 = f.a[mt][3];
+        const i32x8_t ah = {(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+        const i32x8_t al = {(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+        const i32x8_t bv = {(int)b[t][0].x, (int)b[t][0].y, (int)b[t][0].z, (int)b[t][0].w, 0, 0, 0, 0};
+        acc[mt][t] = mfma_fp8_fp4_scaled(al, bv, mfma_fp8_fp4_scaled(ah, bv, acc[mt][t], 131, f.e8[t]), 127, f.e8[t]);
       } else if constexpr (KIND == Q_MXFP4) {
         const u32x4_t a0 = f.a[mt][0], a1 = f.a[mt][1];
         const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
@@ -276,7 +293,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qtile_gemm_kernel(cons
     const int q = (r * NW + wave) * 64 + lane;
     const int row = min(q / L::CH, BM - 1), ch = q % L::CH;
     const int src = a_row(mb * BM + row);
-    const uint32_t a_bytes = KIND == Q_W4A4 ? (uint32_t)p.K / 2 : (uint32_t)p.K;
+    const uint32_t a_bytes = KIND == Q_W4A4 ? (uint32_t)p.K / 2 : KIND == Q_MXFP4_I8 ? 2u * p.K : (uint32_t)p.K;
     a_off[r] = (uint32_t)src * a_bytes + (uint32_t)(ch < L::CH - 1 ? ch : 0) * 16;
   }
   uint32_t as_off[BM / 64];
@@ -287,9 +304,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qtile_gemm_kernel(cons
   }
 
   // per-lane LDS offsets of the fragment reads inside a stage
-  const int a_lane = L::A + (wm * WTM + col) * L::ROW + (KIND == Q_MXFP4 || KIND == Q_W4A4 ? 16 : 32) * c;
+  const int a_lane =
+      L::A + (wm * WTM + col) * L::ROW + (KIND == Q_MXFP4 || KIND == Q_W4A4 || KIND == Q_MXFP4_I8 ? 16 : 32) * c;
   const int w_lane = L::W + (wn * 4) * L::UNIT + lane * 16;
-  const int rec_lane = L::REC + (wn * 4) * 64 + (KIND == Q_MXFP4 || KIND == Q_W4A4 ? lane : col * 4);
+  const int rec_lane =
+      L::REC + (wn * 4) * 64 + (KIND == Q_MXFP4 || KIND == Q_W4A4 || KIND == Q_MXFP4_I8 ? lane : col * 4);
   // fp8: the fp32 scales of the lane's 4 D rows; fp4: the E8M0 byte of the
   // lane's A row and 32-block
   const int as_lane = KIND == Q_W4A4 ? L::AS + (wm * WTM + col) * 4 + c : L::AS + (wm * WTM + 4 * c) * 4;
@@ -389,7 +408,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qtile_gemm_kernel(cons
           float y;
           if constexpr (KIND == Q_W8A8)
             y = (float)acc[mt][t][i] * asc[i] * wsc[t];
-          else if constexpr (KIND == Q_W4A8)
+          else if constexpr (KIND == Q_W4A8 || KIND == Q_MXFP4_I8)
             y = acc[mt][t][i] * asc[i];
           else
             y = acc[mt][t][i];
@@ -477,6 +496,7 @@ hipError_t launch_qtile(Format f, bool moe, int bm, const GemmArgs& a, int m_blo
                  : launch_q<Q_W4A8, false>(a, moe, bm, m_blocks, a.split, s);
     case FMT_MXFP4: return launch_q<Q_MXFP4, false>(a, moe, bm, m_blocks, a.split, s);
     case FMT_W4A4: return launch_q<Q_W4A4, false>(a, moe, bm, m_blocks, a.split, s);
+    case FMT_MXFP4_I8: return launch_q<Q_MXFP4_I8, false>(a, moe, bm, m_blocks, a.split, s);
     default: return hipErrorInvalidValue;
   }
 }

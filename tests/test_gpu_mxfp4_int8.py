@@ -1,5 +1,7 @@
 """MXFP4 weights x per-token int8 activations (the MXFP4 -> INT8 path) on the
-GPU against the fp64 oracle (oracle.ref.gemm_mxfp4_int8).
+GPU against the fp64 oracle (oracle.ref.gemm_mxfp4_int8), through the
+streaming family (M < 64, MoE blocks of 16 and 32 rows) and the 8-bit
+LDS-tiled family (M >= 64, MoE blocks of 64 and 128 rows).
 
 The kernel splits every int8 activation exactly into 16 * hi + lo (E4M3
 planes) and runs the fp8 x fp4 scaled MFMA on both planes, so every product
@@ -31,7 +33,7 @@ def _packed(n, k, codes, e, otype, num_experts=1):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 96, 256), (16, 2048, 7168), (16, 7168, 2048), (37, 200, 640),
-                                   (64, 512, 1024), (200, 272, 512)])
+                                   (64, 512, 1024), (200, 272, 512), (300, 1040, 2048), (512, 2048, 7168)])
 def test_mxfp4_int8_parity(qdg, m, n, k):
     codes, e = _weights(n, k, salt=m)
     a = synth.activations_bf16_bits(m, k, workload_id=2, salt=m + 1)
@@ -40,13 +42,14 @@ def test_mxfp4_int8_parity(qdg, m, n, k):
     for otype in (q.QDG_O_F32, q.QDG_O_BF16):
         layer, pk = _packed(n, k, codes, e, otype)
         y, plan = H.gemm(layer, pk, H.dev(qa), m, a_scales=H.dev(sa))
-        assert "family=stream" in q.qdg_plan_describe(plan, m)
+        # the streaming family below 64 rows, the 8-bit LDS-tiled one from 64
+        assert ("family=qtile " if m >= 64 else "family=stream ") in q.qdg_plan_describe(plan, m)
         err = metrics.rel_frob(H.to_f64(y), y64)
         print(f"MXFP4xINT8 M={m} N={n} K={k} otype={otype}: rel_frob={err:.3e}")
         assert err <= (1e-3 if otype == q.QDG_O_F32 else 2e-3), err
 
 
-@pytest.mark.parametrize("m", [16, 64])
+@pytest.mark.parametrize("m", [16, 64, 128])
 def test_mxfp4_int8_one_hot_extreme_codes(qdg, m):
     # a single code per row, -128, 127 or a small value, at a different k per
     # row, unit token scale: each output row is code * (dequantized weights)
@@ -82,7 +85,7 @@ def test_mxfp4_int8_device_quantizer_pipeline(qdg):
     assert metrics.rel_frob(H.to_f64(y), ref.gemm_mxfp4_int8(qa, sa, codes, e)) <= 2e-3
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
 def test_mxfp4_int8_moe(qdg, bm):
     # grouped MoE: E=4 experts, top-2, gate+up over token rows and down over
     # pair rows, fp32 output against the per-pair oracle rows
@@ -103,6 +106,7 @@ def test_mxfp4_int8_moe(qdg, bm):
         q.qdg_moe_align(H.dev(ids.astype(np.int32)).data_ptr(), t, top_k, E, bm, sid.data_ptr(), blk.data_ptr(),
                         npad.data_ptr(), q.current_stream())
         plan = q.qdg_plan_create(layer, q.moe(top_k))
+        assert ("family=qtile " if bm >= 64 else "family=stream ") in q.qdg_moe_describe(plan, t, bm)
         wsp, nbytes = H.workspace(plan, t)
         y = H.out_tensor(t * top_k, n, q.QDG_O_F32)
         qa_d, sa_d = H.dev(qa), H.dev(sa)
