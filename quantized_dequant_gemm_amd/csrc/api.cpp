@@ -276,6 +276,8 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
       if (split > maxs) split = maxs > 0 ? maxs : 1;
       if (split > 16) split = 16;
     }
+    // a tuning's split beyond the group count would leave empty K ranges
+    if (split > g.groups) split = (int)g.groups;
     ch.sc = StreamCfg{bm / 16, ch.tc.bn / 16, ch.tc.waves, split};
     ch.partial_bytes = split > 1 ? (size_t)tiles * split * ch.tc.bm * ch.tc.bn * 4 : 0;
     ch.rowsum_bytes = P.fmt == FMT_NVFP4 ? 0 : (size_t)ch.grid_m * bm * g.groups * 4;  // NVFP4: no offsets
@@ -354,6 +356,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
       if (split > maxs) split = maxs > 0 ? maxs : 1;
       if (split > 16) split = 16;
     }
+    if (split > g.groups) split = (int)g.groups;  // no empty K ranges
     if (P.layer.otype == QDG_O_I32) split = 1;  // integer results are never split
     ch.sc = StreamCfg{8, 16, 8, split};
     ch.partial_bytes = split > 1 ? (size_t)tiles * split * 128 * 256 * 4 : 0;
@@ -384,6 +387,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
     if (split > maxs) split = maxs > 0 ? maxs : 1;
     if (one_tile) split = 1;
   }
+  if (split > g.groups) split = (int)g.groups;  // no empty K ranges
   if (moe || P.layer.otype == QDG_O_I32) split = 1;  // raw integer results are not split
   ch.sc.split = split;
   ch.partial_bytes = split > 1 ? (size_t)nblocks * ch.grid_m * split * ch.sc.mt * nt * 4 * 64 * 4 : 0;

@@ -300,3 +300,15 @@ def test_noalloc_refuses_oversized_workspace_before_device_work():
     assert _status(q.qdg_gemm_noalloc, plan, None, None, None, None, 8192) == q.QDG_ERR_WORKSPACE
     assert "workspace" in q.qdg_last_error()
     assert q.load().qdg_gemm_noalloc(None, None, None, None, None, 16, None) == q.QDG_ERR_INVALID_ARG
+
+
+def test_tuned_split_never_exceeds_the_k_groups():
+    # K = 1024 holds 8 groups of 128: a tuning that asks for more splits gets
+    # one group per split in every family (no empty K range is launched)
+    cases = [(q.layer_w4a16(4096, 1024), q.TuningConfig(block_m=128, split_k=64), 256, "family=tile"),
+             (q.layer_w8a8(4096, 1024), q.TuningConfig(block_m=128, split_k=64), 256, "family=qtile"),
+             (q.layer_w8a8(4096, 1024), q.TuningConfig(block_m=32, block_n=32, split_k=64), 32, "family=stream"),
+             (q.layer_w4a16(4096, 1024), q.TuningConfig(block_m=16, split_k=64), 16, "family=wstream")]
+    for layer, tun, m, fam in cases:
+        d = q.qdg_plan_describe(q.qdg_plan_create(layer, q.dense(), tun), m)
+        assert fam in d and "split_k=8 " in d, d
