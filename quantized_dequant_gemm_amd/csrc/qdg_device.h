@@ -221,4 +221,21 @@ __device__ __forceinline__ u32x4_t e2m1x8_scaled_bf16(uint32_t d, float s) {
                  e2m1x2_scaled_bf16<3>(d, s)};
 }
 
+// Tile order of the LDS-tiled grouped MoE launches. Which expert blocks hold
+// rows is known on the device only (the first num_padded / BM of the
+// capacity), so the order must not hand any XCD a range of empty blocks:
+// workgroup ids go to the 8 XCDs in turn, and id i takes block
+// 8 * (i / 8 / n_blocks) + i % 8 and column block (i / 8) % n_blocks. Every
+// XCD then runs whole blocks (all their column blocks, so a block's A rows
+// stay in that XCD's L2), and on every XCD the blocks that hold rows come
+// first. The grid covers whole groups of 8 blocks (moe_grid_blocks); blocks
+// past the capacity return like the empty ones.
+__device__ __forceinline__ void moe_tile_order(int n_blocks, int& mb, int& nb) {
+  const int x = (int)(blockIdx.x % 8u), j = (int)(blockIdx.x / 8u);
+  mb = (j / n_blocks) * 8 + x;
+  nb = j % n_blocks;
+}
+
+__host__ __device__ constexpr int moe_grid_blocks(int m_blocks) { return (m_blocks + 7) / 8 * 8; }
+
 }  // namespace qdg

@@ -251,18 +251,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qtile_gemm_kernel(cons
   // XCD-aware tile order: consecutive workgroup ids go to different XCDs,
   // so XCD x takes the x-th eighth of the tile order; that order walks 4 x 8
   // blocks of tiles, so the 32 tiles an XCD runs at once share 4 row blocks
-  // of A and 8 column blocks of W in its L2
-  const int total = m_blocks * n_blocks;
-  int lin = blockIdx.x;
+  // of A and 8 column blocks of W in its L2 (grouped MoE: moe_tile_order)
   int mb, nb;
-  if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
-  if (m_blocks % 4 == 0 && n_blocks % 8 == 0) {
-    const int sb = lin / 32, w = lin % 32;
-    mb = (sb / (n_blocks / 8)) * 4 + w / 8;
-    nb = (sb % (n_blocks / 8)) * 8 + w % 8;
+  if constexpr (MOE) {
+    moe_tile_order(n_blocks, mb, nb);
   } else {
-    mb = lin / n_blocks;
-    nb = lin % n_blocks;
+    const int total = m_blocks * n_blocks;
+    int lin = blockIdx.x;
+    if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
+    if (m_blocks % 4 == 0 && n_blocks % 8 == 0) {
+      const int sb = lin / 32, w = lin % 32;
+      mb = (sb / (n_blocks / 8)) * 4 + w / 8;
+      nb = (sb % (n_blocks / 8)) * 8 + w % 8;
+    } else {
+      mb = lin / n_blocks;
+      nb = lin % n_blocks;
+    }
   }
   const int split = blockIdx.y, nsplit = gridDim.y;
   const int g0 = (int)(((int64_t)split * p.groups) / nsplit);
@@ -463,8 +467,8 @@ hipError_t launch_q(const GemmArgs& a, bool moe, int bm, int m_blocks, int nspli
     constexpr int BM = 64, BN = 512;
     constexpr int NS = 3 * QStage<KIND, BM, BN>::BYTES <= 160 * 1024 ? 3 : 2;
     const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-    hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, true, 1, 8>), dim3(m_blocks * n_blocks, 1), dim3(512), 0, s,
-                       a, m_blocks, n_blocks);
+    hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, true, 1, 8>), dim3(moe_grid_blocks(m_blocks) * n_blocks, 1),
+                       dim3(512), 0, s, a, m_blocks, n_blocks);
     return hipGetLastError();
   }
   if (bm != 128) return hipErrorInvalidValue;
@@ -473,8 +477,8 @@ hipError_t launch_q(const GemmArgs& a, bool moe, int bm, int m_blocks, int nspli
   constexpr int NS = 3 * L::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
   if (moe) {
-    hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, true>), dim3(m_blocks * n_blocks, 1), dim3(512), 0, s, a,
-                       m_blocks, n_blocks);
+    hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, true>), dim3(moe_grid_blocks(m_blocks) * n_blocks, 1),
+                       dim3(512), 0, s, a, m_blocks, n_blocks);
   } else {
     hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, false>), dim3(m_blocks * n_blocks, nsplit), dim3(512), 0,
                        s, a, m_blocks, n_blocks);

@@ -482,18 +482,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   // XCD-aware tile order: consecutive workgroup ids land on different XCDs,
   // so XCD x takes the x-th eighth of the tile order; that order walks 4 x 8
   // blocks of tiles, so the tiles an XCD runs at once share row blocks of A
-  // and column blocks of W in its L2
-  const int total = m_blocks * n_blocks;
-  int lin = blockIdx.x;
-  if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
+  // and column blocks of W in its L2 (grouped MoE: moe_tile_order)
   int mb, nb;
-  if (m_blocks % 4 == 0 && n_blocks % 8 == 0) {
-    const int sb = lin / 32, w = lin % 32;
-    mb = (sb / (n_blocks / 8)) * 4 + w / 8;
-    nb = (sb % (n_blocks / 8)) * 8 + w % 8;
+  if constexpr (MOE) {
+    moe_tile_order(n_blocks, mb, nb);
   } else {
-    mb = lin / n_blocks;
-    nb = lin % n_blocks;
+    const int total = m_blocks * n_blocks;
+    int lin = blockIdx.x;
+    if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
+    if (m_blocks % 4 == 0 && n_blocks % 8 == 0) {
+      const int sb = lin / 32, w = lin % 32;
+      mb = (sb / (n_blocks / 8)) * 4 + w / 8;
+      nb = (sb % (n_blocks / 8)) * 8 + w % 8;
+    } else {
+      mb = lin / n_blocks;
+      nb = lin % n_blocks;
+    }
   }
   // split-K: this workgroup reduces K groups [g0, g1) of the tile
   const int split = blockIdx.y, nsplit = gridDim.y;
@@ -788,7 +792,9 @@ hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStrea
   // 2 for 256 x 128, 64 x 512 and int8 units)
   constexpr int NS = 3 * Stage<BM, BN, W8 ? 2048 : W2 ? 512 : 1024>::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE, NV, W8, W2>), dim3(m_blocks * n_blocks, nsplit),
+  // grouped MoE: whole groups of 8 expert blocks (the order of moe_tile_order)
+  const int grid_m = MOE ? moe_grid_blocks(m_blocks) : m_blocks;
+  hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE, NV, W8, W2>), dim3(grid_m * n_blocks, nsplit),
                      dim3(64 * WAVES_M * WAVES_N), 0, s, a, m_blocks, n_blocks);
   return hipGetLastError();
 }
