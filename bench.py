@@ -543,12 +543,12 @@ def rows_leg(reps=30):
         logits = torch.randn((t, E), generator=g, device=dev, dtype=torch.float32)
         ids = torch.topk(logits, top_k, dim=1).indices.to(torch.int32).contiguous()
         touched = int(torch.unique(ids).numel())
-        # 16 / 32-row blocks in the streaming family while experts hold few
-        # rows, 64-row blocks in the 8-bit LDS-tiled family beyond (measured
-        # on MI355X at T = 4096: 2226 / 1375 us gate+up / down, against
-        # 2583 / 1759 us with 128-row blocks and 4584 / 2859 us with 32-row
-        # streaming blocks)
-        bm = 16 if t == 64 else 32 if t == 512 else 64
+        # 16-row blocks in the streaming family while experts hold a few
+        # rows (T = 64), 64-row blocks in the 8-bit LDS-tiled family from
+        # about 16 rows per expert (measured on MI355X, gate+up / down: T = 512
+        # 802 / 486 us against 898 / 548 us with 32-row streaming blocks;
+        # T = 4096 1959 / 1228 us against 2164 / 1384 us with 128-row blocks)
+        bm = 16 if t * top_k <= 4 * E else 64
         cap = q.qdg_moe_align_capacity(t, top_k, E, bm)
         sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
         block_expert = torch.empty(cap // bm, dtype=torch.int32, device=dev)
