@@ -20,6 +20,7 @@ namespace {
 
 constexpr int kWaves = 16;
 constexpr int kMaxE = 1024;
+constexpr int kU = 8;  // 64-pair chunks whose loads are issued together
 
 __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restrict__ ids, int total, int E,
                                                          int bm, int capacity, int32_t* __restrict__ sorted_ids,
@@ -34,10 +35,22 @@ __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restri
   __syncthreads();
   const int slice = (total + kWaves - 1) / kWaves;
   const int lo = min(total, wave * slice), hi = min(total, lo + slice);
-  for (int i = lo + lane; i < hi; i += 64) {
-    const int e = ids[i];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[wave][e], 1);
-    else if (status) atomicOr(status, QDG_FLAG_BAD_EXPERT_ID);  // the pair is left out
+  // kU loads of the slice go out before their counts, so that a long slice
+  // costs one load latency per kU * 64 pairs, not one per 64
+  for (int base = lo; base < hi; base += kU * 64) {
+    int ev[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * 64 + lane;
+      ev[u] = i < hi ? ids[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = ev[u];
+      if (base + u * 64 + lane >= hi) continue;
+      if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[wave][e], 1);
+      else if (status) atomicOr(status, QDG_FLAG_BAD_EXPERT_ID);  // the pair is left out
+    }
   }
   __syncthreads();
 
@@ -80,22 +93,32 @@ __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restri
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const int e = i < hi ? ids[i] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t ones = __ballot(bit);
-      same &= bit ? ones : ~ones;
+  for (int base = lo; base < hi; base += kU * 64) {
+    int ev[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * 64 + lane;
+      ev[u] = i < hi ? ids[i] : -1;
     }
-    if (valid) {
-      const int rank = __popcll(same & lt);
-      const int n = __popcll(same);
-      const int pos = cnt[wave][e] + rank;
-      sorted_ids[pos] = i;
-      if (rank == n - 1) cnt[wave][e] += n;  // one writer per expert
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      // chunks in order: the runs of chunk u start after those of u - 1
+      const int i = base + u * 64 + lane;
+      const int e = ev[u];
+      const bool valid = (unsigned)e < (unsigned)E;
+      uint64_t same = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t ones = __ballot(bit);
+        same &= bit ? ones : ~ones;
+      }
+      if (valid) {
+        const int rank = __popcll(same & lt);
+        const int n = __popcll(same);
+        const int pos = cnt[wave][e] + rank;
+        sorted_ids[pos] = i;
+        if (rank == n - 1) cnt[wave][e] += n;  // one writer per expert
+      }
     }
   }
 }
