@@ -426,6 +426,16 @@ qdg_status check_tuning(const qdg_layer_config& layer, const qdg_compute_config&
   const bool tile_ok = dense_tiled && (tuning.block_m == 128 || (f == FMT_W4A16 && tuning.block_m == 256));
   // dense W4A16: block_m 64 with block_n 512 names the 64 x 512 tiles
   const bool tile64 = dense_tiled && f == FMT_W4A16 && tuning.block_m == 64 && tuning.block_n == 512;
+  // grouped MoE W4A16: block_n 512 asks for 16 x 512 tiles for 16-row blocks
+  const bool moe_tile16 = compute.kind == QDG_KIND_MOE && !compute.batch_invariant && f == FMT_W4A16 &&
+                          tuning.block_n == 512 && (!tuning.block_m || tuning.block_m == 16);
+  if (moe_tile16) {
+    if (tuning.waves && tuning.waves != 8) return fail(QDG_ERR_UNSUPPORTED, "16 x 512 tiles run 8 waves");
+    if (tuning.block_k && tuning.block_k != 128) return fail(QDG_ERR_UNSUPPORTED, "block_k must be 128");
+    if (tuning.mfma && tuning.mfma != 16) return fail(QDG_ERR_UNSUPPORTED, "mfma must be 16 (16x16 tiles)");
+    if (tuning.split_k > 1) return fail(QDG_ERR_UNSUPPORTED, "grouped MoE does not split K");
+    return QDG_OK;
+  }
   if (tile64) {
     if (tuning.waves && tuning.waves != 8) return fail(QDG_ERR_UNSUPPORTED, "64 x 512 tiles run 8 waves");
     if (tuning.block_k && tuning.block_k != 128) return fail(QDG_ERR_UNSUPPORTED, "block_k must be 128");
@@ -457,6 +467,8 @@ qdg_status check_tuning(const qdg_layer_config& layer, const qdg_compute_config&
 }
 
 }  // namespace
+
+static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, int32_t a_per_pair, Choice* out);
 
 extern "C" {
 
@@ -563,8 +575,18 @@ qdg_status qdg_plan_create(const qdg_layer_config* layer, const qdg_compute_conf
   p->fmt = f;
   p->geom = packed_geom(*layer, f);
   if (tuning) {
-    const Choice c = choose(*p, 1);
-    if (!instance_exists(f, c)) {
+    // grouped plans: the instance of one token in blocks of the tuning's
+    // block_m (16 when it names none)
+    Choice c;
+    bool exists;
+    if (compute->kind == QDG_KIND_MOE) {
+      const int bm = tuning->block_m ? tuning->block_m : 16;
+      exists = choose_moe(*p, 1, bm, 0, &c) == QDG_OK && instance_exists(f, c);
+    } else {
+      c = choose(*p, 1);
+      exists = instance_exists(f, c);
+    }
+    if (!exists) {
       delete p;
       return fail(QDG_ERR_UNSUPPORTED, "no kernel instance for block_m/block_n/waves of this tuning");
     }
@@ -598,9 +620,9 @@ qdg_status qdg_plan_workspace(const qdg_plan* plan, int64_t M, size_t* bytes) {
 }
 
 // Kernel choice of a grouped MoE call: the caller's block size decides the
-// family. 16-row blocks stream the weights (unless a tuning pins the
-// streaming family), 128-row blocks run the LDS-tiled family with one expert
-// per row block, 32 and 64 rows the streaming family.
+// family. W4A16: 16-row blocks run the streaming family (the LDS-tiled one
+// when K is short, weight streaming when a tuning pins it), 32-, 64- and
+// 128-row blocks the LDS-tiled family; the other formats as noted below.
 static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, int32_t a_per_pair, Choice* out) {
   const Choice c0 = choose(plan, T);
   Choice c = c0;
@@ -662,13 +684,20 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
   c.qtile = false;
   // 32-, 64- and 128-row blocks: the LDS-tiled family (32 x 512, 64 x 512
   // and 128 x 256 tiles). Measured on MI355X at E = 256, hidden 7168: at
-  // T = 512 32-row blocks in it run gate+up in 1112 us and down in 577-588 us
-  // (32 x 256 tiles: 1185-1208 and 618-622 us), against 1467 and 1107 us in
-  // the streaming family (1284 and 761 us with 16-row blocks); at T = 4096
-  // 64-row blocks run gate+up in 3260 us and down in 1737 us against 3792 and
-  // 2136 us with 128-row blocks (less padding per expert), where 64-row
+  // T = 512 32-row blocks in it run gate+up in 842 us and down in 449 us,
+  // against 1259 and 758 us for 16-row streaming blocks; at T = 4096 64-row
+  // blocks run gate+up in 2842 us and down in 1583 us against 3203 and
+  // 1813 us with 128-row blocks (less padding per expert), where 64-row
   // streaming blocks took 7.1 and 7.4 ms
-  if (block_m == 128 || ((block_m == 32 || block_m == 64) && !plan.compute.batch_invariant)) {
+  // 16-row blocks: 16 x 512 tiles of the LDS-tiled family when a tuning asks
+  // for them (block_n 512) or, without a tuning, when K holds at most 16
+  // groups. Measured on MI355X at E = 256, T = 64: the down projection
+  // (K = 2048, N = 7168) in 321 us against 380 us in the streaming family
+  // (whose workgroups then hold 4 groups per wave), gate+up (K = 7168) in
+  // 609 against 587 us
+  const bool tile16 = block_m == 16 && !plan.compute.batch_invariant && !c.ws &&
+                      (plan.has_tuning ? tu.block_n == 512 : plan.geom.groups <= 16);
+  if (block_m == 128 || tile16 || ((block_m == 32 || block_m == 64) && !plan.compute.batch_invariant)) {
     // A rows are addressed with 32-bit byte offsets in the tiled family
     const int64_t a_rows = a_per_pair ? rows : T;
     if ((double)a_rows * (double)plan.layer.k * 2.0 >= 4294967296.0)

@@ -817,7 +817,7 @@ bool tile_cfg_supported(Format f, const TileCfg& c) {
   if (f != FMT_W4A16) return false;
   if (c.bm == 256 && c.bn == 128) return c.waves == 8;
   if (c.bm == 128 && c.bn == 256) return c.waves == 8 || c.waves == 4;
-  if (c.bm == 32 && c.bn == 512) return c.waves == 8;
+  if ((c.bm == 16 || c.bm == 32) && c.bn == 512) return c.waves == 8;
   if (c.bm == 64 && c.bn == 512) return c.waves == 8;
   return false;
 }
@@ -845,6 +845,7 @@ hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const Ge
   QDG_T(true, 1, 4, 128, false)
   QDG_T(false, 2, 4, 64, true)
   QDG_T(false, 1, 4, 128, true)
+  QDG_T(false, 1, 8, 16, true)
   QDG_T(false, 1, 8, 32, true)
   QDG_T(false, 1, 8, 64, true)
   QDG_T(false, 1, 8, 64, false)

@@ -142,10 +142,10 @@ def _align(ids, E, bm):
     return sid, blk, npad
 
 
-def _moe_run(layer, pk, a_dev, a_scales, ids, bm, a_per_pair):
+def _moe_run(layer, pk, a_dev, a_scales, ids, bm, a_per_pair, tuning=None):
     t, top_k = ids.shape
     sid, blk, npad = _align(ids, layer.num_experts, bm)
-    plan = q.qdg_plan_create(layer, q.moe(top_k))
+    plan = q.qdg_plan_create(layer, q.moe(top_k), tuning)
     ws, nbytes = H.workspace(plan, t)
     y = H.out_tensor(t * top_k, layer.n, layer.otype)
     q.qdg_moe_gemm(plan, a_dev.data_ptr(), a_scales.data_ptr() if a_scales is not None else None,
@@ -155,10 +155,12 @@ def _moe_run(layer, pk, a_dev, a_scales, ids, bm, a_per_pair):
     return y, q.qdg_moe_describe(plan, t, bm)
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
-def test_moe_w4a16_int4_minus8_one_hot(qdg, bm):
+@pytest.mark.parametrize("bm,stream", [(16, False), (16, True), (32, False), (64, False), (128, False)])
+def test_moe_w4a16_int4_minus8_one_hot(qdg, bm, stream):
     # token t's row is e_{k_t}; each of its top-2 pair rows is then one
-    # column of its expert's dequantized weight, exact in fp32
+    # column of its expert's dequantized weight, exact in fp32 (16-row
+    # blocks of this short K run the LDS-tiled family, or the streaming one
+    # when a tuning pins it)
     E, top_k, k, n, t = 3, 2, 256, 64, 150
     vs = [_int4_codes(n, k, seed=50 + e) for e in range(E)]
     ss = [_f16_pow2_scales(n, k // 128, seed=60 + e) for e in range(E)]
@@ -171,8 +173,9 @@ def test_moe_w4a16_int4_minus8_one_hot(qdg, bm):
     kt = r.integers(0, k, t)
     a = np.zeros((t, k), np.float32)
     a[np.arange(t), kt] = 1.0
-    y, desc = _moe_run(layer, pk, H.bf16_dev(codecs.f32_to_bf16_bits(a)), None, ids, bm, 0)
-    assert ("family=tile" in desc) == (bm in (32, 64, 128))
+    tun = q.TuningConfig(block_n=64, waves=4) if stream else None
+    y, desc = _moe_run(layer, pk, H.bf16_dev(codecs.f32_to_bf16_bits(a)), None, ids, bm, 0, tuning=tun)
+    assert ("family=stream " if stream else "family=tile ") in desc
     want = np.stack([ref.dequant_int4_sym(vs[ids[p // top_k, p % top_k]], ss[ids[p // top_k, p % top_k]])[:, kt[p // top_k]]
                      for p in range(t * top_k)])
     assert np.array_equal(H.to_f64(y), want)

@@ -105,7 +105,9 @@ def test_jit_moe_matches_aot(qdg):
     a_dev = H.bf16_dev(a)
     outs = []
     for use_jit in (False, True):
-        plan = q.qdg_plan_create(layer, q.moe(top_k))
+        # the streaming family (16-row blocks of a K this short default to
+        # the LDS-tiled family, which is compiled ahead of time only)
+        plan = q.qdg_plan_create(layer, q.moe(top_k), q.TuningConfig(block_n=64, waves=4))
         if use_jit:
             q.qdg_plan_jit(plan, t, bm)
             assert "code=jit" in q.qdg_moe_describe(plan, t, bm)

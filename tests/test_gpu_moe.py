@@ -72,22 +72,28 @@ def _moe_gemm(layer, pk, a_dev, ids, bm, a_per_pair, top_k, tuning=None, batch_i
     return y
 
 
-@pytest.mark.parametrize("t,bm", [(8, 16), (64, 16), (256, 32), (300, 64), (300, 128), (1024, 128)])
-def test_moe_gemm_small_experts(qdg, t, bm):
-    # E=16 experts, top-4, hidden 1024 -> intermediate 2*256 (gate+up) and back
+@pytest.mark.parametrize("t,bm,stream", [(8, 16, False), (64, 16, False), (64, 16, True), (256, 32, False),
+                                         (300, 64, False), (300, 128, False), (1024, 128, False)])
+def test_moe_gemm_small_experts(qdg, t, bm, stream):
+    # E=16 experts, top-4, hidden 1024 -> intermediate 2*256 (gate+up) and
+    # back; 16-row blocks of these short K run 16 x 512 tiles, or the
+    # streaming family when a tuning pins it
     E, top_k, hid, inter = 16, 4, 1024, 256
+    tun = q.TuningConfig(block_n=64, waves=4) if stream else None
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=t), top_k)
     qs, ss = _experts(E, 2 * inter, hid, salt=1)
     layer, pk = _moe_packed(qs, ss, 2 * inter, hid)
     x = synth.activations_bf16_bits(t, hid, workload_id=4, salt=t)
-    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 0, top_k)
+    fam = "stream" if stream else "tile"
+    assert f"family={fam} " in q.qdg_moe_describe(q.qdg_plan_create(layer, q.moe(top_k), tun), t, bm)
+    y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 0, top_k, tuning=tun)
     y64 = ref.moe_gemm_rows(x, ids, lambda e: ref.dequant_int4_sym(qs[e], ss[e]), input_is_per_pair=False)
     assert metrics.rel_frob(H.to_f64(y), y64) <= 2e-3
     # down projection: one input row per pair
     qd, sd = _experts(E, hid, inter, salt=2)
     layer_d, pk_d = _moe_packed(qd, sd, hid, inter)
     h = synth.moe_hidden_bf16_bits(t * top_k, inter, salt=t)
-    yd = _moe_gemm(layer_d, pk_d, H.bf16_dev(h), ids, bm, 1, top_k)
+    yd = _moe_gemm(layer_d, pk_d, H.bf16_dev(h), ids, bm, 1, top_k, tuning=tun)
     yd64 = ref.moe_gemm_rows(h, ids, lambda e: ref.dequant_int4_sym(qd[e], sd[e]), input_is_per_pair=True)
     assert metrics.rel_frob(H.to_f64(yd), yd64) <= 2e-3
 
@@ -104,7 +110,9 @@ def test_moe_single_expert_equals_dense(qdg, bm, pin_ws):
     layer, pk = _moe_packed(qs, ss, n, hid)
     x = synth.activations_bf16_bits(t, hid, workload_id=4, salt=5)
     ids = np.zeros((t, 1), np.int32)
-    tm = q.TuningConfig(block_n=64, waves=8) if pin_ws else None
+    # (16-row blocks of this short K default to the LDS-tiled family: the
+    # streaming one is pinned by a tuning)
+    tm = q.TuningConfig(block_n=64, waves=8 if pin_ws else 4) if bm == 16 else None
     plan = q.qdg_plan_create(layer, q.moe(1, batch_invariant=int(bm == 32)), tm)
     fam = q.qdg_moe_describe(plan, t, bm).split("family=")[1].split()[0]
     assert fam == {16: "wstream" if pin_ws else "stream", 32: "stream", 128: "tile"}[bm]
@@ -156,7 +164,8 @@ def test_moe_full_size_sampled_rows(qdg, proj, t, bm):
         x = synth.activations_bf16_bits(t, k, workload_id=4)
     y = _moe_gemm(layer, pk, H.bf16_dev(x), ids, bm, 1 if per_pair else 0, top_k)
     fam = q.qdg_moe_describe(q.qdg_plan_create(layer, q.moe(top_k)), t, bm).split("family=")[1].split()[0]
-    assert fam == ("tile" if bm in (32, 64, 128) else "stream")
+    # 16-row blocks: 16 x 512 tiles when K holds at most 16 groups
+    assert fam == ("tile" if bm in (32, 64, 128) or k <= 2048 else "stream")
     xf = codecs.bf16_bits_to_f64(x)
     for p in pairs:
         e = int(ids.reshape(-1)[p])
@@ -169,15 +178,16 @@ def test_moe_full_size_sampled_rows(qdg, proj, t, bm):
     assert not torch.isnan(y.float()).any()
 
 
-@pytest.mark.parametrize("t,bm,inter", [(8, 16, 256), (64, 16, 144), (64, 32, 256), (64, 32, 144), (300, 64, 256),
-                                         (300, 64, 144), (300, 128, 256), (1024, 128, 144)])
+@pytest.mark.parametrize("t,bm,inter,stream", [(8, 16, 256, True), (64, 16, 144, True), (64, 16, 144, False),
+                                                (64, 32, 256, False), (64, 32, 144, False), (300, 64, 256, False),
+                                                (300, 64, 144, False), (300, 128, 256, False), (1024, 128, 144, False)])
 @pytest.mark.parametrize("otype", [q.QDG_O_F32, q.QDG_O_BF16])
-def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, inter, otype):
+def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, inter, stream, otype):
     # fused gate+up (n = 2I) with the SiLU*mul epilogue: Y = silu(G) * U,
-    # [T*top_k][I]; 16-row blocks run the streaming family (four tiles, two
-    # gate + two up, per workgroup), 32-, 64- and 128-row blocks the LDS-tiled
-    # one (I = 144: an odd number of gate tiles, so a workgroup's tile slots
-    # run partly past the layer)
+    # [T*top_k][I]; 16-row blocks pinned to the streaming family run four
+    # tiles (two gate + two up) per workgroup, every other case here the
+    # LDS-tiled family (I = 144: an odd number of gate tiles, so a
+    # workgroup's tile slots run partly past the layer)
     E, top_k, hid = 16, 4, 1024
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=t + 11), top_k)
     qs, ss = _experts(E, 2 * inter, hid, salt=9)
@@ -188,9 +198,10 @@ def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, inter, otype):
     x = synth.activations_bf16_bits(t, hid, workload_id=4, salt=t + 12)
     a_dev = H.bf16_dev(x)
     sid, blk, npad, cap = _align_dev(ids, E, bm)
-    plan = q.qdg_plan_create(layer, q.moe(top_k, epilogue=q.QDG_EPI_SILU_MUL))
+    tun = q.TuningConfig(block_n=64, waves=4) if stream else None
+    plan = q.qdg_plan_create(layer, q.moe(top_k, epilogue=q.QDG_EPI_SILU_MUL), tun)
     desc = q.qdg_moe_describe(plan, t, bm)
-    assert "epilogue=silu_mul" in desc and ("family=tile" in desc) == (bm in (32, 64, 128))
+    assert "epilogue=silu_mul" in desc and ("family=tile" in desc) == (not stream)
     ws, nbytes = H.workspace(plan, t)
     y = H.out_tensor(t * top_k, inter, otype)
     q.qdg_moe_gemm(plan, a_dev.data_ptr(), None, pk.buf.data_ptr(), sid.data_ptr(), blk.data_ptr(),
@@ -202,6 +213,43 @@ def test_moe_gate_up_silu_mul_epilogue(qdg, t, bm, inter, otype):
     err = metrics.rel_frob(H.to_f64(y), h64)
     print(f"silu*mul T={t} bm={bm} otype={otype}: rel_frob={err:.3e}")
     assert err <= (1e-3 if otype == q.QDG_O_F32 else 2e-3), err
+
+
+@pytest.mark.parametrize("t", [8, 64, 300])
+@pytest.mark.parametrize("silu", [False, True])
+def test_moe_16_row_tiles(qdg, t, silu):
+    # a tuning with block_n 512 runs 16-row blocks as 16 x 512 tiles of the
+    # LDS-tiled family (gate+up over token rows, with or without SiLU*mul;
+    # down over pair rows); I = 144 leaves part of a workgroup's tile slots
+    # past the layer
+    E, top_k, hid, inter = 16, 4, 1024, 144
+    tun = q.TuningConfig(block_m=16, block_n=512, waves=8)
+    ids, _ = ref.route_topk(synth.router_logits(t, E, salt=t + 21), top_k)
+    qs, ss = _experts(E, 2 * inter, hid, salt=13)
+    x = synth.activations_bf16_bits(t, hid, workload_id=4, salt=t + 22)
+    gu64 = ref.moe_gemm_rows(x, ids, lambda e: ref.dequant_int4_sym(qs[e], ss[e]), input_is_per_pair=False)
+    layer, pk = _moe_packed(qs, ss, 2 * inter, hid)
+    sid, blk, npad, cap = _align_dev(ids, E, 16)
+    plan = q.qdg_plan_create(layer, q.moe(top_k, epilogue=q.QDG_EPI_SILU_MUL if silu else 0), tun)
+    assert "family=tile block_m=16 block_n=512" in q.qdg_moe_describe(plan, t, 16)
+    ws, nbytes = H.workspace(plan, t)
+    y = H.out_tensor(t * top_k, inter if silu else 2 * inter, q.QDG_O_BF16)
+    q.qdg_moe_gemm(plan, H.bf16_dev(x).data_ptr(), None, pk.buf.data_ptr(), sid.data_ptr(), blk.data_ptr(),
+                   npad.data_ptr(), t, 16, 0, y.data_ptr(), ws.data_ptr(), nbytes, q.current_stream())
+    torch.cuda.synchronize()
+    assert not torch.isnan(y.float()).any()
+    want = ref.silu_mul(gu64) if silu else gu64
+    err = metrics.rel_frob(H.to_f64(y), want)
+    print(f"16-row tiles T={t} silu={silu}: rel_frob={err:.3e}")
+    assert err <= 2e-3, err
+    if not silu:  # down projection (K = 256: whole groups of 128)
+        qd, sd = _experts(E, hid, 256, salt=14)
+        layer_d, pk_d = _moe_packed(qd, sd, hid, 256)
+        h = synth.moe_hidden_bf16_bits(t * top_k, 256, salt=t + 23)
+        yd = _moe_gemm(layer_d, pk_d, H.bf16_dev(h), ids, 16, 1, top_k, tuning=tun)
+        yd64 = ref.moe_gemm_rows(h, ids, lambda e: ref.dequant_int4_sym(qd[e], sd[e]), input_is_per_pair=True)
+        assert not torch.isnan(yd.float()).any()
+        assert metrics.rel_frob(H.to_f64(yd), yd64) <= 2e-3
 
 
 @pytest.mark.parametrize("t,otype", [(64, q.QDG_O_F32), (64, q.QDG_O_BF16), (1000, q.QDG_O_BF16)])
