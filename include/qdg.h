@@ -153,7 +153,9 @@ enum { QDG_EPI_NONE = 0, QDG_EPI_SILU_MUL = 1 };
      LDS-tiled         block_m 128 (block_n 256) or 256 (block_n 128), waves
                        8 or 4 (dense W4A16; the default from M = 65), and
                        block_m 64 with block_n 512, waves 8 (dense W4A16; the
-                       default for M = 33 to 64); block_m 128, block_n 256,
+                       default for M = 33 to 64); block_n 512 with block_m
+                       16 or 0, waves 8 (grouped MoE W4A16: 16 x 512 tiles
+                       for 16-row expert blocks); block_m 128, block_n 256,
                        waves 8 for dense W8A16, W4A16-NVFP4 and W2A16 (the
                        default from M = 33); the 8-bit activation formats
                        have their own 128 x 256 tiles (the default from
@@ -448,9 +450,12 @@ qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int3
    value passed to qdg_moe_align:
      16, 32, 64   every format, in the streaming family except where
                   noted: for W4A16 a tuning with block_n 64 and 8 waves
-                  pins the weight-streaming family for 16; W4A16 runs 32
-                  and 64 in the LDS-tiled family (32 x 512 and 64 x 512
-                  tiles); W8A8, W4A8-INT8, W4A8-MXFP4, W4A4 and
+                  pins the weight-streaming family for 16, and 16 runs
+                  16 x 512 tiles of the LDS-tiled family when K <= 2048
+                  or a tuning names block_n 512 (a tuning with block_n
+                  16, 32 or 64 and 4 waves keeps the streaming family);
+                  W4A16 runs 32 and 64 in the LDS-tiled family (32 x 512
+                  and 64 x 512 tiles); W8A8, W4A8-INT8, W4A8-MXFP4, W4A4 and
                   W4A8-MXFP4-INT8 run 64 in the 8-bit LDS-tiled family
                   (64 x 512 tiles) when the plan has no epilogue;
                   batch-invariant plans always stream;
