@@ -288,7 +288,13 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   // not depend on which family a given M selects)
   const bool ws_tuning_ok =
       !has_tuning || ((!T.block_m || T.block_m == 16) && (!T.block_n || T.block_n == 64) && (!T.waves || T.waves == 8));
-  if (bm == 16 && P.fmt == FMT_W4A16 && !P.compute.batch_invariant && ws_tuning_ok &&
+  // measured on MI355X (K = 14336, N = 4096, where weight streaming splits K
+  // four ways): up to 8 rows the streaming family (two tiles per workgroup,
+  // its own K split) is faster, 11.4 / 12.3 / 13.3 us at M = 1 / 4 / 8
+  // against 13.4 / 13.5 / 14.0 us; at 16 rows both take 13.7 us
+  const bool ws_split_few_rows =
+      !has_tuning && !moe && M <= 8 && kWsTargetWorkgroups / ((g.ntiles + 3) / 4) > 1;
+  if (bm == 16 && P.fmt == FMT_W4A16 && !P.compute.batch_invariant && ws_tuning_ok && !ws_split_few_rows &&
       (!moe || P.layer.wtype == QDG_W_INT4)) {
     ch.ws = true;
     ch.grid_m = 1;

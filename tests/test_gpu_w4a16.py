@@ -135,6 +135,9 @@ def test_weight_streaming_selected_for_small_m(qdg):
     assert _family(14336, 4096, 1) == "wstream"
     assert _family(4096, 14336, 16) == "wstream"
     assert _family(4096, 14336, 17) == "stream"
+    # where weight streaming would split K (N = 4096), up to 8 rows stream
+    assert _family(4096, 14336, 8) == "stream"
+    assert _family(4096, 14336, 9) == "wstream"
     assert _family(512, 1024, 16, q.TuningConfig(block_m=16, block_n=32)) == "stream"
 
 

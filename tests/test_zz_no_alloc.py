@@ -42,7 +42,7 @@ def test_noalloc_matches_workspace_entry_point(qdg):
     # first: the LDS-tiled family with a K split (fp32 partials and row sums
     # in the scratch array); second, smaller: weight streaming with a K split
     layer, pk = _layer(4096, 4096, salt=1)
-    for m, fam in ((200, "tile"), (8, "wstream")):
+    for m, fam in ((200, "tile"), (16, "wstream")):
         desc, y_ref, y_na = _both(layer, pk, m, 4096, salt=m)
         assert f"family={fam}" in desc and "split_k=1 " not in desc, desc
         assert not torch.isnan(y_ref.float()).any()
