@@ -308,10 +308,17 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   }
   // weight-streaming family of the int8 / fp8 formats (dense M <= 16): the
   // K range of a workgroup must fit its LDS; raw int32 output is not split
+  // Without a tuning only narrow layers (one N tile per workgroup) with at
+  // least 32 K groups stream this way: measured on MI355X at M = 16, W4A8
+  // (K = 4096, N = 4096) 6.3 us against 7.0 us in the streaming family and
+  // W4A8-MXFP4 (7168, 2048) 6.3 against 8.2 us, but W8A8 / W4A8 at
+  // N = 14336 (4 tiles per workgroup) 16.8 / 11.3 against 15.3 / 10.2 us and
+  // W4A8-MXFP4 (2048, 7168) (16 groups) 9.8 against 5.4 us
+  const bool ws8_heuristic_ok = has_tuning || ((g.ntiles + 3) / 4 < 128 && g.groups >= 32);
   if (bm == 16 && P.fmt != FMT_W4A16 && P.fmt != FMT_W4A4 && P.fmt != FMT_W8A16 && P.fmt != FMT_NVFP4 && !moe &&
       !no_wstream &&
       !P.compute.batch_invariant &&
-      ws_tuning_ok) {
+      ws_tuning_ok && ws8_heuristic_ok) {
     // 4 N tiles per workgroup when that gives enough workgroups, else one
     // tile with all 8 waves on its K range (no split across workgroups)
     const int nt = (g.ntiles + 3) / 4 >= 128 ? 4 : 1;
@@ -380,11 +387,22 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   // unpack is VALU-heavy); wider layers keep two tiles and no split
   const bool one_tile = ch.sc.mt == 1 && !P.compute.batch_invariant && !moe && g.ntiles >= 256 &&
                         g.ntiles < 512 && (P.fmt == FMT_NVFP4 || (P.fmt == FMT_W8A16 && g.groups <= 64));
+  // Up to 16 rows of the formats other than W4A16 (measured on MI355X at
+  // M = 16 over tile counts 1, 2, 4 and K splits 1 to 8): one tile per
+  // workgroup while the layer has at most 512 tiles, two beyond (W8A16,
+  // whose unpack is VALU-heavy: four; 17.0 against 18.3 us at N = 14336), and no K
+  // split once that gives 256 workgroups (e.g. W4A4 (2048, 7168) 5.1 us
+  // against 7.8 us for two tiles and two splits, W2A16 (4096, 4096) 7.2
+  // against 8.9 us for two tiles and four splits): the split's extra
+  // reduction launch costs more than the idle CUs
+  const bool few_rows = ch.sc.mt == 1 && !P.compute.batch_invariant && !moe && P.fmt != FMT_W4A16;
+  if (!nt && few_rows) nt = g.ntiles <= 512 ? 1 : P.fmt == FMT_W8A16 ? 4 : 2;
   if (!nt) nt = one_tile || (ch.sc.mt == 1 && g.ntiles < 128 && !P.compute.batch_invariant) ? 1 : 2;
   ch.sc.nt = nt;
   ch.grid_m = (int)((M + bm - 1) / bm);
   const int64_t nblocks = (g.ntiles + nt - 1) / nt;
   int split = has_tuning && T.split_k ? T.split_k : 0;
+  if (!split && few_rows && nblocks >= 256) split = 1;
   if (!split) {
     const int64_t wgs = nblocks * (P.compute.batch_invariant ? 1 : ch.grid_m);
     split = (int)(kTargetWorkgroups / (wgs > 0 ? wgs : 1));

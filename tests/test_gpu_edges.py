@@ -86,9 +86,11 @@ def test_w4a16_int4_minus8_one_hot(qdg, m, family):
 
 # ------------------------------------- W4A8 / W8A8: int4 -8, int8 -128 (raw int32)
 
-@pytest.mark.parametrize("m,family", [(16, "wstream"), (40, "stream"), (160, "qtile")])
+@pytest.mark.parametrize("m,family", [(16, "wstream"), (16, "stream"), (40, "stream"), (160, "qtile")])
 @pytest.mark.parametrize("kind", ["w4a8", "w8a8"])
 def test_int8_paths_extreme_codes_raw_exact(qdg, kind, m, family):
+    # (K = 512 is short: 16 rows stream by default, weight streaming is
+    # pinned by a tuning)
     k, n = 512, 272
     qa = _int8_codes((m, k), seed=m + 7)
     if kind == "w4a8":
@@ -103,7 +105,8 @@ def test_int8_paths_extreme_codes_raw_exact(qdg, kind, m, family):
         layer = q.layer_w8a8(n, k, otype=q.QDG_O_I32)
     pk = H.Packed(layer, qw, sc)
     plan = q.qdg_plan_create(layer, q.dense())
-    tuning = q.TuningConfig(block_m=128) if family == "qtile" else None
+    tuning = (q.TuningConfig(block_m=128) if family == "qtile" else
+              q.TuningConfig(waves=8) if family == "wstream" else None)
     if tuning is None:
         assert _family(plan, m) == family
     y, plan_used = H.gemm(layer, pk, H.dev(qa.astype(np.int8)), m, tuning=tuning)

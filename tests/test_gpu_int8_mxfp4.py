@@ -319,20 +319,24 @@ def _any_case(kind, m, n, k, salt):
 
 
 @pytest.mark.parametrize("kind", ["w8a8", "w4a8", "mxfp4"])
-@pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (3, 272, 1152), (16, 1040, 8320)])
-def test_8bit_weight_streaming(qdg, kind, m, n, k):
+@pytest.mark.parametrize("m,n,k,pin", [(1, 4096, 4096, False), (3, 272, 1152, False), (3, 272, 1152, True),
+                                       (16, 1040, 8320, False)])
+def test_8bit_weight_streaming(qdg, kind, m, n, k, pin):
     # M <= 16 through the weight-streaming family: one row, a ragged tile
-    # count with a short K, and K = 8320 (65 groups: more than one workgroup
-    # holds, so K is split at least in two)
+    # count with a short K (9 groups: the streaming family without a tuning,
+    # weight streaming when a tuning pins it), and K = 8320 (65 groups: more
+    # than one workgroup holds, so K is split at least in two)
     mk, std, ac, sa, y64, p = _any_case(kind, m, n, k, salt=50 + m)
     otypes = (q.QDG_O_F32, q.QDG_O_BF16) if kind == "mxfp4" else (q.QDG_O_I32, q.QDG_O_F32, q.QDG_O_BF16)
+    t = q.TuningConfig(waves=8) if pin else None
     for otype in otypes:
         layer = mk(otype)
-        fam = _family(layer, m)
+        fam = _family(layer, m, t)
         raw = otype == q.QDG_O_I32
-        assert fam == ("stream" if raw and k > 8192 else "wstream"), fam
+        ws = (pin or k // 128 >= 32) and not (raw and k > 8192)
+        assert fam == ("wstream" if ws else "stream"), fam
         pk = H.Packed(layer, *std)
-        y = H.gemm(layer, pk, H.dev(ac), m, a_scales=H.dev(sa))[0]
+        y = H.gemm(layer, pk, H.dev(ac), m, a_scales=H.dev(sa), tuning=t)[0]
         if raw:
             assert np.array_equal(y.cpu().numpy().astype(np.int64), p)
         else:
