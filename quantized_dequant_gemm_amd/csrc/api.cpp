@@ -391,7 +391,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   // M = 16 over tile counts 1, 2, 4 and K splits 1 to 8): one tile per
   // workgroup while the layer has at most 512 tiles, two beyond (W8A16,
   // whose unpack is VALU-heavy: four; 17.0 against 18.3 us at N = 14336), and no K
-  // split once that gives 256 workgroups (e.g. W4A4 (2048, 7168) 5.1 us
+  // split once that gives 128 workgroups (e.g. W4A4 (2048, 7168) 5.1 us
   // against 7.8 us for two tiles and two splits, W2A16 (4096, 4096) 7.2
   // against 8.9 us for two tiles and four splits): the split's extra
   // reduction launch costs more than the idle CUs
@@ -402,7 +402,7 @@ Choice choose_t(const qdg_plan& P, int64_t M, const qdg_tuning_config& T, bool h
   ch.grid_m = (int)((M + bm - 1) / bm);
   const int64_t nblocks = (g.ntiles + nt - 1) / nt;
   int split = has_tuning && T.split_k ? T.split_k : 0;
-  if (!split && few_rows && nblocks >= 256) split = 1;
+  if (!split && few_rows && nblocks >= 128) split = 1;
   if (!split) {
     const int64_t wgs = nblocks * (P.compute.batch_invariant ? 1 : ch.grid_m);
     split = (int)(kTargetWorkgroups / (wgs > 0 ? wgs : 1));
