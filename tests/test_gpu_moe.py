@@ -268,3 +268,28 @@ def test_moe_combine(qdg, t, otype):
     ref64 = ref.moe_combine(y, w, top_k)
     err = metrics.rel_frob(H.to_f64(out), ref64)
     assert err <= (1e-6 if otype == q.QDG_O_F32 else 2e-3), err
+
+
+@pytest.mark.parametrize("bm", [16, 64])
+def test_moe_empty_batch(qdg, bm):
+    # T = 0: the sort yields no blocks (num_padded 0, every block entry -1,
+    # every slot the sentinel T*top_k = 0) and the grouped GEMM and the
+    # combine enqueue nothing (their outputs stay untouched)
+    E, top_k, hid, n = 16, 4, 1024, 512
+    sid, blk, npad, cap = _align_dev(np.zeros((0, top_k), np.int32), E, bm)
+    assert int(npad.item()) == 0
+    assert cap == q.qdg_moe_align_capacity(0, top_k, E, bm)
+    assert torch.all(blk == -1) and torch.all(sid == 0)
+    qs, ss = _experts(E, n, hid, salt=31)
+    layer, pk = _moe_packed(qs, ss, n, hid)
+    plan = q.qdg_plan_create(layer, q.moe(top_k))
+    ws, nbytes = H.workspace(plan, 0)
+    y = torch.full((4, n), 7.0, dtype=torch.bfloat16, device="cuda")
+    dummy = torch.zeros(8, dtype=torch.int16, device="cuda")
+    q.qdg_moe_gemm(plan, dummy.data_ptr(), None, pk.buf.data_ptr(), sid.data_ptr(), blk.data_ptr(),
+                   npad.data_ptr(), 0, bm, 0, y.data_ptr(), ws.data_ptr(), nbytes, q.current_stream())
+    w = torch.ones(4, dtype=torch.float32, device="cuda")
+    yf = torch.zeros((4, n), dtype=torch.float32, device="cuda")
+    q.qdg_moe_combine(yf.data_ptr(), w.data_ptr(), 0, top_k, n, y.data_ptr(), q.QDG_O_BF16, q.current_stream())
+    torch.cuda.synchronize()
+    assert torch.all(y.float() == 7.0)
