@@ -37,61 +37,38 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Row sums of A per 128-wide K group, times `factor`:
 // out[g * m_pad + r] = factor * sum_k A[row(r)][128g + k], row(r) = r (dense;
-// rows >= M give 0) or the gathered MoE row. A workgroup of 256 lanes takes
-// R rows x 16 groups: sixteen lanes per (row, group) pair, 16 bytes each,
-// so a wave reads 1 KiB of contiguous A (four consecutive groups of one
-// row), with the R rows' loads in flight together; the 16 partial sums of a
-// pair meet by lane shuffles. With R = 16 the 16 x 16 sums leave through LDS
-// so that each group's 16 rows are one 64-byte store (large M, where the
-// 4-byte stores of R = 1 cost a fifth of the pass); R = 1 keeps enough
-// workgroups in flight for small M.
-template <int R>
-__global__ __launch_bounds__(256) void rowsum_kernel(const uint16_t* __restrict__ A, const int* __restrict__ sorted_ids,
-                                                     const int* __restrict__ num_padded, int top_k, int a_per_pair,
-                                                     int num_pairs, int M, int K, int m_pad, float factor,
-                                                     float* __restrict__ out) {
-  __shared__ float sums[16][17];
+// rows >= M give 0) or the gathered MoE row. Sixteen lanes take one
+// (row, group) pair, 16 bytes each, so a wave reads 1 KiB of contiguous A
+// (four consecutive groups of one row); the 16 partial sums meet by lane
+// shuffles.
+__global__ void rowsum_kernel(const uint16_t* __restrict__ A, const int* __restrict__ sorted_ids,
+                              const int* __restrict__ num_padded, int top_k, int a_per_pair, int num_pairs,
+                              int M, int K, int m_pad, float factor, float* __restrict__ out) {
   const int groups = K / 128;
-  const int gblocks = (groups + 15) / 16;
-  const int r0 = (int)(blockIdx.x / gblocks) * R, g0 = (int)(blockIdx.x % gblocks) * 16;
-  const int t = threadIdx.x, sub = t & 15, gl = t >> 4;  // lane of the pair, group of the block
-  const int g = g0 + gl;
-  u32x4_t x[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int r = r0 + i;
-    int src = r;
-    bool v = r < M;
-    if (sorted_ids) {
-      v = r < *num_padded;
-      const int id = v ? sorted_ids[r] : num_pairs;
-      v = id < num_pairs;
-      src = v ? (a_per_pair ? id : id / top_k) : 0;
-    }
-    x[i] = v && g < groups ? *(const u32x4_t*)(A + (size_t)src * K + (size_t)g * 128 + sub * 8)
-                           : u32x4_t{0u, 0u, 0u, 0u};
+  const int64_t pair = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  if (pair >= (int64_t)m_pad * groups) return;  // whole 16-lane groups
+  const int r = (int)(pair / groups), g = (int)(pair % groups);
+  int src = r;
+  bool v = r < M;
+  if (sorted_ids) {
+    v = r < *num_padded;
+    const int id = v ? sorted_ids[r] : num_pairs;
+    v = id < num_pairs;
+    src = v ? (a_per_pair ? id : id / top_k) : 0;
   }
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    float s = 0.f;
+  float s = 0.f;
+  if (v) {
+    const u32x4_t x = *(const u32x4_t*)(A + (size_t)src * K + (size_t)g * 128 + sub * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      s += __builtin_bit_cast(float, (uint32_t)(x[i][j] << 16));
-      s += __builtin_bit_cast(float, (uint32_t)(x[i][j] & 0xFFFF0000u));
+      s += __builtin_bit_cast(float, (uint32_t)(x[j] << 16));
+      s += __builtin_bit_cast(float, (uint32_t)(x[j] & 0xFFFF0000u));
     }
+  }
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
-    if constexpr (R == 1) {
-      if (sub == 0 && g < groups) out[(size_t)g * m_pad + r0] = s * factor;
-    } else {
-      if (sub == 0) sums[gl][i] = s * factor;
-    }
-  }
-  if constexpr (R > 1) {
-    __syncthreads();
-    const int wg = t >> 4, wr = t & 15;  // group and row of the store
-    if (g0 + wg < groups && wr < R) out[(size_t)(g0 + wg) * m_pad + r0 + wr] = sums[wg][wr];
-  }
+  for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
+  if (sub == 0) out[(size_t)g * m_pad + r] = s * factor;
 }
 
 // Sum of the split-K partials in split order (deterministic), converted to
@@ -887,13 +864,8 @@ hipError_t launch_reduce_splits(const GemmArgs& a, int m_pad, int n_pad, hipStre
 hipError_t launch_rowsum(const void* a_bf16, const int* sorted_ids, const int* num_padded, int top_k,
                          int a_per_pair, int num_pairs, int M, int K, int m_pad, float factor, float* out,
                          hipStream_t s) {
-  // one workgroup per 16 rows x 16 groups (m_pad is a multiple of 16) when
-  // that still gives 1024 workgroups, else per row x 16 groups (measured on
-  // MI355X: M = 8192, K = 14336 47 -> 38 us; M = 128 3.6 against 6.1 us)
-  const int64_t gblocks = (K / 128 + 15) / 16;
-  const bool wide = (int64_t)(m_pad / 16) * gblocks >= 1024;
-  const int64_t blocks = (int64_t)(wide ? m_pad / 16 : m_pad) * gblocks;
-  hipLaunchKernelGGL(wide ? rowsum_kernel<16> : rowsum_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s,
+  const int64_t threads = (int64_t)m_pad * (K / 128) * 16;  // 16 lanes per (row, group)
+  hipLaunchKernelGGL(rowsum_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                      (const uint16_t*)a_bf16, sorted_ids, num_padded, top_k, a_per_pair, num_pairs, M, K, m_pad,
                      factor, out);
   return hipGetLastError();
