@@ -806,12 +806,14 @@ hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStrea
 // wave tiles (one wave per SIMD, half the unpack work per MFMA), (64, 512, 8)
 // for dense M of 33 to 64 (measured on MI355X at M = 40 to 64: 27-29 us
 // against 31-32 us for one partly filled 128-row block, both shapes) and, for
-// grouped MoE blocks of 32 rows, (32, 512, 8) with 32 x 64 wave tiles (one
-// workgroup per CU with three stages; measured on MI355X at E = 256, hidden
-// 7168, T = 512: 7 % faster than (32, 256, 4) with two stages and two
-// workgroups per CU), and of 64 rows, (64, 512, 8) with 64 x 64 wave tiles
-// and two stages (at T = 4096: 14-19 % faster than 128-row blocks, whose
-// padding wastes more rows; (64, 256, 4) was slower).
+// grouped MoE blocks of 16 rows, (16, 512, 8) with 16 x 64 wave tiles (short
+// K: at T = 64, K = 2048, 321 us against 380 us in the streaming family), of
+// 32 rows, (32, 512, 8) with 32 x 64 wave tiles (one workgroup per CU with
+// three stages; measured on MI355X at E = 256, hidden 7168, T = 512: 7 %
+// faster than (32, 256, 4) with two stages and two workgroups per CU), and
+// of 64 rows, (64, 512, 8) with 64 x 64 wave tiles and two stages (at
+// T = 4096: 11-13 % faster than 128-row blocks, whose padding wastes more
+// rows; (64, 256, 4) was slower).
 bool tile_cfg_supported(Format f, const TileCfg& c) {
   if (f == FMT_NVFP4 || f == FMT_W8A16 || f == FMT_W2A16) return c.bm == 128 && c.bn == 256 && c.waves == 8;
   if (f != FMT_W4A16) return false;
