@@ -312,3 +312,35 @@ def test_tuned_split_never_exceeds_the_k_groups():
     for layer, tun, m, fam in cases:
         d = q.qdg_plan_describe(q.qdg_plan_create(layer, q.dense(), tun), m)
         assert fam in d and "split_k=8 " in d, d
+
+
+def test_moe_16_row_tile_tuning():
+    # block_n 512 names the 16 x 512 tiles of grouped W4A16 16-row blocks;
+    # without a tuning they serve K <= 2048 (16 groups), the streaming family
+    # longer K; other formats and dense plans reject the tuning
+    big = q.layer_w4a16(4096, 7168, num_experts=256)
+    short = q.layer_w4a16(7168, 2048, num_experts=256)
+    t16 = q.TuningConfig(block_m=16, block_n=512, waves=8)
+    assert "family=tile block_m=16 block_n=512" in q.qdg_moe_describe(q.qdg_plan_create(big, q.moe(8), t16), 64, 16)
+    assert "family=stream block_m=16" in q.qdg_moe_describe(q.qdg_plan_create(big, q.moe(8)), 64, 16)
+    assert "family=tile block_m=16 block_n=512" in q.qdg_moe_describe(q.qdg_plan_create(short, q.moe(8)), 64, 16)
+    pin = q.TuningConfig(block_n=64, waves=4)
+    assert "family=stream block_m=16" in q.qdg_moe_describe(q.qdg_plan_create(short, q.moe(8), pin), 64, 16)
+    assert _status(q.qdg_plan_create, q.layer_w8a8(4096, 7168, num_experts=8), q.moe(8), t16) == q.QDG_ERR_UNSUPPORTED
+    assert _status(q.qdg_plan_create, q.layer_w4a16(4096, 7168), q.dense(), t16) == q.QDG_ERR_UNSUPPORTED
+    assert _status(q.qdg_plan_create, big, q.moe(8), q.TuningConfig(block_n=512, waves=4)) == q.QDG_ERR_UNSUPPORTED
+
+
+def test_few_row_routing():
+    # W4A16 up to 8 rows where weight streaming would split K: streaming
+    # family; the 8-bit formats use weight streaming only for narrow layers
+    # with at least 32 K groups, else the streaming family with one tile per
+    # workgroup up to 512 tiles and no K split from 128 workgroups
+    d = lambda layer, m: q.qdg_plan_describe(q.qdg_plan_create(layer, q.dense()), m)  # noqa: E731
+    assert "family=stream block_m=16 block_n=32 split_k=4" in d(q.layer_w4a16(4096, 14336), 8)
+    assert "family=wstream" in d(q.layer_w4a16(4096, 14336), 9)
+    assert "family=wstream" in d(q.layer_w8a8(4096, 4096), 16)
+    assert "family=stream block_m=16 block_n=32 split_k=1" in d(q.layer_w8a8(14336, 4096), 16)
+    assert "family=stream block_m=16 block_n=16 split_k=1" in d(q.layer_mxfp4(7168, 2048), 16)
+    assert "family=wstream" in d(q.layer_mxfp4(2048, 7168), 16)
+    assert "family=stream block_m=16 block_n=64 split_k=1" in d(q.layer_w8a16(14336, 4096), 16)
