@@ -136,12 +136,20 @@ __global__ __launch_bounds__(256) void act_fp8_kernel(const uint16_t* __restrict
   const bool nz = amax > 0.f;
   const float inv = nz ? __fdiv_rn(448.0f, amax) : 0.f;
   if (sub == 0) scales[row * groups + g] = nz ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  // gfx950's v_cvt_pk_fp8_f32 encodes two binary32 values as OCP E4M3 with
+  // round to nearest even (subnormal codes included, the sign kept for
+  // values that round to zero); inputs are clamped to the largest finite
+  // magnitude first, so no code is NaN
   u32x2_t out = {0, 0};
   if (nz) {
+    float t[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float t = fminf(fmaxf(f[i] * inv, -448.f), 448.f);
-      out[i >> 2] |= e4m3_rne(t) << (8 * (i & 3));
+    for (int i = 0; i < 8; ++i) t[i] = fminf(fmaxf(f[i] * inv, -448.f), 448.f);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(t[4 * j], t[4 * j + 1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(t[4 * j + 2], t[4 * j + 3], w, true);
+      out[j] = (uint32_t)w;
     }
   }
   *(u32x2_t*)(q + row * K + g * 128 + sub * 8) = out;

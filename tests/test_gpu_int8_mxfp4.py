@@ -59,6 +59,37 @@ def test_act_quant_fp8_bit_exact(qdg, m, k):
     assert np.array_equal(sa_d.cpu().numpy().view(np.uint32), sa.view(np.uint32))
 
 
+def test_act_quant_fp8_every_bf16_magnitude(qdg):
+    # Every bf16 value of magnitude <= 448, both signs (subnormal and normal
+    # E4M3 codes, every tie between two codes, values that round to a signed
+    # zero): each 128-group also holds +-448, so its amax is 448, the inverse
+    # scale is exactly 1 and the codes are the E4M3 encoding of the inputs
+    # themselves, bit for bit as the oracle's encoder gives them.
+    pos = np.arange(0, 0x43E1, dtype=np.uint16)
+    vals = np.concatenate([pos, pos | np.uint16(0x8000)])
+    per = 127
+    ngroups = -(-vals.size // per)
+    ngroups = -(-ngroups // 8) * 8  # whole rows of 8 groups
+    grid = np.zeros((ngroups, 128), dtype=np.uint16)
+    grid[:, 0] = np.where(np.arange(ngroups) % 2 == 0, 0x43E0, 0xC3E0)  # +-448
+    flat = np.zeros(ngroups * per, dtype=np.uint16)
+    flat[: vals.size] = vals
+    grid[:, 1:] = flat.reshape(ngroups, per)
+    a = grid.reshape(ngroups // 8, 1024)
+    m, k = a.shape
+    codes, sa = quant.quantize_act_fp8(a)
+    assert np.all(sa.view(np.uint32) == np.float32(1.0).view(np.uint32))
+    layer = q.layer_mxfp4(16, k)
+    qa_d = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+    sa_d = torch.empty((m, k // 128), dtype=torch.float32, device="cuda")
+    q.qdg_quantize_act(layer, H.bf16_dev(a).data_ptr(), m, qa_d.data_ptr(), sa_d.data_ptr(), q.current_stream())
+    torch.cuda.synchronize()
+    got = qa_d.cpu().numpy()
+    bad = np.argwhere(got != codes)
+    assert bad.size == 0, [(hex(a[r, c]), hex(got[r, c]), hex(codes[r, c])) for r, c in bad[:8]]
+    assert np.array_equal(sa_d.cpu().numpy().view(np.uint32), sa.view(np.uint32))
+
+
 # ------------------------------------------------------------ W8A8
 
 
