@@ -122,10 +122,14 @@ def test_nvfp4_decode_layer_shape(qdg):
     assert err <= 2e-3, err
 
 
-@pytest.mark.parametrize("per_pair,bm", [(0, 16), (1, 32), (0, 128), (1, 128)])
-def test_nvfp4_moe(qdg, per_pair, bm):
-    E, top_k, t = 4, 2, 40
-    n, k = 96, 256
+# The larger cases give every expert several blocks (about 200 pairs each),
+# two N blocks of the 256-column tiles (the second partly filled) and eight K
+# groups, so the tiled instance runs its steady-state copy ring.
+@pytest.mark.parametrize("per_pair,bm,t,n,k", [(0, 16, 40, 96, 256), (1, 32, 40, 96, 256), (0, 128, 40, 96, 256),
+                                               (1, 128, 40, 96, 256), (0, 128, 400, 384, 1024),
+                                               (1, 128, 400, 384, 1024), (1, 64, 400, 384, 1024)])
+def test_nvfp4_moe(qdg, per_pair, bm, t, n, k):
+    E, top_k = 4, 2
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=5 + per_pair), top_k)
     qs = [quant.quantize_nvfp4(synth.weights_f32(n, k, workload_id=10, salt=700 + e)) for e in range(E)]
     rows_in = t * top_k if per_pair else t

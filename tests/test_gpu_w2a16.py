@@ -105,9 +105,10 @@ def test_w2a16_zero_point_flag(qdg):
     assert int(st.item()) == q.QDG_FLAG_BAD_ZERO_POINT
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
-def test_w2a16_moe(qdg, bm):
-    E, top_k, t, hid, n = 4, 2, 70, 512, 192
+@pytest.mark.parametrize("bm,t,hid,n", [(16, 70, 512, 192), (32, 70, 512, 192), (64, 70, 512, 192),
+                                        (128, 70, 512, 192), (128, 400, 1024, 384)])
+def test_w2a16_moe(qdg, bm, t, hid, n):
+    E, top_k = 4, 2
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=bm + 40), top_k)
     data = [_data(n, hid, salt=200 + e) for e in range(E)]
     layer = q.layer_w2a16(n, hid, otype=q.QDG_O_F32, num_experts=E)

@@ -79,10 +79,13 @@ def test_w8a16_split_k(qdg, split):
     assert metrics.rel_frob(H.to_f64(y), ref.gemm_w8a16(a, qw, sw)) <= 5e-5
 
 
-@pytest.mark.parametrize("bm", [16, 128])
-def test_w8a16_moe(qdg, bm):
-    E, top_k, t = 4, 2, 40
-    n, k = 96, 256
+# The larger cases give every expert several blocks (about 200 pairs each),
+# two N blocks of the 256-column tiles (the second partly filled) and eight K
+# groups, so the tiled instance runs its steady-state copy ring.
+@pytest.mark.parametrize("bm,t,n,k", [(16, 40, 96, 256), (128, 40, 96, 256), (128, 400, 384, 1024),
+                                      (32, 400, 384, 1024)])
+def test_w8a16_moe(qdg, bm, t, n, k):
+    E, top_k = 4, 2
     ids, _ = ref.route_topk(synth.router_logits(t, E, salt=5), top_k)
     qs = [quant.quantize_int8_per_channel(synth.weights_f32(n, k, workload_id=9, salt=700 + e)) for e in range(E)]
     a = synth.activations_bf16_bits(t, k, workload_id=9, salt=77)
