@@ -159,18 +159,11 @@ __global__ __launch_bounds__(256) void act_fp8_kernel(const uint16_t* __restrict
 
 namespace {
 
-// E4M3 code of an integer n with |n| <= 16 (exact: at most 4 significant
-// bits); sign bit 0x80 for negative n.
-__device__ __forceinline__ uint32_t small_int_e4m3(int n) {
-  const uint32_t a = (uint32_t)(n < 0 ? -n : n);
-  if (a == 0) return 0;
-  const int e = 31 - __builtin_clz(a);                    // floor(log2 a), 0..4
-  const uint32_t man = ((a << (3 - (e < 3 ? e : 3))) >> (e > 3 ? e - 3 : 0)) & 7u;  // 3 mantissa bits
-  return (n < 0 ? 0x80u : 0u) | ((uint32_t)(e + 7) << 3) | man;
-}
-
 // int8 activation codes -> two E4M3 planes, q = 16 * hi + lo with
 // hi = q >> 4 in [-8, 7] and lo = q & 15 in [0, 15]: one thread per 16 codes.
+// Both halves are integers that E4M3 holds exactly (at most 4 significant
+// bits), so gfx950's v_cvt_pk_fp8_f32 (OCP E4M3, two values per
+// instruction) encodes them without rounding.
 __global__ __launch_bounds__(256) void act_i8_planes_kernel(const int8_t* __restrict__ qa, int64_t rows, int64_t K,
                                                           uint8_t* __restrict__ planes) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 16-code chunk
@@ -178,12 +171,22 @@ __global__ __launch_bounds__(256) void act_i8_planes_kernel(const int8_t* __rest
   if (q >= rows * per_row) return;
   const int64_t r = q / per_row, k0 = (q % per_row) * 16;
   const u32x4_t v = *(const u32x4_t*)(qa + r * K + k0);
-  u32x4_t hi = {0, 0, 0, 0}, lo = {0, 0, 0, 0};
+  u32x4_t hi, lo;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int code = (int)(int8_t)(v[j / 4] >> (8 * (j % 4)));
-    hi[j / 4] |= small_int_e4m3(code >> 4) << (8 * (j % 4));
-    lo[j / 4] |= small_int_e4m3(code & 15) << (8 * (j % 4));
+  for (int d = 0; d < 4; ++d) {
+    float h[4], l[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int code = (int)(int8_t)(v[d] >> (8 * b));
+      h[b] = (float)(code >> 4);
+      l[b] = (float)(code & 15);
+    }
+    int wh = __builtin_amdgcn_cvt_pk_fp8_f32(h[0], h[1], 0, false);
+    wh = __builtin_amdgcn_cvt_pk_fp8_f32(h[2], h[3], wh, true);
+    int wl = __builtin_amdgcn_cvt_pk_fp8_f32(l[0], l[1], 0, false);
+    wl = __builtin_amdgcn_cvt_pk_fp8_f32(l[2], l[3], wl, true);
+    hi[d] = (uint32_t)wh;
+    lo[d] = (uint32_t)wl;
   }
   uint8_t* row = planes + r * 2 * K + (k0 / 128) * 256 + (k0 % 128);
   *(u32x4_t*)row = hi;

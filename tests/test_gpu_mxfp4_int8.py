@@ -51,22 +51,26 @@ def test_mxfp4_int8_parity(qdg, m, n, k):
 
 @pytest.mark.parametrize("m", [16, 64, 128])
 def test_mxfp4_int8_one_hot_extreme_codes(qdg, m):
-    # a single code per row, -128, 127 or a small value, at a different k per
-    # row, unit token scale: each output row is code * (dequantized weights)
-    # at that k, exact in fp32 (the hi/lo split of -128 is -8 * 16 + 0)
+    # a single code per row at a different k per row, unit token scale: each
+    # output row is code * (dequantized weights) at that k, exact in fp32;
+    # over the calls every int8 code -128 .. 127 appears (the hi/lo split of
+    # -128 is -8 * 16 + 0, of 127 is 7 * 16 + 15)
     k, n = 384, 80
     codes, e = _weights(n, k, salt=7)
     w64 = ref.dequant_mxfp4(codes, e)
-    vals = np.array([-128, 127, 1, -1, 15, -16, 17, 100])
+    vals = np.arange(-128, 128)
     layer, pk = _packed(n, k, codes, e, q.QDG_O_F32)
+    seen = set()
     for base in range(0, k, m):
         ks = np.arange(base, base + m) % k
         qa = np.zeros((m, k), np.int8)
-        v = vals[np.arange(m) % len(vals)]
+        v = vals[(np.arange(m) + base) % len(vals)]
+        seen.update(v[: min(m, k - base)].tolist())
         qa[np.arange(m), ks] = v
         y = H.gemm(layer, pk, H.dev(qa), m, a_scales=H.dev(np.ones(m, np.float32)))[0]
         want = v[:, None].astype(np.float64) * w64[:, ks].T
         assert np.array_equal(H.to_f64(y)[: min(m, k - base)], want[: min(m, k - base)])
+    assert seen == set(range(-128, 128))
 
 
 def test_mxfp4_int8_device_quantizer_pipeline(qdg):
