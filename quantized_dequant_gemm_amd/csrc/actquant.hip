@@ -10,7 +10,11 @@
 //                                     X = floor(log2(amax)) - 2, q = e2m1_rne_sat(x / 2^X)
 // Scale = f32(amax/Q); amax = 0 gives scale 1 and zero codes. Every step is
 // binary32 with RNE and correctly rounded division, so the codes are
-// reproducible bit for bit by any implementation doing the same steps.
+// reproducible bit for bit by any implementation doing the same steps. The
+// E4M3 and E2M1 encodes run on gfx950's conversion instructions
+// (v_cvt_pk_fp8_f32, v_cvt_scalef32_pk_fp4_f32: round to nearest even, the
+// sign kept on zero); the tests compare them with the oracle's encoders over
+// every bf16 input magnitude the encodes can see.
 #include "qdg_device.h"
 #include "qdg_internal.h"
 
@@ -19,24 +23,6 @@ namespace {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
 
-
-// OCP E2M1 code of a real, round to nearest with ties to the even code,
-// saturating at 6 (the largest finite value): magnitudes 0, 0.5, 1, 1.5, 2,
-// 3, 4, 6 are codes 0..7, the sign is bit 3 (also for values that round to 0).
-__device__ __forceinline__ uint32_t e2m1_rne_sat(float v) {
-  const uint32_t sign = __builtin_signbit(v) ? 8u : 0u;
-  const float a = fabsf(v);
-  uint32_t c;
-  if (a <= 0.25f) c = 0;        // tie 0.25 -> 0
-  else if (a < 0.75f) c = 1;    // tie 0.75 -> 1.0
-  else if (a <= 1.25f) c = 2;   // tie 1.25 -> 1.0
-  else if (a < 1.75f) c = 3;    // tie 1.75 -> 2.0
-  else if (a <= 2.5f) c = 4;    // tie 2.5 -> 2.0
-  else if (a < 3.5f) c = 5;     // tie 3.5 -> 4.0
-  else if (a <= 5.0f) c = 6;    // tie 5 -> 4.0
-  else c = 7;
-  return c | sign;
-}
 
 // MXFP4 per (token, 32-block): four lanes per block, 8 values (16 bytes) each;
 // the block's amax comes from a 4-lane reduction. X is read from the
@@ -68,8 +54,14 @@ __global__ __launch_bounds__(256) void act_fp4_kernel(const uint16_t* __restrict
     X = X < -127 ? -127 : X;
     e8 = (uint32_t)(X + 127);
     const float inv = __builtin_bit_cast(float, (uint32_t)(127 - X) << 23);  // 2^-X, X in [-127, 125]
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out |= e2m1_rne_sat(f[i] * inv) << (4 * i);
+    // gfx950's v_cvt_scalef32_pk_fp4_f32 encodes two binary32 values as
+    // E2M1 with round to nearest even and saturation at +-6 (sign kept for
+    // values that round to zero); with scale 1 it encodes x / 2^X itself,
+    // element 2j in the low nibble of byte j
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[0] * inv, f[1] * inv, 1.0f, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[2] * inv, f[3] * inv, 1.0f, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[4] * inv, f[5] * inv, 1.0f, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, f[6] * inv, f[7] * inv, 1.0f, 3);
   }
   *(uint32_t*)(q + b * 16 + sub * 4) = out;
   if (sub == 0) scales[b] = (uint8_t)e8;

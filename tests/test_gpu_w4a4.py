@@ -40,6 +40,34 @@ def test_act_mxfp4_bit_exact(qdg, m, k):
     assert np.array_equal(qa.cpu().numpy(), codecs.pack_nibbles(codes))
 
 
+def test_act_mxfp4_every_bf16_magnitude(qdg):
+    # Every bf16 value of magnitude <= 7.9375, both signs (every E2M1 tie,
+    # saturation above 6, signed zeros, bf16 subnormals): each 32-block also
+    # holds +-7.9375, so its shared exponent is X = floor(log2 7.9375) - 2 = 0
+    # and the codes are the E2M1 encoding of the inputs themselves, bit for
+    # bit as the oracle's encoder gives them.
+    pos = np.arange(0, 0x40FF, dtype=np.uint16)
+    vals = np.concatenate([pos, pos | np.uint16(0x8000)])
+    per = 31
+    nblk = -(-vals.size // per)
+    nblk = -(-nblk // 8) * 8  # whole rows of 8 blocks
+    grid = np.zeros((nblk, 32), dtype=np.uint16)
+    grid[:, 0] = np.where(np.arange(nblk) % 2 == 0, 0x40FE, 0xC0FE)  # +-7.9375
+    flat = np.zeros(nblk * per, dtype=np.uint16)
+    flat[: vals.size] = vals
+    grid[:, 1:] = flat.reshape(nblk, per)
+    a = grid.reshape(nblk // 8, 256)
+    m, k = a.shape
+    codes, e = quant.quantize_act_mxfp4(a)
+    assert np.all(e == 127)
+    qa, sa = _act_fp4_dev(a, m, k)
+    assert np.array_equal(sa.cpu().numpy(), e)
+    got = qa.cpu().numpy()
+    want = codecs.pack_nibbles(codes)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, [(hex(a[r, 2 * c]), hex(a[r, 2 * c + 1]), hex(got[r, c]), hex(want[r, c])) for r, c in bad[:8]]
+
+
 def _w4a4_case(m, n, k, otype, salt):
     w = synth.weights_f32(n, k, workload_id=8, salt=salt)
     wc, we = quant.quantize_mxfp4(w)
