@@ -286,18 +286,31 @@ __device__ __forceinline__ void tile_group32(const char* st, int a_lane, int w_l
 #pragma unroll
       for (int i = 0; i < 16; ++i) pacc[rb][cb][i] = ASYM ? negz[cb] * r[i / 4][i % 4] : r[i / 4][i % 4];
   }
+  // the A fragments of four steps are read together before their MFMAs (the
+  // reads complete in order, so each MFMA waits only for its own): left to
+  // itself the scheduler reads each step's fragment of the second row block
+  // into the same registers right before its MFMAs, exposing one LDS
+  // latency per step (all eight steps at once would need more registers
+  // than two waves per SIMD have)
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    u32x4_t a[2], b[2];
+  for (int hs = 0; hs < 2; ++hs) {
+    u32x4_t a[4][2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-      a[rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + (s / 4) * 128 + (s % 4) * 16);
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) b[cb] = unpack_u4_bf16_offset128(bp[cb][s / 4][s % 4], um, ue);
+      for (int rb = 0; rb < 2; ++rb)
+        a[s][rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + hs * 128 + s * 16);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t b[2];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) pacc[rb][cb] = mfma_bf16_32(a[rb], b[cb], pacc[rb][cb]);
+      for (int cb = 0; cb < 2; ++cb) b[cb] = unpack_u4_bf16_offset128(bp[cb][hs][s], um, ue);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) pacc[rb][cb] = mfma_bf16_32(a[s][rb], b[cb], pacc[rb][cb]);
+    }
   }
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
