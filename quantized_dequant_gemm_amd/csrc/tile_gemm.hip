@@ -351,22 +351,31 @@ __device__ __forceinline__ void tile_group32_w2(const char* st, int a_lane, int 
 #pragma unroll
       for (int i = 0; i < 16; ++i) pacc[rb][cb][i] = negz[cb] * r[i / 4][i % 4];
   }
+  // A fragments of four steps read together before their MFMAs (as in
+  // tile_group32)
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    u32x4_t a[2], b[2];
+  for (int hs = 0; hs < 2; ++hs) {
+    u32x4_t a[4][2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-      a[rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + (s / 4) * 128 + (s % 4) * 16);
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const uint32_t x = bp[cb][s / 4][(s % 4) / 2];
+      for (int rb = 0; rb < 2; ++rb)
+        a[s][rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + hs * 128 + s * 16);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) b[cb][m] = ((x >> (8 * (s % 2) + 2 * m)) & um) | ue;
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t b[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const uint32_t x = bp[cb][hs][s / 2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) b[cb][m] = ((x >> (8 * (s % 2) + 2 * m)) & um) | ue;
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) pacc[rb][cb] = mfma_bf16_32(a[s][rb], b[cb], pacc[rb][cb]);
     }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) pacc[rb][cb] = mfma_bf16_32(a[rb], b[cb], pacc[rb][cb]);
   }
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -396,19 +405,28 @@ __device__ __forceinline__ void tile_group32_nv(const char* st, int a_lane, int 
       bp[cb][q] = *(const u32x4_t*)(st + w_lane + cb * 2048 + q * 512);
       rec[cb][q] = *(const uint16_t*)(st + sv_lane + cb * 256 + q * 64);
     }
+  // A fragments of four steps read together before their MFMAs (as in
+  // tile_group32)
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    u32x4_t a[2], b[2];
+  for (int hs = 0; hs < 2; ++hs) {
+    u32x4_t a[4][2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-      a[rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + (s / 4) * 128 + (s % 4) * 16);
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-      b[cb] = e2m1x8_scaled_bf16(bp[cb][s / 4][s % 4], e4m3_to_f32((rec[cb][s / 4] >> (8 * ((s % 4) / 2))) & 0xFFu));
+      for (int rb = 0; rb < 2; ++rb)
+        a[s][rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + hs * 128 + s * 16);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t b[2];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma_bf16_32(a[rb], b[cb], acc[rb][cb]);
+      for (int cb = 0; cb < 2; ++cb)
+        b[cb] = e2m1x8_scaled_bf16(bp[cb][hs][s], e4m3_to_f32((rec[cb][hs] >> (8 * (s / 2))) & 0xFFu));
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma_bf16_32(a[s][rb], b[cb], acc[rb][cb]);
+    }
   }
 }
 
@@ -434,21 +452,35 @@ __device__ __forceinline__ void tile_group32_w8(const char* st, int a_lane, int 
 #pragma unroll
       for (int i = 0; i < 16; ++i) pacc[rb][cb][i] = r[i / 4][i % 4];
   }
+  // A fragments and weight chunks of four steps read together before their
+  // MFMAs (as in tile_group32)
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    u32x4_t a[2], b[2];
+  for (int hs = 0; hs < 2; ++hs) {
+    u32x4_t a[4][2], ch[2][2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-      a[rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + (s / 4) * 128 + (s % 4) * 16);
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const u32x4_t ch = *(const u32x4_t*)(st + w8_lane + cb * 2 * 2048 + (s / 4) * 512 + ((s % 4) / 2) * 1024);
-      b[cb] = i8x8_bf16_offset128(s % 2 ? ch.z : ch.x, s % 2 ? ch.w : ch.y);
+      for (int rb = 0; rb < 2; ++rb)
+        a[s][rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + hs * 128 + s * 16);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        ch[cb][j] = *(const u32x4_t*)(st + w8_lane + cb * 2 * 2048 + hs * 512 + j * 1024);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t b[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const u32x4_t c4 = ch[cb][s / 2];
+        b[cb] = i8x8_bf16_offset128(s % 2 ? c4.z : c4.x, s % 2 ? c4.w : c4.y);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) pacc[rb][cb] = mfma_bf16_32(a[s][rb], b[cb], pacc[rb][cb]);
     }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) pacc[rb][cb] = mfma_bf16_32(a[rb], b[cb], pacc[rb][cb]);
   }
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
