@@ -29,6 +29,23 @@ def to_f64(t):
     return t.cpu().numpy().astype(np.float64)
 
 
+def assert_elementwise(y, y64):
+    """Per-element bound beside the Frobenius one, for every compared output:
+    |y - y64| <= 2^-8 |y64| + 2^-10 rms(row of y64). Rounding an fp32 result
+    to bf16 (RNE) moves it by at most 2^-9 of itself, so the first term holds
+    the output rounding with a factor 2 to spare (for fp32 outputs it only
+    loosens the bound); the second holds the fp32 accumulation of the kernel,
+    which is orders of magnitude below it, while a wrong element (a dropped
+    group, a swapped column, a stale value) is off by about the row's rms."""
+    y = np.atleast_2d(to_f64(y) if isinstance(y, torch.Tensor) else np.asarray(y, np.float64))
+    y64 = np.atleast_2d(np.asarray(y64, np.float64))
+    assert y.shape == y64.shape, (y.shape, y64.shape)
+    rms = np.sqrt(np.mean(y64 * y64, axis=1, keepdims=True))
+    bound = 2.0 ** -8 * np.abs(y64) + 2.0 ** -10 * rms
+    bad = np.argwhere(~(np.abs(y - y64) <= bound))
+    assert bad.size == 0, [(int(r), int(c), y[r, c], y64[r, c], bound[r, c]) for r, c in bad[:6]]
+
+
 def workspace(plan, m):
     nbytes = q.qdg_plan_workspace(plan, m)
     return torch.zeros(nbytes, dtype=torch.uint8, device="cuda"), nbytes

@@ -86,6 +86,7 @@ def _run(fmt, m, n, k, rows):
         print(f"{fmt} M={m} K={k} N={n} otype={otype} ({d.split('split_k=')[1].split()[0]} splits): "
               f"rel_frob={err:.3e}")
         assert err <= tol, err
+        H.assert_elementwise(ys, y64)
 
 
 def _sampled(m, seed):
