@@ -516,6 +516,17 @@ def rows_leg(reps=30):
                 print(f"row moe-combine T={t}: {us:.2f} us", file=sys.stderr, flush=True)
                 out.append(dict(row="moe-combine", T=t, N=n, top_k=top_k, us=round(us, 3),
                                 gbs=round(by / us / 1e3, 1), hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4)))
+
+                # the same combine straight from the down projection's bf16 rows
+                def comb_b(i):
+                    q.qdg_moe_combine_bf16(y.data_ptr(), rw.data_ptr(), t, top_k, n, yo.data_ptr(), q.QDG_O_BF16,
+                                           sh)
+                comb_b(0)
+                us = _time_launches(comb_b, reps, stream)
+                by = t * top_k * (n * 2 + 4) + t * n * 2
+                print(f"row moe-combine-bf16 T={t}: {us:.2f} us", file=sys.stderr, flush=True)
+                out.append(dict(row="moe-combine-bf16", T=t, N=n, top_k=top_k, us=round(us, 3),
+                                gbs=round(by / us / 1e3, 1), hbm_frac=round(by / us / 1e3 / PEAK_HBM_GBS, 4)))
                 del y32, rw, yo
 
     # ---- grouped MoE W4A8-INT8 (the same experts; int8 activations per token

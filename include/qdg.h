@@ -488,6 +488,19 @@ qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scal
 qdg_status qdg_moe_combine(const float* y, const float* w, int64_t T, int32_t top_k, int64_t n, void* out,
                            int32_t otype, void* stream);
 
+/* The same combine over bf16 pair rows (a qdg_moe_gemm output with otype
+   BF16: half the bytes of the f32 rows, written once and read once): y:
+   bf16 [T*top_k][n], 8-byte aligned; each value is widened exactly to fp32
+   and the sum is the same fp32 chain in ascending j, so the result equals
+   qdg_moe_combine on the widened rows bit for bit. The pages leave the
+   precision of the MoE block's steps open; bf16 rows add one bf16 rounding
+   of every pair result (about 1.6e-3 relative rms), so against the
+   unrounded pair rows the combine stays within 2e-3 relative Frobenius
+   with otype F32, not with a second bf16 rounding of the output.
+   Arguments, alignment of w and out, and errors as for qdg_moe_combine. */
+qdg_status qdg_moe_combine_bf16(const void* y, const float* w, int64_t T, int32_t top_k, int64_t n, void* out,
+                                int32_t otype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

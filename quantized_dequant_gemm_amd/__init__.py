@@ -35,7 +35,7 @@ EXPORTS = (
     "qdg_version", "qdg_last_error", "qdg_validate_layer", "qdg_preprocess_query", "qdg_preprocess",
     "qdg_quantize_weights", "qdg_quantize_act", "qdg_plan_create", "qdg_plan_destroy", "qdg_plan_workspace",
     "qdg_plan_describe", "qdg_moe_describe", "qdg_gemm", "qdg_moe_align_capacity", "qdg_moe_align",
-    "qdg_moe_gemm", "qdg_moe_combine", "qdg_plan_autotune", "qdg_plan_autotune_reset",
+    "qdg_moe_gemm", "qdg_moe_combine", "qdg_moe_combine_bf16", "qdg_plan_autotune", "qdg_plan_autotune_reset",
     "qdg_plan_jit", "qdg_gemm_noalloc",
 )
 
@@ -100,6 +100,7 @@ def load():
         "qdg_moe_align": (I32, [P, I64, I32, I32, I32, P, P, P, P, P]),
         "qdg_moe_gemm": (I32, [P, P, P, P, P, P, P, I64, I32, I32, P, P, SZ, P]),
         "qdg_moe_combine": (I32, [P, P, I64, I32, I64, P, I32, P]),
+        "qdg_moe_combine_bf16": (I32, [P, P, I64, I32, I64, P, I32, P]),
         "qdg_plan_autotune": (I32, [P, P, P, P, P, I64, P, SZ, I32, P, P, P]),
         "qdg_plan_autotune_reset": (I32, [P]),
         "qdg_plan_jit": (I32, [P, I64, I32, ctypes.c_char_p, P]),
@@ -241,6 +242,10 @@ def qdg_moe_gemm(plan, A, a_scales, packed, sorted_ids, block_expert, num_padded
 
 def qdg_moe_combine(y, w, T, top_k, n, out, otype, stream=0):
     _check(load().qdg_moe_combine(y, w, T, top_k, n, out, otype, stream))
+
+
+def qdg_moe_combine_bf16(y, w, T, top_k, n, out, otype, stream=0):
+    _check(load().qdg_moe_combine_bf16(y, w, T, top_k, n, out, otype, stream))
 
 
 def qdg_plan_autotune(plan, A, a_scales, packed, Y, M, workspace, ws_bytes, reps=10, stream=0):

@@ -1210,16 +1210,28 @@ qdg_status qdg_moe_gemm(const qdg_plan* plan, const void* A, const float* a_scal
              block_expert, num_padded, T, block_m, a_per_pair ? 1 : 0);
 }
 
-qdg_status qdg_moe_combine(const float* y, const float* w, int64_t T, int32_t top_k, int64_t n, void* out,
-                           int32_t otype, void* stream) {
+static qdg_status moe_combine(const void* y, bool y_bf16, const float* w, int64_t T, int32_t top_k, int64_t n,
+                              void* out, int32_t otype, void* stream) {
   if (T < 0 || n < 1 || top_k < 1 || top_k > 32) return fail(QDG_ERR_INVALID_ARG, "bad T, n or top_k");
   if (otype != QDG_O_BF16 && otype != QDG_O_F32) return fail(QDG_ERR_INVALID_ARG, "otype must be BF16 or F32");
   if (n % 4 != 0) return fail(QDG_ERR_UNSUPPORTED, "n must be a multiple of 4");
   if (T == 0) return ok();
   if (!y || !w || !out) return fail(QDG_ERR_INVALID_ARG, "NULL pointer");
-  if (!aligned(y, 16) || !aligned(out, 16)) return fail(QDG_ERR_MISALIGNED, "y and out must be 16-byte aligned");
+  if (!aligned(y, y_bf16 ? 8 : 16) || !aligned(out, 16))
+    return fail(QDG_ERR_MISALIGNED, y_bf16 ? "y must be 8-byte and out 16-byte aligned" : "y and out must be 16-byte aligned");
   if (!aligned(w, 4)) return fail(QDG_ERR_MISALIGNED, "w must be 4-byte aligned");
-  return hip_status(launch_moe_combine(y, w, T, top_k, n, out, otype, (hipStream_t)stream), "moe_combine launch");
+  return hip_status(launch_moe_combine(y, y_bf16, w, T, top_k, n, out, otype, (hipStream_t)stream),
+                    "moe_combine launch");
+}
+
+qdg_status qdg_moe_combine(const float* y, const float* w, int64_t T, int32_t top_k, int64_t n, void* out,
+                           int32_t otype, void* stream) {
+  return moe_combine(y, false, w, T, top_k, n, out, otype, stream);
+}
+
+qdg_status qdg_moe_combine_bf16(const void* y, const float* w, int64_t T, int32_t top_k, int64_t n, void* out,
+                                int32_t otype, void* stream) {
+  return moe_combine(y, true, w, T, top_k, n, out, otype, stream);
 }
 
 }  // extern "C"

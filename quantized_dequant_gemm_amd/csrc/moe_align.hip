@@ -125,7 +125,11 @@ __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restri
 
 // Top-k weighted combine: one thread per (token, 4 columns). The top_k pair
 // rows of a token are added in ascending slot order (deterministic).
-__global__ void moe_combine_kernel(const float* __restrict__ y, const float* __restrict__ w, int64_t T,
+// y rows in fp32 (YB16 = false) or bf16 (YB16 = true, widened exactly to
+// fp32 before the multiply); the sum is the same fp32 FMA chain in ascending
+// j either way.
+template <bool YB16>
+__global__ void moe_combine_kernel(const void* __restrict__ yv, const float* __restrict__ w, int64_t T,
                                    int top_k, int64_t n, void* __restrict__ out, int otype) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_row = n / 4;
@@ -135,11 +139,22 @@ __global__ void moe_combine_kernel(const float* __restrict__ y, const float* __r
   for (int j = 0; j < top_k; ++j) {
     const int64_t r = t * top_k + j;
     const float wj = w[r];
-    const float4 v = *(const float4*)(y + r * n + c);
-    s[0] = __builtin_fmaf(wj, v.x, s[0]);
-    s[1] = __builtin_fmaf(wj, v.y, s[1]);
-    s[2] = __builtin_fmaf(wj, v.z, s[2]);
-    s[3] = __builtin_fmaf(wj, v.w, s[3]);
+    float v[4];
+    if constexpr (YB16) {
+      const uint2 h = *(const uint2*)((const uint16_t*)yv + r * n + c);
+      v[0] = __builtin_bit_cast(float, h.x << 16);
+      v[1] = __builtin_bit_cast(float, h.x & 0xFFFF0000u);
+      v[2] = __builtin_bit_cast(float, h.y << 16);
+      v[3] = __builtin_bit_cast(float, h.y & 0xFFFF0000u);
+    } else {
+      const float4 f = *(const float4*)((const float*)yv + r * n + c);
+      v[0] = f.x;
+      v[1] = f.y;
+      v[2] = f.z;
+      v[3] = f.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] = __builtin_fmaf(wj, v[e], s[e]);
   }
   if (otype == QDG_O_F32) {
     *(float4*)((float*)out + t * n + c) = make_float4(s[0], s[1], s[2], s[3]);
@@ -151,11 +166,14 @@ __global__ void moe_combine_kernel(const float* __restrict__ y, const float* __r
 
 }  // namespace
 
-hipError_t launch_moe_combine(const float* y, const float* w, int64_t T, int top_k, int64_t n, void* out,
-                              int otype, hipStream_t s) {
+hipError_t launch_moe_combine(const void* y, bool y_bf16, const float* w, int64_t T, int top_k, int64_t n,
+                              void* out, int otype, hipStream_t s) {
   const int64_t threads = T * (n / 4);
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, y, w, T,
-                     top_k, n, out, otype);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (y_bf16)
+    hipLaunchKernelGGL(moe_combine_kernel<true>, grid, dim3(256), 0, s, y, w, T, top_k, n, out, otype);
+  else
+    hipLaunchKernelGGL(moe_combine_kernel<false>, grid, dim3(256), 0, s, y, w, T, top_k, n, out, otype);
   return hipGetLastError();
 }
 

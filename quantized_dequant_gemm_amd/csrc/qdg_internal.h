@@ -110,8 +110,8 @@ hipError_t launch_quantize_act(int atype, const void* a, int64_t M, int64_t K, v
 // group g, bytes 256g .. 256g+127 hold hi = q >> 4 and 256g+128 .. 256g+255
 // hold lo = q & 15 of the group's K values (q = 16 hi + lo, both exact).
 hipError_t launch_act_i8_planes(const int8_t* qa, int64_t rows, int64_t K, uint8_t* planes, hipStream_t s);
-hipError_t launch_moe_combine(const float* y, const float* w, int64_t T, int top_k, int64_t n, void* out,
-                              int otype, hipStream_t s);
+hipError_t launch_moe_combine(const void* y, bool y_bf16, const float* w, int64_t T, int top_k, int64_t n,
+                              void* out, int otype, hipStream_t s);
 // Run-time compiled streaming-family instance (hipRTC): the loaded kernel,
 // or an error. from_cache: 0 compiled now, 1 code object read from the cache
 // directory, 2 already loaded in this process.

@@ -148,6 +148,11 @@ def test_epilogue_and_combine_validation():
     assert _status(q.qdg_moe_combine, 16, 16, 4, 8, 66, 16, q.QDG_O_BF16) == q.QDG_ERR_UNSUPPORTED
     assert _status(q.qdg_moe_combine, 16, 16, 4, 8, 64, 8, q.QDG_O_BF16) == q.QDG_ERR_MISALIGNED
     q.qdg_moe_combine(0, 0, 0, 8, 64, 0, q.QDG_O_BF16)  # T = 0 enqueues nothing
+    assert _status(q.qdg_moe_combine_bf16, 1, 1, 4, 8, 64, 1, q.QDG_O_I32) == q.QDG_ERR_INVALID_ARG
+    assert _status(q.qdg_moe_combine_bf16, 16, 16, 4, 8, 66, 16, q.QDG_O_BF16) == q.QDG_ERR_UNSUPPORTED
+    assert _status(q.qdg_moe_combine_bf16, 8, 16, 4, 8, 64, 8, q.QDG_O_BF16) == q.QDG_ERR_MISALIGNED
+    assert _status(q.qdg_moe_combine_bf16, 4, 16, 4, 8, 64, 16, q.QDG_O_BF16) == q.QDG_ERR_MISALIGNED
+    q.qdg_moe_combine_bf16(0, 0, 0, 8, 64, 0, q.QDG_O_BF16)  # T = 0 enqueues nothing
 
 
 def test_gemm_argument_errors_before_device_work():

@@ -271,6 +271,37 @@ def test_moe_combine(qdg, t, otype):
     assert err <= (1e-6 if otype == q.QDG_O_F32 else 2e-3), err
 
 
+@pytest.mark.parametrize("t", [64, 1000])
+def test_moe_combine_bf16_rows(qdg, t):
+    # bf16 pair rows: the same fp32 chain as the f32 combine on the widened
+    # rows (bit for bit), within 1e-6 / 2e-3 of the fp64 combine of the same
+    # rows, and within 2e-3 of the combine of the unrounded rows with f32
+    # output (the one bf16 rounding of the rows costs about 1.6e-3)
+    top_k, n = 8, 7168
+    r = np.random.default_rng(90 + t)
+    y64 = r.normal(size=(t * top_k, n))
+    yb = codecs.f32_to_bf16_bits(y64.astype(np.float32))
+    w = r.uniform(0.0, 0.5, t * top_k).astype(np.float32)
+    yb_dev, w_dev = H.bf16_dev(yb), H.dev(w)
+    yw_dev = H.dev(codecs.bf16_bits_to_f64(yb).astype(np.float32))
+    ref_same = ref.moe_combine(codecs.bf16_bits_to_f64(yb), w, top_k)
+    for otype in (q.QDG_O_F32, q.QDG_O_BF16):
+        out = H.out_tensor(t, n, otype)
+        q.qdg_moe_combine_bf16(yb_dev.data_ptr(), w_dev.data_ptr(), t, top_k, n, out.data_ptr(), otype,
+                               q.current_stream())
+        out32 = H.out_tensor(t, n, otype)
+        q.qdg_moe_combine(yw_dev.data_ptr(), w_dev.data_ptr(), t, top_k, n, out32.data_ptr(), otype,
+                          q.current_stream())
+        torch.cuda.synchronize()
+        assert torch.equal(out, out32)
+        err = metrics.rel_frob(H.to_f64(out), ref_same)
+        assert err <= (1e-6 if otype == q.QDG_O_F32 else 2e-3), err
+        if otype == q.QDG_O_F32:
+            e2e = metrics.rel_frob(H.to_f64(out), ref.moe_combine(y64, w, top_k))
+            print(f"combine of bf16 rows T={t}: {e2e:.3e} against the unrounded rows")
+            assert e2e <= 2e-3, e2e
+
+
 @pytest.mark.parametrize("bm", [16, 64])
 def test_moe_empty_batch(qdg, bm):
     # T = 0: the sort yields no blocks (num_padded 0, every block entry -1,
