@@ -14,7 +14,7 @@ step's time, `roofline_m16` the HBM-bound M=16 cases (also as a fraction of
 `cpu_baseline` the fp64 CPU oracle timed on a bounded sample of the same
 workload. The full record (`cases`: every launch of the step; `autotuned`:
 each case again with a plan tuned per M range next to the heuristic plan;
-`jit`: the hipRTC compile time of one streaming-family instance; `rows`: the
+`jit`: the hipRTC compile time of one instance of each W4A16 family; `rows`: the
 other hot-path rows at their own shapes) goes to the JSON file named by
 --detail (default gpurun_out/bench_detail.json), and one progress line per
 measurement goes to stderr.
@@ -250,31 +250,39 @@ def gpu_leg(args):
     # timed against the ahead-of-time instance (rotating weight copies)
     jit = None
     if args.jit:
+        # one instance of each W4A16 family compiled at run time (hipRTC):
+        # streaming (M = 32), weight streaming (M = 16), LDS-tiled (M = 1024);
+        # compile time, and the run-time compiled instance timed beside the
+        # ahead-of-time one
         import tempfile
         k, n = SHAPES[0]
-        m = 32
         layer, plan_h, bufs = layers[(k, n)]
-        plan_j = q.qdg_plan_create(layer, q.dense())
-        with tempfile.TemporaryDirectory() as cache:
-            info = q.qdg_plan_jit(plan_j, m, 0, cache)
-        a = synth.device_activations_bf16(m, k, seed=synth.seed_for(1, synth.TID_A, m))
-        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        wsb = q.qdg_plan_workspace(plan_h, m)
-        wsj = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
+        jit = []
+        for m in (32, 16, 1024):
+            plan_j = q.qdg_plan_create(layer, q.dense())
+            with tempfile.TemporaryDirectory() as cache:
+                info = q.qdg_plan_jit(plan_j, m, 0, cache)
+            a = synth.device_activations_bf16(m, k, seed=synth.seed_for(1, synth.TID_A, m))
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            wsb = q.qdg_plan_workspace(plan_h, m)
+            wsj = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
 
-        def run_j(i, plan):
-            q.qdg_gemm(plan, a.data_ptr(), None, bufs[i % len(bufs)].data_ptr(), y.data_ptr(), m, wsj.data_ptr(),
-                       wsb, sh)
-        run_j(0, plan_h)
-        run_j(0, plan_j)
-        us_aot = _time_launches(lambda i: run_j(i, plan_h), 60, stream)
-        us_jit = _time_launches(lambda i: run_j(i, plan_j), 60, stream)
-        jit = dict(M=m, K=k, N=n, compile_ms=round(info.compile_ms, 1), load_ms=round(info.load_ms, 2),
-                   code_bytes=info.code_bytes, us_aot=round(us_aot, 3), us_jit=round(us_jit, 3),
-                   instance=q.qdg_plan_describe(plan_j, m).split(": ", 1)[1],
-                   note="the pages' figure for compiling one W4A16 kernel: 1.82 s with NVCC (H200 host); context only")
-        print(f"jit M={m} K={k} N={n}: compile {info.compile_ms:.0f} ms, aot {us_aot:.2f} us, jit {us_jit:.2f} us",
-              file=sys.stderr, flush=True)
+            def run_j(i, plan, m=m, a=a, y=y, wsj=wsj, wsb=wsb):
+                q.qdg_gemm(plan, a.data_ptr(), None, bufs[i % len(bufs)].data_ptr(), y.data_ptr(), m,
+                           wsj.data_ptr(), wsb, sh)
+            run_j(0, plan_h)
+            run_j(0, plan_j)
+            reps = 60 if m <= 32 else 20
+            us_aot = _time_launches(lambda i: run_j(i, plan_h), reps, stream)
+            us_jit = _time_launches(lambda i: run_j(i, plan_j), reps, stream)
+            jit.append(dict(M=m, K=k, N=n, compile_ms=round(info.compile_ms, 1), load_ms=round(info.load_ms, 2),
+                            code_bytes=info.code_bytes, us_aot=round(us_aot, 3), us_jit=round(us_jit, 3),
+                            instance=q.qdg_plan_describe(plan_j, m).split(": ", 1)[1]))
+            print(f"jit M={m} K={k} N={n}: compile {info.compile_ms:.0f} ms, aot {us_aot:.2f} us, "
+                  f"jit {us_jit:.2f} us", file=sys.stderr, flush=True)
+            del a, y, wsj
+        jit.append(dict(note="the pages' figure for compiling one W4A16 kernel: 1.82 s with NVCC (H200 host); "
+                             "context only"))
     m16 = [d for d in out_cases if d["M"] == 16]
     roof16 = [dict(bound="hbm", achieved=d["gbs_stream"], peak=PEAK_HBM_GBS, unit="GB/s", frac=d["hbm_frac_stream"],
                    frac_of_copy=round(d["gbs_stream"] / copy_gbs, 4), kernel=f"w4a16 M=16 K={d['K']} N={d['N']}",

@@ -359,16 +359,19 @@ qdg_status qdg_gemm_noalloc(const qdg_plan* plan, const void* A, const float* a_
 /* Run-time compilation (the pages build each kernel instance at run time
    from its configuration: kinachrichten, "Kompilierzeiten und
    gerätespezifisches Tuning"; jetabc, "Humming 的做法", item 3). Compiles
-   with hipRTC the streaming-family instance that serves M rows of the plan
+   with hipRTC the main kernel of the instance that serves M rows of the plan
    (for a MoE plan: T = M tokens in block_m-row blocks; block_m is ignored
-   for dense plans), from the kernel source embedded in the library, loads
-   it on the current device, and makes the plan launch it for every call
-   that selects that instance ("code=jit" in the descriptions). With a
-   cache_dir (may be NULL) the code object is stored there, under a key of
-   the instance, the target, the options and the source text, and later
-   processes load it instead of compiling. Instances of the other families
-   return QDG_ERR_UNSUPPORTED; a compile or load failure QDG_ERR_HIP (with
-   the compiler log in qdg_last_error). Blocks while compiling. The plan is
+   for dense plans), whichever family it belongs to (streaming, weight
+   streaming, LDS-tiled, 8-bit LDS-tiled, 8-bit weight streaming), from that
+   family's kernel source embedded in the library, loads it on the current
+   device, and makes the plan launch it for every call that selects that
+   instance ("code=jit" in the descriptions); the small helper kernels of a
+   call (row sums, split reduce, activation planes) stay ahead of time. With
+   a cache_dir (may be NULL) the code object is stored there, under a key of
+   the kernel, the target, the options, the compiler version and the source
+   text, and later processes load it instead of compiling. QDG_ERR_UNSUPPORTED
+   when no instance serves M; a compile or load failure QDG_ERR_HIP (with the
+   compiler log in qdg_last_error). Blocks while compiling. The plan is
    modified: no other call may use it concurrently. */
 typedef struct qdg_jit_info {
   double compile_ms;  /* hipRTC compile time; 0 when no compile was needed */

@@ -108,9 +108,10 @@ constexpr int kAutoRanges = 32;
 // A run-time compiled streaming-family instance the plan launches instead of
 // the ahead-of-time one (qdg_plan_jit).
 struct JitInstance {
-  int mt, nt, kw, device;
+  int mt, nt, kw, device;  // streaming family: the instance's shape
   bool moe;
   hipFunction_t fn;
+  std::string expr;  // other families: the kernel's name expression (empty for streaming instances)
 };
 
 struct qdg_plan {
@@ -752,13 +753,68 @@ static const char* mfma_name(Format f, const Choice& c) {
   return "16x16x64_i8";
 }
 
-static const JitInstance* find_jit(const qdg_plan& plan, const Choice& c, bool moe) {
-  if (c.ws || c.tile || c.qtile || plan.jit.empty()) return nullptr;
+// The main kernel of a weight-streaming, LDS-tiled or 8-bit LDS-tiled
+// choice: launched, or (desc set) described without launching anything.
+static hipError_t family_launch(const qdg_plan& plan, const Choice& c, const GemmArgs& a, bool moe, hipStream_t s,
+                                KernelLaunch* desc) {
+  const bool asym = plan.layer.wtype == QDG_W_UINT4;
+  if (c.qtile) return launch_qtile(plan.fmt, moe, c.tc.bm, a, c.grid_m, s, desc);
+  if (c.tile) return launch_tile(plan.fmt, asym, moe, c.tc, a, c.grid_m, s, desc);
+  return plan.fmt == FMT_W4A16 ? launch_wstream(asym, moe, a, c.sc.split, c.grid_m, s, desc)
+                               : launch_wstream8(plan.fmt, a, c.sc.split, c.sc.nt, s, desc);
+}
+
+static const JitInstance* find_jit_expr(const qdg_plan& plan, const char* expr, bool moe) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   for (const JitInstance& j : plan.jit)
-    if (j.mt == c.sc.mt && j.nt == c.sc.nt && j.kw == c.sc.kw && j.moe == moe && j.device == dev) return &j;
+    if (!j.expr.empty() && j.expr == expr && j.moe == moe && j.device == dev) return &j;
   return nullptr;
+}
+
+// The size fields a launcher reads to pick its kernel and grid.
+static GemmArgs shape_args(const qdg_plan& plan, const Choice& c) {
+  GemmArgs a{};
+  a.N = (int)plan.layer.n;
+  a.K = (int)plan.layer.k;
+  a.groups = (int)plan.geom.groups;
+  a.ntiles = (int)plan.geom.ntiles;
+  a.otype = plan.layer.otype;
+  a.split = c.sc.split;
+  a.epi = plan.compute.epilogue;
+  return a;
+}
+
+static const JitInstance* find_jit(const qdg_plan& plan, const Choice& c, bool moe) {
+  if (plan.jit.empty()) return nullptr;
+  if (c.ws || c.tile || c.qtile) {
+    KernelLaunch d{};
+    if (family_launch(plan, c, shape_args(plan, c), moe, nullptr, &d) != hipSuccess) return nullptr;
+    return find_jit_expr(plan, d.expr, moe);
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  for (const JitInstance& j : plan.jit)
+    if (j.expr.empty() && j.mt == c.sc.mt && j.nt == c.sc.nt && j.kw == c.sc.kw && j.moe == moe && j.device == dev)
+      return &j;
+  return nullptr;
+}
+
+// The main kernel of a non-streaming choice from the plan's run-time
+// compiled instance when it has one (the weight-streaming split reduce
+// then follows here), else ahead of time.
+static hipError_t launch_main(const qdg_plan& plan, const Choice& c, const GemmArgs& a, bool moe, hipStream_t s) {
+  if (!plan.jit.empty()) {
+    KernelLaunch d{};
+    if (family_launch(plan, c, a, moe, s, &d) == hipSuccess) {
+      if (const JitInstance* j = find_jit_expr(plan, d.expr, moe)) {
+        hipError_t e = launch_jit(j->fn, d, a, s);
+        if (e == hipSuccess && c.ws && !moe && c.sc.split > 1) e = launch_reduce_splits(a, 16, a.ntiles * 16, s);
+        return e;
+      }
+    }
+  }
+  return family_launch(plan, c, a, moe, s, nullptr);
 }
 
 static int describe(const qdg_plan& plan, const Choice& c, int64_t M, const char* kind, char* buf, size_t len) {
@@ -842,7 +898,7 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
   }
   if (c.qtile) {
     a.m_pad = c.grid_m * c.tc.bm;
-    e = launch_qtile(plan->fmt, moe, c.tc.bm, a, c.grid_m, stream);
+    e = launch_main(*plan, c, a, moe, stream);
     if (e == hipSuccess && a.split > 1) {
       const int n_pad = (int)((plan->geom.ntiles + 15) / 16 * 256);
       e = launch_reduce_splits(a, a.m_pad, n_pad, stream);
@@ -862,14 +918,13 @@ static qdg_status run(const qdg_plan* plan, const void* A, const float* a_scales
               : launch_rowsum(A, nullptr, nullptr, 0, 0, (int)rows, (int)M, a.K, a.m_pad, rs_factor, rs,
                               stream);
     if (e != hipSuccess) return hip_status(e, "rowsum launch");
-    e = launch_tile(plan->fmt, asym, moe, c.tc, a, c.grid_m, stream);
+    e = launch_main(*plan, c, a, moe, stream);
     if (e == hipSuccess && a.split > 1) {
       const int n_pad = (int)((plan->geom.ntiles + c.tc.bn / 16 - 1) / (c.tc.bn / 16) * c.tc.bn);
       e = launch_reduce_splits(a, a.m_pad, n_pad, stream);
     }
   } else if (c.ws) {
-    e = plan->fmt == FMT_W4A16 ? launch_wstream(asym, moe, a, c.sc.split, c.grid_m, stream)
-                               : launch_wstream8(plan->fmt, a, c.sc.split, c.sc.nt, stream);
+    e = launch_main(*plan, c, a, moe, stream);
   } else {
     // the streaming family addresses A with 31-bit byte offsets
     const int64_t a_rows = moe ? (a_per_pair ? rows : T) : M;
@@ -1134,22 +1189,44 @@ qdg_status qdg_plan_jit(qdg_plan* plan, int64_t M, int32_t block_m, const char* 
   } else {
     c = choose(*plan, M);
   }
-  if (c.ws || c.tile || c.qtile || !stream_cfg_supported(plan->fmt, c.sc))
-    return fail(QDG_ERR_UNSUPPORTED, "run-time compilation covers the streaming family; this M runs %s",
-                c.qtile ? "the 8-bit LDS-tiled family" : c.tile ? "the LDS-tiled family" : "weight streaming");
+  int dev = 0;
+  if (c.ws || c.tile || c.qtile) {
+    // the instance the plan launches for this M, described by its launcher
+    KernelLaunch d{};
+    if (family_launch(*plan, c, shape_args(*plan, c), moe, nullptr, &d) != hipSuccess)
+      return fail(QDG_ERR_UNSUPPORTED, "no kernel instance for this M");
+    JitResult r = jit_kernel(d.src, d.expr, cache_dir);
+    if (!r.fn) return fail(QDG_ERR_HIP, "%s", r.error.c_str());
+    (void)hipGetDevice(&dev);
+    bool found = false;
+    for (JitInstance& j : plan->jit)
+      if (j.expr == d.expr && j.moe == moe && j.device == dev) {
+        j.fn = r.fn;
+        found = true;
+      }
+    if (!found) plan->jit.push_back(JitInstance{0, 0, 0, dev, moe, r.fn, std::string(d.expr)});
+    if (info) {
+      info->compile_ms = r.compile_ms;
+      info->load_ms = r.load_ms;
+      info->from_cache = r.from_cache;
+      info->code_bytes = r.code_bytes;
+      std::snprintf(info->key, sizeof info->key, "%s", r.key);
+    }
+    return ok();
+  }
+  if (!stream_cfg_supported(plan->fmt, c.sc)) return fail(QDG_ERR_UNSUPPORTED, "no streaming instance for this M");
   const bool asym = plan->layer.wtype == QDG_W_UINT4;
   const bool raw = plan->layer.otype == QDG_O_I32;
   JitResult r = jit_stream_kernel(plan->fmt, asym, raw, c.sc, moe, cache_dir);
   if (!r.fn) return fail(QDG_ERR_HIP, "%s", r.error.c_str());
-  int dev = 0;
   (void)hipGetDevice(&dev);
   bool found = false;
   for (JitInstance& j : plan->jit)
-    if (j.mt == c.sc.mt && j.nt == c.sc.nt && j.kw == c.sc.kw && j.moe == moe && j.device == dev) {
+    if (j.expr.empty() && j.mt == c.sc.mt && j.nt == c.sc.nt && j.kw == c.sc.kw && j.moe == moe && j.device == dev) {
       j.fn = r.fn;
       found = true;
     }
-  if (!found) plan->jit.push_back(JitInstance{c.sc.mt, c.sc.nt, c.sc.kw, dev, moe, r.fn});
+  if (!found) plan->jit.push_back(JitInstance{c.sc.mt, c.sc.nt, c.sc.kw, dev, moe, r.fn, std::string()});
   if (info) {
     info->compile_ms = r.compile_ms;
     info->load_ms = r.load_ms;

@@ -1,12 +1,12 @@
-// Run-time compilation (hipRTC) of streaming-family kernel instances.
+// Run-time compilation (hipRTC) of kernel instances of every family.
 //
 // The pages' library builds each kernel instance at run time from its
 // configuration and times that build against a template-heavy alternative
 // (kinachrichten, "Kompilierzeiten und gerätespezifisches Tuning"; jetabc,
 // "Humming 的做法", item 3). Here every instance is also compiled ahead of
-// time; qdg_plan_jit compiles one streaming-family instance at run time from
-// the same source text (embedded in the library when it is built), loads it,
-// and the plan then launches that code object. Compiled code objects can be
+// time; qdg_plan_jit compiles one instance at run time from the same source
+// text (each family's kernel file, embedded in the library when it is
+// built), loads it, and the plan then launches that code object. Compiled code objects can be
 // kept in a cache directory under a key derived from the instance, the
 // target, the compiler version and the source text, so a later process loads
 // instead of compiling. One cache entry is one file (a header line with the
@@ -25,7 +25,7 @@
 #include <vector>
 
 #include "qdg_internal.h"
-#include "jit_sources.inc"  // kJitStreamSrc, kJitDeviceHdr, kJitInternalHdr, kJitQdgHdr (generated at build)
+#include "jit_sources.inc"  // kJit*Src, kJitDeviceHdr, kJitInternalHdr, kJitQdgHdr (generated at build)
 
 namespace qdg {
 namespace {
@@ -114,15 +114,28 @@ bool parse_entry(const std::vector<char>& in, std::string* name, std::vector<cha
 }  // namespace
 
 JitResult jit_stream_kernel(Format f, bool asym, bool raw, const StreamCfg& c, bool moe, const char* cache_dir) {
-  JitResult r{};
   const char* pol = policy_name(f, asym, raw);
   if (!pol) {
+    JitResult r{};
     r.error = "no streaming policy for this format";
     return r;
   }
   char expr[256];
   std::snprintf(expr, sizeof expr, "qdg::stream_gemm_kernel<%s, %d, %d, %d, 2, %s>", pol, c.mt, c.nt, c.kw,
                 moe ? "true" : "false");
+  return jit_kernel(JIT_SRC_STREAM, expr, cache_dir);
+}
+
+JitResult jit_kernel(int src, const char* expr, const char* cache_dir) {
+  JitResult r{};
+  static const char* const kSrc[JIT_NSRC] = {kJitStreamSrc, kJitTileSrc, kJitWstreamSrc, kJitQtileSrc,
+                                             kJitWstream8Src};
+  static const char* const kSrcName[JIT_NSRC] = {"stream_gemm.hip", "tile_gemm.hip", "wstream_gemm.hip",
+                                                 "qtile_gemm.hip", "wstream8_gemm.hip"};
+  if (src < 0 || src >= JIT_NSRC) {
+    r.error = "no such kernel source";
+    return r;
+  }
   // identity: instance, target, compile options and the source text
   const char* opts[] = {"--offload-arch=gfx950", "-O3", "-std=c++17",
                         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"};
@@ -134,7 +147,7 @@ JitResult jit_stream_kernel(Format f, bool asym, bool raw, const StreamCfg& c, b
   char ver[32];
   std::snprintf(ver, sizeof ver, "hiprtc %d.%d", rtc_major, rtc_minor);
   h = fnv1a(ver, std::strlen(ver), h);
-  const char* texts[] = {kJitStreamSrc, kJitDeviceHdr, kJitInternalHdr, kJitQdgHdr};
+  const char* texts[] = {kSrc[src], kJitDeviceHdr, kJitInternalHdr, kJitQdgHdr};
   for (const char* t : texts) h = fnv1a(t, std::strlen(t), h);
   std::snprintf(r.key, sizeof r.key, "%016llx", (unsigned long long)h);
   int dev = 0;
@@ -160,7 +173,7 @@ JitResult jit_stream_kernel(Format f, bool asym, bool raw, const StreamCfg& c, b
     hiprtcProgram prog;
     const char* hdrs[] = {kJitDeviceHdr, kJitInternalHdr, kJitQdgHdr};
     const char* names[] = {"qdg_device.h", "qdg_internal.h", "qdg.h"};
-    if (hiprtcCreateProgram(&prog, kJitStreamSrc, "stream_gemm.hip", 3, hdrs, names) != HIPRTC_SUCCESS) {
+    if (hiprtcCreateProgram(&prog, kSrc[src], kSrcName[src], 3, hdrs, names) != HIPRTC_SUCCESS) {
       r.error = "hiprtcCreateProgram failed";
       return r;
     }
@@ -208,6 +221,15 @@ JitResult jit_stream_kernel(Format f, bool asym, bool raw, const StreamCfg& c, b
   g_loaded[id] = Loaded{mod, fn};
   r.fn = fn;
   return r;
+}
+
+hipError_t launch_jit(hipFunction_t fn, const KernelLaunch& d, const GemmArgs& a, hipStream_t s) {
+  GemmArgs arg = a;
+  int mb = d.m_blocks, nb = d.n_blocks;
+  void* with_mn[] = {&arg, &mb, &nb};
+  void* plain[] = {&arg};
+  return hipModuleLaunchKernel(fn, d.grid[0], d.grid[1], d.grid[2], d.block, 1, 1, 0, s, d.mn_args ? with_mn : plain,
+                               nullptr);
 }
 
 hipError_t launch_stream_jit(hipFunction_t fn, const StreamCfg& c, const GemmArgs& a, int grid_m, hipStream_t s) {

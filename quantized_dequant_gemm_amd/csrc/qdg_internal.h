@@ -84,14 +84,34 @@ struct TileCfg {
 };
 
 #ifndef __HIPCC_RTC__  // host launchers (not part of a run-time compiled kernel)
+// The source files whose kernels can be compiled at run time (their text is
+// embedded in the library), and one launch of such a kernel: its name
+// expression in that source, grid and block, and its arguments (the
+// GemmArgs, plus the row- and column-block counts for the LDS-tiled kernels).
+enum JitSource { JIT_SRC_STREAM, JIT_SRC_TILE, JIT_SRC_WSTREAM, JIT_SRC_QTILE, JIT_SRC_WSTREAM8, JIT_NSRC };
+struct KernelLaunch {
+  int src;
+  char expr[192];
+  unsigned grid[3], block;
+  bool mn_args;
+  int m_blocks, n_blocks;
+};
+
+// The main-kernel launchers of the families. With desc set, they describe
+// the launch they would make (kernel and grid) instead of making it, and
+// launch nothing else (weight streaming then leaves the split reduce to
+// the caller).
 hipError_t launch_stream(Format f, bool asym, bool moe, const StreamCfg& c, const GemmArgs& a,
                          int grid_m_blocks, hipStream_t s);
 hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const GemmArgs& a,
-                       int grid_m_blocks, hipStream_t s);
+                       int grid_m_blocks, hipStream_t s, KernelLaunch* desc = nullptr);
 hipError_t launch_reduce_splits(const GemmArgs& a, int m_pad, int n_pad, hipStream_t s);
-hipError_t launch_wstream(bool asym, bool moe, const GemmArgs& a, int nsplit, int grid_m, hipStream_t s);
-hipError_t launch_qtile(Format f, bool moe, int bm, const GemmArgs& a, int m_blocks, hipStream_t s);
-hipError_t launch_wstream8(Format f, const GemmArgs& a, int nsplit, int nt, hipStream_t s);
+hipError_t launch_wstream(bool asym, bool moe, const GemmArgs& a, int nsplit, int grid_m, hipStream_t s,
+                          KernelLaunch* desc = nullptr);
+hipError_t launch_qtile(Format f, bool moe, int bm, const GemmArgs& a, int m_blocks, hipStream_t s,
+                        KernelLaunch* desc = nullptr);
+hipError_t launch_wstream8(Format f, const GemmArgs& a, int nsplit, int nt, hipStream_t s,
+                           KernelLaunch* desc = nullptr);
 int wstream8_max_groups();
 bool stream_cfg_supported(Format f, const StreamCfg& c);
 bool tile_cfg_supported(Format f, const TileCfg& c);
@@ -124,6 +144,10 @@ struct JitResult {
 };
 JitResult jit_stream_kernel(Format f, bool asym, bool raw, const StreamCfg& c, bool moe, const char* cache_dir);
 hipError_t launch_stream_jit(hipFunction_t fn, const StreamCfg& c, const GemmArgs& a, int grid_m, hipStream_t s);
+// The kernel a KernelLaunch names, compiled from its embedded source (same
+// cache and load rules as jit_stream_kernel), and its launch.
+JitResult jit_kernel(int src, const char* expr, const char* cache_dir);
+hipError_t launch_jit(hipFunction_t fn, const KernelLaunch& d, const GemmArgs& a, hipStream_t s);
 
 hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int block_m,
                             int64_t capacity, int32_t* sorted_ids, int32_t* block_expert,

@@ -34,6 +34,11 @@
 //     workgroup reads that expert's weights once for 128 rows and gathers its
 //     A rows (and activation scales) through the sorted row ids; padding rows
 //     read row 0 and are never stored.
+#ifndef __HIPCC_RTC__
+#include <cstdio>
+#include <type_traits>
+#endif
+
 #include "qdg_device.h"
 #include "qdg_internal.h"
 
@@ -459,50 +464,72 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qtile_gemm_kernel(cons
   }
 }
 
+#ifndef __HIPCC_RTC__  // host launchers
+// One launch of qtile_gemm_kernel<KIND, RAW, NS, MOE, WM, WN>, or its
+// description (desc set).
+template <int KIND, bool RAW, int NS, bool MOE, int WM, int WN>
+hipError_t launch_q_inst(const GemmArgs& a, dim3 grid, int m_blocks, int n_blocks, hipStream_t s, KernelLaunch* d) {
+  if (d) {
+    d->src = JIT_SRC_QTILE;
+    std::snprintf(d->expr, sizeof d->expr, "qdg::qtile_gemm_kernel<%d, %s, %d, %s, %d, %d>", KIND,
+                  RAW ? "true" : "false", NS, MOE ? "true" : "false", WM, WN);
+    d->grid[0] = grid.x;
+    d->grid[1] = grid.y;
+    d->grid[2] = 1;
+    d->block = 64 * WM * WN;
+    d->mn_args = true;
+    d->m_blocks = m_blocks;
+    d->n_blocks = n_blocks;
+    return hipSuccess;
+  }
+  hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, MOE, WM, WN>), grid, dim3(64 * WM * WN), 0, s, a, m_blocks,
+                     n_blocks);
+  return hipGetLastError();
+}
+
 template <int KIND, bool RAW>
-hipError_t launch_q(const GemmArgs& a, bool moe, int bm, int m_blocks, int nsplit, hipStream_t s) {
+hipError_t launch_q(const GemmArgs& a, bool moe, int bm, int m_blocks, int nsplit, hipStream_t s, KernelLaunch* d) {
   if (moe && nsplit != 1) return hipErrorInvalidValue;  // grouped MoE is not split
   if (moe && bm == 64) {
     // 64-row expert blocks: 64 x 512 tiles, 8 waves in one row
     constexpr int BM = 64, BN = 512;
     constexpr int NS = 3 * QStage<KIND, BM, BN>::BYTES <= 160 * 1024 ? 3 : 2;
     const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-    hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, true, 1, 8>), dim3(moe_grid_blocks(m_blocks) * n_blocks, 1),
-                       dim3(512), 0, s, a, m_blocks, n_blocks);
-    return hipGetLastError();
+    return launch_q_inst<KIND, RAW, NS, true, 1, 8>(a, dim3(moe_grid_blocks(m_blocks) * n_blocks, 1), m_blocks,
+                                                    n_blocks, s, d);
   }
   if (bm != 128) return hipErrorInvalidValue;
   constexpr int BM = 128, BN = 256;
   using L = QStage<KIND, BM, BN>;
   constexpr int NS = 3 * L::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-  if (moe) {
-    hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, true>), dim3(moe_grid_blocks(m_blocks) * n_blocks, 1),
-                       dim3(512), 0, s, a, m_blocks, n_blocks);
-  } else {
-    hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, false>), dim3(m_blocks * n_blocks, nsplit), dim3(512), 0,
-                       s, a, m_blocks, n_blocks);
-  }
-  return hipGetLastError();
+  if (moe)
+    return launch_q_inst<KIND, RAW, NS, true, 2, 4>(a, dim3(moe_grid_blocks(m_blocks) * n_blocks, 1), m_blocks,
+                                                    n_blocks, s, d);
+  return launch_q_inst<KIND, RAW, NS, false, 2, 4>(a, dim3(m_blocks * n_blocks, nsplit), m_blocks, n_blocks, s, d);
 }
+#endif  // __HIPCC_RTC__
 
 }  // namespace
 
-hipError_t launch_qtile(Format f, bool moe, int bm, const GemmArgs& a, int m_blocks, hipStream_t s) {
+#ifndef __HIPCC_RTC__  // host launchers
+hipError_t launch_qtile(Format f, bool moe, int bm, const GemmArgs& a, int m_blocks, hipStream_t s, KernelLaunch* d) {
   const bool raw = a.otype == QDG_O_I32;
   if (raw && a.split > 1) return hipErrorInvalidValue;  // integer partials are not split
   switch (f) {
     case FMT_W8A8:
-      return raw ? launch_q<Q_W8A8, true>(a, moe, bm, m_blocks, 1, s)
-                 : launch_q<Q_W8A8, false>(a, moe, bm, m_blocks, a.split, s);
+      return raw ? launch_q<Q_W8A8, true>(a, moe, bm, m_blocks, 1, s, d)
+                 : launch_q<Q_W8A8, false>(a, moe, bm, m_blocks, a.split, s, d);
     case FMT_W4A8:
-      return raw ? launch_q<Q_W4A8, true>(a, moe, bm, m_blocks, 1, s)
-                 : launch_q<Q_W4A8, false>(a, moe, bm, m_blocks, a.split, s);
-    case FMT_MXFP4: return launch_q<Q_MXFP4, false>(a, moe, bm, m_blocks, a.split, s);
-    case FMT_W4A4: return launch_q<Q_W4A4, false>(a, moe, bm, m_blocks, a.split, s);
-    case FMT_MXFP4_I8: return launch_q<Q_MXFP4_I8, false>(a, moe, bm, m_blocks, a.split, s);
+      return raw ? launch_q<Q_W4A8, true>(a, moe, bm, m_blocks, 1, s, d)
+                 : launch_q<Q_W4A8, false>(a, moe, bm, m_blocks, a.split, s, d);
+    case FMT_MXFP4: return launch_q<Q_MXFP4, false>(a, moe, bm, m_blocks, a.split, s, d);
+    case FMT_W4A4: return launch_q<Q_W4A4, false>(a, moe, bm, m_blocks, a.split, s, d);
+    case FMT_MXFP4_I8: return launch_q<Q_MXFP4_I8, false>(a, moe, bm, m_blocks, a.split, s, d);
     default: return hipErrorInvalidValue;
   }
 }
+
+#endif  // __HIPCC_RTC__
 
 }  // namespace qdg

@@ -25,7 +25,10 @@
 //     the only per-group epilogue is acc += s * P;
 //   * the output tile is transposed through LDS so every global store writes
 //     whole 16-byte row segments; the tile order is XCD-aware.
+#ifndef __HIPCC_RTC__
+#include <cstdio>
 #include <type_traits>
+#endif
 
 #include "qdg_device.h"
 #include "qdg_internal.h"
@@ -829,9 +832,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
   }
 }
 
+#ifndef __HIPCC_RTC__  // host launchers
 template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE, bool NV = false, bool W8 = false,
           bool W2 = false>
-hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s) {
+hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s, KernelLaunch* d) {
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
   // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256 and 32 x 512,
   // 2 for 256 x 128, 64 x 512 and int8 units)
@@ -839,13 +843,29 @@ hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStrea
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
   // grouped MoE: whole groups of 8 expert blocks (the order of moe_tile_order)
   const int grid_m = MOE ? moe_grid_blocks(m_blocks) : m_blocks;
+  if (d) {
+    auto b = [](bool v) { return v ? "true" : "false"; };
+    d->src = JIT_SRC_TILE;
+    std::snprintf(d->expr, sizeof d->expr, "qdg::tile_gemm_kernel<%s, %d, %d, %d, %d, %s, %s, %s, %s>", b(ASYM),
+                  WAVES_M, WAVES_N, WTM, NS, b(MOE), b(NV), b(W8), b(W2));
+    d->grid[0] = (unsigned)(grid_m * n_blocks);
+    d->grid[1] = (unsigned)nsplit;
+    d->grid[2] = 1;
+    d->block = 64 * WAVES_M * WAVES_N;
+    d->mn_args = true;
+    d->m_blocks = m_blocks;
+    d->n_blocks = n_blocks;
+    return hipSuccess;
+  }
   hipLaunchKernelGGL((tile_gemm_kernel<ASYM, WAVES_M, WAVES_N, WTM, NS, MOE, NV, W8, W2>), dim3(grid_m * n_blocks, nsplit),
                      dim3(64 * WAVES_M * WAVES_N), 0, s, a, m_blocks, n_blocks);
   return hipGetLastError();
 }
 
+#endif  // __HIPCC_RTC__
 }  // namespace
 
+#ifndef __HIPCC_RTC__  // host launchers
 // Instances: (block_m, block_n, waves) = (256, 128, 8), (128, 256, 8) with
 // 64 x 64 wave tiles (two waves per SIMD), (128, 256, 4) with 128 x 64
 // wave tiles (one wave per SIMD, half the unpack work per MFMA), (64, 512, 8)
@@ -870,20 +890,20 @@ bool tile_cfg_supported(Format f, const TileCfg& c) {
 }
 
 hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const GemmArgs& a, int m_blocks,
-                       hipStream_t s) {
+                       hipStream_t s, KernelLaunch* d) {
   if (!tile_cfg_supported(f, c)) return hipErrorInvalidValue;
   if (f == FMT_NVFP4)
-    return moe ? launch_tile_cfg<false, 2, 4, 64, true, true>(a, m_blocks, a.split, s)
-               : launch_tile_cfg<false, 2, 4, 64, false, true>(a, m_blocks, a.split, s);
+    return moe ? launch_tile_cfg<false, 2, 4, 64, true, true>(a, m_blocks, a.split, s, d)
+               : launch_tile_cfg<false, 2, 4, 64, false, true>(a, m_blocks, a.split, s, d);
   if (f == FMT_W8A16)
-    return moe ? launch_tile_cfg<false, 2, 4, 64, true, false, true>(a, m_blocks, a.split, s)
-               : launch_tile_cfg<false, 2, 4, 64, false, false, true>(a, m_blocks, a.split, s);
+    return moe ? launch_tile_cfg<false, 2, 4, 64, true, false, true>(a, m_blocks, a.split, s, d)
+               : launch_tile_cfg<false, 2, 4, 64, false, false, true>(a, m_blocks, a.split, s, d);
   if (f == FMT_W2A16)
-    return moe ? launch_tile_cfg<true, 2, 4, 64, true, false, false, true>(a, m_blocks, a.split, s)
-               : launch_tile_cfg<true, 2, 4, 64, false, false, false, true>(a, m_blocks, a.split, s);
+    return moe ? launch_tile_cfg<true, 2, 4, 64, true, false, false, true>(a, m_blocks, a.split, s, d)
+               : launch_tile_cfg<true, 2, 4, 64, false, false, false, true>(a, m_blocks, a.split, s, d);
 #define QDG_T(ASYM_, WM_, WN_, WTM_, MOE_)                                                 \
   if (asym == ASYM_ && c.bm == WM_ * WTM_ && c.waves == WM_ * WN_ && moe == MOE_)         \
-    return launch_tile_cfg<ASYM_, WM_, WN_, WTM_, MOE_>(a, m_blocks, a.split, s);
+    return launch_tile_cfg<ASYM_, WM_, WN_, WTM_, MOE_>(a, m_blocks, a.split, s, d);
   QDG_T(false, 4, 2, 64, false)
   QDG_T(false, 2, 4, 64, false)
   QDG_T(false, 1, 4, 128, false)
@@ -917,5 +937,7 @@ hipError_t launch_rowsum(const void* a_bf16, const int* sorted_ids, const int* n
                      factor, out);
   return hipGetLastError();
 }
+
+#endif  // __HIPCC_RTC__
 
 }  // namespace qdg

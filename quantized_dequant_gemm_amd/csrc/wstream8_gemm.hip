@@ -17,6 +17,11 @@
 //   * the two K halves are added through LDS in a fixed order; K splits
 //     across workgroups only to occupy the CUs, reduced by
 //     reduce_splits_kernel in split order.
+#ifndef __HIPCC_RTC__
+#include <cstdio>
+#include <type_traits>
+#endif
+
 #include "qdg_device.h"
 #include "qdg_internal.h"
 
@@ -248,8 +253,19 @@ __global__ __launch_bounds__(512) void wsr8_kernel(const GemmArgs p) {
   }
 }
 
+#ifndef __HIPCC_RTC__  // host launchers
 template <int KIND, bool RAW>
-hipError_t launch_w8(const GemmArgs& a, int nsplit, int nt, hipStream_t s) {
+hipError_t launch_w8(const GemmArgs& a, int nsplit, int nt, hipStream_t s, KernelLaunch* d) {
+  if (d) {
+    d->src = JIT_SRC_WSTREAM8;
+    std::snprintf(d->expr, sizeof d->expr, "qdg::wsr8_kernel<%d, %s, %d>", KIND, RAW ? "true" : "false", nt);
+    d->grid[0] = (unsigned)(nt == 1 ? a.ntiles : (a.ntiles + 3) / 4);
+    d->grid[1] = (unsigned)nsplit;
+    d->grid[2] = 1;
+    d->block = 64 * WAVES;
+    d->mn_args = false;
+    return hipSuccess;
+  }
   if (nt == 1) {
     hipLaunchKernelGGL((wsr8_kernel<KIND, RAW, 1>), dim3(a.ntiles, nsplit, 1), dim3(64 * WAVES), 0, s, a);
   } else {
@@ -258,24 +274,28 @@ hipError_t launch_w8(const GemmArgs& a, int nsplit, int nt, hipStream_t s) {
   return hipGetLastError();
 }
 
+#endif  // __HIPCC_RTC__
 }  // namespace
 
+#ifndef __HIPCC_RTC__  // host launchers
 // Largest K range (in 128-wide groups) one workgroup of this family holds.
 int wstream8_max_groups() { return RG; }
 
-hipError_t launch_wstream8(Format f, const GemmArgs& a, int nsplit, int nt, hipStream_t s) {
+hipError_t launch_wstream8(Format f, const GemmArgs& a, int nsplit, int nt, hipStream_t s, KernelLaunch* d) {
   const bool raw = a.otype == QDG_O_I32;
   if ((a.groups + nsplit - 1) / nsplit > RG || (raw && nsplit > 1) || (nt != 1 && nt != 4))
     return hipErrorInvalidValue;
   hipError_t e;
   switch (f) {
-    case FMT_W8A8: e = raw ? launch_w8<K_W8A8, true>(a, 1, nt, s) : launch_w8<K_W8A8, false>(a, nsplit, nt, s); break;
-    case FMT_W4A8: e = raw ? launch_w8<K_W4A8, true>(a, 1, nt, s) : launch_w8<K_W4A8, false>(a, nsplit, nt, s); break;
-    case FMT_MXFP4: e = launch_w8<K_MXFP4, false>(a, nsplit, nt, s); break;
+    case FMT_W8A8: e = raw ? launch_w8<K_W8A8, true>(a, 1, nt, s, d) : launch_w8<K_W8A8, false>(a, nsplit, nt, s, d); break;
+    case FMT_W4A8: e = raw ? launch_w8<K_W4A8, true>(a, 1, nt, s, d) : launch_w8<K_W4A8, false>(a, nsplit, nt, s, d); break;
+    case FMT_MXFP4: e = launch_w8<K_MXFP4, false>(a, nsplit, nt, s, d); break;
     default: return hipErrorInvalidValue;
   }
-  if (e == hipSuccess && nsplit > 1) e = launch_reduce_splits(a, 16, a.ntiles * 16, s);
+  if (!d && e == hipSuccess && nsplit > 1) e = launch_reduce_splits(a, 16, a.ntiles * 16, s);
   return e;
 }
+
+#endif  // __HIPCC_RTC__
 
 }  // namespace qdg

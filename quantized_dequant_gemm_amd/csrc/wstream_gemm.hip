@@ -26,6 +26,10 @@
 // asynchronous copy pipeline (kinachrichten, "Wie die Architektur
 // funktioniert"); a register-level pipeline with double-buffered LDS A
 // chunks is the gfx950 form of that idea.
+#ifndef __HIPCC_RTC__
+#include <cstdio>
+#endif
+
 #include "qdg_device.h"
 #include "qdg_internal.h"
 
@@ -443,10 +447,22 @@ __global__ __launch_bounds__(512) void wsr_kernel(const GemmArgs p) {
   ws_store<MOE>(p, acc, tile, split, mb, c, col);
 }
 
+#ifndef __HIPCC_RTC__  // host launchers
 template <bool ASYM, bool MOE>
-hipError_t launch_ws(const GemmArgs& a, int nsplit, int grid_m, hipStream_t s) {
+hipError_t launch_ws(const GemmArgs& a, int nsplit, int grid_m, hipStream_t s, KernelLaunch* d) {
   dim3 grid((a.ntiles + NT - 1) / NT, nsplit, grid_m);
   const bool resident = (a.groups + nsplit - 1) / nsplit <= RG;
+  if (d) {
+    d->src = JIT_SRC_WSTREAM;
+    std::snprintf(d->expr, sizeof d->expr, "qdg::%s<%s, %s>", resident ? "wsr_kernel" : "wstream_kernel",
+                  ASYM ? "true" : "false", MOE ? "true" : "false");
+    d->grid[0] = grid.x;
+    d->grid[1] = grid.y;
+    d->grid[2] = grid.z;
+    d->block = 64 * WAVES;
+    d->mn_args = false;
+    return hipSuccess;
+  }
   if (resident)
     hipLaunchKernelGGL((wsr_kernel<ASYM, MOE>), grid, dim3(64 * WAVES), 0, s, a);
   else
@@ -454,13 +470,18 @@ hipError_t launch_ws(const GemmArgs& a, int nsplit, int grid_m, hipStream_t s) {
   return hipGetLastError();
 }
 
+#endif  // __HIPCC_RTC__
 }  // namespace
 
-hipError_t launch_wstream(bool asym, bool moe, const GemmArgs& a, int nsplit, int grid_m, hipStream_t s) {
-  if (moe) return asym ? hipErrorInvalidValue : launch_ws<false, true>(a, 1, grid_m, s);
-  hipError_t e = asym ? launch_ws<true, false>(a, nsplit, 1, s) : launch_ws<false, false>(a, nsplit, 1, s);
-  if (e == hipSuccess && nsplit > 1) e = launch_reduce_splits(a, 16, a.ntiles * 16, s);
+#ifndef __HIPCC_RTC__  // host launchers
+hipError_t launch_wstream(bool asym, bool moe, const GemmArgs& a, int nsplit, int grid_m, hipStream_t s,
+                          KernelLaunch* d) {
+  if (moe) return asym ? hipErrorInvalidValue : launch_ws<false, true>(a, 1, grid_m, s, d);
+  hipError_t e = asym ? launch_ws<true, false>(a, nsplit, 1, s, d) : launch_ws<false, false>(a, nsplit, 1, s, d);
+  if (!d && e == hipSuccess && nsplit > 1) e = launch_reduce_splits(a, 16, a.ntiles * 16, s);
   return e;
 }
+
+#endif  // __HIPCC_RTC__
 
 }  // namespace qdg

@@ -235,11 +235,12 @@ def test_w8a16_layer_validation():
 
 def test_jit_validation_before_device_work():
     p = q.qdg_plan_create(q.layer_w4a16(14336, 4096), q.dense())
-    # M = 16 runs weight streaming, M = 5000 the LDS-tiled family: not compiled at run time
-    assert _status(q.qdg_plan_jit, p, 16) == q.QDG_ERR_UNSUPPORTED
-    assert _status(q.qdg_plan_jit, p, 5000) == q.QDG_ERR_UNSUPPORTED
     assert _status(q.qdg_plan_jit, p, 0) == q.QDG_ERR_INVALID_ARG
-    assert "code=aot" in q.qdg_plan_describe(p, 24)
+    # a MoE block size no family serves is rejected before any compile
+    pm = q.qdg_plan_create(q.layer_w4a16(4096, 7168, num_experts=8), q.moe(8))
+    assert _status(q.qdg_plan_jit, pm, 64, 48) == q.QDG_ERR_UNSUPPORTED
+    for m in (1, 16, 24, 200, 5000):  # every family starts ahead of time
+        assert "code=aot" in q.qdg_plan_describe(p, m)
 
 
 def test_nvfp4_layer_validation():

@@ -1,8 +1,10 @@
-"""Run-time compilation (qdg_plan_jit): the streaming-family instance that
-hipRTC builds from the embedded source reproduces the ahead-of-time
-instance's output bit for bit (the same source, target and options), and
-both match the oracle; a second process loads the code object from the cache
-directory instead of compiling it."""
+"""Run-time compilation (qdg_plan_jit): the instance of every kernel family
+(streaming, weight streaming in its resident and chunked forms, LDS-tiled,
+8-bit LDS-tiled, 8-bit weight streaming, grouped MoE tiles) that hipRTC
+builds from the embedded source reproduces the ahead-of-time instance's
+output bit for bit (the same source, target and options), and both match
+the oracle; a second process loads the code object from the cache directory
+instead of compiling it."""
 
 import os
 import subprocess
@@ -138,3 +140,85 @@ def test_jit_nvfp4_matches_aot(qdg):
     y_jit = _run(jit, a_dev.data_ptr(), None, pk, m, n, layer.otype)
     assert torch.equal(y_aot, y_jit)
     assert metrics.rel_frob(H.to_f64(y_jit), ref.gemm_nvfp4a16(a, codes, sc, ts)) <= 5e-5
+
+
+def _w4a16_case(m, n, k, salt):
+    qv, sc = quant.quantize_int4_sym(synth.weights_f32(n, k, workload_id=10, salt=salt))
+    a = synth.activations_bf16_bits(m, k, workload_id=10, salt=salt + 1)
+    layer = q.layer_w4a16(n, k)
+    pk = H.Packed(layer, *H.std_w4(qv, sc)[:2])
+    return layer, pk, H.bf16_dev(a), None, ref.gemm_w4a16(a, ref.dequant_int4_sym(qv, sc))
+
+
+def _w8a8_case(m, n, k, salt):
+    qw, sw = quant.quantize_int8_per_channel(synth.weights_f32(n, k, workload_id=10, salt=salt))
+    qa, sa = quant.quantize_act_int8(synth.activations_bf16_bits(m, k, workload_id=10, salt=salt + 1))
+    layer = q.layer_w8a8(n, k)
+    pk = H.Packed(layer, H.dev(qw.astype(np.int8)), H.dev(sw))
+    return layer, pk, H.dev(qa), H.dev(sa), ref.gemm_w8a8(qa, sa, qw, sw)[0]
+
+
+# (family in the plan's description, kernel, case builder, M, N, K, tuning)
+FAMILIES = {
+    "tile": ("tile", _w4a16_case, 200, 1000, 2048, None),
+    "wstream": ("wstream", _w4a16_case, 16, 1000, 2048, None),
+    "wstream_chunked": ("wstream", _w4a16_case, 4, 512, 8192, dict(block_m=16, block_n=64, split_k=1, waves=8)),
+    "wstream_split": ("wstream", _w4a16_case, 16, 256, 4096, dict(block_m=16, block_n=64, split_k=4, waves=8)),
+    "qtile_split": ("qtile", _w8a8_case, 256, 512, 1024, dict(block_m=128, split_k=2)),
+    "wstream8": ("wstream", _w8a8_case, 16, 2048, 4096, None),
+}
+
+
+@pytest.mark.parametrize("case", list(FAMILIES))
+def test_jit_every_family_matches_aot(qdg, tmp_path, case):
+    fam, build, m, n, k, tun = FAMILIES[case]
+    layer, pk, a_dev, sa_dev, y64 = build(m, n, k, salt=len(case))
+    tuning = q.TuningConfig(**tun) if tun else None
+    aot = q.qdg_plan_create(layer, q.dense(), tuning)
+    jit = q.qdg_plan_create(layer, q.dense(), tuning)
+    assert f"family={fam} " in q.qdg_plan_describe(aot, m)
+    info = q.qdg_plan_jit(jit, m, 0, str(tmp_path))
+    print(f"{case}: compile {info.compile_ms:.0f} ms, {info.code_bytes} bytes")
+    assert info.code_bytes > 0 or info.from_cache == 2
+    assert "code=jit" in q.qdg_plan_describe(jit, m) and "code=aot" in q.qdg_plan_describe(aot, m)
+    sa_ptr = sa_dev.data_ptr() if sa_dev is not None else None
+    y_aot = _run(aot, a_dev.data_ptr(), sa_ptr, pk, m, n, layer.otype)
+    y_jit = _run(jit, a_dev.data_ptr(), sa_ptr, pk, m, n, layer.otype)
+    assert torch.equal(y_aot, y_jit)
+    err = metrics.rel_frob(H.to_f64(y_jit), y64)
+    assert err <= 2e-3, err
+
+
+def test_jit_moe_tile_matches_aot(qdg, tmp_path):
+    # grouped MoE in 32-row expert blocks (LDS-tiled 32 x 512 tiles)
+    E, top_k, t, n, k, bm = 4, 2, 100, 512, 1024, 32
+    ids, _ = ref.route_topk(synth.router_logits(t, E, salt=61), top_k)
+    qs = [quant.quantize_int4_sym(synth.weights_f32(n, k, workload_id=10, salt=300 + e)) for e in range(E)]
+    a = synth.activations_bf16_bits(t, k, workload_id=10, salt=62)
+    layer = q.layer_w4a16(n, k, num_experts=E)
+    pk = H.Packed(layer, H.dev(np.stack([codecs.pack_nibbles(codecs.encode_int4(qv)) for qv, _ in qs])),
+                  H.dev(np.stack([np.asarray(sc, np.uint16).view(np.int16) for _, sc in qs])))
+    cap = q.qdg_moe_align_capacity(t, top_k, E, bm)
+    sid = torch.empty(cap, dtype=torch.int32, device="cuda")
+    blk = torch.empty(cap // bm, dtype=torch.int32, device="cuda")
+    npad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids_dev = H.dev(ids.astype(np.int32))
+    q.qdg_moe_align(ids_dev.data_ptr(), t, top_k, E, bm, sid.data_ptr(), blk.data_ptr(), npad.data_ptr(),
+                    q.current_stream())
+    a_dev = H.bf16_dev(a)
+    outs = []
+    for use_jit in (False, True):
+        plan = q.qdg_plan_create(layer, q.moe(top_k))
+        if use_jit:
+            q.qdg_plan_jit(plan, t, bm, str(tmp_path))
+        d = q.qdg_moe_describe(plan, t, bm)
+        assert "family=tile " in d and ("code=jit" if use_jit else "code=aot") in d, d
+        ws, nbytes = H.workspace(plan, t)
+        y = H.out_tensor(t * top_k, n, layer.otype)
+        q.qdg_moe_gemm(plan, a_dev.data_ptr(), None, pk.buf.data_ptr(), sid.data_ptr(), blk.data_ptr(),
+                       npad.data_ptr(), t, bm, 0, y.data_ptr(), ws.data_ptr(), nbytes, q.current_stream())
+        torch.cuda.synchronize()
+        outs.append(y)
+    assert torch.equal(outs[0], outs[1])
+    y64, _ = ref.moe_rows(ids, 0, lambda e, rows: ref.gemm_w4a16(a[rows], ref.dequant_int4_sym(*qs[e])))
+    assert metrics.rel_frob(H.to_f64(outs[1]), y64) <= 2e-3
