@@ -111,9 +111,11 @@ __global__ void reduce_splits_kernel(const float* __restrict__ partial, void* __
 //          16 bytes apart modulo 128, so the 8 lanes served together by a
 //          16-byte LDS read always hit distinct banks, and every fragment
 //          address is one per-lane base plus an immediate offset)
-//   RS     BM floats (row sums, pre-scaled), in a slot of at least 1 KiB
-//          so that one whole-wave copy fills it, starting at the next 1 KiB
-//          boundary after A (the A copies move whole 1 KiB spans)
+//   RS     BM floats (row sums, pre-scaled), starting at the next 1 KiB
+//          boundary after A (the A copies move whole 1 KiB spans), in a slot
+//          one whole-wave copy fills: 256 bytes (4 per lane) for up to 64
+//          rows, else at least 1 KiB (16 per lane); the small slot is what
+//          lets three stages of 64 x 512 tiles fit in the 160 KiB
 //   W      BN/16 packed weight units of UB bytes (1 KiB for 4-bit codes, 2 KiB
 //          for int8; tile-major)
 //   S      BN/16 x 16 scale records of 8 bytes
@@ -124,7 +126,8 @@ struct Stage {
   static constexpr int A_SLOTS = BM * ROW / 16;  // 16-byte slots, 17 per row
   // whole 1 KiB copies fill A (the last one may run past BM rows)
   static constexpr int RS = (BM * ROW + 1023) / 1024 * 1024;
-  static constexpr int W = RS + (BM * 4 > 1024 ? BM * 4 : 1024);
+  static constexpr bool RS_SMALL = BM <= 64;  // 4-byte copies into a 256-byte slot
+  static constexpr int W = RS + (RS_SMALL ? 256 : BM * 4 > 1024 ? BM * 4 : 1024);
   static constexpr int S = W + (BN / 16) * UB;
   static constexpr int BYTES = S + (BN / 16) * 128;
 };
@@ -195,12 +198,17 @@ __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint
   if constexpr (UB != 2048)
     __builtin_amdgcn_global_load_lds(sbase + (size_t)g * 128 + s_off,
                                      (lds_void*)(st + L::S + (wave % (BN / 128)) * 1024), 16, 0, 0);
-  // row sums: one whole-wave copy per wave; lanes past BM / 4 repeat rows
-  // into the unused rest of the slot
+  // row sums: one whole-wave copy per wave; lanes past the block's rows
+  // repeat rows into the unused rest of the slot
   if constexpr (RS) {
-    static_assert(BM / 4 <= 64, "one copy of row sums");
-    const char* rs = (const char*)(p.rowsum + (size_t)g * p.m_pad + mb * BM) + (lane % (BM / 4)) * 16;
-    __builtin_amdgcn_global_load_lds(rs, (lds_void*)(st + L::RS), 16, 0, 0);
+    if constexpr (L::RS_SMALL) {
+      const float* rs = p.rowsum + (size_t)g * p.m_pad + mb * BM + lane % BM;
+      __builtin_amdgcn_global_load_lds(rs, (lds_void*)(st + L::RS), 4, 0, 0);
+    } else {
+      static_assert(BM / 4 <= 64, "one copy of row sums");
+      const char* rs = (const char*)(p.rowsum + (size_t)g * p.m_pad + mb * BM) + (lane % (BM / 4)) * 16;
+      __builtin_amdgcn_global_load_lds(rs, (lds_void*)(st + L::RS), 16, 0, 0);
+    }
   }
 }
 
@@ -837,8 +845,8 @@ template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, bool MOE, bool NV = fals
           bool W2 = false>
 hipError_t launch_tile_cfg(const GemmArgs& a, int m_blocks, int nsplit, hipStream_t s, KernelLaunch* d) {
   constexpr int BM = WTM * WAVES_M, BN = 64 * WAVES_N;
-  // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256 and 32 x 512,
-  // 2 for 256 x 128, 64 x 512 and int8 units)
+  // as many stages as fit in the 160 KiB of LDS (3 for 128 x 256, 16 x 512,
+  // 32 x 512 and 64 x 512, 2 for 256 x 128 and int8 units)
   constexpr int NS = 3 * Stage<BM, BN, W8 ? 2048 : W2 ? 512 : 1024>::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
   // grouped MoE: whole groups of 8 expert blocks (the order of moe_tile_order)
