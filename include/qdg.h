@@ -370,8 +370,11 @@ qdg_status qdg_gemm_noalloc(const qdg_plan* plan, const void* A, const float* a_
    a cache_dir (may be NULL) the code object is stored there, under a key of
    the kernel, the target, the options, the compiler version and the source
    text, and later processes load it instead of compiling. QDG_ERR_UNSUPPORTED
-   when no instance serves M; a compile or load failure QDG_ERR_HIP (with the
-   compiler log in qdg_last_error). Blocks while compiling. The plan is
+   when no instance serves M, and for W4A8-MXFP4 and W4A8-MXFP4-INT8 plans
+   (their fp8 x fp4 scaled-MFMA instances gave results scaled by 2^-127 when
+   launched from a hipRTC code object on MI355X; they run ahead of time); a
+   compile or load failure QDG_ERR_HIP (with the compiler log in
+   qdg_last_error). Blocks while compiling. The plan is
    modified: no other call may use it concurrently. */
 typedef struct qdg_jit_info {
   double compile_ms;  /* hipRTC compile time; 0 when no compile was needed */

@@ -241,6 +241,10 @@ def test_jit_validation_before_device_work():
     assert _status(q.qdg_plan_jit, pm, 64, 48) == q.QDG_ERR_UNSUPPORTED
     for m in (1, 16, 24, 200, 5000):  # every family starts ahead of time
         assert "code=aot" in q.qdg_plan_describe(p, m)
+    # the fp8 x fp4 scaled-MFMA formats are not compiled at run time
+    for layer in (q.layer_mxfp4(2048, 7168), q.layer_mxfp4_int8(2048, 7168)):
+        for m in (16, 32, 512):
+            assert _status(q.qdg_plan_jit, q.qdg_plan_create(layer, q.dense()), m) == q.QDG_ERR_UNSUPPORTED
 
 
 def test_nvfp4_layer_validation():

@@ -107,8 +107,8 @@ def test_jit_moe_matches_aot(qdg):
     a_dev = H.bf16_dev(a)
     outs = []
     for use_jit in (False, True):
-        # the streaming family (16-row blocks of a K this short default to
-        # the LDS-tiled family, which is compiled ahead of time only)
+        # the streaming family, pinned by the tuning (16-row blocks of a K
+        # this short default to the LDS-tiled 16 x 512 tiles)
         plan = q.qdg_plan_create(layer, q.moe(top_k), q.TuningConfig(block_n=64, waves=4))
         if use_jit:
             q.qdg_plan_jit(plan, t, bm)
@@ -158,6 +158,47 @@ def _w8a8_case(m, n, k, salt):
     return layer, pk, H.dev(qa), H.dev(sa), ref.gemm_w8a8(qa, sa, qw, sw)[0]
 
 
+def _w4a8_case(m, n, k, salt):
+    qv, s16 = quant.quantize_int4_sym(synth.weights_f32(n, k, workload_id=10, salt=salt))
+    qa, sa = quant.quantize_act_int8(synth.activations_bf16_bits(m, k, workload_id=10, salt=salt + 1))
+    layer = q.layer_w4a8(n, k)
+    pk = H.Packed(layer, *H.std_w4(qv, s16)[:2])
+    return layer, pk, H.dev(qa), H.dev(sa), ref.gemm_w4a8(qa, sa, qv, s16)[0]
+
+
+def _w4a4_case(m, n, k, salt):
+    codes, e = quant.quantize_mxfp4(synth.weights_f32(n, k, workload_id=10, salt=salt))
+    ac, ae = quant.quantize_act_mxfp4(synth.activations_bf16_bits(m, k, workload_id=10, salt=salt + 1))
+    layer = q.layer_w4a4(n, k)
+    pk = H.Packed(layer, H.dev(codecs.pack_nibbles(codes)), H.dev(e))
+    return layer, pk, H.dev(codecs.pack_nibbles(ac)), H.dev(ae), ref.gemm_w4a4(ac, ae, codes, e)
+
+
+def _w8a16_case(m, n, k, salt):
+    qw, sw = quant.quantize_int8_per_channel(synth.weights_f32(n, k, workload_id=10, salt=salt))
+    a = synth.activations_bf16_bits(m, k, workload_id=10, salt=salt + 1)
+    layer = q.layer_w8a16(n, k)
+    pk = H.Packed(layer, H.dev(qw.astype(np.int8)), H.dev(sw))
+    return layer, pk, H.bf16_dev(a), None, ref.gemm_w8a16(a, qw, sw)
+
+
+def _nvfp4_case(m, n, k, salt):
+    codes, sc, ts = quant.quantize_nvfp4(synth.weights_f32(n, k, workload_id=10, salt=salt))
+    a = synth.activations_bf16_bits(m, k, workload_id=10, salt=salt + 1)
+    layer = q.layer_nvfp4(n, k)
+    pk = H.Packed(layer, H.dev(codecs.pack_nibbles(codes)), H.dev(sc), None,
+                  H.dev(np.atleast_1d(np.asarray(ts, np.float32))))
+    return layer, pk, H.bf16_dev(a), None, ref.gemm_nvfp4a16(a, codes, sc, ts)
+
+
+def _w2a16_case(m, n, k, salt):
+    qv, sc, z = quant.quantize_uint2_asym(synth.weights_f32(n, k, workload_id=10, salt=salt))
+    a = synth.activations_bf16_bits(m, k, workload_id=10, salt=salt + 1)
+    layer = q.layer_w2a16(n, k)
+    pk = H.Packed(layer, H.dev(codecs.pack_crumbs(qv)), H.dev(np.asarray(sc, np.uint16).view(np.int16)), H.dev(z))
+    return layer, pk, H.bf16_dev(a), None, ref.gemm_w4a16(a, ref.dequant_uint2_asym(qv, sc, z))
+
+
 # (family in the plan's description, kernel, case builder, M, N, K, tuning)
 FAMILIES = {
     "tile": ("tile", _w4a16_case, 200, 1000, 2048, None),
@@ -166,6 +207,12 @@ FAMILIES = {
     "wstream_split": ("wstream", _w4a16_case, 16, 256, 4096, dict(block_m=16, block_n=64, split_k=4, waves=8)),
     "qtile_split": ("qtile", _w8a8_case, 256, 512, 1024, dict(block_m=128, split_k=2)),
     "wstream8": ("wstream", _w8a8_case, 16, 2048, 4096, None),
+    "qtile_w4a8": ("qtile", _w4a8_case, 256, 512, 1024, dict(block_m=128)),
+    "qtile_w4a4": ("qtile", _w4a4_case, 256, 512, 1024, dict(block_m=128)),
+    "stream_w4a4": ("stream", _w4a4_case, 32, 512, 1024, None),
+    "tile_w8a16": ("tile", _w8a16_case, 200, 600, 1024, None),
+    "tile_nvfp4": ("tile", _nvfp4_case, 200, 600, 1024, None),
+    "tile_w2a16": ("tile", _w2a16_case, 200, 600, 1024, None),
 }
 
 
