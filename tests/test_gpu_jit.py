@@ -269,3 +269,59 @@ def test_jit_moe_tile_matches_aot(qdg, tmp_path):
     assert torch.equal(outs[0], outs[1])
     y64, _ = ref.moe_rows(ids, 0, lambda e, rows: ref.gemm_w4a16(a[rows], ref.dequant_int4_sym(*qs[e])))
     assert metrics.rel_frob(H.to_f64(outs[1]), y64) <= 2e-3
+
+
+@pytest.mark.parametrize("per_pair", [0, 1])
+def test_jit_moe_qtile_matches_aot(qdg, tmp_path, per_pair):
+    # grouped MoE with int8 activations in 64-row expert blocks (8-bit
+    # LDS-tiled 64 x 512 tiles); per_pair 1 reads one input row per pair
+    E, top_k, t, n, k, bm = 8, 2, 160, 512, 1024, 64
+    ids, _ = ref.route_topk(synth.router_logits(t, E, salt=71 + per_pair), top_k)
+    qs = [quant.quantize_int4_sym(synth.weights_f32(n, k, workload_id=10, salt=400 + e)) for e in range(E)]
+    rows_in = t * top_k if per_pair else t
+    qa, sa = quant.quantize_act_int8(synth.activations_bf16_bits(rows_in, k, workload_id=10, salt=72))
+    layer = q.layer_w4a8(n, k, num_experts=E)
+    pk = H.Packed(layer, H.dev(np.stack([codecs.pack_nibbles(codecs.encode_int4(qv)) for qv, _ in qs])),
+                  H.dev(np.stack([np.asarray(sc, np.uint16).view(np.int16) for _, sc in qs])))
+    cap = q.qdg_moe_align_capacity(t, top_k, E, bm)
+    sid = torch.empty(cap, dtype=torch.int32, device="cuda")
+    blk = torch.empty(cap // bm, dtype=torch.int32, device="cuda")
+    npad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids_dev = H.dev(ids.astype(np.int32))
+    q.qdg_moe_align(ids_dev.data_ptr(), t, top_k, E, bm, sid.data_ptr(), blk.data_ptr(), npad.data_ptr(),
+                    q.current_stream())
+    qa_dev, sa_dev = H.dev(qa), H.dev(sa)
+    outs = []
+    for use_jit in (False, True):
+        plan = q.qdg_plan_create(layer, q.moe(top_k))
+        if use_jit:
+            q.qdg_plan_jit(plan, t, bm, str(tmp_path))
+        d = q.qdg_moe_describe(plan, t, bm)
+        assert "family=qtile " in d and ("code=jit" if use_jit else "code=aot") in d, d
+        ws, nbytes = H.workspace(plan, t)
+        y = H.out_tensor(t * top_k, n, layer.otype)
+        q.qdg_moe_gemm(plan, qa_dev.data_ptr(), sa_dev.data_ptr(), pk.buf.data_ptr(), sid.data_ptr(),
+                       blk.data_ptr(), npad.data_ptr(), t, bm, per_pair, y.data_ptr(), ws.data_ptr(), nbytes,
+                       q.current_stream())
+        torch.cuda.synchronize()
+        outs.append(y)
+    assert torch.equal(outs[0], outs[1])
+    y64, _ = ref.moe_rows(ids, per_pair, lambda e, rows: ref.gemm_w4a8(qa[rows], sa[rows], *qs[e])[0])
+    assert metrics.rel_frob(H.to_f64(outs[1]), y64) <= 2e-3
+
+
+def test_jit_plan_through_noalloc_entry_point(qdg, tmp_path):
+    # a run-time-compiled plan through the allocation-free entry point: the
+    # same output as the workspace entry point, in the LDS-tiled family with
+    # its K split (partials in the library's scratch array)
+    layer, pk, a_dev, _, y64 = _w4a16_case(200, 4096, 4096, salt=91)
+    plan = q.qdg_plan_create(layer, q.dense())
+    q.qdg_plan_jit(plan, 200, 0, str(tmp_path))
+    d = q.qdg_plan_describe(plan, 200)
+    assert "family=tile " in d and "code=jit" in d and "split_k=1 " not in d, d
+    y_ws = _run(plan, a_dev.data_ptr(), None, pk, 200, 4096, layer.otype)
+    y_na = H.out_tensor(200, 4096, layer.otype)
+    q.qdg_gemm_noalloc(plan, a_dev.data_ptr(), None, pk.buf.data_ptr(), y_na.data_ptr(), 200, q.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(y_ws, y_na)
+    assert metrics.rel_frob(H.to_f64(y_na), y64) <= 2e-3
