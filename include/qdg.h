@@ -450,7 +450,10 @@ qdg_status qdg_moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int3
    e = block_expert[b] and r = i (a_per_pair = 1, e.g. the down projection)
    or r = i / top_k (a_per_pair = 0, e.g. gate+up reading token rows).
    Y is [T*top_k][n] (the SiLU*mul epilogue: [T*top_k][n/2]); rows are
-   written only for real pairs. A and a_scales are laid out as for qdg_gemm
+   written only for real pairs. The routing arrays are laid out as
+   qdg_moe_align writes them: within a block the real entries come first and
+   the sentinels after them (the LDS-tiled family skips a 32-row half of a
+   block whose first entry is a sentinel). A and a_scales are laid out as for qdg_gemm
    with one row per r (the 8- and 4-bit activation formats take the codes
    and scales of qdg_quantize_act over those rows). block_m must be the
    value passed to qdg_moe_align:

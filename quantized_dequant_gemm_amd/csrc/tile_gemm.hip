@@ -271,7 +271,9 @@ __device__ __forceinline__ void tile_group(const char* st, int a_lane, int w_lan
 // takes, at step s, dword s % 4 of unit quarter h + 2 * (s / 4), i.e. K
 // values 32 (h + 2 (s / 4)) + 8 (s % 4) .. +7, and reads the same eight
 // A values.
-template <bool ASYM, int BM, int BN>
+// RB = 1 runs only the first row block (grouped MoE: the wave's rows 32..63
+// are all padding).
+template <bool ASYM, int BM, int BN, int RB = 2>
 __device__ __forceinline__ void tile_group32(const char* st, int a_lane, int w_lane, int s_lane, int rs_lane,
                                              uint32_t um, uint32_t ue, f32x16_t (&acc)[2][2]) {
   using L = Stage<BM, BN>;
@@ -288,7 +290,7 @@ __device__ __forceinline__ void tile_group32(const char* st, int a_lane, int w_l
   // each chain starts from the row sums of its rows (times -(128+z))
   f32x16_t pacc[2][2];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     f32x4_t r[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) r[q] = *(const f32x4_t*)(st + rs_lane + rb * 128 + q * 32);
@@ -309,7 +311,7 @@ __device__ __forceinline__ void tile_group32(const char* st, int a_lane, int w_l
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
         a[s][rb] = *(const u32x4_t*)(st + a_lane + rb * 32 * L::ROW + hs * 128 + s * 16);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -318,13 +320,13 @@ __device__ __forceinline__ void tile_group32(const char* st, int a_lane, int w_l
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) b[cb] = unpack_u4_bf16_offset128(bp[cb][hs][s], um, ue);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) pacc[rb][cb] = mfma_bf16_32(a[s][rb], b[cb], pacc[rb][cb]);
     }
   }
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -501,6 +503,11 @@ __device__ __forceinline__ void tile_group32_w8(const char* st, int a_lane, int 
       for (int i = 0; i < 16; ++i) acc[rb][cb][i] += pacc[rb][cb][i];
 }
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 template <bool ASYM, int WAVES_M, int WAVES_N, int WTM, int NS, bool MOE, bool NV = false, bool W8 = false,
           bool W2 = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const GemmArgs p, int m_blocks,
@@ -648,51 +655,67 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
       load_stage<BM, BN, NW, !NV, UB>(stage[q], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane, mb,
                              min(g0 + q, g1 - 1));
   }
-  int gb = g0;
-  for (; gb + NS <= g1; gb += NS) {
+  // The K loop, instantiated per count of the wave's 32-row blocks that
+  // hold real rows: a grouped MoE wave whose rows 32..63 are all padding
+  // (an expert's real entries lead its blocks, so the entry at row 32 tells)
+  // skips their fragment reads and MFMAs. Both instances run the same
+  // barriers, so the waves of one workgroup may take different ones.
+  auto k_loop = [&](auto rb_count) __attribute__((always_inline)) {
+    constexpr int RB = decltype(rb_count)::value;
+    int gb = g0;
+    for (; gb + NS <= g1; gb += NS) {
 #pragma unroll
-    for (int cur = 0; cur < NS; ++cur) {
-      // this wave's copies of group gb+cur are done once at most the copies
-      // of one later group remain in flight (copies complete in order)
-      if constexpr (NS == 3)
-        __builtin_amdgcn_s_waitcnt((VM_NEXT & 15) | (7 << 4) | (15 << 8) | ((VM_NEXT >> 4) << 14));
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      // every wave's copies of the group landed and every wave is done with
-      // the previous group's stage. A bare s_barrier: __syncthreads would also
-      // wait for the copies in flight.
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      asm volatile("s_barrier" ::: "memory");
-      load_stage<BM, BN, NW, !NV, UB>(stage[(cur + NS - 1) % NS], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane,
-                             mb, min(gb + cur + NS - 1, g1 - 1));
-      if constexpr (NV)
-        tile_group32_nv<BM, BN>(stage[cur], a_lane, w_lane, sv_lane, acc32);
-      else if constexpr (W8)
-        tile_group32_w8<BM, BN>(stage[cur], a_lane, w8_lane, rs_lane, acc32);
-      else if constexpr (W2)
-        tile_group32_w2<BM, BN>(stage[cur], a_lane, w2_lane, s_lane, rs_lane, um, ue, acc32);
-      else if constexpr (M32)
-        tile_group32<ASYM, BM, BN>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
-      else
-        tile_group<ASYM, BM, BN, MTW>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
+      for (int cur = 0; cur < NS; ++cur) {
+        // this wave's copies of group gb+cur are done once at most the copies
+        // of one later group remain in flight (copies complete in order)
+        if constexpr (NS == 3)
+          __builtin_amdgcn_s_waitcnt((VM_NEXT & 15) | (7 << 4) | (15 << 8) | ((VM_NEXT >> 4) << 14));
+        else
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        // every wave's copies of the group landed and every wave is done with
+        // the previous group's stage. A bare s_barrier: __syncthreads would also
+        // wait for the copies in flight.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+        load_stage<BM, BN, NW, !NV, UB>(stage[(cur + NS - 1) % NS], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane,
+                               mb, min(gb + cur + NS - 1, g1 - 1));
+        if constexpr (NV)
+          tile_group32_nv<BM, BN>(stage[cur], a_lane, w_lane, sv_lane, acc32);
+        else if constexpr (W8)
+          tile_group32_w8<BM, BN>(stage[cur], a_lane, w8_lane, rs_lane, acc32);
+        else if constexpr (W2)
+          tile_group32_w2<BM, BN>(stage[cur], a_lane, w2_lane, s_lane, rs_lane, um, ue, acc32);
+        else if constexpr (M32)
+          tile_group32<ASYM, BM, BN, RB>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
+        else
+          tile_group<ASYM, BM, BN, MTW>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
+      }
     }
-  }
 #pragma unroll
-  for (int cur = 0; cur < NS - 1; ++cur) {
-    if (gb + cur < g1) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if constexpr (NV)
-        tile_group32_nv<BM, BN>(stage[cur], a_lane, w_lane, sv_lane, acc32);
-      else if constexpr (W8)
-        tile_group32_w8<BM, BN>(stage[cur], a_lane, w8_lane, rs_lane, acc32);
-      else if constexpr (W2)
-        tile_group32_w2<BM, BN>(stage[cur], a_lane, w2_lane, s_lane, rs_lane, um, ue, acc32);
-      else if constexpr (M32)
-        tile_group32<ASYM, BM, BN>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
-      else
-        tile_group<ASYM, BM, BN, MTW>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
+    for (int cur = 0; cur < NS - 1; ++cur) {
+      if (gb + cur < g1) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if constexpr (NV)
+          tile_group32_nv<BM, BN>(stage[cur], a_lane, w_lane, sv_lane, acc32);
+        else if constexpr (W8)
+          tile_group32_w8<BM, BN>(stage[cur], a_lane, w8_lane, rs_lane, acc32);
+        else if constexpr (W2)
+          tile_group32_w2<BM, BN>(stage[cur], a_lane, w2_lane, s_lane, rs_lane, um, ue, acc32);
+        else if constexpr (M32)
+          tile_group32<ASYM, BM, BN, RB>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
+        else
+          tile_group<ASYM, BM, BN, MTW>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
+      }
     }
+  };
+  if constexpr (MOE && M32 && !NV && !W8 && !W2) {
+    if (p.sorted_ids[mb * BM + wm * WTM + 32] >= p.num_pairs)
+      k_loop(IntC<1>{});
+    else
+      k_loop(IntC<2>{});
+  } else {
+    k_loop(IntC<2>{});
   }
 
   // ---- epilogue: per wave, transpose each 16 x 64 strip through LDS so that
