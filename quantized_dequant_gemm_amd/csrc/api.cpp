@@ -229,6 +229,7 @@ struct Choice {
   int grid_m;
   size_t partial_bytes;
   size_t rowsum_bytes;
+  bool pad_skip;  // 8-bit LDS-tiled MoE: the instance that skips all-padding halves of blocks
 };
 
 // Device heuristics per M range for gfx950 (256 CUs): small M streams the
@@ -697,6 +698,13 @@ static qdg_status choose_moe(const qdg_plan& plan, int64_t T, int32_t block_m, i
         if (plan.fmt != FMT_NVFP4) c.rowsum_bytes = (size_t)c.grid_m * 128 * plan.geom.groups * 4;
       } else {
         c.qtile = true;
+        // while experts hold at most one block of rows on average, most
+        // blocks are partly filled and the instance that skips their
+        // all-padding 32-row halves wins (measured on MI355X, W4A8-INT8 at
+        // E = 256, top-8, hidden 7168, 64-row blocks: T = 512 gate+up
+        // 828-846 -> 773-782 us, down 521-524 -> 481 us); with more rows it
+        // loses (T = 4096: 1932-1944 -> 2027-2041 us)
+        c.pad_skip = rows <= E * block_m;
       }
     }
     *out = c;
@@ -758,7 +766,7 @@ static const char* mfma_name(Format f, const Choice& c) {
 static hipError_t family_launch(const qdg_plan& plan, const Choice& c, const GemmArgs& a, bool moe, hipStream_t s,
                                 KernelLaunch* desc) {
   const bool asym = plan.layer.wtype == QDG_W_UINT4;
-  if (c.qtile) return launch_qtile(plan.fmt, moe, c.tc.bm, a, c.grid_m, s, desc);
+  if (c.qtile) return launch_qtile(plan.fmt, moe, c.tc.bm, c.pad_skip, a, c.grid_m, s, desc);
   if (c.tile) return launch_tile(plan.fmt, asym, moe, c.tc, a, c.grid_m, s, desc);
   return plan.fmt == FMT_W4A16 ? launch_wstream(asym, moe, a, c.sc.split, c.grid_m, s, desc)
                                : launch_wstream8(plan.fmt, a, c.sc.split, c.sc.nt, s, desc);
@@ -820,14 +828,14 @@ static hipError_t launch_main(const qdg_plan& plan, const Choice& c, const GemmA
 static int describe(const qdg_plan& plan, const Choice& c, int64_t M, const char* kind, char* buf, size_t len) {
   return snprintf(buf, buf ? len : 0,
                   "%s %s n=%lld k=%lld E=%lld M=%lld: family=%s block_m=%d block_n=%d split_k=%d "
-                  "waves=%d mfma=%s grid_m=%d batch_invariant=%d epilogue=%s tuning=%s code=%s layout=%d arch=gfx950",
+                  "waves=%d mfma=%s grid_m=%d batch_invariant=%d epilogue=%s%s tuning=%s code=%s layout=%d arch=gfx950",
                   fmt_name(plan.fmt, plan.layer), kind, (long long)plan.layer.n, (long long)plan.layer.k,
                   (long long)plan.layer.num_experts, (long long)M,
                   c.qtile ? "qtile" : c.tile ? "tile" : c.ws ? "wstream" : "stream",
                   c.tile || c.qtile ? c.tc.bm : c.sc.mt * 16, c.tile || c.qtile ? c.tc.bn : c.sc.nt * 16,
                   c.sc.split, c.tile || c.qtile ? c.tc.waves : c.sc.kw, mfma_name(plan.fmt, c), c.grid_m,
                   plan.compute.batch_invariant, plan.compute.epilogue == QDG_EPI_SILU_MUL ? "silu_mul" : "none",
-                  c.autotuned ? "autotuned" : plan.has_tuning ? "user" : "heuristic",
+                  c.pad_skip ? " pad_skip=1" : "", c.autotuned ? "autotuned" : plan.has_tuning ? "user" : "heuristic",
                   find_jit(plan, c, plan.compute.kind == QDG_KIND_MOE) ? "jit" : "aot", QDG_LAYOUT_VERSION);
 }
 

@@ -108,7 +108,9 @@ hipError_t launch_tile(Format f, bool asym, bool moe, const TileCfg& c, const Ge
 hipError_t launch_reduce_splits(const GemmArgs& a, int m_pad, int n_pad, hipStream_t s);
 hipError_t launch_wstream(bool asym, bool moe, const GemmArgs& a, int nsplit, int grid_m, hipStream_t s,
                           KernelLaunch* desc = nullptr);
-hipError_t launch_qtile(Format f, bool moe, int bm, const GemmArgs& a, int m_blocks, hipStream_t s,
+// pad_skip (grouped MoE): the instance that skips the all-padding 32-row
+// halves of expert blocks
+hipError_t launch_qtile(Format f, bool moe, int bm, bool pad_skip, const GemmArgs& a, int m_blocks, hipStream_t s,
                         KernelLaunch* desc = nullptr);
 hipError_t launch_wstream8(Format f, const GemmArgs& a, int nsplit, int nt, hipStream_t s,
                            KernelLaunch* desc = nullptr);

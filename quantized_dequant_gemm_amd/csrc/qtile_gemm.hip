@@ -72,10 +72,11 @@ struct QStage {
 // lambda). A: slot q = 64 i + lane is row q / CH, 16-byte chunk q % CH (the
 // last chunk is padding and re-reads chunk 0); a_off holds each slot's row
 // offset.
-// RAW and MOE are not used here: they only give every kernel instance its
-// own specialization (hipcc's host pass rejects a second kernel that calls
-// the same specialization of a device function using target builtins).
-template <int KIND, bool RAW, bool MOE, int BM, int BN, int NW>
+// RAW, MOE and TAG are not used here: they only give every calling function
+// its own specialization (hipcc's host pass rejects a second function that
+// calls the same specialization of a device function using target builtins):
+// TAG = 16 PADSKIP + MT in the K loop, 16 PADSKIP in the kernel's prologue.
+template <int KIND, bool RAW, bool MOE, int BM, int BN, int NW, int TAG>
 __device__ __forceinline__ void q_load_stage(char* st, const char* a_g, const uint32_t* a_off,
                                              const uint32_t* as_off, const GemmArgs& p, const uint8_t* wbase,
                                              const uint8_t* sbase, int wg_tile0, int wave, int lane, int g) {
@@ -132,7 +133,9 @@ struct QFrag {
   int ae8[4];       // W4A4: E8M0 scale of the lane's A row and 32-block
 };
 
-template <int KIND, int BM, int BN>
+// MT: the row tiles read and multiplied (2: the wave's rows 32..63 are
+// padding of a grouped MoE block)
+template <int KIND, int BM, int BN, int MT = 4>
 __device__ __forceinline__ void q_frag_load(QFrag<KIND>& f, const char* st, int a_lane, int w_lane, int rec_lane,
                                             int as_lane) {
   using L = QStage<KIND, BM, BN>;
@@ -150,7 +153,7 @@ __device__ __forceinline__ void q_frag_load(QFrag<KIND>& f, const char* st, int 
     }
   }
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     // int8 operand: lane group c holds K 32c..32c+15 (step 0) and +16 (step 1);
     // fp8 operand: K 16c..16c+15 and 64+16c..64+16c+15
     // fp4 operand: K 32c..32c+31 (16 bytes)
@@ -166,7 +169,7 @@ __device__ __forceinline__ void q_frag_load(QFrag<KIND>& f, const char* st, int 
   }
 }
 
-template <int KIND, bool RAW, bool MOE, int BM, class Acc>  // MOE, BM: a specialization per kernel, as above
+template <int KIND, bool RAW, bool MOE, int BM, int MT, class Acc>  // MOE, BM: a specialization per kernel, as above
 __device__ __forceinline__ void q_frag_compute(const QFrag<KIND>& f, Acc (&acc)[4][4]) {
   u32x4_t b[4][2];
 #pragma unroll
@@ -183,7 +186,7 @@ __device__ __forceinline__ void q_frag_compute(const QFrag<KIND>& f, Acc (&acc)[
     }
   }
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if constexpr (KIND == Q_W4A4) {
@@ -224,7 +227,60 @@ struct QAcc {
   using T = typename std::conditional<KIND == Q_W8A8 || RAW, i32x4_t, f32x4_t>::type;
 };
 
-template <int KIND, bool RAW, int NS, bool MOE, int WAVES_M = 2, int WAVES_N = 4>
+// The K loop of the 8-bit tile over groups [g0, g1) (the first NS - 1
+// stages already in flight): full rounds of NS groups run unrolled with
+// constant stage indices; MT row tiles of the wave are read and multiplied.
+template <int KIND, bool RAW, int NS, bool MOE, int BM, int BN, int NW, int VM_NEXT, bool PADSKIP, int MT, class Acc>
+__device__ __forceinline__ void q_k_loop(char* const (&stage)[3], const char* a_g, const uint32_t* a_off,
+                                         const uint32_t* as_off, const GemmArgs& p, const uint8_t* wbase,
+                                         const uint8_t* sbase, int wg_tile0, int wave, int lane, int g0, int g1,
+                                         int a_lane, int w_lane, int rec_lane, int as_lane, Acc (&acc)[4][4]) {
+  QFrag<KIND> fr;
+  int gb = g0;
+  for (; gb + NS <= g1; gb += NS) {
+#pragma unroll
+    for (int cur = 0; cur < NS; ++cur) {
+      // this wave's copies of group gb+cur are done once at most the copies
+      // of the NS - 2 later groups in flight remain (copies complete in
+      // order; with two stages nothing later is in flight yet)
+      constexpr int VM_LEFT = VM_NEXT * (NS - 2);
+      __builtin_amdgcn_s_waitcnt((VM_LEFT & 15) | (7 << 4) | (15 << 8) | ((VM_LEFT >> 4) << 14));
+      // every wave's copies of the group landed; the stage of the previous
+      // group is free. A bare s_barrier: __syncthreads would also wait for
+      // the copies in flight.
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+      q_load_stage<KIND, RAW, MOE, BM, BN, NW, 16 * PADSKIP + MT>(stage[(cur + NS - 1) % NS], a_g, a_off, as_off, p, wbase, sbase,
+                                          wg_tile0, wave, lane, min(gb + cur + NS - 1, g1 - 1));
+      q_frag_load<KIND, BM, BN, MT>(fr, stage[cur], a_lane, w_lane, rec_lane, as_lane);
+      // MXFP4: all of the group's fragment reads go out before its first
+      // MFMA (left to itself the scheduler sinks each row tile's reads next
+      // to its MFMAs, and every row tile then waits out a full LDS latency;
+      // measured on MI355X at M = 4096: 84 -> 78 us at K = 7168, 113 -> 110 us
+      // at K = 2048; the int8 formats run as fast or faster without it)
+      if constexpr (KIND == Q_MXFP4) __builtin_amdgcn_sched_barrier(0);
+      q_frag_compute<KIND, RAW, MOE, BM, MT>(fr, acc);
+    }
+  }
+#pragma unroll
+  for (int cur = 0; cur < NS - 1; ++cur) {
+    if (gb + cur < g1) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      q_frag_load<KIND, BM, BN, MT>(fr, stage[cur], a_lane, w_lane, rec_lane, as_lane);
+      q_frag_compute<KIND, RAW, MOE, BM, MT>(fr, acc);
+    }
+  }
+}
+
+// PADSKIP (grouped MoE): a wave whose rows 32..63 are all padding runs a
+// second instance of the K loop without their fragment reads and MFMAs (an
+// expert's real entries lead its blocks, so the entry at row 32 tells). Both
+// instances run the same barriers, so the waves of one workgroup may take
+// different ones. It is a separate kernel instance because the second K loop
+// changes how the compiler schedules the first (every copy of a group issued
+// right after the barrier), which measured slower where most blocks are full.
+template <int KIND, bool RAW, int NS, bool MOE, int WAVES_M = 2, int WAVES_N = 4, bool PADSKIP = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qtile_gemm_kernel(const GemmArgs p, int m_blocks,
                                                                             int n_blocks) {
   constexpr int NW = WAVES_M * WAVES_N, WTM = 64;
@@ -335,43 +391,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qtile_gemm_kernel(cons
   // before LDS reads stay exact; the last partial round waits for all copies.
 #pragma unroll
   for (int q = 0; q < NS - 1; ++q)
-    q_load_stage<KIND, RAW, MOE, BM, BN, NW>(stage[q], a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane,
+    q_load_stage<KIND, RAW, MOE, BM, BN, NW, 16 * PADSKIP>(stage[q], a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane,
                                         min(g0 + q, g1 - 1));
-  QFrag<KIND> fr;
-  int gb = g0;
-  for (; gb + NS <= g1; gb += NS) {
-#pragma unroll
-    for (int cur = 0; cur < NS; ++cur) {
-      // this wave's copies of group gb+cur are done once at most the copies
-      // of the NS - 2 later groups in flight remain (copies complete in
-      // order; with two stages nothing later is in flight yet)
-      constexpr int VM_LEFT = VM_NEXT * (NS - 2);
-      __builtin_amdgcn_s_waitcnt((VM_LEFT & 15) | (7 << 4) | (15 << 8) | ((VM_LEFT >> 4) << 14));
-      // every wave's copies of the group landed; the stage of the previous
-      // group is free. A bare s_barrier: __syncthreads would also wait for
-      // the copies in flight.
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      asm volatile("s_barrier" ::: "memory");
-      q_load_stage<KIND, RAW, MOE, BM, BN, NW>(stage[(cur + NS - 1) % NS], a_g, a_off, as_off, p, wbase, sbase,
-                                          wg_tile0, wave, lane, min(gb + cur + NS - 1, g1 - 1));
-      q_frag_load<KIND, BM, BN>(fr, stage[cur], a_lane, w_lane, rec_lane, as_lane);
-      // MXFP4: all of the group's fragment reads go out before its first
-      // MFMA (left to itself the scheduler sinks each row tile's reads next
-      // to its MFMAs, and every row tile then waits out a full LDS latency;
-      // measured on MI355X at M = 4096: 84 -> 78 us at K = 7168, 113 -> 110 us
-      // at K = 2048; the int8 formats run as fast or faster without it)
-      if constexpr (KIND == Q_MXFP4) __builtin_amdgcn_sched_barrier(0);
-      q_frag_compute<KIND, RAW, MOE, BM>(fr, acc);
-    }
-  }
-#pragma unroll
-  for (int cur = 0; cur < NS - 1; ++cur) {
-    if (gb + cur < g1) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      q_frag_load<KIND, BM, BN>(fr, stage[cur], a_lane, w_lane, rec_lane, as_lane);
-      q_frag_compute<KIND, RAW, MOE, BM>(fr, acc);
-    }
+  if constexpr (PADSKIP) {
+    static_assert(MOE, "padding halves exist in grouped MoE blocks only");
+    if (p.sorted_ids[mb * BM + wm * WTM + 32] >= p.num_pairs)
+      q_k_loop<KIND, RAW, NS, MOE, BM, BN, NW, VM_NEXT, PADSKIP, 2>(stage, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane, g0, g1, a_lane, w_lane, rec_lane, as_lane, acc);
+    else
+      q_k_loop<KIND, RAW, NS, MOE, BM, BN, NW, VM_NEXT, PADSKIP, 4>(stage, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane, g0, g1, a_lane, w_lane, rec_lane, as_lane, acc);
+  } else {
+    q_k_loop<KIND, RAW, NS, MOE, BM, BN, NW, VM_NEXT, PADSKIP, 4>(stage, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane, g0, g1, a_lane, w_lane, rec_lane, as_lane, acc);
   }
 
   // ---- epilogue: scale, then per wave transpose each 16 x 64 strip through
@@ -467,12 +496,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qtile_gemm_kernel(cons
 #ifndef __HIPCC_RTC__  // host launchers
 // One launch of qtile_gemm_kernel<KIND, RAW, NS, MOE, WM, WN>, or its
 // description (desc set).
-template <int KIND, bool RAW, int NS, bool MOE, int WM, int WN>
+template <int KIND, bool RAW, int NS, bool MOE, int WM, int WN, bool PADSKIP = false>
 hipError_t launch_q_inst(const GemmArgs& a, dim3 grid, int m_blocks, int n_blocks, hipStream_t s, KernelLaunch* d) {
   if (d) {
     d->src = JIT_SRC_QTILE;
-    std::snprintf(d->expr, sizeof d->expr, "qdg::qtile_gemm_kernel<%d, %s, %d, %s, %d, %d>", KIND,
-                  RAW ? "true" : "false", NS, MOE ? "true" : "false", WM, WN);
+    std::snprintf(d->expr, sizeof d->expr, "qdg::qtile_gemm_kernel<%d, %s, %d, %s, %d, %d, %s>", KIND,
+                  RAW ? "true" : "false", NS, MOE ? "true" : "false", WM, WN, PADSKIP ? "true" : "false");
     d->grid[0] = grid.x;
     d->grid[1] = grid.y;
     d->grid[2] = 1;
@@ -482,30 +511,34 @@ hipError_t launch_q_inst(const GemmArgs& a, dim3 grid, int m_blocks, int n_block
     d->n_blocks = n_blocks;
     return hipSuccess;
   }
-  hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, MOE, WM, WN>), grid, dim3(64 * WM * WN), 0, s, a, m_blocks,
+  hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, MOE, WM, WN, PADSKIP>), grid, dim3(64 * WM * WN), 0, s, a, m_blocks,
                      n_blocks);
   return hipGetLastError();
 }
 
 template <int KIND, bool RAW>
-hipError_t launch_q(const GemmArgs& a, bool moe, int bm, int m_blocks, int nsplit, hipStream_t s, KernelLaunch* d) {
+hipError_t launch_q(const GemmArgs& a, bool moe, int bm, int m_blocks, int nsplit, bool pad_skip, hipStream_t s,
+                    KernelLaunch* d) {
   if (moe && nsplit != 1) return hipErrorInvalidValue;  // grouped MoE is not split
   if (moe && bm == 64) {
     // 64-row expert blocks: 64 x 512 tiles, 8 waves in one row
     constexpr int BM = 64, BN = 512;
     constexpr int NS = 3 * QStage<KIND, BM, BN>::BYTES <= 160 * 1024 ? 3 : 2;
     const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-    return launch_q_inst<KIND, RAW, NS, true, 1, 8>(a, dim3(moe_grid_blocks(m_blocks) * n_blocks, 1), m_blocks,
-                                                    n_blocks, s, d);
+    const dim3 grid(moe_grid_blocks(m_blocks) * n_blocks, 1);
+    return pad_skip ? launch_q_inst<KIND, RAW, NS, true, 1, 8, true>(a, grid, m_blocks, n_blocks, s, d)
+                    : launch_q_inst<KIND, RAW, NS, true, 1, 8>(a, grid, m_blocks, n_blocks, s, d);
   }
   if (bm != 128) return hipErrorInvalidValue;
   constexpr int BM = 128, BN = 256;
   using L = QStage<KIND, BM, BN>;
   constexpr int NS = 3 * L::BYTES <= 160 * 1024 ? 3 : 2;
   const int n_blocks = (a.ntiles + BN / 16 - 1) / (BN / 16);
-  if (moe)
-    return launch_q_inst<KIND, RAW, NS, true, 2, 4>(a, dim3(moe_grid_blocks(m_blocks) * n_blocks, 1), m_blocks,
-                                                    n_blocks, s, d);
+  if (moe) {
+    const dim3 grid(moe_grid_blocks(m_blocks) * n_blocks, 1);
+    return pad_skip ? launch_q_inst<KIND, RAW, NS, true, 2, 4, true>(a, grid, m_blocks, n_blocks, s, d)
+                    : launch_q_inst<KIND, RAW, NS, true, 2, 4>(a, grid, m_blocks, n_blocks, s, d);
+  }
   return launch_q_inst<KIND, RAW, NS, false, 2, 4>(a, dim3(m_blocks * n_blocks, nsplit), m_blocks, n_blocks, s, d);
 }
 #endif  // __HIPCC_RTC__
@@ -513,19 +546,20 @@ hipError_t launch_q(const GemmArgs& a, bool moe, int bm, int m_blocks, int nspli
 }  // namespace
 
 #ifndef __HIPCC_RTC__  // host launchers
-hipError_t launch_qtile(Format f, bool moe, int bm, const GemmArgs& a, int m_blocks, hipStream_t s, KernelLaunch* d) {
+hipError_t launch_qtile(Format f, bool moe, int bm, bool pad_skip, const GemmArgs& a, int m_blocks, hipStream_t s,
+                        KernelLaunch* d) {
   const bool raw = a.otype == QDG_O_I32;
   if (raw && a.split > 1) return hipErrorInvalidValue;  // integer partials are not split
   switch (f) {
     case FMT_W8A8:
-      return raw ? launch_q<Q_W8A8, true>(a, moe, bm, m_blocks, 1, s, d)
-                 : launch_q<Q_W8A8, false>(a, moe, bm, m_blocks, a.split, s, d);
+      return raw ? launch_q<Q_W8A8, true>(a, moe, bm, m_blocks, 1, pad_skip, s, d)
+                 : launch_q<Q_W8A8, false>(a, moe, bm, m_blocks, a.split, pad_skip, s, d);
     case FMT_W4A8:
-      return raw ? launch_q<Q_W4A8, true>(a, moe, bm, m_blocks, 1, s, d)
-                 : launch_q<Q_W4A8, false>(a, moe, bm, m_blocks, a.split, s, d);
-    case FMT_MXFP4: return launch_q<Q_MXFP4, false>(a, moe, bm, m_blocks, a.split, s, d);
-    case FMT_W4A4: return launch_q<Q_W4A4, false>(a, moe, bm, m_blocks, a.split, s, d);
-    case FMT_MXFP4_I8: return launch_q<Q_MXFP4_I8, false>(a, moe, bm, m_blocks, a.split, s, d);
+      return raw ? launch_q<Q_W4A8, true>(a, moe, bm, m_blocks, 1, pad_skip, s, d)
+                 : launch_q<Q_W4A8, false>(a, moe, bm, m_blocks, a.split, pad_skip, s, d);
+    case FMT_MXFP4: return launch_q<Q_MXFP4, false>(a, moe, bm, m_blocks, a.split, pad_skip, s, d);
+    case FMT_W4A4: return launch_q<Q_W4A4, false>(a, moe, bm, m_blocks, a.split, pad_skip, s, d);
+    case FMT_MXFP4_I8: return launch_q<Q_MXFP4_I8, false>(a, moe, bm, m_blocks, a.split, pad_skip, s, d);
     default: return hipErrorInvalidValue;
   }
 }

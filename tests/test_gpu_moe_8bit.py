@@ -4,7 +4,9 @@ reference on that pair's input row (exact int32 accumulators with raw output,
 relative Frobenius <= 1e-3 with fp32 and <= 2e-3 with bf16 output), every real
 pair row is written and padding rows are never touched. 16- and 32-row
 expert blocks run the streaming family, 64- and 128-row blocks the 8-bit
-LDS-tiled one (64 x 512 and 128 x 256 tiles)."""
+LDS-tiled one (64 x 512 and 128 x 256 tiles), in the instance that skips
+all-padding 32-row halves of blocks while experts average at most one block
+of rows."""
 
 import numpy as np
 import pytest
@@ -61,7 +63,7 @@ def _acts(kind, rows, k, salt):
 
 
 @pytest.mark.parametrize("kind", ["w8a8", "w4a8", "mxfp4"])
-@pytest.mark.parametrize("t,bm", [(8, 16), (64, 32), (300, 64), (1024, 64), (300, 128), (1024, 128)])
+@pytest.mark.parametrize("t,bm", [(8, 16), (64, 32), (200, 64), (300, 64), (1024, 64), (300, 128), (1024, 128)])
 @pytest.mark.parametrize("per_pair", [0, 1])
 def test_moe_8bit(qdg, kind, t, bm, per_pair):
     # gate+up reads token rows (per_pair 0), down one row per pair (1)
@@ -78,7 +80,11 @@ def test_moe_8bit(qdg, kind, t, bm, per_pair):
         layer = _layer(kind, n, k, otype)
         pk = H.Packed(layer, *std)
         plan = q.qdg_plan_create(layer, q.moe(TOP_K))
-        assert ("family=qtile " if bm in (64, 128) else "family=stream ") in q.qdg_moe_describe(plan, t, bm)
+        d = q.qdg_moe_describe(plan, t, bm)
+        assert ("family=qtile " if bm in (64, 128) else "family=stream ") in d, d
+        # at most one block of rows per expert on average: the instance that
+        # skips all-padding 32-row halves of blocks
+        assert ("pad_skip=1" in d) == (bm in (64, 128) and t * TOP_K <= E * bm), d
         ws, nbytes = H.workspace(plan, t)
         y = H.out_tensor(t * TOP_K, n, otype)  # NaN / INT_MIN canary
         q.qdg_moe_gemm(plan, a_dev.data_ptr(), sa_dev.data_ptr(), pk.buf.data_ptr(), sid.data_ptr(),
