@@ -324,6 +324,22 @@ def test_tuned_split_never_exceeds_the_k_groups():
         assert fam in d and "split_k=8 " in d, d
 
 
+def test_moe_padding_skip_choice():
+    # 8-bit LDS-tiled MoE: the instance that skips all-padding 32-row halves
+    # of blocks serves calls whose experts average at most one block of rows
+    # (T*top_k <= E*block_m); the bf16 tiles skip inside every MoE instance
+    E, top_k = 256, 8
+    for mk in (q.layer_w8a8, q.layer_w4a8, q.layer_mxfp4, q.layer_w4a4, q.layer_mxfp4_int8):
+        p = q.qdg_plan_create(mk(4096, 7168, num_experts=E), q.moe(top_k))
+        for t, bm in ((512, 64), (2048, 64), (2049, 64), (4096, 64), (4096, 128), (4097, 128)):
+            d = q.qdg_moe_describe(p, t, bm)
+            assert "family=qtile " in d, d
+            assert ("pad_skip=1" in d) == (t * top_k <= E * bm), (t, bm, d)
+        assert "pad_skip" not in q.qdg_plan_describe(q.qdg_plan_create(mk(4096, 7168), q.dense()), 4096)
+    pw = q.qdg_plan_create(q.layer_w4a16(4096, 7168, num_experts=E), q.moe(top_k))
+    assert "pad_skip" not in q.qdg_moe_describe(pw, 512, 64)
+
+
 def test_moe_16_row_tile_tuning():
     # block_n 512 names the 16 x 512 tiles of grouped W4A16 16-row blocks;
     # without a tuning they serve K <= 2048 (16 groups), the streaming family
