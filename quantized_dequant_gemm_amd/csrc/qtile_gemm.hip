@@ -250,8 +250,9 @@ __device__ __forceinline__ void q_k_loop(char* const (&stage)[3], const char* a_
       // the copies in flight.
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       asm volatile("s_barrier" ::: "memory");
-      q_load_stage<KIND, RAW, MOE, BM, BN, NW, 16 * PADSKIP + MT>(stage[(cur + NS - 1) % NS], a_g, a_off, as_off, p, wbase, sbase,
-                                          wg_tile0, wave, lane, min(gb + cur + NS - 1, g1 - 1));
+      q_load_stage<KIND, RAW, MOE, BM, BN, NW, 16 * PADSKIP + MT>(stage[(cur + NS - 1) % NS], a_g, a_off, as_off, p,
+                                                                 wbase, sbase, wg_tile0, wave, lane,
+                                                                 min(gb + cur + NS - 1, g1 - 1));
       q_frag_load<KIND, BM, BN, MT>(fr, stage[cur], a_lane, w_lane, rec_lane, as_lane);
       // MXFP4: all of the group's fragment reads go out before its first
       // MFMA (left to itself the scheduler sinks each row tile's reads next
@@ -391,16 +392,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qtile_gemm_kernel(cons
   // before LDS reads stay exact; the last partial round waits for all copies.
 #pragma unroll
   for (int q = 0; q < NS - 1; ++q)
-    q_load_stage<KIND, RAW, MOE, BM, BN, NW, 16 * PADSKIP>(stage[q], a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane,
-                                        min(g0 + q, g1 - 1));
+    q_load_stage<KIND, RAW, MOE, BM, BN, NW, 16 * PADSKIP>(stage[q], a_g, a_off, as_off, p, wbase, sbase, wg_tile0,
+                                                          wave, lane, min(g0 + q, g1 - 1));
   if constexpr (PADSKIP) {
     static_assert(MOE, "padding halves exist in grouped MoE blocks only");
     if (p.sorted_ids[mb * BM + wm * WTM + 32] >= p.num_pairs)
-      q_k_loop<KIND, RAW, NS, MOE, BM, BN, NW, VM_NEXT, PADSKIP, 2>(stage, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane, g0, g1, a_lane, w_lane, rec_lane, as_lane, acc);
+      q_k_loop<KIND, RAW, NS, MOE, BM, BN, NW, VM_NEXT, PADSKIP, 2>(
+          stage, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane, g0, g1, a_lane, w_lane, rec_lane,
+          as_lane, acc);
     else
-      q_k_loop<KIND, RAW, NS, MOE, BM, BN, NW, VM_NEXT, PADSKIP, 4>(stage, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane, g0, g1, a_lane, w_lane, rec_lane, as_lane, acc);
+      q_k_loop<KIND, RAW, NS, MOE, BM, BN, NW, VM_NEXT, PADSKIP, 4>(
+          stage, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane, g0, g1, a_lane, w_lane, rec_lane,
+          as_lane, acc);
   } else {
-    q_k_loop<KIND, RAW, NS, MOE, BM, BN, NW, VM_NEXT, PADSKIP, 4>(stage, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane, g0, g1, a_lane, w_lane, rec_lane, as_lane, acc);
+    q_k_loop<KIND, RAW, NS, MOE, BM, BN, NW, VM_NEXT, PADSKIP, 4>(
+        stage, a_g, a_off, as_off, p, wbase, sbase, wg_tile0, wave, lane, g0, g1, a_lane, w_lane, rec_lane,
+        as_lane, acc);
   }
 
   // ---- epilogue: scale, then per wave transpose each 16 x 64 strip through
@@ -511,8 +518,8 @@ hipError_t launch_q_inst(const GemmArgs& a, dim3 grid, int m_blocks, int n_block
     d->n_blocks = n_blocks;
     return hipSuccess;
   }
-  hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, MOE, WM, WN, PADSKIP>), grid, dim3(64 * WM * WN), 0, s, a, m_blocks,
-                     n_blocks);
+  hipLaunchKernelGGL((qtile_gemm_kernel<KIND, RAW, NS, MOE, WM, WN, PADSKIP>), grid, dim3(64 * WM * WN), 0, s, a,
+                     m_blocks, n_blocks);
   return hipGetLastError();
 }
 
