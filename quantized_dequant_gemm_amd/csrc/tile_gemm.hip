@@ -217,7 +217,9 @@ __device__ __forceinline__ void load_stage(char* st, const char* a_g, const uint
 // (each chain seeded with -(128+z) * rowsum) and fold them into the
 // accumulators with the group scales. N tiles past the end of the layer hold
 // duplicate data: computed like the others and never stored.
-template <bool ASYM, int BM, int BN, int MTW>
+// MTR: the row tiles run (grouped MoE: fewer when the wave's later rows are
+// all padding).
+template <bool ASYM, int BM, int BN, int MTW, int MTR = MTW>
 __device__ __forceinline__ void tile_group(const char* st, int a_lane, int w_lane, int s_lane, int rs_lane,
                                            uint32_t um, uint32_t ue, f32x4_t (&acc)[MTW][4]) {
   using L = Stage<BM, BN>;
@@ -232,7 +234,7 @@ __device__ __forceinline__ void tile_group(const char* st, int a_lane, int w_lan
     negz[t] = __builtin_bit_cast(float, (rec.y & 0xFFFFu) << 16);  // -(128+z)
   }
 #pragma unroll
-  for (int mt = 0; mt < MTW; ++mt) {
+  for (int mt = 0; mt < MTR; ++mt) {
     u32x4_t a[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) a[j] = *(const u32x4_t*)(st + a_lane + mt * 16 * L::ROW + j * 16);
@@ -655,11 +657,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
       load_stage<BM, BN, NW, !NV, UB>(stage[q], a_g, a_off, p, wbase, sbase, s_off, wg_tile0, wave, lane, mb,
                              min(g0 + q, g1 - 1));
   }
-  // The K loop, instantiated per count of the wave's 32-row blocks that
-  // hold real rows: a grouped MoE wave whose rows 32..63 are all padding
-  // (an expert's real entries lead its blocks, so the entry at row 32 tells)
-  // skips their fragment reads and MFMAs. Both instances run the same
-  // barriers, so the waves of one workgroup may take different ones.
+  // The K loop, instantiated per count of the wave's row blocks that hold
+  // real rows (RB = 1: only the first half): a grouped MoE wave whose second
+  // half of rows (32..63 of a 64-row wave tile, 16..31 of a 32-row one) is
+  // all padding (an expert's real entries lead its blocks, so the entry at
+  // the half's first row tells) skips their fragment reads and MFMAs. Both
+  // instances run the same barriers, so the waves of one workgroup may take
+  // different ones.
   auto k_loop = [&](auto rb_count) __attribute__((always_inline)) {
     constexpr int RB = decltype(rb_count)::value;
     int gb = g0;
@@ -688,7 +692,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
         else if constexpr (M32)
           tile_group32<ASYM, BM, BN, RB>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
         else
-          tile_group<ASYM, BM, BN, MTW>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
+          tile_group<ASYM, BM, BN, MTW, RB == 2 ? MTW : 1>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
       }
     }
 #pragma unroll
@@ -705,12 +709,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void tile_gemm_kernel(const
         else if constexpr (M32)
           tile_group32<ASYM, BM, BN, RB>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc32);
         else
-          tile_group<ASYM, BM, BN, MTW>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
+          tile_group<ASYM, BM, BN, MTW, RB == 2 ? MTW : 1>(stage[cur], a_lane, w_lane, s_lane, rs_lane, um, ue, acc);
       }
     }
   };
   if constexpr (MOE && M32 && !NV && !W8 && !W2) {
     if (p.sorted_ids[mb * BM + wm * WTM + 32] >= p.num_pairs)
+      k_loop(IntC<1>{});
+    else
+      k_loop(IntC<2>{});
+  } else if constexpr (MOE && !M32 && MTW == 2) {
+    // 32-row wave tiles of 16 x 16 MFMAs: rows 16..31 all padding
+    if (p.sorted_ids[mb * BM + wm * WTM + 16] >= p.num_pairs)
       k_loop(IntC<1>{});
     else
       k_loop(IntC<2>{});
